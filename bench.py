@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the Mamba-2 SSD chunked-scan forward (libssd) on one MI355X.
+
+A step is one full forward -- chunk_cumsum, chunk_state, state_passing,
+chunk_scan -- over one batch of seeded synthetic input already resident in
+HBM.  Prints one JSON line with whole-job tokens/s, the roofline position of
+the dominant kernel (timed with HIP events on the launch stream), and the CPU
+oracle timed on a bounded sample of the same workload on the host cores.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "SSD fwd tokens/sec per layer + % of MFMA/HBM roofline (H=80,P=64,N=128)"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3        # MI355X fp32 vector
+STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
+KERNEL_SOURCES = {
+    "chunk_cumsum": "k_scan_prep.hip", "state_passing": "k_scan_prep.hip",
+    "chunk_state": "k_chunk_state.hip", "chunk_scan": "k_chunk_scan.hip",
+}
+
+
+def log(msg: str) -> None:
+    print(msg, file=sys.stderr, flush=True)
+
+
+def algorithmic(w, stage: str):
+    """Compulsory HBM bytes and MFMA flops of one launch of a stage.
+
+    Per token (T tokens, nc chunks, S sequences, s = element bytes of x/B/C/y,
+    h = element bytes of the hprev buffer):
+      chunk_cumsum   bytes 8 H                      (dt in, cumulative decay out)
+      chunk_state    bytes s H P + s G N + 8 H, plus 4 H P N per chunk (S out)
+                     flops 2 H P N
+      state_passing  bytes (4 + h) H P N per chunk, plus 4 H P N per sequence for
+                     the final state (and 4 H P N more when an initial state is read)
+      chunk_scan     bytes 2 s H P + 2 s G N + 8 H, plus h H P N per chunk
+                     flops H (2 P N + (Q + 1) P) + G (Q + 1) N  (causal pairs only,
+                     C.B^T once per group)
+    """
+    T, H, P, N, G, Q = w.tokens, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
+    nseq = w.nsequences
+    lens = [int(w.seq_off[i + 1] - w.seq_off[i]) for i in range(nseq)]
+    nc = sum(-(-L // Q) for L in lens)
+    s = 2 if w.dtype == "bf16" else 4
+    hsz = s
+    if stage == "chunk_cumsum":
+        return 8 * T * H, 0
+    if stage == "chunk_state":
+        return s * T * H * P + s * T * G * N + 8 * T * H + 4 * nc * H * P * N, 2 * T * H * P * N
+    if stage == "state_passing":
+        init = 4 * nseq * H * P * N if w.h0 is not None else 0
+        return (4 + hsz) * nc * H * P * N + 4 * nseq * H * P * N + init, 0
+    if stage == "chunk_scan":
+        b = 2 * s * T * H * P + 2 * s * T * G * N + 8 * T * H + hsz * nc * H * P * N
+        f = T * (H * (2 * P * N + (Q + 1) * P) + G * (Q + 1) * N)
+        return b, f
+    raise KeyError(stage)
+
+
+def kernel_hash(stage: str) -> str:
+    h = hashlib.sha256()
+    for f in (KERNEL_SOURCES[stage], "ssd_device.hpp"):
+        with open(os.path.join(ROOT, "mamba_ssd_layer_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(stage: str, workload: str):
+    """HBM traffic per launch from committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"{stage}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_src_sha") != kernel_hash(stage):
+        return None
+    return rec.get("traffic_bytes")
+
+
+def cpu_baseline(w, target_cpu_seconds: float = 20.0):
+    """The fp64 oracle, as it stands, on a bounded sample of (sequence, head)
+    pairs of the same workload, scaled to tokens/s of the whole workload."""
+    import numpy as np
+    import oracle
+    threads = oracle.max_threads()
+    nseq, H = w.nsequences, w.nheads
+    total_pairs = nseq * H
+    r = np.random.default_rng(1)
+    order = [(int(p // H), int(p % H)) for p in r.permutation(total_pairs)]
+    # calibrate on one pair, single-threaded
+    t0 = time.perf_counter()
+    oracle.recurrence_workload(w, pairs=order[:1], nthreads=1)
+    per_pair = time.perf_counter() - t0
+    n = int(max(1, min(total_pairs, target_cpu_seconds / max(per_pair, 1e-6))))
+    n = max(min(threads, total_pairs), (n // threads) * threads)
+    n = min(n, total_pairs)
+    pairs = order[:n]
+    lens = np.diff(w.seq_off)
+    sample_tokens = int(sum(lens[s] for s, _ in pairs))  # token-heads in the sample
+    t0 = time.perf_counter()
+    oracle.recurrence_workload(w, pairs=pairs, nthreads=threads)
+    el = time.perf_counter() - t0
+    used = min(threads, n)
+    # the workload is T tokens x H heads of work; the sample covered sample_tokens token-heads
+    value = (sample_tokens / H) / el
+    return {"value": value, "unit": "tokens/s", "cores": used, "kind": "oracle",
+            "sample": f"{n} of {total_pairs} (sequence, head) pairs of {w.name}, "
+                      f"{sample_tokens} token-heads, fp64 recurrence, {el:.2f} s wall on {used} "
+                      f"threads ({per_pair:.2f} s for one pair on one thread)"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="large_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stage-timing", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build measures one GPU only; the SSD forward shards over "
+              "(sequence, head) with no exchange, and no multi-GPU run is part of it. "
+              "Run with --gpus 1.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import mamba_ssd_layer_amd as ssd
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    log(f"bench: generating workload {args.workload}")
+    w = workloads.make_workload(args.workload)
+    io = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    T, H, P, G, N = w.tokens, w.nheads, w.headdim, w.ngroups, w.dstate
+    lead = (1, T) if w.nseq else (w.batch, w.seqlen)
+
+    def up(a, shape, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return (t.to(dtype) if dtype is not None else t).view(*shape).contiguous()
+
+    x = up(w.x, (*lead, H, P), io)
+    dt = up(w.dt, (*lead, H))
+    A = up(w.A, (H,))
+    Bm = up(w.B, (*lead, G, N), io)
+    Cm = up(w.C, (*lead, G, N), io)
+    D = up(w.D, (H,))
+    h0 = up(w.h0, w.h0.shape) if w.h0 is not None else None
+    cu = up(w.cu_seqlens, (w.nseq + 1,)) if w.nseq else None
+    dims = ssd.dims_for(x, Bm, cu)
+    plan = ssd.SSDForward(dims, w.chunk, device=dev)
+    y = torch.empty_like(x)
+    fin = torch.empty((w.nsequences, H, P, N), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    log(f"bench: {T} tokens, workspace {plan.layout.total_bytes / 2**20:.1f} MiB; "
+        f"{args.warmup} warmup + {args.steps} timed steps")
+
+    def step():
+        plan(x, dt, A, Bm, Cm, D, h0, cu, y=y, final_state=fin)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev0 = torch.cuda.Event(enable_timing=True)
+    ev1 = torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for _ in range(args.steps):
+        step()
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = ev0.elapsed_time(ev1) / args.steps
+    value = T / (ms / 1e3)
+    log(f"bench: {ms * 1e3:.1f} us/step ({wall / args.steps * 1e3:.1f} us wall), "
+        f"{value / 1e6:.1f} M tokens/s")
+
+    # per-stage times: the same stages launched one by one, HIP events between
+    stage_us = {}
+    if not args.no_stage_timing:
+        calls = {
+            "chunk_cumsum": lambda: plan.cumsum(dt, A, cu),
+            "chunk_state": lambda: plan.state(x, Bm),
+            "state_passing": lambda: plan.passing(h0, fin),
+            "chunk_scan": lambda: plan.scan(x, Bm, Cm, D, y),
+        }
+        evs = {s: [] for s in STAGES}
+        for _ in range(args.steps):
+            for s in STAGES:
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                calls[s]()
+                e1.record(stream)
+                evs[s].append((e0, e1))
+        torch.cuda.synchronize()
+        for s in STAGES:
+            stage_us[s] = sum(a.elapsed_time(b) for a, b in evs[s]) / len(evs[s]) * 1e3
+    kernels = {}
+    for s in STAGES:
+        b, f = algorithmic(w, s)
+        entry = {"bytes": b, "flops": f}
+        if s in stage_us:
+            t = stage_us[s] * 1e-6
+            entry.update(us=round(stage_us[s], 2), GBs=round(b / t / 1e9, 1),
+                         TFLOPs=round(f / t / 1e12, 2) if f else 0.0,
+                         hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4))
+        kernels[s] = entry
+    roofline = None
+    if stage_us:
+        dom = max(stage_us, key=stage_us.get)
+        b, f = algorithmic(w, dom)
+        t = stage_us[dom] * 1e-6
+        mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        t_hbm = b / (HBM_PEAK_GBS * 1e9)
+        t_mfma = f / (mfma_peak * 1e12)
+        if t_hbm >= t_mfma:
+            roofline = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s"}
+        else:
+            roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu",
+                        "achieved": round(f / t / 1e12, 2), "peak": mfma_peak, "unit": "TFLOP/s"}
+        roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
+        roofline["traffic"] = load_traffic(dom, w.name)
+        roofline["kernel"] = dom
+        roofline["kernel_us"] = round(stage_us[dom], 2)
+        roofline["algorithmic_bytes"] = b
+        roofline["algorithmic_flops"] = f
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("bench: timing the CPU oracle on a sample")
+        cpu = cpu_baseline(w)
+
+    out = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "config": {**workloads.describe(w), "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

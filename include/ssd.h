@@ -1,0 +1,189 @@
+/*
+ * libssd -- Mamba-2 SSD (structured state space duality) chunked-scan forward
+ * for AMD Instinct MI355X (gfx950).  C ABI.
+ *
+ * The operation (per sequence s, head h, group g = floor(h*G/H)):
+ *
+ *   h_{-1} = init_state[s,h]                          (zeros if init_state == NULL)
+ *   h_t    = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t B_t^T     (P x N state)
+ *   y_t    = C_t h_t + D_h * x_t                      (D == NULL means D = 0)
+ *   final_state[s,h] = h after the sequence's last token
+ *
+ * i.e. the selective state space recurrence with a scalar-identity transition
+ * (page "State Space Duality and Mamba-2: Unifying Transformers and
+ * Semiseparable Matrices", sections "Mathematical Foundations" and "The
+ * Scalar-Identity Structural Constraint"), evaluated blockwise as on page
+ * "Mamba-2 Architecture: State Space Duality Explained", section "2. The
+ * Chunked SSD Algorithm": within a chunk of Q tokens the masked product
+ * (C B^T o L) X, between chunks a hand-off of the P x N state.  The pages are
+ * silent on the input discretisation and the skip term; the library takes the
+ * Euler weight dt_t on B_t x_t and adds D_h x_t.  dt is taken as given
+ * (already positive, no softplus inside).  Heads in one group share B and C
+ * (same page, item 4 of the chunked algorithm).
+ *
+ * Layouts (row-major, contiguous, last index fastest).  T = batch * seqlen
+ * tokens for a fixed-length batch, or the packed total for variable length:
+ *   x          [T, H, P]   io dtype        y           [T, H, P] io dtype
+ *   B, C       [T, G, N]   io dtype        dt          [T, H]    float
+ *   A, D       [H]         float           init/final  [S, H, P, N] float
+ * where S = batch (fixed length) or nseq (variable length).
+ *
+ * Memory and ownership.  Every pointer argument except `dims` and the layout
+ * struct is device memory owned by the caller.  The library allocates
+ * nothing, keeps no mutable global state and never synchronises: every entry
+ * point only enqueues kernels on `stream` (a hipStream_t; NULL = the default
+ * stream) and returns.  Calls on different streams are independent provided
+ * they use distinct workspaces.
+ *
+ * Alignment.  x, B, C, y, init_state, final_state: 16 bytes; dt, A, D: 4
+ * bytes; workspace: 256 bytes.
+ *
+ * Errors.  Every entry point returns an ssd_status.  Arguments are validated
+ * before any HIP call, so a rejected call touches no device state.  A failed
+ * kernel launch returns SSD_ERR_HIP; faults inside kernels surface at the
+ * caller's next synchronisation, as with any asynchronous HIP work.  Nothing
+ * is printed and nothing is thrown.
+ *
+ * Aliasing.  y must not overlap x, B, C or dt.  final_state may be the same
+ * pointer as init_state (the state is read before it is overwritten) but may
+ * not otherwise overlap it.
+ */
+#ifndef LIBSSD_SSD_H_
+#define LIBSSD_SSD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_VERSION 1
+
+typedef enum {
+  SSD_OK = 0,
+  SSD_ERR_INVALID_ARG = 1, /* null/misaligned pointer, bad size, overlap, bad dims */
+  SSD_ERR_UNSUPPORTED = 2, /* valid, but outside the compiled shapes (see below) */
+  SSD_ERR_WORKSPACE = 3,   /* workspace missing or smaller than ssd_workspace_size() */
+  SSD_ERR_HIP = 4          /* a HIP call or kernel launch failed */
+} ssd_status;
+
+/* Element type of x, B, C, y (and of the Hprev workspace buffer). */
+typedef enum { SSD_F32 = 0, SSD_BF16 = 1 } ssd_dtype;
+
+typedef struct {
+  int64_t batch;    /* fixed-length rows; must be 1 when nseq > 0 */
+  int64_t seqlen;   /* tokens per row; when nseq > 0 the total packed token count T */
+  int64_t nheads;   /* H */
+  int64_t headdim;  /* P */
+  int64_t dstate;   /* N */
+  int64_t ngroups;  /* G, must divide H */
+  int64_t nseq;     /* 0: fixed-length batch; > 0: packed sequences given by cu_seqlens */
+  int32_t io_dtype; /* an ssd_dtype */
+  int32_t reserved; /* must be 0 */
+} ssd_dims;
+
+/* Supported shapes.
+ *   chunk_len Q in {64, 128, 256}.
+ *   SSD_BF16: headdim P == 64, dstate N in {64, 128, 256}; all contractions on
+ *             bf16 MFMA with fp32 accumulation; y rounded to nearest-even.
+ *   SSD_F32:  headdim and dstate multiples of 16, at most 256; fp32 throughout.
+ *   T, nseq and every sequence length below 2^31.
+ * Anything else valid returns SSD_ERR_UNSUPPORTED. */
+
+/* Byte offsets of the workspace buffers (all 256-byte aligned).  The
+ * per-stage entry points below read and write these; tests read them to check
+ * each stage.  nc_max chunks are laid out, numbered sequence-major:
+ *   fixed length: nc_max = batch * ceil(seqlen / Q), chunk c = b * ceil(L/Q) + k
+ *   packed:       nc_max = ceil(T / Q) + nseq (upper bound; the exact count is
+ *                 written to the chunk directory), chunks restart at each
+ *                 sequence start.
+ *   acum   float [nc_max][H][Q]   inclusive cumulative sum of dt*A from the chunk
+ *                                 start; positions past a partial chunk's end hold
+ *                                 the chunk's last value
+ *   dtq    float [nc_max][H][Q]   dt transposed to chunk-major, 0 past the end
+ *   states float [nc_max][H][P][N] chunk states S_c (decay-weighted sum of
+ *                                 dt_l x_l B_l^T over the chunk)
+ *   hprev  io    [nc_max][H][P][N] state entering each chunk
+ *   chunk_table  int32 [nc_max][4] (sequence, first token, length, 0)   packed only
+ *   chunk_dir    int32 [nseq + 2]  first chunk of each sequence, then the total,
+ *                                  then an error word (nonzero: cu_seqlens was not
+ *                                  non-decreasing from 0 to T)          packed only
+ */
+typedef struct {
+  size_t total_bytes;
+  int64_t nc_max;
+  size_t acum_offset;
+  size_t dtq_offset;
+  size_t states_offset;
+  size_t hprev_offset;
+  size_t chunk_table_offset; /* 0 and unused for fixed-length batches */
+  size_t chunk_dir_offset;   /* 0 and unused for fixed-length batches */
+} ssd_workspace_layout;
+
+/* Workspace bytes needed for these dims and chunk length; 0 if they are
+ * invalid or unsupported.  Host-only, no HIP call. */
+size_t ssd_workspace_size(const ssd_dims *dims, int chunk_len);
+
+/* Fills *out with the workspace layout.  Host-only, no HIP call. */
+ssd_status ssd_get_workspace_layout(const ssd_dims *dims, int chunk_len,
+                                    ssd_workspace_layout *out);
+
+/* The whole forward: chunk_cumsum, chunk_state, state_passing, chunk_scan, in
+ * that order on `stream`.
+ *   cu_seqlens: device int32 [nseq + 1] when dims->nseq > 0 (non-decreasing,
+ *               cu_seqlens[0] = 0, cu_seqlens[nseq] = T), else NULL.  Values
+ *               that break this never cause an out-of-bounds access: lengths
+ *               are clamped and the error word of the chunk directory is set.
+ *   D, init_state, final_state: may be NULL.
+ * Returns after enqueueing. */
+ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, int chunk_len,
+                              const float *init_state, const int32_t *cu_seqlens, void *y,
+                              float *final_state, const ssd_dims *dims, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Stage 1 (chunk_cumsum): for packed batches first builds the chunk table and
+ * directory from cu_seqlens; then writes acum and dtq.  The log-space
+ * cumulative decay: the product of the scalar decays between tokens i and j
+ * is exp(s_j - s_i), page "State Space Duality and Mamba-2 ...", section "The
+ * Scalar-Identity Structural Constraint". */
+ssd_status ssd_chunk_cumsum(const float *dt, const float *A, int chunk_len,
+                            const int32_t *cu_seqlens, const ssd_dims *dims, void *workspace,
+                            size_t workspace_bytes, void *stream);
+
+/* Stage 2 (chunk_state): states[c,h] = sum_l exp(acum_last - acum_l) dtq_l
+ * x_l^T B_l over the chunk's tokens, the state each chunk would leave from a
+ * zero start (page "Mamba-2 Architecture: State Space Duality Explained",
+ * "2. The Chunked SSD Algorithm", item 2, with the decay weights the
+ * recurrence implies).  Needs stage 1's output in the same workspace. */
+ssd_status ssd_chunk_state(const void *x, const void *B, int chunk_len, const ssd_dims *dims,
+                           void *workspace, size_t workspace_bytes, void *stream);
+
+/* Stage 3 (state_passing): per sequence and head, in chunk order,
+ * hprev[c] = h; h = exp(acum_last[c]) h + states[c], starting from
+ * init_state (or 0); final_state = h at the sequence end (same page and item:
+ * the scalar recurrence between chunk boundaries).  Needs stages 1-2. */
+ssd_status ssd_state_passing(const float *init_state, float *final_state, int chunk_len,
+                             const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                             void *stream);
+
+/* Stage 4 (chunk_scan): per chunk, y_l = sum_{s<=l} (C_l . B_s)
+ * exp(acum_l - acum_s) dt_s x_s + exp(acum_l) C_l hprev^T + D x_l -- the
+ * masked product (C B^T o L) X plus the state handed in (same page, item 1
+ * and the inter-chunk hand-off).  Needs stages 1-3. */
+ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const float *D, void *y,
+                          int chunk_len, const ssd_dims *dims, void *workspace,
+                          size_t workspace_bytes, void *stream);
+
+/* Static text for a status code. */
+const char *ssd_status_string(ssd_status status);
+
+/* SSD_VERSION of the built library. */
+int ssd_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H_ */

@@ -1,0 +1,131 @@
+"""mamba_ssd_layer_amd -- Mamba-2 SSD chunked-scan forward on AMD MI355X.
+
+The compute lives in libssd.so (HIP kernels for gfx950 behind the C ABI of
+include/ssd.h).  This package is its Python face:
+
+  libssd             ctypes binding, same names as the C entry points
+  chunk_scan_fwd()   convenience wrapper: infers the dims from torch tensors,
+                     allocates y / final_state / workspace, runs the forward
+  SSDForward         a reusable plan (fixed dims, workspace allocated once)
+
+Tensors (GPU, contiguous):
+  x [B, L, H, P]   dt [B, L, H] float32   A [H] float32   B, C [B, L, G, N]
+  D [H] float32 or None   init_state [B, H, P, N] float32 or None
+For a packed variable-length batch pass cu_seqlens (int32 [nseq + 1], GPU),
+B = 1 (the leading dim may be dropped), and init_state [nseq, H, P, N].
+x, B, C and y are bfloat16 or float32 (all the same).
+"""
+from __future__ import annotations
+
+from typing import Optional, Tuple
+
+import torch
+
+from . import libssd
+from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsupported,
+                     SSDWorkspaceError, make_dims)
+
+__all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDError", "SSDInvalidArgument",
+           "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for"]
+
+
+def _io_dtype(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, f"unsupported dtype {t.dtype}")
+
+
+def dims_for(x: torch.Tensor, B: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None):
+    """ssd_dims from tensor shapes (see the module docstring)."""
+    if cu_seqlens is not None:
+        if x.dim() == 4:
+            if x.shape[0] != 1:
+                raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG,
+                                         "packed batches have a leading dim of 1")
+            _, T, H, P = x.shape
+        else:
+            T, H, P = x.shape
+        G, N = B.shape[-2], B.shape[-1]
+        nseq = cu_seqlens.numel() - 1
+        return make_dims(1, T, H, P, N, G, nseq, _io_dtype(x))
+    if x.dim() != 4 or B.dim() != 4:
+        raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "x and B must be 4-D")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    return make_dims(b, L, H, P, N, G, 0, _io_dtype(x))
+
+
+class SSDForward:
+    """A plan for one set of dims: the workspace is allocated once and every
+    call enqueues the four stages on the current stream."""
+
+    def __init__(self, dims, chunk_len: int, device="cuda"):
+        self.dims = dims
+        self.chunk_len = int(chunk_len)
+        self.layout = libssd.ssd_get_workspace_layout(dims, chunk_len)
+        self.workspace = torch.empty(self.layout.total_bytes, dtype=torch.uint8, device=device)
+        self.nrows = dims.nseq if dims.nseq > 0 else dims.batch
+
+    def __call__(self, x, dt, A, B, C, D=None, init_state=None, cu_seqlens=None, y=None,
+                 final_state=None, want_final: bool = True, stream=None):
+        if y is None:
+            y = torch.empty_like(x)
+        if final_state is None and want_final:
+            final_state = torch.empty((self.nrows, self.dims.nheads, self.dims.headdim,
+                                       self.dims.dstate), dtype=torch.float32, device=x.device)
+        libssd.ssd_chunk_scan_fwd(x, dt, A, B, C, D, self.chunk_len, init_state, cu_seqlens, y,
+                                  final_state, self.dims, self.workspace, stream)
+        return y, final_state
+
+    # per-stage calls on the plan's workspace (for checks and timing)
+    def cumsum(self, dt, A, cu_seqlens=None, stream=None):
+        libssd.ssd_chunk_cumsum(dt, A, self.chunk_len, cu_seqlens, self.dims, self.workspace,
+                                stream)
+
+    def state(self, x, B, stream=None):
+        libssd.ssd_chunk_state(x, B, self.chunk_len, self.dims, self.workspace, stream)
+
+    def passing(self, init_state, final_state, stream=None):
+        libssd.ssd_state_passing(init_state, final_state, self.chunk_len, self.dims,
+                                 self.workspace, stream)
+
+    def scan(self, x, B, C, D, y, stream=None):
+        libssd.ssd_chunk_scan(x, B, C, D, y, self.chunk_len, self.dims, self.workspace, stream)
+
+    def view(self, name: str) -> torch.Tensor:
+        """A typed view of one workspace buffer (acum, dtq, states, hprev,
+        chunk_table, chunk_dir) in its documented shape."""
+        d, L, Q = self.dims, self.layout, self.chunk_len
+        nc, H, P, N = L.nc_max, d.nheads, d.headdim, d.dstate
+        ws = self.workspace
+
+        def sl(off, n, dtype):
+            nbytes = n * torch.tensor([], dtype=dtype).element_size()
+            return ws[off:off + nbytes].view(dtype)
+
+        if name == "acum":
+            return sl(L.acum_offset, nc * H * Q, torch.float32).view(nc, H, Q)
+        if name == "dtq":
+            return sl(L.dtq_offset, nc * H * Q, torch.float32).view(nc, H, Q)
+        if name == "states":
+            return sl(L.states_offset, nc * H * P * N, torch.float32).view(nc, H, P, N)
+        if name == "hprev":
+            dt_ = torch.bfloat16 if d.io_dtype == SSD_BF16 else torch.float32
+            return sl(L.hprev_offset, nc * H * P * N, dt_).view(nc, H, P, N)
+        if name == "chunk_table":
+            return sl(L.chunk_table_offset, nc * 4, torch.int32).view(nc, 4)
+        if name == "chunk_dir":
+            return sl(L.chunk_dir_offset, d.nseq + 2, torch.int32)
+        raise KeyError(name)
+
+
+def chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                   C: torch.Tensor, D: Optional[torch.Tensor] = None, chunk_len: int = 256,
+                   init_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None) -> Tuple[torch.Tensor, torch.Tensor]:
+    """y, final_state = SSD forward (allocates outputs and a workspace)."""
+    dims = dims_for(x, B, cu_seqlens)
+    plan = SSDForward(dims, chunk_len, device=x.device)
+    return plan(x, dt, A, B, C, D, init_state, cu_seqlens)

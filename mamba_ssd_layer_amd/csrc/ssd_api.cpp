@@ -1,0 +1,314 @@
+// libssd C ABI: argument validation, workspace layout and launch order.
+// Every check runs before the first HIP call, so a rejected call leaves all
+// device state untouched and can be tested on a machine without a GPU.
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "ssd.h"
+#include "ssd_launch.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  ssd::Geometry geo;
+  ssd_workspace_layout ws;
+  bool bf16;
+  size_t io_size;
+};
+
+// Validates dims + chunk length and computes geometry and workspace layout.
+ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
+  if (!d || !plan) return SSD_ERR_INVALID_ARG;
+  if (d->reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
+  if (d->batch < 1 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
+      d->ngroups < 1 || d->nseq < 0)
+    return SSD_ERR_INVALID_ARG;
+  if (d->nheads % d->ngroups != 0) return SSD_ERR_INVALID_ARG;
+  if (d->nseq > 0 && d->batch != 1) return SSD_ERR_INVALID_ARG;
+  if (chunk_len < 1) return SSD_ERR_INVALID_ARG;
+  if (chunk_len != 64 && chunk_len != 128 && chunk_len != 256) return SSD_ERR_UNSUPPORTED;
+  const int64_t H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+  const bool bf16 = d->io_dtype == SSD_BF16;
+  if (P % 16 != 0 || N % 16 != 0 || P > 256 || N > 256) return SSD_ERR_UNSUPPORTED;
+  if (bf16 && (!ssd::chunk_state_bf16_supported((int)P, (int)N, chunk_len) ||
+               !ssd::chunk_scan_bf16_supported((int)P, (int)N, chunk_len)))
+    return SSD_ERR_UNSUPPORTED;
+  // grid limits: heads and rows sit on grid y / z (at most 65535)
+  const int64_t nrows = d->nseq > 0 ? d->nseq : d->batch;
+  if (H > 65535 || nrows > 65535) return SSD_ERR_UNSUPPORTED;
+  const int64_t T = d->nseq > 0 ? d->seqlen : d->batch * d->seqlen;
+  if (d->nseq == 0 && d->seqlen > 0 && d->batch > INT64_MAX / d->seqlen) return SSD_ERR_UNSUPPORTED;
+  if (T >= ((int64_t)1 << 31)) return SSD_ERR_UNSUPPORTED;
+  const int64_t Q = chunk_len;
+  const int64_t nc_row = d->nseq > 0 ? 0 : ceil_div(d->seqlen, Q);
+  const int64_t nc_max = d->nseq > 0 ? ceil_div(T, Q) + d->nseq : d->batch * nc_row;
+  if (nc_max >= ((int64_t)1 << 31)) return SSD_ERR_UNSUPPORTED;
+
+  Plan p{};
+  p.bf16 = bf16;
+  p.io_size = bf16 ? 2 : 4;
+  ssd::Geometry &g = p.geo;
+  g.tokens = T;
+  g.L = d->nseq > 0 ? T : d->seqlen;
+  g.nc_row = (int32_t)nc_row;
+  g.Q = chunk_len;
+  g.nc_max = nc_max;
+  g.nrows = nrows;
+  g.H = (int32_t)H;
+  g.P = (int32_t)P;
+  g.N = (int32_t)N;
+  g.G = (int32_t)G;
+  g.packed = d->nseq > 0;
+  g.table = nullptr;
+  g.dir = nullptr;
+
+  ssd_workspace_layout &w = p.ws;
+  size_t off = 0;
+  const size_t nch = (size_t)nc_max * (size_t)H;
+  w.nc_max = nc_max;
+  w.acum_offset = off;
+  off = align_up(off + nch * Q * sizeof(float));
+  w.dtq_offset = off;
+  off = align_up(off + nch * Q * sizeof(float));
+  w.states_offset = off;
+  off = align_up(off + nch * (size_t)(P * N) * sizeof(float));
+  w.hprev_offset = off;
+  off = align_up(off + nch * (size_t)(P * N) * p.io_size);
+  if (g.packed) {
+    w.chunk_table_offset = off;
+    off = align_up(off + (size_t)nc_max * 4 * sizeof(int32_t));
+    w.chunk_dir_offset = off;
+    off = align_up(off + (size_t)(d->nseq + 2) * sizeof(int32_t));
+  } else {
+    w.chunk_table_offset = 0;
+    w.chunk_dir_offset = 0;
+  }
+  w.total_bytes = off == 0 ? kAlign : off;
+  *plan = p;
+  return SSD_OK;
+}
+
+// Binds the workspace pointers of the plan; checks size and alignment.
+ssd_status bind_workspace(Plan *p, void *workspace, size_t workspace_bytes) {
+  if (!workspace || workspace_bytes < p->ws.total_bytes) return SSD_ERR_WORKSPACE;
+  if (!aligned(workspace, kAlign)) return SSD_ERR_INVALID_ARG;
+  if (p->geo.packed) {
+    char *base = static_cast<char *>(workspace);
+    p->geo.table = reinterpret_cast<const int32_t *>(base + p->ws.chunk_table_offset);
+    p->geo.dir = reinterpret_cast<const int32_t *>(base + p->ws.chunk_dir_offset);
+  }
+  return SSD_OK;
+}
+
+template <typename T>
+T *ws_ptr(void *workspace, size_t offset) {
+  return reinterpret_cast<T *>(static_cast<char *>(workspace) + offset);
+}
+
+bool overlaps(const void *a, size_t na, const void *b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+struct Sizes {
+  size_t x, bc, dt, state;
+};
+
+Sizes tensor_bytes(const Plan &p) {
+  const ssd::Geometry &g = p.geo;
+  Sizes s;
+  s.x = (size_t)g.tokens * g.H * g.P * p.io_size;
+  s.bc = (size_t)g.tokens * g.G * g.N * p.io_size;
+  s.dt = (size_t)g.tokens * g.H * sizeof(float);
+  s.state = (size_t)g.nrows * g.H * g.P * g.N * sizeof(float);
+  return s;
+}
+
+// Token tensors may be NULL only when there are no tokens.
+bool tok_ptr_ok(const void *ptr, const Plan &p, size_t align) {
+  if (p.geo.tokens == 0) return ptr == nullptr || aligned(ptr, align);
+  return ptr != nullptr && aligned(ptr, align);
+}
+
+ssd_status check_cumsum_args(const float *dt, const float *A, const int32_t *cu, const Plan &p) {
+  if (!tok_ptr_ok(dt, p, 4)) return SSD_ERR_INVALID_ARG;
+  if (!A || !aligned(A, 4)) return SSD_ERR_INVALID_ARG;
+  if (p.geo.packed && (!cu || !aligned(cu, 4))) return SSD_ERR_INVALID_ARG;
+  return SSD_OK;
+}
+
+ssd_status check_state_args(const void *x, const void *B, const Plan &p) {
+  if (!tok_ptr_ok(x, p, 16) || !tok_ptr_ok(B, p, 16)) return SSD_ERR_INVALID_ARG;
+  return SSD_OK;
+}
+
+ssd_status check_pass_args(const float *init, const float *fin, const Plan &p) {
+  const size_t sb = tensor_bytes(p).state;
+  if (init && !aligned(init, 16)) return SSD_ERR_INVALID_ARG;
+  if (fin && !aligned(fin, 16)) return SSD_ERR_INVALID_ARG;
+  if (init && fin && init != fin && overlaps(init, sb, fin, sb)) return SSD_ERR_INVALID_ARG;
+  return SSD_OK;
+}
+
+ssd_status check_scan_args(const void *x, const void *B, const void *C, const float *D, const void *y,
+                           const float *dt, const Plan &p) {
+  if (!tok_ptr_ok(x, p, 16) || !tok_ptr_ok(B, p, 16) || !tok_ptr_ok(C, p, 16) ||
+      !tok_ptr_ok(y, p, 16))
+    return SSD_ERR_INVALID_ARG;
+  if (D && !aligned(D, 4)) return SSD_ERR_INVALID_ARG;
+  const Sizes s = tensor_bytes(p);
+  if (overlaps(y, s.x, x, s.x) || overlaps(y, s.x, B, s.bc) || overlaps(y, s.x, C, s.bc) ||
+      overlaps(y, s.x, dt, s.dt))
+    return SSD_ERR_INVALID_ARG;
+  return SSD_OK;
+}
+
+ssd_status hip_status(hipError_t e) { return e == hipSuccess ? SSD_OK : SSD_ERR_HIP; }
+
+ssd_status run_cumsum(const float *dt, const float *A, const int32_t *cu, const Plan &p,
+                      void *ws, hipStream_t st) {
+  if (p.geo.packed) {
+    hipError_t e = ssd::launch_chunk_table(cu, p.geo, ws_ptr<int32_t>(ws, p.ws.chunk_table_offset),
+                                           ws_ptr<int32_t>(ws, p.ws.chunk_dir_offset), st);
+    if (e != hipSuccess) return SSD_ERR_HIP;
+  }
+  return hip_status(ssd::launch_chunk_cumsum(dt, A, p.geo, ws_ptr<float>(ws, p.ws.acum_offset),
+                                             ws_ptr<float>(ws, p.ws.dtq_offset), st));
+}
+
+ssd_status run_state(const void *x, const void *B, const Plan &p, void *ws, hipStream_t st) {
+  const float *acum = ws_ptr<float>(ws, p.ws.acum_offset);
+  const float *dtq = ws_ptr<float>(ws, p.ws.dtq_offset);
+  float *states = ws_ptr<float>(ws, p.ws.states_offset);
+  if (p.bf16)
+    return hip_status(ssd::launch_chunk_state_bf16(x, B, acum, dtq, states, p.geo, st));
+  return hip_status(ssd::launch_chunk_state_f32(static_cast<const float *>(x),
+                                                static_cast<const float *>(B), acum, dtq, states,
+                                                p.geo, st));
+}
+
+ssd_status run_pass(const float *init, float *fin, const Plan &p, void *ws, hipStream_t st) {
+  return hip_status(ssd::launch_state_passing(
+      ws_ptr<float>(ws, p.ws.states_offset), ws_ptr<void>(ws, p.ws.hprev_offset), p.bf16,
+      ws_ptr<float>(ws, p.ws.acum_offset), init, fin, p.geo, st));
+}
+
+ssd_status run_scan(const void *x, const void *B, const void *C, const float *D, void *y,
+                    const Plan &p, void *ws, hipStream_t st) {
+  const float *acum = ws_ptr<float>(ws, p.ws.acum_offset);
+  const float *dtq = ws_ptr<float>(ws, p.ws.dtq_offset);
+  const void *hprev = ws_ptr<void>(ws, p.ws.hprev_offset);
+  if (p.bf16)
+    return hip_status(ssd::launch_chunk_scan_bf16(x, B, C, D, acum, dtq, hprev, y, p.geo, st));
+  return hip_status(ssd::launch_chunk_scan_f32(
+      static_cast<const float *>(x), static_cast<const float *>(B), static_cast<const float *>(C),
+      D, acum, dtq, static_cast<const float *>(hprev), static_cast<float *>(y), p.geo, st));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_workspace_size(const ssd_dims *dims, int chunk_len) {
+  Plan p;
+  if (make_plan(dims, chunk_len, &p) != SSD_OK) return 0;
+  return p.ws.total_bytes;
+}
+
+ssd_status ssd_get_workspace_layout(const ssd_dims *dims, int chunk_len, ssd_workspace_layout *out) {
+  if (!out) return SSD_ERR_INVALID_ARG;
+  Plan p;
+  const ssd_status s = make_plan(dims, chunk_len, &p);
+  if (s != SSD_OK) return s;
+  *out = p.ws;
+  return SSD_OK;
+}
+
+ssd_status ssd_chunk_cumsum(const float *dt, const float *A, int chunk_len, const int32_t *cu_seqlens,
+                            const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                            void *stream) {
+  Plan p;
+  ssd_status s = make_plan(dims, chunk_len, &p);
+  if (s != SSD_OK) return s;
+  if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
+  if ((s = bind_workspace(&p, workspace, workspace_bytes)) != SSD_OK) return s;
+  return run_cumsum(dt, A, cu_seqlens, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+ssd_status ssd_chunk_state(const void *x, const void *B, int chunk_len, const ssd_dims *dims,
+                           void *workspace, size_t workspace_bytes, void *stream) {
+  Plan p;
+  ssd_status s = make_plan(dims, chunk_len, &p);
+  if (s != SSD_OK) return s;
+  if ((s = check_state_args(x, B, p)) != SSD_OK) return s;
+  if ((s = bind_workspace(&p, workspace, workspace_bytes)) != SSD_OK) return s;
+  return run_state(x, B, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+ssd_status ssd_state_passing(const float *init_state, float *final_state, int chunk_len,
+                             const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                             void *stream) {
+  Plan p;
+  ssd_status s = make_plan(dims, chunk_len, &p);
+  if (s != SSD_OK) return s;
+  if ((s = check_pass_args(init_state, final_state, p)) != SSD_OK) return s;
+  if ((s = bind_workspace(&p, workspace, workspace_bytes)) != SSD_OK) return s;
+  return run_pass(init_state, final_state, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const float *D, void *y,
+                          int chunk_len, const ssd_dims *dims, void *workspace,
+                          size_t workspace_bytes, void *stream) {
+  Plan p;
+  ssd_status s = make_plan(dims, chunk_len, &p);
+  if (s != SSD_OK) return s;
+  if ((s = check_scan_args(x, B, C, D, y, nullptr, p)) != SSD_OK) return s;
+  if ((s = bind_workspace(&p, workspace, workspace_bytes)) != SSD_OK) return s;
+  return run_scan(x, B, C, D, y, p, workspace, static_cast<hipStream_t>(stream));
+}
+
+ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, int chunk_len,
+                              const float *init_state, const int32_t *cu_seqlens, void *y,
+                              float *final_state, const ssd_dims *dims, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  Plan p;
+  ssd_status s = make_plan(dims, chunk_len, &p);
+  if (s != SSD_OK) return s;
+  if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
+  if ((s = check_state_args(x, B, p)) != SSD_OK) return s;
+  if ((s = check_pass_args(init_state, final_state, p)) != SSD_OK) return s;
+  if ((s = check_scan_args(x, B, C, D, y, dt, p)) != SSD_OK) return s;
+  if ((s = bind_workspace(&p, workspace, workspace_bytes)) != SSD_OK) return s;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = run_cumsum(dt, A, cu_seqlens, p, workspace, st)) != SSD_OK) return s;
+  if ((s = run_state(x, B, p, workspace, st)) != SSD_OK) return s;
+  if ((s = run_pass(init_state, final_state, p, workspace, st)) != SSD_OK) return s;
+  return run_scan(x, B, C, D, y, p, workspace, st);
+}
+
+const char *ssd_status_string(ssd_status status) {
+  switch (status) {
+    case SSD_OK: return "ok";
+    case SSD_ERR_INVALID_ARG: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported shape or chunk length";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP launch error";
+  }
+  return "unknown status";
+}
+
+int ssd_version(void) { return SSD_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,97 @@
+// Device-side helpers shared by the libssd kernels (gfx950 / CDNA4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// ----------------------------------------------------------------- chunk geometry
+// A chunk is at most Q consecutive tokens of one sequence.  Fixed-length
+// batches: row b has nc_row = ceil(L/Q) chunks, chunk c = b*nc_row + k starts
+// at token b*L + k*Q.  Packed batches: a table built on the device lists
+// (sequence, first token, length) per chunk; unused entries have length 0.
+struct ChunkGeom {
+  int64_t L;             // tokens per row (fixed length)
+  int32_t nc_row;        // chunks per row (fixed length)
+  int32_t Q;             // chunk length
+  const int32_t *table;  // packed: [nc_max][4]; nullptr for fixed length
+};
+
+struct ChunkInfo {
+  int seq;
+  int len;
+  int64_t t0;
+};
+
+__device__ __forceinline__ ChunkInfo chunk_info(const ChunkGeom &g, int c) {
+  ChunkInfo ci;
+  if (g.table) {
+    const int4 e = reinterpret_cast<const int4 *>(g.table)[c];
+    ci.seq = e.x;
+    ci.t0 = e.y;
+    ci.len = e.z;
+  } else {
+    const int b = c / g.nc_row;
+    const int k = c - b * g.nc_row;
+    ci.seq = b;
+    ci.t0 = (int64_t)b * g.L + (int64_t)k * g.Q;
+    const int64_t rem = g.L - (int64_t)k * g.Q;
+    ci.len = rem < g.Q ? (int)rem : g.Q;
+  }
+  return ci;
+}
+
+// ----------------------------------------------------------------- bf16 helpers
+__device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (lo in bits 0..15), round to nearest even
+// (gfx950 v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  bf16x2 v;
+  v.x = (__bf16)lo;
+  v.y = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+// Word holding element (lo of a, lo of b) or (hi of a, hi of b): byte selects
+// for v_perm_b32, which picks bytes of {a (bytes 4..7), b (bytes 0..3)}.
+__device__ __forceinline__ uint32_t pair_lo(uint32_t a, uint32_t b) {
+  // result = [b.lo16 (low half)?]  we want low half = a.lo, high half = b.lo
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pair_hi(uint32_t a, uint32_t b) {
+  // low half = a.hi, high half = b.hi
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+// ----------------------------------------------------------------- MFMA wrappers
+// v_mfma_f32_32x32x16_bf16: D(32x32) += A(32x16) * B(16x32), wave64.
+// Operand layout: lane i holds A[row i%32][k = 8*(i/32) .. +7] and
+// B[k = 8*(i/32) .. +7][col i%32].  Result: lane i, register r holds
+// D[row 8*(r/4) + 4*(i/32) + r%4][col i%32].
+__device__ __forceinline__ f32x16 mfma32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+// Row of result register r for the lane group g = lane/32 (32x32 tiles).
+__device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >> 2) + 4 * g + (r & 3); }
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+template <typename T>
+__device__ __forceinline__ T wave_bcast(T v, int src) { return __shfl(v, src, 64); }
+
+}  // namespace ssd

@@ -1,0 +1,47 @@
+// Host-side launchers of the libssd kernels (internal; the public ABI is ssd.h).
+// Every launcher only enqueues on `stream` and returns hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+struct Geometry {
+  int64_t tokens;   // T
+  int64_t L;        // tokens per row (fixed length)
+  int32_t nc_row;   // chunks per row (fixed length)
+  int32_t Q;        // chunk length
+  int64_t nc_max;   // chunks laid out in the workspace
+  int64_t nrows;    // sequences: batch (fixed) or nseq (packed)
+  int32_t H, P, N, G;
+  bool packed;
+  const int32_t *table;  // packed: chunk table in the workspace
+  const int32_t *dir;    // packed: chunk directory in the workspace
+};
+
+hipError_t launch_chunk_table(const int32_t *cu_seqlens, const Geometry &geo, int32_t *table,
+                              int32_t *dir, hipStream_t stream);
+hipError_t launch_chunk_cumsum(const float *dt, const float *A, const Geometry &geo, float *acum,
+                               float *dtq, hipStream_t stream);
+hipError_t launch_state_passing(const float *states, void *hprev, bool hprev_bf16,
+                                const float *acum, const float *init, float *final_state,
+                                const Geometry &geo, hipStream_t stream);
+// bf16 io, MFMA contractions
+bool chunk_state_bf16_supported(int P, int N, int Q);
+hipError_t launch_chunk_state_bf16(const void *x, const void *B, const float *acum,
+                                   const float *dtq, float *states, const Geometry &geo,
+                                   hipStream_t stream);
+bool chunk_scan_bf16_supported(int P, int N, int Q);
+hipError_t launch_chunk_scan_bf16(const void *x, const void *B, const void *C, const float *D,
+                                  const float *acum, const float *dtq, const void *hprev, void *y,
+                                  const Geometry &geo, hipStream_t stream);
+// fp32 io, fp32 vector-ALU contractions
+hipError_t launch_chunk_state_f32(const float *x, const float *B, const float *acum,
+                                  const float *dtq, float *states, const Geometry &geo,
+                                  hipStream_t stream);
+hipError_t launch_chunk_scan_f32(const float *x, const float *B, const float *C, const float *D,
+                                 const float *acum, const float *dtq, const float *hprev, float *y,
+                                 const Geometry &geo, hipStream_t stream);
+
+}  // namespace ssd

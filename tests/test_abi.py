@@ -1,0 +1,203 @@
+"""libssd C ABI on the host (no GPU): the library loads, exports every entry
+point declared in include/ssd.h, computes the documented workspace layout, and
+rejects bad arguments with the documented status before touching the GPU.
+
+Only invalid calls are made here, so nothing reaches a kernel launch.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+libssd = pytest.importorskip("mamba_ssd_layer_amd.libssd")
+from mamba_ssd_layer_amd.libssd import (SSD_BF16, SSD_ERR_INVALID_ARG, SSD_ERR_UNSUPPORTED,  # noqa: E402
+                                        SSD_ERR_WORKSPACE, SSD_F32, SSD_OK, make_dims)
+
+L = libssd.lib()
+FAKE = 0x7f0000000000  # aligned, never dereferenced: validation fails first
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert "ssd_chunk_scan_fwd" in names and len(names) >= 9
+    for n in names:
+        assert hasattr(L, n), f"libssd.so does not export {n}"
+    assert set(names) == set(libssd.EXPORTS)
+
+
+def test_version_and_status_strings():
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define SSD_VERSION (\d+)", text).group(1))
+    assert libssd.ssd_version() == ver
+    for s in range(5):
+        assert libssd.ssd_status_string(s)
+    assert libssd.ssd_status_string(SSD_OK) == "ok"
+    assert libssd.ssd_status_string(99) == "unknown status"
+
+
+def _ws_expected(batch, L_, H, P, N, G, Q, nseq=0, io=2):
+    al = lambda v: (v + 255) // 256 * 256
+    if nseq:
+        nc = math.ceil(L_ / Q) + nseq
+    else:
+        nc = batch * math.ceil(L_ / Q)
+    off = al(nc * H * Q * 4)
+    off = al(off + nc * H * Q * 4)
+    off = al(off + nc * H * P * N * 4)
+    off = al(off + nc * H * P * N * io)
+    if nseq:
+        off = al(off + nc * 16)
+        off = al(off + (nseq + 2) * 4)
+    return nc, max(off, 256)
+
+
+@pytest.mark.parametrize("case", [
+    (8, 4096, 80, 64, 128, 1, 256, 0, SSD_BF16),
+    (4, 2048, 24, 64, 128, 1, 256, 0, SSD_BF16),
+    (1, 65536, 80, 64, 256, 1, 256, 0, SSD_BF16),
+    (1, 275772, 64, 64, 128, 8, 256, 64, SSD_BF16),
+    (1, 256, 4, 16, 16, 1, 64, 0, SSD_F32),
+    (3, 1000, 2, 64, 64, 2, 128, 0, SSD_BF16),
+])
+def test_workspace_layout(case):
+    b, L_, H, P, N, G, Q, nseq, io = case
+    d = make_dims(b, L_, H, P, N, G, nseq, io)
+    lay = libssd.ssd_get_workspace_layout(d, Q)
+    nc, total = _ws_expected(b, L_, H, P, N, G, Q, nseq, 2 if io == SSD_BF16 else 4)
+    assert lay.nc_max == nc
+    assert lay.total_bytes == total == libssd.ssd_workspace_size(d, Q)
+    offs = [lay.acum_offset, lay.dtq_offset, lay.states_offset, lay.hprev_offset]
+    assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
+    if nseq:
+        assert lay.hprev_offset < lay.chunk_table_offset < lay.chunk_dir_offset < lay.total_bytes
+
+
+def test_varlen_chunk_bound_covers_every_split():
+    # sum over sequences of ceil(len/Q) never exceeds ceil(T/Q) + nseq
+    import numpy as np
+    r = np.random.default_rng(0)
+    for _ in range(200):
+        nseq = int(r.integers(1, 50))
+        lens = r.integers(0, 700, nseq)
+        Q = int(r.choice([64, 128, 256]))
+        T = int(lens.sum())
+        assert sum(math.ceil(l / Q) for l in lens) <= math.ceil(T / Q) + nseq
+
+
+def fwd(dims, Q=256, x=FAKE, dt=FAKE, A=FAKE, B=FAKE + (1 << 30), C=FAKE + (2 << 30), D=None,
+        init=None, cu=None, y=FAKE + (3 << 30), fin=None, ws=FAKE + (4 << 30), wsb=None):
+    if wsb is None:
+        wsb = L.ssd_workspace_size(ctypes.byref(dims), Q)
+    v = lambda a: None if a is None else ctypes.c_void_p(a)
+    return L.ssd_chunk_scan_fwd(v(x), v(dt), v(A), v(B), v(C), v(D), Q, v(init), v(cu), v(y),
+                                v(fin), ctypes.byref(dims), v(ws), wsb, None)
+
+
+def good():
+    return make_dims(2, 512, 4, 64, 64, 1, 0, SSD_BF16)
+
+
+@pytest.mark.parametrize("mut,expect", [
+    (dict(batch=0), SSD_ERR_INVALID_ARG),
+    (dict(seqlen=-1), SSD_ERR_INVALID_ARG),
+    (dict(nheads=0), SSD_ERR_INVALID_ARG),
+    (dict(ngroups=3), SSD_ERR_INVALID_ARG),          # 4 % 3 != 0
+    (dict(nseq=2), SSD_ERR_INVALID_ARG),             # packed needs batch == 1
+    (dict(io_dtype=7), SSD_ERR_INVALID_ARG),
+    (dict(reserved=1), SSD_ERR_INVALID_ARG),
+    (dict(headdim=32), SSD_ERR_UNSUPPORTED),          # bf16 path compiled for P = 64
+    (dict(headdim=72), SSD_ERR_UNSUPPORTED),          # not a multiple of 16
+    (dict(dstate=48), SSD_ERR_UNSUPPORTED),
+    (dict(dstate=512), SSD_ERR_UNSUPPORTED),
+    (dict(nheads=70000, ngroups=1), SSD_ERR_UNSUPPORTED),
+])
+def test_bad_dims(mut, expect):
+    d = good()
+    for k, v in mut.items():
+        setattr(d, k, v)
+    wsb = 1 << 40
+    assert fwd(d, wsb=wsb) == expect
+
+
+@pytest.mark.parametrize("Q,expect", [(32, SSD_ERR_UNSUPPORTED), (100, SSD_ERR_UNSUPPORTED),
+                                      (512, SSD_ERR_UNSUPPORTED), (0, SSD_ERR_INVALID_ARG),
+                                      (-64, SSD_ERR_INVALID_ARG)])
+def test_bad_chunk_len(Q, expect):
+    assert fwd(good(), Q=Q, wsb=1 << 40) == expect
+
+
+def test_null_and_misaligned_pointers():
+    d = good()
+    assert fwd(d, x=None) == SSD_ERR_INVALID_ARG
+    assert fwd(d, dt=None) == SSD_ERR_INVALID_ARG
+    assert fwd(d, A=None) == SSD_ERR_INVALID_ARG
+    assert fwd(d, B=None) == SSD_ERR_INVALID_ARG
+    assert fwd(d, C=None) == SSD_ERR_INVALID_ARG
+    assert fwd(d, y=None) == SSD_ERR_INVALID_ARG
+    assert fwd(d, x=FAKE + 8) == SSD_ERR_INVALID_ARG       # x needs 16-byte alignment
+    assert fwd(d, dt=FAKE + 2) == SSD_ERR_INVALID_ARG
+    assert fwd(d, init=FAKE + (5 << 30) + 4) == SSD_ERR_INVALID_ARG
+    assert fwd(d, ws=FAKE + (4 << 30) + 16) == SSD_ERR_INVALID_ARG  # workspace: 256 bytes
+
+
+def test_workspace_checks():
+    d = good()
+    need = L.ssd_workspace_size(ctypes.byref(d), 256)
+    assert need > 0
+    assert fwd(d, wsb=need - 1) == SSD_ERR_WORKSPACE
+    assert fwd(d, ws=None) == SSD_ERR_WORKSPACE
+
+
+def test_overlaps_rejected():
+    d = good()
+    xbytes = 2 * 512 * 4 * 64 * 2
+    assert fwd(d, y=FAKE) == SSD_ERR_INVALID_ARG                 # y == x
+    assert fwd(d, y=FAKE + xbytes - 16) == SSD_ERR_INVALID_ARG   # y tail overlaps x
+    sb = 2 * 4 * 64 * 64 * 4
+    base = FAKE + (6 << 30)
+    assert fwd(d, init=base, fin=base + 256) == SSD_ERR_INVALID_ARG   # partial overlap
+    # final_state == init_state is allowed; with a too-small workspace the call
+    # still stops before any launch, proving the aliasing check passed
+    assert fwd(d, init=base, fin=base, wsb=16) == SSD_ERR_WORKSPACE
+    assert fwd(d, init=base, fin=base + sb, wsb=16) == SSD_ERR_WORKSPACE
+
+
+def test_packed_needs_cu_seqlens():
+    d = make_dims(1, 1000, 4, 64, 64, 2, 3, SSD_BF16)
+    assert fwd(d, cu=None, wsb=1 << 40) == SSD_ERR_INVALID_ARG
+    assert fwd(d, cu=FAKE + (7 << 30), wsb=16) == SSD_ERR_WORKSPACE
+
+
+def test_per_stage_entry_points_validate():
+    d = good()
+    v = ctypes.c_void_p
+    dp = ctypes.byref(d)
+    assert L.ssd_chunk_cumsum(None, v(FAKE), 256, None, dp, v(FAKE), 1 << 40, None) == SSD_ERR_INVALID_ARG
+    assert L.ssd_chunk_state(v(FAKE), None, 256, dp, v(FAKE), 1 << 40, None) == SSD_ERR_INVALID_ARG
+    assert L.ssd_state_passing(v(FAKE + 4), None, 256, dp, v(FAKE), 1 << 40, None) == SSD_ERR_INVALID_ARG
+    assert L.ssd_chunk_scan(v(FAKE), v(FAKE), v(FAKE), None, v(FAKE), 256, dp, v(FAKE), 1 << 40,
+                            None) == SSD_ERR_INVALID_ARG   # y == x
+    assert L.ssd_chunk_scan(v(FAKE), v(FAKE), v(FAKE), None, v(FAKE + (3 << 30)), 256, dp,
+                            v(FAKE), 16, None) == SSD_ERR_WORKSPACE
+
+
+def test_layout_rejects_like_fwd():
+    d = good()
+    d.headdim = 48
+    with pytest.raises(libssd.SSDUnsupported):
+        libssd.ssd_get_workspace_layout(d, 256)
+    assert libssd.ssd_workspace_size(d, 256) == 0
+    d = good()
+    with pytest.raises(libssd.SSDUnsupported):
+        libssd.ssd_get_workspace_layout(d, 96)

@@ -1,0 +1,206 @@
+"""GPU parity of the whole forward (libssd through its C ABI) against the fp64
+CPU oracle, on the seeded workloads and on stress cases.
+
+Bound: max|y - y_ref| / max|y_ref| <= 1e-4 for fp32 inputs and <= 2e-2 for
+bf16 inputs (fp32 accumulation), the same for the final state.  Small problems
+compare every output; the full-size workloads compare sampled (sequence, head)
+pairs, which the oracle computes one by one, in the launch configuration the
+benchmark times.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_helpers import (TOL, check_full, check_sampled, plan_for, run, sample_pairs,  # noqa: E402
+                         say, upload, y_host)
+
+
+# ---------------------------------------------------------------- seeded workloads
+def test_tiny_f32_full():
+    w = workloads.make_workload("tiny_f32")
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin)
+
+
+def test_small_bf16_full():
+    w = workloads.make_workload("small_bf16")
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin)
+
+
+def test_large_bf16_sampled():
+    w = workloads.make_workload("large_bf16")
+    y, fin, _, _ = run(w)
+    check_sampled(w, y, fin, sample_pairs(w, 16))
+
+
+@pytest.mark.parametrize("name", ["long_n64", "long_n128", "long_n256"])
+def test_long_context_sampled(name):
+    w = workloads.make_workload(name)
+    y, fin, _, _ = run(w)
+    check_sampled(w, y, fin, sample_pairs(w, 6), head_tokens=8)
+
+
+def test_varlen_sampled():
+    w = workloads.make_workload("varlen_bf16")
+    say(f"  varlen: {w.nseq} sequences, {w.tokens} tokens")
+    y, fin, plan, _ = run(w)
+    d = plan.view("chunk_dir").cpu().numpy()
+    assert d[-1] == 0, "chunk directory error word set"
+    check_sampled(w, y, fin, sample_pairs(w, 12))
+
+
+# ---------------------------------------------------------------- page demo shapes
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_page_demo_shape(dtype):
+    # the chunked-kernel demo shape: batch 2, length 128, 4 heads, head dim 64,
+    # state 64; dt ~ 0.1 U[0,1), A = -1, B and C ~ N(0, 1)
+    w = workloads.make_custom(2, 128, 4, 64, 64, 1, 64, dtype, seed=11)
+    r = np.random.default_rng(12)
+    w.dt[:] = (0.1 * r.random(w.dt.shape)).astype(np.float32)
+    w.A[:] = -1.0
+    w.B[:] = r.standard_normal(w.B.shape).astype(np.float32)
+    w.C[:] = r.standard_normal(w.C.shape).astype(np.float32)
+    if dtype == "bf16":
+        workloads.bf16_round_(w.B)
+        workloads.bf16_round_(w.C)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin)
+
+
+# ---------------------------------------------------------------- stress cases
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+def test_ragged_tail_and_chunk_lengths(dtype, chunk):
+    # L % Q != 0 and several rows: the last chunk of every row is partial
+    N = 64 if dtype == "bf16" else 32
+    P = 64 if dtype == "bf16" else 16
+    w = workloads.make_custom(3, 1000, 4, P, N, 2, chunk, dtype, seed=100 + chunk, init_std=0.2)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label=f"{dtype} Q{chunk}")
+
+
+@pytest.mark.parametrize("N", [64, 128, 256])
+def test_state_sizes(N):
+    w = workloads.make_custom(2, 700, 8, 64, N, 2, 256, "bf16", seed=200 + N)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label=f"N{N}")
+
+
+@pytest.mark.parametrize("G", [1, 2, 8])
+def test_groups(G):
+    w = workloads.make_custom(2, 600, 8, 64, 64, G, 128, "bf16", seed=300 + G)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label=f"G{G}")
+
+
+@pytest.mark.parametrize("kind", ["A_zero", "A_tiny", "dt_small"])
+def test_long_memory(kind):
+    # slow or no decay: the state handed between chunks dominates the output,
+    # so a hand-off bug cannot hide under the bound
+    kw = {}
+    if kind == "A_zero":
+        kw = dict(a_zero=True)
+    elif kind == "A_tiny":
+        kw = dict(a_log_range=(np.log(1e-4), np.log(1e-2)))
+    else:
+        kw = dict(dt_const=1e-3)
+    w = workloads.make_custom(2, 1500, 4, 64, 128, 1, 256, "bf16", seed=400, init_std=0.5, **kw)
+    y, fin, _, _ = run(w)
+    _, _, y_ref, _ = check_full(w, y, fin, label=kind)
+    # first 8 tokens of each chunk
+    yg = y_host(y, w)
+    idx = np.arange(w.seqlen)
+    sel = np.tile((idx % w.chunk) < 8, w.batch)
+    e = np.max(np.abs(yg[sel] - y_ref[sel])) / np.max(np.abs(y_ref[sel]))
+    say(f"    first 8 tokens of each chunk: rel err {e:.3e}")
+    assert e <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_varlen_edge_lengths(dtype):
+    # length-1 sequences, empty sequences, exact multiples of the chunk, and a
+    # long one; nonzero initial states
+    lens = [1, 0, 256, 1, 700, 0, 255, 257, 3, 1024, 1]
+    P, N = (64, 64) if dtype == "bf16" else (16, 32)
+    w = workloads.make_custom(1, 0, 4, P, N, 2, 256, dtype, seed=500, lens=lens, init_std=0.3)
+    y, fin, plan, _ = run(w)
+    check_full(w, y, fin, label=f"varlen edges {dtype}")
+    # empty sequences keep their initial state exactly
+    f = fin.cpu().numpy()
+    for s, L in enumerate(lens):
+        if L == 0:
+            assert np.array_equal(f[s], w.h0[s])
+    tab = plan.view("chunk_table").cpu().numpy()
+    d = plan.view("chunk_dir").cpu().numpy()
+    # chunk table: exact integers
+    exp = []
+    so = w.seq_off
+    for s, L in enumerate(lens):
+        for k in range(0, L, 256):
+            exp.append((s, so[s] + k, min(256, L - k), 0))
+    exp = np.array(exp, np.int32)
+    assert d[len(lens)] == len(exp) and d[-1] == 0
+    assert np.array_equal(tab[:len(exp)], exp)
+    assert np.all(tab[len(exp):, 2] == 0)
+
+
+def test_empty_input_returns_init_state():
+    w = workloads.make_custom(2, 0, 4, 64, 64, 1, 256, "bf16", seed=600, init_std=0.5)
+    t = upload(w)
+    plan = plan_for(w, t)
+    y, fin = plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], None)
+    torch.cuda.synchronize()
+    assert y.numel() == 0
+    assert torch.equal(fin, t["h0"])
+
+
+def test_final_state_may_alias_init_state():
+    w = workloads.make_custom(2, 777, 4, 64, 64, 2, 128, "bf16", seed=700, init_std=0.5)
+    t = upload(w)
+    plan = plan_for(w, t)
+    st = t["h0"].clone()
+    y, fin = plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], st, None, final_state=st)
+    torch.cuda.synchronize()
+    assert fin.data_ptr() == st.data_ptr()
+    check_full(w, y, fin, label="aliased state")
+
+
+def test_no_D_no_init():
+    w = workloads.make_custom(2, 500, 4, 64, 128, 1, 256, "bf16", seed=800, with_D=False)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label="D=None")
+
+
+def test_split_streaming_matches_one_call():
+    # two calls, the second starting from the first one's final state, equal one call
+    w = workloads.make_custom(1, 1024, 4, 64, 64, 1, 256, "bf16", seed=900)
+    y, fin, _, t = run(w)
+    L1 = 384
+    w1 = workloads.make_custom(1, L1, 4, 64, 64, 1, 256, "bf16", seed=900)
+    for k in ("x", "dt", "B", "C"):
+        getattr(w1, k)[:] = getattr(w, k)[:L1]
+    w1.A[:] = w.A
+    w1.D[:] = w.D
+    y1, f1, _, _ = run(w1)
+    w2 = workloads.make_custom(1, 1024 - L1, 4, 64, 64, 1, 256, "bf16", seed=901)
+    for k in ("x", "dt", "B", "C"):
+        getattr(w2, k)[:] = getattr(w, k)[L1:]
+    w2.A[:] = w.A
+    w2.D[:] = w.D
+    t2 = upload(w2)
+    plan2 = plan_for(w2, t2)
+    y2, f2 = plan2(t2["x"], t2["dt"], t2["A"], t2["B"], t2["C"], t2["D"], f1, None)
+    torch.cuda.synchronize()
+    ycat = torch.cat([y1, y2], dim=1).float()
+    e = (ycat - y.float()).abs().max().item() / y.float().abs().max().item()
+    ef = (f2 - fin).abs().max().item() / fin.abs().max().item()
+    say(f"  split at {L1}: y rel diff {e:.3e}, final rel diff {ef:.3e}")
+    assert e <= 1e-2 and ef <= 1e-2

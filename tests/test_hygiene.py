@@ -1,0 +1,81 @@
+"""GPU hygiene of the forward: bitwise determinism across runs (an LDS race
+would show up as run-to-run differences), no reads of uninitialised workspace
+(a NaN-filled workspace gives bit-identical outputs), and no writes outside y
+and final_state (guard bands around them stay intact)."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from gpu_helpers import plan_for, say, upload  # noqa: E402
+
+
+@pytest.fixture(scope="module")
+def case():
+    w = workloads.make_custom(3, 1100, 8, 64, 128, 2, 256, "bf16", seed=42, init_std=0.2)
+    t = upload(w)
+    return w, t
+
+
+def test_bitwise_deterministic(case):
+    w, t = case
+    plan = plan_for(w, t)
+    outs = []
+    for _ in range(3):
+        y, fin = plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], None)
+        torch.cuda.synchronize()
+        outs.append((y.clone(), fin.clone()))
+    for y, f in outs[1:]:
+        assert torch.equal(y, outs[0][0]) and torch.equal(f, outs[0][1])
+
+
+def test_nan_workspace_gives_same_result(case):
+    w, t = case
+    plan = plan_for(w, t)
+    y0, f0 = plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], None)
+    torch.cuda.synchronize()
+    y0, f0 = y0.clone(), f0.clone()
+    plan.workspace.view(torch.uint8).fill_(0xFF)  # every float in it is NaN
+    y1, f1 = plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], None)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
+
+
+def test_guard_bands_intact(case):
+    w, t = case
+    plan = plan_for(w, t)
+    G = 4096  # guard elements on each side
+    ybuf = torch.full((t["x"].numel() + 2 * G,), 1234.0, dtype=torch.bfloat16, device=t["x"].device)
+    fbuf = torch.full((t["h0"].numel() + 2 * G,), -777.0, dtype=torch.float32, device=t["x"].device)
+    y = ybuf[G:G + t["x"].numel()].view_as(t["x"])
+    fin = fbuf[G:G + t["h0"].numel()].view_as(t["h0"])
+    plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], None, y=y, final_state=fin)
+    torch.cuda.synchronize()
+    for buf, val in ((ybuf, 1234.0), (fbuf, -777.0)):
+        assert torch.all(buf[:G].float() == val) and torch.all(buf[-G:].float() == val)
+    assert torch.isfinite(y.float()).all() and torch.isfinite(fin).all()
+    say("  guard bands intact")
+
+
+def test_streams_are_independent(case):
+    # two plans with separate workspaces on two streams give the single-stream result
+    w, t = case
+    p1, p2 = plan_for(w, t), plan_for(w, t)
+    ref, fref = p1(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], None)
+    torch.cuda.synchronize()
+    ref, fref = ref.clone(), fref.clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(s1):
+        ya, fa = p1(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], None)
+    with torch.cuda.stream(s2):
+        yb, fb = p2(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], None)
+    torch.cuda.synchronize()
+    for y, f in ((ya, fa), (yb, fb)):
+        assert torch.equal(y, ref) and torch.equal(f, fref)
