@@ -11,20 +11,38 @@
 // Algorithm", item 1); the second is the inter-chunk hand-off of item 2, with
 // the in-chunk decay exp(acum_l) that the page's listing leaves out.
 //
-// Design (per block = (chunk, head), Q/64 wavefronts).  The output is formed
-// transposed, Y^T [P x Q], as 32x32 MFMA tiles (M = p, N = l):
-//   * wavefront w owns the token tiles w and Q/32-1-w (balanced causal work);
-//   * for its token tile it keeps the C rows as MFMA B-operands in registers;
-//   * inter term: Y^T += Hprev . C^T over K = n (Hprev read as bf16 A-operands),
-//     then each lane scales by exp(acum_l) -- one factor per lane because a lane
-//     owns one output column l;
-//   * intra term, for every source tile s <= l: Z = B_s . C^T over K = n on MFMA,
-//     then the decay mask is applied to Z in registers (masking before the exp
-//     argument can overflow), the fp32 accumulator is rounded to bf16 and used
-//     directly as the B-operand of Y^T += X^T . G^T: the K-order of that MFMA
-//     is permuted to the accumulator's row order, and X^T is read from LDS in
-//     the same order, so no cross-lane shuffle is needed;
-//   * X^T for the whole chunk is staged once in LDS (transposed on the way in).
+// Shared design (block = (chunk, head), Q/64 wavefronts, XCD-aware order).
+// The output is formed transposed, Y^T [P x Q], as 32x32 MFMA tiles
+// (M = p, N = l), the chunk cut into Q/32 token tiles:
+//   * wavefront w owns the token tiles w and Q/32-1-w (balanced causal work)
+//     and keeps their C rows as MFMA B-operands in registers;
+//   * inter term: Y^T += Hprev . C^T over K = n, then each lane scales by
+//     exp(acum_l) -- a lane owns one output column l;
+//   * intra term, per source tile k <= j: Z = B_k . C_j^T on MFMA, the decay
+//     mask applied to Z in registers, the fp32 accumulator rounded to bf16 and
+//     used directly as the B-operand of Y^T += X_k^T . G^T: that MFMA's K order
+//     is permuted to the accumulator's row order and X^T is read from LDS in the
+//     same order, so no cross-lane shuffle is needed;
+//   * decay: off the diagonal (k < j) exp(acum_l - acum_s) is split at
+//     m = acum at the token tile's first token into u_l = exp(acum_l - m) (one
+//     per lane) and v_s = exp(m - acum_s) dt_s (a per-chunk table in LDS); both
+//     are <= 1 for non-increasing acum, so nothing overflows.  Diagonal tiles
+//     take exp(acum_l - acum_s) per element, masked to s <= l before the
+//     exponent is formed.
+//
+// k_chunk_scan_lds (N <= 128): MFMA operands come from LDS, filled with
+// coalesced loads, instead of one cache line per lane.  At the start the block
+// stages X^T of the whole chunk (transposed on the way in) and hprev, so the
+// HBM reads are in flight together; then it walks the source tiles in
+// lockstep with B tiles (L2-resident, shared by the heads of a group)
+// double-buffered one tile ahead; when a wavefront has both its token tiles
+// in play, their MFMA chains share the B and X operand reads.  Only when the
+// loop is done do the outputs leave, through per-wavefront LDS staging, as
+// full 16-byte row segments with D x_l added in fp32 -- so no store is in
+// flight while the loop waits on its tile loads.
+// k_chunk_scan_regs (N = 256, whose C operands of two token tiles would not fit
+// in registers): one token tile at a time, X^T for the whole chunk in LDS,
+// B operands read straight from global memory.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -32,12 +50,365 @@ namespace ssd {
 
 namespace {
 
+template <int KN>
+__device__ __forceinline__ void load_rows(u32x4 (&dst)[KN], const uint16_t *row, bool valid) {
+#pragma unroll
+  for (int q = 0; q < KN; ++q)
+    dst[q] = valid ? *reinterpret_cast<const u32x4 *>(row + q * 16) : u32x4{0u, 0u, 0u, 0u};
+}
+
+// Off-diagonal decay: g = z * u_l * v[s] for the lane's 16 accumulator rows.
+__device__ __forceinline__ void decay_offdiag(const f32x16 &z, float ul, const float *vrow, int kg,
+                                              float (&gv)[16]) {
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(vrow + 8 * rb + 4 * kg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gv[rb * 4 + e] = z[rb * 4 + e] * (ul * v[e]);
+  }
+}
+
+// Diagonal decay: g = z * exp(acum_l - acum_s) * dt_s for s <= l, else 0.  The
+// lane's 16 rows are 4 runs of 4 consecutive s, read as 16-byte vectors; the
+// mask is applied to the exponent's argument before exp is taken.
+__device__ __forceinline__ void decay_diag(const f32x16 &z, float al, int l, int s0, int kg,
+                                           const float *sa, const float *sd, float (&gv)[16]) {
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const int sb = s0 + 8 * rb + 4 * kg;
+    const f32x4 a = *reinterpret_cast<const f32x4 *>(sa + sb);
+    const f32x4 d = *reinterpret_cast<const f32x4 *>(sd + sb);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const bool keep = sb + e <= l;
+      const float arg = keep ? (al - a[e]) : -__builtin_inff();
+      gv[rb * 4 + e] = keep ? z[rb * 4 + e] * __expf(arg) * d[e] : 0.f;
+    }
+  }
+}
+
+__device__ __forceinline__ void pack_g(const float (&gv)[16], u32x4 &g0, u32x4 &g1) {
+  g0.x = pack_bf16x2(gv[0], gv[1]);
+  g0.y = pack_bf16x2(gv[2], gv[3]);
+  g0.z = pack_bf16x2(gv[4], gv[5]);
+  g0.w = pack_bf16x2(gv[6], gv[7]);
+  g1.x = pack_bf16x2(gv[8], gv[9]);
+  g1.y = pack_bf16x2(gv[10], gv[11]);
+  g1.z = pack_bf16x2(gv[12], gv[13]);
+  g1.w = pack_bf16x2(gv[14], gv[15]);
+}
+
+// Y^T += X^T . G^T for one source tile: X^T rows p = 32t + col, read in the K
+// order of the accumulator rows (offsets {4kg..4kg+3, 8+4kg..}, then +16).
+template <int TP>
+__device__ __forceinline__ void mfma_xg(f32x16 (&acc)[TP], const uint16_t *xrow0, int ld,
+                                        const u32x4 &g0, const u32x4 &g1) {
+#pragma unroll
+  for (int t = 0; t < TP; ++t) {
+    const uint16_t *xr = xrow0 + t * 32 * ld;
+    const u32x2 a0 = *reinterpret_cast<const u32x2 *>(xr);
+    const u32x2 a1 = *reinterpret_cast<const u32x2 *>(xr + 8);
+    const u32x2 b0 = *reinterpret_cast<const u32x2 *>(xr + 16);
+    const u32x2 b1 = *reinterpret_cast<const u32x2 *>(xr + 24);
+    const u32x4 xa{a0.x, a0.y, a1.x, a1.y};
+    const u32x4 xb{b0.x, b0.y, b1.x, b1.y};
+    acc[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g0), acc[t]);
+    acc[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g1), acc[t]);
+  }
+}
+
+// ============================================================ LDS-staged kernel
 template <int Q, int P, int N>
-__global__ __launch_bounds__(Q) void k_chunk_scan_bf16(
+__global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
     const uint16_t *__restrict__ Cm, const float *__restrict__ Dv, const float *__restrict__ acum,
-    const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int H,
-    int G, uint16_t *__restrict__ y) {
+    const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int nc,
+    int H, int G, uint16_t *__restrict__ y) {
+  static_assert(P % 32 == 0 && N % 16 == 0 && Q % 64 == 0, "tile shape");
+  static_assert(P <= 64, "hprev is staged in the two B tiles (64 rows)");
+  constexpr int NT = Q;          // threads
+  constexpr int NW = Q / 64;     // wavefronts
+  constexpr int NLT = Q / 32;    // token tiles
+  constexpr int TP = P / 32;     // p tiles
+  constexpr int KN = N / 16;     // K steps over n
+  constexpr int LDX = Q + 4;     // X^T row: Q tokens (bf16) + pad
+  constexpr int LBT = N + 8;     // B / hprev row (bf16) + pad
+  constexpr int LYB = P + 4;     // output staging row (fp32) + pad
+  constexpr int BV = 32 * N / 8;              // 16-byte vectors per B tile
+  constexpr int BPT = (BV + NT - 1) / NT;
+  constexpr int XT_BYTES = P * LDX * 2;
+  constexpr int BS_BYTES = 2 * 32 * LBT * 2;
+  constexpr int YB_BYTES = NW * 32 * LYB * 4;
+  constexpr int SMEM = XT_BYTES + BS_BYTES > YB_BYTES ? XT_BYTES + BS_BYTES : YB_BYTES;
+
+  // X^T of the chunk and two B stages during the loop; per-wave output
+  // staging buffers in the same bytes afterwards
+  __shared__ __align__(16) unsigned char smem[SMEM];
+  __shared__ __align__(16) float sa[Q];
+  __shared__ __align__(16) float sd[Q];
+  __shared__ __align__(16) float vt[NLT][Q];  // vt[j][s] = exp(acum[32j] - acum[s]) dt[s], s < 32j
+  uint16_t(*xt)[LDX] = reinterpret_cast<uint16_t(*)[LDX]>(smem);
+  uint16_t(*bs)[32][LBT] = reinterpret_cast<uint16_t(*)[32][LBT]>(smem + XT_BYTES);
+  uint16_t(*hs)[LBT] = reinterpret_cast<uint16_t(*)[LBT]>(smem + XT_BYTES);  // hprev [P][LBT]
+
+  int c, h;
+  xcd_chunk_head(H, c, h);
+  if (c >= nc) return;
+  const int g = h / (H / G);
+  const ChunkInfo ci = chunk_info(geom, c);
+  if (ci.len <= 0) return;
+  const int64_t ch = (int64_t)c * H + h;
+  const int nk = (ci.len + 31) >> 5;  // token tiles that hold tokens
+  const int64_t ldx = (int64_t)H * P;
+  const int64_t ldb = (int64_t)G * N;
+  const uint16_t *xbase = x + ci.t0 * ldx + (int64_t)h * P;
+  const uint16_t *bbase = Bm + ci.t0 * ldb + (int64_t)g * N;
+  const uint16_t *cbase = Cm + ci.t0 * ldb + (int64_t)g * N;
+  const int tid = threadIdx.x;
+
+  // ---- stage acum, dt, X^T of the whole chunk and hprev
+  for (int l = tid; l < Q; l += NT) {
+    sa[l] = acum[ch * Q + l];
+    sd[l] = dtq[ch * Q + l];
+  }
+  {
+    constexpr int RQ = Q / 4;
+    constexpr int UNITS = RQ * (P / 8);
+    for (int u = tid; u < UNITS; u += NT) {
+      const int rq = u % RQ;  // 4 token rows x 8 columns per unit, row quad fastest
+      const int cb = u / RQ;
+      const int l0 = rq * 4;
+      u32x4 r[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        r[i] = l0 + i < ci.len
+                   ? *reinterpret_cast<const u32x4 *>(xbase + (int64_t)(l0 + i) * ldx + cb * 8)
+                   : u32x4{0u, 0u, 0u, 0u};
+      }
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        u32x2 lo, hi;
+        lo.x = pair_lo(r[0][m], r[1][m]);
+        lo.y = pair_lo(r[2][m], r[3][m]);
+        hi.x = pair_hi(r[0][m], r[1][m]);
+        hi.y = pair_hi(r[2][m], r[3][m]);
+        *reinterpret_cast<u32x2 *>(&xt[cb * 8 + 2 * m][l0]) = lo;
+        *reinterpret_cast<u32x2 *>(&xt[cb * 8 + 2 * m + 1][l0]) = hi;
+      }
+    }
+    const uint16_t *hp = hprev + ch * (int64_t)P * N;
+    for (int v = tid; v < P * N / 8; v += NT) {
+      const int row = v / (N / 8);
+      const int cv = v - row * (N / 8);
+      *reinterpret_cast<u32x4 *>(&hs[row][cv * 8]) =
+          *reinterpret_cast<const u32x4 *>(hp + (int64_t)row * N + cv * 8);
+    }
+  }
+
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int lane = tid & 63;
+  const int col = lane & 31;
+  const int kg = lane >> 5;
+  const int j1 = wave;
+  const int j2 = NLT - 1 - wave;  // > j1
+  const int l1 = j1 * 32 + col;
+  const int l2 = j2 * 32 + col;
+  const bool act1 = j1 < nk;
+  const bool act2 = j2 < nk;
+
+  u32x4 c1[KN], c2[KN];
+  load_rows<KN>(c1, cbase + (int64_t)l1 * ldb + kg * 8, l1 < ci.len);
+  load_rows<KN>(c2, cbase + (int64_t)l2 * ldb + kg * 8, l2 < ci.len);
+  __syncthreads();  // sa, sd, X^T, hprev staged
+
+  for (int idx = tid; idx < NLT * Q; idx += NT) {
+    const int j = idx / Q;
+    const int s = idx - j * Q;
+    if (s < 32 * j) vt[j][s] = __expf(sa[32 * j] - sa[s]) * sd[s];
+  }
+  f32x16 acc1[TP], acc2[TP];
+#pragma unroll
+  for (int t = 0; t < TP; ++t) {
+    acc1[t] = f32x16{};
+    acc2[t] = f32x16{};
+  }
+  // ---- inter-chunk term for both token tiles (shared hprev operands)
+#pragma unroll
+  for (int t = 0; t < TP; ++t) {
+#pragma unroll
+    for (int q = 0; q < KN; ++q) {
+      const u32x4 a = *reinterpret_cast<const u32x4 *>(&hs[t * 32 + col][q * 16 + kg * 8]);
+      acc1[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(c1[q]), acc1[t]);
+      acc2[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(c2[q]), acc2[t]);
+    }
+  }
+  const float al1 = sa[l1], al2 = sa[l2];
+  {
+    const float e1 = __expf(al1), e2 = __expf(al2);
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      acc1[t] *= e1;
+      acc2[t] *= e2;
+    }
+  }
+  const float u1 = __expf(al1 - sa[32 * j1]);
+  const float u2 = __expf(al2 - sa[32 * j2]);
+
+  // B source tiles: global (L2) -> registers -> LDS stage, coalesced rows
+  u32x4 breg[BPT];
+  auto load_tile = [&](int k) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int v = tid + i * NT;
+      const int row = v / (N / 8);
+      const int cv = v - row * (N / 8);
+      const int s = 32 * k + row;
+      breg[i] = (v < BV && s < ci.len)
+                    ? *reinterpret_cast<const u32x4 *>(bbase + (int64_t)s * ldb + cv * 8)
+                    : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto store_tile = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < BPT; ++i) {
+      const int v = tid + i * NT;
+      if (v < BV) {
+        const int row = v / (N / 8);
+        const int cv = v - row * (N / 8);
+        *reinterpret_cast<u32x4 *>(&bs[buf][row][cv * 8]) = breg[i];
+      }
+    }
+  };
+  load_tile(0);
+  __syncthreads();  // hprev consumed, vt complete
+  store_tile(0);
+  if (nk > 1) load_tile(1);
+  __syncthreads();  // B tile 0 staged
+
+  // source tile k for one token tile (j, l) held in (acc, creg)
+  auto step_one = [&](f32x16 (&acc)[TP], const u32x4 (&creg)[KN], int j, int l, float al, float u,
+                      int k, int buf) {
+    f32x16 z = f32x16{};
+#pragma unroll
+    for (int q = 0; q < KN; ++q) {
+      const u32x4 b = *reinterpret_cast<const u32x4 *>(&bs[buf][col][q * 16 + kg * 8]);
+      z = mfma32x32x16(as_bf16x8(b), as_bf16x8(creg[q]), z);
+    }
+    float gv[16];
+    if (k < j) {
+      decay_offdiag(z, u, &vt[j][32 * k], kg, gv);
+    } else {
+      decay_diag(z, al, l, 32 * k, kg, sa, sd, gv);
+    }
+    u32x4 g0, g1;
+    pack_g(gv, g0, g1);
+    mfma_xg<TP>(acc, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
+  };
+  // source tile k for both token tiles (k <= j1 < j2): the B and X operand
+  // reads are shared, and the two MFMA chains interleave
+  auto step_two = [&](int k, int buf) {
+    f32x16 z1 = f32x16{}, z2 = f32x16{};
+#pragma unroll
+    for (int q = 0; q < KN; ++q) {
+      const u32x4 b = *reinterpret_cast<const u32x4 *>(&bs[buf][col][q * 16 + kg * 8]);
+      z1 = mfma32x32x16(as_bf16x8(b), as_bf16x8(c1[q]), z1);
+      z2 = mfma32x32x16(as_bf16x8(b), as_bf16x8(c2[q]), z2);
+    }
+    float gv1[16], gv2[16];
+    if (k < j1) {
+      decay_offdiag(z1, u1, &vt[j1][32 * k], kg, gv1);
+    } else {
+      decay_diag(z1, al1, l1, 32 * k, kg, sa, sd, gv1);
+    }
+    decay_offdiag(z2, u2, &vt[j2][32 * k], kg, gv2);
+    u32x4 g10, g11, g20, g21;
+    pack_g(gv1, g10, g11);
+    pack_g(gv2, g20, g21);
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      const uint16_t *xr = &xt[t * 32 + col][32 * k + 4 * kg];
+      const u32x2 a0 = *reinterpret_cast<const u32x2 *>(xr);
+      const u32x2 a1 = *reinterpret_cast<const u32x2 *>(xr + 8);
+      const u32x2 b0 = *reinterpret_cast<const u32x2 *>(xr + 16);
+      const u32x2 b1 = *reinterpret_cast<const u32x2 *>(xr + 24);
+      const u32x4 xa{a0.x, a0.y, a1.x, a1.y};
+      const u32x4 xb{b0.x, b0.y, b1.x, b1.y};
+      acc1[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g10), acc1[t]);
+      acc2[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g20), acc2[t]);
+      acc1[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g11), acc1[t]);
+      acc2[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g21), acc2[t]);
+    }
+  };
+
+  // ---- intra-chunk term: all source tiles in lockstep
+#pragma unroll 1
+  for (int k = 0; k < nk; ++k) {
+    const int buf = k & 1;
+    if (act2) {
+      if (k <= j1) {
+        step_two(k, buf);
+      } else if (k <= j2) {
+        step_one(acc2, c2, j2, l2, al2, u2, k, buf);
+      }
+    } else if (act1 && k <= j1) {
+      step_one(acc1, c1, j1, l1, al1, u1, k, buf);
+    }
+    if (k + 1 < nk) {
+      store_tile(buf ^ 1);  // tile k+1, loaded one step earlier
+      if (k + 2 < nk) load_tile(k + 2);
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue: each wave stages its token tiles through its own LDS slice
+  // as fp32 [token][p], adds D x in fp32, rounds, and stores 16-byte row segments
+  const float Dh = Dv ? Dv[h] : 0.f;
+  float(*yb)[LYB] = reinterpret_cast<float(*)[LYB]>(smem + wave * 32 * LYB * 4);
+  auto epilogue = [&](const f32x16 (&acc)[TP], int j) {
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const f32x4 v{acc[t][rb * 4 + 0], acc[t][rb * 4 + 1], acc[t][rb * 4 + 2], acc[t][rb * 4 + 3]};
+        *reinterpret_cast<f32x4 *>(&yb[col][t * 32 + rb * 8 + kg * 4]) = v;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    constexpr int G8 = P / 8;
+#pragma unroll
+    for (int it = lane; it < 32 * G8; it += 64) {
+      const int r = it / G8;
+      const int gp = it - r * G8;
+      const int l = j * 32 + r;
+      if (l < ci.len) {
+        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&yb[r][gp * 8]);
+        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&yb[r][gp * 8 + 4]);
+        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xbase + (int64_t)l * ldx + gp * 8);
+        u32x4 o;
+        o.x = pack_bf16x2(v0.x + Dh * bf16lo(xv.x), v0.y + Dh * bf16hi(xv.x));
+        o.y = pack_bf16x2(v0.z + Dh * bf16lo(xv.y), v0.w + Dh * bf16hi(xv.y));
+        o.z = pack_bf16x2(v1.x + Dh * bf16lo(xv.z), v1.y + Dh * bf16hi(xv.z));
+        o.w = pack_bf16x2(v1.z + Dh * bf16lo(xv.w), v1.w + Dh * bf16hi(xv.w));
+        *reinterpret_cast<u32x4 *>(y + (ci.t0 + l) * ldx + (int64_t)h * P + gp * 8) = o;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  if (act1) epilogue(acc1, j1);
+  if (act2) epilogue(acc2, j2);
+}
+
+// ============================================================ register-resident kernel
+template <int Q, int P, int N>
+__global__ __launch_bounds__(Q) void k_chunk_scan_regs(
+    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
+    const uint16_t *__restrict__ Cm, const float *__restrict__ Dv, const float *__restrict__ acum,
+    const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int nc,
+    int H, int G, uint16_t *__restrict__ y) {
   static_assert(P % 32 == 0 && N % 16 == 0 && Q % 64 == 0, "tile shape");
   constexpr int NT = Q;          // threads
   constexpr int NLT = Q / 32;    // token tiles
@@ -46,17 +417,18 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_bf16(
   constexpr int LDX = Q + 4;     // padded LDS row of X^T (bf16 elements)
 
   __shared__ __align__(16) uint16_t xt[P][LDX];
-  __shared__ float sa[Q];
-  __shared__ float sd[Q];
+  __shared__ __align__(16) float sa[Q];
+  __shared__ __align__(16) float sd[Q];
+  __shared__ __align__(16) float vt[NLT][Q];
 
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
+  int c, h;
+  xcd_chunk_head(H, c, h);
+  if (c >= nc) return;
   const int g = h / (H / G);
   const ChunkInfo ci = chunk_info(geom, c);
   if (ci.len <= 0) return;
   const int64_t ch = (int64_t)c * H + h;
 
-  // ---- stage acum, dt and X^T
   for (int l = threadIdx.x; l < Q; l += NT) {
     sa[l] = acum[ch * Q + l];
     sd[l] = dtq[ch * Q + l];
@@ -73,11 +445,9 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_bf16(
       u32x4 r[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        if (l0 + i < ci.len) {
-          r[i] = *reinterpret_cast<const u32x4 *>(xbase + (int64_t)(l0 + i) * ldx + cb * 8);
-        } else {
-          r[i] = u32x4{0u, 0u, 0u, 0u};
-        }
+        r[i] = l0 + i < ci.len
+                   ? *reinterpret_cast<const u32x4 *>(xbase + (int64_t)(l0 + i) * ldx + cb * 8)
+                   : u32x4{0u, 0u, 0u, 0u};
       }
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -92,6 +462,12 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_bf16(
     }
   }
   __syncthreads();
+  for (int idx = threadIdx.x; idx < NLT * Q; idx += NT) {
+    const int j = idx / Q;
+    const int s = idx - j * Q;
+    if (s < 32 * j) vt[j][s] = __expf(sa[32 * j] - sa[s]) * sd[s];
+  }
+  __syncthreads();
 
   const int wave = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
@@ -100,8 +476,8 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_bf16(
   const float Dh = Dv ? Dv[h] : 0.f;
   const uint16_t *hp = hprev + ch * (int64_t)P * N;
   const int64_t ldb = (int64_t)G * N;
-  const uint16_t *bbase = Bm + ci.t0 * ldb + (int64_t)g * N;
-  const uint16_t *cbase = Cm + ci.t0 * ldb + (int64_t)g * N;
+  const uint16_t *bbase = Bm + ci.t0 * ldb + (int64_t)g * N + kg * 8;
+  const uint16_t *cbase = Cm + ci.t0 * ldb + (int64_t)g * N + kg * 8;
 
 #pragma unroll 1
   for (int jj = 0; jj < 2; ++jj) {
@@ -109,25 +485,17 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_bf16(
     const int l = j * 32 + col;
     const bool lvalid = l < ci.len;
 
-    // C rows of this token tile as B-operands: lane holds C[l][16q + 8kg .. +8]
     u32x4 creg[KN];
-#pragma unroll
-    for (int q = 0; q < KN; ++q) {
-      creg[q] = lvalid ? *reinterpret_cast<const u32x4 *>(cbase + (int64_t)l * ldb + q * 16 + kg * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
-    }
-
+    load_rows<KN>(creg, cbase + (int64_t)l * ldb, lvalid);
     f32x16 acc[TP];
 #pragma unroll
     for (int t = 0; t < TP; ++t) acc[t] = f32x16{};
-
-    // ---- inter-chunk term: Y^T[p][l] = sum_n Hprev[p][n] C[l][n]
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
-      const uint16_t *hrow = hp + (int64_t)(t * 32 + col) * N + kg * 8;
 #pragma unroll
       for (int q = 0; q < KN; ++q) {
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(hrow + q * 16);
+        const u32x4 a =
+            *reinterpret_cast<const u32x4 *>(hp + (int64_t)(t * 32 + col) * N + q * 16 + kg * 8);
         acc[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(creg[q]), acc[t]);
       }
     }
@@ -135,56 +503,27 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_bf16(
     const float el = __expf(al);
 #pragma unroll
     for (int t = 0; t < TP; ++t) acc[t] *= el;
+    const float ul = __expf(al - sa[32 * j]);
 
-    // ---- intra-chunk term over source tiles k <= j
 #pragma unroll 1
     for (int k = 0; k <= j; ++k) {
       const int s0 = k * 32;
-      const bool svalid = s0 + col < ci.len;
-      const uint16_t *brow = bbase + (int64_t)(s0 + col) * ldb + kg * 8;
+      u32x4 bcur[KN];
+      load_rows<KN>(bcur, bbase + (int64_t)(s0 + col) * ldb, s0 + col < ci.len);
       f32x16 z = f32x16{};
 #pragma unroll
-      for (int q = 0; q < KN; ++q) {
-        const u32x4 b = svalid ? *reinterpret_cast<const u32x4 *>(brow + q * 16)
-                               : u32x4{0u, 0u, 0u, 0u};
-        z = mfma32x32x16(as_bf16x8(b), as_bf16x8(creg[q]), z);
-      }
-      // z[r] = Z[s = s0 + acc_row(r, kg)][l] = C_l . B_s ; apply the decay mask
+      for (int q = 0; q < KN; ++q) z = mfma32x32x16(as_bf16x8(bcur[q]), as_bf16x8(creg[q]), z);
       float gv[16];
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int s = s0 + acc_row(r, kg);
-        const bool keep = (k < j) || (s <= l);
-        const float arg = keep ? (al - sa[s]) : -__builtin_inff();
-        const float v = z[r] * __expf(arg) * sd[s];
-        gv[r] = keep ? v : 0.f;
+      if (k < j) {
+        decay_offdiag(z, ul, &vt[j][s0], kg, gv);
+      } else {
+        decay_diag(z, al, l, s0, kg, sa, sd, gv);
       }
       u32x4 g0, g1;
-      g0.x = pack_bf16x2(gv[0], gv[1]);
-      g0.y = pack_bf16x2(gv[2], gv[3]);
-      g0.z = pack_bf16x2(gv[4], gv[5]);
-      g0.w = pack_bf16x2(gv[6], gv[7]);
-      g1.x = pack_bf16x2(gv[8], gv[9]);
-      g1.y = pack_bf16x2(gv[10], gv[11]);
-      g1.z = pack_bf16x2(gv[12], gv[13]);
-      g1.w = pack_bf16x2(gv[14], gv[15]);
-      // X^T operands in the same K order: MFMA 0 covers s-offsets
-      // {4kg..4kg+3, 8+4kg..8+4kg+3}, MFMA 1 the same plus 16.
-#pragma unroll
-      for (int t = 0; t < TP; ++t) {
-        const uint16_t *xr = &xt[t * 32 + col][s0 + 4 * kg];
-        const u32x2 a0 = *reinterpret_cast<const u32x2 *>(xr);
-        const u32x2 a1 = *reinterpret_cast<const u32x2 *>(xr + 8);
-        const u32x2 b0 = *reinterpret_cast<const u32x2 *>(xr + 16);
-        const u32x2 b1 = *reinterpret_cast<const u32x2 *>(xr + 24);
-        const u32x4 xa{a0.x, a0.y, a1.x, a1.y};
-        const u32x4 xb{b0.x, b0.y, b1.x, b1.y};
-        acc[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g0), acc[t]);
-        acc[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g1), acc[t]);
-      }
+      pack_g(gv, g0, g1);
+      mfma_xg<TP>(acc, &xt[col][s0 + 4 * kg], LDX, g0, g1);
     }
 
-    // ---- epilogue: + D x_l, round to bf16, store y[t0 + l][h][p]
     if (lvalid) {
       const uint16_t *xrow = xbase + (int64_t)l * ldx;
       uint16_t *yrow = y + (ci.t0 + l) * ldx + (int64_t)h * P;
@@ -219,11 +558,20 @@ static void launch_sc(const void *x, const void *B, const void *C, const float *
                       const float *acum, const float *dtq, const void *hprev, void *y,
                       const Geometry &geo, hipStream_t stream) {
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
-  hipLaunchKernelGGL((k_chunk_scan_bf16<Q, P, N>), dim3((unsigned)geo.nc_max, (unsigned)geo.H),
-                     dim3(Q), 0, stream, static_cast<const uint16_t *>(x),
-                     static_cast<const uint16_t *>(B), static_cast<const uint16_t *>(C), D, acum,
-                     dtq, static_cast<const uint16_t *>(hprev), cg, geo.H, geo.G,
-                     static_cast<uint16_t *>(y));
+  const dim3 grid(xcd_grid(geo.nc_max, geo.H));
+  if constexpr (N <= 128) {
+    hipLaunchKernelGGL((k_chunk_scan_lds<Q, P, N>), grid, dim3(Q), 0, stream,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
+                       static_cast<const uint16_t *>(C), D, acum, dtq,
+                       static_cast<const uint16_t *>(hprev), cg, (int)geo.nc_max, geo.H, geo.G,
+                       static_cast<uint16_t *>(y));
+  } else {
+    hipLaunchKernelGGL((k_chunk_scan_regs<Q, P, N>), grid, dim3(Q), 0, stream,
+                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
+                       static_cast<const uint16_t *>(C), D, acum, dtq,
+                       static_cast<const uint16_t *>(hprev), cg, (int)geo.nc_max, geo.H, geo.G,
+                       static_cast<uint16_t *>(y));
+  }
 }
 
 template <int Q>

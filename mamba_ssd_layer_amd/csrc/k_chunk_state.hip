@@ -15,7 +15,7 @@
 // into bf16 pairs and writes 8-byte runs of 4 tokens.  The MFMA then reads
 // 16-byte K-runs (8 tokens) per lane.  Padded LDS rows (K + 8 elements,
 // 144 bytes) keep the 16-byte column reads of 16 consecutive rows on distinct
-// banks.  Block = (chunk, head), 4 wavefronts; the (P/32) x (N/32) output tiles
+// banks.  Block = (chunk, head) in XCD-aware order, 4 wavefronts; the (P/32) x (N/32) output tiles
 // of 32x32 are split evenly over the wavefronts; fp32 accumulation, fp32 S.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
@@ -83,7 +83,8 @@ __device__ __forceinline__ void stage_transposed(const uint16_t *__restrict__ sr
 template <int Q, int P, int N>
 __global__ __launch_bounds__(kStateThreads) void k_chunk_state_bf16(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm, const float *__restrict__ acum,
-    const float *__restrict__ dtq, ChunkGeom geom, int H, int G, float *__restrict__ states) {
+    const float *__restrict__ dtq, ChunkGeom geom, int nc, int H, int G,
+    float *__restrict__ states) {
   static_assert(P % 32 == 0 && N % 32 == 0, "tile shape");
   constexpr int TP = P / 32;
   constexpr int TN = N / 32;
@@ -95,8 +96,9 @@ __global__ __launch_bounds__(kStateThreads) void k_chunk_state_bf16(
   __shared__ __align__(16) uint16_t bs[N][kLDK];
   __shared__ float sw[Q];
 
-  const int c = blockIdx.x;
-  const int h = blockIdx.y;
+  int c, h;
+  xcd_chunk_head(H, c, h);
+  if (c >= nc) return;
   const int g = h / (H / G);
   const ChunkInfo ci = chunk_info(geom, c);
   if (ci.len <= 0) return;
@@ -165,9 +167,10 @@ template <int Q, int P, int N>
 static void launch_cs(const void *x, const void *B, const float *acum, const float *dtq,
                       float *states, const Geometry &geo, hipStream_t stream) {
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
-  hipLaunchKernelGGL((k_chunk_state_bf16<Q, P, N>), dim3((unsigned)geo.nc_max, (unsigned)geo.H),
+  hipLaunchKernelGGL((k_chunk_state_bf16<Q, P, N>), dim3(xcd_grid(geo.nc_max, geo.H)),
                      dim3(kStateThreads), 0, stream, static_cast<const uint16_t *>(x),
-                     static_cast<const uint16_t *>(B), acum, dtq, cg, geo.H, geo.G, states);
+                     static_cast<const uint16_t *>(B), acum, dtq, cg, (int)geo.nc_max, geo.H,
+                     geo.G, states);
 }
 
 template <int Q>

@@ -145,11 +145,19 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
     }
     float excl = __shfl_up(incl, 1, 64);
     if (lane == 0) excl = 0.f;
+    // positions past a partial chunk's end repeat the value at its last token
+    const int last = ci.len - 1;
+    float mine = 0.f;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      if (e == last % E) mine = excl + pre[e];
+    }
+    const float lastval = __shfl(mine, last / E, 64);
     float *ao = acum + ((int64_t)c * H + h) * Q + lane * E;
     float *dq = dtq + ((int64_t)c * H + h) * Q + lane * E;
 #pragma unroll
     for (int e = 0; e < E; ++e) {
-      ao[e] = excl + pre[e];
+      ao[e] = lane * E + e < ci.len ? excl + pre[e] : lastval;
       dq[e] = v[e];
     }
   }

@@ -52,7 +52,8 @@ ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
   const int64_t Q = chunk_len;
   const int64_t nc_row = d->nseq > 0 ? 0 : ceil_div(d->seqlen, Q);
   const int64_t nc_max = d->nseq > 0 ? ceil_div(T, Q) + d->nseq : d->batch * nc_row;
-  if (nc_max >= ((int64_t)1 << 31)) return SSD_ERR_UNSUPPORTED;
+  // the (chunk, head) grids launch 8*ceil(nc/8)*H blocks of up to 256 threads
+  if ((nc_max + 8) * H >= ((int64_t)1 << 24)) return SSD_ERR_UNSUPPORTED;
 
   Plan p{};
   p.bf16 = bf16;

@@ -50,6 +50,26 @@ __device__ __forceinline__ ChunkInfo chunk_info(const ChunkGeom &g, int c) {
   return ci;
 }
 
+// XCD-aware block order for the (chunk, head) grids.  Workgroups are handed
+// to the 8 XCDs round-robin by linear id, and each XCD has its own L2.  Block
+// b runs chunk c = (b / (8 H)) * 8 + b % 8 and head h = (b / 8) % H, so every
+// head of a chunk lands on the same XCD (the chunk's B and C are fetched into
+// one L2 once and reused by all heads) and each XCD walks the heads of a chunk
+// back to back (the chunk's token rows of x are read as contiguous runs).
+// The grid has 8 * H * ceil(nc / 8) blocks; those with c >= nc exit.
+constexpr int kXcds = 8;
+
+__device__ __forceinline__ void xcd_chunk_head(int H, int &c, int &h) {
+  const int b = blockIdx.x;
+  const int r = b / kXcds;
+  h = r % H;
+  c = (r / H) * kXcds + (b % kXcds);
+}
+
+inline unsigned xcd_grid(int64_t nc, int H) {
+  return (unsigned)(((nc + kXcds - 1) / kXcds) * kXcds * H);
+}
+
 // ----------------------------------------------------------------- bf16 helpers
 __device__ __forceinline__ float bf16lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
