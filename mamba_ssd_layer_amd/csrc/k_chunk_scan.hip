@@ -28,7 +28,8 @@
 //     per lane) and v_s = exp(m - acum_s) dt_s (a per-chunk table in LDS); both
 //     are <= 1 for non-increasing acum, so nothing overflows.  Diagonal tiles
 //     take exp(acum_l - acum_s) per element, masked to s <= l before the
-//     exponent is formed.
+//     exponent is formed.  (The LDS-staged kernel also takes u_l out of the
+//     sum over off-diagonal tiles, leaving one multiply per element there.)
 //
 // k_chunk_scan_lds (N <= 128): MFMA operands come from LDS, filled with
 // coalesced loads, instead of one cache line per lane.  At the start the block
@@ -37,9 +38,10 @@
 // lockstep with B tiles (L2-resident, shared by the heads of a group)
 // double-buffered one tile ahead; when a wavefront has both its token tiles
 // in play, their MFMA chains share the B and X operand reads.  Only when the
-// loop is done do the outputs leave, through per-wavefront LDS staging, as
-// full 16-byte row segments with D x_l added in fp32 -- so no store is in
-// flight while the loop waits on its tile loads.
+// loop is done do the outputs leave: D x_l is added in fp32 from the X^T
+// still in LDS, then each wavefront stages its tiles through its own LDS
+// slice and writes full 16-byte row segments -- no store is in flight while
+// the loop waits on its tile loads, and x is read from memory only once.
 // k_chunk_scan_regs (N = 256, whose C operands of two token tiles would not fit
 // in registers): one token tile at a time, X^T for the whole chunk in LDS,
 // B operands read straight from global memory.
@@ -65,6 +67,17 @@ __device__ __forceinline__ void decay_offdiag(const f32x16 &z, float ul, const f
     const f32x4 v = *reinterpret_cast<const f32x4 *>(vrow + 8 * rb + 4 * kg);
 #pragma unroll
     for (int e = 0; e < 4; ++e) gv[rb * 4 + e] = z[rb * 4 + e] * (ul * v[e]);
+  }
+}
+
+// Off-diagonal decay with the per-lane factor taken out of the sum: g = z * v[s].
+__device__ __forceinline__ void decay_offdiag_v(const f32x16 &z, const float *vrow, int kg,
+                                                float (&gv)[16]) {
+#pragma unroll
+  for (int rb = 0; rb < 4; ++rb) {
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(vrow + 8 * rb + 4 * kg);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) gv[rb * 4 + e] = z[rb * 4 + e] * v[e];
   }
 }
 
@@ -242,9 +255,18 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
       acc2[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(c2[q]), acc2[t]);
     }
   }
+  // Decay bookkeeping per token tile j (first token 32j, m_j = acum[32j]):
+  //   exp(acum_l)          = u_l * exp(m_j),   u_l = exp(acum_l - m_j) <= 1
+  //   exp(acum_l - acum_s) = u_l * v_j[s],     v_j[s] = exp(m_j - acum_s) dt_s, s < 32j
+  // so the inter term (scaled by the wave-uniform exp(m_j)) and all
+  // off-diagonal source tiles (g = z v_j[s]) accumulate without u_l; the
+  // accumulator is scaled by u_l once, just before the diagonal tile.
   const float al1 = sa[l1], al2 = sa[l2];
   {
-    const float e1 = __expf(al1), e2 = __expf(al2);
+    const float m1 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sa[32 * j1])));
+    const float m2 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sa[32 * j2])));
+    const float e1 = __expf(m1);
+    const float e2 = __expf(m2);
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
       acc1[t] *= e1;
@@ -285,45 +307,36 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
   if (nk > 1) load_tile(1);
   __syncthreads();  // B tile 0 staged
 
-  // source tile k for one token tile (j, l) held in (acc, creg)
-  auto step_one = [&](f32x16 (&acc)[TP], const u32x4 (&creg)[KN], int j, int l, float al, float u,
-                      int k, int buf) {
+  auto scale_rows = [&](f32x16 (&acc)[TP], float u) {
+#pragma unroll
+    for (int t = 0; t < TP; ++t) acc[t] *= u;
+  };
+  // Z = B_k C_j^T for source tile k, token tile j (8 chained MFMAs)
+  auto tile_z = [&](const u32x4 (&creg)[KN], int buf) {
     f32x16 z = f32x16{};
 #pragma unroll
     for (int q = 0; q < KN; ++q) {
       const u32x4 b = *reinterpret_cast<const u32x4 *>(&bs[buf][col][q * 16 + kg * 8]);
       z = mfma32x32x16(as_bf16x8(b), as_bf16x8(creg[q]), z);
     }
-    float gv[16];
-    if (k < j) {
-      decay_offdiag(z, u, &vt[j][32 * k], kg, gv);
-    } else {
-      decay_diag(z, al, l, 32 * k, kg, sa, sd, gv);
-    }
-    u32x4 g0, g1;
-    pack_g(gv, g0, g1);
-    mfma_xg<TP>(acc, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
+    return z;
   };
-  // source tile k for both token tiles (k <= j1 < j2): the B and X operand
-  // reads are shared, and the two MFMA chains interleave
-  auto step_two = [&](int k, int buf) {
-    f32x16 z1 = f32x16{}, z2 = f32x16{};
-#pragma unroll
-    for (int q = 0; q < KN; ++q) {
-      const u32x4 b = *reinterpret_cast<const u32x4 *>(&bs[buf][col][q * 16 + kg * 8]);
-      z1 = mfma32x32x16(as_bf16x8(b), as_bf16x8(c1[q]), z1);
-      z2 = mfma32x32x16(as_bf16x8(b), as_bf16x8(c2[q]), z2);
-    }
-    float gv1[16], gv2[16];
-    if (k < j1) {
-      decay_offdiag(z1, u1, &vt[j1][32 * k], kg, gv1);
-    } else {
-      decay_diag(z1, al1, l1, 32 * k, kg, sa, sd, gv1);
-    }
-    decay_offdiag(z2, u2, &vt[j2][32 * k], kg, gv2);
-    u32x4 g10, g11, g20, g21;
-    pack_g(gv1, g10, g11);
-    pack_g(gv2, g20, g21);
+  auto g_off = [&](const u32x4 (&creg)[KN], int j, int k, int buf, u32x4 &g0, u32x4 &g1) {
+    const f32x16 z = tile_z(creg, buf);
+    float gv[16];
+    decay_offdiag_v(z, &vt[j][32 * k], kg, gv);
+    pack_g(gv, g0, g1);
+  };
+  auto g_diag = [&](const u32x4 (&creg)[KN], int l, float al, int k, int buf, u32x4 &g0,
+                    u32x4 &g1) {
+    const f32x16 z = tile_z(creg, buf);
+    float gv[16];
+    decay_diag(z, al, l, 32 * k, kg, sa, sd, gv);
+    pack_g(gv, g0, g1);
+  };
+  // Y^T += X_k^T G^T for two accumulators sharing the X operand reads
+  auto xg_two = [&](int k, const u32x4 &g10, const u32x4 &g11, const u32x4 &g20,
+                    const u32x4 &g21) {
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
       const uint16_t *xr = &xt[t * 32 + col][32 * k + 4 * kg];
@@ -339,30 +352,93 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
       acc2[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g21), acc2[t]);
     }
   };
-
-  // ---- intra-chunk term: all source tiles in lockstep
-#pragma unroll 1
-  for (int k = 0; k < nk; ++k) {
-    const int buf = k & 1;
-    if (act2) {
-      if (k <= j1) {
-        step_two(k, buf);
-      } else if (k <= j2) {
-        step_one(acc2, c2, j2, l2, al2, u2, k, buf);
-      }
-    } else if (act1 && k <= j1) {
-      step_one(acc1, c1, j1, l1, al1, u1, k, buf);
-    }
+  // end of a lockstep step: stage the next B tile (loaded one step earlier),
+  // start loading the one after, and wait for the whole block
+  auto advance = [&](int k) {
     if (k + 1 < nk) {
-      store_tile(buf ^ 1);  // tile k+1, loaded one step earlier
+      store_tile((k + 1) & 1);
       if (k + 2 < nk) load_tile(k + 2);
     }
     __syncthreads();
+  };
+
+  // ---- intra-chunk term: all source tiles in lockstep, in phases that are
+  // uniform per wavefront (j1 < j2): both tiles off-diagonal, tile 1 on its
+  // diagonal, tile 2 alone off-diagonal, tile 2 on its diagonal, then idle.
+  // Every wavefront passes nk barriers in total.
+  int k = 0;
+  if (act2) {
+#pragma unroll 1
+    for (; k < j1; ++k) {
+      u32x4 g10, g11, g20, g21;
+      g_off(c1, j1, k, k & 1, g10, g11);
+      g_off(c2, j2, k, k & 1, g20, g21);
+      xg_two(k, g10, g11, g20, g21);
+      advance(k);
+    }
+    {  // k == j1
+      u32x4 g10, g11, g20, g21;
+      g_diag(c1, l1, al1, k, k & 1, g10, g11);
+      g_off(c2, j2, k, k & 1, g20, g21);
+      scale_rows(acc1, u1);
+      xg_two(k, g10, g11, g20, g21);
+      advance(k);
+      ++k;
+    }
+#pragma unroll 1
+    for (; k < j2; ++k) {
+      u32x4 g0, g1;
+      g_off(c2, j2, k, k & 1, g0, g1);
+      mfma_xg<TP>(acc2, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
+      advance(k);
+    }
+    {  // k == j2
+      u32x4 g0, g1;
+      g_diag(c2, l2, al2, k, k & 1, g0, g1);
+      scale_rows(acc2, u2);
+      mfma_xg<TP>(acc2, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
+      advance(k);
+      ++k;
+    }
+  } else if (act1) {
+#pragma unroll 1
+    for (; k < j1; ++k) {
+      u32x4 g0, g1;
+      g_off(c1, j1, k, k & 1, g0, g1);
+      mfma_xg<TP>(acc1, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
+      advance(k);
+    }
+    {  // k == j1
+      u32x4 g0, g1;
+      g_diag(c1, l1, al1, k, k & 1, g0, g1);
+      scale_rows(acc1, u1);
+      mfma_xg<TP>(acc1, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
+      advance(k);
+      ++k;
+    }
   }
+#pragma unroll 1
+  for (; k < nk; ++k) advance(k);
+
+  // ---- skip term D x_l, in fp32 from the X^T still in LDS: a lane's
+  // accumulator rows p of column l are x[l][p] = xt[p][l]
+  const float Dh = Dv ? Dv[h] : 0.f;
+  auto add_skip = [&](f32x16 (&acc)[TP], int l) {
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint32_t bits = xt[t * 32 + acc_row(r, kg)][l];
+        acc[t][r] += Dh * __uint_as_float(bits << 16);
+      }
+    }
+  };
+  if (act1) add_skip(acc1, l1);
+  if (act2) add_skip(acc2, l2);
+  __syncthreads();  // X^T no longer needed: its bytes become output staging
 
   // ---- epilogue: each wave stages its token tiles through its own LDS slice
-  // as fp32 [token][p], adds D x in fp32, rounds, and stores 16-byte row segments
-  const float Dh = Dv ? Dv[h] : 0.f;
+  // as fp32 [token][p], rounds, and stores 16-byte row segments
   float(*yb)[LYB] = reinterpret_cast<float(*)[LYB]>(smem + wave * 32 * LYB * 4);
   auto epilogue = [&](const f32x16 (&acc)[TP], int j) {
 #pragma unroll
@@ -385,12 +461,11 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
       if (l < ci.len) {
         const f32x4 v0 = *reinterpret_cast<const f32x4 *>(&yb[r][gp * 8]);
         const f32x4 v1 = *reinterpret_cast<const f32x4 *>(&yb[r][gp * 8 + 4]);
-        const u32x4 xv = *reinterpret_cast<const u32x4 *>(xbase + (int64_t)l * ldx + gp * 8);
         u32x4 o;
-        o.x = pack_bf16x2(v0.x + Dh * bf16lo(xv.x), v0.y + Dh * bf16hi(xv.x));
-        o.y = pack_bf16x2(v0.z + Dh * bf16lo(xv.y), v0.w + Dh * bf16hi(xv.y));
-        o.z = pack_bf16x2(v1.x + Dh * bf16lo(xv.z), v1.y + Dh * bf16hi(xv.z));
-        o.w = pack_bf16x2(v1.z + Dh * bf16lo(xv.w), v1.w + Dh * bf16hi(xv.w));
+        o.x = pack_bf16x2(v0.x, v0.y);
+        o.y = pack_bf16x2(v0.z, v0.w);
+        o.z = pack_bf16x2(v1.x, v1.y);
+        o.w = pack_bf16x2(v1.z, v1.w);
         *reinterpret_cast<u32x4 *>(y + (ci.t0 + l) * ldx + (int64_t)h * P + gp * 8) = o;
       }
     }

@@ -12,7 +12,9 @@
 // operand needs runs along the contracted (token) index, so both tiles are
 // transposed on their way into LDS: each thread loads 4 token rows x 8
 // columns (four 16-byte loads), scales x by w_l in fp32, repacks column-wise
-// into bf16 pairs and writes 8-byte runs of 4 tokens.  The MFMA then reads
+// into bf16 pairs and writes 8-byte runs of 4 tokens.  The chunk goes through
+// in stages of 64 tokens; a stage's global loads are issued before the
+// previous stage's MFMAs, so only the first one waits on memory.  The MFMA then reads
 // 16-byte K-runs (8 tokens) per lane.  Padded LDS rows (K + 8 elements,
 // 144 bytes) keep the 16-byte column reads of 16 consecutive rows on distinct
 // banks.  Block = (chunk, head) in XCD-aware order, 4 wavefronts; the (P/32) x (N/32) output tiles
@@ -28,57 +30,73 @@ constexpr int kStateThreads = 256;
 constexpr int kKT = 64;         // tokens per LDS stage
 constexpr int kLDK = kKT + 8;   // padded LDS row (bf16 elements)
 
-// Stage rows [kt, kt+kKT) of a [tokens x D] bf16 matrix (row stride `ld`
-// elements) into LDS transposed, dst[d][l] with row length kLDK.  Rows at or
-// past `len` are written as zeros and never read from global memory.  If
-// `wt` is given, row l is scaled by wt[l] (fp32) before rounding to bf16.
+// A stage is kKT token rows of a [tokens x D] bf16 matrix (row stride `ld`
+// elements), moved in units of 4 rows x 8 columns: four 16-byte loads per
+// unit, row quad fastest across threads.  Rows at or past `len` are zeros and
+// never read from global memory.
 template <int D>
-__device__ __forceinline__ void stage_transposed(const uint16_t *__restrict__ src, int64_t ld,
-                                                 int kt, int len, const float *wt,
-                                                 uint16_t (*dst)[kLDK]) {
-  constexpr int RQ = kKT / 4;       // row quads per stage
-  constexpr int UNITS = RQ * (D / 8);
-  for (int u = threadIdx.x; u < UNITS; u += kStateThreads) {
-    const int rq = u % RQ;  // row quad fastest: conflict-free 8-byte LDS writes
-    const int cb = u / RQ;
-    const int l0 = kt + rq * 4;
-    u32x4 r[4];
+struct Stage {
+  static constexpr int RQ = kKT / 4;  // row quads per stage
+  static constexpr int UNITS = RQ * (D / 8);
+  static constexpr int PER_THREAD = (UNITS + kStateThreads - 1) / kStateThreads;
+  u32x4 r[PER_THREAD][4];
+
+  __device__ __forceinline__ void load(const uint16_t *__restrict__ src, int64_t ld, int kt,
+                                       int len) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (l0 + i < len) {
-        r[i] = *reinterpret_cast<const u32x4 *>(src + (int64_t)(l0 + i) * ld + cb * 8);
-      } else {
-        r[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int u = threadIdx.x + i * kStateThreads;
+      const int rq = u % RQ;
+      const int cb = u / RQ;
+      const int l0 = kt + rq * 4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        r[i][e] = (u < UNITS && l0 + e < len)
+                      ? *reinterpret_cast<const u32x4 *>(src + (int64_t)(l0 + e) * ld + cb * 8)
+                      : u32x4{0u, 0u, 0u, 0u};
       }
-    }
-    u32x2 out[8];
-    if (wt) {
-      float w[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) w[i] = wt[l0 + i];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        // columns 2m (low halves) and 2m+1 (high halves) of word m
-        out[2 * m].x = pack_bf16x2(bf16lo(r[0][m]) * w[0], bf16lo(r[1][m]) * w[1]);
-        out[2 * m].y = pack_bf16x2(bf16lo(r[2][m]) * w[2], bf16lo(r[3][m]) * w[3]);
-        out[2 * m + 1].x = pack_bf16x2(bf16hi(r[0][m]) * w[0], bf16hi(r[1][m]) * w[1]);
-        out[2 * m + 1].y = pack_bf16x2(bf16hi(r[2][m]) * w[2], bf16hi(r[3][m]) * w[3]);
-      }
-    } else {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        out[2 * m].x = pair_lo(r[0][m], r[1][m]);
-        out[2 * m].y = pair_lo(r[2][m], r[3][m]);
-        out[2 * m + 1].x = pair_hi(r[0][m], r[1][m]);
-        out[2 * m + 1].y = pair_hi(r[2][m], r[3][m]);
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      *reinterpret_cast<u32x2 *>(&dst[cb * 8 + j][rq * 4]) = out[j];
     }
   }
-}
+
+  // Writes the stage transposed, dst[d][l] with row length kLDK: column-wise
+  // bf16 pairs, 8-byte runs of 4 tokens.  If `wt` is given, row l is scaled by
+  // wt[l] in fp32 and rounded once to bf16.
+  __device__ __forceinline__ void store(const float *wt, int kt, uint16_t (*dst)[kLDK]) const {
+#pragma unroll
+    for (int i = 0; i < PER_THREAD; ++i) {
+      const int u = threadIdx.x + i * kStateThreads;
+      if (u >= UNITS) continue;
+      const int rq = u % RQ;
+      const int cb = u / RQ;
+      u32x2 out[8];
+      if (wt) {
+        float w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) w[e] = wt[kt + rq * 4 + e];
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          // columns 2m (low halves) and 2m+1 (high halves) of word m
+          out[2 * m].x = pack_bf16x2(bf16lo(r[i][0][m]) * w[0], bf16lo(r[i][1][m]) * w[1]);
+          out[2 * m].y = pack_bf16x2(bf16lo(r[i][2][m]) * w[2], bf16lo(r[i][3][m]) * w[3]);
+          out[2 * m + 1].x = pack_bf16x2(bf16hi(r[i][0][m]) * w[0], bf16hi(r[i][1][m]) * w[1]);
+          out[2 * m + 1].y = pack_bf16x2(bf16hi(r[i][2][m]) * w[2], bf16hi(r[i][3][m]) * w[3]);
+        }
+      } else {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          out[2 * m].x = pair_lo(r[i][0][m], r[i][1][m]);
+          out[2 * m].y = pair_lo(r[i][2][m], r[i][3][m]);
+          out[2 * m + 1].x = pair_hi(r[i][0][m], r[i][1][m]);
+          out[2 * m + 1].y = pair_hi(r[i][2][m], r[i][3][m]);
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        *reinterpret_cast<u32x2 *>(&dst[cb * 8 + jj][rq * 4]) = out[jj];
+      }
+    }
+  }
+};
 
 template <int Q, int P, int N>
 __global__ __launch_bounds__(kStateThreads) void k_chunk_state_bf16(
@@ -104,6 +122,13 @@ __global__ __launch_bounds__(kStateThreads) void k_chunk_state_bf16(
   if (ci.len <= 0) return;
 
   const int64_t ch = (int64_t)c * H + h;
+  const uint16_t *xbase = x + ci.t0 * (int64_t)H * P + (int64_t)h * P;
+  const uint16_t *bbase = Bm + ci.t0 * (int64_t)G * N + (int64_t)g * N;
+  Stage<P> xst;
+  Stage<N> bst;
+  // the first stage's loads go out before anything waits
+  xst.load(xbase, (int64_t)H * P, 0, ci.len);
+  bst.load(bbase, (int64_t)G * N, 0, ci.len);
   {
     const float *ac = acum + ch * Q;
     const float *dq = dtq + ch * Q;
@@ -121,13 +146,15 @@ __global__ __launch_bounds__(kStateThreads) void k_chunk_state_bf16(
 #pragma unroll
   for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
 
-  const uint16_t *xbase = x + ci.t0 * (int64_t)H * P + (int64_t)h * P;
-  const uint16_t *bbase = Bm + ci.t0 * (int64_t)G * N + (int64_t)g * N;
-
+#pragma unroll 1
   for (int kt = 0; kt < ci.len; kt += kKT) {
-    stage_transposed<P>(xbase, (int64_t)H * P, kt, ci.len, sw, xs);
-    stage_transposed<N>(bbase, (int64_t)G * N, kt, ci.len, nullptr, bs);
+    xst.store(sw, kt, xs);
+    bst.store(nullptr, kt, bs);
     __syncthreads();
+    if (kt + kKT < ci.len) {  // next stage's loads overlap this stage's MFMAs
+      xst.load(xbase, (int64_t)H * P, kt + kKT, ci.len);
+      bst.load(bbase, (int64_t)G * N, kt + kKT, ci.len);
+    }
 #pragma unroll
     for (int ks = 0; ks < kKT / 16; ++ks) {
 #pragma unroll
