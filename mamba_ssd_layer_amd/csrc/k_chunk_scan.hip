@@ -131,38 +131,46 @@ __device__ __forceinline__ void mfma_xg(f32x16 (&acc)[TP], const uint16_t *xrow0
 }
 
 // ============================================================ LDS-staged kernel
+// 16-byte chunk swizzle of an LDS tile row of `nc` chunks, so that 16 lanes
+// reading the same chunk column of 16 consecutive rows hit distinct banks.
+__device__ __forceinline__ constexpr int chunk_swz(int row, int nc) {
+  return nc >= 16 ? (row & 15) : ((row >> 1) & (nc - 1));
+}
+
 template <int Q, int P, int N>
 __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
     const uint16_t *__restrict__ Cm, const float *__restrict__ Dv, const float *__restrict__ acum,
     const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int nc,
     int H, int G, uint16_t *__restrict__ y) {
-  static_assert(P % 32 == 0 && N % 16 == 0 && Q % 64 == 0, "tile shape");
-  static_assert(P <= 64, "hprev is staged in the two B tiles (64 rows)");
+  static_assert(P == 64 && N % 64 == 0 && Q % 64 == 0, "tile shape");
   constexpr int NT = Q;          // threads
   constexpr int NW = Q / 64;     // wavefronts
   constexpr int NLT = Q / 32;    // token tiles
   constexpr int TP = P / 32;     // p tiles
   constexpr int KN = N / 16;     // K steps over n
-  constexpr int LDX = Q + 4;     // X^T row: Q tokens (bf16) + pad
-  constexpr int LBT = N + 8;     // B / hprev row (bf16) + pad
-  constexpr int LYB = P + 4;     // output staging row (fp32) + pad
-  constexpr int BV = 32 * N / 8;              // 16-byte vectors per B tile
-  constexpr int BPT = (BV + NT - 1) / NT;
-  constexpr int XT_BYTES = P * LDX * 2;
-  constexpr int BS_BYTES = 2 * 32 * LBT * 2;
-  constexpr int YB_BYTES = NW * 32 * LYB * 4;
-  constexpr int SMEM = XT_BYTES + BS_BYTES > YB_BYTES ? XT_BYTES + BS_BYTES : YB_BYTES;
+  constexpr int NCB = N / 8;     // 16-byte chunks per B / hprev row
+  constexpr int NCX = P / 8;     // 16-byte chunks per x row
+  constexpr int BT = 32 * N * 2;   // B tile bytes
+  constexpr int XT = 32 * P * 2;   // x tile bytes
+  constexpr int DEPTH = N <= 128 ? 4 : 2;  // ring slots: tiles k .. k+DEPTH-1
+  constexpr int BI = BT / 1024 / NW;       // 1 KB direct loads per wave per B tile
+  constexpr int XI = XT / 1024 / NW;       // ... per x tile
+  constexpr int HI = P * N * 2 / 1024 / NW;
+  constexpr int LPT = BI + XI;             // loads per thread per source tile
+  static_assert(BI * NW * 1024 == BT && XI * NW * 1024 == XT && HI * NW * 1024 == P * N * 2,
+                "tiles split evenly into 1 KB wave loads");
+  constexpr int RB = 0;                    // ring of B tiles
+  constexpr int RX = DEPTH * BT;           // ring of x tiles
+  constexpr int HS = RX + DEPTH * XT;      // hprev [P][N]
+  constexpr int LYB = P + 4;               // output staging row (fp32) + pad
+  constexpr int YS = NW * 32 * LYB * 4;    // output staging, after everything else
+  constexpr int MAIN = HS + P * N * 2 > YS ? HS + P * N * 2 : YS;
 
-  // X^T of the chunk and two B stages during the loop; per-wave output
-  // staging buffers in the same bytes afterwards
-  __shared__ __align__(16) unsigned char smem[SMEM];
+  __shared__ __align__(16) unsigned char smem[MAIN];
   __shared__ __align__(16) float sa[Q];
   __shared__ __align__(16) float sd[Q];
   __shared__ __align__(16) float vt[NLT][Q];  // vt[j][s] = exp(acum[32j] - acum[s]) dt[s], s < 32j
-  uint16_t(*xt)[LDX] = reinterpret_cast<uint16_t(*)[LDX]>(smem);
-  uint16_t(*bs)[32][LBT] = reinterpret_cast<uint16_t(*)[32][LBT]>(smem + XT_BYTES);
-  uint16_t(*hs)[LBT] = reinterpret_cast<uint16_t(*)[LBT]>(smem + XT_BYTES);  // hprev [P][LBT]
 
   int c, h;
   xcd_chunk_head(H, c, h);
@@ -178,46 +186,6 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
   const uint16_t *bbase = Bm + ci.t0 * ldb + (int64_t)g * N;
   const uint16_t *cbase = Cm + ci.t0 * ldb + (int64_t)g * N;
   const int tid = threadIdx.x;
-
-  // ---- stage acum, dt, X^T of the whole chunk and hprev
-  for (int l = tid; l < Q; l += NT) {
-    sa[l] = acum[ch * Q + l];
-    sd[l] = dtq[ch * Q + l];
-  }
-  {
-    constexpr int RQ = Q / 4;
-    constexpr int UNITS = RQ * (P / 8);
-    for (int u = tid; u < UNITS; u += NT) {
-      const int rq = u % RQ;  // 4 token rows x 8 columns per unit, row quad fastest
-      const int cb = u / RQ;
-      const int l0 = rq * 4;
-      u32x4 r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r[i] = l0 + i < ci.len
-                   ? *reinterpret_cast<const u32x4 *>(xbase + (int64_t)(l0 + i) * ldx + cb * 8)
-                   : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        u32x2 lo, hi;
-        lo.x = pair_lo(r[0][m], r[1][m]);
-        lo.y = pair_lo(r[2][m], r[3][m]);
-        hi.x = pair_hi(r[0][m], r[1][m]);
-        hi.y = pair_hi(r[2][m], r[3][m]);
-        *reinterpret_cast<u32x2 *>(&xt[cb * 8 + 2 * m][l0]) = lo;
-        *reinterpret_cast<u32x2 *>(&xt[cb * 8 + 2 * m + 1][l0]) = hi;
-      }
-    }
-    const uint16_t *hp = hprev + ch * (int64_t)P * N;
-    for (int v = tid; v < P * N / 8; v += NT) {
-      const int row = v / (N / 8);
-      const int cv = v - row * (N / 8);
-      *reinterpret_cast<u32x4 *>(&hs[row][cv * 8]) =
-          *reinterpret_cast<const u32x4 *>(hp + (int64_t)row * N + cv * 8);
-    }
-  }
-
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int lane = tid & 63;
   const int col = lane & 31;
@@ -229,213 +197,255 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
   const bool act1 = j1 < nk;
   const bool act2 = j2 < nk;
 
+  // ---- register loads first (acum, dt, the C operands of both token tiles),
+  // so the compiler's waits for them leave the direct loads below in flight
+  for (int l = tid; l < Q; l += NT) {
+    sa[l] = acum[ch * Q + l];
+    sd[l] = dtq[ch * Q + l];
+  }
   u32x4 c1[KN], c2[KN];
   load_rows<KN>(c1, cbase + (int64_t)l1 * ldb + kg * 8, l1 < ci.len);
   load_rows<KN>(c2, cbase + (int64_t)l2 * ldb + kg * 8, l2 < ci.len);
-  __syncthreads();  // sa, sd, X^T, hprev staged
 
+  // ---- direct loads: hprev, then source tiles 0 .. DEPTH-2.  Rows past the
+  // chunk's end read its last row (finite data the zero dt then cancels).
+  {
+    const uint16_t *hp = hprev + ch * (int64_t)P * N;
+#pragma unroll
+    for (int i = 0; i < HI; ++i) {
+      const int m = (wave * HI + i) * 64 + lane;
+      const int r = m / NCB, cc = (m % NCB) ^ chunk_swz(m / NCB, NCB);
+      load_lds16(hp + (int64_t)r * N + cc * 8, smem + HS + (wave * HI + i) * 1024);
+    }
+  }
+  auto issue_tile = [&](int k) {
+    const int slot = k % DEPTH;
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int m = (wave * BI + i) * 64 + lane;
+      const int r = m / NCB, cc = (m % NCB) ^ chunk_swz(m / NCB, NCB);
+      const int s = min(32 * k + r, ci.len - 1);
+      load_lds16(bbase + (int64_t)s * ldb + cc * 8, smem + RB + slot * BT + (wave * BI + i) * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int m = (wave * XI + i) * 64 + lane;
+      const int r = m / NCX, cc = (m % NCX) ^ chunk_swz(m / NCX, NCX);
+      const int s = min(32 * k + r, ci.len - 1);
+      load_lds16(xbase + (int64_t)s * ldx + cc * 8, smem + RX + slot * XT + (wave * XI + i) * 1024);
+    }
+  };
+#pragma unroll
+  for (int k = 0; k < DEPTH - 1; ++k) {
+    if (k < nk) issue_tile(k);
+  }
+
+  __syncthreads();  // sa, sd
   for (int idx = tid; idx < NLT * Q; idx += NT) {
     const int j = idx / Q;
     const int s = idx - j * Q;
     if (s < 32 * j) vt[j][s] = __expf(sa[32 * j] - sa[s]) * sd[s];
   }
+  const float al1 = sa[l1], al2 = sa[l2];
+  const float u1 = __expf(al1 - sa[32 * j1]);  // <= 1: exp(acum_l - acum at the tile's start)
+  const float u2 = __expf(al2 - sa[32 * j2]);
+  const float Dh = Dv ? Dv[h] : 0.f;
+
   f32x16 acc1[TP], acc2[TP];
 #pragma unroll
   for (int t = 0; t < TP; ++t) {
     acc1[t] = f32x16{};
     acc2[t] = f32x16{};
   }
-  // ---- inter-chunk term for both token tiles (shared hprev operands)
-#pragma unroll
-  for (int t = 0; t < TP; ++t) {
-#pragma unroll
-    for (int q = 0; q < KN; ++q) {
-      const u32x4 a = *reinterpret_cast<const u32x4 *>(&hs[t * 32 + col][q * 16 + kg * 8]);
-      acc1[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(c1[q]), acc1[t]);
-      acc2[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(c2[q]), acc2[t]);
-    }
-  }
-  // Decay bookkeeping per token tile j (first token 32j, m_j = acum[32j]):
-  //   exp(acum_l)          = u_l * exp(m_j),   u_l = exp(acum_l - m_j) <= 1
-  //   exp(acum_l - acum_s) = u_l * v_j[s],     v_j[s] = exp(m_j - acum_s) dt_s, s < 32j
-  // so the inter term (scaled by the wave-uniform exp(m_j)) and all
-  // off-diagonal source tiles (g = z v_j[s]) accumulate without u_l; the
-  // accumulator is scaled by u_l once, just before the diagonal tile.
-  const float al1 = sa[l1], al2 = sa[l2];
-  {
-    const float m1 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sa[32 * j1])));
-    const float m2 = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(sa[32 * j2])));
-    const float e1 = __expf(m1);
-    const float e2 = __expf(m2);
-#pragma unroll
-    for (int t = 0; t < TP; ++t) {
-      acc1[t] *= e1;
-      acc2[t] *= e2;
-    }
-  }
-  const float u1 = __expf(al1 - sa[32 * j1]);
-  const float u2 = __expf(al2 - sa[32 * j2]);
-
-  // B source tiles: global (L2) -> registers -> LDS stage, coalesced rows
-  u32x4 breg[BPT];
-  auto load_tile = [&](int k) {
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int v = tid + i * NT;
-      const int row = v / (N / 8);
-      const int cv = v - row * (N / 8);
-      const int s = 32 * k + row;
-      breg[i] = (v < BV && s < ci.len)
-                    ? *reinterpret_cast<const u32x4 *>(bbase + (int64_t)s * ldb + cv * 8)
-                    : u32x4{0u, 0u, 0u, 0u};
-    }
-  };
-  auto store_tile = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < BPT; ++i) {
-      const int v = tid + i * NT;
-      if (v < BV) {
-        const int row = v / (N / 8);
-        const int cv = v - row * (N / 8);
-        *reinterpret_cast<u32x4 *>(&bs[buf][row][cv * 8]) = breg[i];
-      }
-    }
-  };
-  load_tile(0);
-  __syncthreads();  // hprev consumed, vt complete
-  store_tile(0);
-  if (nk > 1) load_tile(1);
-  __syncthreads();  // B tile 0 staged
 
   auto scale_rows = [&](f32x16 (&acc)[TP], float u) {
 #pragma unroll
     for (int t = 0; t < TP; ++t) acc[t] *= u;
   };
-  // Z = B_k C_j^T for source tile k, token tile j (8 chained MFMAs)
-  auto tile_z = [&](const u32x4 (&creg)[KN], int buf) {
+  // Z = B_k C_j^T (8 chained MFMAs); B rows from the ring slot
+  auto tile_z = [&](const u32x4 (&creg)[KN], int slot) {
+    const unsigned char *bt = smem + RB + slot * BT + col * (N * 2);
     f32x16 z = f32x16{};
 #pragma unroll
     for (int q = 0; q < KN; ++q) {
-      const u32x4 b = *reinterpret_cast<const u32x4 *>(&bs[buf][col][q * 16 + kg * 8]);
+      const int cc = (2 * q + kg) ^ chunk_swz(col, NCB);
+      const u32x4 b = *reinterpret_cast<const u32x4 *>(bt + cc * 16);
       z = mfma32x32x16(as_bf16x8(b), as_bf16x8(creg[q]), z);
     }
     return z;
   };
-  auto g_off = [&](const u32x4 (&creg)[KN], int j, int k, int buf, u32x4 &g0, u32x4 &g1) {
-    const f32x16 z = tile_z(creg, buf);
+  auto g_off = [&](const u32x4 (&creg)[KN], int j, int k, u32x4 &g0, u32x4 &g1) {
+    const f32x16 z = tile_z(creg, k % DEPTH);
     float gv[16];
     decay_offdiag_v(z, &vt[j][32 * k], kg, gv);
     pack_g(gv, g0, g1);
   };
-  auto g_diag = [&](const u32x4 (&creg)[KN], int l, float al, int k, int buf, u32x4 &g0,
-                    u32x4 &g1) {
-    const f32x16 z = tile_z(creg, buf);
+  auto g_diag = [&](const u32x4 (&creg)[KN], int l, float al, int k, u32x4 &g0, u32x4 &g1) {
+    const f32x16 z = tile_z(creg, k % DEPTH);
     float gv[16];
     decay_diag(z, al, l, 32 * k, kg, sa, sd, gv);
     pack_g(gv, g0, g1);
   };
-  // Y^T += X_k^T G^T for two accumulators sharing the X operand reads
+  // X^T operands of source tile k straight from the row-major x tile by a
+  // transposing LDS read: lane (group gq = lane/16, d = lane%16) addresses
+  // token row sb + d/4, columns 4(d%4).., and receives p = 16(gq%2) + d of
+  // tokens sb .. sb+3.  sb follows the accumulator row order of G.
+  auto x_ops = [&](int k, int t, u32x4 &xa, u32x4 &xb) {
+    const unsigned char *xtile = smem + RX + (k % DEPTH) * XT;
+    const int gq = lane >> 4, d = lane & 15;
+    const int p0 = t * 32 + 16 * (gq & 1) + 4 * (d & 3);
+    u32x2 part[4];
+#pragma unroll
+    for (int h4 = 0; h4 < 4; ++h4) {  // s offsets 4kg, 8+4kg, 16+4kg, 24+4kg
+      const int row = 8 * h4 + 4 * kg + (d >> 2);
+      const int cc = (p0 >> 3) ^ chunk_swz(row, NCX);
+      part[h4] = lds_read_tr16(xtile + row * (P * 2) + cc * 16 + (p0 & 7) * 2);
+    }
+    xa = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
+    xb = u32x4{part[2].x, part[2].y, part[3].x, part[3].y};
+  };
+  auto xg_one = [&](f32x16 (&acc)[TP], int k, const u32x4 &g0, const u32x4 &g1) {
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+      u32x4 xa, xb;
+      x_ops(k, t, xa, xb);
+      acc[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g0), acc[t]);
+      acc[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g1), acc[t]);
+    }
+  };
   auto xg_two = [&](int k, const u32x4 &g10, const u32x4 &g11, const u32x4 &g20,
                     const u32x4 &g21) {
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
-      const uint16_t *xr = &xt[t * 32 + col][32 * k + 4 * kg];
-      const u32x2 a0 = *reinterpret_cast<const u32x2 *>(xr);
-      const u32x2 a1 = *reinterpret_cast<const u32x2 *>(xr + 8);
-      const u32x2 b0 = *reinterpret_cast<const u32x2 *>(xr + 16);
-      const u32x2 b1 = *reinterpret_cast<const u32x2 *>(xr + 24);
-      const u32x4 xa{a0.x, a0.y, a1.x, a1.y};
-      const u32x4 xb{b0.x, b0.y, b1.x, b1.y};
+      u32x4 xa, xb;
+      x_ops(k, t, xa, xb);
       acc1[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g10), acc1[t]);
       acc2[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g20), acc2[t]);
       acc1[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g11), acc1[t]);
       acc2[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g21), acc2[t]);
     }
   };
-  // end of a lockstep step: stage the next B tile (loaded one step earlier),
-  // start loading the one after, and wait for the whole block
-  auto advance = [&](int k) {
-    if (k + 1 < nk) {
-      store_tile((k + 1) & 1);
-      if (k + 2 < nk) load_tile(k + 2);
+  // skip term D x_l in fp32 at the token tile's diagonal step: the lane's
+  // accumulator rows p = 32t + 8rb + 4kg + e of column l are 4 consecutive
+  // elements of x row l, one 8-byte LDS read each
+  auto add_skip = [&](f32x16 (&acc)[TP], int k) {
+    const unsigned char *xtile = smem + RX + (k % DEPTH) * XT;
+#pragma unroll
+    for (int t = 0; t < TP; ++t) {
+#pragma unroll
+      for (int rb = 0; rb < 4; ++rb) {
+        const int p = t * 32 + rb * 8 + kg * 4;
+        const int cc = (p >> 3) ^ chunk_swz(col, NCX);
+        const u32x2 xv = *reinterpret_cast<const u32x2 *>(xtile + col * (P * 2) + cc * 16 + (p & 7) * 2);
+        acc[t][rb * 4 + 0] += Dh * bf16lo(xv.x);
+        acc[t][rb * 4 + 1] += Dh * bf16hi(xv.x);
+        acc[t][rb * 4 + 2] += Dh * bf16lo(xv.y);
+        acc[t][rb * 4 + 3] += Dh * bf16hi(xv.y);
+      }
+    }
+  };
+  // top of step k: this thread's loads of tile k are done (the loads of the
+  // tiles issued after it may stay in flight), then the whole block is
+  // (everyone's tile k landed, everyone left step k-1), then tile k+DEPTH-1
+  // goes into the slot step k-1 used
+  auto begin_step = [&](int k) {
+    const int after = min(DEPTH - 2, nk - 1 - k);
+    if (after >= 2) {
+      wait_vmcnt<2 * LPT>();
+    } else if (after == 1) {
+      wait_vmcnt<LPT>();
+    } else {
+      wait_vmcnt<0>();
     }
     __syncthreads();
+    if (k + DEPTH - 1 < nk) issue_tile(k + DEPTH - 1);
   };
+  static_assert(DEPTH <= 4, "begin_step waits for at most two later tiles");
 
-  // ---- intra-chunk term: all source tiles in lockstep, in phases that are
-  // uniform per wavefront (j1 < j2): both tiles off-diagonal, tile 1 on its
-  // diagonal, tile 2 alone off-diagonal, tile 2 on its diagonal, then idle.
-  // Every wavefront passes nk barriers in total.
+  // ---- intra-chunk term: source tiles in lockstep, in phases uniform per
+  // wavefront (j1 < j2): both tiles off-diagonal, tile 1 on its diagonal,
+  // tile 2 alone off-diagonal, tile 2 on its diagonal, then idle.  Each
+  // token tile accumulates u_l-free until its diagonal step multiplies by u_l.
   int k = 0;
   if (act2) {
 #pragma unroll 1
     for (; k < j1; ++k) {
+      begin_step(k);
       u32x4 g10, g11, g20, g21;
-      g_off(c1, j1, k, k & 1, g10, g11);
-      g_off(c2, j2, k, k & 1, g20, g21);
+      g_off(c1, j1, k, g10, g11);
+      g_off(c2, j2, k, g20, g21);
       xg_two(k, g10, g11, g20, g21);
-      advance(k);
     }
     {  // k == j1
+      begin_step(k);
       u32x4 g10, g11, g20, g21;
-      g_diag(c1, l1, al1, k, k & 1, g10, g11);
-      g_off(c2, j2, k, k & 1, g20, g21);
+      g_diag(c1, l1, al1, k, g10, g11);
+      g_off(c2, j2, k, g20, g21);
       scale_rows(acc1, u1);
+      add_skip(acc1, k);
       xg_two(k, g10, g11, g20, g21);
-      advance(k);
       ++k;
     }
 #pragma unroll 1
     for (; k < j2; ++k) {
+      begin_step(k);
       u32x4 g0, g1;
-      g_off(c2, j2, k, k & 1, g0, g1);
-      mfma_xg<TP>(acc2, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
-      advance(k);
+      g_off(c2, j2, k, g0, g1);
+      xg_one(acc2, k, g0, g1);
     }
     {  // k == j2
+      begin_step(k);
       u32x4 g0, g1;
-      g_diag(c2, l2, al2, k, k & 1, g0, g1);
+      g_diag(c2, l2, al2, k, g0, g1);
       scale_rows(acc2, u2);
-      mfma_xg<TP>(acc2, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
-      advance(k);
+      add_skip(acc2, k);
+      xg_one(acc2, k, g0, g1);
       ++k;
     }
   } else if (act1) {
 #pragma unroll 1
     for (; k < j1; ++k) {
+      begin_step(k);
       u32x4 g0, g1;
-      g_off(c1, j1, k, k & 1, g0, g1);
-      mfma_xg<TP>(acc1, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
-      advance(k);
+      g_off(c1, j1, k, g0, g1);
+      xg_one(acc1, k, g0, g1);
     }
     {  // k == j1
+      begin_step(k);
       u32x4 g0, g1;
-      g_diag(c1, l1, al1, k, k & 1, g0, g1);
+      g_diag(c1, l1, al1, k, g0, g1);
       scale_rows(acc1, u1);
-      mfma_xg<TP>(acc1, &xt[col][32 * k + 4 * kg], LDX, g0, g1);
-      advance(k);
+      add_skip(acc1, k);
+      xg_one(acc1, k, g0, g1);
       ++k;
     }
   }
 #pragma unroll 1
-  for (; k < nk; ++k) advance(k);
+  for (; k < nk; ++k) begin_step(k);
+  __syncthreads();  // every wavefront is done with the rings
 
-  // ---- skip term D x_l, in fp32 from the X^T still in LDS: a lane's
-  // accumulator rows p of column l are x[l][p] = xt[p][l]
-  const float Dh = Dv ? Dv[h] : 0.f;
-  auto add_skip = [&](f32x16 (&acc)[TP], int l) {
+  // ---- inter-chunk term, added last: exp(acum_l) C_l hprev^T (hprev landed
+  // before tile 0 did)
+  auto add_inter = [&](f32x16 (&acc)[TP], const u32x4 (&creg)[KN], float al) {
+    const float el = __expf(al);
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
+      const int row = t * 32 + col;
+      const unsigned char *hrow = smem + HS + row * (N * 2);
+      f32x16 v = f32x16{};
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const uint32_t bits = xt[t * 32 + acc_row(r, kg)][l];
-        acc[t][r] += Dh * __uint_as_float(bits << 16);
+      for (int q = 0; q < KN; ++q) {
+        const int cc = (2 * q + kg) ^ chunk_swz(row, NCB);
+        const u32x4 a = *reinterpret_cast<const u32x4 *>(hrow + cc * 16);
+        v = mfma32x32x16(as_bf16x8(a), as_bf16x8(creg[q]), v);
       }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[t][r] += el * v[r];
     }
   };
-  if (act1) add_skip(acc1, l1);
-  if (act2) add_skip(acc2, l2);
-  __syncthreads();  // X^T no longer needed: its bytes become output staging
+  if (act1) add_inter(acc1, c1, al1);
+  if (act2) add_inter(acc2, c2, al2);
+  __syncthreads();  // hprev consumed: all of smem becomes output staging
 
   // ---- epilogue: each wave stages its token tiles through its own LDS slice
   // as fp32 [token][p], rounds, and stores 16-byte row segments
@@ -634,7 +644,7 @@ static void launch_sc(const void *x, const void *B, const void *C, const float *
                       const Geometry &geo, hipStream_t stream) {
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
   const dim3 grid(xcd_grid(geo.nc_max, geo.H));
-  if constexpr (N <= 128) {
+  if constexpr (N <= 256) {
     hipLaunchKernelGGL((k_chunk_scan_lds<Q, P, N>), grid, dim3(Q), 0, stream,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                        static_cast<const uint16_t *>(C), D, acum, dtq,

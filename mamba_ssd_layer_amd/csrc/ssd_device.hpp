@@ -111,6 +111,34 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
+// ----------------------------------------------------------------- direct-to-LDS loads
+// gfx950 global_load_lds_dwordx4: each lane fetches 16 bytes from its own
+// global address; the wavefront's 64 chunks land contiguously in LDS at the
+// (wave-uniform) destination, lane i at +16 i.  Completion is tracked by
+// vmcnt only -- the compiler inserts no wait before LDS reads of the data, so
+// every use is preceded by an explicit wait_vmcnt and a barrier.
+__device__ __forceinline__ void load_lds16(const void *gsrc, unsigned char *lds_dst) {
+  __builtin_amdgcn_global_load_lds(gsrc, lds_dst, 16, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) leaving expcnt and lgkmcnt alone (gfx9 encoding:
+// vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane 4i+j receives
+// element j of the 4-element (8-byte) chunks addressed by lanes i, i+4, i+8,
+// i+12 of the group -- a 16 x 4 transpose of bf16 data in LDS.
+__device__ __forceinline__ u32x2 lds_read_tr16(const void *lds_src) {
+  typedef short i16x4 __attribute__((ext_vector_type(4)));
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4 *)(lds_src));
+  return __builtin_bit_cast(u32x2, v);
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_bcast(T v, int src) { return __shfl(v, src, 64); }
 
