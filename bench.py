@@ -132,6 +132,10 @@ def main() -> int:
     ap.add_argument("--workload", default="large_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="first run 3 elementwise copies (dst = -src, one read and one write per "
+                         "element) of MIB MiB: a known-size reference for the hardware byte "
+                         "counters")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -150,6 +154,16 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     dev = torch.device("cuda:0")
+    if args.calibrate_copy:
+        n = args.calibrate_copy << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"bench: copy calibration, 3 copies of {n} bytes ({args.calibrate_copy} MiB read + "
+            f"{args.calibrate_copy} MiB written each)")
+        del src, dst
     log(f"bench: generating workload {args.workload}")
     w = workloads.make_workload(args.workload)
     io = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -193,7 +207,7 @@ def main() -> int:
     wall = time.perf_counter() - wall0
     ms = ev0.elapsed_time(ev1) / args.steps
     value = T / (ms / 1e3)
-    log(f"bench: {ms * 1e3:.1f} us/step ({wall / args.steps * 1e3:.1f} us wall), "
+    log(f"bench: {ms * 1e3:.1f} us/step ({wall / args.steps * 1e6:.1f} us wall), "
         f"{value / 1e6:.1f} M tokens/s")
 
     # per-stage times: the same stages launched one by one, HIP events between
