@@ -636,48 +636,53 @@ __global__ __launch_bounds__(Q) void k_chunk_scan_regs(
 // ============================================================ head-batched kernel
 // Q = 256, P = 64, N <= 128.  The heads of a group share B and C, so Z = B C^T
 // of a chunk is the same for all of them: block = (chunk, group, run of hb
-// heads), one block per CU.  The block stages the chunk's B and C in LDS once,
-// forms the nine Z tiles of each wavefront (token tiles w and 7-w against
-// every source tile at or below them) and keeps them in registers.  Then it
-// walks its heads through a two-slot LDS ring for x (and acum, dt) and one
-// slot for hprev, per head:
-//   1. y of the previous head, staged over that head's x, goes out in
-//      128-byte row segments; the v table of this head is built;
-//   2. the next head's x goes out into the other slot;
-//   3. inter term first: Y^T = exp(acum at the tile's first token) Hprev C^T;
-//      then the next head's hprev goes out (it lands during step 4);
-//   4. intra term over the source tiles (u_l applied at the diagonal tile,
-//      which turns the step-3 factor into exp(acum_l)), skip term;
-//   5. the result is rounded to bf16 and staged over this head's x.
-// Four block barriers per head and no global-memory wait inside a head: each
-// load has a full step or more to land before the vmcnt(0) at the next top.
+// heads), one block of 8 wavefronts per CU.  Each wavefront owns one token
+// tile: wavefront w < 4 tile w, wavefront w >= 4 tile 11-w, so tiles j and 7-j
+// share a SIMD.  The causal work is balanced by handing pairs over: wavefront
+// s < 4 also forms the off-diagonal pairs (7-s, i < 4-s) and passes their sum
+// to the owner of tile 7-s through LDS, so every wavefront has 3 or 4
+// off-diagonal pairs and one diagonal pair.  Its five Z tiles (pairs formed
+// once per block from the chunk's B staged in LDS) and the C rows of its tile
+// stay in registers.  The block then walks its heads; x, acum, dt and hprev
+// of head i+1 stream into the other half of two-slot LDS rings while head i
+// computes, and y of head i, staged over its x as bf16, goes out at the top of
+// head i+1 in 128-byte row segments.  Per head:
+//   1. y of the previous head is stored; the v table of this head is built;
+//   2. the next head's loads go out;
+//   3. handed-over pairs (wavefronts 0-3), summed and written to LDS;
+//   4. inter term Y^T = exp(acum at the tile's first token) Hprev C^T, then
+//      the tile's own off-diagonal pairs;
+//   5. (barrier) the handed-over sum is added, u_l applied, then the diagonal
+//      pair and the skip term;
+//   6. (barrier) the tile is rounded to bf16 and staged over this head's x.
 template <int N>
-__global__ __launch_bounds__(256, 1) void k_chunk_scan_hb(
+__global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
     const uint16_t *__restrict__ Cm, const float *__restrict__ Dv, const float *__restrict__ acum,
     const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int nc,
     int H, int G, int hb, int nkb, uint16_t *__restrict__ y) {
   constexpr int Q = 256, P = 64;
   static_assert(N == 64 || N == 128, "head-batched tile shape");
-  constexpr int NT = 256;             // threads
-  constexpr int NW = 4;               // wavefronts
+  constexpr int NT = 512;             // threads
+  constexpr int NW = 8;               // wavefronts
   constexpr int NLT = Q / 32;         // token tiles
   constexpr int TP = P / 32;          // p tiles
   constexpr int KN = N / 16;          // K steps over n
-  constexpr int NCB = N / 8;          // 16-byte chunks per B / C / hprev row
+  constexpr int NCB = N / 8;          // 16-byte chunks per B / hprev row
   constexpr int NCX = P / 8;          // 16-byte chunks per x / y row
   constexpr int XB = Q * P * 2;       // x (then y) of one head
   constexpr int HB = P * N * 2;       // hprev of one head
   constexpr int ADB = 2 * Q * 4;      // acum and dt of one head
-  constexpr int CB = Q * N * 2;       // C of the chunk (and B, during the Z phase)
+  constexpr int BB = Q * N * 2;       // B of the chunk, Z phase only
+  constexpr int PSB = 32 * P * 4;     // one handed-over partial sum (fp32)
   constexpr int XI = XB / 1024 / NW;  // 1 KB direct loads per wavefront
   constexpr int HI = HB / 1024 / NW;
-  constexpr int CI = CB / 1024 / NW;
-  static_assert(XI * NW * 1024 == XB && HI * NW * 1024 == HB && CI * NW * 1024 == CB, "1 KB loads");
-  // [XS0][XS1][HS][AD0][AD1][VT][CS]; B is staged over XS0 + XS1
-  constexpr int XS0 = 0, XS1 = XB, HS = 2 * XB, AD0 = HS + HB, AD1 = AD0 + ADB;
-  constexpr int VT = AD1 + ADB, CS = VT + NLT * Q * 4, TOTAL = CS + CB;
-  static_assert(2 * XB >= CB, "B staging fits over the x ring");
+  constexpr int BI = BB / 1024 / NW;
+  static_assert(XI * NW * 1024 == XB && HI * NW * 1024 == HB && BI * NW * 1024 == BB, "1 KB loads");
+  // [XS0][XS1][HS0][HS1][AD0][AD1][VT][PS0..PS3]; B is staged over XS0 + XS1
+  constexpr int XS0 = 0, XS1 = XB, HS0 = 2 * XB, HS1 = HS0 + HB, AD0 = HS1 + HB, AD1 = AD0 + ADB;
+  constexpr int VT = AD1 + ADB, PS = VT + NLT * Q * 4, TOTAL = PS + 4 * PSB;
+  static_assert(2 * XB >= BB, "B staging fits over the x ring");
   __shared__ __align__(16) unsigned char smem[TOTAL];
 
   int c, hk;
@@ -692,53 +697,57 @@ __global__ __launch_bounds__(256, 1) void k_chunk_scan_hb(
   const ChunkInfo ci = chunk_info(geom, c);
   if (ci.len <= 0) return;
 
+  // Lane indices.  Inside the head loop they are re-read from an opaque copy
+  // each head, so the compiler forms lane-dependent addresses where they are
+  // used instead of keeping dozens of them live across heads.
+  struct Lane {
+    int tid, lane, col, kg;
+    __device__ explicit Lane(int t) : tid(t), lane(t & 63), col(t & 31), kg((t >> 5) & 1) {}
+  };
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int col = lane & 31;
-  const int kg = lane >> 5;
-  const int j1 = wave;             // 0 .. NLT/2-1
-  const int j2 = NLT - 1 - wave;   // NLT/2 .. NLT-1
-  const int l1 = j1 * 32 + col;
-  const int l2 = j2 * 32 + col;
+  const Lane L0(tid);
+  const int lane = L0.lane;
+  const int col = L0.col;
+  const int kg = L0.kg;
+  const int s4 = wave & 3;
+  const bool donor = wave < 4;
+  const int T = donor ? s4 : NLT - 1 - s4;  // own token tile
+  const int TD = NLT - 1 - s4;              // tile of the handed-over pairs
+  const int nd = donor ? 4 - s4 : 0;        // handed-over pairs: source tiles 0 .. nd-1 of TD
+  const int l = T * 32 + col;               // this lane's token (output column)
   const int64_t ldx = (int64_t)H * P;
   const int64_t ldb = (int64_t)G * N;
   const int64_t xrow0 = ci.t0 * ldx;
+  const int ldx32 = H * P;  // row offsets inside a chunk: Q * H * P < 2^31 (H < 2^16)
 
   // Direct loads, 16-byte chunks XOR-swizzled per row.  Token rows past the
   // chunk's end repeat its last row: finite data that dt = 0 cancels, in rows
   // of y that are never stored.
-  auto issue_x = [&](int hh, unsigned char *xs) {
+  auto issue_head = [&](const Lane &Ln, int hh, int slot) {
+    const int lane = Ln.lane;
     const uint16_t *xb = x + xrow0 + (int64_t)hh * P;
+    unsigned char *xs = smem + (slot ? XS1 : XS0);
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       const int m = (wave * XI + i) * 64 + lane;
       const int r = m / NCX, cc = (m % NCX) ^ chunk_swz(m / NCX, NCX);
-      load_lds16(xb + (int64_t)min(r, ci.len - 1) * ldx + cc * 8, xs + (wave * XI + i) * 1024);
+      load_lds16(xb + min(r, ci.len - 1) * ldx32 + cc * 8, xs + (wave * XI + i) * 1024);
     }
-  };
-  auto issue_rows_n = [&](const uint16_t *src, unsigned char *dst) {  // B or C of the chunk
-#pragma unroll
-    for (int i = 0; i < CI; ++i) {
-      const int m = (wave * CI + i) * 64 + lane;
-      const int r = m / NCB, cc = (m % NCB) ^ chunk_swz(m / NCB, NCB);
-      load_lds16(src + (int64_t)min(r, ci.len - 1) * ldb + cc * 8, dst + (wave * CI + i) * 1024);
-    }
-  };
-  auto issue_hprev = [&](int hh) {
-    const uint16_t *hp = hprev + ((int64_t)c * H + hh) * (P * N);
+    const int64_t ch = (int64_t)c * H + hh;
+    const uint16_t *hp = hprev + ch * (P * N);
+    unsigned char *hs = smem + (slot ? HS1 : HS0);
 #pragma unroll
     for (int i = 0; i < HI; ++i) {
       const int m = (wave * HI + i) * 64 + lane;
       const int r = m / NCB, cc = (m % NCB) ^ chunk_swz(m / NCB, NCB);
-      load_lds16(hp + r * N + cc * 8, smem + HS + (wave * HI + i) * 1024);
+      load_lds16(hp + r * N + cc * 8, hs + (wave * HI + i) * 1024);
     }
+    if (wave < 2)  // wavefront 0: acum, 1: dt
+      load_lds16((wave == 0 ? acum : dtq) + ch * Q + lane * 4, smem + (slot ? AD1 : AD0) + wave * 1024);
   };
-  auto issue_ad = [&](int hh, unsigned char *ad) {  // wave 0: acum, wave 1: dt
-    if (wave < 2)
-      load_lds16((wave == 0 ? acum : dtq) + ((int64_t)c * H + hh) * Q + lane * 4, ad + wave * 1024);
-  };
-  auto store_y = [&](int hh, const unsigned char *ys) {
+  auto store_y = [&](const Lane &Ln, int hh, const unsigned char *ys) {
+    const int tid = Ln.tid;
     uint16_t *yb = y + xrow0 + (int64_t)hh * P;
 #pragma unroll
     for (int i = 0; i < Q * NCX / NT; ++i) {
@@ -746,52 +755,58 @@ __global__ __launch_bounds__(256, 1) void k_chunk_scan_hb(
       const int r = u / NCX, gp = u % NCX;
       if (r < ci.len) {
         const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + r * (P * 2) + (gp ^ chunk_swz(r, NCX)) * 16);
-        *reinterpret_cast<u32x4 *>(yb + (int64_t)r * ldx + gp * 8) = v;
+        *reinterpret_cast<u32x4 *>(yb + r * ldx32 + gp * 8) = v;
       }
     }
   };
-  // C_l operand (B of the MFMA): lane (col, kg) holds n = 16q + 8kg .. +7 of row l
-  auto c_op = [&](int l, int q) {
-    const int cc = (2 * q + kg) ^ chunk_swz(l, NCB);
-    return *reinterpret_cast<const u32x4 *>(smem + CS + l * (N * 2) + cc * 16);
-  };
 
-  // ---- Z phase
-  issue_rows_n(Bm + ci.t0 * ldb + (int64_t)g * N, smem + XS0);
-  issue_rows_n(Cm + ci.t0 * ldb + (int64_t)g * N, smem + CS);
-  issue_hprev(hfirst);
-  issue_ad(hfirst, smem + AD0);
+  // ---- Z phase: the chunk's B, head 0's data, and the C rows of the lane's
+  // own and handed-over tiles (registers)
+  {
+    const uint16_t *bb = Bm + ci.t0 * ldb + (int64_t)g * N;
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int m = (wave * BI + i) * 64 + lane;
+      const int r = m / NCB, cc = (m % NCB) ^ chunk_swz(m / NCB, NCB);
+      load_lds16(bb + (int64_t)min(r, ci.len - 1) * ldb + cc * 8, smem + XS0 + (wave * BI + i) * 1024);
+    }
+  }
+  const uint16_t *cbase = Cm + ci.t0 * ldb + (int64_t)g * N + kg * 8;
+  u32x4 cown[KN], cdon[KN];
+  load_rows<KN>(cown, cbase + (int64_t)l * ldb, l < ci.len);
+  load_rows<KN>(cdon, cbase + (int64_t)(TD * 32 + col) * ldb, TD * 32 + col < ci.len);
   wait_vmcnt<0>();
   __syncthreads();
-  // Slot k holds token tile j2 against source tile k for k <= j2, and token
-  // tile j1 against source tile NLT-k above that.  Each slot's operands are
-  // picked by address, with no branches, so every tile is formed in the
-  // registers it stays in.
-  f32x16 z[NLT + 1];
+  // slot k < 4: handed-over pair (TD, k) for k < nd, else own off-diagonal
+  // pair (T, k - nd) on a donor and (T, T - 3 + k) on a receiver (k = 3 unused
+  // there); slot 4: the diagonal pair (T, T).  Operands are picked by value,
+  // with no branches, so each tile is formed in the registers it stays in.
+  f32x16 z[5];
 #pragma unroll
-  for (int k = 0; k <= NLT; ++k) {
-    const bool second = k <= j2;
-    const int i = second ? k : NLT - k;
-    const int l = second ? l2 : l1;
-    const unsigned char *brow = smem + XS0 + (32 * i + col) * (N * 2);
+  for (int k = 0; k < 5; ++k) {
+    const bool dk = k < nd;
+    const int zi = k == 4 ? T : (donor ? (dk ? k : k - nd) : min(T - 3 + k, T));
+    const unsigned char *brow = smem + XS0 + (32 * zi + col) * (N * 2);
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int q = 0; q < KN; ++q) {
       const int cc = (2 * q + kg) ^ chunk_swz(col, NCB);
-      const u32x4 b = *reinterpret_cast<const u32x4 *>(brow + cc * 16);
-      acc = mfma32x32x16(as_bf16x8(b), as_bf16x8(c_op(l, q)), acc);
+      const u32x4 bq = *reinterpret_cast<const u32x4 *>(brow + cc * 16);
+      const u32x4 cq = dk ? cdon[q] : cown[q];
+      acc = mfma32x32x16(as_bf16x8(bq), as_bf16x8(cq), acc);
     }
     z[k] = acc;
   }
   __syncthreads();  // B consumed: the x ring is free
-  issue_x(hfirst, smem + XS0);
+  issue_head(L0, hfirst, 0);
 
   // X^T operands of source tile i by transposing LDS reads: lane (gq = lane/16,
   // d = lane%16) addresses token row 32i + 8h4 + 4kg + d/4, columns 4(d%4)..,
   // and receives p = 32t + 16(gq%2) + d of 4 consecutive tokens -- the K order
   // of the accumulator rows of G (offsets 4kg.., 8+4kg.., 16+4kg.., 24+4kg..)
-  auto x_ops = [&](const unsigned char *xs, int i, int t, u32x4 &xa, u32x4 &xb) {
-    const int gq = lane >> 4, d = lane & 15;
+  auto x_ops = [&](const Lane &Ln, const unsigned char *xs, int i, int t, u32x4 &xa, u32x4 &xb) {
+    const int kg = Ln.kg;
+    const int gq = Ln.lane >> 4, d = Ln.lane & 15;
     const int p0 = t * 32 + 16 * (gq & 1) + 4 * (d & 3);
     u32x2 part[4];
 #pragma unroll
@@ -803,24 +818,145 @@ __global__ __launch_bounds__(256, 1) void k_chunk_scan_hb(
     xa = u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
     xb = u32x4{part[2].x, part[2].y, part[3].x, part[3].y};
   };
-  // D x_l in fp32: the lane's accumulator rows p = 32t + 8rb + 4kg + e of
-  // column l are 4 consecutive elements of x row l
-  auto add_skip = [&](f32x16 (&acc)[TP], const unsigned char *xs, int l, float Dh) {
+  // acc += X_i^T G^T with G = the decayed, bf16-rounded Z tile
+  auto pair_xg = [&](const Lane &Ln, f32x16 (&acc)[TP], const unsigned char *xs, int i,
+                     const float (&gv)[16]) {
+    u32x4 g0, g1;
+    pack_g(gv, g0, g1);
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
-#pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int p = t * 32 + rb * 8 + kg * 4;
-        const int cc = (p >> 3) ^ chunk_swz(l, NCX);
-        const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + l * (P * 2) + cc * 16 + (p & 7) * 2);
-        acc[t][rb * 4 + 0] += Dh * bf16lo(xv.x);
-        acc[t][rb * 4 + 1] += Dh * bf16hi(xv.x);
-        acc[t][rb * 4 + 2] += Dh * bf16lo(xv.y);
-        acc[t][rb * 4 + 3] += Dh * bf16hi(xv.y);
-      }
+      u32x4 xa, xb;
+      x_ops(Ln, xs, i, t, xa, xb);
+      acc[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g0), acc[t]);
+      acc[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g1), acc[t]);
     }
   };
-  auto stage_y = [&](const f32x16 (&acc)[TP], int l, unsigned char *ys) {
+
+#pragma unroll 1
+  for (int hi = 0; hi < nh; ++hi) {
+    const int hh = hfirst + hi;
+    const int slot = hi & 1;
+    unsigned char *xs = smem + (slot ? XS1 : XS0);
+    const unsigned char *hs = smem + (slot ? HS1 : HS0);
+    const float *sa = reinterpret_cast<const float *>(smem + (slot ? AD1 : AD0));
+    const float *sd = sa + Q;
+    float *vt = reinterpret_cast<float *>(smem + VT);  // vt[j][s] = exp(acum[32j] - acum[s]) dt[s]
+
+    int tid_o = tid;
+    asm volatile("" : "+v"(tid_o));
+    const Lane Lh(tid_o);
+    const int lane = Lh.lane, col = Lh.col, kg = Lh.kg;
+    const int l = T * 32 + col;
+
+    wait_vmcnt<0>();  // this head's loads; the stores of y two heads back
+    __syncthreads();  // ... for every thread; the previous head is done everywhere
+    if (hi > 0) store_y(Lh, hh - 1, smem + (slot ? XS0 : XS1));
+    {  // column s = tid % Q, rows j in this thread's half
+      const int s = tid_o & (Q - 1);
+      const float as = sa[s], ds = sd[s];
+#pragma unroll
+      for (int jj = 1; jj <= NLT / 2; ++jj) {
+        const int j = tid_o < Q ? jj : jj + NLT / 2 - 1;
+        if (j < NLT && s < 32 * j) vt[j * Q + s] = __expf(sa[32 * j] - as) * ds;
+      }
+    }
+    __syncthreads();  // v table ready; the other slot's y has been read out
+    if (hi + 1 < nh) issue_head(Lh, hh + 1, slot ^ 1);
+
+    f32x16 acc[TP];
+    // 3. handed-over pairs (donors): sum over source tiles 0 .. nd-1 of tile TD
+    if (donor) {
+#pragma unroll
+      for (int t = 0; t < TP; ++t) acc[t] = f32x16{};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        if (k < nd) {
+          float gv[16];
+          decay_offdiag_v(z[k], vt + TD * Q + 32 * k, kg, gv);
+          pair_xg(Lh, acc, xs, k, gv);
+        }
+      }
+      float *ps = reinterpret_cast<float *>(smem + PS + s4 * PSB);
+#pragma unroll
+      for (int t = 0; t < TP; ++t)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb)
+          *reinterpret_cast<f32x4 *>(ps + ((t * 4 + rb) * 64 + lane) * 4) =
+              f32x4{acc[t][rb * 4], acc[t][rb * 4 + 1], acc[t][rb * 4 + 2], acc[t][rb * 4 + 3]};
+    }
+    // 4. inter term, scaled by exp(acum at the tile's first token), then the
+    // tile's own off-diagonal pairs
+    const float al = sa[l];
+    const float m0 = sa[32 * T];
+#pragma unroll
+    for (int t = 0; t < TP; ++t) acc[t] = f32x16{};
+#pragma unroll
+    for (int q = 0; q < KN; ++q) {
+#pragma unroll
+      for (int t = 0; t < TP; ++t) {
+        const int row = t * 32 + col;
+        const int cc = (2 * q + kg) ^ chunk_swz(row, NCB);
+        const u32x4 hq = *reinterpret_cast<const u32x4 *>(hs + row * (N * 2) + cc * 16);
+        acc[t] = mfma32x32x16(as_bf16x8(hq), as_bf16x8(cown[q]), acc[t]);
+      }
+    }
+    {
+      const float em = __expf(m0);
+#pragma unroll
+      for (int t = 0; t < TP; ++t) acc[t] *= em;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const bool own = donor ? k >= nd : k < 3;
+      if (own) {
+        const int i = donor ? k - nd : T - 3 + k;
+        float gv[16];
+        decay_offdiag_v(z[k], vt + T * Q + 32 * i, kg, gv);
+        pair_xg(Lh, acc, xs, i, gv);
+      }
+    }
+    __syncthreads();  // handed-over sums are in LDS
+    // 5. handed-over sum (receivers), u_l, the diagonal pair, the skip term
+    if (!donor) {
+      const float *ps = reinterpret_cast<const float *>(smem + PS + s4 * PSB);
+#pragma unroll
+      for (int t = 0; t < TP; ++t)
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(ps + ((t * 4 + rb) * 64 + lane) * 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[t][rb * 4 + e] += v[e];
+        }
+    }
+    {
+      const float u = __expf(al - m0);  // <= 1
+#pragma unroll
+      for (int t = 0; t < TP; ++t) acc[t] *= u;
+    }
+    {
+      float gv[16];
+      decay_diag(z[4], al, l, 32 * T, kg, sa, sd, gv);
+      pair_xg(Lh, acc, xs, T, gv);
+    }
+    {  // D x_l in fp32: rows p = 32t + 8rb + 4kg + e of column l are 4
+       // consecutive elements of x row l
+      const float Dh = Dv ? Dv[hh] : 0.f;
+#pragma unroll
+      for (int t = 0; t < TP; ++t) {
+#pragma unroll
+        for (int rb = 0; rb < 4; ++rb) {
+          const int p = t * 32 + rb * 8 + kg * 4;
+          const int cc = (p >> 3) ^ chunk_swz(l, NCX);
+          const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + l * (P * 2) + cc * 16 + (p & 7) * 2);
+          acc[t][rb * 4 + 0] += Dh * bf16lo(xv.x);
+          acc[t][rb * 4 + 1] += Dh * bf16hi(xv.x);
+          acc[t][rb * 4 + 2] += Dh * bf16lo(xv.y);
+          acc[t][rb * 4 + 3] += Dh * bf16hi(xv.y);
+        }
+      }
+    }
+    __syncthreads();  // this head's x and the handed-over sums read by everyone
+    // 6. stage y over this head's x
 #pragma unroll
     for (int t = 0; t < TP; ++t) {
 #pragma unroll
@@ -829,114 +965,12 @@ __global__ __launch_bounds__(256, 1) void k_chunk_scan_hb(
         u32x2 o;
         o.x = pack_bf16x2(acc[t][rb * 4 + 0], acc[t][rb * 4 + 1]);
         o.y = pack_bf16x2(acc[t][rb * 4 + 2], acc[t][rb * 4 + 3]);
-        *reinterpret_cast<u32x2 *>(ys + l * (P * 2) + ((p >> 3) ^ chunk_swz(l, NCX)) * 16 + (p & 7) * 2) = o;
+        *reinterpret_cast<u32x2 *>(xs + l * (P * 2) + ((p >> 3) ^ chunk_swz(l, NCX)) * 16 + (p & 7) * 2) = o;
       }
     }
-  };
-  auto mfma_g = [&](f32x16 (&acc)[TP], const u32x4 (&xa)[TP], const u32x4 (&xb)[TP],
-                    const float (&gv)[16]) {
-    u32x4 g0, g1;
-    pack_g(gv, g0, g1);
-#pragma unroll
-    for (int t = 0; t < TP; ++t) {
-      acc[t] = mfma32x32x16(as_bf16x8(xa[t]), as_bf16x8(g0), acc[t]);
-      acc[t] = mfma32x32x16(as_bf16x8(xb[t]), as_bf16x8(g1), acc[t]);
-    }
-  };
-
-#pragma unroll 1
-  for (int hi = 0; hi < nh; ++hi) {
-    const int hh = hfirst + hi;
-    unsigned char *xs = smem + ((hi & 1) ? XS1 : XS0);
-    unsigned char *xo = smem + ((hi & 1) ? XS0 : XS1);
-    const float *sa = reinterpret_cast<const float *>(smem + ((hi & 1) ? AD1 : AD0));
-    const float *sd = sa + Q;
-    float *vt = reinterpret_cast<float *>(smem + VT);  // vt[j][s] = exp(acum[32j] - acum[s]) dt[s]
-
-    wait_vmcnt<0>();  // x, acum, dt, hprev of this head; stores of y two heads back
-    __syncthreads();  // ... for every thread; the previous head is done everywhere
-    if (hi > 0) store_y(hh - 1, xo);
-    for (int idx = tid; idx < NLT * Q; idx += NT) {
-      const int j = idx / Q;
-      const int s = idx - j * Q;
-      if (s < 32 * j) vt[idx] = __expf(sa[32 * j] - sa[s]) * sd[s];
-    }
-    __syncthreads();  // v table ready; the other slot's y has been read out
-    if (hi + 1 < nh) {
-      issue_x(hh + 1, xo);
-      issue_ad(hh + 1, smem + ((hi & 1) ? AD0 : AD1));
-    }
-
-    const float al1 = sa[l1], al2 = sa[l2];
-    const float m1 = sa[32 * j1], m2 = sa[32 * j2];
-    const float Dh = Dv ? Dv[hh] : 0.f;
-    f32x16 acc1[TP], acc2[TP];
-#pragma unroll
-    for (int t = 0; t < TP; ++t) {
-      acc1[t] = f32x16{};
-      acc2[t] = f32x16{};
-    }
-    // inter term: Y^T = Hprev . C^T, scaled by exp(acum at the tile's first token)
-#pragma unroll
-    for (int q = 0; q < KN; ++q) {
-      const u32x4 cq1 = c_op(l1, q), cq2 = c_op(l2, q);
-#pragma unroll
-      for (int t = 0; t < TP; ++t) {
-        const int row = t * 32 + col;
-        const int cc = (2 * q + kg) ^ chunk_swz(row, NCB);
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(smem + HS + row * (N * 2) + cc * 16);
-        acc1[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(cq1), acc1[t]);
-        acc2[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(cq2), acc2[t]);
-      }
-    }
-    {
-      const float e1 = __expf(m1), e2 = __expf(m2);
-#pragma unroll
-      for (int t = 0; t < TP; ++t) {
-        acc1[t] *= e1;
-        acc2[t] *= e2;
-      }
-    }
-    __syncthreads();  // hprev consumed
-    if (hi + 1 < nh) issue_hprev(hh + 1);
-
-    // intra term; u_l = exp(acum_l - acum at the tile's first token) <= 1
-    const float u1 = __expf(al1 - m1);
-    const float u2 = __expf(al2 - m2);
-#pragma unroll
-    for (int i = 0; i < NLT; ++i) {
-      if (i > j2) break;
-      u32x4 xa[TP], xb[TP];
-#pragma unroll
-      for (int t = 0; t < TP; ++t) x_ops(xs, i, t, xa[t], xb[t]);
-      float gv[16];
-      if (i >= NLT / 2 && i == j2) {
-#pragma unroll
-        for (int t = 0; t < TP; ++t) acc2[t] *= u2;
-        add_skip(acc2, xs, l2, Dh);
-        decay_diag(z[i], al2, l2, 32 * i, kg, sa, sd, gv);
-      } else {
-        decay_offdiag_v(z[i], vt + j2 * Q + 32 * i, kg, gv);
-      }
-      mfma_g(acc2, xa, xb, gv);
-      if (i < NLT / 2 && i <= j1) {
-        if (i == j1) {
-#pragma unroll
-          for (int t = 0; t < TP; ++t) acc1[t] *= u1;
-          add_skip(acc1, xs, l1, Dh);
-          decay_diag(z[NLT - i], al1, l1, 32 * i, kg, sa, sd, gv);
-        } else {
-          decay_offdiag_v(z[NLT - i], vt + j1 * Q + 32 * i, kg, gv);
-        }
-        mfma_g(acc1, xa, xb, gv);
-      }
-    }
-    __syncthreads();  // this head's x read by everyone
-    stage_y(acc1, l1, xs);
-    stage_y(acc2, l2, xs);
   }
   __syncthreads();
-  store_y(hfirst + nh - 1, smem + (((nh - 1) & 1) ? XS1 : XS0));
+  store_y(L0, hfirst + nh - 1, smem + (((nh - 1) & 1) ? XS1 : XS0));
 }
 
 }  // namespace
@@ -988,7 +1022,7 @@ static void launch_sc(const void *x, const void *B, const void *C, const float *
   if constexpr (Q == 256 && P == 64 && N <= 128) {
     int nkb = 1;
     const int hb = pick_heads_per_block(geo.nc_max, geo.H, geo.G, device_cus(), nkb);
-    hipLaunchKernelGGL((k_chunk_scan_hb<N>), dim3(xcd_grid(geo.nc_max, geo.G * nkb)), dim3(256), 0,
+    hipLaunchKernelGGL((k_chunk_scan_hb<N>), dim3(xcd_grid(geo.nc_max, geo.G * nkb)), dim3(512), 0,
                        stream, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                        static_cast<const uint16_t *>(C), D, acum, dtq,
                        static_cast<const uint16_t *>(hprev), cg, (int)geo.nc_max, geo.H, geo.G, hb,
