@@ -11,40 +11,31 @@
 // Algorithm", item 1); the second is the inter-chunk hand-off of item 2, with
 // the in-chunk decay exp(acum_l) that the page's listing leaves out.
 //
-// Shared design (block = (chunk, head), Q/64 wavefronts, XCD-aware order).
-// The output is formed transposed, Y^T [P x Q], as 32x32 MFMA tiles
-// (M = p, N = l), the chunk cut into Q/32 token tiles:
-//   * wavefront w owns the token tiles w and Q/32-1-w (balanced causal work)
-//     and keeps their C rows as MFMA B-operands in registers;
-//   * inter term: Y^T += Hprev . C^T over K = n, then each lane scales by
-//     exp(acum_l) -- a lane owns one output column l;
+// Shared design.  The output is formed transposed, Y^T [P x Q], as 32x32
+// MFMA tiles (M = p, N = l), the chunk cut into Q/32 token tiles:
+//   * inter term: Y^T += Hprev . C^T over K = n, then each lane scales by the
+//     decay of its token -- a lane owns one output column l;
 //   * intra term, per source tile k <= j: Z = B_k . C_j^T on MFMA, the decay
 //     mask applied to Z in registers, the fp32 accumulator rounded to bf16 and
 //     used directly as the B-operand of Y^T += X_k^T . G^T: that MFMA's K order
-//     is permuted to the accumulator's row order and X^T is read from LDS in the
-//     same order, so no cross-lane shuffle is needed;
+//     is permuted to the accumulator's row order and X^T is read from LDS in
+//     the same order (a transposing LDS read), so no cross-lane shuffle is
+//     needed;
 //   * decay: off the diagonal (k < j) exp(acum_l - acum_s) is split at
 //     m = acum at the token tile's first token into u_l = exp(acum_l - m) (one
-//     per lane) and v_s = exp(m - acum_s) dt_s (a per-chunk table in LDS); both
-//     are <= 1 for non-increasing acum, so nothing overflows.  Diagonal tiles
-//     take exp(acum_l - acum_s) per element, masked to s <= l before the
-//     exponent is formed.  (The LDS-staged kernel also takes u_l out of the
-//     sum over off-diagonal tiles, leaving one multiply per element there.)
+//     per lane, taken out of the sum over off-diagonal tiles) and
+//     v_s = exp(m - acum_s) dt_s (a per-chunk table in LDS); both are <= 1 for
+//     non-increasing acum, so nothing overflows.  Diagonal tiles take
+//     exp(acum_l - acum_s) per element, masked to s <= l before the exponent
+//     is formed.
 //
-// k_chunk_scan_lds (N <= 128): MFMA operands come from LDS, filled with
-// coalesced loads, instead of one cache line per lane.  At the start the block
-// stages X^T of the whole chunk (transposed on the way in) and hprev, so the
-// HBM reads are in flight together; then it walks the source tiles in
-// lockstep with B tiles (L2-resident, shared by the heads of a group)
-// double-buffered one tile ahead; when a wavefront has both its token tiles
-// in play, their MFMA chains share the B and X operand reads.  Only when the
-// loop is done do the outputs leave: D x_l is added in fp32 from the X^T
-// still in LDS, then each wavefront stages its tiles through its own LDS
-// slice and writes full 16-byte row segments -- no store is in flight while
-// the loop waits on its tile loads, and x is read from memory only once.
-// k_chunk_scan_regs (N = 256, whose C operands of two token tiles would not fit
-// in registers): one token tile at a time, X^T for the whole chunk in LDS,
-// B operands read straight from global memory.
+// Two kernels share this arithmetic:
+//   * k_chunk_scan_hb (Q = 256, P = 64, N <= 128): one block per CU walks a
+//     run of heads of one chunk; Z is formed once and kept in registers, and
+//     x / hprev of the next head stream in while the current one computes.
+//   * k_chunk_scan_lds (other shapes): block = (chunk, head) in XCD-aware
+//     order; B and x tiles stream through LDS rings filled by direct-to-LDS
+//     loads, Z is formed per head.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -57,17 +48,6 @@ __device__ __forceinline__ void load_rows(u32x4 (&dst)[KN], const uint16_t *row,
 #pragma unroll
   for (int q = 0; q < KN; ++q)
     dst[q] = valid ? *reinterpret_cast<const u32x4 *>(row + q * 16) : u32x4{0u, 0u, 0u, 0u};
-}
-
-// Off-diagonal decay: g = z * u_l * v[s] for the lane's 16 accumulator rows.
-__device__ __forceinline__ void decay_offdiag(const f32x16 &z, float ul, const float *vrow, int kg,
-                                              float (&gv)[16]) {
-#pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
-    const f32x4 v = *reinterpret_cast<const f32x4 *>(vrow + 8 * rb + 4 * kg);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) gv[rb * 4 + e] = z[rb * 4 + e] * (ul * v[e]);
-  }
 }
 
 // Off-diagonal decay with the per-lane factor taken out of the sum: g = z * v[s].
@@ -111,25 +91,6 @@ __device__ __forceinline__ void pack_g(const float (&gv)[16], u32x4 &g0, u32x4 &
   g1.w = pack_bf16x2(gv[14], gv[15]);
 }
 
-// Y^T += X^T . G^T for one source tile: X^T rows p = 32t + col, read in the K
-// order of the accumulator rows (offsets {4kg..4kg+3, 8+4kg..}, then +16).
-template <int TP>
-__device__ __forceinline__ void mfma_xg(f32x16 (&acc)[TP], const uint16_t *xrow0, int ld,
-                                        const u32x4 &g0, const u32x4 &g1) {
-#pragma unroll
-  for (int t = 0; t < TP; ++t) {
-    const uint16_t *xr = xrow0 + t * 32 * ld;
-    const u32x2 a0 = *reinterpret_cast<const u32x2 *>(xr);
-    const u32x2 a1 = *reinterpret_cast<const u32x2 *>(xr + 8);
-    const u32x2 b0 = *reinterpret_cast<const u32x2 *>(xr + 16);
-    const u32x2 b1 = *reinterpret_cast<const u32x2 *>(xr + 24);
-    const u32x4 xa{a0.x, a0.y, a1.x, a1.y};
-    const u32x4 xb{b0.x, b0.y, b1.x, b1.y};
-    acc[t] = mfma32x32x16(as_bf16x8(xa), as_bf16x8(g0), acc[t]);
-    acc[t] = mfma32x32x16(as_bf16x8(xb), as_bf16x8(g1), acc[t]);
-  }
-}
-
 // ============================================================ LDS-staged kernel
 // 16-byte chunk swizzle of an LDS tile row of `nc` chunks, so that 16 lanes
 // reading the same chunk column of 16 consecutive rows hit distinct banks.
@@ -137,6 +98,15 @@ __device__ __forceinline__ constexpr int chunk_swz(int row, int nc) {
   return nc >= 16 ? (row & 15) : ((row >> 1) & (nc - 1));
 }
 
+// Block = (chunk, head), Q/64 wavefronts; wavefront w owns token tiles w and
+// Q/32-1-w (balanced causal work) and keeps their C rows in registers.  The
+// source tiles go by in lockstep: B and x tiles of 32 tokens stream through
+// DEPTH-slot LDS rings filled by direct-to-LDS loads issued DEPTH-1 tiles
+// ahead; each step waits for its own tile only, then a block barrier.  When a
+// wavefront has both token tiles in play their MFMA chains share the operand
+// reads.  hprev is staged once; the inter term and D x are added after the
+// loop, and each wavefront writes its tiles through an LDS slice as 16-byte
+// row segments.
 template <int Q, int P, int N>
 __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
@@ -486,152 +456,6 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
   if (act1) epilogue(acc1, j1);
   if (act2) epilogue(acc2, j2);
 }
-
-// ============================================================ register-resident kernel
-template <int Q, int P, int N>
-__global__ __launch_bounds__(Q) void k_chunk_scan_regs(
-    const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
-    const uint16_t *__restrict__ Cm, const float *__restrict__ Dv, const float *__restrict__ acum,
-    const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int nc,
-    int H, int G, uint16_t *__restrict__ y) {
-  static_assert(P % 32 == 0 && N % 16 == 0 && Q % 64 == 0, "tile shape");
-  constexpr int NT = Q;          // threads
-  constexpr int NLT = Q / 32;    // token tiles
-  constexpr int TP = P / 32;     // p tiles
-  constexpr int KN = N / 16;     // K steps over n
-  constexpr int LDX = Q + 4;     // padded LDS row of X^T (bf16 elements)
-
-  __shared__ __align__(16) uint16_t xt[P][LDX];
-  __shared__ __align__(16) float sa[Q];
-  __shared__ __align__(16) float sd[Q];
-  __shared__ __align__(16) float vt[NLT][Q];
-
-  int c, h;
-  xcd_chunk_head(H, c, h);
-  if (c >= nc) return;
-  const int g = h / (H / G);
-  const ChunkInfo ci = chunk_info(geom, c);
-  if (ci.len <= 0) return;
-  const int64_t ch = (int64_t)c * H + h;
-
-  for (int l = threadIdx.x; l < Q; l += NT) {
-    sa[l] = acum[ch * Q + l];
-    sd[l] = dtq[ch * Q + l];
-  }
-  const int64_t ldx = (int64_t)H * P;
-  const uint16_t *xbase = x + ci.t0 * ldx + (int64_t)h * P;
-  {
-    constexpr int RQ = Q / 4;
-    constexpr int UNITS = RQ * (P / 8);
-    for (int u = threadIdx.x; u < UNITS; u += NT) {
-      const int rq = u % RQ;
-      const int cb = u / RQ;
-      const int l0 = rq * 4;
-      u32x4 r[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        r[i] = l0 + i < ci.len
-                   ? *reinterpret_cast<const u32x4 *>(xbase + (int64_t)(l0 + i) * ldx + cb * 8)
-                   : u32x4{0u, 0u, 0u, 0u};
-      }
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        u32x2 lo, hi;
-        lo.x = pair_lo(r[0][m], r[1][m]);
-        lo.y = pair_lo(r[2][m], r[3][m]);
-        hi.x = pair_hi(r[0][m], r[1][m]);
-        hi.y = pair_hi(r[2][m], r[3][m]);
-        *reinterpret_cast<u32x2 *>(&xt[cb * 8 + 2 * m][l0]) = lo;
-        *reinterpret_cast<u32x2 *>(&xt[cb * 8 + 2 * m + 1][l0]) = hi;
-      }
-    }
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < NLT * Q; idx += NT) {
-    const int j = idx / Q;
-    const int s = idx - j * Q;
-    if (s < 32 * j) vt[j][s] = __expf(sa[32 * j] - sa[s]) * sd[s];
-  }
-  __syncthreads();
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 31;
-  const int kg = lane >> 5;
-  const float Dh = Dv ? Dv[h] : 0.f;
-  const uint16_t *hp = hprev + ch * (int64_t)P * N;
-  const int64_t ldb = (int64_t)G * N;
-  const uint16_t *bbase = Bm + ci.t0 * ldb + (int64_t)g * N + kg * 8;
-  const uint16_t *cbase = Cm + ci.t0 * ldb + (int64_t)g * N + kg * 8;
-
-#pragma unroll 1
-  for (int jj = 0; jj < 2; ++jj) {
-    const int j = jj == 0 ? wave : NLT - 1 - wave;
-    const int l = j * 32 + col;
-    const bool lvalid = l < ci.len;
-
-    u32x4 creg[KN];
-    load_rows<KN>(creg, cbase + (int64_t)l * ldb, lvalid);
-    f32x16 acc[TP];
-#pragma unroll
-    for (int t = 0; t < TP; ++t) acc[t] = f32x16{};
-#pragma unroll
-    for (int t = 0; t < TP; ++t) {
-#pragma unroll
-      for (int q = 0; q < KN; ++q) {
-        const u32x4 a =
-            *reinterpret_cast<const u32x4 *>(hp + (int64_t)(t * 32 + col) * N + q * 16 + kg * 8);
-        acc[t] = mfma32x32x16(as_bf16x8(a), as_bf16x8(creg[q]), acc[t]);
-      }
-    }
-    const float al = sa[l];
-    const float el = __expf(al);
-#pragma unroll
-    for (int t = 0; t < TP; ++t) acc[t] *= el;
-    const float ul = __expf(al - sa[32 * j]);
-
-#pragma unroll 1
-    for (int k = 0; k <= j; ++k) {
-      const int s0 = k * 32;
-      u32x4 bcur[KN];
-      load_rows<KN>(bcur, bbase + (int64_t)(s0 + col) * ldb, s0 + col < ci.len);
-      f32x16 z = f32x16{};
-#pragma unroll
-      for (int q = 0; q < KN; ++q) z = mfma32x32x16(as_bf16x8(bcur[q]), as_bf16x8(creg[q]), z);
-      float gv[16];
-      if (k < j) {
-        decay_offdiag(z, ul, &vt[j][s0], kg, gv);
-      } else {
-        decay_diag(z, al, l, s0, kg, sa, sd, gv);
-      }
-      u32x4 g0, g1;
-      pack_g(gv, g0, g1);
-      mfma_xg<TP>(acc, &xt[col][s0 + 4 * kg], LDX, g0, g1);
-    }
-
-    if (lvalid) {
-      const uint16_t *xrow = xbase + (int64_t)l * ldx;
-      uint16_t *yrow = y + (ci.t0 + l) * ldx + (int64_t)h * P;
-#pragma unroll
-      for (int t = 0; t < TP; ++t) {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          const int p = t * 32 + rb * 8 + kg * 4;
-          const u32x2 xv = *reinterpret_cast<const u32x2 *>(xrow + p);
-          const float v0 = acc[t][rb * 4 + 0] + Dh * bf16lo(xv.x);
-          const float v1 = acc[t][rb * 4 + 1] + Dh * bf16hi(xv.x);
-          const float v2 = acc[t][rb * 4 + 2] + Dh * bf16lo(xv.y);
-          const float v3 = acc[t][rb * 4 + 3] + Dh * bf16hi(xv.y);
-          u32x2 o;
-          o.x = pack_bf16x2(v0, v1);
-          o.y = pack_bf16x2(v2, v3);
-          *reinterpret_cast<u32x2 *>(yrow + p) = o;
-        }
-      }
-    }
-  }
-}
-
 
 // ============================================================ head-batched kernel
 // Q = 256, P = 64, N <= 128.  The heads of a group share B and C, so Z = B C^T
@@ -1027,14 +851,8 @@ static void launch_sc(const void *x, const void *B, const void *C, const float *
                        static_cast<const uint16_t *>(C), D, acum, dtq,
                        static_cast<const uint16_t *>(hprev), cg, (int)geo.nc_max, geo.H, geo.G, hb,
                        nkb, static_cast<uint16_t *>(y));
-  } else if constexpr (N <= 256) {
-    hipLaunchKernelGGL((k_chunk_scan_lds<Q, P, N>), grid, dim3(Q), 0, stream,
-                       static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
-                       static_cast<const uint16_t *>(C), D, acum, dtq,
-                       static_cast<const uint16_t *>(hprev), cg, (int)geo.nc_max, geo.H, geo.G,
-                       static_cast<uint16_t *>(y));
   } else {
-    hipLaunchKernelGGL((k_chunk_scan_regs<Q, P, N>), grid, dim3(Q), 0, stream,
+    hipLaunchKernelGGL((k_chunk_scan_lds<Q, P, N>), grid, dim3(Q), 0, stream,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                        static_cast<const uint16_t *>(C), D, acum, dtq,
                        static_cast<const uint16_t *>(hprev), cg, (int)geo.nc_max, geo.H, geo.G,
