@@ -92,12 +92,6 @@ __device__ __forceinline__ void pack_g(const float (&gv)[16], u32x4 &g0, u32x4 &
 }
 
 // ============================================================ LDS-staged kernel
-// 16-byte chunk swizzle of an LDS tile row of `nc` chunks, so that 16 lanes
-// reading the same chunk column of 16 consecutive rows hit distinct banks.
-__device__ __forceinline__ constexpr int chunk_swz(int row, int nc) {
-  return nc >= 16 ? (row & 15) : ((row >> 1) & (nc - 1));
-}
-
 // Block = (chunk, head), Q/64 wavefronts; wavefront w owns token tiles w and
 // Q/32-1-w (balanced causal work) and keeps their C rows in registers.  The
 // source tiles go by in lockstep: B and x tiles of 32 tokens stream through
@@ -803,40 +797,6 @@ bool chunk_scan_bf16_supported(int P, int N, int Q) {
   return P == 64 && (N == 64 || N == 128 || N == 256) && (Q == 64 || Q == 128 || Q == 256);
 }
 
-// Compute units of the current device (cached per device).
-static int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
-  if (v <= 0) {
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
-      v = 256;
-    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
-  }
-  return v;
-}
-
-// Heads per block of the head-batched kernel: one block per CU at a time, so
-// the launch takes ceil(blocks / CUs) rounds of (hb heads + the Z phase, about
-// 1.5 heads' time); pick the run length with the fewest head-times, then even
-// out the runs of a group.
-static int pick_heads_per_block(int64_t nc, int H, int G, int cus, int &nkb) {
-  const int HG = H / G;
-  int best = HG;
-  double best_cost = 1e300;
-  for (int hb = 1; hb <= HG; ++hb) {
-    const int64_t blocks = nc * G * ((HG + hb - 1) / hb);
-    const double cost = (double)((blocks + cus - 1) / cus) * (hb + 1.5);
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = hb;
-    }
-  }
-  nkb = (HG + best - 1) / best;
-  return (HG + nkb - 1) / nkb;
-}
-
 template <int Q, int P, int N>
 static void launch_sc(const void *x, const void *B, const void *C, const float *D,
                       const float *acum, const float *dtq, const void *hprev, void *y,
@@ -845,7 +805,7 @@ static void launch_sc(const void *x, const void *B, const void *C, const float *
   const dim3 grid(xcd_grid(geo.nc_max, geo.H));
   if constexpr (Q == 256 && P == 64 && N <= 128) {
     int nkb = 1;
-    const int hb = pick_heads_per_block(geo.nc_max, geo.H, geo.G, device_cus(), nkb);
+    const int hb = pick_heads_per_block(geo.nc_max, geo.H, geo.G, device_cus(), 1.5, nkb);
     hipLaunchKernelGGL((k_chunk_scan_hb<N>), dim3(xcd_grid(geo.nc_max, geo.G * nkb)), dim3(512), 0,
                        stream, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                        static_cast<const uint16_t *>(C), D, acum, dtq,

@@ -8,17 +8,23 @@
 // weights, which the recurrence implies).  It is a [P x Q] . [Q x N]
 // contraction over the chunk's tokens.
 //
-// Design.  x [T,H,P] and B [T,G,N] keep the token index strided, while an MFMA
-// operand needs runs along the contracted (token) index, so both tiles are
-// transposed on their way into LDS: each thread loads 4 token rows x 8
-// columns (four 16-byte loads), scales x by w_l in fp32, repacks column-wise
-// into bf16 pairs and writes 8-byte runs of 4 tokens.  The chunk goes through
-// in stages of 64 tokens; a stage's global loads are issued before the
-// previous stage's MFMAs, so only the first one waits on memory.  The MFMA then reads
-// 16-byte K-runs (8 tokens) per lane.  Padded LDS rows (K + 8 elements,
-// 144 bytes) keep the 16-byte column reads of 16 consecutive rows on distinct
-// banks.  Block = (chunk, head) in XCD-aware order, 4 wavefronts; the (P/32) x (N/32) output tiles
-// of 32x32 are split evenly over the wavefronts; fp32 accumulation, fp32 S.
+// Design.  The heads of a group share B, so a block takes a run of heads of
+// one chunk (block = (chunk, group, run of hb heads), 8 wavefronts, XCD-aware
+// order).  The chunk's B is staged in LDS once and each wavefront keeps its
+// MFMA B-operands in registers: its 32x32 output tile's 32 columns n over all
+// Q tokens, read by transposing LDS reads (ds_read_b64_tr_b16) so the
+// contracted token index runs along each lane's registers.  Per head:
+//   1. S of the previous head, staged in LDS, is stored (16-byte segments);
+//      this head's x, already in its ring slot, is scaled in place by w_l in
+//      fp32 and rounded once to bf16;
+//   2. the next head's x, acum and dt go into the other slot by direct-to-LDS
+//      loads and land while this head computes;
+//   3. each wavefront forms its tile(s) on v_mfma_f32_32x32x16_bf16 from
+//      transposing reads of the scaled x, and stages them in LDS (fp32).
+// With N = 64 the four tiles are split over K between wavefront pairs and the
+// two halves are added when S is stored; with N = 256 a wavefront owns two
+// tiles.  Token rows past a partial chunk's end repeat its last row, which the
+// zero dt there cancels.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -26,162 +32,170 @@ namespace ssd {
 
 namespace {
 
-constexpr int kStateThreads = 256;
-constexpr int kKT = 64;         // tokens per LDS stage
-constexpr int kLDK = kKT + 8;   // padded LDS row (bf16 elements)
-
-// A stage is kKT token rows of a [tokens x D] bf16 matrix (row stride `ld`
-// elements), moved in units of 4 rows x 8 columns: four 16-byte loads per
-// unit, row quad fastest across threads.  Rows at or past `len` are zeros and
-// never read from global memory.
-template <int D>
-struct Stage {
-  static constexpr int RQ = kKT / 4;  // row quads per stage
-  static constexpr int UNITS = RQ * (D / 8);
-  static constexpr int PER_THREAD = (UNITS + kStateThreads - 1) / kStateThreads;
-  u32x4 r[PER_THREAD][4];
-
-  __device__ __forceinline__ void load(const uint16_t *__restrict__ src, int64_t ld, int kt,
-                                       int len) {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int u = threadIdx.x + i * kStateThreads;
-      const int rq = u % RQ;
-      const int cb = u / RQ;
-      const int l0 = kt + rq * 4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        r[i][e] = (u < UNITS && l0 + e < len)
-                      ? *reinterpret_cast<const u32x4 *>(src + (int64_t)(l0 + e) * ld + cb * 8)
-                      : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  }
-
-  // Writes the stage transposed, dst[d][l] with row length kLDK: column-wise
-  // bf16 pairs, 8-byte runs of 4 tokens.  If `wt` is given, row l is scaled by
-  // wt[l] in fp32 and rounded once to bf16.
-  __device__ __forceinline__ void store(const float *wt, int kt, uint16_t (*dst)[kLDK]) const {
-#pragma unroll
-    for (int i = 0; i < PER_THREAD; ++i) {
-      const int u = threadIdx.x + i * kStateThreads;
-      if (u >= UNITS) continue;
-      const int rq = u % RQ;
-      const int cb = u / RQ;
-      u32x2 out[8];
-      if (wt) {
-        float w[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) w[e] = wt[kt + rq * 4 + e];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // columns 2m (low halves) and 2m+1 (high halves) of word m
-          out[2 * m].x = pack_bf16x2(bf16lo(r[i][0][m]) * w[0], bf16lo(r[i][1][m]) * w[1]);
-          out[2 * m].y = pack_bf16x2(bf16lo(r[i][2][m]) * w[2], bf16lo(r[i][3][m]) * w[3]);
-          out[2 * m + 1].x = pack_bf16x2(bf16hi(r[i][0][m]) * w[0], bf16hi(r[i][1][m]) * w[1]);
-          out[2 * m + 1].y = pack_bf16x2(bf16hi(r[i][2][m]) * w[2], bf16hi(r[i][3][m]) * w[3]);
-        }
-      } else {
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          out[2 * m].x = pair_lo(r[i][0][m], r[i][1][m]);
-          out[2 * m].y = pair_lo(r[i][2][m], r[i][3][m]);
-          out[2 * m + 1].x = pair_hi(r[i][0][m], r[i][1][m]);
-          out[2 * m + 1].y = pair_hi(r[i][2][m], r[i][3][m]);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        *reinterpret_cast<u32x2 *>(&dst[cb * 8 + jj][rq * 4]) = out[jj];
-      }
-    }
-  }
-};
-
-template <int Q, int P, int N>
-__global__ __launch_bounds__(kStateThreads) void k_chunk_state_bf16(
+template <int Q, int N>
+__global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm, const float *__restrict__ acum,
-    const float *__restrict__ dtq, ChunkGeom geom, int nc, int H, int G,
+    const float *__restrict__ dtq, ChunkGeom geom, int nc, int H, int G, int hb, int nkb,
     float *__restrict__ states) {
-  static_assert(P % 32 == 0 && N % 32 == 0, "tile shape");
-  constexpr int TP = P / 32;
-  constexpr int TN = N / 32;
-  constexpr int NT = TP * TN;
-  static_assert(NT % 4 == 0, "tiles must split evenly over 4 wavefronts");
-  constexpr int TPW = NT / 4;
+  constexpr int P = 64;
+  constexpr int NT = 512, NW = 8;
+  constexpr int TPN = P / 32;                            // p tiles
+  constexpr int TILES = TPN * (N / 32);                  // 32x32 output tiles
+  constexpr int TPW = TILES > NW ? TILES / NW : 1;       // tiles per wavefront
+  constexpr int KSPLIT = TILES < NW ? NW / TILES : 1;    // wavefronts per tile (split over K)
+  constexpr int TG = NW / KSPLIT;                        // wavefronts over distinct tiles
+  constexpr int KS = Q / 16 / KSPLIT;                    // K steps per wavefront
+  static_assert(TG * TPW == TILES && KS * 16 * KSPLIT == Q, "work split");
+  constexpr int NCX = P / 8, NCB = N / 8;                // 16-byte chunks per x / B row
+  constexpr int XB = Q * P * 2, BB = Q * N * 2, ADB = 2 * Q * 4;
+  constexpr int LSS = N + 8;                             // S staging row (fp32) + pad
+  constexpr int SSB = P * LSS * 4;
+  constexpr int XI = XB / 1024 / NW, BI = BB / 1024 / NW;
+  static_assert(XI * NW * 1024 == XB && BI * NW * 1024 == BB, "1 KB loads");
+  // [XS0][XS1][AD0][AD1][SS x KSPLIT]; B is staged over all of it first
+  constexpr int XS0 = 0, XS1 = XB, AD0 = 2 * XB, AD1 = AD0 + ADB, SS = AD1 + ADB;
+  constexpr int MAIN = SS + KSPLIT * SSB;
+  constexpr int TOTAL = MAIN > BB ? MAIN : BB;
+  __shared__ __align__(16) unsigned char smem[TOTAL];
 
-  __shared__ __align__(16) uint16_t xs[P][kLDK];
-  __shared__ __align__(16) uint16_t bs[N][kLDK];
-  __shared__ float sw[Q];
-
-  int c, h;
-  xcd_chunk_head(H, c, h);
+  int c, hk;
+  xcd_chunk_head(G * nkb, c, hk);
   if (c >= nc) return;
-  const int g = h / (H / G);
+  const int g = hk / nkb;
+  const int kb = hk - g * nkb;
+  const int HG = H / G;
+  const int hfirst = g * HG + kb * hb;
+  const int nh = min(hb, HG - kb * hb);
+  if (nh <= 0) return;
   const ChunkInfo ci = chunk_info(geom, c);
   if (ci.len <= 0) return;
 
-  const int64_t ch = (int64_t)c * H + h;
-  const uint16_t *xbase = x + ci.t0 * (int64_t)H * P + (int64_t)h * P;
-  const uint16_t *bbase = Bm + ci.t0 * (int64_t)G * N + (int64_t)g * N;
-  Stage<P> xst;
-  Stage<N> bst;
-  // the first stage's loads go out before anything waits
-  xst.load(xbase, (int64_t)H * P, 0, ci.len);
-  bst.load(bbase, (int64_t)G * N, 0, ci.len);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tg = wave % TG;  // tile group
+  const int kp = wave / TG;  // K part
+  const int ldx32 = H * P;   // row offsets inside a chunk: Q * H * P < 2^31
+  const int64_t xrow0 = ci.t0 * (int64_t)ldx32;
+
+  // Transposing read of a 16-token K step for MFMA operands: lane (col, kg)
+  // receives element [r0 + 8kg + j][c0 + col], j = 0..7, of a row-major bf16
+  // tile with `ncc` 16-byte chunks per row (chunk-swizzled), as 4 words in K
+  // order.
+  auto tr_op = [](int lane, const unsigned char *tile, int ncc, int r0, int c0) {
+    const int kg = lane >> 5, gq = lane >> 4, d = lane & 15;
+    const int cidx = c0 + 16 * (gq & 1) + 4 * (d & 3);
+    u32x2 part[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = r0 + 8 * kg + 4 * hf + (d >> 2);
+      const int cc = (cidx >> 3) ^ chunk_swz(row, ncc);
+      part[hf] = lds_read_tr16(tile + row * (ncc * 16) + cc * 16 + (cidx & 7) * 2);
+    }
+    return u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
+  };
+  auto issue_head = [&](int lane, int hh, int slot) {
+    const uint16_t *xb = x + xrow0 + (int64_t)hh * P;
+    unsigned char *xs = smem + (slot ? XS1 : XS0);
+#pragma unroll
+    for (int i = 0; i < XI; ++i) {
+      const int m = (wave * XI + i) * 64 + lane;
+      const int r = m / NCX, cc = (m % NCX) ^ chunk_swz(m / NCX, NCX);
+      load_lds16(xb + min(r, ci.len - 1) * ldx32 + cc * 8, xs + (wave * XI + i) * 1024);
+    }
+    if (wave < 2 && lane < Q / 4)  // wavefront 0: acum, 1: dt
+      load_lds16((wave == 0 ? acum : dtq) + ((int64_t)c * H + hh) * Q + lane * 4,
+                 smem + (slot ? AD1 : AD0) + wave * (Q * 4));
+  };
+  auto store_s = [&](int t, int hh) {
+    float *out = states + ((int64_t)c * H + hh) * (P * N);
+#pragma unroll
+    for (int i = 0; i < P * N / 4 / NT; ++i) {
+      const int u = t + i * NT;
+      const int p = u / (N / 4), c4 = u % (N / 4);
+      f32x4 v = *reinterpret_cast<const f32x4 *>(smem + SS + (p * LSS + 4 * c4) * 4);
+#pragma unroll
+      for (int k = 1; k < KSPLIT; ++k)
+        v += *reinterpret_cast<const f32x4 *>(smem + SS + k * SSB + (p * LSS + 4 * c4) * 4);
+      *reinterpret_cast<f32x4 *>(out + p * N + 4 * c4) = v;
+    }
+  };
+
+  // ---- B operands, once per block
   {
-    const float *ac = acum + ch * Q;
-    const float *dq = dtq + ch * Q;
-    const float alast = ac[Q - 1];
-    for (int l = threadIdx.x; l < Q; l += kStateThreads) sw[l] = __expf(alast - ac[l]) * dq[l];
+    const uint16_t *bb = Bm + ci.t0 * (int64_t)G * N + (int64_t)g * N;
+    const int lane = tid & 63;
+#pragma unroll
+    for (int i = 0; i < BI; ++i) {
+      const int m = (wave * BI + i) * 64 + lane;
+      const int r = m / NCB, cc = (m % NCB) ^ chunk_swz(m / NCB, NCB);
+      load_lds16(bb + (int64_t)min(r, ci.len - 1) * G * N + cc * 8, smem + (wave * BI + i) * 1024);
+    }
   }
+  wait_vmcnt<0>();
   __syncthreads();
-
-  const int wave = threadIdx.x >> 6;
-  const int lane = threadIdx.x & 63;
-  const int col = lane & 31;
-  const int kg = lane >> 5;
-
-  f32x16 acc[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) acc[i] = f32x16{};
-
-#pragma unroll 1
-  for (int kt = 0; kt < ci.len; kt += kKT) {
-    xst.store(sw, kt, xs);
-    bst.store(nullptr, kt, bs);
-    __syncthreads();
-    if (kt + kKT < ci.len) {  // next stage's loads overlap this stage's MFMAs
-      xst.load(xbase, (int64_t)H * P, kt + kKT, ci.len);
-      bst.load(bbase, (int64_t)G * N, kt + kKT, ci.len);
-    }
-#pragma unroll
-    for (int ks = 0; ks < kKT / 16; ++ks) {
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int t = wave * TPW + i;
-        const int tp = t % TP;
-        const int tn = t / TP;
-        const u32x4 a = *reinterpret_cast<const u32x4 *>(&xs[tp * 32 + col][ks * 16 + kg * 8]);
-        const u32x4 b = *reinterpret_cast<const u32x4 *>(&bs[tn * 32 + col][ks * 16 + kg * 8]);
-        acc[i] = mfma32x32x16(as_bf16x8(a), as_bf16x8(b), acc[i]);
-      }
-    }
-    __syncthreads();
-  }
-
-  float *out = states + ch * (int64_t)P * N;
+  u32x4 bop[TPW][KS];
 #pragma unroll
   for (int i = 0; i < TPW; ++i) {
-    const int t = wave * TPW + i;
-    const int tp = t % TP;
-    const int tn = t / TP;
+    const int tn = (tg * TPW + i) / TPN;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = tp * 32 + acc_row(r, kg);
-      out[p * N + tn * 32 + col] = acc[i][r];
+    for (int ks = 0; ks < KS; ++ks) bop[i][ks] = tr_op(tid & 63, smem, NCB, 16 * (kp * KS + ks), 32 * tn);
+  }
+  __syncthreads();  // B consumed: the rings are free
+  issue_head(tid & 63, hfirst, 0);
+
+#pragma unroll 1
+  for (int hi = 0; hi < nh; ++hi) {
+    const int hh = hfirst + hi;
+    const int slot = hi & 1;
+    // lane indices re-read per head, so lane-dependent addresses are formed
+    // where they are used rather than kept live across heads
+    int t = tid;
+    asm volatile("" : "+v"(t));
+    const int lane = t & 63, col = lane & 31, kg = lane >> 5;
+    unsigned char *xs = smem + (slot ? XS1 : XS0);
+    const float *sa = reinterpret_cast<const float *>(smem + (slot ? AD1 : AD0));
+    const float *sd = sa + Q;
+
+    wait_vmcnt<0>();  // this head's x, acum, dt; the stores of S two heads back
+    __syncthreads();  // ... for every thread; the previous head is done everywhere
+    if (hi > 0) store_s(t, hh - 1);
+    {  // x_l *= w_l in place (fp32, one rounding)
+      const float alast = sa[Q - 1];
+#pragma unroll
+      for (int i = 0; i < Q * NCX / NT; ++i) {
+        const int m = t + i * NT;
+        const int l = m / NCX;
+        const float w = __expf(alast - sa[l]) * sd[l];
+        u32x4 *pc = reinterpret_cast<u32x4 *>(xs + m * 16);
+        const u32x4 v = *pc;
+        u32x4 o;
+        o.x = pack_bf16x2(bf16lo(v.x) * w, bf16hi(v.x) * w);
+        o.y = pack_bf16x2(bf16lo(v.y) * w, bf16hi(v.y) * w);
+        o.z = pack_bf16x2(bf16lo(v.z) * w, bf16hi(v.z) * w);
+        o.w = pack_bf16x2(bf16lo(v.w) * w, bf16hi(v.w) * w);
+        *pc = o;
+      }
+    }
+    __syncthreads();  // scaled x ready; staged S read out
+    if (hi + 1 < nh) issue_head(lane, hh + 1, slot ^ 1);
+
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int tt = tg * TPW + i;
+      const int tp = tt % TPN, tn = tt / TPN;
+      f32x16 acc = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const u32x4 a = tr_op(lane, xs, NCX, 16 * (kp * KS + ks), 32 * tp);
+        acc = mfma32x32x16(as_bf16x8(a), as_bf16x8(bop[i][ks]), acc);
+      }
+      float *ss = reinterpret_cast<float *>(smem + SS + kp * SSB);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ss[(tp * 32 + acc_row(r, kg)) * LSS + tn * 32 + col] = acc[r];
     }
   }
+  __syncthreads();
+  store_s(tid, hfirst + nh - 1);
 }
 
 }  // namespace
@@ -193,11 +207,13 @@ bool chunk_state_bf16_supported(int P, int N, int Q) {
 template <int Q, int P, int N>
 static void launch_cs(const void *x, const void *B, const float *acum, const float *dtq,
                       float *states, const Geometry &geo, hipStream_t stream) {
+  static_assert(P == 64, "head dimension");
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
-  hipLaunchKernelGGL((k_chunk_state_bf16<Q, P, N>), dim3(xcd_grid(geo.nc_max, geo.H)),
-                     dim3(kStateThreads), 0, stream, static_cast<const uint16_t *>(x),
-                     static_cast<const uint16_t *>(B), acum, dtq, cg, (int)geo.nc_max, geo.H,
-                     geo.G, states);
+  int nkb = 1;
+  const int hb = pick_heads_per_block(geo.nc_max, geo.H, geo.G, device_cus(), 1.0, nkb);
+  hipLaunchKernelGGL((k_chunk_state_hb<Q, N>), dim3(xcd_grid(geo.nc_max, geo.G * nkb)), dim3(512),
+                     0, stream, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
+                     acum, dtq, cg, (int)geo.nc_max, geo.H, geo.G, hb, nkb, states);
 }
 
 template <int Q>

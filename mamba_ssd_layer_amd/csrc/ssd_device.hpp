@@ -139,6 +139,13 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const void *lds_src) {
   return __builtin_bit_cast(u32x2, v);
 }
 
+// 16-byte chunk swizzle of an LDS tile row of `nc` chunks (XOR on the chunk
+// index), so that 16 lanes reading the same chunk column of 16 consecutive
+// rows hit distinct banks.
+__device__ __forceinline__ constexpr int chunk_swz(int row, int nc) {
+  return nc >= 16 ? (row & 15) : ((row >> 1) & (nc - 1));
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_bcast(T v, int src) { return __shfl(v, src, 64); }
 

@@ -44,4 +44,38 @@ hipError_t launch_chunk_scan_f32(const float *x, const float *B, const float *C,
                                  const float *acum, const float *dtq, const float *hprev, float *y,
                                  const Geometry &geo, hipStream_t stream);
 
+// Compute units of the current device (cached per device).
+inline int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int v = __atomic_load_n(&cache[dev], __ATOMIC_RELAXED);
+  if (v <= 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0)
+      v = 256;
+    __atomic_store_n(&cache[dev], v, __ATOMIC_RELAXED);
+  }
+  return v;
+}
+
+// Heads per block of a head-batched kernel (one block per CU at a time): a
+// launch takes ceil(blocks / slots) rounds of (hb heads + a prologue worth
+// `prologue` heads' time); pick the run length with the fewest head-times,
+// then even out the runs of a group.  Returns hb; nkb = runs per group.
+inline int pick_heads_per_block(int64_t nc, int H, int G, int slots, double prologue, int &nkb) {
+  const int HG = H / G;
+  int best = HG;
+  double best_cost = 1e300;
+  for (int hb = 1; hb <= HG; ++hb) {
+    const int64_t blocks = nc * G * ((HG + hb - 1) / hb);
+    const double cost = (double)((blocks + slots - 1) / slots) * (hb + prologue);
+    if (cost < best_cost) {
+      best_cost = cost;
+      best = hb;
+    }
+  }
+  nkb = (HG + best - 1) / best;
+  return (HG + nkb - 1) / nkb;
+}
+
 }  // namespace ssd
