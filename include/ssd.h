@@ -176,6 +176,28 @@ ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const flo
                           int chunk_len, const ssd_dims *dims, void *workspace,
                           size_t workspace_bytes, void *stream);
 
+/* Single-token recurrent step, for decoding: one new token per sequence, the
+ * state updated in place (page "State Space Duality and Mamba-2: Unifying
+ * Transformers and Semiseparable Matrices", section "The Dual Perspectives of
+ * Semiseparable Multiplication", item 1, the recurrent mode with a constant
+ * state per head; page "Mamba-2 Architecture: State Space Duality
+ * Explained", "Step 3: Autoregressive Token Generation without KV Cache"):
+ *   state[s,h] <- exp(dt[s,h] A_h) state[s,h] + dt[s,h] x[s,h] B[s,g]^T
+ *   y[s,h]      = C[s,g] state[s,h] + D_h x[s,h]
+ * i.e. the recurrence at the top of this file for one token.  Calling it for
+ * tokens t0, t1, ... continues ssd_chunk_scan_fwd from its final_state: the
+ * results agree with one forward over all the tokens up to rounding.
+ *   dims: batch = S sequences, seqlen = 1, nseq = 0, other fields as above.
+ *   x [S, H, P] io, dt [S, H] float, B and C [S, G, N] io, D [H] float or
+ *   NULL, state [S, H, P, N] float (read, then overwritten), y [S, H, P] io.
+ * Supported: dstate N in {16, 32, 64, 128, 256}; any headdim P >= 1; both io
+ * dtypes; fp32 arithmetic, y rounded to nearest-even for bf16.  Alignment as
+ * above; state must not overlap any other argument, y none of the inputs.
+ * One pass over the state: it is bound by 2 * S*H*P*N*4 bytes of HBM traffic.
+ * Returns after enqueueing. */
+ssd_status ssd_step(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                    const float *D, float *state, void *y, const ssd_dims *dims, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -7,6 +7,7 @@ include/ssd.h).  This package is its Python face:
   chunk_scan_fwd()   convenience wrapper: infers the dims from torch tensors,
                      allocates y / final_state / workspace, runs the forward
   SSDForward         a reusable plan (fixed dims, workspace allocated once)
+  step()             one recurrent decode step per sequence, state updated in place
 
 Tensors (GPU, contiguous):
   x [B, L, H, P]   dt [B, L, H] float32   A [H] float32   B, C [B, L, G, N]
@@ -26,7 +27,7 @@ from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsuppo
                      SSDWorkspaceError, make_dims)
 
 __all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDError", "SSDInvalidArgument",
-           "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for"]
+           "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "step"]
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -129,3 +130,20 @@ def chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
     dims = dims_for(x, B, cu_seqlens)
     plan = SSDForward(dims, chunk_len, device=x.device)
     return plan(x, dt, A, B, C, D, init_state, cu_seqlens)
+
+
+def step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,
+         state: torch.Tensor, D: Optional[torch.Tensor] = None,
+         y: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step (ssd_step): x [S, H, P], dt [S, H], B/C [S, G, N],
+    state [S, H, P, N] float32 (updated in place).  Returns y [S, H, P]."""
+    if x.dim() != 3 or B.dim() != 3 or state.dim() != 4:
+        raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG,
+                                 "x [S,H,P], B/C [S,G,N], state [S,H,P,N] expected")
+    S, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    dims = make_dims(S, 1, H, P, N, G, 0, _io_dtype(x))
+    if y is None:
+        y = torch.empty_like(x)
+    libssd.ssd_step(x, dt, A, B, C, D, state, y, dims, stream)
+    return y

@@ -299,6 +299,38 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, co
   return run_scan(x, B, C, D, y, p, workspace, st);
 }
 
+ssd_status ssd_step(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                    const float *D, float *state, void *y, const ssd_dims *d, void *stream) {
+  if (!d) return SSD_ERR_INVALID_ARG;
+  if (d->reserved != 0) return SSD_ERR_INVALID_ARG;
+  if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
+  if (d->batch < 0 || d->seqlen != 1 || d->nseq != 0 || d->nheads < 1 || d->headdim < 1 ||
+      d->dstate < 1 || d->ngroups < 1 || d->nheads % d->ngroups != 0)
+    return SSD_ERR_INVALID_ARG;
+  const int64_t S = d->batch, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+  if (!ssd::step_supported((int)N)) return SSD_ERR_UNSUPPORTED;
+  // one block per (sequence, head); element offsets of the state below 2^62
+  if (H > (1 << 20) || P > (1 << 20) || S * H >= ((int64_t)1 << 31)) return SSD_ERR_UNSUPPORTED;
+  if (!A || !aligned(A, 4) || (D && !aligned(D, 4))) return SSD_ERR_INVALID_ARG;
+  if (S == 0) return SSD_OK;
+  const size_t io = d->io_dtype == SSD_BF16 ? 2 : 4;
+  const size_t xb = (size_t)S * H * P * io, bcb = (size_t)S * G * N * io, dtb = (size_t)S * H * 4;
+  const size_t sb = (size_t)S * H * P * N * 4;
+  if (!x || !dt || !B || !C || !state || !y) return SSD_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(dt, 4) || !aligned(B, 16) || !aligned(C, 16) ||
+      !aligned(state, 16) || !aligned(y, 16))
+    return SSD_ERR_INVALID_ARG;
+  if (overlaps(state, sb, x, xb) || overlaps(state, sb, B, bcb) || overlaps(state, sb, C, bcb) ||
+      overlaps(state, sb, dt, dtb) || overlaps(state, sb, y, xb) || overlaps(state, sb, A, H * 4) ||
+      (D && overlaps(state, sb, D, H * 4)))
+    return SSD_ERR_INVALID_ARG;
+  if (overlaps(y, xb, x, xb) || overlaps(y, xb, B, bcb) || overlaps(y, xb, C, bcb) ||
+      overlaps(y, xb, dt, dtb))
+    return SSD_ERR_INVALID_ARG;
+  return hip_status(ssd::launch_step(x, dt, A, B, C, D, state, y, io == 2, S, (int)H, (int)P,
+                                     (int)N, (int)G, static_cast<hipStream_t>(stream)));
+}
+
 const char *ssd_status_string(ssd_status status) {
   switch (status) {
     case SSD_OK: return "ok";

@@ -44,6 +44,12 @@ hipError_t launch_chunk_scan_f32(const float *x, const float *B, const float *C,
                                  const float *acum, const float *dtq, const float *hprev, float *y,
                                  const Geometry &geo, hipStream_t stream);
 
+// single-token recurrent step (decode)
+bool step_supported(int N);
+hipError_t launch_step(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                       const float *D, float *state, void *y, bool bf16, int64_t S, int H, int P,
+                       int N, int G, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 inline int device_cus() {
   static int cache[64];

@@ -59,7 +59,7 @@ class ssd_workspace_layout(ctypes.Structure):
 
 EXPORTS = ["ssd_workspace_size", "ssd_get_workspace_layout", "ssd_chunk_scan_fwd",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
-           "ssd_status_string", "ssd_version"]
+           "ssd_step", "ssd_status_string", "ssd_version"]
 
 
 def _load() -> ctypes.CDLL:
@@ -83,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.ssd_state_passing.argtypes = [p, p, i32, dims_p, p, sz, p]
     lib.ssd_chunk_scan.restype = i32
     lib.ssd_chunk_scan.argtypes = [p, p, p, p, p, i32, dims_p, p, sz, p]
+    lib.ssd_step.restype = i32
+    lib.ssd_step.argtypes = [p, p, p, p, p, p, p, p, dims_p, p]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_version.restype = i32
@@ -179,3 +181,8 @@ def ssd_chunk_scan(x, B, C, D, y, chunk_len, dims, workspace, stream=None) -> No
     _check(_lib.ssd_chunk_scan(_ptr(x), _ptr(B), _ptr(C), _ptr(D), _ptr(y), int(chunk_len),
                                ctypes.byref(dims), _ptr(workspace),
                                workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def ssd_step(x, dt, A, B, C, D, state, y, dims, stream=None) -> None:
+    _check(_lib.ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
+                         _ptr(y), ctypes.byref(dims), _stream(stream)))

@@ -201,3 +201,52 @@ def test_layout_rejects_like_fwd():
     d = good()
     with pytest.raises(libssd.SSDUnsupported):
         libssd.ssd_get_workspace_layout(d, 96)
+
+
+# ---------------------------------------------------------------- ssd_step
+def step(d, **kw):
+    """ssd_step with distinct, aligned fake pointers 1 GiB apart (overridable)."""
+    v = ctypes.c_void_p
+    args = dict(x=FAKE, dt=FAKE + (1 << 30), A=FAKE + (2 << 30), B=FAKE + (3 << 30),
+                C=FAKE + (4 << 30), D=None, state=FAKE + (5 << 30), y=FAKE + (7 << 30))
+    args.update(kw)
+    return L.ssd_step(*(None if args[k] is None else v(args[k])
+                        for k in ("x", "dt", "A", "B", "C", "D", "state", "y")),
+                      ctypes.byref(d), None)
+
+
+def good_step():
+    return make_dims(4, 1, 8, 64, 128, 2, 0, SSD_BF16)
+
+
+def test_step_dims():
+    d = good_step(); d.seqlen = 2
+    assert step(d) == SSD_ERR_INVALID_ARG          # one token per sequence
+    d = good_step(); d.nseq = 3
+    assert step(d) == SSD_ERR_INVALID_ARG
+    d = good_step(); d.ngroups = 3
+    assert step(d) == SSD_ERR_INVALID_ARG          # G must divide H
+    d = good_step(); d.dstate = 96
+    assert step(d) == SSD_ERR_UNSUPPORTED
+    d = good_step(); d.io_dtype = 7
+    assert step(d) == SSD_ERR_INVALID_ARG
+    d = good_step(); d.batch = 0
+    assert step(d, x=None, dt=None, B=None, C=None, state=None, y=None) == SSD_OK  # nothing to do
+
+
+def test_step_pointers():
+    d = good_step()
+    for k in ("x", "dt", "A", "B", "C", "state", "y"):
+        assert step(d, **{k: None}) == SSD_ERR_INVALID_ARG, k
+    assert step(d, x=FAKE + 8) == SSD_ERR_INVALID_ARG
+    assert step(d, state=FAKE + (5 << 30) + 4) == SSD_ERR_INVALID_ARG
+    assert step(d, D=FAKE + (6 << 30) + 2) == SSD_ERR_INVALID_ARG
+
+
+def test_step_overlaps():
+    d = good_step()
+    sb = 4 * 8 * 64 * 128 * 4
+    assert step(d, y=FAKE) == SSD_ERR_INVALID_ARG                      # y == x
+    assert step(d, state=FAKE + (3 << 30)) == SSD_ERR_INVALID_ARG      # state == B
+    assert step(d, y=FAKE + (5 << 30) + sb - 16) == SSD_ERR_INVALID_ARG  # y inside the state
+    assert step(d, A=FAKE + (5 << 30) + 64) == SSD_ERR_INVALID_ARG     # A inside the state
