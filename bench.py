@@ -124,6 +124,49 @@ def cpu_baseline(w, target_cpu_seconds: float = 20.0):
                       f"threads ({per_pair:.2f} s for one pair on one thread)"}
 
 
+def decode_step(torch, ssd, workloads, dev, steps: int, warmup: int):
+    """ssd_step on a serving-sized batch: 128 sequences, the large layer's heads
+    and state (H80 P64 N128, bf16 io), one token each.  The fp32 state (671 MB)
+    exceeds the 256 MB MALL, so every step streams it from HBM; the step is
+    bound by reading and writing it once."""
+    import numpy as np
+    w = workloads.make_custom(128, 1, 80, 64, 128, 1, 64, "bf16", seed=5000, init_std=0.1)
+    S, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+
+    def up(a, shape, dtype=None):
+        t = torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+        return (t.to(dtype) if dtype is not None else t).view(*shape).contiguous()
+
+    x = up(w.x, (S, H, P), torch.bfloat16)
+    dt = up(w.dt, (S, H))
+    A = up(w.A, (H,))
+    Bm = up(w.B, (S, G, N), torch.bfloat16)
+    Cm = up(w.C, (S, G, N), torch.bfloat16)
+    D = up(w.D, (H,))
+    state = up(w.h0, (S, H, P, N))
+    y = torch.empty_like(x)
+    stream = torch.cuda.current_stream()
+    for _ in range(warmup):
+        ssd.step(x, dt, A, Bm, Cm, state, D=D, y=y)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        ssd.step(x, dt, A, Bm, Cm, state, D=D, y=y)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) / steps * 1e3
+    nbytes = 2 * S * H * P * N * 4 + 2 * S * H * P * 2 + 2 * S * G * N * 2 + S * H * 4
+    gbs = nbytes / (us * 1e-6) / 1e9
+    log(f"bench: decode step S{S} H{H} P{P} N{N}: {us:.1f} us, {gbs:.0f} GB/s")
+    return {"workload": f"decode_s{S}_h{H}_p{P}_n{N}_g{G}_bf16", "sequences": S, "us": round(us, 2),
+            "tokens_per_s": round(S / (us * 1e-6), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": nbytes}}
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -132,6 +175,8 @@ def main() -> int:
     ap.add_argument("--workload", default="large_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stage-timing", action="store_true")
+    ap.add_argument("--no-decode", action="store_true",
+                    help="skip the single-token decode (ssd_step) measurement")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 elementwise copies (dst = -src, one read and one write per "
                          "element) of MIB MiB: a known-size reference for the hardware byte "
@@ -262,6 +307,10 @@ def main() -> int:
         roofline["algorithmic_bytes"] = b
         roofline["algorithmic_flops"] = f
 
+    decode = None
+    if not args.no_decode:
+        decode = decode_step(torch, ssd, workloads, dev, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
@@ -273,7 +322,7 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {**workloads.describe(w), "parallelism": "none (1 GPU)"},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels,
+        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "decode_step": decode,
     }
     print(json.dumps(out), flush=True)
     return 0
