@@ -13,11 +13,18 @@ Contents
                     states, state hand-off, inter-chunk output), numpy fp64; it
                     also returns the per-chunk intermediates.
   recurrence_py(...) the same recurrence as plain numpy loops (tiny inputs).
+  conv1d_silu(...), gate_rmsnorm(...), silu(...)
+                    the core's neighbours in the Mamba-2 block (block.py): the
+                    causal depthwise convolution + SiLU before it, the SiLU gate
+                    and RMS normalisation after it, numpy fp64.
 
 Nothing here is "parity unpinned": tests/test_oracle.py pins recurrence() to
 hand-computed values, closed forms, the quadratic dual, the A = 0 linear
 attention special case, chunk/split invariance, linearity, the rank bound and
-brute force on tiny inputs.
+brute force on tiny inputs; tests/test_oracle_block.py pins the block
+neighbours to torch's own conv1d / silu / rms_norm in fp64 on the CPU (library
+routines), to closed forms (width-1 kernel, shift kernels, zero gate) and to
+the scale invariance of the normalisation.
 """
 from __future__ import annotations
 
@@ -28,6 +35,7 @@ from typing import Optional, Sequence, Tuple
 import numpy as np
 
 from .reference import quadratic, chunked, recurrence_py  # noqa: F401
+from .block import conv1d_silu, gate_rmsnorm, silu  # noqa: F401
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libssd_oracle.so")
