@@ -198,6 +198,42 @@ ssd_status ssd_chunk_scan(const void *x, const void *B, const void *C, const flo
 ssd_status ssd_step(const void *x, const float *dt, const float *A, const void *B, const void *C,
                     const float *D, float *state, void *y, const ssd_dims *dims, void *stream);
 
+/* The core's neighbours in the Mamba-2 block (page "Mamba-2 Architecture:
+ * State Space Duality Explained", "Step 2: Full Mamba-2 Block with Gated
+ * Projections").  Both are HBM-bound and take T token rows; the sequences are
+ * `batch` rows of `seqlen` tokens (cu_seqlens NULL, nseq 0, T = batch *
+ * seqlen) or nseq packed sequences given by the device int32 cu_seqlens
+ * [nseq + 1] (batch 1, T = seqlen), as for ssd_chunk_scan_fwd.
+ *
+ * ssd_conv1d_silu: the causal depthwise convolution over the token axis that
+ * precedes the core (width K, left padding K - 1, outputs truncated to the
+ * sequence), then SiLU:
+ *   out[t, c] = silu(bias[c] + sum_{k<K} weight[c * K + k] * in[t - (K-1) + k, c])
+ * where positions before the first token of t's sequence read zero, and
+ * silu(v) = v / (1 + exp(-v)).
+ *   in:  T rows of in_stride elements; channels 0 .. channels-1 of each row are
+ *        read, so one slice (x, B or C) of a packed projection can be read in
+ *        place by offsetting the pointer.  out: T rows of out_stride elements.
+ *   weight [channels][K] float; bias [channels] float or NULL; 1 <= K <= 4.
+ *   channels, in_stride and out_stride multiples of 8 (bf16) / 4 (fp32)
+ *   elements; in and out 16-byte aligned; out must not overlap in.
+ *   Malformed cu_seqlens never cause an out-of-bounds access (as above).
+ *
+ * ssd_gate_rmsnorm: the gate and normalisation after the core:
+ *   g = y * silu(z);  out = weight ? g / sqrt(mean over the row of g^2 + eps) * weight : g
+ * per token row of `width` channels (H * P for the core's output).
+ *   y, z, out [T, width] io dtype, 16-byte aligned; out may be y or z itself
+ *   but must not otherwise overlap them; weight [width] float or NULL;
+ *   width a multiple of 8 (bf16) / 4 (fp32); eps >= 0.
+ * fp32 arithmetic, bf16 results rounded to nearest-even.  Return after
+ * enqueueing. */
+ssd_status ssd_conv1d_silu(const void *in, int64_t in_stride, const float *weight,
+                           const float *bias, int kernel_width, void *out, int64_t out_stride,
+                           int64_t batch, int64_t seqlen, int64_t nseq, const int32_t *cu_seqlens,
+                           int64_t channels, int32_t io_dtype, void *stream);
+ssd_status ssd_gate_rmsnorm(const void *y, const void *z, const float *weight, float eps, void *out,
+                            int64_t tokens, int64_t width, int32_t io_dtype, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -8,6 +8,8 @@ include/ssd.h).  This package is its Python face:
                      allocates y / final_state / workspace, runs the forward
   SSDForward         a reusable plan (fixed dims, workspace allocated once)
   step()             one recurrent decode step per sequence, state updated in place
+  conv1d_silu()      the causal depthwise conv1d + SiLU before the core
+  gate_rmsnorm()     y * SiLU(z), then RMS norm over the channel width, after it
 
 Tensors (GPU, contiguous):
   x [B, L, H, P]   dt [B, L, H] float32   A [H] float32   B, C [B, L, G, N]
@@ -27,7 +29,8 @@ from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsuppo
                      SSDWorkspaceError, make_dims)
 
 __all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDError", "SSDInvalidArgument",
-           "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "step"]
+           "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "step",
+           "conv1d_silu", "gate_rmsnorm"]
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -147,3 +150,46 @@ def step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C:
         y = torch.empty_like(x)
     libssd.ssd_step(x, dt, A, B, C, D, state, y, dims, stream)
     return y
+
+
+def conv1d_silu(inp: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Tensor] = None,
+                cu_seqlens: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                stream=None) -> torch.Tensor:
+    """Causal depthwise conv1d (width weight.shape[1] <= 4) + SiLU over the token
+    axis.  inp: [B, L, C] or (packed, with cu_seqlens) [T, C]; its last dim must
+    be contiguous, and it may be a column slice of wider rows (x, B or C of a
+    packed projection).  weight [C, K] float32, bias [C] float32 or None.
+    Returns out (contiguous, same shape) unless given."""
+    if inp.stride(-1) != 1:
+        raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "channels must be contiguous")
+    C = inp.shape[-1]
+    if cu_seqlens is not None:
+        if inp.dim() != 2:
+            raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "packed inp must be [T, C]")
+        T = inp.shape[0]
+        batch, seqlen, nseq = 1, T, cu_seqlens.numel() - 1
+    else:
+        if inp.dim() != 3:
+            raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "inp must be [B, L, C]")
+        batch, seqlen, nseq = inp.shape[0], inp.shape[1], 0
+        if batch > 1 and inp.stride(0) != seqlen * inp.stride(1):
+            raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "rows must be evenly strided")
+    in_stride = inp.stride(-2)
+    if out is None:
+        out = torch.empty(inp.shape, dtype=inp.dtype, device=inp.device)
+    libssd.ssd_conv1d_silu(inp, in_stride, weight, bias, weight.shape[1], out, out.stride(-2),
+                           batch, seqlen, nseq, cu_seqlens, C, _io_dtype(inp), stream)
+    return out
+
+
+def gate_rmsnorm(y: torch.Tensor, z: torch.Tensor, weight: Optional[torch.Tensor] = None,
+                 eps: float = 1e-5, out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """y * SiLU(z), then (with a weight) RMS norm over the last dim(s) of width
+    `weight.numel()`: y and z [..., H, P] or [..., W], contiguous."""
+    W = weight.numel() if weight is not None else y.shape[-1] * (y.shape[-2] if y.dim() >= 3 else 1)
+    if y.numel() % W:
+        raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "width does not divide the tensor")
+    if out is None:
+        out = torch.empty_like(y)
+    libssd.ssd_gate_rmsnorm(y, z, weight, eps, out, y.numel() // W, W, _io_dtype(y), stream)
+    return out

@@ -1,0 +1,238 @@
+// libssd: the SSD core's neighbours in the Mamba-2 block (page "Mamba-2
+// Architecture: State Space Duality Explained", "Step 2: Full Mamba-2 Block
+// with Gated Projections"):
+//   * before the core, a causal depthwise convolution of width K over the
+//     token axis of each channel (bias, left padding K-1, outputs truncated to
+//     the sequence) followed by SiLU;
+//   * after it, the output gated by SiLU(z) and RMS-normalised over the whole
+//     channel width with a learned weight.
+// Both are elementwise along channels and HBM-bound: each reads its inputs and
+// writes its output once.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+
+// VEC channels per 16-byte access: 8 bf16 or 4 fp32
+template <typename IO> struct Vec;
+template <> struct Vec<uint16_t> {
+  static constexpr int N = 8;
+  __device__ static void load(const uint16_t *p, float (&v)[8]) {
+    const u32x4 q = *reinterpret_cast<const u32x4 *>(p);
+    v[0] = bf16lo(q.x); v[1] = bf16hi(q.x); v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
+    v[4] = bf16lo(q.z); v[5] = bf16hi(q.z); v[6] = bf16lo(q.w); v[7] = bf16hi(q.w);
+  }
+  __device__ static void store(uint16_t *p, const float (&v)[8]) {
+    *reinterpret_cast<u32x4 *>(p) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                          pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
+  }
+};
+template <> struct Vec<float> {
+  static constexpr int N = 4;
+  __device__ static void load(const float *p, float (&v)[4]) {
+    const f32x4 q = *reinterpret_cast<const f32x4 *>(p);
+    v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+  }
+  __device__ static void store(float *p, const float (&v)[4]) {
+    *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+  }
+};
+
+__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+
+constexpr int kConvRun = 32;  // tokens per thread
+
+// Thread = (channel group of VEC, run of kConvRun tokens), channel groups
+// fastest so a wavefront reads contiguous row segments.  The K-1 previous
+// inputs of the group stay in registers; at a sequence start they reset to 0.
+template <typename IO, int K>
+__global__ __launch_bounds__(256) void k_conv1d_silu(const IO *__restrict__ in, int64_t in_stride,
+                                                     const float *__restrict__ weight,
+                                                     const float *__restrict__ bias,
+                                                     IO *__restrict__ out, int64_t out_stride,
+                                                     int64_t T, int64_t seqlen, int nseq,
+                                                     const int32_t *__restrict__ cu, int groups) {
+  constexpr int V = Vec<IO>::N;
+  const int64_t gid = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+  const int64_t runs = (T + kConvRun - 1) / kConvRun;
+  if (gid >= runs * groups) return;
+  const int grp = static_cast<int>(gid % groups);
+  const int64_t t0 = (gid / groups) * kConvRun;
+  const int64_t t1 = min(T, t0 + kConvRun);
+  const int c0 = grp * V;
+
+  float w[V][K], b[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+#pragma unroll
+    for (int k = 0; k < K; ++k) w[v][k] = weight[(int64_t)(c0 + v) * K + k];
+    b[v] = bias ? bias[c0 + v] : 0.f;
+  }
+  // the sequence holding t0: [s_begin, s_end)
+  int64_t s_begin, s_end;
+  int s = 0;
+  if (cu) {
+    int lo = 0, hi = nseq - 1;  // largest s with cu[s] <= t0
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (cu[mid] <= t0) lo = mid; else hi = mid - 1;
+    }
+    s = lo;
+    s_begin = cu[s];
+    s_end = cu[s + 1];
+    while (s_end <= t0 && s + 1 < nseq) {  // skip empty sequences
+      ++s;
+      s_begin = cu[s];
+      s_end = cu[s + 1];
+    }
+    s_begin = s_begin < 0 ? 0 : s_begin;  // any cu_seqlens: reads stay inside [0, T)
+  } else {
+    s_begin = (t0 / seqlen) * seqlen;
+    s_end = s_begin + seqlen;
+  }
+  float win[K > 1 ? K - 1 : 1][V];  // win[j] = input at t - (K-1) + j
+#pragma unroll
+  for (int j = 0; j < K - 1; ++j) {
+    const int64_t src = t0 - (K - 1) + j;
+    if (src >= s_begin) {
+      Vec<IO>::load(in + src * in_stride + c0, win[j]);
+    } else {
+#pragma unroll
+      for (int v = 0; v < V; ++v) win[j][v] = 0.f;
+    }
+  }
+  for (int64_t t = t0; t < t1; ++t) {
+    if (t >= s_end) {  // a new sequence starts here: the window empties
+      if (cu) {
+        while (s + 1 < nseq && cu[s + 1] <= t) ++s;
+        s_begin = cu[s] < 0 ? 0 : cu[s];
+        s_end = cu[s + 1] > t ? cu[s + 1] : T;  // a malformed table never loops back
+      } else {
+        s_begin = t;
+        s_end = t + seqlen;
+      }
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j)
+#pragma unroll
+        for (int v = 0; v < V; ++v) win[j][v] = 0.f;
+    }
+    float cur[V], o[V];
+    Vec<IO>::load(in + t * in_stride + c0, cur);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      float acc = b[v];
+#pragma unroll
+      for (int j = 0; j < K - 1; ++j) acc += w[v][j] * win[j][v];
+      acc += w[v][K - 1] * cur[v];
+      o[v] = silu(acc);
+    }
+    Vec<IO>::store(out + t * out_stride + c0, o);
+#pragma unroll
+    for (int j = 0; j + 1 < K - 1; ++j)
+#pragma unroll
+      for (int v = 0; v < V; ++v) win[j][v] = win[j + 1][v];
+    if (K > 1) {
+#pragma unroll
+      for (int v = 0; v < V; ++v) win[K > 1 ? K - 2 : 0][v] = cur[v];
+    }
+  }
+}
+
+// Block = one token row of `width` channels.  Pass 1 sums g^2 (g = y silu(z))
+// over the row; pass 2 recomputes g from the same (cached) row and writes
+// g * rsqrt(mean + eps) * weight, or g alone without a weight.
+template <typename IO>
+__global__ __launch_bounds__(256) void k_gate_rmsnorm(const IO *y, const IO *z,
+                                                      const float *__restrict__ weight, float eps,
+                                                      IO *out, int width) {
+  constexpr int V = Vec<IO>::N;
+  __shared__ float part[4];
+  const int64_t row = blockIdx.x;
+  const IO *yr = y + row * width;
+  const IO *zr = z + row * width;
+  IO *orow = out + row * width;
+  const int nvec = width / V;
+  float scale = 1.f;
+  if (weight) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < nvec; i += 256) {
+      float a[V], c[V];
+      Vec<IO>::load(yr + i * V, a);
+      Vec<IO>::load(zr + i * V, c);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float g = a[v] * silu(c[v]);
+        ss += g * g;
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    const float tot = part[0] + part[1] + part[2] + part[3];
+    scale = rsqrtf(tot / width + eps);
+  }
+  for (int i = threadIdx.x; i < nvec; i += 256) {
+    float a[V], c[V], o[V];
+    Vec<IO>::load(yr + i * V, a);
+    Vec<IO>::load(zr + i * V, c);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const float g = a[v] * silu(c[v]);
+      o[v] = weight ? g * scale * weight[i * V + v] : g;
+    }
+    Vec<IO>::store(orow + i * V, o);
+  }
+}
+
+template <typename IO>
+hipError_t conv_t(const void *in, int64_t in_stride, const float *w, const float *b, int K,
+                  void *out, int64_t out_stride, int64_t T, int64_t seqlen, int nseq,
+                  const int32_t *cu, int64_t channels, hipStream_t stream) {
+  const int groups = static_cast<int>(channels / Vec<IO>::N);
+  const int64_t threads = ((T + kConvRun - 1) / kConvRun) * groups;
+  const dim3 grid(static_cast<unsigned>((threads + 255) / 256));
+  const IO *i = static_cast<const IO *>(in);
+  IO *o = static_cast<IO *>(out);
+  switch (K) {
+    case 1: hipLaunchKernelGGL((k_conv1d_silu<IO, 1>), grid, dim3(256), 0, stream, i, in_stride, w, b, o, out_stride, T, seqlen, nseq, cu, groups); break;
+    case 2: hipLaunchKernelGGL((k_conv1d_silu<IO, 2>), grid, dim3(256), 0, stream, i, in_stride, w, b, o, out_stride, T, seqlen, nseq, cu, groups); break;
+    case 3: hipLaunchKernelGGL((k_conv1d_silu<IO, 3>), grid, dim3(256), 0, stream, i, in_stride, w, b, o, out_stride, T, seqlen, nseq, cu, groups); break;
+    case 4: hipLaunchKernelGGL((k_conv1d_silu<IO, 4>), grid, dim3(256), 0, stream, i, in_stride, w, b, o, out_stride, T, seqlen, nseq, cu, groups); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_conv1d_silu(const void *in, int64_t in_stride, const float *weight,
+                              const float *bias, int K, void *out, int64_t out_stride, int64_t T,
+                              int64_t seqlen, int nseq, const int32_t *cu_seqlens,
+                              int64_t channels, bool bf16, hipStream_t stream) {
+  if (T == 0) return hipSuccess;
+  return bf16 ? conv_t<uint16_t>(in, in_stride, weight, bias, K, out, out_stride, T, seqlen, nseq,
+                                 cu_seqlens, channels, stream)
+              : conv_t<float>(in, in_stride, weight, bias, K, out, out_stride, T, seqlen, nseq,
+                              cu_seqlens, channels, stream);
+}
+
+hipError_t launch_gate_rmsnorm(const void *y, const void *z, const float *weight, float eps,
+                               void *out, int64_t tokens, int width, bool bf16,
+                               hipStream_t stream) {
+  if (tokens == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(tokens));
+  if (bf16)
+    hipLaunchKernelGGL(k_gate_rmsnorm<uint16_t>, grid, dim3(256), 0, stream,
+                       static_cast<const uint16_t *>(y), static_cast<const uint16_t *>(z), weight,
+                       eps, static_cast<uint16_t *>(out), width);
+  else
+    hipLaunchKernelGGL(k_gate_rmsnorm<float>, grid, dim3(256), 0, stream,
+                       static_cast<const float *>(y), static_cast<const float *>(z), weight, eps,
+                       static_cast<float *>(out), width);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

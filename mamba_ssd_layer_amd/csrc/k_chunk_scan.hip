@@ -548,33 +548,36 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     unsigned char *xs = smem + (slot ? XS1 : XS0);
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
-      const int m = (wave * XI + i) * 64 + lane;
-      const int r = m / NCX, cc = (m % NCX) ^ chunk_swz(m / NCX, NCX);
-      load_lds16(xb + min(r, ci.len - 1) * ldx32 + cc * 8, xs + (wave * XI + i) * 1024);
+      const unsigned m = (wave * XI + i) * 64 + lane, r = m / NCX;
+      const unsigned cc = (m % NCX) ^ chunk_swz(r, NCX);
+      load_lds16(xb + min((int)r, ci.len - 1) * ldx32 + cc * 8, xs + (wave * XI + i) * 1024);
     }
     const int64_t ch = (int64_t)c * H + hh;
     const uint16_t *hp = hprev + ch * (P * N);
     unsigned char *hs = smem + (slot ? HS1 : HS0);
 #pragma unroll
     for (int i = 0; i < HI; ++i) {
-      const int m = (wave * HI + i) * 64 + lane;
-      const int r = m / NCB, cc = (m % NCB) ^ chunk_swz(m / NCB, NCB);
+      const unsigned m = (wave * HI + i) * 64 + lane, r = m / NCB;
+      const unsigned cc = (m % NCB) ^ chunk_swz(r, NCB);
       load_lds16(hp + r * N + cc * 8, hs + (wave * HI + i) * 1024);
     }
     if (wave < 2)  // wavefront 0: acum, 1: dt
       load_lds16((wave == 0 ? acum : dtq) + ch * Q + lane * 4, smem + (slot ? AD1 : AD0) + wave * 1024);
   };
   auto store_y = [&](const Lane &Ln, int hh, const unsigned char *ys) {
-    const int tid = Ln.tid;
+    const unsigned tid = Ln.tid;
     uint16_t *yb = y + xrow0 + (int64_t)hh * P;
+    constexpr int NI = Q * NCX / NT;
+    u32x4 v[NI];
 #pragma unroll
-    for (int i = 0; i < Q * NCX / NT; ++i) {
-      const int u = tid + i * NT;
-      const int r = u / NCX, gp = u % NCX;
-      if (r < ci.len) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + r * (P * 2) + (gp ^ chunk_swz(r, NCX)) * 16);
-        *reinterpret_cast<u32x4 *>(yb + r * ldx32 + gp * 8) = v;
-      }
+    for (int i = 0; i < NI; ++i) {  // all LDS reads first, then the stores
+      const unsigned u = tid + i * NT, r = u / NCX, gp = u % NCX;
+      v[i] = *reinterpret_cast<const u32x4 *>(ys + r * (P * 2) + (gp ^ chunk_swz(r, NCX)) * 16);
+    }
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const unsigned u = tid + i * NT, r = u / NCX, gp = u % NCX;
+      if ((int)r < ci.len) *reinterpret_cast<u32x4 *>(yb + r * ldx32 + gp * 8) = v[i];
     }
   };
 
@@ -669,14 +672,17 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     wait_vmcnt<0>();  // this head's loads; the stores of y two heads back
     __syncthreads();  // ... for every thread; the previous head is done everywhere
     if (hi > 0) store_y(Lh, hh - 1, smem + (slot ? XS0 : XS1));
-    {  // column s = tid % Q, rows j in this thread's half
-      const int s = tid_o & (Q - 1);
+    {  // column s = tid % Q; rows 1..3 (first half of the block) or 4..7
+      const unsigned s = tid_o & (Q - 1);
+      const int j0 = tid_o < Q ? 1 : NLT / 2;
+      const int jend = tid_o < Q ? NLT / 2 : NLT;
       const float as = sa[s], ds = sd[s];
+      float e[NLT / 2];
 #pragma unroll
-      for (int jj = 1; jj <= NLT / 2; ++jj) {
-        const int j = tid_o < Q ? jj : jj + NLT / 2 - 1;
-        if (j < NLT && s < 32 * j) vt[j * Q + s] = __expf(sa[32 * j] - as) * ds;
-      }
+      for (int jj = 0; jj < NLT / 2; ++jj) e[jj] = __expf(sa[32 * (j0 + jj)] - as) * ds;
+#pragma unroll
+      for (int jj = 0; jj < NLT / 2; ++jj)
+        if (j0 + jj < jend && (int)s < 32 * (j0 + jj)) vt[(j0 + jj) * Q + s] = e[jj];
     }
     __syncthreads();  // v table ready; the other slot's y has been read out
     if (hi + 1 < nh) issue_head(Lh, hh + 1, slot ^ 1);

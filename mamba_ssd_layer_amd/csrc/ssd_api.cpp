@@ -331,6 +331,55 @@ ssd_status ssd_step(const void *x, const float *dt, const float *A, const void *
                                      (int)N, (int)G, static_cast<hipStream_t>(stream)));
 }
 
+ssd_status ssd_conv1d_silu(const void *in, int64_t in_stride, const float *weight,
+                           const float *bias, int K, void *out, int64_t out_stride, int64_t batch,
+                           int64_t seqlen, int64_t nseq, const int32_t *cu_seqlens,
+                           int64_t channels, int32_t io_dtype, void *stream) {
+  if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
+  const int64_t vec = io_dtype == SSD_BF16 ? 8 : 4;
+  const size_t io = io_dtype == SSD_BF16 ? 2 : 4;
+  if (K < 1 || channels < 1 || batch < 1 || seqlen < 0 || nseq < 0) return SSD_ERR_INVALID_ARG;
+  if (K > 4) return SSD_ERR_UNSUPPORTED;
+  if (channels % vec || in_stride < channels || out_stride < channels || in_stride % vec ||
+      out_stride % vec)
+    return SSD_ERR_INVALID_ARG;
+  if (nseq > 0 && batch != 1) return SSD_ERR_INVALID_ARG;
+  if (nseq == 0 && seqlen > 0 && batch > INT64_MAX / seqlen) return SSD_ERR_UNSUPPORTED;
+  const int64_t T = nseq > 0 ? seqlen : batch * seqlen;
+  if (T >= ((int64_t)1 << 31) || nseq >= ((int64_t)1 << 31) || channels >= ((int64_t)1 << 31))
+    return SSD_ERR_UNSUPPORTED;
+  if (!weight || !aligned(weight, 4) || (bias && !aligned(bias, 4))) return SSD_ERR_INVALID_ARG;
+  if (nseq > 0 && (!cu_seqlens || !aligned(cu_seqlens, 4))) return SSD_ERR_INVALID_ARG;
+  if (T == 0) return SSD_OK;
+  if (!in || !out || !aligned(in, 16) || !aligned(out, 16)) return SSD_ERR_INVALID_ARG;
+  const size_t inb = ((size_t)(T - 1) * in_stride + channels) * io;
+  const size_t outb = ((size_t)(T - 1) * out_stride + channels) * io;
+  if (overlaps(in, inb, out, outb)) return SSD_ERR_INVALID_ARG;
+  return hip_status(ssd::launch_conv1d_silu(in, in_stride, weight, bias, K, out, out_stride, T,
+                                            nseq > 0 ? 0 : seqlen, (int)nseq,
+                                            nseq > 0 ? cu_seqlens : nullptr, channels,
+                                            io_dtype == SSD_BF16, static_cast<hipStream_t>(stream)));
+}
+
+ssd_status ssd_gate_rmsnorm(const void *y, const void *z, const float *weight, float eps, void *out,
+                            int64_t tokens, int64_t width, int32_t io_dtype, void *stream) {
+  if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
+  const int64_t vec = io_dtype == SSD_BF16 ? 8 : 4;
+  const size_t io = io_dtype == SSD_BF16 ? 2 : 4;
+  if (tokens < 0 || width < 1 || width % vec || !(eps >= 0.f)) return SSD_ERR_INVALID_ARG;
+  if (tokens >= ((int64_t)1 << 31) || width >= ((int64_t)1 << 30)) return SSD_ERR_UNSUPPORTED;
+  if (weight && !aligned(weight, 4)) return SSD_ERR_INVALID_ARG;
+  if (tokens == 0) return SSD_OK;
+  if (!y || !z || !out || !aligned(y, 16) || !aligned(z, 16) || !aligned(out, 16))
+    return SSD_ERR_INVALID_ARG;
+  const size_t nb = (size_t)tokens * width * io;
+  if ((out != y && overlaps(out, nb, y, nb)) || (out != z && overlaps(out, nb, z, nb)))
+    return SSD_ERR_INVALID_ARG;
+  return hip_status(ssd::launch_gate_rmsnorm(y, z, weight, eps, out, tokens, (int)width,
+                                             io_dtype == SSD_BF16,
+                                             static_cast<hipStream_t>(stream)));
+}
+
 const char *ssd_status_string(ssd_status status) {
   switch (status) {
     case SSD_OK: return "ok";

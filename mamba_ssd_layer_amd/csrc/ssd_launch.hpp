@@ -50,6 +50,14 @@ hipError_t launch_step(const void *x, const float *dt, const float *A, const voi
                        const float *D, float *state, void *y, bool bf16, int64_t S, int H, int P,
                        int N, int G, hipStream_t stream);
 
+// the core's block neighbours: causal depthwise conv1d + SiLU, SiLU gate + RMS norm
+hipError_t launch_conv1d_silu(const void *in, int64_t in_stride, const float *weight,
+                              const float *bias, int K, void *out, int64_t out_stride, int64_t T,
+                              int64_t seqlen, int nseq, const int32_t *cu_seqlens,
+                              int64_t channels, bool bf16, hipStream_t stream);
+hipError_t launch_gate_rmsnorm(const void *y, const void *z, const float *weight, float eps,
+                               void *out, int64_t tokens, int width, bool bf16, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 inline int device_cus() {
   static int cache[64];

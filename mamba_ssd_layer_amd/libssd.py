@@ -59,7 +59,8 @@ class ssd_workspace_layout(ctypes.Structure):
 
 EXPORTS = ["ssd_workspace_size", "ssd_get_workspace_layout", "ssd_chunk_scan_fwd",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
-           "ssd_step", "ssd_status_string", "ssd_version"]
+           "ssd_step", "ssd_conv1d_silu", "ssd_gate_rmsnorm", "ssd_status_string",
+           "ssd_version"]
 
 
 def _load() -> ctypes.CDLL:
@@ -85,6 +86,11 @@ def _load() -> ctypes.CDLL:
     lib.ssd_chunk_scan.argtypes = [p, p, p, p, p, i32, dims_p, p, sz, p]
     lib.ssd_step.restype = i32
     lib.ssd_step.argtypes = [p, p, p, p, p, p, p, p, dims_p, p]
+    i64 = ctypes.c_int64
+    lib.ssd_conv1d_silu.restype = i32
+    lib.ssd_conv1d_silu.argtypes = [p, i64, p, p, i32, p, i64, i64, i64, i64, p, i64, i32, p]
+    lib.ssd_gate_rmsnorm.restype = i32
+    lib.ssd_gate_rmsnorm.argtypes = [p, p, p, ctypes.c_float, p, i64, i64, i32, p]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_version.restype = i32
@@ -186,3 +192,27 @@ def ssd_chunk_scan(x, B, C, D, y, chunk_len, dims, workspace, stream=None) -> No
 def ssd_step(x, dt, A, B, C, D, state, y, dims, stream=None) -> None:
     _check(_lib.ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
                          _ptr(y), ctypes.byref(dims), _stream(stream)))
+
+
+def _raw_ptr(t: Optional[torch.Tensor], offset_elems: int = 0):
+    """Device address of t's storage start + offset (t may be a strided view)."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "tensor is not on the GPU")
+    return ctypes.c_void_p(t.data_ptr() + offset_elems * t.element_size()) if t.numel() else None
+
+
+def ssd_conv1d_silu(inp, in_stride, weight, bias, kernel_width, out, out_stride, batch, seqlen,
+                    nseq, cu_seqlens, channels, io_dtype, stream=None) -> None:
+    """inp / out: tensors whose first element is channel 0 of token 0 (row
+    strides given in elements, so they may be column slices of wider rows)."""
+    _check(_lib.ssd_conv1d_silu(_raw_ptr(inp), int(in_stride), _ptr(weight), _ptr(bias),
+                                int(kernel_width), _raw_ptr(out), int(out_stride), int(batch),
+                                int(seqlen), int(nseq), _ptr(cu_seqlens), int(channels),
+                                int(io_dtype), _stream(stream)))
+
+
+def ssd_gate_rmsnorm(y, z, weight, eps, out, tokens, width, io_dtype, stream=None) -> None:
+    _check(_lib.ssd_gate_rmsnorm(_ptr(y), _ptr(z), _ptr(weight), float(eps), _ptr(out),
+                                 int(tokens), int(width), int(io_dtype), _stream(stream)))

@@ -25,7 +25,7 @@ FAKE = 0x7f0000000000  # aligned, never dereferenced: validation fails first
 def header_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(ssd_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
@@ -250,3 +250,45 @@ def test_step_overlaps():
     assert step(d, state=FAKE + (3 << 30)) == SSD_ERR_INVALID_ARG      # state == B
     assert step(d, y=FAKE + (5 << 30) + sb - 16) == SSD_ERR_INVALID_ARG  # y inside the state
     assert step(d, A=FAKE + (5 << 30) + 64) == SSD_ERR_INVALID_ARG     # A inside the state
+
+
+# ---------------------------------------------------------------- block neighbours
+def conv(**kw):
+    v = ctypes.c_void_p
+    a = dict(inp=FAKE, in_stride=64, weight=FAKE + (1 << 30), bias=None, K=4, out=FAKE + (2 << 30),
+             out_stride=64, batch=2, seqlen=100, nseq=0, cu=None, channels=64, io=SSD_BF16)
+    a.update(kw)
+    pv = lambda x: None if x is None else v(x)
+    return L.ssd_conv1d_silu(pv(a["inp"]), a["in_stride"], pv(a["weight"]), pv(a["bias"]), a["K"],
+                             pv(a["out"]), a["out_stride"], a["batch"], a["seqlen"], a["nseq"],
+                             pv(a["cu"]), a["channels"], a["io"], None)
+
+
+def test_conv1d_validation():
+    assert conv(K=0) == SSD_ERR_INVALID_ARG
+    assert conv(K=5) == SSD_ERR_UNSUPPORTED
+    assert conv(channels=60) == SSD_ERR_INVALID_ARG           # bf16: multiple of 8
+    assert conv(in_stride=32) == SSD_ERR_INVALID_ARG          # stride < channels
+    assert conv(out_stride=68) == SSD_ERR_INVALID_ARG         # not a multiple of 8
+    assert conv(weight=None) == SSD_ERR_INVALID_ARG
+    assert conv(inp=FAKE + 8) == SSD_ERR_INVALID_ARG          # 16-byte alignment
+    assert conv(out=FAKE + 64) == SSD_ERR_INVALID_ARG         # out overlaps in
+    assert conv(nseq=3, batch=2) == SSD_ERR_INVALID_ARG       # packed needs batch 1
+    assert conv(nseq=3, batch=1, cu=None) == SSD_ERR_INVALID_ARG
+    assert conv(io=5) == SSD_ERR_INVALID_ARG
+    assert conv(seqlen=0, inp=None, out=None) == SSD_OK       # nothing to do
+    assert conv(io=SSD_F32, channels=36, in_stride=36, out_stride=36, seqlen=0) == SSD_OK
+
+
+def test_gate_rmsnorm_validation():
+    v = ctypes.c_void_p
+    g = lambda y=FAKE, z=FAKE + (1 << 30), w=None, eps=1e-5, out=FAKE + (2 << 30), T=10, W=64, io=SSD_BF16: \
+        L.ssd_gate_rmsnorm(None if y is None else v(y), None if z is None else v(z),
+                           None if w is None else v(w), eps, None if out is None else v(out), T, W, io, None)
+    assert g(W=60) == SSD_ERR_INVALID_ARG
+    assert g(eps=-1.0) == SSD_ERR_INVALID_ARG
+    assert g(eps=float("nan")) == SSD_ERR_INVALID_ARG
+    assert g(y=None) == SSD_ERR_INVALID_ARG
+    assert g(out=FAKE + 16) == SSD_ERR_INVALID_ARG     # partial overlap with y
+    assert g(w=FAKE + (3 << 30) + 2) == SSD_ERR_INVALID_ARG
+    assert g(T=0, y=None, z=None, out=None) == SSD_OK
