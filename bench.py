@@ -167,6 +167,51 @@ def decode_step(torch, ssd, workloads, dev, steps: int, warmup: int):
                          "algorithmic_bytes": nbytes}}
 
 
+def block_neighbours(torch, ssd, dev, w, steps: int, warmup: int):
+    """The core's neighbours at the workload's widths: the causal conv1d + SiLU
+    over x|B|C (H*P + 2*G*N channels) and the SiLU gate + RMS norm over y
+    (H*P channels), on seeded synthetic bf16 inputs generated on the device.
+    Both are HBM-bound; bytes = one read of each input and one write."""
+    gen = torch.Generator(device=dev).manual_seed(6000)
+    T, HP, GN = w.tokens, w.nheads * w.headdim, w.ngroups * w.dstate
+    lead = (w.batch, w.seqlen) if not w.nseq else (1, T)
+    C = HP + 2 * GN
+    xbc = torch.randn(*lead, C, generator=gen, device=dev).to(torch.bfloat16)
+    cw = torch.randn(C, 4, generator=gen, device=dev) * 0.5
+    cb = torch.randn(C, generator=gen, device=dev) * 0.1
+    y = torch.randn(T, HP, generator=gen, device=dev).to(torch.bfloat16)
+    z = torch.randn(T, HP, generator=gen, device=dev).to(torch.bfloat16)
+    nw = 1.0 + 0.1 * torch.randn(HP, generator=gen, device=dev)
+    cout = torch.empty_like(xbc)
+    gout = torch.empty_like(y)
+    stream = torch.cuda.current_stream()
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    res = {}
+    for name, fn, nbytes in (
+            ("conv1d_silu", lambda: ssd.conv1d_silu(xbc, cw, cb, out=cout), 2 * xbc.numel() * 2),
+            ("gate_rmsnorm", lambda: ssd.gate_rmsnorm(y, z, nw, 1e-5, out=gout), 3 * y.numel() * 2)):
+        us = timed(fn)
+        gbs = nbytes / (us * 1e-6) / 1e9
+        res[name] = {"us": round(us, 2), "bytes": nbytes, "GBs": round(gbs, 1),
+                     "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+        log(f"bench: {name}: {us:.1f} us, {gbs:.0f} GB/s")
+    res["widths"] = {"conv_channels": C, "gate_channels": HP, "tokens": T}
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -177,6 +222,8 @@ def main() -> int:
     ap.add_argument("--no-stage-timing", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the single-token decode (ssd_step) measurement")
+    ap.add_argument("--no-block", action="store_true",
+                    help="skip the conv1d+SiLU and gate+RMS-norm measurements")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
                     help="first run 3 elementwise copies (dst = -src, one read and one write per "
                          "element) of MIB MiB: a known-size reference for the hardware byte "
@@ -311,6 +358,10 @@ def main() -> int:
     if not args.no_decode:
         decode = decode_step(torch, ssd, workloads, dev, args.steps, args.warmup)
 
+    block = None
+    if not args.no_block:
+        block = block_neighbours(torch, ssd, dev, w, args.steps, args.warmup)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("bench: timing the CPU oracle on a sample")
@@ -323,6 +374,7 @@ def main() -> int:
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "config": {**workloads.describe(w), "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "decode_step": decode,
+        "block_neighbours": block,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -140,50 +140,90 @@ __global__ __launch_bounds__(256) void k_conv1d_silu(const IO *__restrict__ in, 
   }
 }
 
-// Block = one token row of `width` channels.  Pass 1 sums g^2 (g = y silu(z))
-// over the row; pass 2 recomputes g from the same (cached) row and writes
-// g * rsqrt(mean + eps) * weight, or g alone without a weight.
-template <typename IO>
+// Block = ROWS consecutive token rows of `width` channels; thread t owns the
+// 16-byte column chunks t, t + 256, ... (up to CACHE of them), whose weights it
+// loads once.  Per row: g = y silu(z) in registers, squares summed over the
+// row (cross-lane shuffles, then one LDS slot per wavefront, double-buffered
+// so one barrier per row suffices), then g * rsqrt(mean + eps) * weight is
+// written; without a weight, g.  Rows wider than 256 * CACHE chunks form g
+// again for the chunks past the cache.
+template <typename IO, int CACHE, int ROWS>
 __global__ __launch_bounds__(256) void k_gate_rmsnorm(const IO *y, const IO *z,
                                                       const float *__restrict__ weight, float eps,
-                                                      IO *out, int width) {
+                                                      IO *out, int64_t tokens, int width) {
   constexpr int V = Vec<IO>::N;
-  __shared__ float part[4];
-  const int64_t row = blockIdx.x;
-  const IO *yr = y + row * width;
-  const IO *zr = z + row * width;
-  IO *orow = out + row * width;
+  __shared__ float part[2][4];
   const int nvec = width / V;
-  float scale = 1.f;
-  if (weight) {
+  const int tid = threadIdx.x;
+  float wv[CACHE][V];
+#pragma unroll
+  for (int k = 0; k < CACHE; ++k) {
+    const int i = tid + 256 * k;
+#pragma unroll
+    for (int v = 0; v < V; ++v) wv[k][v] = (weight && i < nvec) ? weight[i * V + v] : 1.f;
+  }
+  const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+  for (int rr = 0; rr < ROWS; ++rr) {
+    const int64_t row = r0 + rr;
+    if (row >= tokens) break;
+    const IO *yr = y + row * width;
+    const IO *zr = z + row * width;
+    IO *orow = out + row * width;
+    float g[CACHE][V];
     float ss = 0.f;
-    for (int i = threadIdx.x; i < nvec; i += 256) {
+#pragma unroll
+    for (int k = 0; k < CACHE; ++k) {
+      const int i = tid + 256 * k;
+      if (i < nvec) {
+        float a[V], c[V];
+        Vec<IO>::load(yr + i * V, a);
+        Vec<IO>::load(zr + i * V, c);
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          g[k][v] = a[v] * silu(c[v]);
+          ss += g[k][v] * g[k][v];
+        }
+      }
+    }
+    for (int i = tid + 256 * CACHE; i < nvec; i += 256) {
       float a[V], c[V];
       Vec<IO>::load(yr + i * V, a);
       Vec<IO>::load(zr + i * V, c);
 #pragma unroll
       for (int v = 0; v < V; ++v) {
-        const float g = a[v] * silu(c[v]);
-        ss += g * g;
+        const float gv = a[v] * silu(c[v]);
+        ss += gv * gv;
       }
     }
+    float scale = 1.f;
+    if (weight) {
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
-    if ((threadIdx.x & 63) == 0) part[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    const float tot = part[0] + part[1] + part[2] + part[3];
-    scale = rsqrtf(tot / width + eps);
-  }
-  for (int i = threadIdx.x; i < nvec; i += 256) {
-    float a[V], c[V], o[V];
-    Vec<IO>::load(yr + i * V, a);
-    Vec<IO>::load(zr + i * V, c);
-#pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const float g = a[v] * silu(c[v]);
-      o[v] = weight ? g * scale * weight[i * V + v] : g;
+      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      if ((tid & 63) == 0) part[rr & 1][tid >> 6] = ss;
+      __syncthreads();
+      scale = rsqrtf((part[rr & 1][0] + part[rr & 1][1] + part[rr & 1][2] + part[rr & 1][3]) / width + eps);
     }
-    Vec<IO>::store(orow + i * V, o);
+#pragma unroll
+    for (int k = 0; k < CACHE; ++k) {
+      const int i = tid + 256 * k;
+      if (i < nvec) {
+        float o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = g[k][v] * scale * wv[k][v];
+        Vec<IO>::store(orow + i * V, o);
+      }
+    }
+    for (int i = tid + 256 * CACHE; i < nvec; i += 256) {
+      float a[V], c[V], o[V];
+      Vec<IO>::load(yr + i * V, a);
+      Vec<IO>::load(zr + i * V, c);
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const float gv = a[v] * silu(c[v]);
+        o[v] = weight ? gv * scale * weight[i * V + v] : gv;
+      }
+      Vec<IO>::store(orow + i * V, o);
+    }
   }
 }
 
@@ -223,15 +263,16 @@ hipError_t launch_gate_rmsnorm(const void *y, const void *z, const float *weight
                                void *out, int64_t tokens, int width, bool bf16,
                                hipStream_t stream) {
   if (tokens == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(tokens));
+  constexpr int kRows = 16;
+  const dim3 grid(static_cast<unsigned>((tokens + kRows - 1) / kRows));
   if (bf16)
-    hipLaunchKernelGGL(k_gate_rmsnorm<uint16_t>, grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_gate_rmsnorm<uint16_t, 3, kRows>), grid, dim3(256), 0, stream,
                        static_cast<const uint16_t *>(y), static_cast<const uint16_t *>(z), weight,
-                       eps, static_cast<uint16_t *>(out), width);
+                       eps, static_cast<uint16_t *>(out), tokens, width);
   else
-    hipLaunchKernelGGL(k_gate_rmsnorm<float>, grid, dim3(256), 0, stream,
+    hipLaunchKernelGGL((k_gate_rmsnorm<float, 5, kRows>), grid, dim3(256), 0, stream,
                        static_cast<const float *>(y), static_cast<const float *>(z), weight, eps,
-                       static_cast<float *>(out), width);
+                       static_cast<float *>(out), tokens, width);
   return hipGetLastError();
 }
 
