@@ -234,6 +234,21 @@ ssd_status ssd_conv1d_silu(const void *in, int64_t in_stride, const float *weigh
 ssd_status ssd_gate_rmsnorm(const void *y, const void *z, const float *weight, float eps, void *out,
                             int64_t tokens, int64_t width, int32_t io_dtype, void *stream);
 
+/* The same forward in one pass per (sequence, head), the P x N state kept on
+ * chip across chunks, so that only x, B, C, dt and y cross HBM (no workspace,
+ * no chunk_len: it walks chunks of 32 tokens, and chunking is exact).  The
+ * arguments, layouts, aliasing rules and results are those of
+ * ssd_chunk_scan_fwd, to rounding.
+ * Supported: SSD_BF16, headdim P == 64, dstate N in {64, 128}; else
+ * SSD_ERR_UNSUPPORTED.  It keeps one block per (sequence, head) busy for the
+ * sequence's whole length, so it pays off when sequences x heads fills the
+ * GPU (hundreds or more); a single long sequence is better served by the
+ * chunk-parallel ssd_chunk_scan_fwd.  Returns after enqueueing. */
+ssd_status ssd_fused_fwd(const void *x, const float *dt, const float *A, const void *B,
+                         const void *C, const float *D, const float *init_state,
+                         const int32_t *cu_seqlens, void *y, float *final_state,
+                         const ssd_dims *dims, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -7,6 +7,8 @@ include/ssd.h).  This package is its Python face:
   chunk_scan_fwd()   convenience wrapper: infers the dims from torch tensors,
                      allocates y / final_state / workspace, runs the forward
   SSDForward         a reusable plan (fixed dims, workspace allocated once)
+  fused_fwd()        the same forward in one pass per (sequence, head), no workspace
+                     (bf16, headdim 64, dstate 64 / 128)
   step()             one recurrent decode step per sequence, state updated in place
   conv1d_silu()      the causal depthwise conv1d + SiLU before the core
   gate_rmsnorm()     y * SiLU(z), then RMS norm over the channel width, after it
@@ -30,7 +32,7 @@ from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsuppo
 
 __all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDError", "SSDInvalidArgument",
            "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "step",
-           "conv1d_silu", "gate_rmsnorm"]
+           "conv1d_silu", "gate_rmsnorm", "fused_fwd"]
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -133,6 +135,26 @@ def chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.
     dims = dims_for(x, B, cu_seqlens)
     plan = SSDForward(dims, chunk_len, device=x.device)
     return plan(x, dt, A, B, C, D, init_state, cu_seqlens)
+
+
+def fused_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+              C: torch.Tensor, D: Optional[torch.Tensor] = None,
+              init_state: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+              final_state: Optional[torch.Tensor] = None, want_final: bool = True,
+              stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """y, final_state = SSD forward in one pass per (sequence, head) (ssd_fused_fwd:
+    bf16, headdim 64, dstate 64 or 128; no workspace).  Same arguments and
+    results as chunk_scan_fwd."""
+    dims = dims_for(x, B, cu_seqlens)
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and want_final:
+        nrows = dims.nseq if dims.nseq > 0 else dims.batch
+        final_state = torch.empty((nrows, dims.nheads, dims.headdim, dims.dstate),
+                                  dtype=torch.float32, device=x.device)
+    libssd.ssd_fused_fwd(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, dims, stream)
+    return y, final_state
 
 
 def step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

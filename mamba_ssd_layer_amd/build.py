@@ -18,7 +18,8 @@ LIB = os.path.join(HERE, "lib", "libssd.so")
 OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["ssd_api.cpp", "k_scan_prep.hip", "k_chunk_state.hip", "k_chunk_scan.hip", "k_f32.hip",
-           "k_step.hip", "k_block.hip"]
+           "k_step.hip", "k_block.hip",
+           "k_fused.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

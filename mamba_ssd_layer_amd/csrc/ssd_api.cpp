@@ -380,6 +380,26 @@ ssd_status ssd_gate_rmsnorm(const void *y, const void *z, const float *weight, f
                                              static_cast<hipStream_t>(stream)));
 }
 
+ssd_status ssd_fused_fwd(const void *x, const float *dt, const float *A, const void *B,
+                         const void *C, const float *D, const float *init_state,
+                         const int32_t *cu_seqlens, void *y, float *final_state,
+                         const ssd_dims *dims, void *stream) {
+  Plan p;
+  ssd_status s = make_plan(dims, 64, &p);  // the chunk length only sizes the (unused) workspace
+  if (s != SSD_OK) return s;
+  if (!p.bf16 || !ssd::fused_supported(p.geo.P, p.geo.N)) return SSD_ERR_UNSUPPORTED;
+  if (p.geo.nrows >= ((int64_t)1 << 24) / p.geo.H) return SSD_ERR_UNSUPPORTED;
+  if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
+  if ((s = check_state_args(x, B, p)) != SSD_OK) return s;
+  if ((s = check_pass_args(init_state, final_state, p)) != SSD_OK) return s;
+  if ((s = check_scan_args(x, B, C, D, y, dt, p)) != SSD_OK) return s;
+  const ssd::Geometry &g = p.geo;
+  return hip_status(ssd::launch_fused(x, dt, A, B, C, D, init_state,
+                                      g.packed ? cu_seqlens : nullptr, g.L, g.tokens, (int)g.nrows,
+                                      g.H, g.P, g.N, g.G, y, final_state,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 const char *ssd_status_string(ssd_status status) {
   switch (status) {
     case SSD_OK: return "ok";

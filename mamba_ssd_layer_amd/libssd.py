@@ -59,8 +59,8 @@ class ssd_workspace_layout(ctypes.Structure):
 
 EXPORTS = ["ssd_workspace_size", "ssd_get_workspace_layout", "ssd_chunk_scan_fwd",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
-           "ssd_step", "ssd_conv1d_silu", "ssd_gate_rmsnorm", "ssd_status_string",
-           "ssd_version"]
+           "ssd_step", "ssd_conv1d_silu", "ssd_gate_rmsnorm", "ssd_fused_fwd",
+           "ssd_status_string", "ssd_version"]
 
 
 def _load() -> ctypes.CDLL:
@@ -91,6 +91,8 @@ def _load() -> ctypes.CDLL:
     lib.ssd_conv1d_silu.argtypes = [p, i64, p, p, i32, p, i64, i64, i64, i64, p, i64, i32, p]
     lib.ssd_gate_rmsnorm.restype = i32
     lib.ssd_gate_rmsnorm.argtypes = [p, p, p, ctypes.c_float, p, i64, i64, i32, p]
+    lib.ssd_fused_fwd.restype = i32
+    lib.ssd_fused_fwd.argtypes = [p, p, p, p, p, p, p, p, p, p, dims_p, p]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_version.restype = i32
@@ -192,6 +194,13 @@ def ssd_chunk_scan(x, B, C, D, y, chunk_len, dims, workspace, stream=None) -> No
 def ssd_step(x, dt, A, B, C, D, state, y, dims, stream=None) -> None:
     _check(_lib.ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
                          _ptr(y), ctypes.byref(dims), _stream(stream)))
+
+
+def ssd_fused_fwd(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, dims,
+                  stream=None) -> None:
+    _check(_lib.ssd_fused_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                              _ptr(init_state), _ptr(cu_seqlens), _ptr(y), _ptr(final_state),
+                              ctypes.byref(dims), _stream(stream)))
 
 
 def _raw_ptr(t: Optional[torch.Tensor], offset_elems: int = 0):

@@ -292,3 +292,46 @@ def test_gate_rmsnorm_validation():
     assert g(out=FAKE + 16) == SSD_ERR_INVALID_ARG     # partial overlap with y
     assert g(w=FAKE + (3 << 30) + 2) == SSD_ERR_INVALID_ARG
     assert g(T=0, y=None, z=None, out=None) == SSD_OK
+
+
+# ---------------------------------------------------------------- ssd_fused_fwd
+def fused(d, **kw):
+    """ssd_fused_fwd with distinct, aligned fake pointers 1 GiB apart (overridable)."""
+    v = ctypes.c_void_p
+    args = dict(x=FAKE, dt=FAKE + (1 << 30), A=FAKE + (2 << 30), B=FAKE + (3 << 30),
+                C=FAKE + (4 << 30), D=None, init=None, cu=None, y=FAKE + (7 << 30),
+                fin=FAKE + (5 << 30))
+    args.update(kw)
+    return L.ssd_fused_fwd(*(None if args[k] is None else v(args[k])
+                             for k in ("x", "dt", "A", "B", "C", "D", "init", "cu", "y", "fin")),
+                           ctypes.byref(d), None)
+
+
+@pytest.mark.parametrize("mut,expect", [
+    (dict(io_dtype=SSD_F32), SSD_ERR_UNSUPPORTED),    # bf16 only
+    (dict(headdim=128), SSD_ERR_UNSUPPORTED),         # P == 64 only
+    (dict(dstate=32), SSD_ERR_UNSUPPORTED),
+    (dict(dstate=256), SSD_ERR_UNSUPPORTED),
+    (dict(ngroups=3), SSD_ERR_INVALID_ARG),
+    (dict(reserved=1), SSD_ERR_INVALID_ARG),
+    (dict(batch=-1), SSD_ERR_INVALID_ARG),
+])
+def test_fused_dims(mut, expect):
+    d = good()
+    for k, val in mut.items():
+        setattr(d, k, val)
+    assert fused(d) == expect
+
+
+def test_fused_pointers_and_overlaps():
+    d = good()
+    for k in ("x", "dt", "A", "B", "C", "y"):
+        assert fused(d, **{k: None}) == SSD_ERR_INVALID_ARG, k
+    assert fused(d, x=FAKE + 8) == SSD_ERR_INVALID_ARG               # 16-byte alignment
+    assert fused(d, init=FAKE + (6 << 30) + 4) == SSD_ERR_INVALID_ARG
+    assert fused(d, y=FAKE) == SSD_ERR_INVALID_ARG                   # y == x
+    assert fused(d, y=FAKE + (3 << 30) + 64) == SSD_ERR_INVALID_ARG  # y over B
+    base = FAKE + (6 << 30)
+    assert fused(d, init=base, fin=base + 256) == SSD_ERR_INVALID_ARG  # partial state overlap
+    dp = make_dims(1, 1000, 4, 64, 64, 2, 3, SSD_BF16)
+    assert fused(dp, cu=None) == SSD_ERR_INVALID_ARG                 # packed needs cu_seqlens
