@@ -239,8 +239,8 @@ ssd_status ssd_gate_rmsnorm(const void *y, const void *z, const float *weight, f
  * no chunk_len: it walks chunks of 32 tokens, and chunking is exact).  The
  * arguments, layouts, aliasing rules and results are those of
  * ssd_chunk_scan_fwd, to rounding.
- * Supported: SSD_BF16, headdim P == 64, dstate N in {64, 128}; else
- * SSD_ERR_UNSUPPORTED.  It keeps one block per (sequence, head) busy for the
+ * Supported: SSD_BF16, headdim P == 64, dstate N in {64, 128}, an even
+ * number of heads per group (nheads / ngroups); else SSD_ERR_UNSUPPORTED.  It keeps one block per (sequence, head) busy for the
  * sequence's whole length, so it pays off when sequences x heads fills the
  * GPU (hundreds or more); a single long sequence is better served by the
  * chunk-parallel ssd_chunk_scan_fwd.  Returns after enqueueing. */

@@ -4,32 +4,38 @@
 // Algorithm", with the three chunk-level steps -- chunk state, hand-off,
 // output -- done back to back for each chunk instead of as separate passes
 // over all chunks).  Chunking is exact, so the chunk length is a free choice:
-// this kernel walks 32-token chunks (one MFMA tile), for which the intra-chunk
-// product is a single diagonal tile.
+// this kernel walks 32-token chunks, for which the intra-chunk product is one
+// 32 x 32 causal tile.
 //
-// Design.  Block = (sequence, head) in XCD-aware order (all heads of a
-// sequence on one XCD, so its B and C rows are read from one L2), 2
-// wavefronts; wavefront w owns rows p in [32w, 32w + 32) of the P x N state,
-// held transposed (h^T, rows n, columns p) as N/32 fp32 MFMA accumulator
-// tiles.  Per 32-token chunk, with the next chunk's x and B arriving in the
-// other half of a two-slot LDS ring (direct-to-LDS loads) and its C rows and
-// dt in registers:
-//   1. acum_l = inclusive cumulative sum of dt A over the chunk (a wavefront
-//      scan), and the weights w_l = exp(acum_last - acum_l) dt_l;
-//   2. inter term: Y^T = exp(acum_l) Hprev . C^T on MFMA, the A-operand being
-//      the state registers rounded to bf16 (their row order is the K order;
-//      C is read in the same order);
-//   3. intra term: Z^T = B . C^T on MFMA (same K order), the causal decay
-//      mask exp(acum_l - acum_s) dt_s applied in registers (masked before the
-//      exponent), then Y^T += X^T . G^T with the accumulator as the B-operand
-//      (X^T from transposing LDS reads in the accumulator's row order); plus
-//      D x in fp32;
-//   4. state: h^T = exp(acum_last) h^T + B^T . (w x) on MFMA, from
-//      transposing LDS reads of B and x (x scaled by w_l in fp32, rounded
-//      once);
-//   5. y, rounded to bf16, is staged in LDS and stored at the next chunk's
-//      top in 16-byte row segments.
-// No workspace: nothing but x, B, C, dt (and y) crosses HBM.
+// Design.  Block = (sequence, two heads of one group) in XCD-aware order (all
+// heads of a sequence on one XCD, so its B and C rows come from one L2), 4
+// wavefronts: wavefront (head hh, half ph) owns state rows p in
+// [32 ph, 32 ph + 32) of head hh, held transposed (h^T, rows n, columns p) as
+// 2 x N/16 fp32 tiles of the 16x16x32 bf16 MFMA.  The two heads share their B
+// and C tiles in LDS.
+//
+// Data movement.  A three-slot LDS ring per block holds chunk k's x (each
+// wavefront's own 32 x 32 slice), B, C and dt (each wavefront's head) while
+// chunk k + 2 is in flight (direct-to-LDS loads).  Vector-memory operations
+// complete in issue order, so a wavefront knows chunk k has landed once at
+// most the operations it issued after that chunk are pending; it waits for
+// exactly that count, then one barrier per chunk publishes the tiles.  y of a
+// chunk is staged (bf16) in the wavefront's own x slice of that chunk and
+// stored in 16-byte row segments at the next chunk's top, before that slot is
+// refilled.  No workspace: nothing but x, B, C, dt and y crosses HBM.
+//
+// Per chunk and wavefront (a_l = cumulative sum of dt A within the chunk,
+// from a DPP scan of the 32 dt values):
+//   1. inter term: Y^T = h C^T on MFMA, the A-operand being the state rows
+//      rounded to bf16 in their accumulator order (C read in the same order),
+//      then scaled by exp(a_l);
+//   2. intra term: Z^T = B C^T for the three nonzero 16 x 16 tiles of the
+//      causal 32 x 32 block (same K order), the decay exp(a_l - a_s) dt_s
+//      applied per element in the log2 domain and the tile above the diagonal
+//      masked, then Y^T += X^T G^T with the accumulators as B-operands and
+//      X^T from transposing LDS reads in the matching token order; plus D x;
+//   3. state: h^T = exp(a_last) h^T + B^T (w x) with w_s = exp(a_last - a_s)
+//      dt_s, from transposing reads of B and the same X^T registers.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -37,48 +43,77 @@ namespace ssd {
 
 namespace {
 
-// Transposing read of a 16-token K step: lane (col, kg) receives element
-// [r0 + 8kg + j][c0 + col], j = 0..7, of a row-major bf16 tile with `ncc`
-// 16-byte chunks per row (chunk-swizzled), as 4 words in K order.
-__device__ __forceinline__ u32x4 tr_k16(int lane, const unsigned char *tile, int ncc, int r0, int c0) {
-  const int kg = lane >> 5, gq = lane >> 4, d = lane & 15;
-  const int cidx = c0 + 16 * (gq & 1) + 4 * (d & 3);
-  u32x2 part[2];
-#pragma unroll
-  for (int hf = 0; hf < 2; ++hf) {
-    const int row = r0 + 8 * kg + 4 * hf + (d >> 2);
-    const int cc = (cidx >> 3) ^ chunk_swz(row, ncc);
-    part[hf] = lds_read_tr16(tile + row * (ncc * 16) + cc * 16 + (cidx & 7) * 2);
-  }
-  return u32x4{part[0].x, part[0].y, part[1].x, part[1].y};
+constexpr float kLog2e = 1.4426950408889634f;
+
+// v_mfma_f32_16x16x32_bf16: D(16x16) += A(16x32) * B(32x16), wave64.  Lane i
+// holds A[row i%16][k = 8(i/16) .. +7] and B[k = 8(i/16) .. +7][col i%16];
+// result register r of lane i is D[row 4(i/16) + r][col i%16].
+__device__ __forceinline__ f32x4 mfma16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float exp2_fast(float v) { return __builtin_amdgcn_exp2f(v); }
+
+// DPP move of v across lanes (0 where the source lane is outside the row or
+// the destination row is masked off).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+
+// Inclusive prefix sum over lanes 0..31 and, independently, over 32..63:
+// shifts 1, 2, 4, 8 within each 16-lane row, then row 15's total carried
+// into rows 1 and 3.
+__device__ __forceinline__ float scan32(float a) {
+  a += dpp<0x111, 0xF>(a);
+  a += dpp<0x112, 0xF>(a);
+  a += dpp<0x114, 0xF>(a);
+  a += dpp<0x118, 0xF>(a);
+  a += dpp<0x142, 0xA>(a);
+  return a;
+}
+
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int N>
-__global__ __launch_bounds__(128) void k_ssd_fused(
+__global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
     const float *__restrict__ h0, const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows,
     int H, int G, uint16_t *__restrict__ y, float *__restrict__ hfin) {
-  constexpr int P = 64, CQ = 32;           // head dim, chunk length
-  constexpr int NT = N / 32;               // state tiles per wavefront (over n)
-  constexpr int KN = N / 16;               // K steps over n
-  constexpr int NCX = P / 8, NCB = N / 8;  // 16-byte chunks per x / B row
-  constexpr int XB = CQ * P * 2;           // x of a chunk
-  constexpr int BB = CQ * N * 2;           // B of a chunk
-  constexpr int LYS = 32 + 8;              // y staging row (bf16 elements)
-  constexpr int XI = XB / 1024 / 2, BI = BB / 1024 / 2;  // 1 KB direct loads per wavefront
-  static_assert(XI * 2048 == XB && BI * 2048 == BB, "1 KB loads");
-  // [XS0][XS1][BS0][BS1][CS0][CS1][YS w0][YS w1][AD w0][AD w1]
-  constexpr int XS0 = 0, XS1 = XB, BS0 = 2 * XB, BS1 = BS0 + BB, CS0 = BS1 + BB, CS1 = CS0 + BB;
-  constexpr int YS = CS1 + BB;
-  constexpr int YSB = CQ * LYS * 2, AD = YS + 2 * YSB, ADB = 3 * CQ * 4;
-  constexpr int TOTAL = AD + 2 * ADB + 2 * CQ * 4;
+  constexpr int P = 64, CQ = 32;
+  constexpr int NT = N / 16;   // state tiles per p-tile (over n)
+  constexpr int KQ = N / 32;   // K steps over n
+  constexpr int NCB = N / 8;   // 16-byte chunks per B / C row
+  constexpr int XW = CQ * 32 * 2;            // a wavefront's x slice of a chunk: 32 tokens x 32 p
+  constexpr int BT = CQ * N * 2;             // B (or C) of a chunk
+  constexpr int DW = 64 * 4;                 // a wavefront's dt of a chunk (lanes 32..63 repeat)
+  constexpr int OX = 0, OB = 4 * XW, OC = OB + BT, OD = OC + BT;
+  constexpr int SLOT = OD + 4 * DW;
+  constexpr int AD = 3 * SLOT;               // per wavefront: [al2 | bs2 | w], 32 floats each
+  constexpr int ADW = 3 * CQ * 4;
+  constexpr int TOTAL = AD + 4 * ADW;
+  constexpr int BCI = 2 * BT / 1024 / 4;     // 1 KB pieces of B and C per wavefront
+  constexpr int LDC = 2 + BCI + 1;           // vector-memory ops a wavefront issues per chunk load
+  constexpr int STC = 2;                     // ... per chunk of y it stores
+  static_assert(BCI * 4 * 1024 == 2 * BT, "B and C split evenly over 4 wavefronts");
+  static_assert(TOTAL <= 160 * 1024 / (N == 64 ? 3 : 2), "blocks per CU");
   __shared__ __align__(16) unsigned char smem[TOTAL];
 
-  int s, h;
-  xcd_chunk_head(H, s, h);
+  int s, pr;
+  xcd_chunk_head(H >> 1, s, pr);
   if (s >= rows) return;
-  const int g = h / (H / G);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int hh = wave >> 1, ph = wave & 1;
+  const int h = 2 * pr + hh;
+  const int g = (2 * pr) / (H / G);
   int64_t tb, len;
   if (cu) {
     tb = cu[s];
@@ -91,248 +126,266 @@ __global__ __launch_bounds__(128) void k_ssd_fused(
     len = L;
   }
   const int64_t sh = (int64_t)s * H + h;
-
-  const int tid = threadIdx.x;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int lane = tid & 63;
-  const int col = lane & 31;
-  const int kg = lane >> 5;
-  const int ldx = H * P;
-  const int ldb = G * N;
+  const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
   const float Ah = A[h];
   const float Dh = Dv ? Dv[h] : 0.f;
-  float *ad = reinterpret_cast<float *>(smem + AD + wave * ADB);  // [a | dt | w] of the chunk
+  float *adw = reinterpret_cast<float *>(smem + AD + wave * ADW);
 
-  // state h^T: tile j holds rows n = 32j + acc_row(r, kg), column p = 32w + col
-  f32x16 hst[NT];
+  // state h^T: hst[pt][j] holds rows n = 16 j + 4 g4 + r, column
+  // p = 32 ph + 16 pt + c16
+  f32x4 hst[2][NT];
 #pragma unroll
-  for (int j = 0; j < NT; ++j) {
+  for (int pt = 0; pt < 2; ++pt) {
+    const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N + 4 * g4;
 #pragma unroll
-    for (int r = 0; r < 16; ++r)
-      hst[j][r] = h0 ? h0[sh * (P * N) + (int64_t)(32 * wave + col) * N + 32 * j + acc_row(r, kg)] : 0.f;
+    for (int j = 0; j < NT; ++j)
+      hst[pt][j] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + prow + 16 * j) : f32x4{};
   }
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
 
-  float dtn = 0.f;  // dt of the chunk being loaded (wavefront 0, lanes < 32)
-  auto issue_chunk = [&](int k, int slot) {  // x, B and C rows of chunk k into the ring
+  // chunk k's loads into ring slot sl: LDC vector-memory ops per wavefront
+  auto issue = [&](int k, int sl) {
     const int64_t t0 = tb + (int64_t)k * CQ;
     const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
-    unsigned char *xs = smem + (slot ? XS1 : XS0);
-    unsigned char *bs = smem + (slot ? BS1 : BS0);
-    unsigned char *cs = smem + (slot ? CS1 : CS0);
+    const uint32_t base = lds_off(smem) + sl * SLOT;
 #pragma unroll
-    for (int i = 0; i < XI; ++i) {
-      const unsigned m = (wave * XI + i) * 64 + lane, r = m / NCX;
-      const unsigned cc = (m % NCX) ^ chunk_swz(r, NCX);
-      load_lds16(x + (t0 + min((int)r, last)) * ldx + (int64_t)h * P + cc * 8, xs + (wave * XI + i) * 1024);
+    for (int i = 0; i < 2; ++i) {  // this wavefront's x slice: 32 rows of 4 chunks
+      const int m = i * 64 + lane, r = m >> 2, cc = (m & 3) ^ chunk_swz(r, 4);
+      dma_lds16(x + (t0 + min(r, last)) * ldx + (int64_t)h * P + 32 * ph + 8 * cc,
+                base + OX + wave * XW + i * 1024);
     }
 #pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const unsigned m = (wave * BI + i) * 64 + lane, r = m / NCB;
-      const unsigned cc = (m % NCB) ^ chunk_swz(r, NCB);
-      load_lds16(Bm + (t0 + min((int)r, last)) * ldb + (int64_t)g * N + cc * 8, bs + (wave * BI + i) * 1024);
-      load_lds16(Cm + (t0 + min((int)r, last)) * ldb + (int64_t)g * N + cc * 8, cs + (wave * BI + i) * 1024);
+    for (int i = 0; i < BCI; ++i) {  // B and C pieces
+      const int u = wave * BCI + i, tile = u / (BT / 1024), pi = u % (BT / 1024);
+      const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ chunk_swz(r, NCB);
+      dma_lds16((tile ? Cm : Bm) + (t0 + min(r, last)) * ldb + (int64_t)g * N + 8 * cc,
+                base + (tile ? OC : OB) + pi * 1024);
     }
-    if (wave == 0 && lane < CQ)  // dt of the chunk (0 past the sequence's end)
-      dtn = lane <= last ? dt[(t0 + lane) * H + h] : 0.f;
+    // dt of this wavefront's head, 4 bytes a lane
+    dma_lds4(dt + (t0 + min(lane & 31, last)) * H + h, base + OD + wave * DW);
   };
-  // C operands in the state's K order: k-step q covers n-offsets
-  // 16q + {4kg .. 4kg+3} and 16q + 8 + {4kg .. 4kg+3} of token row col (the
-  // same order serves the B rows of Z)
+  // y of chunk k from its staging (the wavefront's x slice of slot sl): STC stores
+  auto store_y = [&](int k, int sl) {
+    const int64_t t0 = tb + (int64_t)k * CQ;
+    const int rem = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ));
+    const unsigned char *ys = smem + sl * SLOT + OX + wave * XW;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = i * 64 + lane, r = m >> 2, cc = m & 3;
+      const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + r * 64 + ((cc ^ chunk_swz(r, 4)) << 4));
+      if (r < rem)
+        *reinterpret_cast<u32x4 *>(y + (t0 + r) * ldx + (int64_t)h * P + 32 * ph + 8 * cc) = v;
+    }
+  };
+  // row operand of a B or C tile in the state's K order: K step q covers
+  // n = 32q + 4 g4 + {0..3} and 32q + 16 + 4 g4 + {0..3}
   auto row_op = [&](const unsigned char *tile, int row, int q) {
     const unsigned char *rp = tile + row * (N * 2);
     const int sw = chunk_swz(row, NCB);
-    const u32x2 lo = *reinterpret_cast<const u32x2 *>(rp + ((2 * q) ^ sw) * 16 + 8 * kg);
-    const u32x2 hi = *reinterpret_cast<const u32x2 *>(rp + ((2 * q + 1) ^ sw) * 16 + 8 * kg);
+    const int c0 = 4 * q + (g4 >> 1), off = 8 * (g4 & 1);
+    const u32x2 lo = *reinterpret_cast<const u32x2 *>(rp + ((c0 ^ sw) << 4) + off);
+    const u32x2 hi = *reinterpret_cast<const u32x2 *>(rp + (((c0 + 2) ^ sw) << 4) + off);
     return u32x4{lo.x, lo.y, hi.x, hi.y};
   };
-  auto store_y = [&](int k, const unsigned char *ys) {  // the wavefront's 32 p of chunk k
-    const int64_t t0 = tb + (int64_t)k * CQ;
-    const int rem = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ));
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int u = lane + 64 * i, r = u >> 2, c4 = u & 3;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + (r * LYS + 8 * c4) * 2);
-      if (r < rem) *reinterpret_cast<u32x4 *>(y + (t0 + r) * ldx + (int64_t)h * P + 32 * wave + 8 * c4) = v;
-    }
-  };
-  auto wave_sync = []() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // transposing read of 4 token rows row0 + {0..3} at column col0 + c16 of a
+  // row-major tile (ncc chunks a row, row bytes rb)
+  auto tr4 = [&](const unsigned char *tile, int rb, int ncc, int row0, int col0) {
+    const int row = row0 + (c16 >> 2), col = col0 + 4 * (c16 & 3);
+    const int cc = (col >> 3) ^ chunk_swz(row, ncc);
+    return lds_read_tr16(tile + row * rb + (cc << 4) + (col & 7) * 2);
   };
 
-  unsigned char *ysw = smem + YS + wave * YSB;
-  float *dts = reinterpret_cast<float *>(smem + AD + 2 * ADB);  // dt of the next chunk (wave 0 writes)
-  if (nck > 0) issue_chunk(0, 0);
-
+  if (nck > 0) issue(0, 0);
+  if (nck > 1) issue(1, 1);
+  int sl = 0;
 #pragma unroll 1
   for (int k = 0; k < nck; ++k) {
-    const int slot = k & 1;
-    const unsigned char *xs = smem + (slot ? XS1 : XS0);
-    const unsigned char *bs = smem + (slot ? BS1 : BS0);
-    const unsigned char *cs = smem + (slot ? CS1 : CS0);
-    wait_vmcnt<0>();  // chunk k's x, B, C, dt; the y stores of chunk k-2
-    if (wave == 0 && lane < CQ) dts[slot * CQ + lane] = dtn;
-    __syncthreads();  // ... for every thread; chunk k-1 is done everywhere
-    const float dtv = dts[slot * CQ + col];
-    if (k > 0) store_y(k - 1, ysw);
-    if (k + 1 < nck) issue_chunk(k + 1, slot ^ 1);
-    u32x4 cop[KN];
-#pragma unroll
-    for (int q = 0; q < KN; ++q) cop[q] = row_op(cs, col, q);
-
-    // 1. cumulative decay over the chunk (both halves of the wavefront hold
-    // the same 32 values), weights of the chunk state
-    float a = dtv * Ah;
-#pragma unroll
-    for (int off = 1; off < 32; off <<= 1) {
-      const float t = __shfl_up(a, off, 32);
-      if (col >= off) a += t;
+    // chunk k has landed once at most the later ops of this wavefront are
+    // pending: the y stores of iteration k-1 (k >= 2) and chunk k+1's loads
+    const bool more = k + 1 < nck;
+    if (k >= 2) {
+      if (more) wait_vmcnt<STC + LDC>(); else wait_vmcnt<STC>();
+    } else {
+      if (more) wait_vmcnt<LDC>(); else wait_vmcnt<0>();
     }
-    const float alast = __shfl(a, 31, 32);
-    if (kg == 0) {
-      ad[col] = a;
-      ad[CQ + col] = dtv;
-      ad[2 * CQ + col] = __expf(alast - a) * dtv;
+    __syncthreads();  // every wavefront's share of chunk k is in; chunk k-1 is done everywhere
+    const int slp = sl == 0 ? 2 : sl - 1;  // slot of chunk k-1, and of chunk k+2
+    if (k >= 1) store_y(k - 1, slp);
+    if (k + 2 < nck) issue(k + 2, slp);
+
+    unsigned char *xs = smem + sl * SLOT + OX + wave * XW;
+    const unsigned char *bs = smem + sl * SLOT + OB;
+    const unsigned char *cs = smem + sl * SLOT + OC;
+    const float *dts = reinterpret_cast<const float *>(smem + sl * SLOT + OD + wave * DW);
+    const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
+
+    // cumulative decay (lanes l and 32 + l hold token l) and per-token tables
+    const int tl = lane & 31;
+    const float dtv = tl <= last ? dts[lane] : 0.f;
+    const float a = scan32(dtv * Ah);
+    const float alast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 31));
+    if (lane < 32) {
+      const float al = a * kLog2e;
+      adw[tl] = al;                                            // log2 exp(a_l)
+      adw[CQ + tl] = __builtin_amdgcn_logf(dtv) - al;          // log2(dt_s exp(-a_s))
+      adw[2 * CQ + tl] = exp2_fast((alast - a) * kLog2e) * dtv;  // w_s
     }
     wave_sync();
 
-    // 2. inter term
-    f32x16 ya = f32x16{};
+    // 1. inter term
+    u32x4 cop[2][KQ];
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        const u32x4 hq{pack_bf16x2(hst[j][8 * hf + 0], hst[j][8 * hf + 1]),
-                       pack_bf16x2(hst[j][8 * hf + 2], hst[j][8 * hf + 3]),
-                       pack_bf16x2(hst[j][8 * hf + 4], hst[j][8 * hf + 5]),
-                       pack_bf16x2(hst[j][8 * hf + 6], hst[j][8 * hf + 7])};
-        ya = mfma32x32x16(as_bf16x8(hq), as_bf16x8(cop[2 * j + hf]), ya);
+      for (int q = 0; q < KQ; ++q) cop[lt][q] = row_op(cs, 16 * lt + c16, q);
+    f32x4 ya[2][2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+      for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = f32x4{};
+#pragma unroll
+    for (int q = 0; q < KQ; ++q) {
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        const f32x4 u = hst[pt][2 * q], v = hst[pt][2 * q + 1];
+        const u32x4 sop{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
+                        pack_bf16x2(v.z, v.w)};
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(sop, cop[lt][q], ya[pt][lt]);
       }
     }
-    ya *= __expf(a);
-
-    // 3. intra term (the diagonal tile) and the skip term
-    f32x16 za = f32x16{};
+    const float al0 = adw[c16], al1 = adw[16 + c16];
+    const float f0 = exp2_fast(al0), f1 = exp2_fast(al1);
 #pragma unroll
-    for (int q = 0; q < KN; ++q) za = mfma32x32x16(as_bf16x8(row_op(bs, col, q)), as_bf16x8(cop[q]), za);
+    for (int pt = 0; pt < 2; ++pt) {
+      ya[pt][0] *= f0;
+      ya[pt][1] *= f1;
+    }
+
+    // 2. intra term: Z^T tiles (s-block, l-block) = (0,0), (1,1), (0,1)
+    u32x4 gop[2];
     {
-      float gv[16];
+      f32x4 z00{}, z11{}, z01{};
 #pragma unroll
-      for (int rb = 0; rb < 4; ++rb) {
-        const int sb = 8 * rb + 4 * kg;
-        const f32x4 as = *reinterpret_cast<const f32x4 *>(ad + sb);
-        const f32x4 ds = *reinterpret_cast<const f32x4 *>(ad + CQ + sb);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const bool keep = sb + e <= col;
-          const float arg = keep ? (a - as[e]) : -__builtin_inff();
-          gv[rb * 4 + e] = keep ? za[rb * 4 + e] * __expf(arg) * ds[e] : 0.f;
-        }
+      for (int q = 0; q < KQ; ++q) {
+        const u32x4 b0 = row_op(bs, c16, q), b1 = row_op(bs, 16 + c16, q);
+        z00 = mfma16(b0, cop[0][q], z00);
+        z01 = mfma16(b0, cop[1][q], z01);
+        z11 = mfma16(b1, cop[1][q], z11);
       }
-      u32x4 g0, g1;
-      g0.x = pack_bf16x2(gv[0], gv[1]);
-      g0.y = pack_bf16x2(gv[2], gv[3]);
-      g0.z = pack_bf16x2(gv[4], gv[5]);
-      g0.w = pack_bf16x2(gv[6], gv[7]);
-      g1.x = pack_bf16x2(gv[8], gv[9]);
-      g1.y = pack_bf16x2(gv[10], gv[11]);
-      g1.z = pack_bf16x2(gv[12], gv[13]);
-      g1.w = pack_bf16x2(gv[14], gv[15]);
-      // X^T operands in the accumulator's row order (s offsets 4kg.., 8+4kg..,
-      // 16+4kg.., 24+4kg..) by transposing reads: lane (gq, d) addresses row
-      // 8h4 + 4kg + d/4, columns p0 .. p0+3
-      const int gq = lane >> 4, d = lane & 15;
-      const int p0 = 32 * wave + 16 * (gq & 1) + 4 * (d & 3);
-      u32x2 part[4];
+      // lane holds s = 16 sb + 4 g4 + r, l = 16 lb + c16
+      const f32x4 bs0 = *reinterpret_cast<const f32x4 *>(adw + CQ + 4 * g4);
+      const f32x4 bs1 = *reinterpret_cast<const f32x4 *>(adw + CQ + 16 + 4 * g4);
+      float g00[4], g11[4], g01[4];
 #pragma unroll
-      for (int h4 = 0; h4 < 4; ++h4) {
-        const int row = 8 * h4 + 4 * kg + (d >> 2);
-        const int cc = (p0 >> 3) ^ chunk_swz(row, NCX);
-        part[h4] = lds_read_tr16(xs + row * (P * 2) + cc * 16 + (p0 & 7) * 2);
+      for (int r = 0; r < 4; ++r) {
+        const float keep = 4 * g4 + r <= c16 ? 1.f : 0.f;
+        // for s > l the exponent may be large; min() keeps it finite so the
+        // 0 mask wins
+        g00[r] = z00[r] * (exp2_fast(fminf(al0 + bs0[r], 64.f)) * keep);
+        g11[r] = z11[r] * (exp2_fast(fminf(al1 + bs1[r], 64.f)) * keep);
+        g01[r] = z01[r] * exp2_fast(al1 + bs0[r]);
       }
-      ya = mfma32x32x16(as_bf16x8(u32x4{part[0].x, part[0].y, part[1].x, part[1].y}),
-                        as_bf16x8(g0), ya);
-      ya = mfma32x32x16(as_bf16x8(u32x4{part[2].x, part[2].y, part[3].x, part[3].y}),
-                        as_bf16x8(g1), ya);
+      gop[0] = u32x4{pack_bf16x2(g00[0], g00[1]), pack_bf16x2(g00[2], g00[3]), 0u, 0u};
+      gop[1] = u32x4{pack_bf16x2(g01[0], g01[1]), pack_bf16x2(g01[2], g01[3]),
+                     pack_bf16x2(g11[0], g11[1]), pack_bf16x2(g11[2], g11[3])};
+    }
+    // X^T in the same token order: s = 4 g4 + {0..3}, 16 + 4 g4 + {0..3}
+    u32x4 xop[2];
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const u32x2 t0 = tr4(xs, 64, 4, 4 * g4, 16 * pt), t1 = tr4(xs, 64, 4, 16 + 4 * g4, 16 * pt);
+      xop[pt] = u32x4{t0.x, t0.y, t1.x, t1.y};
+#pragma unroll
+      for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(xop[pt], gop[lt], ya[pt][lt]);
     }
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {  // D x_l: rows p = 32w + 8rb + 4kg + e of column l = col
-      const int p = 32 * wave + 8 * rb + 4 * kg;
-      const int cc = (p >> 3) ^ chunk_swz(col, NCX);
-      const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + col * (P * 2) + cc * 16 + (p & 7) * 2);
-      ya[rb * 4 + 0] += Dh * bf16lo(xv.x);
-      ya[rb * 4 + 1] += Dh * bf16hi(xv.x);
-      ya[rb * 4 + 2] += Dh * bf16lo(xv.y);
-      ya[rb * 4 + 3] += Dh * bf16hi(xv.y);
+    for (int pt = 0; pt < 2; ++pt) {  // D x: rows p = 16 pt + 4 g4 + r of token l
+#pragma unroll
+      for (int lt = 0; lt < 2; ++lt) {
+        const int l = 16 * lt + c16, col = 16 * pt + 4 * g4;
+        const u32x2 v = *reinterpret_cast<const u32x2 *>(
+            xs + l * 64 + (((col >> 3) ^ chunk_swz(l, 4)) << 4) + (col & 7) * 2);
+        ya[pt][lt].x += Dh * bf16lo(v.x);
+        ya[pt][lt].y += Dh * bf16hi(v.x);
+        ya[pt][lt].z += Dh * bf16lo(v.y);
+        ya[pt][lt].w += Dh * bf16hi(v.y);
+      }
     }
 
-    // 4. state: h^T = exp(acum_last) h^T + B^T . (w x)
+    // 3. state: h^T = exp(a_last) h^T + B^T (w x)
     {
-      const float ed = __expf(alast);
+      const float e = exp2_fast(alast * kLog2e);
+      const f32x4 w0 = *reinterpret_cast<const f32x4 *>(adw + 2 * CQ + 4 * g4);
+      const f32x4 w1 = *reinterpret_cast<const f32x4 *>(adw + 2 * CQ + 16 + 4 * g4);
+      u32x4 xw[2];
 #pragma unroll
-      for (int j = 0; j < NT; ++j) hst[j] *= ed;
+      for (int pt = 0; pt < 2; ++pt) {
+        const u32x4 q = xop[pt];
+        xw[pt] = u32x4{pack_bf16x2(bf16lo(q.x) * w0.x, bf16hi(q.x) * w0.y),
+                       pack_bf16x2(bf16lo(q.y) * w0.z, bf16hi(q.y) * w0.w),
+                       pack_bf16x2(bf16lo(q.z) * w1.x, bf16hi(q.z) * w1.y),
+                       pack_bf16x2(bf16lo(q.w) * w1.z, bf16hi(q.w) * w1.w)};
 #pragma unroll
-      for (int ks = 0; ks < CQ / 16; ++ks) {
-        const u32x4 xq = tr_k16(lane, xs, NCX, 16 * ks, 32 * wave);
-        const float *wl = ad + 2 * CQ + 16 * ks + 8 * kg;
-        const f32x4 w0 = *reinterpret_cast<const f32x4 *>(wl);
-        const f32x4 w1 = *reinterpret_cast<const f32x4 *>(wl + 4);
-        const u32x4 xw{pack_bf16x2(bf16lo(xq.x) * w0.x, bf16hi(xq.x) * w0.y),
-                       pack_bf16x2(bf16lo(xq.y) * w0.z, bf16hi(xq.y) * w0.w),
-                       pack_bf16x2(bf16lo(xq.z) * w1.x, bf16hi(xq.z) * w1.y),
-                       pack_bf16x2(bf16lo(xq.w) * w1.z, bf16hi(xq.w) * w1.w)};
+        for (int j = 0; j < NT; ++j) hst[pt][j] *= e;
+      }
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const u32x4 bq = tr_k16(lane, bs, NCB, 16 * ks, 32 * j);
-          hst[j] = mfma32x32x16(as_bf16x8(bq), as_bf16x8(xw), hst[j]);
-        }
+      for (int j = 0; j < NT; ++j) {
+        const u32x2 t0 = tr4(bs, N * 2, NCB, 4 * g4, 16 * j), t1 = tr4(bs, N * 2, NCB, 16 + 4 * g4, 16 * j);
+        const u32x4 bt{t0.x, t0.y, t1.x, t1.y};
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt) hst[pt][j] = mfma16(bt, xw[pt], hst[pt][j]);
       }
     }
 
-    // 5. y of this chunk staged (bf16) for the store at the next top
+    // y staged (bf16) in this wavefront's x slice, now fully read
 #pragma unroll
-    for (int rb = 0; rb < 4; ++rb) {
-      const int p = 8 * rb + 4 * kg;
-      u32x2 o;
-      o.x = pack_bf16x2(ya[rb * 4 + 0], ya[rb * 4 + 1]);
-      o.y = pack_bf16x2(ya[rb * 4 + 2], ya[rb * 4 + 3]);
-      *reinterpret_cast<u32x2 *>(ysw + (col * LYS + p) * 2) = o;
+    for (int pt = 0; pt < 2; ++pt) {
+#pragma unroll
+      for (int lt = 0; lt < 2; ++lt) {
+        const int l = 16 * lt + c16, col = 16 * pt + 4 * g4;
+        const u32x2 o{pack_bf16x2(ya[pt][lt].x, ya[pt][lt].y), pack_bf16x2(ya[pt][lt].z, ya[pt][lt].w)};
+        *reinterpret_cast<u32x2 *>(xs + l * 64 + (((col >> 3) ^ chunk_swz(l, 4)) << 4) + (col & 7) * 2) = o;
+      }
     }
-    wave_sync();
+    sl = sl == 2 ? 0 : sl + 1;
   }
-  if (nck > 0) store_y(nck - 1, ysw);
+  if (nck > 0) {
+    wave_sync();
+    store_y(nck - 1, (nck - 1) % 3);
+  }
   if (hfin) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
+    for (int pt = 0; pt < 2; ++pt) {
+      const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N + 4 * g4;
 #pragma unroll
-      for (int r = 0; r < 16; ++r)
-        hfin[sh * (P * N) + (int64_t)(32 * wave + col) * N + 32 * j + acc_row(r, kg)] = hst[j][r];
+      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(hfin + prow + 16 * j) = hst[pt][j];
     }
   }
 }
 
 }  // namespace
 
-bool fused_supported(int P, int N) { return P == 64 && (N == 64 || N == 128); }
+bool fused_supported(int H, int P, int N, int G) {
+  return P == 64 && (N == 64 || N == 128) && (H / G) % 2 == 0;
+}
 
 hipError_t launch_fused(const void *x, const float *dt, const float *A, const void *B, const void *C,
                         const float *D, const float *h0, const int32_t *cu, int64_t L, int64_t T,
                         int rows, int H, int P, int N, int G, void *y, float *hfin,
                         hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  if (!fused_supported(P, N)) return hipErrorInvalidValue;
-  const dim3 grid(xcd_grid(rows, H));
+  if (!fused_supported(H, P, N, G)) return hipErrorInvalidValue;
+  const dim3 grid(xcd_grid(rows, H / 2));
   const uint16_t *xi = static_cast<const uint16_t *>(x);
   const uint16_t *bi = static_cast<const uint16_t *>(B);
   const uint16_t *ci = static_cast<const uint16_t *>(C);
   uint16_t *yo = static_cast<uint16_t *>(y);
   if (N == 64)
-    hipLaunchKernelGGL(k_ssd_fused<64>, grid, dim3(128), 0, stream, xi, dt, A, bi, ci, D, h0, cu, L,
+    hipLaunchKernelGGL(k_ssd_fused<64>, grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, h0, cu, L,
                        T, rows, H, G, yo, hfin);
   else
-    hipLaunchKernelGGL(k_ssd_fused<128>, grid, dim3(128), 0, stream, xi, dt, A, bi, ci, D, h0, cu,
+    hipLaunchKernelGGL(k_ssd_fused<128>, grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, h0, cu,
                        L, T, rows, H, G, yo, hfin);
   return hipGetLastError();
 }

@@ -387,7 +387,7 @@ ssd_status ssd_fused_fwd(const void *x, const float *dt, const float *A, const v
   Plan p;
   ssd_status s = make_plan(dims, 64, &p);  // the chunk length only sizes the (unused) workspace
   if (s != SSD_OK) return s;
-  if (!p.bf16 || !ssd::fused_supported(p.geo.P, p.geo.N)) return SSD_ERR_UNSUPPORTED;
+  if (!p.bf16 || !ssd::fused_supported(p.geo.H, p.geo.P, p.geo.N, p.geo.G)) return SSD_ERR_UNSUPPORTED;
   if (p.geo.nrows >= ((int64_t)1 << 24) / p.geo.H) return SSD_ERR_UNSUPPORTED;
   if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
   if ((s = check_state_args(x, B, p)) != SSD_OK) return s;

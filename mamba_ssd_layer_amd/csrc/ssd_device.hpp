@@ -121,6 +121,31 @@ __device__ __forceinline__ void load_lds16(const void *gsrc, unsigned char *lds_
   __builtin_amdgcn_global_load_lds(gsrc, lds_dst, 16, 0, 0);
 }
 
+// The same direct-to-LDS loads (16 or 4 bytes a lane) issued from inline
+// assembly.  The compiler's wait insertion does not see these, so it adds no
+// vmcnt wait in front of later LDS reads -- for the builtin form it inserts a
+// full vmcnt(0) before every transposing LDS read that follows, which drains
+// the prefetch pipeline.  Completion is tracked by explicit wait_vmcnt only.
+// lds_off is the wave-uniform LDS byte offset of the wavefront's destination
+// (lane i at +16i or +4i); M0 carries it, with the one wait state its write
+// needs before the load.
+__device__ __forceinline__ uint32_t lds_off(const void *p) {
+  return static_cast<uint32_t>(
+      reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
+}
+__device__ __forceinline__ void dma_lds16(const void *gsrc, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(const void *gsrc, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+               :
+               : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
+               : "memory", "m0");
+}
+
 // s_waitcnt vmcnt(n) leaving expcnt and lgkmcnt alone (gfx9 encoding:
 // vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14).
 template <int n>

@@ -59,7 +59,7 @@ hipError_t launch_gate_rmsnorm(const void *y, const void *z, const float *weight
                                void *out, int64_t tokens, int width, bool bf16, hipStream_t stream);
 
 // the whole forward in one pass per (sequence, head)
-bool fused_supported(int P, int N);
+bool fused_supported(int H, int P, int N, int G);
 hipError_t launch_fused(const void *x, const float *dt, const float *A, const void *B, const void *C,
                         const float *D, const float *h0, const int32_t *cu, int64_t L, int64_t T,
                         int rows, int H, int P, int N, int G, void *y, float *hfin,

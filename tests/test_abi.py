@@ -312,6 +312,8 @@ def fused(d, **kw):
     (dict(headdim=128), SSD_ERR_UNSUPPORTED),         # P == 64 only
     (dict(dstate=32), SSD_ERR_UNSUPPORTED),
     (dict(dstate=256), SSD_ERR_UNSUPPORTED),
+    (dict(ngroups=4), SSD_ERR_UNSUPPORTED),           # heads per group must be even
+    (dict(nheads=6, ngroups=2), SSD_ERR_UNSUPPORTED),
     (dict(ngroups=3), SSD_ERR_INVALID_ARG),
     (dict(reserved=1), SSD_ERR_INVALID_ARG),
     (dict(batch=-1), SSD_ERR_INVALID_ARG),
