@@ -112,23 +112,17 @@ __device__ __forceinline__ constexpr int acc_row(int r, int g) { return 8 * (r >
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
 
 // ----------------------------------------------------------------- direct-to-LDS loads
-// gfx950 global_load_lds_dwordx4: each lane fetches 16 bytes from its own
-// global address; the wavefront's 64 chunks land contiguously in LDS at the
-// (wave-uniform) destination, lane i at +16 i.  Completion is tracked by
-// vmcnt only -- the compiler inserts no wait before LDS reads of the data, so
-// every use is preceded by an explicit wait_vmcnt and a barrier.
-__device__ __forceinline__ void load_lds16(const void *gsrc, unsigned char *lds_dst) {
-  __builtin_amdgcn_global_load_lds(gsrc, lds_dst, 16, 0, 0);
-}
-
-// The same direct-to-LDS loads (16 or 4 bytes a lane) issued from inline
-// assembly.  The compiler's wait insertion does not see these, so it adds no
-// vmcnt wait in front of later LDS reads -- for the builtin form it inserts a
-// full vmcnt(0) before every transposing LDS read that follows, which drains
-// the prefetch pipeline.  Completion is tracked by explicit wait_vmcnt only.
-// lds_off is the wave-uniform LDS byte offset of the wavefront's destination
-// (lane i at +16i or +4i); M0 carries it, with the one wait state its write
-// needs before the load.
+// gfx950 global_load_lds_dwordx4 / _dword: each lane fetches 16 (4) bytes from
+// its own global address; the wavefront's 64 pieces land contiguously in LDS
+// at the wave-uniform destination, lane i at +16i (+4i).  M0 carries the LDS
+// byte offset, with the one wait state its write needs before the load.
+//
+// Issued from inline assembly on purpose: the compiler's wait insertion does
+// not see these loads, so it adds no vmcnt wait in front of later LDS reads
+// (for the builtin form it puts a full vmcnt(0) before every transposing LDS
+// read that follows one, which drains any prefetch in flight).  Completion is
+// tracked by explicit wait_vmcnt only, and every use of the data is preceded
+// by one and, across wavefronts, by a barrier.
 __device__ __forceinline__ uint32_t lds_off(const void *p) {
   return static_cast<uint32_t>(
       reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void *)p));
@@ -144,6 +138,9 @@ __device__ __forceinline__ void dma_lds4(const void *gsrc, uint32_t lds_dst) {
                :
                : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
                : "memory", "m0");
+}
+__device__ __forceinline__ void load_lds16(const void *gsrc, unsigned char *lds_dst) {
+  dma_lds16(gsrc, lds_off(lds_dst));
 }
 
 // s_waitcnt vmcnt(n) leaving expcnt and lgkmcnt alone (gfx9 encoding:
