@@ -7,22 +7,27 @@
 // this kernel walks 32-token chunks, for which the intra-chunk product is one
 // 32 x 32 causal tile.
 //
-// Design.  Block = (sequence, two heads of one group) in XCD-aware order (all
-// heads of a sequence on one XCD, so its B and C rows come from one L2), 4
-// wavefronts: wavefront (head hh, half ph) owns state rows p in
+// Design.  Block = (sequence, HPB heads of one group) in XCD-aware order (all
+// heads of a sequence on one XCD, so its B and C rows come from one L2),
+// 2 HPB wavefronts: wavefront (head hh, half ph) owns state rows p in
 // [32 ph, 32 ph + 32) of head hh, held transposed (h^T, rows n, columns p) as
-// 2 x N/16 fp32 tiles of the 16x16x32 bf16 MFMA.  The two heads share their B
-// and C tiles in LDS.
+// 2 x N/16 fp32 tiles of the 16x16x32 bf16 MFMA.  The block's heads share
+// their B and C tiles in LDS.  The launch uses HPB = 2 (two or three blocks a
+// CU); four heads a block (one block a CU) cut the B/C traffic further but
+// measured no faster, since each wavefront's chunk latency dominates.
 //
-// Data movement.  A three-slot LDS ring per block holds chunk k's x (each
-// wavefront's own 32 x 32 slice), B, C and dt (each wavefront's head) while
-// chunk k + 2 is in flight (direct-to-LDS loads).  Vector-memory operations
-// complete in issue order, so a wavefront knows chunk k has landed once at
-// most the operations it issued after that chunk are pending; it waits for
-// exactly that count, then one barrier per chunk publishes the tiles.  y of a
-// chunk is staged (bf16) in the wavefront's own x slice of that chunk and
-// stored in 16-byte row segments at the next chunk's top, before that slot is
-// refilled.  No workspace: nothing but x, B, C, dt and y crosses HBM.
+// Data movement.  An R-slot LDS ring per block holds chunk k's x (a 32 x 64
+// tile per head), B, C and dt while chunks k+1 .. k+R-2 are in flight
+// (direct-to-LDS loads; wavefront (hh, ph) fetches rows [16 ph, 16 ph + 16)
+// of head hh's x, whole 128-byte rows).  Vector-memory operations complete in
+// issue order, so a wavefront knows chunk k has landed once at most the
+// operations it issued after that chunk are pending; it waits for exactly
+// that count, then one barrier per chunk publishes the tiles.  Each
+// wavefront stages its y (bf16) over its own columns of the chunk's x tile
+// once it has read them; at the next chunk's top, after the barrier,
+// wavefront (hh, ph) stores rows [16 ph, 16 ph + 16) of head hh's y as whole
+// rows and then refills exactly those LDS rows with a later chunk's x.  No
+// workspace: nothing but x, B, C, dt and y crosses HBM.
 //
 // Per chunk and wavefront (a_l = cumulative sum of dt A within the chunk,
 // from a DPP scan of the 32 dt values):
@@ -79,41 +84,69 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int N>
-__global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
+// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 31]
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define SSD_W(i) case i: wait_vmcnt<i>(); break;
+    SSD_W(0) SSD_W(1) SSD_W(2) SSD_W(3) SSD_W(4) SSD_W(5) SSD_W(6) SSD_W(7)
+    SSD_W(8) SSD_W(9) SSD_W(10) SSD_W(11) SSD_W(12) SSD_W(13) SSD_W(14) SSD_W(15)
+    SSD_W(16) SSD_W(17) SSD_W(18) SSD_W(19) SSD_W(20) SSD_W(21) SSD_W(22) SSD_W(23)
+    SSD_W(24) SSD_W(25) SSD_W(26) SSD_W(27) SSD_W(28) SSD_W(29) SSD_W(30)
+#undef SSD_W
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
+// Geometry of one kernel instance: N state size, HPB heads per block, R ring slots.
+template <int N, int HPB, int R>
+struct FusedCfg {
+  static constexpr int P = 64, CQ = 32, WAVES = 2 * HPB, THREADS = 64 * WAVES;
+  static constexpr int XH = CQ * P * 2;          // x of one head and chunk: 32 rows x 128 B
+  static constexpr int BT = CQ * N * 2;          // B (or C) of a chunk
+  static constexpr int DW = 64 * 4;              // one wavefront's dt piece
+  static constexpr int OX = 0, OB = HPB * XH, OC = OB + BT, OD = OC + BT;
+  static constexpr int SLOT = OD + WAVES * DW;
+  static constexpr int AD = R * SLOT;            // per wavefront: [al2 | bs2 | w], 32 floats each
+  static constexpr int ADW = 3 * CQ * 4;
+  static constexpr int TOTAL = AD + WAVES * ADW;
+  static constexpr int BCI = 2 * BT / 1024 / WAVES;  // 1 KB pieces of B and C per wavefront
+  static constexpr int LDC = 2 + BCI + 1;        // vector-memory ops a wavefront issues per chunk load
+  static constexpr int STC = 2;                  // ... per chunk of y it stores
+  static constexpr int BLOCKS_PER_CU = (160 * 1024) / TOTAL;
+  static constexpr int WAVES_PER_SIMD = BLOCKS_PER_CU * WAVES / 4;
+  static_assert(BCI * WAVES * 1024 == 2 * BT, "B and C split evenly over the wavefronts");
+  static_assert(32 * HPB <= 64 * WAVES, "dt pieces");
+  static_assert(R >= 3 && (R - 2) * (LDC + STC) <= 30, "wait counts");
+  static_assert(BLOCKS_PER_CU >= 1 && WAVES_PER_SIMD >= 2, "occupancy");
+};
+
+template <int N, int HPB, int R>
+__global__ __launch_bounds__((FusedCfg<N, HPB, R>::THREADS), (FusedCfg<N, HPB, R>::WAVES_PER_SIMD))
+void k_ssd_fused(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
     const float *__restrict__ h0, const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows,
     int H, int G, uint16_t *__restrict__ y, float *__restrict__ hfin) {
-  constexpr int P = 64, CQ = 32;
+  using F = FusedCfg<N, HPB, R>;
+  constexpr int P = F::P, CQ = F::CQ;
   constexpr int NT = N / 16;   // state tiles per p-tile (over n)
   constexpr int KQ = N / 32;   // K steps over n
   constexpr int NCB = N / 8;   // 16-byte chunks per B / C row
-  constexpr int XW = CQ * 32 * 2;            // a wavefront's x slice of a chunk: 32 tokens x 32 p
-  constexpr int BT = CQ * N * 2;             // B (or C) of a chunk
-  constexpr int DW = 64 * 4;                 // a wavefront's dt of a chunk (lanes 32..63 repeat)
-  constexpr int OX = 0, OB = 4 * XW, OC = OB + BT, OD = OC + BT;
-  constexpr int SLOT = OD + 4 * DW;
-  constexpr int AD = 3 * SLOT;               // per wavefront: [al2 | bs2 | w], 32 floats each
-  constexpr int ADW = 3 * CQ * 4;
-  constexpr int TOTAL = AD + 4 * ADW;
-  constexpr int BCI = 2 * BT / 1024 / 4;     // 1 KB pieces of B and C per wavefront
-  constexpr int LDC = 2 + BCI + 1;           // vector-memory ops a wavefront issues per chunk load
-  constexpr int STC = 2;                     // ... per chunk of y it stores
-  static_assert(BCI * 4 * 1024 == 2 * BT, "B and C split evenly over 4 wavefronts");
-  static_assert(TOTAL <= 160 * 1024 / (N == 64 ? 3 : 2), "blocks per CU");
-  __shared__ __align__(16) unsigned char smem[TOTAL];
+  constexpr int XH = F::XH, BT = F::BT, DW = F::DW, OX = F::OX, OB = F::OB, OC = F::OC, OD = F::OD;
+  constexpr int SLOT = F::SLOT, AD = F::AD, ADW = F::ADW, BCI = F::BCI, LDC = F::LDC, STC = F::STC;
+  __shared__ __align__(16) unsigned char smem[F::TOTAL];
 
-  int s, pr;
-  xcd_chunk_head(H >> 1, s, pr);
+  int s, hb;
+  xcd_chunk_head(H / HPB, s, hb);
   if (s >= rows) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
   const int hh = wave >> 1, ph = wave & 1;
-  const int h = 2 * pr + hh;
-  const int g = (2 * pr) / (H / G);
+  const int h0b = HPB * hb;  // the block's first head
+  const int h = h0b + hh;
+  const int g = h0b / (H / G);
   int64_t tb, len;
   if (cu) {
     tb = cu[s];
@@ -142,39 +175,64 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
       hst[pt][j] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + prow + 16 * j) : f32x4{};
   }
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
+  // The registers hold S = h / 2^lam: the decay of a chunk goes into lam
+  // (wave-uniform) instead of into 2 N/16 x 4 multiplies a lane; S is
+  // rescaled only when lam drops below -32, or before a chunk whose own
+  // decay exceeds 2^-40 (there the exact per-chunk form is used).
+  float lam = 0.f;
 
-  // chunk k's loads into ring slot sl: LDC vector-memory ops per wavefront
-  auto issue = [&](int k, int sl) {
-    const int64_t t0 = tb + (int64_t)k * CQ;
-    const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
-    const uint32_t base = lds_off(smem) + sl * SLOT;
+  // chunk k's loads into ring slot sl: LDC vector-memory ops per wavefront.
+  // Each load is a wave-uniform base (the chunk's first row) plus a per-lane
+  // byte offset fixed for the whole sequence; only a partial last chunk
+  // recomputes the offsets with its rows clamped.
+  uint32_t xoff[2], bcoff[BCI], dtoff;
+  auto lane_offsets = [&](int last) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // this wavefront's x slice: 32 rows of 4 chunks
-      const int m = i * 64 + lane, r = m >> 2, cc = (m & 3) ^ chunk_swz(r, 4);
-      dma_lds16(x + (t0 + min(r, last)) * ldx + (int64_t)h * P + 32 * ph + 8 * cc,
-                base + OX + wave * XW + i * 1024);
+    for (int i = 0; i < 2; ++i) {  // rows 16 ph .. 16 ph + 15 of head hh's x, 8 chunks each
+      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = (m & 7) ^ chunk_swz(r, 8);
+      xoff[i] = static_cast<uint32_t>((min(r, last) * ldx + (int64_t)h * P + 8 * cc) * 2);
     }
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {  // B and C pieces
-      const int u = wave * BCI + i, tile = u / (BT / 1024), pi = u % (BT / 1024);
+      const int u = wave * BCI + i, pi = u % (BT / 1024);
       const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ chunk_swz(r, NCB);
-      dma_lds16((tile ? Cm : Bm) + (t0 + min(r, last)) * ldb + (int64_t)g * N + 8 * cc,
-                base + (tile ? OC : OB) + pi * 1024);
+      bcoff[i] = static_cast<uint32_t>((min(r, last) * ldb + (int64_t)g * N + 8 * cc) * 2);
     }
-    // dt of this wavefront's head, 4 bytes a lane
-    dma_lds4(dt + (t0 + min(lane & 31, last)) * H + h, base + OD + wave * DW);
+    // dt of the block's heads: entry e = token * HPB + head, 64 entries a
+    // wavefront (past the last entry every lane reads that one)
+    const int e = min(wave * 64 + lane, CQ * HPB - 1);
+    dtoff = static_cast<uint32_t>((min(e / HPB, last) * H + h0b + e % HPB) * 4);
   };
-  // y of chunk k from its staging (the wavefront's x slice of slot sl): STC stores
+  lane_offsets(CQ - 1);
+  auto issue = [&](int k, int sl) {
+    const int64_t t0 = tb + (int64_t)k * CQ;
+    const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
+    if (last < CQ - 1) lane_offsets(last);
+    const uint32_t base = lds_off(smem) + sl * SLOT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) dma_lds16_sb(xoff[i], x + t0 * ldx, base + OX + hh * XH + 16 * ph * 128 + i * 1024);
+#pragma unroll
+    for (int i = 0; i < BCI; ++i) {
+      const int u = wave * BCI + i, tile = u / (BT / 1024), pi = u % (BT / 1024);
+      dma_lds16_sb(bcoff[i], (tile ? Cm : Bm) + t0 * ldb, base + (tile ? OC : OB) + pi * 1024);
+    }
+    dma_lds4_sb(dtoff, dt + t0 * H, base + OD + wave * DW);
+  };
+  // rows 16 ph .. 16 ph + 15 of head hh's y of chunk k (staged in slot sl): STC stores
   auto store_y = [&](int k, int sl) {
     const int64_t t0 = tb + (int64_t)k * CQ;
     const int rem = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ));
-    const unsigned char *ys = smem + sl * SLOT + OX + wave * XW;
+    const unsigned char *ys = smem + sl * SLOT + OX + hh * XH;
+    u32x4 v[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const int m = i * 64 + lane, r = m >> 2, cc = m & 3;
-      const u32x4 v = *reinterpret_cast<const u32x4 *>(ys + r * 64 + ((cc ^ chunk_swz(r, 4)) << 4));
-      if (r < rem)
-        *reinterpret_cast<u32x4 *>(y + (t0 + r) * ldx + (int64_t)h * P + 32 * ph + 8 * cc) = v;
+      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = m & 7;
+      v[i] = *reinterpret_cast<const u32x4 *>(ys + r * 128 + ((cc ^ chunk_swz(r, 8)) << 4));
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = m & 7;
+      if (r < rem) *reinterpret_cast<u32x4 *>(y + (t0 + r) * ldx + (int64_t)h * P + 8 * cc) = v[i];
     }
   };
   // row operand of a B or C tile in the state's K order: K step q covers
@@ -195,40 +253,46 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
     return lds_read_tr16(tile + row * rb + (cc << 4) + (col & 7) * 2);
   };
 
-  if (nck > 0) issue(0, 0);
-  if (nck > 1) issue(1, 1);
+  constexpr int D = R - 1;  // chunks in flight ahead of the one being computed
+#pragma unroll
+  for (int c = 0; c < D; ++c)
+    if (c < nck) issue(c, c);
   int sl = 0;
 #pragma unroll 1
   for (int k = 0; k < nck; ++k) {
-    // chunk k has landed once at most the later ops of this wavefront are
-    // pending: the y stores of iteration k-1 (k >= 2) and chunk k+1's loads
-    const bool more = k + 1 < nck;
-    if (k >= 2) {
-      if (more) wait_vmcnt<STC + LDC>(); else wait_vmcnt<STC>();
-    } else {
-      if (more) wait_vmcnt<LDC>(); else wait_vmcnt<0>();
+    // chunk k has landed once at most the ops this wavefront issued after its
+    // loads are pending: loads of later chunks (prologue, then one chunk per
+    // iteration) and the y stores of the iterations in between
+    {
+      int n = k < D ? (min(D, nck) - 1 - k) * LDC : 0;
+      for (int j = k < D ? 0 : k - D + 1; j < k; ++j) n += (j >= 1 ? STC : 0) + (j + D < nck ? LDC : 0);
+      wait_vmcnt_dyn(n);
     }
     __syncthreads();  // every wavefront's share of chunk k is in; chunk k-1 is done everywhere
-    const int slp = sl == 0 ? 2 : sl - 1;  // slot of chunk k-1, and of chunk k+2
+    const int slp = sl == 0 ? R - 1 : sl - 1;  // slot of chunk k-1, and of chunk k+D
     if (k >= 1) store_y(k - 1, slp);
-    if (k + 2 < nck) issue(k + 2, slp);
+    if (k + D < nck) issue(k + D, slp);
 
-    unsigned char *xs = smem + sl * SLOT + OX + wave * XW;
+    unsigned char *xh = smem + sl * SLOT + OX + hh * XH;  // head hh's x tile (this wavefront: columns 32 ph ..)
     const unsigned char *bs = smem + sl * SLOT + OB;
     const unsigned char *cs = smem + sl * SLOT + OC;
-    const float *dts = reinterpret_cast<const float *>(smem + sl * SLOT + OD + wave * DW);
+    const float *dts = reinterpret_cast<const float *>(smem + sl * SLOT + OD);
     const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
 
     // cumulative decay (lanes l and 32 + l hold token l) and per-token tables
     const int tl = lane & 31;
-    const float dtv = tl <= last ? dts[lane] : 0.f;
+    const float dtv = tl <= last ? dts[tl * HPB + hh] : 0.f;
     const float a = scan32(dtv * Ah);
     const float alast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 31));
+    const float a2last = alast * kLog2e;
+    const bool steep = a2last < -40.f;          // exact per-chunk form for this chunk
+    const float wshift = steep ? a2last : -lam;  // log2 of w_s / (dt_s exp(-a_s))
     if (lane < 32) {
       const float al = a * kLog2e;
-      adw[tl] = al;                                            // log2 exp(a_l)
-      adw[CQ + tl] = __builtin_amdgcn_logf(dtv) - al;          // log2(dt_s exp(-a_s))
-      adw[2 * CQ + tl] = exp2_fast((alast - a) * kLog2e) * dtv;  // w_s
+      const float bs = __builtin_amdgcn_logf(dtv) - al;
+      adw[tl] = al;                              // log2 exp(a_l)
+      adw[CQ + tl] = bs;                         // log2(dt_s exp(-a_s))
+      adw[2 * CQ + tl] = exp2_fast(bs + wshift);  // the state update's token weight
     }
     wave_sync();
 
@@ -255,7 +319,7 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
       }
     }
     const float al0 = adw[c16], al1 = adw[16 + c16];
-    const float f0 = exp2_fast(al0), f1 = exp2_fast(al1);
+    const float f0 = exp2_fast(al0 + lam), f1 = exp2_fast(al1 + lam);
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
       ya[pt][0] *= f0;
@@ -294,7 +358,8 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
     u32x4 xop[2];
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
-      const u32x2 t0 = tr4(xs, 64, 4, 4 * g4, 16 * pt), t1 = tr4(xs, 64, 4, 16 + 4 * g4, 16 * pt);
+      const u32x2 t0 = tr4(xh, 128, 8, 4 * g4, 32 * ph + 16 * pt);
+      const u32x2 t1 = tr4(xh, 128, 8, 16 + 4 * g4, 32 * ph + 16 * pt);
       xop[pt] = u32x4{t0.x, t0.y, t1.x, t1.y};
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(xop[pt], gop[lt], ya[pt][lt]);
@@ -303,9 +368,9 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
     for (int pt = 0; pt < 2; ++pt) {  // D x: rows p = 16 pt + 4 g4 + r of token l
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) {
-        const int l = 16 * lt + c16, col = 16 * pt + 4 * g4;
+        const int l = 16 * lt + c16, col = 32 * ph + 16 * pt + 4 * g4;
         const u32x2 v = *reinterpret_cast<const u32x2 *>(
-            xs + l * 64 + (((col >> 3) ^ chunk_swz(l, 4)) << 4) + (col & 7) * 2);
+            xh + l * 128 + (((col >> 3) ^ chunk_swz(l, 8)) << 4) + (col & 7) * 2);
         ya[pt][lt].x += Dh * bf16lo(v.x);
         ya[pt][lt].y += Dh * bf16hi(v.x);
         ya[pt][lt].z += Dh * bf16lo(v.y);
@@ -313,9 +378,18 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
       }
     }
 
-    // 3. state: h^T = exp(a_last) h^T + B^T (w x)
+    // 3. state: h = exp(a_last) h + B^T (w x), as S = h / 2^lam: normally
+    // lam += a_last log2(e) and S += B^T (w' x) with w'_s = w_s / 2^lam_new;
+    // for a steep chunk S is first turned into exp(a_last) h and lam = 0
     {
-      const float e = exp2_fast(alast * kLog2e);
+      if (steep) {
+        const float e = exp2_fast(lam + a2last);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) hst[pt][j] *= e;
+      }
+      lam = steep ? 0.f : lam + a2last;
       const f32x4 w0 = *reinterpret_cast<const f32x4 *>(adw + 2 * CQ + 4 * g4);
       const f32x4 w1 = *reinterpret_cast<const f32x4 *>(adw + 2 * CQ + 16 + 4 * g4);
       u32x4 xw[2];
@@ -326,8 +400,6 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
                        pack_bf16x2(bf16lo(q.y) * w0.z, bf16hi(q.y) * w0.w),
                        pack_bf16x2(bf16lo(q.z) * w1.x, bf16hi(q.z) * w1.y),
                        pack_bf16x2(bf16lo(q.w) * w1.z, bf16hi(q.w) * w1.w)};
-#pragma unroll
-        for (int j = 0; j < NT; ++j) hst[pt][j] *= e;
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
@@ -336,30 +408,39 @@ __global__ __launch_bounds__(256, N == 64 ? 3 : 2) void k_ssd_fused(
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) hst[pt][j] = mfma16(bt, xw[pt], hst[pt][j]);
       }
+      if (lam < -32.f) {
+        const float e = exp2_fast(lam);
+#pragma unroll
+        for (int pt = 0; pt < 2; ++pt)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) hst[pt][j] *= e;
+        lam = 0.f;
+      }
     }
 
-    // y staged (bf16) in this wavefront's x slice, now fully read
+    // y staged (bf16) over this wavefront's columns of the x tile, now fully read
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) {
-        const int l = 16 * lt + c16, col = 16 * pt + 4 * g4;
+        const int l = 16 * lt + c16, col = 32 * ph + 16 * pt + 4 * g4;
         const u32x2 o{pack_bf16x2(ya[pt][lt].x, ya[pt][lt].y), pack_bf16x2(ya[pt][lt].z, ya[pt][lt].w)};
-        *reinterpret_cast<u32x2 *>(xs + l * 64 + (((col >> 3) ^ chunk_swz(l, 4)) << 4) + (col & 7) * 2) = o;
+        *reinterpret_cast<u32x2 *>(xh + l * 128 + (((col >> 3) ^ chunk_swz(l, 8)) << 4) + (col & 7) * 2) = o;
       }
     }
-    sl = sl == 2 ? 0 : sl + 1;
+    sl = sl == R - 1 ? 0 : sl + 1;
   }
   if (nck > 0) {
-    wave_sync();
-    store_y(nck - 1, (nck - 1) % 3);
+    __syncthreads();  // both halves of the last chunk's y are staged
+    store_y(nck - 1, (nck - 1) % R);
   }
   if (hfin) {
+    const float e = exp2_fast(lam);
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
       const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N + 4 * g4;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(hfin + prow + 16 * j) = hst[pt][j];
+      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(hfin + prow + 16 * j) = hst[pt][j] * e;
     }
   }
 }
@@ -370,23 +451,31 @@ bool fused_supported(int H, int P, int N, int G) {
   return P == 64 && (N == 64 || N == 128) && (H / G) % 2 == 0;
 }
 
+namespace {
+template <int N, int HPB, int R>
+void launch_fused_t(const uint16_t *x, const float *dt, const float *A, const uint16_t *B,
+                    const uint16_t *C, const float *D, const float *h0, const int32_t *cu, int64_t L,
+                    int64_t T, int rows, int H, int G, uint16_t *y, float *hfin, hipStream_t stream) {
+  hipLaunchKernelGGL((k_ssd_fused<N, HPB, R>), dim3(xcd_grid(rows, H / HPB)),
+                     dim3(FusedCfg<N, HPB, R>::THREADS), 0, stream, x, dt, A, B, C, D, h0, cu, L, T,
+                     rows, H, G, y, hfin);
+}
+}  // namespace
+
 hipError_t launch_fused(const void *x, const float *dt, const float *A, const void *B, const void *C,
                         const float *D, const float *h0, const int32_t *cu, int64_t L, int64_t T,
                         int rows, int H, int P, int N, int G, void *y, float *hfin,
                         hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   if (!fused_supported(H, P, N, G)) return hipErrorInvalidValue;
-  const dim3 grid(xcd_grid(rows, H / 2));
   const uint16_t *xi = static_cast<const uint16_t *>(x);
   const uint16_t *bi = static_cast<const uint16_t *>(B);
   const uint16_t *ci = static_cast<const uint16_t *>(C);
   uint16_t *yo = static_cast<uint16_t *>(y);
   if (N == 64)
-    hipLaunchKernelGGL(k_ssd_fused<64>, grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, h0, cu, L,
-                       T, rows, H, G, yo, hfin);
+    launch_fused_t<64, 2, 3>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, stream);
   else
-    hipLaunchKernelGGL(k_ssd_fused<128>, grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, h0, cu,
-                       L, T, rows, H, G, yo, hfin);
+    launch_fused_t<128, 2, 3>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, stream);
   return hipGetLastError();
 }
 

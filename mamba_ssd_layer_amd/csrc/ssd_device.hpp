@@ -139,6 +139,20 @@ __device__ __forceinline__ void dma_lds4(const void *gsrc, uint32_t lds_dst) {
                : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
                : "memory", "m0");
 }
+// Same, addressed as a wave-uniform 64-bit base (SGPRs) plus a per-lane
+// 32-bit byte offset.
+__device__ __forceinline__ void dma_lds16_sb(uint32_t voff, const void *sbase, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
+               : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4_sb(uint32_t voff, const void *sbase, uint32_t lds_dst) {
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_dst))
+               : "memory", "m0");
+}
 __device__ __forceinline__ void load_lds16(const void *gsrc, unsigned char *lds_dst) {
   dma_lds16(gsrc, lds_off(lds_dst));
 }

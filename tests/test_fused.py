@@ -76,6 +76,17 @@ def test_long_memory(kind):
     check_full(w, y, fin, label=f"fused {kind}")
 
 
+@pytest.mark.parametrize("dt_shift", [-1.0, 0.5])
+def test_fast_decay(dt_shift):
+    # large dt: chunks whose own decay exceeds 2^-40 (handled in the exact
+    # per-chunk form) next to chunks whose decay is folded into the state's
+    # running scale, which is renormalised every few chunks
+    w = workloads.make_custom(2, 1200, 8, 64, 128, 2, 256, "bf16", seed=1350, init_std=0.5,
+                              dt_shift=dt_shift)
+    y, fin, _ = run_fused(w)
+    check_full(w, y, fin, label=f"fused fast decay {dt_shift}")
+
+
 def test_varlen_edge_lengths():
     # empty, one-token, exactly one and two chunks, one token either side of
     # a chunk boundary, and a long sequence; nonzero initial states
