@@ -1,11 +1,16 @@
 #!/usr/bin/env python3
 """Benchmark of the Mamba-2 SSD chunked-scan forward (libssd) on one MI355X.
 
-A step is one full forward -- chunk_cumsum, chunk_state, state_passing,
-chunk_scan -- over one batch of seeded synthetic input already resident in
-HBM.  Prints one JSON line with whole-job tokens/s, the roofline position of
-the dominant kernel (timed with HIP events on the launch stream), and the CPU
-oracle timed on a bounded sample of the same workload on the host cores.
+A step is one full forward over one batch of seeded synthetic input already
+resident in HBM, timed two ways: the chunked forward (ssd_chunk_scan_fwd:
+chunk_cumsum, chunk_state, state_passing, chunk_scan) and, where its shape is
+supported, the one-pass forward (ssd_fused_fwd: the same steps per 32-token
+chunk with the state kept on chip).  `value` is the faster of the two (named
+in config.path); both are reported.  Prints one JSON line with whole-job
+tokens/s, the roofline position of that path's dominant kernel (timed with HIP
+events on the launch stream), per-kernel figures of the chunked stages, and
+the CPU oracle timed on a bounded sample of the same workload on the host
+cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
@@ -30,7 +35,9 @@ STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
 KERNEL_SOURCES = {
     "chunk_cumsum": "k_scan_prep.hip", "state_passing": "k_scan_prep.hip",
     "chunk_state": "k_chunk_state.hip", "chunk_scan": "k_chunk_scan.hip",
+    "fused_fwd": "k_fused.hip",
 }
+FUSED_CHUNK = 32  # the one-pass forward's chunk length
 
 
 def log(msg: str) -> None:
@@ -50,6 +57,9 @@ def algorithmic(w, stage: str):
       chunk_scan     bytes 2 s H P + 2 s G N + 8 H, plus h H P N per chunk
                      flops H (2 P N + (Q + 1) P) + G (Q + 1) N  (causal pairs only,
                      C.B^T once per group)
+      fused_fwd      bytes 2 s H P + 2 s G N + 4 H, plus 4 H P N per sequence for
+                     the final state (and the initial state when read)
+                     flops H (4 P N + 33 P) + 33 G N  (Q = 32: inter, state, intra)
     """
     T, H, P, N, G, Q = w.tokens, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nseq = w.nsequences
@@ -67,6 +77,12 @@ def algorithmic(w, stage: str):
     if stage == "chunk_scan":
         b = 2 * s * T * H * P + 2 * s * T * G * N + 8 * T * H + hsz * nc * H * P * N
         f = T * (H * (2 * P * N + (Q + 1) * P) + G * (Q + 1) * N)
+        return b, f
+    if stage == "fused_fwd":
+        q = FUSED_CHUNK
+        init = 4 * nseq * H * P * N if w.h0 is not None else 0
+        b = 2 * s * T * H * P + 2 * s * T * G * N + 4 * T * H + 4 * nseq * H * P * N + init
+        f = T * (H * (4 * P * N + (q + 1) * P) + G * (q + 1) * N)
         return b, f
     raise KeyError(stage)
 
@@ -299,8 +315,38 @@ def main() -> int:
     wall = time.perf_counter() - wall0
     ms = ev0.elapsed_time(ev1) / args.steps
     value = T / (ms / 1e3)
-    log(f"bench: {ms * 1e3:.1f} us/step ({wall / args.steps * 1e6:.1f} us wall), "
+    log(f"bench: chunked forward {ms * 1e3:.1f} us/step ({wall / args.steps * 1e6:.1f} us wall), "
         f"{value / 1e6:.1f} M tokens/s")
+
+    # the one-pass forward on the same inputs, where its shape is supported
+    fused = None
+    if w.dtype == "bf16" and P == 64 and N in (64, 128) and (H // G) % 2 == 0:
+        yf = torch.empty_like(x)
+        ff = torch.empty_like(fin)
+
+        def fstep():
+            ssd.fused_fwd(x, dt, A, Bm, Cm, D, h0, cu, y=yf, final_state=ff)
+
+        for _ in range(args.warmup):
+            fstep()
+        torch.cuda.synchronize()
+        fe0 = torch.cuda.Event(enable_timing=True)
+        fe1 = torch.cuda.Event(enable_timing=True)
+        fwall0 = time.perf_counter()
+        fe0.record(stream)
+        for _ in range(args.steps):
+            fstep()
+        fe1.record(stream)
+        torch.cuda.synchronize()
+        fwall = time.perf_counter() - fwall0
+        fms = fe0.elapsed_time(fe1) / args.steps
+        fb, ff_ = algorithmic(w, "fused_fwd")
+        ft = fms * 1e-3
+        fused = {"us": round(fms * 1e3, 2), "wall_us": round(fwall / args.steps * 1e6, 2),
+                 "tokens_per_s": round(T / ft, 1), "bytes": fb, "flops": ff_,
+                 "GBs": round(fb / ft / 1e9, 1), "TFLOPs": round(ff_ / ft / 1e12, 2),
+                 "hbm_frac": round(fb / ft / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"bench: one-pass forward {fms * 1e3:.1f} us/step, {T / ft / 1e6:.1f} M tokens/s")
 
     # per-stage times: the same stages launched one by one, HIP events between
     stage_us = {}
@@ -333,26 +379,38 @@ def main() -> int:
                          TFLOPs=round(f / t / 1e12, 2) if f else 0.0,
                          hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4))
         kernels[s] = entry
-    roofline = None
-    if stage_us:
-        dom = max(stage_us, key=stage_us.get)
-        b, f = algorithmic(w, dom)
-        t = stage_us[dom] * 1e-6
+    def roofline_of(kernel: str, us: float):
+        b, f = algorithmic(w, kernel)
+        t = us * 1e-6
         mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
         t_hbm = b / (HBM_PEAK_GBS * 1e9)
         t_mfma = f / (mfma_peak * 1e12)
         if t_hbm >= t_mfma:
-            roofline = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s"}
+            r = {"bound": "hbm", "achieved": round(b / t / 1e9, 1), "peak": HBM_PEAK_GBS,
+                 "unit": "GB/s"}
         else:
-            roofline = {"bound": "mfma" if w.dtype == "bf16" else "alu",
-                        "achieved": round(f / t / 1e12, 2), "peak": mfma_peak, "unit": "TFLOP/s"}
-        roofline["frac"] = round(roofline["achieved"] / roofline["peak"], 4)
-        roofline["traffic"] = load_traffic(dom, w.name)
-        roofline["kernel"] = dom
-        roofline["kernel_us"] = round(stage_us[dom], 2)
-        roofline["algorithmic_bytes"] = b
-        roofline["algorithmic_flops"] = f
+            r = {"bound": "mfma" if w.dtype == "bf16" else "alu",
+                 "achieved": round(f / t / 1e12, 2), "peak": mfma_peak, "unit": "TFLOP/s"}
+        r["frac"] = round(r["achieved"] / r["peak"], 4)
+        r["traffic"] = load_traffic(kernel, w.name)
+        r["kernel"] = kernel
+        r["kernel_us"] = round(us, 2)
+        r["algorithmic_bytes"] = b
+        r["algorithmic_flops"] = f
+        return r
+
+    chunked_roofline = None
+    if stage_us:
+        dom = max(stage_us, key=stage_us.get)
+        chunked_roofline = roofline_of(dom, stage_us[dom])
+    chunked = {"us": round(ms * 1e3, 2), "wall_us": round(wall / args.steps * 1e6, 2),
+               "tokens_per_s": round(value, 1), "roofline": chunked_roofline}
+    path, roofline, ms_step = "ssd_chunk_scan_fwd", chunked_roofline, ms
+    if fused is not None:
+        fused["roofline"] = roofline_of("fused_fwd", fused["us"])
+        if fused["us"] < ms * 1e3:
+            path, roofline, ms_step, value = ("ssd_fused_fwd", fused["roofline"], fused["us"] / 1e3,
+                                              fused["tokens_per_s"])
 
     decode = None
     if not args.no_decode:
@@ -369,12 +427,15 @@ def main() -> int:
 
     out = {
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 5),
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
-        "config": {**workloads.describe(w), "parallelism": "none (1 GPU)"},
-        "roofline": roofline, "cpu_baseline": cpu, "kernels": kernels, "decode_step": decode,
-        "block_neighbours": block,
+        "config": {**workloads.describe(w), "path": path,
+                   "chunk": FUSED_CHUNK if path == "ssd_fused_fwd" else w.chunk,
+                   "parallelism": "none (1 GPU)"},
+        "roofline": roofline, "cpu_baseline": cpu,
+        "forwards": {"ssd_chunk_scan_fwd": chunked, "ssd_fused_fwd": fused},
+        "kernels": kernels, "decode_step": decode, "block_neighbours": block,
     }
     print(json.dumps(out), flush=True)
     return 0
