@@ -164,15 +164,18 @@ void k_ssd_fused(
   const float Dh = Dv ? Dv[h] : 0.f;
   float *adw = reinterpret_cast<float *>(smem + AD + wave * ADW);
 
-  // state h^T: hst[pt][j] holds rows n = 16 j + 4 g4 + r, column
-  // p = 32 ph + 16 pt + c16
+  // state h^T: hst[pt][j] holds column p = 32 ph + 16 pt + c16 and rows
+  // n = nrow(j) + r, nrow(j) = 32 (j/2) + 8 g4 + 4 (j%2): tiles 2q and 2q+1
+  // together give lane group g4 the 8 consecutive n = 32q + 8 g4 + 0..7, so a
+  // K step of the inter term reads its C operand as one 16-byte piece
+  auto nrow = [&](int j) { return 32 * (j >> 1) + 8 * g4 + 4 * (j & 1); };
   f32x4 hst[2][NT];
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
-    const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N + 4 * g4;
+    const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      hst[pt][j] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + prow + 16 * j) : f32x4{};
+      hst[pt][j] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + prow + nrow(j)) : f32x4{};
   }
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
   // The registers hold S = h / 2^lam: the decay of a chunk goes into lam
@@ -235,15 +238,18 @@ void k_ssd_fused(
       if (r < rem) *reinterpret_cast<u32x4 *>(y + (t0 + r) * ldx + (int64_t)h * P + 8 * cc) = v[i];
     }
   };
-  // row operand of a B or C tile in the state's K order: K step q covers
-  // n = 32q + 4 g4 + {0..3} and 32q + 16 + 4 g4 + {0..3}
+  // row operand of a B or C tile in the state's K order: K step q gives lane
+  // group g4 n = 32q + 8 g4 + {0..7}, one 16-byte chunk
   auto row_op = [&](const unsigned char *tile, int row, int q) {
-    const unsigned char *rp = tile + row * (N * 2);
-    const int sw = chunk_swz(row, NCB);
-    const int c0 = 4 * q + (g4 >> 1), off = 8 * (g4 & 1);
-    const u32x2 lo = *reinterpret_cast<const u32x2 *>(rp + ((c0 ^ sw) << 4) + off);
-    const u32x2 hi = *reinterpret_cast<const u32x2 *>(rp + (((c0 + 2) ^ sw) << 4) + off);
-    return u32x4{lo.x, lo.y, hi.x, hi.y};
+    return *reinterpret_cast<const u32x4 *>(tile + row * (N * 2) + (((4 * q + g4) ^ chunk_swz(row, NCB)) << 4));
+  };
+  // B^T operand of state tile j: transposing read of token rows row0 + {0..3};
+  // lane (c16, g4) receives column nrow-order n = 32 (j/2) + 8 (c16/4) +
+  // 4 (j%2) + c16 % 4 (each 4-lane group addresses its own 4-column piece)
+  auto trb = [&](const unsigned char *tile, int row0, int j) {
+    const int row = row0 + (c16 >> 2), col = 32 * (j >> 1) + 8 * (c16 & 3) + 4 * (j & 1);
+    const int cc = (col >> 3) ^ chunk_swz(row, NCB);
+    return lds_read_tr16(tile + row * (N * 2) + (cc << 4) + (col & 7) * 2);
   };
   // transposing read of 4 token rows row0 + {0..3} at column col0 + c16 of a
   // row-major tile (ncc chunks a row, row bytes rb)
@@ -403,7 +409,7 @@ void k_ssd_fused(
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const u32x2 t0 = tr4(bs, N * 2, NCB, 4 * g4, 16 * j), t1 = tr4(bs, N * 2, NCB, 16 + 4 * g4, 16 * j);
+        const u32x2 t0 = trb(bs, 4 * g4, j), t1 = trb(bs, 16 + 4 * g4, j);
         const u32x4 bt{t0.x, t0.y, t1.x, t1.y};
 #pragma unroll
         for (int pt = 0; pt < 2; ++pt) hst[pt][j] = mfma16(bt, xw[pt], hst[pt][j]);
@@ -438,9 +444,9 @@ void k_ssd_fused(
     const float e = exp2_fast(lam);
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
-      const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N + 4 * g4;
+      const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(hfin + prow + 16 * j) = hst[pt][j] * e;
+      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(hfin + prow + nrow(j)) = hst[pt][j] * e;
     }
   }
 }
