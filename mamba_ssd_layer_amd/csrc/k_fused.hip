@@ -78,6 +78,16 @@ __device__ __forceinline__ float scan32(float a) {
   return a;
 }
 
+// XOR swizzle of the 16-byte chunks of an LDS tile row (NC = 8 or 16 chunks a
+// row).  The transposing reads take 4 consecutive rows x 4 consecutive
+// chunks per 16 lanes, and the row operands 16 consecutive rows x 1 chunk:
+// swapping the row's two low bit pairs into the chunk index (16 chunks), or
+// the row-pair index's (8 chunks), keeps both patterns on distinct banks.
+template <int NC>
+__device__ __forceinline__ int rot_swz(int r) {
+  return NC == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
 __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -192,13 +202,13 @@ void k_ssd_fused(
   auto lane_offsets = [&](int last) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {  // rows 16 ph .. 16 ph + 15 of head hh's x, 8 chunks each
-      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = (m & 7) ^ chunk_swz(r, 8);
+      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = (m & 7) ^ rot_swz<8>(r);
       xoff[i] = static_cast<uint32_t>((min(r, last) * ldx + (int64_t)h * P + 8 * cc) * 2);
     }
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {  // B and C pieces
       const int u = wave * BCI + i, pi = u % (BT / 1024);
-      const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ chunk_swz(r, NCB);
+      const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ rot_swz<NCB>(r);
       bcoff[i] = static_cast<uint32_t>((min(r, last) * ldb + (int64_t)g * N + 8 * cc) * 2);
     }
     // dt of the block's heads: entry e = token * HPB + head, 64 entries a
@@ -230,7 +240,7 @@ void k_ssd_fused(
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = m & 7;
-      v[i] = *reinterpret_cast<const u32x4 *>(ys + r * 128 + ((cc ^ chunk_swz(r, 8)) << 4));
+      v[i] = *reinterpret_cast<const u32x4 *>(ys + r * 128 + ((cc ^ rot_swz<8>(r)) << 4));
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -241,21 +251,21 @@ void k_ssd_fused(
   // row operand of a B or C tile in the state's K order: K step q gives lane
   // group g4 n = 32q + 8 g4 + {0..7}, one 16-byte chunk
   auto row_op = [&](const unsigned char *tile, int row, int q) {
-    return *reinterpret_cast<const u32x4 *>(tile + row * (N * 2) + (((4 * q + g4) ^ chunk_swz(row, NCB)) << 4));
+    return *reinterpret_cast<const u32x4 *>(tile + row * (N * 2) + (((4 * q + g4) ^ rot_swz<NCB>(row)) << 4));
   };
   // B^T operand of state tile j: transposing read of token rows row0 + {0..3};
   // lane (c16, g4) receives column nrow-order n = 32 (j/2) + 8 (c16/4) +
   // 4 (j%2) + c16 % 4 (each 4-lane group addresses its own 4-column piece)
   auto trb = [&](const unsigned char *tile, int row0, int j) {
     const int row = row0 + (c16 >> 2), col = 32 * (j >> 1) + 8 * (c16 & 3) + 4 * (j & 1);
-    const int cc = (col >> 3) ^ chunk_swz(row, NCB);
+    const int cc = (col >> 3) ^ rot_swz<NCB>(row);
     return lds_read_tr16(tile + row * (N * 2) + (cc << 4) + (col & 7) * 2);
   };
   // transposing read of 4 token rows row0 + {0..3} at column col0 + c16 of a
   // row-major tile (ncc chunks a row, row bytes rb)
   auto tr4 = [&](const unsigned char *tile, int rb, int ncc, int row0, int col0) {
     const int row = row0 + (c16 >> 2), col = col0 + 4 * (c16 & 3);
-    const int cc = (col >> 3) ^ chunk_swz(row, ncc);
+    const int cc = (col >> 3) ^ rot_swz<8>(row);
     return lds_read_tr16(tile + row * rb + (cc << 4) + (col & 7) * 2);
   };
 
@@ -376,7 +386,7 @@ void k_ssd_fused(
       for (int lt = 0; lt < 2; ++lt) {
         const int l = 16 * lt + c16, col = 32 * ph + 16 * pt + 4 * g4;
         const u32x2 v = *reinterpret_cast<const u32x2 *>(
-            xh + l * 128 + (((col >> 3) ^ chunk_swz(l, 8)) << 4) + (col & 7) * 2);
+            xh + l * 128 + (((col >> 3) ^ rot_swz<8>(l)) << 4) + (col & 7) * 2);
         ya[pt][lt].x += Dh * bf16lo(v.x);
         ya[pt][lt].y += Dh * bf16hi(v.x);
         ya[pt][lt].z += Dh * bf16lo(v.y);
@@ -431,7 +441,7 @@ void k_ssd_fused(
       for (int lt = 0; lt < 2; ++lt) {
         const int l = 16 * lt + c16, col = 32 * ph + 16 * pt + 4 * g4;
         const u32x2 o{pack_bf16x2(ya[pt][lt].x, ya[pt][lt].y), pack_bf16x2(ya[pt][lt].z, ya[pt][lt].w)};
-        *reinterpret_cast<u32x2 *>(xh + l * 128 + (((col >> 3) ^ chunk_swz(l, 8)) << 4) + (col & 7) * 2) = o;
+        *reinterpret_cast<u32x2 *>(xh + l * 128 + (((col >> 3) ^ rot_swz<8>(l)) << 4) + (col & 7) * 2) = o;
       }
     }
     sl = sl == R - 1 ? 0 : sl + 1;
