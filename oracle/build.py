@@ -10,13 +10,13 @@ import subprocess
 import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-SRC = os.path.join(HERE, "ssd_recurrence.c")
+SRCS = [os.path.join(HERE, "ssd_recurrence.c"), os.path.join(HERE, "ssd_recurrence_bwd.c")]
 LIB = os.path.join(HERE, "libssd_oracle.so")
 
 
 def build(verbose: bool = False) -> str:
     cmd = ["gcc", "-O2", "-fPIC", "-shared", "-fopenmp", "-std=c99", "-Wall", "-Wextra",
-           "-fno-fast-math", "-ffp-contract=off", SRC, "-o", LIB + ".tmp", "-lm"]
+           "-fno-fast-math", "-ffp-contract=off", *SRCS, "-o", LIB + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
