@@ -249,6 +249,67 @@ ssd_status ssd_fused_fwd(const void *x, const float *dt, const float *A, const v
                          const int32_t *cu_seqlens, void *y, float *final_state,
                          const ssd_dims *dims, void *stream);
 
+/* ssd_fused_fwd that also saves, for the backward pass, the state entering
+ * every 32-token chunk (the inter-chunk states of page "Mamba-2 Architecture:
+ * State Space Duality Explained", "2. The Chunked SSD Algorithm", item 3),
+ * rounded to bf16:
+ *   chunk_states  device bf16 [nchunks][H][P][N], 16-byte aligned, not
+ *                 overlapping any other argument; chunk c = the sequence-major
+ *                 index of the 32-token chunk (sequence s's chunks start at
+ *                 the sum of ceil(len_i / 32) over i < s); NULL: nothing saved
+ *                 (then this is ssd_fused_fwd);
+ *   states_bytes  its size, at least ssd_fused_states_size(dims), else
+ *                 SSD_ERR_WORKSPACE.
+ * Everything else as ssd_fused_fwd.  Returns after enqueueing. */
+ssd_status ssd_fused_fwd_train(const void *x, const float *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *init_state,
+                               const int32_t *cu_seqlens, void *y, float *final_state,
+                               void *chunk_states, size_t states_bytes, const ssd_dims *dims,
+                               void *stream);
+
+/* Bytes of ssd_fused_fwd_train's chunk_states for these dims (nchunks =
+ * batch * ceil(seqlen / 32), or ceil(T / 32) + nseq for packed sequences);
+ * 0 if the dims are invalid or outside ssd_fused_fwd's shapes.  Host-only. */
+size_t ssd_fused_states_size(const ssd_dims *dims);
+
+/* Workspace bytes of ssd_fused_bwd (the gradient w.r.t. the state leaving
+ * every chunk, bf16, laid out like chunk_states).  Host-only. */
+size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
+
+/* Gradients of the forward.  The pages give the recurrence h_t = exp(dt_t A)
+ * h_{t-1} + dt_t x_t B_t^T, y_t = h_t C_t + D x_t (page "State Space Duality
+ * and Mamba-2: Unifying Transformers and Semiseparable Matrices", section
+ * "Mathematical Foundations", with the scalar-identity decay of "The
+ * Scalar-Identity Structural Constraint"), but no backward pass; this is the
+ * chain rule applied to it, for the scalar loss
+ *   sum_t <dy_t, y_t> + sum_{s,h} <dfinal[s,h], final_state[s,h]>.
+ * Inputs (the forward's, same layouts): x, dt, A, B, C, D (may be NULL),
+ * cu_seqlens, and
+ *   chunk_states  what ssd_fused_fwd_train saved for these inputs and
+ *                 init_state (states_bytes its size);
+ *   dy            device bf16 [T, H, P], the gradient w.r.t. y;
+ *   dfinal        device float [rows, H, P, N] or NULL (zero).
+ * Outputs (device, overwritten; none may overlap an input or another output):
+ *   dx   bf16  [T, H, P]    16-byte aligned
+ *   ddt  float [T, H]
+ *   dA   float [H]
+ *   dB   float [T, G, N]    summed over the heads of each group, 16-byte aligned
+ *   dC   float [T, G, N]    likewise
+ *   dD   float [H], NULL exactly when D is NULL
+ *   dinit float [rows, H, P, N] (the gradient w.r.t. init_state) or NULL.
+ * workspace: device memory of at least ssd_fused_bwd_workspace_size(dims)
+ * bytes, 16-byte aligned, else SSD_ERR_WORKSPACE.  Supported shapes are
+ * ssd_fused_fwd's.  Three kernels on `stream` (dA and dD cleared, the
+ * reverse sweep of the state gradient, the per-chunk gradients); the
+ * per-chunk pass adds into dA and dD with float atomics, so those two sum in
+ * an unspecified order.  Returns after enqueueing. */
+ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const void *B,
+                         const void *C, const float *D, const int32_t *cu_seqlens,
+                         const void *chunk_states, size_t states_bytes, const void *dy,
+                         const float *dfinal, void *dx, float *ddt, float *dA, float *dB,
+                         float *dC, float *dD, float *dinit, const ssd_dims *dims, void *workspace,
+                         size_t workspace_bytes, void *stream);
+
 /* Static text for a status code. */
 const char *ssd_status_string(ssd_status status);
 

@@ -32,7 +32,7 @@ from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsuppo
 
 __all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDError", "SSDInvalidArgument",
            "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "step",
-           "conv1d_silu", "gate_rmsnorm", "fused_fwd"]
+           "conv1d_silu", "gate_rmsnorm", "fused_fwd", "make_fused_states", "fused_bwd"]
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -142,10 +142,13 @@ def fused_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
               init_state: Optional[torch.Tensor] = None,
               cu_seqlens: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
               final_state: Optional[torch.Tensor] = None, want_final: bool = True,
+              chunk_states: Optional[torch.Tensor] = None,
               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """y, final_state = SSD forward in one pass per (sequence, head) (ssd_fused_fwd:
     bf16, headdim 64, dstate 64 or 128; no workspace).  Same arguments and
-    results as chunk_scan_fwd."""
+    results as chunk_scan_fwd.  With chunk_states (a uint8 device buffer of
+    fused_states_bytes(...) bytes, see make_fused_states) it also saves the
+    state entering every 32-token chunk for fused_bwd (ssd_fused_fwd_train)."""
     dims = dims_for(x, B, cu_seqlens)
     if y is None:
         y = torch.empty_like(x)
@@ -153,8 +156,58 @@ def fused_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
         nrows = dims.nseq if dims.nseq > 0 else dims.batch
         final_state = torch.empty((nrows, dims.nheads, dims.headdim, dims.dstate),
                                   dtype=torch.float32, device=x.device)
-    libssd.ssd_fused_fwd(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, dims, stream)
+    if chunk_states is None:
+        libssd.ssd_fused_fwd(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, dims,
+                             stream)
+    else:
+        libssd.ssd_fused_fwd_train(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state,
+                                   chunk_states, chunk_states.numel() * chunk_states.element_size(),
+                                   dims, stream)
     return y, final_state
+
+
+def make_fused_states(x: torch.Tensor, B: torch.Tensor,
+                      cu_seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """A device byte buffer for fused_fwd's saved chunk states (or for
+    fused_bwd's workspace, which has the same size)."""
+    dims = dims_for(x, B, cu_seqlens)
+    n = libssd.ssd_fused_states_size(dims)
+    if n == 0:
+        raise SSDUnsupported(libssd.SSD_ERR_UNSUPPORTED, "shape outside the one-pass forward")
+    return torch.empty(n, dtype=torch.uint8, device=x.device)
+
+
+def fused_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+              C: torch.Tensor, D: Optional[torch.Tensor], chunk_states: torch.Tensor,
+              dy: torch.Tensor, dfinal: Optional[torch.Tensor] = None,
+              cu_seqlens: Optional[torch.Tensor] = None, want_dinit: bool = True,
+              workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of fused_fwd (ssd_fused_bwd) for the loss
+    sum <dy, y> + sum <dfinal, final_state>, given the chunk states fused_fwd
+    saved for the same inputs.  Returns a dict with dx (like x, bf16), ddt
+    (like dt, float32), dA [H], dB and dC (float32, shaped like B and C),
+    dD [H] (None when D is None) and dinit [rows, H, P, N] (None unless
+    want_dinit)."""
+    dims = dims_for(x, B, cu_seqlens)
+    dev = x.device
+    nrows = dims.nseq if dims.nseq > 0 else dims.batch
+    if workspace is None:
+        n = libssd.ssd_fused_bwd_workspace_size(dims)
+        if n == 0:
+            raise SSDUnsupported(libssd.SSD_ERR_UNSUPPORTED, "shape outside the one-pass forward")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty(dt.shape, dtype=torch.float32, device=dev),
+               dA=torch.empty(dims.nheads, dtype=torch.float32, device=dev),
+               dB=torch.empty(B.shape, dtype=torch.float32, device=dev),
+               dC=torch.empty(C.shape, dtype=torch.float32, device=dev),
+               dD=torch.empty(dims.nheads, dtype=torch.float32, device=dev) if D is not None else None,
+               dinit=torch.empty((nrows, dims.nheads, dims.headdim, dims.dstate),
+                                 dtype=torch.float32, device=dev) if want_dinit else None)
+    libssd.ssd_fused_bwd(x, dt, A, B, C, D, cu_seqlens, chunk_states,
+                         chunk_states.numel() * chunk_states.element_size(), dy, dfinal,
+                         out["dx"], out["ddt"], out["dA"], out["dB"], out["dC"], out["dD"],
+                         out["dinit"], dims, workspace, workspace.numel(), stream)
+    return out
 
 
 def step(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor, C: torch.Tensor,

@@ -1,0 +1,740 @@
+// libssd: the backward pass of the SSD forward (its gradients), in 32-token
+// chunks, for bf16 io, P = 64, N in {64, 128}.
+//
+// The pages state no backward pass; it follows from the recurrence by the
+// chain rule (page "State Space Duality and Mamba-2: Unifying Transformers and
+// Semiseparable Matrices", section "Mathematical Foundations", with the
+// scalar-identity transition of "The Scalar-Identity Structural Constraint"
+// and the decay exp(dt A) of page "Mamba-2 Architecture: State Space Duality
+// Explained", Step 1).  With a_t = exp(dt_t A), h_t = a_t h_{t-1} + dt_t x_t
+// B_t^T, y_t = h_t C_t + D x_t and g_t = dL/dh_t:
+//   g_t = dy_t C_t^T + a_{t+1} g_{t+1}
+//   dx_t = D dy_t + dt_t g_t B_t,   dB_t = dt_t g_t^T x_t,   dC_t = h_t^T dy_t
+//   ddt_t = x_t^T g_t B_t + A a_t <g_t, h_{t-1}>,   dA = sum_t dt_t a_t <g_t, h_{t-1}>
+// Inside a chunk (tokens l, s; a_l the cumulative dt A from the chunk's start,
+// L_ls = exp(a_l - a_s) for s <= l; h_s the state at the chunk's start, g_e
+// the gradient flowing in from the next chunk) these become the blockwise
+// products the forward uses, transposed:
+//   Z_ls = C_l.B_s, E_ls = dy_l.x_s, M = Z o L dt_s, EL = E o L dt_s
+//   dx^T = dy^T M + (g_e B^T) w_s + D dy^T           w_s = exp(a_last - a_s) dt_s
+//   dB^T = C^T EL + (g_e^T x^T) w_s   (summed over the heads of a group)
+//   dC^T = B^T EL^T + (h_s^T dy^T) exp(a_l)
+//   ddt_t = sum_{l>=t} (E o Z o L)_lt + exp(a_last - a_t) q_t
+//           + A (R_t + V_t + U_t),   dA = sum_t dt_t (R_t + V_t + U_t)
+// with q_s = x_s^T g_e B_s, v_l = exp(a_l) dy_l.(h_s C_l), K = E o Z o L dt_s,
+// R_t = sum over l >= t > s of K_ls (a suffix sum of row sums minus column
+// sums of K's strict lower part), V_t = sum_{l>=t} v_l and
+// U_t = exp(a_last) <g_e, h_s> + sum_{s<t} w_s q_s.
+//
+// Three passes:
+//   1. the one-pass forward saves h_s of every chunk (k_ssd_fused, SAVE);
+//   2. k_bwd_reverse walks each (sequence, two heads) backwards, keeping g on
+//      chip like the forward keeps h (g <- exp(a_last) g + C^T (exp(a_l) dy)),
+//      saving g_e of every chunk and writing dL/dh0;
+//   3. k_bwd_chunk, one block per (chunk, group), walks the group's heads:
+//      the chunk's B and C stay in LDS, each head's x, dy, h_s and g_e stream
+//      through a two-slot LDS ring; dx and ddt are written per head, dB and dC
+//      accumulate over the heads in registers and are written once, dA and dD
+//      are added atomically per head.
+#include "ssd_device.hpp"
+#include "ssd_launch.hpp"
+
+namespace ssd {
+
+namespace {
+
+constexpr float kLog2eB = 1.4426950408889634f;
+
+__device__ __forceinline__ f32x4 mfma16b(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+__device__ __forceinline__ float exp2b(float v) { return __builtin_amdgcn_exp2f(v); }
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dppb(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+// inclusive prefix sum over lanes 0..31 (and independently 32..63)
+__device__ __forceinline__ float scan32b(float a) {
+  a += dppb<0x111, 0xF>(a);
+  a += dppb<0x112, 0xF>(a);
+  a += dppb<0x114, 0xF>(a);
+  a += dppb<0x118, 0xF>(a);
+  a += dppb<0x142, 0xA>(a);
+  return a;
+}
+__device__ __forceinline__ float lane31(float v) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
+}
+__device__ __forceinline__ void wsync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+// chunk swizzle of an LDS tile row of NC 16-byte chunks (as the forward's)
+template <int NC>
+__device__ __forceinline__ int swz(int r) {
+  return NC == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
+}
+
+// ---------------------------------------------------------------- pass 2
+// Block = (sequence, two heads of a group), 4 wavefronts (head hh, half ph);
+// wavefront (hh, ph) keeps rows p in [32 ph, 32 ph + 32) of head hh's g, held
+// transposed like the forward's state (tiles 2q, 2q+1 give lane group g4 the
+// n = 32q + 8 g4 + 0..7).  Chunks in reverse order through a three-slot ring
+// of dy (per head), C and dt.
+template <int N>
+__global__ __launch_bounds__(256, 2) void k_bwd_reverse(
+    const uint16_t *__restrict__ dy, const float *__restrict__ dt, const float *__restrict__ A,
+    const uint16_t *__restrict__ Cm, const float *__restrict__ dfinal,
+    const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows, int H, int G,
+    uint16_t *__restrict__ gsave, float *__restrict__ dinit) {
+  constexpr int P = 64, CQ = 32, R = 3;
+  constexpr int NT = N / 16, KQ = N / 32, NCB = N / 8;
+  constexpr int XH = CQ * P * 2, BT = CQ * N * 2, DW = 256;
+  constexpr int OY = 0, OC = 2 * XH, OD = OC + BT, SLOT = OD + 4 * DW;
+  constexpr int AD = R * SLOT, ADW = 2 * CQ * 4;
+  constexpr int BCI = BT / 1024 / 4;  // 1 KB pieces of C per wavefront
+  static_assert(BCI * 4 * 1024 == BT, "C split over 4 wavefronts");
+  __shared__ __align__(16) unsigned char smem[AD + 4 * ADW];
+
+  int s, hb;
+  xcd_chunk_head(H / 2, s, hb);
+  if (s >= rows) return;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4;
+  const int hh = wave >> 1, ph = wave & 1;
+  const int h = 2 * hb + hh, g = 2 * hb / (H / G);
+  int64_t tb, len;
+  seq_range(cu, s, L, T, tb, len);
+  const int nck = static_cast<int>((len + CQ - 1) / CQ);
+  const int64_t cbase = chunk_base32(cu, s, L, T);
+  const int64_t sh = (int64_t)s * H + h;
+  const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
+  const float Ah = A[h];
+  float *adw = reinterpret_cast<float *>(smem + AD + wave * ADW);
+  auto nrow = [&](int j) { return 32 * (j >> 1) + 8 * g4 + 4 * (j & 1); };
+
+  f32x4 gst[2][NT];
+#pragma unroll
+  for (int pt = 0; pt < 2; ++pt) {
+    const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N;
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      gst[pt][j] = dfinal ? *reinterpret_cast<const f32x4 *>(dfinal + prow + nrow(j)) : f32x4{};
+  }
+
+  auto issue = [&](int k, int sl) {
+    const int64_t t0 = tb + (int64_t)k * CQ;
+    const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
+    const uint32_t base = lds_off(smem) + sl * SLOT;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {  // rows 16 ph .. +15 of head hh's dy
+      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = (m & 7) ^ swz<8>(r);
+      dma_lds16(dy + (t0 + min(r, last)) * ldx + (int64_t)h * P + 8 * cc,
+                base + OY + hh * XH + 16 * ph * 128 + i * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < BCI; ++i) {
+      const int pi = wave * BCI + i, m = pi * 64 + lane, r = m / NCB;
+      const int cc = (m % NCB) ^ swz<NCB>(r);
+      dma_lds16(Cm + (t0 + min(r, last)) * ldb + (int64_t)g * N + 8 * cc, base + OC + pi * 1024);
+    }
+    dma_lds4(dt + (t0 + min(lane & 31, last)) * H + h, base + OD + wave * DW);
+  };
+
+  // reverse order: iteration i handles chunk nck - 1 - i in slot i % 3
+  if (nck > 0) issue(nck - 1, 0);
+  if (nck > 1) issue(nck - 2, 1);
+  int sl = 0;
+#pragma unroll 1
+  for (int i = 0; i < nck; ++i) {
+    const int k = nck - 1 - i;
+    wait_vmcnt<0>();
+    __syncthreads();
+    const int slp = sl == 0 ? 2 : sl - 1;
+    if (k - 2 >= 0) issue(k - 2, slp);
+    // the gradient flowing into chunk k from the later chunks
+    {
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        uint16_t *dst = gsave + ((cbase + k) * H + h) * (int64_t)(P * N) +
+                        (int64_t)(32 * ph + 16 * pt + c16) * N + 8 * g4;
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+          const f32x4 u = gst[pt][2 * q], v = gst[pt][2 * q + 1];
+          *reinterpret_cast<u32x4 *>(dst + 32 * q) =
+              u32x4{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
+                    pack_bf16x2(v.z, v.w)};
+        }
+      }
+    }
+    const unsigned char *ys = smem + sl * SLOT + OY + hh * XH;
+    const unsigned char *cs = smem + sl * SLOT + OC;
+    const float *dts = reinterpret_cast<const float *>(smem + sl * SLOT + OD + wave * DW);
+    const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
+    const int tl = lane & 31;
+    const float dtv = tl <= last ? dts[lane] : 0.f;
+    const float a = scan32b(dtv * Ah);
+    const float alast = lane31(a);
+    // exp(a_l); 0 for the rows past a partial chunk's end (they repeat its last row)
+    if (lane < 32) adw[tl] = tl <= last ? exp2b(a * kLog2eB) : 0.f;
+    wsync();
+    // g <- exp(a_last) g + C^T (exp(a_l) dy)
+    const float e = exp2b(alast * kLog2eB);
+    u32x4 fy[2];
+    {
+      const f32x4 f0 = *reinterpret_cast<const f32x4 *>(adw + 4 * g4);
+      const f32x4 f1 = *reinterpret_cast<const f32x4 *>(adw + 16 + 4 * g4);
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        u32x2 t[2];
+#pragma unroll
+        for (int hf = 0; hf < 2; ++hf) {
+          const int row = 16 * hf + 4 * g4 + (c16 >> 2), col = 32 * ph + 16 * pt + 4 * (c16 & 3);
+          const int cc = (col >> 3) ^ swz<8>(row);
+          t[hf] = lds_read_tr16(ys + row * 128 + (cc << 4) + (col & 7) * 2);
+        }
+        fy[pt] = u32x4{pack_bf16x2(bf16lo(t[0].x) * f0.x, bf16hi(t[0].x) * f0.y),
+                       pack_bf16x2(bf16lo(t[0].y) * f0.z, bf16hi(t[0].y) * f0.w),
+                       pack_bf16x2(bf16lo(t[1].x) * f1.x, bf16hi(t[1].x) * f1.y),
+                       pack_bf16x2(bf16lo(t[1].y) * f1.z, bf16hi(t[1].y) * f1.w)};
+#pragma unroll
+        for (int j = 0; j < NT; ++j) gst[pt][j] *= e;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      u32x2 t[2];
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        const int row = 16 * hf + 4 * g4 + (c16 >> 2);
+        const int col = 32 * (j >> 1) + 8 * (c16 & 3) + 4 * (j & 1);
+        const int cc = (col >> 3) ^ swz<NCB>(row);
+        t[hf] = lds_read_tr16(cs + row * (N * 2) + (cc << 4) + (col & 7) * 2);
+      }
+      const u32x4 ct{t[0].x, t[0].y, t[1].x, t[1].y};
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) gst[pt][j] = mfma16b(ct, fy[pt], gst[pt][j]);
+    }
+    sl = sl == 2 ? 0 : sl + 1;
+  }
+  if (dinit) {
+#pragma unroll
+    for (int pt = 0; pt < 2; ++pt) {
+      const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N;
+#pragma unroll
+      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(dinit + prow + nrow(j)) = gst[pt][j];
+    }
+  }
+}
+
+// ---------------------------------------------------------------- pass 3
+// Block = (32-token chunk, group), 4 wavefronts, walking the group's heads.
+// LDS: the chunk's B and C (rows = tokens), and a two-slot ring per head of
+// x and dy (rows = tokens, 8 chunks a row), h_s and g_e (rows = p, N/8
+// chunks a row) and dt; per-wavefront tables; cross-wavefront partial sums.
+// Tile conventions (16x16x32 MFMA): an "E-layout" tile holds matrix[l][s] with
+// lane (c16 = s, g4) rows l = 16 lt + 4 g4 + r; its pair (lt = 0, 1) packs to a
+// B-operand with K = l in the order {4 g4 + 0..3, 16 + 4 g4 + 0..3}, matched by
+// transposing reads of token rows in the same order for the A-operand.
+template <int N>
+struct BwdCfg {
+  static constexpr int P = 64, CQ = 32, NCB = N / 8;
+  static constexpr int XT = CQ * P * 2;      // x or dy of a head: 32 rows x 128 B
+  static constexpr int ST = P * N * 2;       // h_s or g_e of a head: 64 rows x N bf16
+  static constexpr int BT = CQ * N * 2;      // B or C of the chunk
+  static constexpr int OX = 0, OY = XT, OH = 2 * XT, OG = OH + ST, ODT = OG + ST;
+  static constexpr int HSLOT = ODT + 256;
+  static constexpr int OB = 2 * HSLOT, OCC = OB + BT;
+  static constexpr int OTAB = OCC + BT;       // per wavefront: 6 tables of 32 floats
+  static constexpr int TABW = 6 * CQ * 4;
+  static constexpr int OPART = OTAB + 4 * TABW;  // per wavefront: v[32], q[32], gh
+  static constexpr int PARTW = (2 * CQ + 4) * 4;
+  static constexpr int OSC = OPART + 4 * PARTW;  // term1a[32], rowK[32], colK[32], diagE[32]
+  static constexpr int TOTAL = OSC + 4 * CQ * 4;
+  static constexpr int PIECES = (2 * XT + 2 * ST) / 1024;  // 1 KB pieces of a head's tiles
+  static constexpr int BLOCKS = (160 * 1024) / TOTAL;
+  static_assert(PIECES % 4 == 0, "pieces split over 4 wavefronts");
+  static_assert(BLOCKS >= 1, "LDS");
+};
+
+template <int N>
+__global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
+    const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
+    const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
+    const uint16_t *__restrict__ dy, const uint16_t *__restrict__ hsave,
+    const uint16_t *__restrict__ gsave, const int32_t *__restrict__ cu, int64_t L, int64_t T,
+    int rows, int64_t nchunks, int H, int G, uint16_t *__restrict__ dx,
+    float *__restrict__ ddt, float *__restrict__ dA, float *__restrict__ dB,
+    float *__restrict__ dC, float *__restrict__ dD) {
+  using F = BwdCfg<N>;
+  constexpr int P = F::P, CQ = F::CQ, NCB = F::NCB;
+  constexpr int KQ = N / 32;       // K steps over n
+  constexpr int NTW = N / 16 / 4;  // n-tiles of dB / dC a wavefront owns
+  __shared__ __align__(16) unsigned char smem[F::TOTAL];
+
+  const int64_t c = blockIdx.x / G;
+  const int g = static_cast<int>(blockIdx.x % G);
+  if (c >= nchunks) return;
+  // chunk c of the sequence-major list -> (sequence, chunk within it)
+  int s = -1;
+  int64_t k = 0, tb = 0, len = 0;
+  if (!cu) {
+    const int64_t nckr = (L + CQ - 1) / CQ;
+    if (nckr == 0) return;
+    s = static_cast<int>(c / nckr);
+    k = c % nckr;
+    if (s >= rows) return;
+    seq_range(cu, s, L, T, tb, len);
+  } else {
+    int64_t acc = 0;
+    for (int i = 0; i < rows; ++i) {
+      int64_t b, l;
+      seq_range(cu, i, L, T, b, l);
+      const int64_t n = (l + CQ - 1) / CQ;
+      if (c < acc + n) {
+        s = i;
+        k = c - acc;
+        tb = b;
+        len = l;
+        break;
+      }
+      acc += n;
+    }
+    if (s < 0) return;
+  }
+  const int64_t t0 = tb + k * CQ;
+  const int last = static_cast<int>(min((int64_t)CQ, len - k * CQ)) - 1;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int c16 = lane & 15, g4 = lane >> 4, tl = lane & 31;
+  const int hpg = H / G;
+  const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
+  const uint32_t lbase = lds_off(smem);
+  const unsigned char *bsm = smem + F::OB;
+  const unsigned char *csm = smem + F::OCC;
+  float *tab = reinterpret_cast<float *>(smem + F::OTAB + wave * F::TABW);
+  float *part = reinterpret_cast<float *>(smem + F::OPART);
+  float *sc = reinterpret_cast<float *>(smem + F::OSC);
+  enum { TA2 = 0, TF = 32, TW = 64, TDT = 96, TEL = 128 };           // table rows
+  enum { PV = 0, PQ = 32, PGH = 64 };                                // partials, per wavefront
+  enum { ST1 = 0, SRK = 32, SCK = 64, SDE = 96 };                    // scalars of wavefront 0
+
+  // ---- operand reads ----
+  // 16 bytes of a token row of x / dy (8 chunks): p = 32 kq + 8 g4 + 0..7
+  auto rowx = [&](const unsigned char *t, int row, int kq) {
+    return *reinterpret_cast<const u32x4 *>(t + row * 128 + (((4 * kq + g4) ^ swz<8>(row)) << 4));
+  };
+  // 16 bytes of a row of an N-wide tile (B, C, h_s, g_e): n = 32 q + 8 g4 + 0..7
+  auto rown = [&](const unsigned char *t, int row, int q) {
+    return *reinterpret_cast<const u32x4 *>(t + row * (N * 2) + (((4 * q + g4) ^ swz<NCB>(row)) << 4));
+  };
+  // transposing read: rows r0 + (c16 >> 2) and r1 + (c16 >> 2), column col0 + c16 of the lane
+  auto trn = [&](const unsigned char *t, int rb, int r0, int r1, int col0, bool wide) {
+    u32x2 v[2];
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const int row = (hf ? r1 : r0) + (c16 >> 2), col = col0 + 4 * (c16 & 3);
+      const int cc = (col >> 3) ^ (wide ? swz<NCB>(row) : swz<8>(row));
+      v[hf] = lds_read_tr16(t + row * rb + (cc << 4) + (col & 7) * 2);
+    }
+    return u32x4{v[0].x, v[0].y, v[1].x, v[1].y};
+  };
+
+  // head j's x, dy, h_s, g_e (1 KB pieces split over the wavefronts) and dt
+  auto issue_head = [&](int j, int sl) {
+    const int h = g * hpg + j;
+    const uint32_t base = lbase + sl * F::HSLOT;
+#pragma unroll
+    for (int i = 0; i < F::PIECES / 4; ++i) {
+      const int u = wave + 4 * i;
+      if (u < 8) {  // x (0..3) or dy (4..7): 32 rows x 8 chunks
+        const int pi = u & 3, m = pi * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz<8>(r);
+        dma_lds16((u < 4 ? x : dy) + (t0 + min(r, last)) * ldx + (int64_t)h * P + 8 * cc,
+                  base + (u < 4 ? F::OX : F::OY) + pi * 1024);
+      } else {  // h_s (8..) or g_e: 64 rows x N/8 chunks
+        const int v = u - 8, tile = v / (F::ST / 1024), pi = v % (F::ST / 1024);
+        const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz<NCB>(r);
+        dma_lds16((tile ? gsave : hsave) + (c * H + h) * (int64_t)(P * N) + (int64_t)r * N + 8 * cc,
+                  base + (tile ? F::OG : F::OH) + pi * 1024);
+      }
+    }
+    if (wave == 0) dma_lds4(dt + (t0 + min(lane & 31, last)) * H + h, base + F::ODT);
+  };
+
+  // ---- the chunk's B and C, head 0 ----
+  {
+    constexpr int BCP = 2 * F::BT / 1024 / 4;
+#pragma unroll
+    for (int i = 0; i < BCP; ++i) {
+      const int u = wave * BCP + i, tile = u / (F::BT / 1024), pi = u % (F::BT / 1024);
+      const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz<NCB>(r);
+      dma_lds16((tile ? Cm : Bm) + (t0 + min(r, last)) * ldb + (int64_t)g * N + 8 * cc,
+                lbase + (tile ? F::OCC : F::OB) + pi * 1024);
+    }
+  }
+  issue_head(0, 0);
+  wait_vmcnt<0>();
+  __syncthreads();
+  // Z = C B^T in E-layout tiles [lt][st]
+  f32x4 z[2][2];
+#pragma unroll
+  for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      f32x4 acc{};
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) acc = mfma16b(rown(csm, 16 * lt + c16, q), rown(bsm, 16 * st + c16, q), acc);
+      z[lt][st] = acc;
+    }
+
+  f32x4 dBa[NTW][2], dCa[NTW][2];
+#pragma unroll
+  for (int i = 0; i < NTW; ++i)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      dBa[i][t] = f32x4{};
+      dCa[i][t] = f32x4{};
+    }
+
+#pragma unroll 1
+  for (int j = 0; j < hpg; ++j) {
+    const int sl = j & 1;
+    const int h = g * hpg + j;
+    if (j > 0) {
+      wait_vmcnt<0>();
+      __syncthreads();  // head j is in everywhere; head j-1 is done everywhere
+    }
+    if (j + 1 < hpg) issue_head(j + 1, sl ^ 1);
+    unsigned char *hsl = smem + sl * F::HSLOT;
+    const unsigned char *xs = hsl + F::OX;
+    unsigned char *ys = hsl + F::OY;
+    const unsigned char *hss = hsl + F::OH;
+    const unsigned char *gss = hsl + F::OG;
+    const float *dts = reinterpret_cast<const float *>(hsl + F::ODT);
+    if (last < CQ - 1) {  // dy of tokens past the sequence's end is zero
+      for (int i = threadIdx.x; i < (CQ - 1 - last) * 8; i += 256) {
+        const int row = last + 1 + (i >> 3);
+        *reinterpret_cast<u32x4 *>(ys + row * 128 + ((i & 7) << 4)) = u32x4{0u, 0u, 0u, 0u};
+      }
+      __syncthreads();
+    }
+    const float Ah = A[h];
+    // per-token tables: a_l (log2), exp(a_l), w_s, dt_s, exp(a_last - a_t)
+    const float dtv = tl <= last ? dts[tl] : 0.f;
+    const float a = scan32b(dtv * Ah);
+    const float alast = lane31(a);
+    if (lane < 32) {
+      tab[TA2 + tl] = a * kLog2eB;
+      tab[TF + tl] = exp2b(a * kLog2eB);
+      tab[TW + tl] = exp2b((alast - a) * kLog2eB) * dtv;
+      tab[TDT + tl] = dtv;
+      tab[TEL + tl] = exp2b((alast - a) * kLog2eB);
+    }
+    wsync();
+
+    // E = dy x^T (E-layout [lt][st]) and E^T (ET-layout [st][lt])
+    f32x4 e[2][2], et[2][2];
+#pragma unroll
+    for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        f32x4 a1{}, a2{};
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          const u32x4 yl = rowx(ys, 16 * lt + c16, kq), xsr = rowx(xs, 16 * st + c16, kq);
+          a1 = mfma16b(yl, rowx(xs, 16 * st + c16, kq), a1);
+          a2 = mfma16b(xsr, rowx(ys, 16 * lt + c16, kq), a2);
+        }
+        e[lt][st] = a1;
+        et[st][lt] = a2;
+      }
+    // masked, decayed products.  E-layout (lt, st): l = 16 lt + 4 g4 + r, s = 16 st + c16
+    u32x4 mop[2], elop[2], eltop[2];
+    float pv[2][2][4];  // E o Z o L (no dt), E-layout
+    {
+      float m_[2][2][4], el_[2][2][4], elt_[2][2][4];
+#pragma unroll
+      for (int lt = 0; lt < 2; ++lt) {
+        const f32x4 al = *reinterpret_cast<const f32x4 *>(tab + TA2 + 16 * lt + 4 * g4);
+#pragma unroll
+        for (int st = 0; st < 2; ++st) {
+          const float as = tab[TA2 + 16 * st + c16], ds = tab[TDT + 16 * st + c16];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int l = 16 * lt + 4 * g4 + r, sx = 16 * st + c16;
+            const bool ok = sx <= l;
+            const float lf = ok ? exp2b(fminf(al[r] - as, 0.f)) : 0.f;
+            m_[lt][st][r] = z[lt][st][r] * lf * ds;
+            el_[lt][st][r] = e[lt][st][r] * lf * ds;
+            pv[lt][st][r] = e[lt][st][r] * z[lt][st][r] * lf;
+          }
+        }
+      }
+      // ET-layout (st, lt): s = 16 st + 4 g4 + r, l = 16 lt + c16
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const f32x4 as = *reinterpret_cast<const f32x4 *>(tab + TA2 + 16 * st + 4 * g4);
+        const f32x4 ds = *reinterpret_cast<const f32x4 *>(tab + TDT + 16 * st + 4 * g4);
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+          const float al = tab[TA2 + 16 * lt + c16];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int sx = 16 * st + 4 * g4 + r, l = 16 * lt + c16;
+            const bool ok = sx <= l;
+            const float lf = ok ? exp2b(fminf(al - as[r], 0.f)) : 0.f;
+            elt_[st][lt][r] = et[st][lt][r] * lf * ds[r];
+          }
+        }
+      }
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        mop[t] = u32x4{pack_bf16x2(m_[0][t][0], m_[0][t][1]), pack_bf16x2(m_[0][t][2], m_[0][t][3]),
+                       pack_bf16x2(m_[1][t][0], m_[1][t][1]), pack_bf16x2(m_[1][t][2], m_[1][t][3])};
+        elop[t] = u32x4{pack_bf16x2(el_[0][t][0], el_[0][t][1]), pack_bf16x2(el_[0][t][2], el_[0][t][3]),
+                        pack_bf16x2(el_[1][t][0], el_[1][t][1]), pack_bf16x2(el_[1][t][2], el_[1][t][3])};
+        eltop[t] = u32x4{pack_bf16x2(elt_[0][t][0], elt_[0][t][1]), pack_bf16x2(elt_[0][t][2], elt_[0][t][3]),
+                         pack_bf16x2(elt_[1][t][0], elt_[1][t][1]), pack_bf16x2(elt_[1][t][2], elt_[1][t][3])};
+      }
+    }
+
+    // ---- dx rows of p-tile pt = wave; q_s and v_l partials ----
+    const float Dh = Dv ? Dv[h] : 0.f;
+    {
+      const int pt = wave;
+      const u32x4 dyt = trn(ys, 128, 4 * g4, 16 + 4 * g4, 16 * pt, false);
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        f32x4 acc = mfma16b(dyt, mop[st], f32x4{});
+        f32x4 gb{};
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) gb = mfma16b(rown(gss, 16 * pt + c16, q), rown(bsm, 16 * st + c16, q), gb);
+        // lane: column s, rows p = 16 pt + 4 g4 + r
+        const int sx = 16 * st + c16, col = 16 * pt + 4 * g4;
+        const float ws = tab[TW + sx];
+        const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2);
+        const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2);
+        const float o0 = acc.x + ws * gb.x + Dh * bf16lo(dv.x);
+        const float o1 = acc.y + ws * gb.y + Dh * bf16hi(dv.x);
+        const float o2 = acc.z + ws * gb.z + Dh * bf16lo(dv.y);
+        const float o3 = acc.w + ws * gb.w + Dh * bf16hi(dv.y);
+        if (sx <= last)
+          *reinterpret_cast<u32x2 *>(dx + (t0 + sx) * ldx + (int64_t)h * P + col) =
+              u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+        float qv = bf16lo(xv.x) * gb.x + bf16hi(xv.x) * gb.y + bf16lo(xv.y) * gb.z + bf16hi(xv.y) * gb.w;
+        qv += __shfl_xor(qv, 16, 64);
+        qv += __shfl_xor(qv, 32, 64);
+        if (lane < 16) part[wave * (2 * CQ + 4) + PQ + sx] = qv;
+      }
+#pragma unroll
+      for (int lt = 0; lt < 2; ++lt) {
+        f32x4 hc{};
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) hc = mfma16b(rown(hss, 16 * pt + c16, q), rown(csm, 16 * lt + c16, q), hc);
+        const int lx = 16 * lt + c16, col = 16 * pt + 4 * g4;
+        const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + lx * 128 + (((col >> 3) ^ swz<8>(lx)) << 4) + (col & 7) * 2);
+        float vv = bf16lo(dv.x) * hc.x + bf16hi(dv.x) * hc.y + bf16lo(dv.y) * hc.z + bf16hi(dv.y) * hc.w;
+        vv += __shfl_xor(vv, 16, 64);
+        vv += __shfl_xor(vv, 32, 64);
+        if (lane < 16) part[wave * (2 * CQ + 4) + PV + lx] = vv;
+      }
+      // <g_e, h_s> over rows p = 16 pt .. +15: lane takes a quarter row
+      {
+        const int row = 16 * pt + (lane >> 2);
+        float acc = 0.f;
+#pragma unroll
+        for (int cj = 0; cj < NCB / 4; ++cj) {
+          const int ch = (lane & 3) * (NCB / 4) + cj;
+          const int off = row * (N * 2) + ((ch ^ swz<NCB>(row)) << 4);
+          const u32x4 gv = *reinterpret_cast<const u32x4 *>(gss + off);
+          const u32x4 hv = *reinterpret_cast<const u32x4 *>(hss + off);
+          acc += bf16lo(gv.x) * bf16lo(hv.x) + bf16hi(gv.x) * bf16hi(hv.x) + bf16lo(gv.y) * bf16lo(hv.y) +
+                 bf16hi(gv.y) * bf16hi(hv.y) + bf16lo(gv.z) * bf16lo(hv.z) + bf16hi(gv.z) * bf16hi(hv.z) +
+                 bf16lo(gv.w) * bf16lo(hv.w) + bf16hi(gv.w) * bf16hi(hv.w);
+        }
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
+        if (lane == 0) part[wave * (2 * CQ + 4) + PGH] = acc;
+      }
+    }
+
+    // ---- dB, dC over the wavefront's n-tiles ----
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+      const int nt = wave * NTW + i;
+      const u32x4 ct = trn(csm, N * 2, 4 * g4, 16 + 4 * g4, 16 * nt, true);
+      const u32x4 bt = trn(bsm, N * 2, 4 * g4, 16 + 4 * g4, 16 * nt, true);
+#pragma unroll
+      for (int t = 0; t < 2; ++t) {
+        dBa[i][t] = mfma16b(ct, elop[t], dBa[i][t]);
+        dCa[i][t] = mfma16b(bt, eltop[t], dCa[i][t]);
+        f32x4 gx{}, hy{};
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          const u32x4 gsT = trn(gss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
+          const u32x4 hsT = trn(hss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
+          gx = mfma16b(gsT, rowx(xs, 16 * t + c16, kq), gx);
+          hy = mfma16b(hsT, rowx(ys, 16 * t + c16, kq), hy);
+        }
+        const float ws = tab[TW + 16 * t + c16], fl = tab[TF + 16 * t + c16];
+        dBa[i][t] += gx * ws;
+        dCa[i][t] += hy * fl;
+      }
+    }
+
+    // ---- the scalars of this head (wavefront 0) ----
+    if (wave == 0) {
+      // column sums (l >= s, and l > s with dt) and row sums (s < l, with dt) of E o Z o L
+#pragma unroll
+      for (int st = 0; st < 2; ++st) {
+        const int sx = 16 * st + c16;
+        const float ds = tab[TDT + sx];
+        float t1 = 0.f, ck = 0.f;
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int l = 16 * lt + 4 * g4 + r;
+            t1 += pv[lt][st][r];
+            if (l > sx) ck += pv[lt][st][r] * ds;
+            if (l == sx) sc[SDE + sx] = e[lt][st][r];
+          }
+        t1 += __shfl_xor(t1, 16, 64);
+        t1 += __shfl_xor(t1, 32, 64);
+        ck += __shfl_xor(ck, 16, 64);
+        ck += __shfl_xor(ck, 32, 64);
+        if (lane < 16) {
+          sc[ST1 + sx] = t1;
+          sc[SCK + sx] = ck;
+        }
+      }
+#pragma unroll
+      for (int lt = 0; lt < 2; ++lt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int l = 16 * lt + 4 * g4 + r;
+          float rk = 0.f;
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int sx = 16 * st + c16;
+            if (sx < l) rk += pv[lt][st][r] * tab[TDT + sx];
+          }
+#pragma unroll
+          for (int off = 8; off >= 1; off >>= 1) rk += __shfl_xor(rk, off, 64);
+          if (c16 == 0) sc[SRK + l] = rk;
+        }
+    }
+    __syncthreads();  // partials of every wavefront and wavefront 0's sums are in LDS
+    if (wave == 0) {
+      float q = 0.f, v = 0.f, gh = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        q += part[w * (2 * CQ + 4) + PQ + tl];
+        v += part[w * (2 * CQ + 4) + PV + tl];
+        gh += part[w * (2 * CQ + 4) + PGH];
+      }
+      v *= tab[TF + tl];
+      const float u = tab[TW + tl] * q;
+      const float uin = scan32b(u);
+      const float vin = scan32b(v);
+      const float rkv = sc[SRK + tl] - sc[SCK + tl];
+      const float rin = scan32b(rkv);
+      const float U = exp2b(alast * kLog2eB) * gh + (uin - u);
+      const float V = lane31(vin) - vin + v;
+      const float Rr = lane31(rin) - rin + rkv;
+      const float term1 = sc[ST1 + tl] + tab[TEL + tl] * q;
+      const float dd = term1 + Ah * (Rr + V + U);
+      const bool ok = lane < 32 && tl <= last;
+      if (ok) ddt[(t0 + tl) * H + h] = dd;
+      float da = ok ? tab[TDT + tl] * (Rr + V + U) : 0.f;
+      float dsum = ok ? sc[SDE + tl] : 0.f;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        da += __shfl_xor(da, off, 64);
+        dsum += __shfl_xor(dsum, off, 64);
+      }
+      if (lane == 0) {
+        atomicAdd(dA + h, da);
+        if (dD) atomicAdd(dD + h, dsum);
+      }
+    }
+  }
+
+  // ---- dB, dC of the chunk's rows: lane column s, rows n = 16 nt + 4 g4 + r ----
+#pragma unroll
+  for (int i = 0; i < NTW; ++i) {
+    const int nt = wave * NTW + i;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int sx = 16 * t + c16;
+      if (sx <= last) {
+        const int64_t off = (t0 + sx) * ldb + (int64_t)g * N + 16 * nt + 4 * g4;
+        *reinterpret_cast<f32x4 *>(dB + off) = dBa[i][t];
+        *reinterpret_cast<f32x4 *>(dC + off) = dCa[i][t];
+      }
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_f32(float *__restrict__ p, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0.f;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, const void *C,
+                              const float *dfinal, const int32_t *cu, int64_t L, int64_t T,
+                              int rows, int H, int N, int G, void *gsave, float *dinit,
+                              hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  const dim3 grid(xcd_grid(rows, H / 2));
+  const uint16_t *d = static_cast<const uint16_t *>(dy);
+  const uint16_t *c = static_cast<const uint16_t *>(C);
+  uint16_t *gs = static_cast<uint16_t *>(gsave);
+  if (N == 64)
+    hipLaunchKernelGGL(k_bwd_reverse<64>, grid, dim3(256), 0, stream, d, dt, A, c, dfinal, cu, L, T,
+                       rows, H, G, gs, dinit);
+  else if (N == 128)
+    hipLaunchKernelGGL(k_bwd_reverse<128>, grid, dim3(256), 0, stream, d, dt, A, c, dfinal, cu, L, T,
+                       rows, H, G, gs, dinit);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,
+                            const void *C, const float *D, const void *dy, const void *hsave,
+                            const void *gsave, const int32_t *cu, int64_t L, int64_t T, int rows,
+                            int64_t nchunks, int H, int N, int G, void *dx, float *ddt, float *dA,
+                            float *dB, float *dC, float *dD, hipStream_t stream) {
+  if (nchunks == 0) return hipSuccess;
+  const dim3 grid(static_cast<unsigned>(nchunks * G));
+  const uint16_t *xi = static_cast<const uint16_t *>(x);
+  const uint16_t *bi = static_cast<const uint16_t *>(B);
+  const uint16_t *ci = static_cast<const uint16_t *>(C);
+  const uint16_t *di = static_cast<const uint16_t *>(dy);
+  const uint16_t *hs = static_cast<const uint16_t *>(hsave);
+  const uint16_t *gs = static_cast<const uint16_t *>(gsave);
+  uint16_t *dxo = static_cast<uint16_t *>(dx);
+  if (N == 64)
+    hipLaunchKernelGGL(k_bwd_chunk<64>, grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, di, hs, gs,
+                       cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+  else if (N == 128)
+    hipLaunchKernelGGL(k_bwd_chunk<128>, grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, di, hs, gs,
+                       cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+  else
+    return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                     p, n);
+  return hipGetLastError();
+}
+
+}  // namespace ssd

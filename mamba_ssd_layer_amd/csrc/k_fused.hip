@@ -130,13 +130,14 @@ struct FusedCfg {
   static_assert(BLOCKS_PER_CU >= 1 && WAVES_PER_SIMD >= 2, "occupancy");
 };
 
-template <int N, int HPB, int R>
+template <int N, int HPB, int R, bool SAVE>
 __global__ __launch_bounds__((FusedCfg<N, HPB, R>::THREADS), (FusedCfg<N, HPB, R>::WAVES_PER_SIMD))
 void k_ssd_fused(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
     const float *__restrict__ h0, const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows,
-    int H, int G, uint16_t *__restrict__ y, float *__restrict__ hfin) {
+    int H, int G, uint16_t *__restrict__ y, float *__restrict__ hfin,
+    uint16_t *__restrict__ hsave) {
   using F = FusedCfg<N, HPB, R>;
   constexpr int P = F::P, CQ = F::CQ;
   constexpr int NT = N / 16;   // state tiles per p-tile (over n)
@@ -158,16 +159,7 @@ void k_ssd_fused(
   const int h = h0b + hh;
   const int g = h0b / (H / G);
   int64_t tb, len;
-  if (cu) {
-    tb = cu[s];
-    const int64_t te = cu[s + 1];
-    tb = tb < 0 ? 0 : (tb > T ? T : tb);
-    len = (te > T ? T : te) - tb;
-    if (len < 0) len = 0;
-  } else {
-    tb = (int64_t)s * L;
-    len = L;
-  }
+  seq_range(cu, s, L, T, tb, len);
   const int64_t sh = (int64_t)s * H + h;
   const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
   const float Ah = A[h];
@@ -188,6 +180,7 @@ void k_ssd_fused(
       hst[pt][j] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + prow + nrow(j)) : f32x4{};
   }
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
+  const int64_t cbase = SAVE ? chunk_base32(cu, s, L, T) : 0;
   // The registers hold S = h / 2^lam: the decay of a chunk goes into lam
   // (wave-uniform) instead of into 2 N/16 x 4 multiplies a lane; S is
   // rescaled only when lam drops below -32, or before a chunk whose own
@@ -279,12 +272,29 @@ void k_ssd_fused(
     // chunk k has landed once at most the ops this wavefront issued after its
     // loads are pending: loads of later chunks (prologue, then one chunk per
     // iteration) and the y stores of the iterations in between
-    {
+    if (SAVE) {
+      wait_vmcnt<0>();  // the state stores below are not counted
+    } else {
       int n = k < D ? (min(D, nck) - 1 - k) * LDC : 0;
       for (int j = k < D ? 0 : k - D + 1; j < k; ++j) n += (j >= 1 ? STC : 0) + (j + D < nck ? LDC : 0);
       wait_vmcnt_dyn(n);
     }
     __syncthreads();  // every wavefront's share of chunk k is in; chunk k-1 is done everywhere
+    if (SAVE) {  // the state at the chunk's start, h = S 2^lam, rounded to bf16
+      const float e = exp2_fast(lam);
+#pragma unroll
+      for (int pt = 0; pt < 2; ++pt) {
+        uint16_t *dst = hsave + ((cbase + k) * H + h) * (int64_t)(P * N) +
+                        (int64_t)(32 * ph + 16 * pt + c16) * N + 8 * g4;
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+          const f32x4 u = hst[pt][2 * q] * e, v = hst[pt][2 * q + 1] * e;
+          *reinterpret_cast<u32x4 *>(dst + 32 * q) =
+              u32x4{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
+                    pack_bf16x2(v.z, v.w)};
+        }
+      }
+    }
     const int slp = sl == 0 ? R - 1 : sl - 1;  // slot of chunk k-1, and of chunk k+D
     if (k >= 1) store_y(k - 1, slp);
     if (k + D < nck) issue(k + D, slp);
@@ -468,19 +478,20 @@ bool fused_supported(int H, int P, int N, int G) {
 }
 
 namespace {
-template <int N, int HPB, int R>
+template <int N, int HPB, int R, bool SAVE>
 void launch_fused_t(const uint16_t *x, const float *dt, const float *A, const uint16_t *B,
                     const uint16_t *C, const float *D, const float *h0, const int32_t *cu, int64_t L,
-                    int64_t T, int rows, int H, int G, uint16_t *y, float *hfin, hipStream_t stream) {
-  hipLaunchKernelGGL((k_ssd_fused<N, HPB, R>), dim3(xcd_grid(rows, H / HPB)),
+                    int64_t T, int rows, int H, int G, uint16_t *y, float *hfin, uint16_t *hsave,
+                    hipStream_t stream) {
+  hipLaunchKernelGGL((k_ssd_fused<N, HPB, R, SAVE>), dim3(xcd_grid(rows, H / HPB)),
                      dim3(FusedCfg<N, HPB, R>::THREADS), 0, stream, x, dt, A, B, C, D, h0, cu, L, T,
-                     rows, H, G, y, hfin);
+                     rows, H, G, y, hfin, hsave);
 }
 }  // namespace
 
 hipError_t launch_fused(const void *x, const float *dt, const float *A, const void *B, const void *C,
                         const float *D, const float *h0, const int32_t *cu, int64_t L, int64_t T,
-                        int rows, int H, int P, int N, int G, void *y, float *hfin,
+                        int rows, int H, int P, int N, int G, void *y, float *hfin, void *hsave,
                         hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   if (!fused_supported(H, P, N, G)) return hipErrorInvalidValue;
@@ -488,10 +499,14 @@ hipError_t launch_fused(const void *x, const float *dt, const float *A, const vo
   const uint16_t *bi = static_cast<const uint16_t *>(B);
   const uint16_t *ci = static_cast<const uint16_t *>(C);
   uint16_t *yo = static_cast<uint16_t *>(y);
-  if (N == 64)
-    launch_fused_t<64, 2, 3>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, stream);
-  else
-    launch_fused_t<128, 2, 3>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, stream);
+  uint16_t *hs = static_cast<uint16_t *>(hsave);
+  if (N == 64) {
+    if (hs) launch_fused_t<64, 2, 3, true>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, hs, stream);
+    else launch_fused_t<64, 2, 3, false>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, hs, stream);
+  } else {
+    if (hs) launch_fused_t<128, 2, 3, true>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, hs, stream);
+    else launch_fused_t<128, 2, 3, false>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, hs, stream);
+  }
   return hipGetLastError();
 }
 

@@ -384,20 +384,125 @@ ssd_status ssd_fused_fwd(const void *x, const float *dt, const float *A, const v
                          const void *C, const float *D, const float *init_state,
                          const int32_t *cu_seqlens, void *y, float *final_state,
                          const ssd_dims *dims, void *stream) {
-  Plan p;
-  ssd_status s = make_plan(dims, 64, &p);  // the chunk length only sizes the (unused) workspace
+  return ssd_fused_fwd_train(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, nullptr, 0,
+                             dims, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Plan of the one-pass forward and its backward: the chunked plan's checks,
+// then the one-pass shape limits.
+ssd_status make_fused_plan(const ssd_dims *dims, Plan *p) {
+  ssd_status s = make_plan(dims, 64, p);  // the chunk length only sizes the (unused) workspace
   if (s != SSD_OK) return s;
-  if (!p.bf16 || !ssd::fused_supported(p.geo.H, p.geo.P, p.geo.N, p.geo.G)) return SSD_ERR_UNSUPPORTED;
-  if (p.geo.nrows >= ((int64_t)1 << 24) / p.geo.H) return SSD_ERR_UNSUPPORTED;
+  if (!p->bf16 || !ssd::fused_supported(p->geo.H, p->geo.P, p->geo.N, p->geo.G))
+    return SSD_ERR_UNSUPPORTED;
+  if (p->geo.nrows >= ((int64_t)1 << 24) / p->geo.H) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+// 32-token chunks of the batch (packed: an upper bound, ceil(T/32) + nseq)
+int64_t chunks32(const Plan &p) {
+  const ssd::Geometry &g = p.geo;
+  return g.packed ? ceil_div(g.tokens, 32) + g.nrows : g.nrows * ceil_div(g.L, 32);
+}
+
+size_t chunk_states_bytes(const Plan &p) {
+  return align_up((size_t)chunks32(p) * p.geo.H * p.geo.P * p.geo.N * 2);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_fused_states_size(const ssd_dims *dims) {
+  Plan p;
+  if (make_fused_plan(dims, &p) != SSD_OK) return 0;
+  return chunk_states_bytes(p);
+}
+
+ssd_status ssd_fused_fwd_train(const void *x, const float *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *init_state,
+                               const int32_t *cu_seqlens, void *y, float *final_state,
+                               void *chunk_states, size_t states_bytes, const ssd_dims *dims,
+                               void *stream) {
+  Plan p;
+  ssd_status s = make_fused_plan(dims, &p);
+  if (s != SSD_OK) return s;
   if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
   if ((s = check_state_args(x, B, p)) != SSD_OK) return s;
   if ((s = check_pass_args(init_state, final_state, p)) != SSD_OK) return s;
   if ((s = check_scan_args(x, B, C, D, y, dt, p)) != SSD_OK) return s;
+  if (chunk_states) {
+    if (!aligned(chunk_states, 16)) return SSD_ERR_INVALID_ARG;
+    if (states_bytes < chunk_states_bytes(p)) return SSD_ERR_WORKSPACE;
+    const Sizes z = tensor_bytes(p);
+    const size_t hb = chunk_states_bytes(p);
+    if (overlaps(chunk_states, hb, x, z.x) || overlaps(chunk_states, hb, y, z.x) ||
+        overlaps(chunk_states, hb, B, z.bc) || overlaps(chunk_states, hb, C, z.bc) ||
+        overlaps(chunk_states, hb, dt, z.dt) || overlaps(chunk_states, hb, init_state, z.state) ||
+        overlaps(chunk_states, hb, final_state, z.state))
+      return SSD_ERR_INVALID_ARG;
+  }
   const ssd::Geometry &g = p.geo;
   return hip_status(ssd::launch_fused(x, dt, A, B, C, D, init_state,
                                       g.packed ? cu_seqlens : nullptr, g.L, g.tokens, (int)g.nrows,
-                                      g.H, g.P, g.N, g.G, y, final_state,
+                                      g.H, g.P, g.N, g.G, y, final_state, chunk_states,
                                       static_cast<hipStream_t>(stream)));
+}
+
+size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims) { return ssd_fused_states_size(dims); }
+
+ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const void *B,
+                         const void *C, const float *D, const int32_t *cu_seqlens,
+                         const void *chunk_states, size_t states_bytes, const void *dy,
+                         const float *dfinal, void *dx, float *ddt, float *dA, float *dB,
+                         float *dC, float *dD, float *dinit, const ssd_dims *dims, void *workspace,
+                         size_t workspace_bytes, void *stream) {
+  Plan p;
+  ssd_status s = make_fused_plan(dims, &p);
+  if (s != SSD_OK) return s;
+  if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
+  if ((s = check_scan_args(x, B, C, D, dy, dt, p)) != SSD_OK) return s;
+  if (!tok_ptr_ok(dx, p, 16) || !tok_ptr_ok(ddt, p, 4) || !tok_ptr_ok(dB, p, 16) ||
+      !tok_ptr_ok(dC, p, 16))
+    return SSD_ERR_INVALID_ARG;
+  if (!dA || !aligned(dA, 4) || (dD && !aligned(dD, 4))) return SSD_ERR_INVALID_ARG;
+  if ((dD != nullptr) != (D != nullptr)) return SSD_ERR_INVALID_ARG;
+  if ((dfinal && !aligned(dfinal, 16)) || (dinit && !aligned(dinit, 16))) return SSD_ERR_INVALID_ARG;
+  const size_t hb = chunk_states_bytes(p);
+  if (!chunk_states || !aligned(chunk_states, 16)) return SSD_ERR_INVALID_ARG;
+  if (states_bytes < hb) return SSD_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < hb) return SSD_ERR_WORKSPACE;
+  if (!aligned(workspace, 16)) return SSD_ERR_INVALID_ARG;
+  // outputs overlap no input and no other output
+  const Sizes z = tensor_bytes(p);
+  const ssd::Geometry &g = p.geo;
+  const size_t bdt = z.dt, bbc32 = (size_t)g.tokens * g.G * g.N * 4, bh = (size_t)g.H * 4;
+  const void *ins[] = {x, dt, A, B, C, D, chunk_states, dy, dfinal, workspace};
+  const size_t insz[] = {z.x, bdt, bh, z.bc, z.bc, bh, hb, z.x, z.state, hb};
+  const void *outs[] = {dx, ddt, dA, dB, dC, dD, dinit};
+  const size_t outsz[] = {z.x, bdt, bh, bbc32, bbc32, bh, z.state};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return SSD_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return SSD_ERR_INVALID_ARG;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int32_t *cu = g.packed ? cu_seqlens : nullptr;
+  hipError_t e = ssd::launch_fill_f32(dA, g.H, st);
+  if (e == hipSuccess && dD) e = ssd::launch_fill_f32(dD, g.H, st);
+  if (e == hipSuccess)
+    e = ssd::launch_bwd_reverse(dy, dt, A, C, dfinal, cu, g.L, g.tokens, (int)g.nrows, g.H, g.N,
+                                g.G, workspace, dinit, st);
+  if (e == hipSuccess)
+    e = ssd::launch_bwd_chunk(x, dt, A, B, C, D, dy, chunk_states, workspace, cu, g.L, g.tokens,
+                              (int)g.nrows, chunks32(p), g.H, g.N, g.G, dx, ddt, dA, dB, dC, dD,
+                              st);
+  return hip_status(e);
 }
 
 const char *ssd_status_string(ssd_status status) {

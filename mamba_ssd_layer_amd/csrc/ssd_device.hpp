@@ -185,4 +185,33 @@ __device__ __forceinline__ constexpr int chunk_swz(int row, int nc) {
 template <typename T>
 __device__ __forceinline__ T wave_bcast(T v, int src) { return __shfl(v, src, 64); }
 
+// Token range of sequence s: fixed rows of L tokens, or cu_seqlens clamped to
+// [0, T] (an inverted range is empty).
+__device__ __forceinline__ void seq_range(const int32_t *cu, int s, int64_t L, int64_t T,
+                                          int64_t &tb, int64_t &len) {
+  if (cu) {
+    tb = cu[s];
+    const int64_t te = cu[s + 1];
+    tb = tb < 0 ? 0 : (tb > T ? T : tb);
+    len = (te > T ? T : te) - tb;
+    if (len < 0) len = 0;
+  } else {
+    tb = (int64_t)s * L;
+    len = L;
+  }
+}
+
+// Index of sequence s's first 32-token chunk in the sequence-major list of
+// the batch's 32-token chunks (the layout of saved per-chunk states).
+__device__ inline int64_t chunk_base32(const int32_t *cu, int s, int64_t L, int64_t T) {
+  if (!cu) return (int64_t)s * ((L + 31) / 32);
+  int64_t acc = 0;
+  for (int i = 0; i < s; ++i) {
+    int64_t tb, len;
+    seq_range(cu, i, L, T, tb, len);
+    acc += (len + 31) / 32;
+  }
+  return acc;
+}
+
 }  // namespace ssd

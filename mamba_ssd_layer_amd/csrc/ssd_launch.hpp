@@ -62,8 +62,19 @@ hipError_t launch_gate_rmsnorm(const void *y, const void *z, const float *weight
 bool fused_supported(int H, int P, int N, int G);
 hipError_t launch_fused(const void *x, const float *dt, const float *A, const void *B, const void *C,
                         const float *D, const float *h0, const int32_t *cu, int64_t L, int64_t T,
-                        int rows, int H, int P, int N, int G, void *y, float *hfin,
+                        int rows, int H, int P, int N, int G, void *y, float *hfin, void *hsave,
                         hipStream_t stream);
+// backward of the one-pass forward (bf16, P == 64, N in {64, 128}, even heads per group)
+hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, const void *C,
+                              const float *dfinal, const int32_t *cu, int64_t L, int64_t T,
+                              int rows, int H, int N, int G, void *gsave, float *dinit,
+                              hipStream_t stream);
+hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,
+                            const void *C, const float *D, const void *dy, const void *hsave,
+                            const void *gsave, const int32_t *cu, int64_t L, int64_t T, int rows,
+                            int64_t nchunks, int H, int N, int G, void *dx, float *ddt, float *dA,
+                            float *dB, float *dC, float *dD, hipStream_t stream);
+hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t stream);
 
 // Compute units of the current device (cached per device).
 inline int device_cus() {

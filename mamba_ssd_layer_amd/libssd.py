@@ -60,6 +60,8 @@ class ssd_workspace_layout(ctypes.Structure):
 EXPORTS = ["ssd_workspace_size", "ssd_get_workspace_layout", "ssd_chunk_scan_fwd",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
            "ssd_step", "ssd_conv1d_silu", "ssd_gate_rmsnorm", "ssd_fused_fwd",
+           "ssd_fused_fwd_train", "ssd_fused_states_size", "ssd_fused_bwd_workspace_size",
+           "ssd_fused_bwd",
            "ssd_status_string", "ssd_version"]
 
 
@@ -93,6 +95,15 @@ def _load() -> ctypes.CDLL:
     lib.ssd_gate_rmsnorm.argtypes = [p, p, p, ctypes.c_float, p, i64, i64, i32, p]
     lib.ssd_fused_fwd.restype = i32
     lib.ssd_fused_fwd.argtypes = [p, p, p, p, p, p, p, p, p, p, dims_p, p]
+    lib.ssd_fused_fwd_train.restype = i32
+    lib.ssd_fused_fwd_train.argtypes = [p, p, p, p, p, p, p, p, p, p, p, sz, dims_p, p]
+    lib.ssd_fused_states_size.restype = sz
+    lib.ssd_fused_states_size.argtypes = [dims_p]
+    lib.ssd_fused_bwd_workspace_size.restype = sz
+    lib.ssd_fused_bwd_workspace_size.argtypes = [dims_p]
+    lib.ssd_fused_bwd.restype = i32
+    lib.ssd_fused_bwd.argtypes = [p, p, p, p, p, p, p, p, sz, p, p, p, p, p, p, p, p, p, dims_p,
+                                  p, sz, p]
     lib.ssd_status_string.restype = ctypes.c_char_p
     lib.ssd_status_string.argtypes = [i32]
     lib.ssd_version.restype = i32
@@ -201,6 +212,31 @@ def ssd_fused_fwd(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, dim
     _check(_lib.ssd_fused_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
                               _ptr(init_state), _ptr(cu_seqlens), _ptr(y), _ptr(final_state),
                               ctypes.byref(dims), _stream(stream)))
+
+
+def ssd_fused_states_size(dims) -> int:
+    return int(_lib.ssd_fused_states_size(ctypes.byref(dims)))
+
+
+def ssd_fused_bwd_workspace_size(dims) -> int:
+    return int(_lib.ssd_fused_bwd_workspace_size(ctypes.byref(dims)))
+
+
+def ssd_fused_fwd_train(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, chunk_states,
+                        states_bytes, dims, stream=None) -> None:
+    _check(_lib.ssd_fused_fwd_train(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                    _ptr(init_state), _ptr(cu_seqlens), _ptr(y),
+                                    _ptr(final_state), _ptr(chunk_states), int(states_bytes),
+                                    ctypes.byref(dims), _stream(stream)))
+
+
+def ssd_fused_bwd(x, dt, A, B, C, D, cu_seqlens, chunk_states, states_bytes, dy, dfinal, dx, ddt,
+                  dA, dB, dC, dD, dinit, dims, workspace, workspace_bytes, stream=None) -> None:
+    _check(_lib.ssd_fused_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                              _ptr(cu_seqlens), _ptr(chunk_states), int(states_bytes), _ptr(dy),
+                              _ptr(dfinal), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC),
+                              _ptr(dD), _ptr(dinit), ctypes.byref(dims), _ptr(workspace),
+                              int(workspace_bytes), _stream(stream)))
 
 
 def _raw_ptr(t: Optional[torch.Tensor], offset_elems: int = 0):

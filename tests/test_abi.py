@@ -337,3 +337,85 @@ def test_fused_pointers_and_overlaps():
     assert fused(d, init=base, fin=base + 256) == SSD_ERR_INVALID_ARG  # partial state overlap
     dp = make_dims(1, 1000, 4, 64, 64, 2, 3, SSD_BF16)
     assert fused(dp, cu=None) == SSD_ERR_INVALID_ARG                 # packed needs cu_seqlens
+
+
+# ------------------------------------------- ssd_fused_fwd_train, ssd_fused_bwd
+def test_fused_states_size():
+    # bf16 [nchunks][H][P][N], nchunks = batch * ceil(L / 32), rounded up to 256 bytes
+    d = good()  # 2 x 512 tokens, H 4, P 64, N 64
+    assert L.ssd_fused_states_size(ctypes.byref(d)) == 2 * 16 * 4 * 64 * 64 * 2
+    d = make_dims(3, 1000, 4, 64, 128, 2, 0, SSD_BF16)
+    assert L.ssd_fused_states_size(ctypes.byref(d)) == 3 * 32 * 4 * 64 * 128 * 2
+    dp = make_dims(1, 1000, 4, 64, 64, 2, 3, SSD_BF16)  # packed: ceil(T / 32) + nseq
+    assert L.ssd_fused_states_size(ctypes.byref(dp)) == (32 + 3) * 4 * 64 * 64 * 2
+    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(dp)) == (32 + 3) * 4 * 64 * 64 * 2
+    for mut in (dict(io_dtype=SSD_F32), dict(headdim=128), dict(ngroups=4)):
+        d = good()
+        for k, val in mut.items():
+            setattr(d, k, val)
+        assert L.ssd_fused_states_size(ctypes.byref(d)) == 0
+        assert L.ssd_fused_bwd_workspace_size(ctypes.byref(d)) == 0
+
+
+def fused_train(d, states=FAKE + (8 << 30), nbytes=None, **kw):
+    v = ctypes.c_void_p
+    args = dict(x=FAKE, dt=FAKE + (1 << 30), A=FAKE + (2 << 30), B=FAKE + (3 << 30),
+                C=FAKE + (4 << 30), D=None, init=None, cu=None, y=FAKE + (7 << 30),
+                fin=FAKE + (5 << 30))
+    args.update(kw)
+    if nbytes is None:
+        nbytes = L.ssd_fused_states_size(ctypes.byref(d))
+    return L.ssd_fused_fwd_train(*(None if args[k] is None else v(args[k])
+                                   for k in ("x", "dt", "A", "B", "C", "D", "init", "cu", "y",
+                                             "fin")),
+                                 None if states is None else v(states), ctypes.c_size_t(nbytes),
+                                 ctypes.byref(d), None)
+
+
+def test_fused_train_validation():
+    d = good()
+    need = L.ssd_fused_states_size(ctypes.byref(d))
+    assert fused_train(d, nbytes=need - 1) == SSD_ERR_WORKSPACE
+    assert fused_train(d, states=FAKE + (8 << 30) + 8) == SSD_ERR_INVALID_ARG  # alignment
+    assert fused_train(d, states=FAKE + (7 << 30)) == SSD_ERR_INVALID_ARG      # over y
+    assert fused_train(d, states=FAKE + 4096) == SSD_ERR_INVALID_ARG           # over x
+    assert fused_train(d, x=None) == SSD_ERR_INVALID_ARG
+    d.dstate = 32
+    assert fused_train(d) == SSD_ERR_UNSUPPORTED
+
+
+BWD_ARGS = ("x", "dt", "A", "B", "C", "D", "cu", "states", "dy", "dfinal", "dx", "ddt", "dA",
+            "dB", "dC", "dD", "dinit")
+
+
+def fused_bwd(d, sbytes=None, ws=FAKE + (20 << 30), wbytes=None, **kw):
+    v = ctypes.c_void_p
+    args = {k: FAKE + (i << 30) for i, k in enumerate(BWD_ARGS)}
+    args.update(D=None, dD=None, cu=None, dfinal=None, dinit=None)
+    args.update(kw)
+    need = L.ssd_fused_bwd_workspace_size(ctypes.byref(d))
+    sbytes = need if sbytes is None else sbytes
+    wbytes = need if wbytes is None else wbytes
+    ptrs = [None if args[k] is None else v(args[k]) for k in BWD_ARGS]
+    return L.ssd_fused_bwd(*ptrs[:8], ctypes.c_size_t(sbytes), *ptrs[8:], ctypes.byref(d),
+                           None if ws is None else v(ws), ctypes.c_size_t(wbytes), None)
+
+
+def test_fused_bwd_validation():
+    d = good()
+    need = L.ssd_fused_bwd_workspace_size(ctypes.byref(d))
+    for k in ("x", "dt", "A", "B", "C", "dy", "dx", "ddt", "dA", "dB", "dC", "states"):
+        assert fused_bwd(d, **{k: None}) == SSD_ERR_INVALID_ARG, k
+    assert fused_bwd(d, sbytes=need - 1) == SSD_ERR_WORKSPACE
+    assert fused_bwd(d, wbytes=need - 1) == SSD_ERR_WORKSPACE
+    assert fused_bwd(d, ws=None) == SSD_ERR_WORKSPACE
+    assert fused_bwd(d, dD=FAKE + (21 << 30)) == SSD_ERR_INVALID_ARG         # dD without D
+    assert fused_bwd(d, D=FAKE + (21 << 30)) == SSD_ERR_INVALID_ARG          # D without dD
+    assert fused_bwd(d, dx=FAKE + 64) == SSD_ERR_INVALID_ARG                 # dx over x
+    assert fused_bwd(d, dB=FAKE + (10 << 30)) == SSD_ERR_INVALID_ARG         # dB over dx
+    assert fused_bwd(d, dinit=FAKE + (20 << 30)) == SSD_ERR_INVALID_ARG      # over workspace
+    assert fused_bwd(d, dB=FAKE + (13 << 30) + 8) == SSD_ERR_INVALID_ARG     # alignment
+    dp = make_dims(1, 1000, 4, 64, 64, 2, 3, SSD_BF16)
+    assert fused_bwd(dp) == SSD_ERR_INVALID_ARG                              # packed needs cu
+    d.io_dtype = SSD_F32
+    assert fused_bwd(d) == SSD_ERR_UNSUPPORTED

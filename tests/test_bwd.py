@@ -1,0 +1,218 @@
+"""ssd_fused_bwd (the gradients of the one-pass forward) on the GPU against the
+fp64 oracle of the backward pass (oracle.recurrence_bwd, itself pinned to the
+adjoint identity and to finite differences of the forward oracle).
+
+Tolerance: each gradient's max |gpu - oracle| / max |oracle| <= 2e-2, the
+forward's bf16 bound.  The path rounds to bf16 where the forward does (the
+operands of every MFMA: dy and C, the decay-weighted products of a chunk) and
+in three more places, each a relative 2^-9: the saved chunk-start states, the
+saved state gradients and the dx output.  Each output is a sum of O(P N) such
+terms with independent rounding, so the normalised error stays near 1e-3;
+2e-2 leaves room for the cancellation in ddt's and dA's sums of signed terms.
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import mamba_ssd_layer_amd as ssd  # noqa: E402
+import oracle  # noqa: E402
+from gpu_helpers import DEV, rel, say, upload  # noqa: E402
+
+TOLB = 2e-2
+
+
+def fwd_bwd(w, t, dy, dfinal):
+    st = ssd.make_fused_states(t["x"], t["B"], t["cu"])
+    y, fin = ssd.fused_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"],
+                           chunk_states=st)
+    dyd = torch.from_numpy(dy).to(DEV).to(torch.bfloat16).view(t["x"].shape)
+    dfd = None if dfinal is None else torch.from_numpy(dfinal).to(DEV)
+    g = ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], st, dyd, dfd, t["cu"])
+    torch.cuda.synchronize()
+    return y, fin, st, g
+
+
+def host(g, w):
+    T, H, P, G, N = w.tokens, w.nheads, w.headdim, w.ngroups, w.dstate
+    out = {"dx": g["dx"].float().cpu().numpy().reshape(T, H, P),
+           "ddt": g["ddt"].cpu().numpy().reshape(T, H),
+           "dB": g["dB"].cpu().numpy().reshape(T, G, N),
+           "dC": g["dC"].cpu().numpy().reshape(T, G, N),
+           "dA": g["dA"].cpu().numpy()}
+    if g["dD"] is not None:
+        out["dD"] = g["dD"].cpu().numpy()
+    if g["dinit"] is not None:
+        out["dh0"] = g["dinit"].cpu().numpy()
+    return out
+
+
+def check_grads(w, g, ref, label, names=None, tol=TOLB):
+    got = host(g, w)
+    names = names or [k for k in ("dx", "ddt", "dB", "dC", "dA", "dD", "dh0") if k in got]
+    errs = {k: rel(got[k], ref[k]) for k in names}
+    say(f"  {label}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()) + f" (tol {tol:g})")
+    for k, v in errs.items():
+        assert v <= tol, f"{label}: {k} rel err {v:.3e} > {tol}"
+    return errs
+
+
+def full_case(w, seed, dfinal_std=1.0, label=""):
+    dy, dfinal = workloads.make_output_grads(w, seed, dfinal_std)
+    t = upload(w)
+    _, _, _, g = fwd_bwd(w, t, dy, dfinal)
+    ref = oracle.recurrence_bwd(w.x, w.dt, w.A, w.B, w.C, w.D, w.h0, w.seq_off, dy, dfinal)
+    return check_grads(w, g, ref, label or w.name)
+
+
+def test_small_full():
+    w = workloads.make_custom(2, 300, 4, 64, 64, 2, 256, "bf16", seed=2100, init_std=0.3)
+    full_case(w, 1, label="bwd small N64 G2")
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_ragged_tail(N):
+    # 1000 tokens a row: 31 full 32-token chunks and a tail of 8
+    w = workloads.make_custom(3, 1000, 4, 64, N, 2, 256, "bf16", seed=2200 + N, init_std=0.2)
+    full_case(w, 2, label=f"bwd ragged N{N}")
+
+
+@pytest.mark.parametrize("G", [1, 4])
+def test_groups(G):
+    # 8 heads: 8 heads share B, C (G 1) or 2 do (G 4); dB, dC sum over them
+    w = workloads.make_custom(2, 600, 8, 64, 128, G, 256, "bf16", seed=2300 + G, init_std=0.1)
+    full_case(w, 3, label=f"bwd G{G}")
+
+
+def test_varlen_edge_lengths():
+    lens = [1, 0, 32, 31, 33, 64, 0, 700, 3, 1024, 1]
+    w = workloads.make_custom(1, 0, 4, 64, 64, 2, 256, "bf16", seed=2400, lens=lens, init_std=0.3)
+    full_case(w, 4, label="bwd varlen edges")
+
+
+def test_no_D_no_init_no_dfinal():
+    w = workloads.make_custom(2, 500, 4, 64, 128, 1, 256, "bf16", seed=2500, with_D=False)
+    dy, _ = workloads.make_output_grads(w, 5, 0.0)
+    t = upload(w)
+    _, _, _, g = fwd_bwd(w, t, dy, None)
+    assert g["dD"] is None
+    ref = oracle.recurrence_bwd(w.x, w.dt, w.A, w.B, w.C, None, None, w.seq_off, dy, None)
+    check_grads(w, g, ref, "bwd no D / h0 / dfinal")
+
+
+@pytest.mark.parametrize("dt_shift", [-1.0, 0.5])
+def test_fast_decay(dt_shift):
+    w = workloads.make_custom(2, 700, 4, 64, 128, 2, 256, "bf16", seed=2600, init_std=0.5,
+                              dt_shift=dt_shift)
+    full_case(w, 6, label=f"bwd fast decay {dt_shift}")
+
+
+@pytest.mark.parametrize("kind", ["A_zero", "dt_small"])
+def test_long_memory(kind):
+    kw = {"A_zero": dict(a_zero=True), "dt_small": dict(dt_const=1e-3)}[kind]
+    w = workloads.make_custom(2, 900, 4, 64, 64, 1, 256, "bf16", seed=2700, init_std=0.5, **kw)
+    full_case(w, 7, label=f"bwd {kind}")
+
+
+def test_saved_chunk_states_are_prefix_final_states():
+    # the state entering 32-token chunk k of a row is the oracle's final state
+    # of the row's first 32 k tokens (from the same initial state)
+    w = workloads.make_custom(2, 200, 4, 64, 64, 2, 256, "bf16", seed=2800, init_std=0.3)
+    t = upload(w)
+    st = ssd.make_fused_states(t["x"], t["B"], t["cu"])
+    ssd.fused_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"],
+                  chunk_states=st)
+    torch.cuda.synchronize()
+    H, P, N, L = w.nheads, w.headdim, w.dstate, w.seqlen
+    nck = (L + 31) // 32
+    hs = st.view(torch.bfloat16)[: w.batch * nck * H * P * N].float().cpu().numpy()
+    hs = hs.reshape(w.batch, nck, H, P, N)
+    worst = 0.0
+    for b in range(w.batch):
+        sl = slice(b * L, (b + 1) * L)
+        for k in range(nck):
+            n = 32 * k
+            if n == 0:
+                ref = w.h0[b].astype(np.float64)
+            else:
+                _, f = oracle.recurrence(w.x[sl][:n], w.dt[sl][:n], w.A, w.B[sl][:n],
+                                         w.C[sl][:n], w.D, w.h0[b:b + 1], np.array([0, n]))
+                ref = f[0]
+            worst = max(worst, rel(hs[b, k], ref))
+    say(f"  saved chunk states: rel err {worst:.3e}")
+    assert worst <= 1e-2
+
+
+def test_train_forward_matches_plain_forward():
+    # saving the states changes nothing in y or the final state, bit for bit
+    w = workloads.make_custom(2, 777, 4, 64, 128, 2, 256, "bf16", seed=2900, init_std=0.2)
+    t = upload(w)
+    y1, f1 = ssd.fused_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"])
+    st = ssd.make_fused_states(t["x"], t["B"], t["cu"])
+    y2, f2 = ssd.fused_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"],
+                           chunk_states=st)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+def test_large_sampled():
+    # the headline shape, 8 x 4096 tokens, 80 heads, P 64, N 128, G 1: dx,
+    # ddt and dinit on sampled (sequence, head) pairs; dB and dC of one whole
+    # sequence (all 80 heads of its group)
+    w = workloads.make_workload("large_bf16")
+    dy, dfinal = workloads.make_output_grads(w, 8)
+    t = upload(w)
+    _, _, _, g = fwd_bwd(w, t, dy, dfinal)
+    got = host(g, w)
+    r = np.random.default_rng(0)
+    pairs = sorted({(0, 0), (7, 79), (3, 40)} | {(int(r.integers(8)), int(r.integers(80)))
+                                                 for _ in range(5)})
+    ref = oracle.recurrence_bwd(w.x, w.dt, w.A, w.B, w.C, w.D, w.h0, w.seq_off, dy, dfinal,
+                                pairs=pairs)
+    so = w.seq_off
+    num = {k: 0.0 for k in ("dx", "ddt", "dh0")}
+    den = dict(num)
+    for k, (s, h) in enumerate(pairs):
+        a, b = so[s], so[s + 1]
+        for name, gv, rv in (("dx", got["dx"][a:b, h], ref["dx"][a:b, h]),
+                             ("ddt", got["ddt"][a:b, h], ref["ddt"][a:b, h]),
+                             ("dh0", got["dh0"][s, h], ref["dh0"][s, h])):
+            num[name] = max(num[name], float(np.max(np.abs(gv - rv))))
+            den[name] = max(den[name], float(np.max(np.abs(rv))))
+    errs = {k: num[k] / den[k] for k in num}
+    # one sequence, every head: its rows of dB and dC are complete
+    s = 5
+    a, b = so[s], so[s + 1]
+    ref1 = oracle.recurrence_bwd(w.x, w.dt, w.A, w.B, w.C, w.D, w.h0, w.seq_off, dy, dfinal,
+                                 pairs=[(s, h) for h in range(w.nheads)])
+    errs["dB"] = rel(got["dB"][a:b], ref1["dB"][a:b])
+    errs["dC"] = rel(got["dC"][a:b], ref1["dC"][a:b])
+    say("  bwd large sampled: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOLB, f"{k} rel err {v:.3e}"
+
+
+def test_unsupported_and_invalid():
+    w = workloads.make_custom(1, 64, 4, 32, 64, 1, 256, "bf16", seed=3000)
+    t = upload(w)
+    with pytest.raises(ssd.SSDUnsupported):
+        ssd.make_fused_states(t["x"], t["B"])
+    w = workloads.make_custom(1, 64, 4, 64, 64, 1, 256, "bf16", seed=3001)
+    t = upload(w)
+    st = ssd.make_fused_states(t["x"], t["B"])
+    dy = torch.zeros_like(t["x"])
+    with pytest.raises(ssd.SSDWorkspaceError):  # saved states too small
+        ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], st[:16], dy)
+    with pytest.raises(ssd.SSDInvalidArgument):  # dD without D is refused
+        ssd.libssd.ssd_fused_bwd(
+            t["x"], t["dt"], t["A"], t["B"], t["C"], None, None, st, st.numel(), dy, None,
+            torch.empty_like(dy), torch.empty_like(t["dt"]), torch.empty(4, device=DEV),
+            torch.empty(t["B"].shape, device=DEV), torch.empty(t["C"].shape, device=DEV),
+            torch.empty(4, device=DEV), None, ssd.dims_for(t["x"], t["B"], None),
+            torch.empty_like(st), st.numel())

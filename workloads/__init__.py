@@ -35,7 +35,7 @@ from typing import Optional
 import numpy as np
 
 __all__ = [
-    "Workload", "WORKLOADS", "make_workload", "make_custom", "bf16_round_",
+    "Workload", "WORKLOADS", "make_workload", "make_custom", "make_output_grads", "bf16_round_",
     "bf16_bits", "describe",
 ]
 
@@ -211,6 +211,22 @@ def make_custom(batch: int, seqlen: int, nheads: int, headdim: int, dstate: int,
                     seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G, nseq=nseq,
                     x=x, dt=dt, A=A, B=Bm, C=Cm, D=D, h0=h0, seq_off=seq_off,
                     cu_seqlens=cu)
+
+
+def make_output_grads(w: Workload, seed: int, dfinal_std: float = 1.0):
+    """Seeded upstream gradients for a backward pass over w: dy [T, H, P] ~
+    N(0, 1) (bf16-exact for bf16 workloads) and dfinal [rows, H, P, N] ~
+    N(0, dfinal_std^2) float32 (None when dfinal_std is 0).  Draw order: dy ->
+    dfinal."""
+    rng = np.random.default_rng(seed)
+    dy = _normal32(rng, (w.tokens, w.nheads, w.headdim))
+    if w.dtype == "bf16":
+        bf16_round_(dy)
+    dfinal = None
+    if dfinal_std > 0.0:
+        dfinal = (_normal32(rng, (w.nsequences, w.nheads, w.headdim, w.dstate)) *
+                  np.float32(dfinal_std)).astype(np.float32)
+    return dy, dfinal
 
 
 def make_workload(name: str) -> Workload:
