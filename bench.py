@@ -228,6 +228,76 @@ def block_neighbours(torch, ssd, dev, w, steps: int, warmup: int):
     return res
 
 
+def backward_bytes(w):
+    """Compulsory HBM bytes of the two backward kernels (bf16 io, Q = 32 chunks,
+    c = total 32-token chunks, S sequences; state tiles s P N bytes per chunk
+    and head):
+      k_bwd_reverse  dy, C, dt in; the state gradient entering every chunk out;
+                     dfinal in and dinit out per sequence:
+                     s T H P + s T G N + 4 T H + s c H P N + 8 S H P N
+      k_bwd_chunk    x, dy, B, C, dt, saved states and state gradients in;
+                     dx, ddt, dB, dC (float) out:
+                     3 s T H P + 2 s T G N + 8 T H + 8 T G N + 2 s c H P N"""
+    T, H, P, N, G = w.tokens, w.nheads, w.headdim, w.dstate, w.ngroups
+    S = w.nsequences
+    lens = [int(w.seq_off[i + 1] - w.seq_off[i]) for i in range(S)]
+    c = sum(-(-L // FUSED_CHUNK) for L in lens)
+    s = 2
+    rev = s * T * H * P + s * T * G * N + 4 * T * H + s * c * H * P * N + 8 * S * H * P * N
+    chk = 3 * s * T * H * P + 2 * s * T * G * N + 8 * T * H + 8 * T * G * N + 2 * s * c * H * P * N
+    return rev, chk
+
+
+def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
+    """The one-pass forward that saves its chunk states, then the backward
+    (ssd_fused_bwd) for seeded upstream gradients dy, dfinal; each timed with
+    HIP events on the launch stream."""
+    dev = t["x"].device
+    dy, dfinal = workloads.make_output_grads(w, 6100)
+    dyd = torch.from_numpy(dy).to(dev).to(torch.bfloat16).view(t["x"].shape)
+    dfd = torch.from_numpy(dfinal).to(dev)
+    states = ssd.make_fused_states(t["x"], t["B"], t["cu"])
+    ws = torch.empty_like(states)
+    y = torch.empty_like(t["x"])
+    fin = torch.empty_like(dfd)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        ssd.fused_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"], y=y,
+                      final_state=fin, chunk_states=states)
+
+    def bwd():
+        ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], states, dyd, dfd, t["cu"],
+                      workspace=ws)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    fus = timed(fwd)
+    bus = timed(bwd)
+    rev, chk = backward_bytes(w)
+    T = w.tokens
+    res = {"fwd_train_us": round(fus, 2), "bwd_us": round(bus, 2),
+           "tokens_per_s": round(T / ((fus + bus) * 1e-6), 1),
+           "bwd_tokens_per_s": round(T / (bus * 1e-6), 1),
+           "bwd_bytes": {"k_bwd_reverse": rev, "k_bwd_chunk": chk},
+           "bwd_GBs": round((rev + chk) / (bus * 1e-6) / 1e9, 1),
+           "bwd_hbm_frac": round((rev + chk) / (bus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
+    log(f"bench: training step: forward saving states {fus:.1f} us, backward {bus:.1f} us, "
+        f"{res['tokens_per_s'] / 1e6:.1f} M tokens/s")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,6 +308,8 @@ def main() -> int:
     ap.add_argument("--no-stage-timing", action="store_true")
     ap.add_argument("--no-decode", action="store_true",
                     help="skip the single-token decode (ssd_step) measurement")
+    ap.add_argument("--no-train", action="store_true",
+                    help="skip the forward-with-saved-states + backward timing")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the conv1d+SiLU and gate+RMS-norm measurements")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -416,6 +488,12 @@ def main() -> int:
     if not args.no_decode:
         decode = decode_step(torch, ssd, workloads, dev, args.steps, args.warmup)
 
+    train = None
+    if fused is not None and not args.no_train:
+        train = training_step(torch, ssd, workloads, w,
+                              {"x": x, "dt": dt, "A": A, "B": Bm, "C": Cm, "D": D, "h0": h0,
+                               "cu": cu}, args.steps, args.warmup)
+
     block = None
     if not args.no_block:
         block = block_neighbours(torch, ssd, dev, w, args.steps, args.warmup)
@@ -436,6 +514,7 @@ def main() -> int:
         "roofline": roofline, "cpu_baseline": cpu,
         "forwards": {"ssd_chunk_scan_fwd": chunked, "ssd_fused_fwd": fused},
         "kernels": kernels, "decode_step": decode, "block_neighbours": block,
+        "training_step": train,
     }
     print(json.dumps(out), flush=True)
     return 0

@@ -62,6 +62,14 @@ __device__ __forceinline__ float scan32b(float a) {
   a += dppb<0x142, 0xA>(a);
   return a;
 }
+// sum over the 16 lanes of each row of the wavefront (every lane gets it)
+__device__ __forceinline__ float rowsum16(float v) {
+  v += dppb<0xB1, 0xF>(v);   // quad_perm [1, 0, 3, 2]
+  v += dppb<0x4E, 0xF>(v);   // quad_perm [2, 3, 0, 1]
+  v += dppb<0x141, 0xF>(v);  // row_half_mirror
+  v += dppb<0x140, 0xF>(v);  // row_mirror
+  return v;
+}
 __device__ __forceinline__ float lane31(float v) {
   return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 31));
 }
@@ -95,6 +103,8 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
   constexpr int AD = R * SLOT, ADW = 2 * CQ * 4;
   constexpr int BCI = BT / 1024 / 4;  // 1 KB pieces of C per wavefront
   static_assert(BCI * 4 * 1024 == BT, "C split over 4 wavefronts");
+  constexpr int LDR = 2 + BCI + 1;  // vector-memory ops a wavefront issues per chunk load
+  constexpr int SV = 2 * KQ;        // state-gradient stores a wavefront issues per chunk
   __shared__ __align__(16) unsigned char smem[AD + 4 * ADW];
 
   int s, hb;
@@ -150,7 +160,10 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
 #pragma unroll 1
   for (int i = 0; i < nck; ++i) {
     const int k = nck - 1 - i;
-    wait_vmcnt<0>();
+    // chunk k's loads have landed once at most the later ops are pending
+    // (completion in issue order): the state-gradient stores of iterations
+    // i-2 and i-1 (SV each) and the loads of chunk k-1 (LDR)
+    wait_vmcnt_dyn((i >= 2 ? SV : 0) + (i + 1 < nck ? LDR : 0) + (i >= 1 ? SV : 0));
     __syncthreads();
     const int slp = sl == 0 ? 2 : sl - 1;
     if (k - 2 >= 0) issue(k - 2, slp);
@@ -238,7 +251,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
 // lane (c16 = s, g4) rows l = 16 lt + 4 g4 + r; its pair (lt = 0, 1) packs to a
 // B-operand with K = l in the order {4 g4 + 0..3, 16 + 4 g4 + 0..3}, matched by
 // transposing reads of token rows in the same order for the A-operand.
-template <int N>
+template <int N, int R>
 struct BwdCfg {
   static constexpr int P = 64, CQ = 32, NCB = N / 8;
   static constexpr int XT = CQ * P * 2;      // x or dy of a head: 32 rows x 128 B
@@ -246,21 +259,28 @@ struct BwdCfg {
   static constexpr int BT = CQ * N * 2;      // B or C of the chunk
   static constexpr int OX = 0, OY = XT, OH = 2 * XT, OG = OH + ST, ODT = OG + ST;
   static constexpr int HSLOT = ODT + 256;
-  static constexpr int OB = 2 * HSLOT, OCC = OB + BT;
-  static constexpr int OTAB = OCC + BT;       // per wavefront: 6 tables of 32 floats
+  static constexpr int OB = R * HSLOT, OCC = OB + BT;   // R ring slots of a head's tiles
+  // per-head scratch, two buffers (head parity): the per-wavefront tables
+  // (6 x 32 floats), the per-wavefront partials v[32], q[32], gh, and the
+  // per-token sums below
+  static constexpr int OTAB = OCC + BT;
   static constexpr int TABW = 6 * CQ * 4;
-  static constexpr int OPART = OTAB + 4 * TABW;  // per wavefront: v[32], q[32], gh
+  static constexpr int OPART = OTAB + 2 * 4 * TABW;
   static constexpr int PARTW = (2 * CQ + 4) * 4;
-  static constexpr int OSC = OPART + 4 * PARTW;  // term1a[32], rowK[32], colK[32], diagE[32]
-  static constexpr int TOTAL = OSC + 4 * CQ * 4;
+  // column partials [4][32] of E o Z o L (all l >= s, and l > s times dt_s),
+  // row sums [32] (s < l, times dt_s), diagonal of E [32]
+  static constexpr int OSC = OPART + 2 * 4 * PARTW;
+  static constexpr int SCW = (8 * CQ + 2 * CQ) * 4;
+  static constexpr int TOTAL = OSC + 2 * SCW;
   static constexpr int PIECES = (2 * XT + 2 * ST) / 1024;  // 1 KB pieces of a head's tiles
   static constexpr int BLOCKS = (160 * 1024) / TOTAL;
   static_assert(PIECES % 4 == 0, "pieces split over 4 wavefronts");
+  static constexpr int LD = PIECES / 4;   // vector-memory ops a wavefront issues per head (+1: dt)
   static_assert(BLOCKS >= 1, "LDS");
 };
 
-template <int N>
-__global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
+template <int N, int R>
+__global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
     const uint16_t *__restrict__ dy, const uint16_t *__restrict__ hsave,
@@ -268,7 +288,7 @@ __global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
     int rows, int64_t nchunks, int H, int G, uint16_t *__restrict__ dx,
     float *__restrict__ ddt, float *__restrict__ dA, float *__restrict__ dB,
     float *__restrict__ dC, float *__restrict__ dD) {
-  using F = BwdCfg<N>;
+  using F = BwdCfg<N, R>;
   constexpr int P = F::P, CQ = F::CQ, NCB = F::NCB;
   constexpr int KQ = N / 32;       // K steps over n
   constexpr int NTW = N / 16 / 4;  // n-tiles of dB / dC a wavefront owns
@@ -314,12 +334,13 @@ __global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
   const uint32_t lbase = lds_off(smem);
   const unsigned char *bsm = smem + F::OB;
   const unsigned char *csm = smem + F::OCC;
-  float *tab = reinterpret_cast<float *>(smem + F::OTAB + wave * F::TABW);
-  float *part = reinterpret_cast<float *>(smem + F::OPART);
-  float *sc = reinterpret_cast<float *>(smem + F::OSC);
+  // buffer b of the per-head scratch
+  auto tab_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OTAB + (b * 4 + wave) * F::TABW); };
+  auto part_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OPART + b * 4 * F::PARTW); };
+  auto sc_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OSC + b * F::SCW); };
   enum { TA2 = 0, TF = 32, TW = 64, TDT = 96, TEL = 128 };           // table rows
   enum { PV = 0, PQ = 32, PGH = 64 };                                // partials, per wavefront
-  enum { ST1 = 0, SRK = 32, SCK = 64, SDE = 96 };                    // scalars of wavefront 0
+  enum { SC1 = 0, SCK = 128, SRK = 256, SDE = 288 };                 // per-token sums
 
   // ---- operand reads ----
   // 16 bytes of a token row of x / dy (8 chunks): p = 32 kq + 8 g4 + 0..7
@@ -374,8 +395,16 @@ __global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
                 lbase + (tile ? F::OCC : F::OB) + pi * 1024);
     }
   }
-  issue_head(0, 0);
-  wait_vmcnt<0>();
+  // heads 0 .. R-2 ahead; head j + R - 1 is issued at the start of head j
+  const int LDW = F::LD + (wave == 0 ? 1 : 0);
+  // stores and atomics a wavefront issues in iteration m: dx of head m (2);
+  // wavefront 0 also ddt, dA, dD of head m - 1
+  auto stw = [&](int m) { return 2 + (wave == 0 && m >= 1 ? 2 + (dD ? 1 : 0) : 0); };
+  const bool full = last == CQ - 1;
+#pragma unroll
+  for (int jj = 0; jj < R - 1; ++jj)
+    if (jj < hpg) issue_head(jj, jj);
+  wait_vmcnt_dyn(min(R - 1, hpg) * LDW);  // B and C are in (the head loads issued after them may not be)
   __syncthreads();
   // Z = C B^T in E-layout tiles [lt][st]
   f32x4 z[2][2];
@@ -389,6 +418,46 @@ __global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
       z[lt][st] = acc;
     }
 
+  // ---- per-token scalars of head jj (its partials complete): every
+  // wavefront computes them, wavefront 0 writes ddt and adds dA, dD ----
+  auto finish = [&](int jj, float Ah, float alast) {
+    const int h = g * hpg + jj;
+    const float *tab = tab_of(jj & 1);
+    const float *part = part_of(jj & 1);
+    const float *sc = sc_of(jj & 1);
+    float q = 0.f, v = 0.f, gh = 0.f, t1 = 0.f, ck = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      q += part[w * (2 * CQ + 4) + PQ + tl];
+      v += part[w * (2 * CQ + 4) + PV + tl];
+      gh += part[w * (2 * CQ + 4) + PGH];
+      t1 += sc[SC1 + 32 * w + tl];
+      ck += sc[SCK + 32 * w + tl];
+    }
+    v *= tab[TF + tl];
+    const float u = tab[TW + tl] * q;
+    const float uin = scan32b(u);
+    const float vin = scan32b(v);
+    const float rkv = sc[SRK + tl] - ck;
+    const float rin = scan32b(rkv);
+    const float U = exp2b(alast * kLog2eB) * gh + (uin - u);
+    const float V = lane31(vin) - vin + v;
+    const float Rr = lane31(rin) - rin + rkv;
+    const float term1 = t1 + tab[TEL + tl] * q;
+    const float dd = term1 + Ah * (Rr + V + U);
+    const bool ok = lane < 32 && tl <= last;
+    const float da = lane31(scan32b(ok ? tab[TDT + tl] * (Rr + V + U) : 0.f));
+    const float dsum = lane31(scan32b(ok ? sc[SDE + tl] : 0.f));
+    if (wave == 0) {
+      if (ok) ddt[(t0 + tl) * H + h] = dd;
+      if (lane == 0) {
+        atomicAdd(dA + h, da);
+        if (dD) atomicAdd(dD + h, dsum);
+      }
+    }
+  };
+  float pAh = 0.f, palast = 0.f;  // of the previous head
+
   f32x4 dBa[NTW][2], dCa[NTW][2];
 #pragma unroll
   for (int i = 0; i < NTW; ++i)
@@ -400,13 +469,33 @@ __global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
 
 #pragma unroll 1
   for (int j = 0; j < hpg; ++j) {
-    const int sl = j & 1;
+    const int sl = j % R;
     const int h = g * hpg + j;
-    if (j > 0) {
-      wait_vmcnt<0>();
-      __syncthreads();  // head j is in everywhere; head j-1 is done everywhere
+    {
+      // Head j's loads have landed once at most the ops this wavefront issued
+      // after them are pending (completion in issue order): the later
+      // prologue loads, then per head m < j the loads of head m + R - 1 and
+      // m's stores.  A partial chunk may skip stores: there wait for all.
+      int n = 0;
+      if (full) {
+        const int m0 = j - (R - 1);
+        if (m0 < 0) {
+          n = (min(R - 2, hpg - 1) - j) * LDW;
+          for (int m = 0; m < j; ++m) n += (m + R - 1 < hpg ? LDW : 0) + stw(m);
+        } else {
+          n = stw(m0);
+          for (int m = m0 + 1; m < j; ++m) n += (m + R - 1 < hpg ? LDW : 0) + stw(m);
+        }
+      }
+      wait_vmcnt_dyn(n);
+      __syncthreads();  // head j is in everywhere; head j-1 (and its partials) is done everywhere
     }
-    if (j + 1 < hpg) issue_head(j + 1, sl ^ 1);
+    if (j + R - 1 < hpg) issue_head(j + R - 1, (j + R - 1) % R);
+    if (j > 0) finish(j - 1, pAh, palast);
+    const int pb = j & 1;
+    float *tab = tab_of(pb);
+    float *part = part_of(pb);
+    float *sc = sc_of(pb);
     unsigned char *hsl = smem + sl * F::HSLOT;
     const unsigned char *xs = hsl + F::OX;
     unsigned char *ys = hsl + F::OY;
@@ -584,9 +673,8 @@ __global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
       }
     }
 
-    // ---- the scalars of this head (wavefront 0) ----
-    if (wave == 0) {
-      // column sums (l >= s, and l > s with dt) and row sums (s < l, with dt) of E o Z o L
+    // ---- per-token sums of E o Z o L, one kind per wavefront ----
+    if (wave == 0) {  // column partials over this lane group's rows l (all l >= s; l > s times dt_s)
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
         const int sx = 16 * st + c16;
@@ -596,20 +684,13 @@ __global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
         for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const int l = 16 * lt + 4 * g4 + r;
             t1 += pv[lt][st][r];
-            if (l > sx) ck += pv[lt][st][r] * ds;
-            if (l == sx) sc[SDE + sx] = e[lt][st][r];
+            if (16 * lt + 4 * g4 + r > sx) ck += pv[lt][st][r] * ds;
           }
-        t1 += __shfl_xor(t1, 16, 64);
-        t1 += __shfl_xor(t1, 32, 64);
-        ck += __shfl_xor(ck, 16, 64);
-        ck += __shfl_xor(ck, 32, 64);
-        if (lane < 16) {
-          sc[ST1 + sx] = t1;
-          sc[SCK + sx] = ck;
-        }
+        sc[SC1 + 32 * g4 + sx] = t1;
+        sc[SCK + 32 * g4 + sx] = ck;
       }
+    } else if (wave == 1) {  // row sums over s < l, times dt_s
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
@@ -621,46 +702,24 @@ __global__ __launch_bounds__(256, BwdCfg<N>::BLOCKS) void k_bwd_chunk(
             const int sx = 16 * st + c16;
             if (sx < l) rk += pv[lt][st][r] * tab[TDT + sx];
           }
-#pragma unroll
-          for (int off = 8; off >= 1; off >>= 1) rk += __shfl_xor(rk, off, 64);
+          rk = rowsum16(rk);
           if (c16 == 0) sc[SRK + l] = rk;
         }
-    }
-    __syncthreads();  // partials of every wavefront and wavefront 0's sums are in LDS
-    if (wave == 0) {
-      float q = 0.f, v = 0.f, gh = 0.f;
+    } else if (wave == 2) {  // the diagonal E_ss (for dD)
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        q += part[w * (2 * CQ + 4) + PQ + tl];
-        v += part[w * (2 * CQ + 4) + PV + tl];
-        gh += part[w * (2 * CQ + 4) + PGH];
-      }
-      v *= tab[TF + tl];
-      const float u = tab[TW + tl] * q;
-      const float uin = scan32b(u);
-      const float vin = scan32b(v);
-      const float rkv = sc[SRK + tl] - sc[SCK + tl];
-      const float rin = scan32b(rkv);
-      const float U = exp2b(alast * kLog2eB) * gh + (uin - u);
-      const float V = lane31(vin) - vin + v;
-      const float Rr = lane31(rin) - rin + rkv;
-      const float term1 = sc[ST1 + tl] + tab[TEL + tl] * q;
-      const float dd = term1 + Ah * (Rr + V + U);
-      const bool ok = lane < 32 && tl <= last;
-      if (ok) ddt[(t0 + tl) * H + h] = dd;
-      float da = ok ? tab[TDT + tl] * (Rr + V + U) : 0.f;
-      float dsum = ok ? sc[SDE + tl] : 0.f;
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        da += __shfl_xor(da, off, 64);
-        dsum += __shfl_xor(dsum, off, 64);
-      }
-      if (lane == 0) {
-        atomicAdd(dA + h, da);
-        if (dD) atomicAdd(dD + h, dsum);
-      }
+      for (int st = 0; st < 2; ++st)
+        if ((c16 >> 2) == g4) {
+          const f32x4 ev = e[st][st];
+          const int r = c16 & 3;
+          sc[SDE + 16 * st + c16] = r == 0 ? ev.x : r == 1 ? ev.y : r == 2 ? ev.z : ev.w;
+        }
     }
+    pAh = Ah;
+    palast = alast;
   }
+
+  __syncthreads();  // the last head's partials are in everywhere
+  finish(hpg - 1, pAh, palast);
 
   // ---- dB, dC of the chunk's rows: lane column s, rows n = 16 nt + 4 g4 + r ----
 #pragma unroll
@@ -719,12 +778,13 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
   const uint16_t *hs = static_cast<const uint16_t *>(hsave);
   const uint16_t *gs = static_cast<const uint16_t *>(gsave);
   uint16_t *dxo = static_cast<uint16_t *>(dx);
+  // N 64: two slots, two blocks a CU; N 128: three slots (two heads in flight), one block
   if (N == 64)
-    hipLaunchKernelGGL(k_bwd_chunk<64>, grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, di, hs, gs,
-                       cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+    hipLaunchKernelGGL((k_bwd_chunk<64, 2>), grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, di, hs,
+                       gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else if (N == 128)
-    hipLaunchKernelGGL(k_bwd_chunk<128>, grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, di, hs, gs,
-                       cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+    hipLaunchKernelGGL((k_bwd_chunk<128, 3>), grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, di, hs,
+                       gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

@@ -94,19 +94,6 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// s_waitcnt vmcnt(n) for a wave-uniform n in [0, 31]
-__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
-  switch (n) {
-#define SSD_W(i) case i: wait_vmcnt<i>(); break;
-    SSD_W(0) SSD_W(1) SSD_W(2) SSD_W(3) SSD_W(4) SSD_W(5) SSD_W(6) SSD_W(7)
-    SSD_W(8) SSD_W(9) SSD_W(10) SSD_W(11) SSD_W(12) SSD_W(13) SSD_W(14) SSD_W(15)
-    SSD_W(16) SSD_W(17) SSD_W(18) SSD_W(19) SSD_W(20) SSD_W(21) SSD_W(22) SSD_W(23)
-    SSD_W(24) SSD_W(25) SSD_W(26) SSD_W(27) SSD_W(28) SSD_W(29) SSD_W(30)
-#undef SSD_W
-    default: wait_vmcnt<0>(); break;
-  }
-}
-
 // Geometry of one kernel instance: N state size, HPB heads per block, R ring slots.
 template <int N, int HPB, int R>
 struct FusedCfg {
@@ -126,7 +113,8 @@ struct FusedCfg {
   static constexpr int WAVES_PER_SIMD = BLOCKS_PER_CU * WAVES / 4;
   static_assert(BCI * WAVES * 1024 == 2 * BT, "B and C split evenly over the wavefronts");
   static_assert(32 * HPB <= 64 * WAVES, "dt pieces");
-  static_assert(R >= 3 && (R - 2) * (LDC + STC) <= 30, "wait counts");
+  static constexpr int SVC = N / 16;             // ... per saved chunk-start state
+  static_assert(R >= 3 && (R - 2) * (LDC + STC + SVC) <= 47, "wait counts");
   static_assert(BLOCKS_PER_CU >= 1 && WAVES_PER_SIMD >= 2, "occupancy");
 };
 
@@ -144,7 +132,8 @@ void k_ssd_fused(
   constexpr int KQ = N / 32;   // K steps over n
   constexpr int NCB = N / 8;   // 16-byte chunks per B / C row
   constexpr int XH = F::XH, BT = F::BT, DW = F::DW, OX = F::OX, OB = F::OB, OC = F::OC, OD = F::OD;
-  constexpr int SLOT = F::SLOT, AD = F::AD, ADW = F::ADW, BCI = F::BCI, LDC = F::LDC, STC = F::STC;
+  constexpr int SLOT = F::SLOT, AD = F::AD, ADW = F::ADW, BCI = F::BCI, LDC = F::LDC, STC = F::STC,
+                SVC = F::SVC;
   __shared__ __align__(16) unsigned char smem[F::TOTAL];
 
   int s, hb;
@@ -272,11 +261,11 @@ void k_ssd_fused(
     // chunk k has landed once at most the ops this wavefront issued after its
     // loads are pending: loads of later chunks (prologue, then one chunk per
     // iteration) and the y stores of the iterations in between
-    if (SAVE) {
-      wait_vmcnt<0>();  // the state stores below are not counted
-    } else {
+    // (and, when saving, the state stores of those iterations: SVC each)
+    {
       int n = k < D ? (min(D, nck) - 1 - k) * LDC : 0;
-      for (int j = k < D ? 0 : k - D + 1; j < k; ++j) n += (j >= 1 ? STC : 0) + (j + D < nck ? LDC : 0);
+      for (int j = k < D ? 0 : k - D + 1; j < k; ++j)
+        n += (SAVE ? SVC : 0) + (j >= 1 ? STC : 0) + (j + D < nck ? LDC : 0);
       wait_vmcnt_dyn(n);
     }
     __syncthreads();  // every wavefront's share of chunk k is in; chunk k-1 is done everywhere

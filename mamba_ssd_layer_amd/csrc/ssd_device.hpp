@@ -165,6 +165,22 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt vmcnt(n) for a run-time n (a switch over the immediates); counts
+// above 47 wait for everything.
+__device__ __forceinline__ void wait_vmcnt_dyn(int n) {
+  switch (n) {
+#define SSD_W(i) case i: wait_vmcnt<i>(); break;
+    SSD_W(0) SSD_W(1) SSD_W(2) SSD_W(3) SSD_W(4) SSD_W(5) SSD_W(6) SSD_W(7)
+    SSD_W(8) SSD_W(9) SSD_W(10) SSD_W(11) SSD_W(12) SSD_W(13) SSD_W(14) SSD_W(15)
+    SSD_W(16) SSD_W(17) SSD_W(18) SSD_W(19) SSD_W(20) SSD_W(21) SSD_W(22) SSD_W(23)
+    SSD_W(24) SSD_W(25) SSD_W(26) SSD_W(27) SSD_W(28) SSD_W(29) SSD_W(30) SSD_W(31)
+    SSD_W(32) SSD_W(33) SSD_W(34) SSD_W(35) SSD_W(36) SSD_W(37) SSD_W(38) SSD_W(39)
+    SSD_W(40) SSD_W(41) SSD_W(42) SSD_W(43) SSD_W(44) SSD_W(45) SSD_W(46) SSD_W(47)
+#undef SSD_W
+    default: wait_vmcnt<0>(); break;
+  }
+}
+
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane 4i+j receives
 // element j of the 4-element (8-byte) chunks addressed by lanes i, i+4, i+8,
 // i+12 of the group -- a 16 x 4 transpose of bf16 data in LDS.
