@@ -364,25 +364,36 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
   };
 
   // head j's x, dy, h_s, g_e (1 KB pieces split over the wavefronts) and dt
+  // Per-lane byte offsets of this wavefront's DMA pieces, fixed for the block
+  // (one chunk): x and dy piece `wave` (rows 8 wave .. +7, clamped to the
+  // chunk's end), h_s and g_e pieces wave + 4 k (the swizzle repeats every
+  // 16 rows, so piece k's offsets are piece 0's plus 4 KB k), and dt.
+  uint32_t xoff, hoff, dtoff;
+  {
+    const int m = wave * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz<8>(r);
+    xoff = static_cast<uint32_t>((min(r, last) * ldx + 8 * cc) * 2);
+    const int rh = m / NCB, ch = (m % NCB) ^ swz<NCB>(rh);
+    hoff = static_cast<uint32_t>((rh * N + 8 * ch) * 2);
+    dtoff = static_cast<uint32_t>(min(lane & 31, last) * H * 4);
+  }
+  constexpr int KP = F::ST / 1024 / 4;  // h_s (and g_e) pieces per wavefront
+  static_assert(2 + 2 * KP == F::PIECES / 4, "pieces per wavefront");
+  // head j's x, dy, h_s, g_e and dt into ring slot sl: scalar bases, fixed lane offsets
   auto issue_head = [&](int j, int sl) {
     const int h = g * hpg + j;
     const uint32_t base = lbase + sl * F::HSLOT;
+    dma_lds16_sb(xoff, x + t0 * ldx + (int64_t)h * P, base + F::OX + wave * 1024);
+    dma_lds16_sb(xoff, dy + t0 * ldx + (int64_t)h * P, base + F::OY + wave * 1024);
+    const int64_t st0 = (c * H + h) * (int64_t)(P * N);
 #pragma unroll
-    for (int i = 0; i < F::PIECES / 4; ++i) {
-      const int u = wave + 4 * i;
-      if (u < 8) {  // x (0..3) or dy (4..7): 32 rows x 8 chunks
-        const int pi = u & 3, m = pi * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz<8>(r);
-        dma_lds16((u < 4 ? x : dy) + (t0 + min(r, last)) * ldx + (int64_t)h * P + 8 * cc,
-                  base + (u < 4 ? F::OX : F::OY) + pi * 1024);
-      } else {  // h_s (8..) or g_e: 64 rows x N/8 chunks
-        const int v = u - 8, tile = v / (F::ST / 1024), pi = v % (F::ST / 1024);
-        const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz<NCB>(r);
-        dma_lds16((tile ? gsave : hsave) + (c * H + h) * (int64_t)(P * N) + (int64_t)r * N + 8 * cc,
-                  base + (tile ? F::OG : F::OH) + pi * 1024);
-      }
-    }
-    if (wave == 0) dma_lds4(dt + (t0 + min(lane & 31, last)) * H + h, base + F::ODT);
+    for (int k = 0; k < KP; ++k)
+      dma_lds16_sb(hoff, hsave + st0 + 2048 * k, base + F::OH + (wave + 4 * k) * 1024);
+#pragma unroll
+    for (int k = 0; k < KP; ++k)
+      dma_lds16_sb(hoff, gsave + st0 + 2048 * k, base + F::OG + (wave + 4 * k) * 1024);
+    if (wave == 0) dma_lds4_sb(dtoff, dt + t0 * H + h, base + F::ODT);
   };
+
 
   // ---- the chunk's B and C, head 0 ----
   {
