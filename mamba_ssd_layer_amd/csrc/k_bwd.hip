@@ -243,44 +243,47 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
 }
 
 // ---------------------------------------------------------------- pass 3
-// Block = (32-token chunk, group), 4 wavefronts, walking the group's heads.
-// LDS: the chunk's B and C (rows = tokens), and a two-slot ring per head of
-// x and dy (rows = tokens, 8 chunks a row), h_s and g_e (rows = p, N/8
-// chunks a row) and dt; per-wavefront tables; cross-wavefront partial sums.
-// Tile conventions (16x16x32 MFMA): an "E-layout" tile holds matrix[l][s] with
-// lane (c16 = s, g4) rows l = 16 lt + 4 g4 + r; its pair (lt = 0, 1) packs to a
-// B-operand with K = l in the order {4 g4 + 0..3, 16 + 4 g4 + 0..3}, matched by
-// transposing reads of token rows in the same order for the A-operand.
+// Block = (32-token chunk, group), 8 wavefronts (two per SIMD), walking the
+// group's heads.  LDS: the chunk's B and C (rows = tokens); an R-slot ring per
+// head of x and dy (rows = tokens, 8 chunks a row), h_s and g_e (rows = p, N/8
+// chunks a row) and dt; the head's masked products as ready MFMA operands;
+// per-wavefront tables and cross-wavefront partial sums (two buffers, by head
+// parity, since a head's sums are finished one head later).
+// Tile conventions (16x16x32 MFMA): an "E-layout" tile (lt, st) holds
+// matrix[l][s] with lane (c16 = s, g4) rows l = 16 lt + 4 g4 + r; the tiles
+// lt = 0, 1 of one st together form a B operand with K = l in the order
+// {4 g4 + 0..3, 16 + 4 g4 + 0..3} (8 bytes of each tile per lane), matched by
+// transposing reads of token rows in that order for the A operand.  An
+// "ET-layout" tile (st, lt) holds matrix[s][l] the same way.
+// Per head: wavefronts 0-3 form one E-layout tile each of E = dy x^T and from
+// it M = Z o L dt_s, EL = E o L dt_s and the sums of K = E o Z o L dt_s;
+// wavefronts 4-7 one ET-layout tile each of E^T and EL^T; after a barrier each
+// wavefront computes one 16 x 16 tile of dx (p-tile w/2, s-tile w%2) with the
+// matching tile of h_s C^T, and N/64 tiles of dB and of dC.
 template <int N, int R>
 struct BwdCfg {
-  static constexpr int P = 64, CQ = 32, NCB = N / 8;
+  static constexpr int P = 64, CQ = 32, NCB = N / 8, WAVES = 8;
   static constexpr int XT = CQ * P * 2;      // x or dy of a head: 32 rows x 128 B
   static constexpr int ST = P * N * 2;       // h_s or g_e of a head: 64 rows x N bf16
   static constexpr int BT = CQ * N * 2;      // B or C of the chunk
   static constexpr int OX = 0, OY = XT, OH = 2 * XT, OG = OH + ST, ODT = OG + ST;
   static constexpr int HSLOT = ODT + 256;
   static constexpr int OB = R * HSLOT, OCC = OB + BT;   // R ring slots of a head's tiles
-  // per-head scratch, two buffers (head parity): the per-wavefront tables
-  // (6 x 32 floats), the per-wavefront partials v[32], q[32], gh, and the
-  // per-token sums below
-  static constexpr int OTAB = OCC + BT;
-  static constexpr int TABW = 6 * CQ * 4;
-  static constexpr int OPART = OTAB + 2 * 4 * TABW;
-  static constexpr int PARTW = (2 * CQ + 4) * 4;
-  // column partials [4][32] of E o Z o L (all l >= s, and l > s times dt_s),
-  // row sums [32] (s < l, times dt_s), diagonal of E [32]
-  static constexpr int OSC = OPART + 2 * 4 * PARTW;
-  static constexpr int SCW = (8 * CQ + 2 * CQ) * 4;
-  static constexpr int TOTAL = OSC + 2 * SCW;
-  static constexpr int PIECES = (2 * XT + 2 * ST) / 1024;  // 1 KB pieces of a head's tiles
-  static constexpr int BLOCKS = (160 * 1024) / TOTAL;
-  static_assert(PIECES % 4 == 0, "pieces split over 4 wavefronts");
-  static constexpr int LD = PIECES / 4;   // vector-memory ops a wavefront issues per head (+1: dt)
-  static_assert(BLOCKS >= 1, "LDS");
+  static constexpr int OOP = OCC + BT;                   // operands M, EL, ELT: [2][64 lanes][16 B] each
+  static constexpr int OTAB = OOP + 3 * 2048;            // per wavefront and buffer: 5 tables of 32 floats
+  static constexpr int TABW = 5 * CQ * 4;
+  static constexpr int OPART = OTAB + 2 * WAVES * TABW;  // per buffer: the partial sums below
+  static constexpr int PARTW = 512 * 4;
+  static constexpr int TOTAL = OPART + 2 * PARTW;
+  static constexpr int KP = ST / 1024 / WAVES;           // h_s (and g_e) pieces per wavefront
+  static constexpr int LD = 1 + 2 * KP;                  // vector-memory ops a wavefront issues per head (+1: dt)
+  static constexpr int NTW = N / 64;                     // tiles of dB (and dC) per wavefront
+  static_assert(KP >= 1 && KP * WAVES * 1024 == ST, "state pieces");
+  static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
 template <int N, int R>
-__global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
+__global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
     const uint16_t *__restrict__ dy, const uint16_t *__restrict__ hsave,
@@ -289,9 +292,8 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
     float *__restrict__ ddt, float *__restrict__ dA, float *__restrict__ dB,
     float *__restrict__ dC, float *__restrict__ dD) {
   using F = BwdCfg<N, R>;
-  constexpr int P = F::P, CQ = F::CQ, NCB = F::NCB;
-  constexpr int KQ = N / 32;       // K steps over n
-  constexpr int NTW = N / 16 / 4;  // n-tiles of dB / dC a wavefront owns
+  constexpr int P = F::P, CQ = F::CQ, NCB = F::NCB, KP = F::KP, NTW = F::NTW;
+  constexpr int KQ = N / 32;  // K steps over n
   __shared__ __align__(16) unsigned char smem[F::TOTAL];
 
   const int64_t c = blockIdx.x / G;
@@ -326,6 +328,7 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
   }
   const int64_t t0 = tb + k * CQ;
   const int last = static_cast<int>(min((int64_t)CQ, len - k * CQ)) - 1;
+  const bool full = last == CQ - 1;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g4 = lane >> 4, tl = lane & 31;
@@ -334,13 +337,14 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
   const uint32_t lbase = lds_off(smem);
   const unsigned char *bsm = smem + F::OB;
   const unsigned char *csm = smem + F::OCC;
-  // buffer b of the per-head scratch
-  auto tab_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OTAB + (b * 4 + wave) * F::TABW); };
-  auto part_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OPART + b * 4 * F::PARTW); };
-  auto sc_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OSC + b * F::SCW); };
-  enum { TA2 = 0, TF = 32, TW = 64, TDT = 96, TEL = 128 };           // table rows
-  enum { PV = 0, PQ = 32, PGH = 64 };                                // partials, per wavefront
-  enum { SC1 = 0, SCK = 128, SRK = 256, SDE = 288 };                 // per-token sums
+  unsigned char *opm = smem + F::OOP, *opel = opm + 2048, *opelt = opm + 4096;
+  auto tab_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OTAB + (b * 8 + wave) * F::TABW); };
+  auto part_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OPART + b * F::PARTW); };
+  enum { TA2 = 0, TF = 32, TW = 64, TDT = 96, TEL = 128 };  // tables: a_l log2(e), exp(a_l), w_s, dt_s, exp(a_last - a_s)
+  // partial sums: q_s [p-tile][s], v_l [p-tile][l], <g_e, h_s> [wavefront], column
+  // sums of E o Z o L [lt][s] (all l >= s) and of K [lt][s] (l > s), row sums
+  // of K [st][l] (s < l), diagonal of E [s]
+  enum { PQ = 0, PV = 128, PGH = 256, PC1 = 264, PCK = 328, PRK = 392, PDE = 456 };
 
   // ---- operand reads ----
   // 16 bytes of a token row of x / dy (8 chunks): p = 32 kq + 8 g4 + 0..7
@@ -351,7 +355,8 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
   auto rown = [&](const unsigned char *t, int row, int q) {
     return *reinterpret_cast<const u32x4 *>(t + row * (N * 2) + (((4 * q + g4) ^ swz<NCB>(row)) << 4));
   };
-  // transposing read: rows r0 + (c16 >> 2) and r1 + (c16 >> 2), column col0 + c16 of the lane
+  // transposing read: lane (c16, g4) gets column col0 + c16 of rows r0 + 0..3
+  // and r1 + 0..3 (r0, r1 per lane group)
   auto trn = [&](const unsigned char *t, int rb, int r0, int r1, int col0, bool wide) {
     u32x2 v[2];
 #pragma unroll
@@ -363,41 +368,37 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
     return u32x4{v[0].x, v[0].y, v[1].x, v[1].y};
   };
 
-  // head j's x, dy, h_s, g_e (1 KB pieces split over the wavefronts) and dt
-  // Per-lane byte offsets of this wavefront's DMA pieces, fixed for the block
-  // (one chunk): x and dy piece `wave` (rows 8 wave .. +7, clamped to the
-  // chunk's end), h_s and g_e pieces wave + 4 k (the swizzle repeats every
-  // 16 rows, so piece k's offsets are piece 0's plus 4 KB k), and dt.
+  // Per-lane byte offsets of this wavefront's DMA pieces, fixed for the block:
+  // x (wavefronts 0-3) or dy (4-7) piece wave % 4 (rows 8 (wave % 4) .. +7,
+  // clamped to the chunk's end); h_s and g_e pieces wave + 8 k (the swizzle
+  // repeats every 16 rows, so piece k's offsets are piece 0's plus 8 KB k); dt.
   uint32_t xoff, hoff, dtoff;
   {
-    const int m = wave * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz<8>(r);
+    const int m = (wave & 3) * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz<8>(r);
     xoff = static_cast<uint32_t>((min(r, last) * ldx + 8 * cc) * 2);
-    const int rh = m / NCB, ch = (m % NCB) ^ swz<NCB>(rh);
+    const int mh = wave * 64 + lane, rh = mh / NCB, ch = (mh % NCB) ^ swz<NCB>(rh);
     hoff = static_cast<uint32_t>((rh * N + 8 * ch) * 2);
-    dtoff = static_cast<uint32_t>(min(lane & 31, last) * H * 4);
+    dtoff = static_cast<uint32_t>(min(tl, last) * H * 4);
   }
-  constexpr int KP = F::ST / 1024 / 4;  // h_s (and g_e) pieces per wavefront
-  static_assert(2 + 2 * KP == F::PIECES / 4, "pieces per wavefront");
   // head j's x, dy, h_s, g_e and dt into ring slot sl: scalar bases, fixed lane offsets
   auto issue_head = [&](int j, int sl) {
     const int h = g * hpg + j;
     const uint32_t base = lbase + sl * F::HSLOT;
-    dma_lds16_sb(xoff, x + t0 * ldx + (int64_t)h * P, base + F::OX + wave * 1024);
-    dma_lds16_sb(xoff, dy + t0 * ldx + (int64_t)h * P, base + F::OY + wave * 1024);
+    dma_lds16_sb(xoff, (wave < 4 ? x : dy) + t0 * ldx + (int64_t)h * P,
+                 base + (wave < 4 ? F::OX : F::OY) + (wave & 3) * 1024);
     const int64_t st0 = (c * H + h) * (int64_t)(P * N);
 #pragma unroll
-    for (int k = 0; k < KP; ++k)
-      dma_lds16_sb(hoff, hsave + st0 + 2048 * k, base + F::OH + (wave + 4 * k) * 1024);
+    for (int kk = 0; kk < KP; ++kk)
+      dma_lds16_sb(hoff, hsave + st0 + 4096 * kk, base + F::OH + (wave + 8 * kk) * 1024);
 #pragma unroll
-    for (int k = 0; k < KP; ++k)
-      dma_lds16_sb(hoff, gsave + st0 + 2048 * k, base + F::OG + (wave + 4 * k) * 1024);
+    for (int kk = 0; kk < KP; ++kk)
+      dma_lds16_sb(hoff, gsave + st0 + 4096 * kk, base + F::OG + (wave + 8 * kk) * 1024);
     if (wave == 0) dma_lds4_sb(dtoff, dt + t0 * H + h, base + F::ODT);
   };
 
-
-  // ---- the chunk's B and C, head 0 ----
+  // ---- the chunk's B and C, then heads 0 .. R-2 ahead ----
   {
-    constexpr int BCP = 2 * F::BT / 1024 / 4;
+    constexpr int BCP = 2 * F::BT / 1024 / 8;
 #pragma unroll
     for (int i = 0; i < BCP; ++i) {
       const int u = wave * BCP + i, tile = u / (F::BT / 1024), pi = u % (F::BT / 1024);
@@ -406,28 +407,33 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
                 lbase + (tile ? F::OCC : F::OB) + pi * 1024);
     }
   }
-  // heads 0 .. R-2 ahead; head j + R - 1 is issued at the start of head j
   const int LDW = F::LD + (wave == 0 ? 1 : 0);
-  // stores and atomics a wavefront issues in iteration m: dx of head m (2);
-  // wavefront 0 also ddt, dA, dD of head m - 1
-  auto stw = [&](int m) { return 2 + (wave == 0 && m >= 1 ? 2 + (dD ? 1 : 0) : 0); };
-  const bool full = last == CQ - 1;
+  // stores and atomics a wavefront issues in iteration m: its dx tile of head
+  // m; wavefront 0 also ddt, dA, dD of head m - 1
+  auto stw = [&](int m) { return 1 + (wave == 0 && m >= 1 ? 2 + (dD ? 1 : 0) : 0); };
 #pragma unroll
   for (int jj = 0; jj < R - 1; ++jj)
     if (jj < hpg) issue_head(jj, jj);
   wait_vmcnt_dyn(min(R - 1, hpg) * LDW);  // B and C are in (the head loads issued after them may not be)
   __syncthreads();
-  // Z = C B^T in E-layout tiles [lt][st]
-  f32x4 z[2][2];
+
+  // this wavefront's roles
+  const bool etile = wave < 4;               // E-layout tile (lt, st) = (wave / 2, wave % 2)
+  const int qa = (wave >> 1) & 1, qb = wave & 1;  // E: (lt, st) = (qa, qb); ET: (st, lt) = (qa, qb)
+  const int pt = wave >> 1, sh = wave & 1;   // dx / h_s C^T tile (p-tile, s- or l-tile)
+  // Z = C B^T, the E-layout tile (qa, qb) (wavefronts 0-3)
+  f32x4 z{};
+  if (etile) {
 #pragma unroll
-  for (int lt = 0; lt < 2; ++lt)
+    for (int q = 0; q < KQ; ++q) z = mfma16b(rown(csm, 16 * qa + c16, q), rown(bsm, 16 * qb + c16, q), z);
+  }
+
+  f32x4 dBa[NTW], dCa[NTW];
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      f32x4 acc{};
-#pragma unroll
-      for (int q = 0; q < KQ; ++q) acc = mfma16b(rown(csm, 16 * lt + c16, q), rown(bsm, 16 * st + c16, q), acc);
-      z[lt][st] = acc;
-    }
+  for (int i = 0; i < NTW; ++i) {
+    dBa[i] = f32x4{};
+    dCa[i] = f32x4{};
+  }
 
   // ---- per-token scalars of head jj (its partials complete): every
   // wavefront computes them, wavefront 0 writes ddt and adds dA, dD ----
@@ -435,21 +441,22 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
     const int h = g * hpg + jj;
     const float *tab = tab_of(jj & 1);
     const float *part = part_of(jj & 1);
-    const float *sc = sc_of(jj & 1);
-    float q = 0.f, v = 0.f, gh = 0.f, t1 = 0.f, ck = 0.f;
+    float q = 0.f, v = 0.f, gh = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
-      q += part[w * (2 * CQ + 4) + PQ + tl];
-      v += part[w * (2 * CQ + 4) + PV + tl];
-      gh += part[w * (2 * CQ + 4) + PGH];
-      t1 += sc[SC1 + 32 * w + tl];
-      ck += sc[SCK + 32 * w + tl];
+      q += part[PQ + 32 * w + tl];
+      v += part[PV + 32 * w + tl];
     }
+#pragma unroll
+    for (int w = 0; w < 8; ++w) gh += part[PGH + w];
+    const float t1 = part[PC1 + tl] + part[PC1 + 32 + tl];
+    const float ck = part[PCK + tl] + part[PCK + 32 + tl];
+    const float rkr = part[PRK + tl] + part[PRK + 32 + tl];
     v *= tab[TF + tl];
     const float u = tab[TW + tl] * q;
     const float uin = scan32b(u);
     const float vin = scan32b(v);
-    const float rkv = sc[SRK + tl] - ck;
+    const float rkv = rkr - ck;
     const float rin = scan32b(rkv);
     const float U = exp2b(alast * kLog2eB) * gh + (uin - u);
     const float V = lane31(vin) - vin + v;
@@ -458,7 +465,7 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
     const float dd = term1 + Ah * (Rr + V + U);
     const bool ok = lane < 32 && tl <= last;
     const float da = lane31(scan32b(ok ? tab[TDT + tl] * (Rr + V + U) : 0.f));
-    const float dsum = lane31(scan32b(ok ? sc[SDE + tl] : 0.f));
+    const float dsum = lane31(scan32b(ok ? part[PDE + tl] : 0.f));
     if (wave == 0) {
       if (ok) ddt[(t0 + tl) * H + h] = dd;
       if (lane == 0) {
@@ -468,15 +475,6 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
     }
   };
   float pAh = 0.f, palast = 0.f;  // of the previous head
-
-  f32x4 dBa[NTW][2], dCa[NTW][2];
-#pragma unroll
-  for (int i = 0; i < NTW; ++i)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      dBa[i][t] = f32x4{};
-      dCa[i][t] = f32x4{};
-    }
 
 #pragma unroll 1
   for (int j = 0; j < hpg; ++j) {
@@ -499,29 +497,28 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
         }
       }
       wait_vmcnt_dyn(n);
-      __syncthreads();  // head j is in everywhere; head j-1 (and its partials) is done everywhere
+      __syncthreads();  // head j is in everywhere; head j-1 and its partials are done everywhere
     }
     if (j + R - 1 < hpg) issue_head(j + R - 1, (j + R - 1) % R);
     if (j > 0) finish(j - 1, pAh, palast);
     const int pb = j & 1;
     float *tab = tab_of(pb);
     float *part = part_of(pb);
-    float *sc = sc_of(pb);
     unsigned char *hsl = smem + sl * F::HSLOT;
     const unsigned char *xs = hsl + F::OX;
     unsigned char *ys = hsl + F::OY;
     const unsigned char *hss = hsl + F::OH;
     const unsigned char *gss = hsl + F::OG;
     const float *dts = reinterpret_cast<const float *>(hsl + F::ODT);
-    if (last < CQ - 1) {  // dy of tokens past the sequence's end is zero
-      for (int i = threadIdx.x; i < (CQ - 1 - last) * 8; i += 256) {
+    if (!full) {  // dy of tokens past the sequence's end is zero
+      for (int i = threadIdx.x; i < (CQ - 1 - last) * 8; i += 512) {
         const int row = last + 1 + (i >> 3);
         *reinterpret_cast<u32x4 *>(ys + row * 128 + ((i & 7) << 4)) = u32x4{0u, 0u, 0u, 0u};
       }
       __syncthreads();
     }
     const float Ah = A[h];
-    // per-token tables: a_l (log2), exp(a_l), w_s, dt_s, exp(a_last - a_t)
+    // per-token tables: a_l (log2), exp(a_l), w_s, dt_s, exp(a_last - a_s)
     const float dtv = tl <= last ? dts[tl] : 0.f;
     const float a = scan32b(dtv * Ah);
     const float alast = lane31(a);
@@ -534,216 +531,160 @@ __global__ __launch_bounds__(256, (BwdCfg<N, R>::BLOCKS)) void k_bwd_chunk(
     }
     wsync();
 
-    // E = dy x^T (E-layout [lt][st]) and E^T (ET-layout [st][lt])
-    f32x4 e[2][2], et[2][2];
+    // ---- phase 1: one tile of the masked products per wavefront ----
+    if (etile) {
+      // E-layout (lt, st) = (qa, qb): l = 16 qa + 4 g4 + r, s = 16 qb + c16
+      f32x4 e{};
 #pragma unroll
-    for (int lt = 0; lt < 2; ++lt)
+      for (int kq = 0; kq < 2; ++kq) e = mfma16b(rowx(ys, 16 * qa + c16, kq), rowx(xs, 16 * qb + c16, kq), e);
+      const int sx = 16 * qb + c16;
+      const f32x4 al = *reinterpret_cast<const f32x4 *>(tab + TA2 + 16 * qa + 4 * g4);
+      const float as = tab[TA2 + sx], ds = tab[TDT + sx];
+      float mv[4], elv[4], t1 = 0.f, ck = 0.f;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x4 a1{}, a2{};
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-          const u32x4 yl = rowx(ys, 16 * lt + c16, kq), xsr = rowx(xs, 16 * st + c16, kq);
-          a1 = mfma16b(yl, rowx(xs, 16 * st + c16, kq), a1);
-          a2 = mfma16b(xsr, rowx(ys, 16 * lt + c16, kq), a2);
-        }
-        e[lt][st] = a1;
-        et[st][lt] = a2;
+      for (int r = 0; r < 4; ++r) {
+        const int l = 16 * qa + 4 * g4 + r;
+        const float lf = sx <= l ? exp2b(fminf(al[r] - as, 0.f)) : 0.f;
+        mv[r] = z[r] * lf * ds;
+        elv[r] = e[r] * lf * ds;
+        const float pvr = e[r] * z[r] * lf;
+        t1 += pvr;
+        if (l > sx) ck += pvr * ds;
+        float rk = sx < l ? pvr * ds : 0.f;
+        rk = rowsum16(rk);
+        if (c16 == 0) part[PRK + 32 * qb + l] = rk;
       }
-    // masked, decayed products.  E-layout (lt, st): l = 16 lt + 4 g4 + r, s = 16 st + c16
-    u32x4 mop[2], elop[2], eltop[2];
-    float pv[2][2][4];  // E o Z o L (no dt), E-layout
-    {
-      float m_[2][2][4], el_[2][2][4], elt_[2][2][4];
-#pragma unroll
-      for (int lt = 0; lt < 2; ++lt) {
-        const f32x4 al = *reinterpret_cast<const f32x4 *>(tab + TA2 + 16 * lt + 4 * g4);
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const float as = tab[TA2 + 16 * st + c16], ds = tab[TDT + 16 * st + c16];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int l = 16 * lt + 4 * g4 + r, sx = 16 * st + c16;
-            const bool ok = sx <= l;
-            const float lf = ok ? exp2b(fminf(al[r] - as, 0.f)) : 0.f;
-            m_[lt][st][r] = z[lt][st][r] * lf * ds;
-            el_[lt][st][r] = e[lt][st][r] * lf * ds;
-            pv[lt][st][r] = e[lt][st][r] * z[lt][st][r] * lf;
-          }
-        }
+      *reinterpret_cast<u32x2 *>(opm + qb * 1024 + lane * 16 + qa * 8) =
+          u32x2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
+      *reinterpret_cast<u32x2 *>(opel + qb * 1024 + lane * 16 + qa * 8) =
+          u32x2{pack_bf16x2(elv[0], elv[1]), pack_bf16x2(elv[2], elv[3])};
+      t1 += __shfl_xor(t1, 16, 64);
+      t1 += __shfl_xor(t1, 32, 64);
+      ck += __shfl_xor(ck, 16, 64);
+      ck += __shfl_xor(ck, 32, 64);
+      if (lane < 16) {
+        part[PC1 + 32 * qa + sx] = t1;
+        part[PCK + 32 * qa + sx] = ck;
       }
-      // ET-layout (st, lt): s = 16 st + 4 g4 + r, l = 16 lt + c16
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const f32x4 as = *reinterpret_cast<const f32x4 *>(tab + TA2 + 16 * st + 4 * g4);
-        const f32x4 ds = *reinterpret_cast<const f32x4 *>(tab + TDT + 16 * st + 4 * g4);
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt) {
-          const float al = tab[TA2 + 16 * lt + c16];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int sx = 16 * st + 4 * g4 + r, l = 16 * lt + c16;
-            const bool ok = sx <= l;
-            const float lf = ok ? exp2b(fminf(al - as[r], 0.f)) : 0.f;
-            elt_[st][lt][r] = et[st][lt][r] * lf * ds[r];
-          }
-        }
+      if (qa == qb && (c16 >> 2) == g4) {  // the diagonal E_ss
+        const int r = c16 & 3;
+        part[PDE + sx] = r == 0 ? e.x : r == 1 ? e.y : r == 2 ? e.z : e.w;
       }
+    } else {
+      // ET-layout (st, lt) = (qa, qb): s = 16 qa + 4 g4 + r, l = 16 qb + c16
+      f32x4 et{};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        mop[t] = u32x4{pack_bf16x2(m_[0][t][0], m_[0][t][1]), pack_bf16x2(m_[0][t][2], m_[0][t][3]),
-                       pack_bf16x2(m_[1][t][0], m_[1][t][1]), pack_bf16x2(m_[1][t][2], m_[1][t][3])};
-        elop[t] = u32x4{pack_bf16x2(el_[0][t][0], el_[0][t][1]), pack_bf16x2(el_[0][t][2], el_[0][t][3]),
-                        pack_bf16x2(el_[1][t][0], el_[1][t][1]), pack_bf16x2(el_[1][t][2], el_[1][t][3])};
-        eltop[t] = u32x4{pack_bf16x2(elt_[0][t][0], elt_[0][t][1]), pack_bf16x2(elt_[0][t][2], elt_[0][t][3]),
-                         pack_bf16x2(elt_[1][t][0], elt_[1][t][1]), pack_bf16x2(elt_[1][t][2], elt_[1][t][3])};
+      for (int kq = 0; kq < 2; ++kq) et = mfma16b(rowx(xs, 16 * qa + c16, kq), rowx(ys, 16 * qb + c16, kq), et);
+      const int lx = 16 * qb + c16;
+      const f32x4 as = *reinterpret_cast<const f32x4 *>(tab + TA2 + 16 * qa + 4 * g4);
+      const f32x4 ds = *reinterpret_cast<const f32x4 *>(tab + TDT + 16 * qa + 4 * g4);
+      const float al = tab[TA2 + lx];
+      float ev[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int sx = 16 * qa + 4 * g4 + r;
+        const float lf = sx <= lx ? exp2b(fminf(al - as[r], 0.f)) : 0.f;
+        ev[r] = et[r] * lf * ds[r];
       }
+      *reinterpret_cast<u32x2 *>(opelt + qb * 1024 + lane * 16 + qa * 8) =
+          u32x2{pack_bf16x2(ev[0], ev[1]), pack_bf16x2(ev[2], ev[3])};
     }
+    __syncthreads();  // the head's operands and sums of phase 1 are in LDS
 
-    // ---- dx rows of p-tile pt = wave; q_s and v_l partials ----
+    // ---- phase 2 ----
     const float Dh = Dv ? Dv[h] : 0.f;
     {
-      const int pt = wave;
+      // dx tile (p-tile pt, s-tile sh): dy^T M + w_s g_e B^T + D dy; q_s partial
       const u32x4 dyt = trn(ys, 128, 4 * g4, 16 + 4 * g4, 16 * pt, false);
+      const u32x4 mop = *reinterpret_cast<const u32x4 *>(opm + sh * 1024 + lane * 16);
+      f32x4 acc = mfma16b(dyt, mop, f32x4{});
+      f32x4 gb{};
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        f32x4 acc = mfma16b(dyt, mop[st], f32x4{});
-        f32x4 gb{};
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) gb = mfma16b(rown(gss, 16 * pt + c16, q), rown(bsm, 16 * st + c16, q), gb);
-        // lane: column s, rows p = 16 pt + 4 g4 + r
-        const int sx = 16 * st + c16, col = 16 * pt + 4 * g4;
-        const float ws = tab[TW + sx];
-        const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2);
-        const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2);
-        const float o0 = acc.x + ws * gb.x + Dh * bf16lo(dv.x);
-        const float o1 = acc.y + ws * gb.y + Dh * bf16hi(dv.x);
-        const float o2 = acc.z + ws * gb.z + Dh * bf16lo(dv.y);
-        const float o3 = acc.w + ws * gb.w + Dh * bf16hi(dv.y);
-        if (sx <= last)
-          *reinterpret_cast<u32x2 *>(dx + (t0 + sx) * ldx + (int64_t)h * P + col) =
-              u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-        float qv = bf16lo(xv.x) * gb.x + bf16hi(xv.x) * gb.y + bf16lo(xv.y) * gb.z + bf16hi(xv.y) * gb.w;
-        qv += __shfl_xor(qv, 16, 64);
-        qv += __shfl_xor(qv, 32, 64);
-        if (lane < 16) part[wave * (2 * CQ + 4) + PQ + sx] = qv;
-      }
-#pragma unroll
-      for (int lt = 0; lt < 2; ++lt) {
-        f32x4 hc{};
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) hc = mfma16b(rown(hss, 16 * pt + c16, q), rown(csm, 16 * lt + c16, q), hc);
-        const int lx = 16 * lt + c16, col = 16 * pt + 4 * g4;
-        const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + lx * 128 + (((col >> 3) ^ swz<8>(lx)) << 4) + (col & 7) * 2);
-        float vv = bf16lo(dv.x) * hc.x + bf16hi(dv.x) * hc.y + bf16lo(dv.y) * hc.z + bf16hi(dv.y) * hc.w;
-        vv += __shfl_xor(vv, 16, 64);
-        vv += __shfl_xor(vv, 32, 64);
-        if (lane < 16) part[wave * (2 * CQ + 4) + PV + lx] = vv;
-      }
-      // <g_e, h_s> over rows p = 16 pt .. +15: lane takes a quarter row
-      {
-        const int row = 16 * pt + (lane >> 2);
-        float acc = 0.f;
-#pragma unroll
-        for (int cj = 0; cj < NCB / 4; ++cj) {
-          const int ch = (lane & 3) * (NCB / 4) + cj;
-          const int off = row * (N * 2) + ((ch ^ swz<NCB>(row)) << 4);
-          const u32x4 gv = *reinterpret_cast<const u32x4 *>(gss + off);
-          const u32x4 hv = *reinterpret_cast<const u32x4 *>(hss + off);
-          acc += bf16lo(gv.x) * bf16lo(hv.x) + bf16hi(gv.x) * bf16hi(hv.x) + bf16lo(gv.y) * bf16lo(hv.y) +
-                 bf16hi(gv.y) * bf16hi(hv.y) + bf16lo(gv.z) * bf16lo(hv.z) + bf16hi(gv.z) * bf16hi(hv.z) +
-                 bf16lo(gv.w) * bf16lo(hv.w) + bf16hi(gv.w) * bf16hi(hv.w);
-        }
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off, 64);
-        if (lane == 0) part[wave * (2 * CQ + 4) + PGH] = acc;
-      }
+      for (int q = 0; q < KQ; ++q) gb = mfma16b(rown(gss, 16 * pt + c16, q), rown(bsm, 16 * sh + c16, q), gb);
+      // lane: column s, rows p = 16 pt + 4 g4 + r
+      const int sx = 16 * sh + c16, col = 16 * pt + 4 * g4;
+      const float ws = tab[TW + sx];
+      const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2);
+      const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2);
+      const float o0 = acc.x + ws * gb.x + Dh * bf16lo(dv.x);
+      const float o1 = acc.y + ws * gb.y + Dh * bf16hi(dv.x);
+      const float o2 = acc.z + ws * gb.z + Dh * bf16lo(dv.y);
+      const float o3 = acc.w + ws * gb.w + Dh * bf16hi(dv.y);
+      if (sx <= last)
+        *reinterpret_cast<u32x2 *>(dx + (t0 + sx) * ldx + (int64_t)h * P + col) =
+            u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
+      float qv = bf16lo(xv.x) * gb.x + bf16hi(xv.x) * gb.y + bf16lo(xv.y) * gb.z + bf16hi(xv.y) * gb.w;
+      qv += __shfl_xor(qv, 16, 64);
+      qv += __shfl_xor(qv, 32, 64);
+      if (lane < 16) part[PQ + 32 * pt + sx] = qv;
     }
-
-    // ---- dB, dC over the wavefront's n-tiles ----
+    {
+      // h_s C^T tile (p-tile pt, l-tile sh): v_l partial dy_l . (h_s C_l)
+      f32x4 hc{};
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) hc = mfma16b(rown(hss, 16 * pt + c16, q), rown(csm, 16 * sh + c16, q), hc);
+      const int lx = 16 * sh + c16, col = 16 * pt + 4 * g4;
+      const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + lx * 128 + (((col >> 3) ^ swz<8>(lx)) << 4) + (col & 7) * 2);
+      float vv = bf16lo(dv.x) * hc.x + bf16hi(dv.x) * hc.y + bf16lo(dv.y) * hc.z + bf16hi(dv.y) * hc.w;
+      vv += __shfl_xor(vv, 16, 64);
+      vv += __shfl_xor(vv, 32, 64);
+      if (lane < 16) part[PV + 32 * pt + lx] = vv;
+    }
+    {
+      // <g_e, h_s> over rows p = 8 wave .. +7: lane takes 1/8 of a row
+      const int row = 8 * wave + (lane >> 3);
+      float acc = 0.f;
+#pragma unroll
+      for (int cj = 0; cj < NCB / 8; ++cj) {
+        const int off = row * (N * 2) + ((((lane & 7) * (NCB / 8) + cj) ^ swz<NCB>(row)) << 4);
+        const u32x4 gv = *reinterpret_cast<const u32x4 *>(gss + off);
+        const u32x4 hv = *reinterpret_cast<const u32x4 *>(hss + off);
+        acc += bf16lo(gv.x) * bf16lo(hv.x) + bf16hi(gv.x) * bf16hi(hv.x) + bf16lo(gv.y) * bf16lo(hv.y) +
+               bf16hi(gv.y) * bf16hi(hv.y) + bf16lo(gv.z) * bf16lo(hv.z) + bf16hi(gv.z) * bf16hi(hv.z) +
+               bf16lo(gv.w) * bf16lo(hv.w) + bf16hi(gv.w) * bf16hi(hv.w);
+      }
+      acc = rowsum16(acc);
+      acc += __shfl_xor(acc, 16, 64);
+      acc += __shfl_xor(acc, 32, 64);
+      if (lane == 0) part[PGH + wave] = acc;
+    }
+    // dB, dC tiles u = NTW wave + i: n-tile u / 2, s-tile (l-tile) u % 2
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
-      const int nt = wave * NTW + i;
+      const int u = NTW * wave + i, nt = u >> 1, t = u & 1;
       const u32x4 ct = trn(csm, N * 2, 4 * g4, 16 + 4 * g4, 16 * nt, true);
       const u32x4 bt = trn(bsm, N * 2, 4 * g4, 16 + 4 * g4, 16 * nt, true);
+      const u32x4 elop = *reinterpret_cast<const u32x4 *>(opel + t * 1024 + lane * 16);
+      const u32x4 eltop = *reinterpret_cast<const u32x4 *>(opelt + t * 1024 + lane * 16);
+      dBa[i] = mfma16b(ct, elop, dBa[i]);
+      dCa[i] = mfma16b(bt, eltop, dCa[i]);
+      f32x4 gx{}, hy{};
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        dBa[i][t] = mfma16b(ct, elop[t], dBa[i][t]);
-        dCa[i][t] = mfma16b(bt, eltop[t], dCa[i][t]);
-        f32x4 gx{}, hy{};
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-          const u32x4 gsT = trn(gss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
-          const u32x4 hsT = trn(hss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
-          gx = mfma16b(gsT, rowx(xs, 16 * t + c16, kq), gx);
-          hy = mfma16b(hsT, rowx(ys, 16 * t + c16, kq), hy);
-        }
-        const float ws = tab[TW + 16 * t + c16], fl = tab[TF + 16 * t + c16];
-        dBa[i][t] += gx * ws;
-        dCa[i][t] += hy * fl;
+      for (int kq = 0; kq < 2; ++kq) {
+        const u32x4 gsT = trn(gss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
+        const u32x4 hsT = trn(hss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
+        gx = mfma16b(gsT, rowx(xs, 16 * t + c16, kq), gx);
+        hy = mfma16b(hsT, rowx(ys, 16 * t + c16, kq), hy);
       }
-    }
-
-    // ---- per-token sums of E o Z o L, one kind per wavefront ----
-    if (wave == 0) {  // column partials over this lane group's rows l (all l >= s; l > s times dt_s)
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        const int sx = 16 * st + c16;
-        const float ds = tab[TDT + sx];
-        float t1 = 0.f, ck = 0.f;
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            t1 += pv[lt][st][r];
-            if (16 * lt + 4 * g4 + r > sx) ck += pv[lt][st][r] * ds;
-          }
-        sc[SC1 + 32 * g4 + sx] = t1;
-        sc[SCK + 32 * g4 + sx] = ck;
-      }
-    } else if (wave == 1) {  // row sums over s < l, times dt_s
-#pragma unroll
-      for (int lt = 0; lt < 2; ++lt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int l = 16 * lt + 4 * g4 + r;
-          float rk = 0.f;
-#pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const int sx = 16 * st + c16;
-            if (sx < l) rk += pv[lt][st][r] * tab[TDT + sx];
-          }
-          rk = rowsum16(rk);
-          if (c16 == 0) sc[SRK + l] = rk;
-        }
-    } else if (wave == 2) {  // the diagonal E_ss (for dD)
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-        if ((c16 >> 2) == g4) {
-          const f32x4 ev = e[st][st];
-          const int r = c16 & 3;
-          sc[SDE + 16 * st + c16] = r == 0 ? ev.x : r == 1 ? ev.y : r == 2 ? ev.z : ev.w;
-        }
+      const float ws = tab[TW + 16 * t + c16], fl = tab[TF + 16 * t + c16];
+      dBa[i] += gx * ws;
+      dCa[i] += hy * fl;
     }
     pAh = Ah;
     palast = alast;
   }
-
   __syncthreads();  // the last head's partials are in everywhere
   finish(hpg - 1, pAh, palast);
 
   // ---- dB, dC of the chunk's rows: lane column s, rows n = 16 nt + 4 g4 + r ----
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
-    const int nt = wave * NTW + i;
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int sx = 16 * t + c16;
-      if (sx <= last) {
-        const int64_t off = (t0 + sx) * ldb + (int64_t)g * N + 16 * nt + 4 * g4;
-        *reinterpret_cast<f32x4 *>(dB + off) = dBa[i][t];
-        *reinterpret_cast<f32x4 *>(dC + off) = dCa[i][t];
-      }
+    const int u = NTW * wave + i, nt = u >> 1, t = u & 1;
+    const int sx = 16 * t + c16;
+    if (sx <= last) {
+      const int64_t off = (t0 + sx) * ldb + (int64_t)g * N + 16 * nt + 4 * g4;
+      *reinterpret_cast<f32x4 *>(dB + off) = dBa[i];
+      *reinterpret_cast<f32x4 *>(dC + off) = dCa[i];
     }
   }
 }
@@ -789,12 +730,12 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
   const uint16_t *hs = static_cast<const uint16_t *>(hsave);
   const uint16_t *gs = static_cast<const uint16_t *>(gsave);
   uint16_t *dxo = static_cast<uint16_t *>(dx);
-  // N 64: two slots, two blocks a CU; N 128: three slots (two heads in flight), one block
+  // N 64: two slots; N 128: three slots (two heads in flight); one block of 8 wavefronts a CU
   if (N == 64)
-    hipLaunchKernelGGL((k_bwd_chunk<64, 2>), grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, di, hs,
+    hipLaunchKernelGGL((k_bwd_chunk<64, 2>), grid, dim3(512), 0, stream, xi, dt, A, bi, ci, D, di, hs,
                        gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else if (N == 128)
-    hipLaunchKernelGGL((k_bwd_chunk<128, 3>), grid, dim3(256), 0, stream, xi, dt, A, bi, ci, D, di, hs,
+    hipLaunchKernelGGL((k_bwd_chunk<128, 3>), grid, dim3(512), 0, stream, xi, dt, A, bi, ci, D, di, hs,
                        gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else
     return hipErrorInvalidValue;
