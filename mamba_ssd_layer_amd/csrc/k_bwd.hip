@@ -341,7 +341,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   auto tab_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OTAB + (b * 8 + wave) * F::TABW); };
   auto part_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OPART + b * F::PARTW); };
   enum { TA2 = 0, TF = 32, TW = 64, TDT = 96, TEL = 128 };  // tables: a_l log2(e), exp(a_l), w_s, dt_s, exp(a_last - a_s)
-  // partial sums: q_s [p-tile][s], v_l [p-tile][l], <g_e, h_s> [wavefront], column
+  // partial sums: q_s [p-tile][s], v_l [p-tile][l], <g_e, h_s> [p-tile], column
   // sums of E o Z o L [lt][s] (all l >= s) and of K [lt][s] (l > s), row sums
   // of K [st][l] (s < l), diagonal of E [s]
   enum { PQ = 0, PV = 128, PGH = 256, PC1 = 264, PCK = 328, PRK = 392, PDE = 456 };
@@ -409,8 +409,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   }
   const int LDW = F::LD + (wave == 0 ? 1 : 0);
   // stores and atomics a wavefront issues in iteration m: its dx tile of head
-  // m; wavefront 0 also ddt, dA, dD of head m - 1
-  auto stw = [&](int m) { return 1 + (wave == 0 && m >= 1 ? 2 + (dD ? 1 : 0) : 0); };
+  // m; wavefront 4 also ddt, dA, dD of head m - 1
+  auto stw = [&](int m) { return 1 + (wave == 4 && m >= 1 ? 2 + (dD ? 1 : 0) : 0); };
 #pragma unroll
   for (int jj = 0; jj < R - 1; ++jj)
     if (jj < hpg) issue_head(jj, jj);
@@ -435,8 +435,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     dCa[i] = f32x4{};
   }
 
-  // ---- per-token scalars of head jj (its partials complete): every
-  // wavefront computes them, wavefront 0 writes ddt and adds dA, dD ----
+  // ---- per-token scalars of head jj (its partials complete): computed by
+  // wavefronts 4-7 (one per SIMD, while 0-3 start the next head's heavier
+  // phase 1); wavefront 4 writes ddt and adds dA, dD ----
   auto finish = [&](int jj, float Ah, float alast) {
     const int h = g * hpg + jj;
     const float *tab = tab_of(jj & 1);
@@ -448,7 +449,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
       v += part[PV + 32 * w + tl];
     }
 #pragma unroll
-    for (int w = 0; w < 8; ++w) gh += part[PGH + w];
+    for (int w = 0; w < 4; ++w) gh += part[PGH + w];
     const float t1 = part[PC1 + tl] + part[PC1 + 32 + tl];
     const float ck = part[PCK + tl] + part[PCK + 32 + tl];
     const float rkr = part[PRK + tl] + part[PRK + 32 + tl];
@@ -466,7 +467,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     const bool ok = lane < 32 && tl <= last;
     const float da = lane31(scan32b(ok ? tab[TDT + tl] * (Rr + V + U) : 0.f));
     const float dsum = lane31(scan32b(ok ? part[PDE + tl] : 0.f));
-    if (wave == 0) {
+    if (wave == 4) {
       if (ok) ddt[(t0 + tl) * H + h] = dd;
       if (lane == 0) {
         atomicAdd(dA + h, da);
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
       __syncthreads();  // head j is in everywhere; head j-1 and its partials are done everywhere
     }
     if (j + R - 1 < hpg) issue_head(j + R - 1, (j + R - 1) % R);
-    if (j > 0) finish(j - 1, pAh, palast);
+    if (j > 0 && !etile) finish(j - 1, pAh, palast);
     const int pb = j & 1;
     float *tab = tab_of(pb);
     float *part = part_of(pb);
@@ -594,18 +595,30 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     // ---- phase 2 ----
     const float Dh = Dv ? Dv[h] : 0.f;
     {
+      // rows 16 pt + c16 of g_e and h_s (n = 32 q + 8 g4 + 0..7): the A
+      // operands of g_e B^T and h_s C^T, and together all of p-tile pt
+      u32x4 gr[KQ], hr[KQ];
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+        gr[q] = rown(gss, 16 * pt + c16, q);
+        hr[q] = rown(hss, 16 * pt + c16, q);
+      }
       // dx tile (p-tile pt, s-tile sh): dy^T M + w_s g_e B^T + D dy; q_s partial
       const u32x4 dyt = trn(ys, 128, 4 * g4, 16 + 4 * g4, 16 * pt, false);
       const u32x4 mop = *reinterpret_cast<const u32x4 *>(opm + sh * 1024 + lane * 16);
       f32x4 acc = mfma16b(dyt, mop, f32x4{});
-      f32x4 gb{};
+      f32x4 gb{}, hc{};
 #pragma unroll
-      for (int q = 0; q < KQ; ++q) gb = mfma16b(rown(gss, 16 * pt + c16, q), rown(bsm, 16 * sh + c16, q), gb);
-      // lane: column s, rows p = 16 pt + 4 g4 + r
+      for (int q = 0; q < KQ; ++q) {
+        gb = mfma16b(gr[q], rown(bsm, 16 * sh + c16, q), gb);
+        hc = mfma16b(hr[q], rown(csm, 16 * sh + c16, q), hc);
+      }
+      // lane: column s (or l) = 16 sh + c16, rows p = 16 pt + 4 g4 + r
       const int sx = 16 * sh + c16, col = 16 * pt + 4 * g4;
       const float ws = tab[TW + sx];
-      const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2);
-      const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2);
+      const int ro = sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2;
+      const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + ro);
+      const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + ro);
       const float o0 = acc.x + ws * gb.x + Dh * bf16lo(dv.x);
       const float o1 = acc.y + ws * gb.y + Dh * bf16hi(dv.x);
       const float o2 = acc.z + ws * gb.z + Dh * bf16lo(dv.y);
@@ -614,72 +627,70 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
         *reinterpret_cast<u32x2 *>(dx + (t0 + sx) * ldx + (int64_t)h * P + col) =
             u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
       float qv = bf16lo(xv.x) * gb.x + bf16hi(xv.x) * gb.y + bf16lo(xv.y) * gb.z + bf16hi(xv.y) * gb.w;
+      // v_l partial dy_l . (h_s C_l) (the same rows of dy: l = sx)
+      float vv = bf16lo(dv.x) * hc.x + bf16hi(dv.x) * hc.y + bf16lo(dv.y) * hc.z + bf16hi(dv.y) * hc.w;
       qv += __shfl_xor(qv, 16, 64);
       qv += __shfl_xor(qv, 32, 64);
-      if (lane < 16) part[PQ + 32 * pt + sx] = qv;
-    }
-    {
-      // h_s C^T tile (p-tile pt, l-tile sh): v_l partial dy_l . (h_s C_l)
-      f32x4 hc{};
-#pragma unroll
-      for (int q = 0; q < KQ; ++q) hc = mfma16b(rown(hss, 16 * pt + c16, q), rown(csm, 16 * sh + c16, q), hc);
-      const int lx = 16 * sh + c16, col = 16 * pt + 4 * g4;
-      const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + lx * 128 + (((col >> 3) ^ swz<8>(lx)) << 4) + (col & 7) * 2);
-      float vv = bf16lo(dv.x) * hc.x + bf16hi(dv.x) * hc.y + bf16lo(dv.y) * hc.z + bf16hi(dv.y) * hc.w;
       vv += __shfl_xor(vv, 16, 64);
       vv += __shfl_xor(vv, 32, 64);
-      if (lane < 16) part[PV + 32 * pt + lx] = vv;
+      if (lane < 16) {
+        part[PQ + 32 * pt + sx] = qv;
+        part[PV + 32 * pt + sx] = vv;
+      }
+      if (sh == 0) {  // <g_e, h_s> over p-tile pt, from the same registers
+        float gh = 0.f;
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+          const u32x4 a = gr[q], b = hr[q];
+          gh += bf16lo(a.x) * bf16lo(b.x) + bf16hi(a.x) * bf16hi(b.x) + bf16lo(a.y) * bf16lo(b.y) +
+                bf16hi(a.y) * bf16hi(b.y) + bf16lo(a.z) * bf16lo(b.z) + bf16hi(a.z) * bf16hi(b.z) +
+                bf16lo(a.w) * bf16lo(b.w) + bf16hi(a.w) * bf16hi(b.w);
+        }
+        gh = rowsum16(gh);
+        gh += __shfl_xor(gh, 16, 64);
+        gh += __shfl_xor(gh, 32, 64);
+        if (lane == 0) part[PGH + pt] = gh;
+      }
     }
     {
-      // <g_e, h_s> over rows p = 8 wave .. +7: lane takes 1/8 of a row
-      const int row = 8 * wave + (lane >> 3);
-      float acc = 0.f;
-#pragma unroll
-      for (int cj = 0; cj < NCB / 8; ++cj) {
-        const int off = row * (N * 2) + ((((lane & 7) * (NCB / 8) + cj) ^ swz<NCB>(row)) << 4);
-        const u32x4 gv = *reinterpret_cast<const u32x4 *>(gss + off);
-        const u32x4 hv = *reinterpret_cast<const u32x4 *>(hss + off);
-        acc += bf16lo(gv.x) * bf16lo(hv.x) + bf16hi(gv.x) * bf16hi(hv.x) + bf16lo(gv.y) * bf16lo(hv.y) +
-               bf16hi(gv.y) * bf16hi(hv.y) + bf16lo(gv.z) * bf16lo(hv.z) + bf16hi(gv.z) * bf16hi(hv.z) +
-               bf16lo(gv.w) * bf16lo(hv.w) + bf16hi(gv.w) * bf16hi(hv.w);
-      }
-      acc = rowsum16(acc);
-      acc += __shfl_xor(acc, 16, 64);
-      acc += __shfl_xor(acc, 32, 64);
-      if (lane == 0) part[PGH + wave] = acc;
-    }
-    // dB, dC tiles u = NTW wave + i: n-tile u / 2, s-tile (l-tile) u % 2
-#pragma unroll
-    for (int i = 0; i < NTW; ++i) {
-      const int u = NTW * wave + i, nt = u >> 1, t = u & 1;
+      // dB, dC tiles: n-tile nt, s-tiles (l-tiles) t0d .. t0d + NTW - 1
+      const int nt = (NTW * wave) >> 1, t0d = (NTW * wave) & 1;
       const u32x4 ct = trn(csm, N * 2, 4 * g4, 16 + 4 * g4, 16 * nt, true);
       const u32x4 bt = trn(bsm, N * 2, 4 * g4, 16 + 4 * g4, 16 * nt, true);
-      const u32x4 elop = *reinterpret_cast<const u32x4 *>(opel + t * 1024 + lane * 16);
-      const u32x4 eltop = *reinterpret_cast<const u32x4 *>(opelt + t * 1024 + lane * 16);
-      dBa[i] = mfma16b(ct, elop, dBa[i]);
-      dCa[i] = mfma16b(bt, eltop, dCa[i]);
-      f32x4 gx{}, hy{};
+      u32x4 gsT[2], hsT[2];  // g_e^T, h_s^T rows n = 16 nt + c16, K = p = 32 kq + 8 g4 + 0..7
 #pragma unroll
       for (int kq = 0; kq < 2; ++kq) {
-        const u32x4 gsT = trn(gss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
-        const u32x4 hsT = trn(hss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
-        gx = mfma16b(gsT, rowx(xs, 16 * t + c16, kq), gx);
-        hy = mfma16b(hsT, rowx(ys, 16 * t + c16, kq), hy);
+        gsT[kq] = trn(gss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
+        hsT[kq] = trn(hss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
       }
-      const float ws = tab[TW + 16 * t + c16], fl = tab[TF + 16 * t + c16];
-      dBa[i] += gx * ws;
-      dCa[i] += hy * fl;
+#pragma unroll
+      for (int i = 0; i < NTW; ++i) {
+        const int t = t0d + i;
+        const u32x4 elop = *reinterpret_cast<const u32x4 *>(opel + t * 1024 + lane * 16);
+        const u32x4 eltop = *reinterpret_cast<const u32x4 *>(opelt + t * 1024 + lane * 16);
+        dBa[i] = mfma16b(ct, elop, dBa[i]);
+        dCa[i] = mfma16b(bt, eltop, dCa[i]);
+        f32x4 gx{}, hy{};
+#pragma unroll
+        for (int kq = 0; kq < 2; ++kq) {
+          gx = mfma16b(gsT[kq], rowx(xs, 16 * t + c16, kq), gx);
+          hy = mfma16b(hsT[kq], rowx(ys, 16 * t + c16, kq), hy);
+        }
+        const float ws = tab[TW + 16 * t + c16], fl = tab[TF + 16 * t + c16];
+        dBa[i] += gx * ws;
+        dCa[i] += hy * fl;
+      }
     }
     pAh = Ah;
     palast = alast;
   }
   __syncthreads();  // the last head's partials are in everywhere
-  finish(hpg - 1, pAh, palast);
+  if (!etile) finish(hpg - 1, pAh, palast);
 
   // ---- dB, dC of the chunk's rows: lane column s, rows n = 16 nt + 4 g4 + r ----
 #pragma unroll
   for (int i = 0; i < NTW; ++i) {
-    const int u = NTW * wave + i, nt = u >> 1, t = u & 1;
+    const int nt = (NTW * wave) >> 1, t = ((NTW * wave) & 1) + i;
     const int sx = 16 * t + c16;
     if (sx <= last) {
       const int64_t off = (t0 + sx) * ldb + (int64_t)g * N + 16 * nt + 4 * g4;
