@@ -216,3 +216,68 @@ def test_unsupported_and_invalid():
             torch.empty(t["B"].shape, device=DEV), torch.empty(t["C"].shape, device=DEV),
             torch.empty(4, device=DEV), None, ssd.dims_for(t["x"], t["B"], None),
             torch.empty_like(st), st.numel())
+
+
+def seq_oracle(w, s, heads, dy, dfinal):
+    """The backward oracle on sequence s alone (its rows of every input), for
+    the given heads: the oracle's outputs are full-size arrays, so slicing keeps
+    them small at the packed workload's 275k tokens."""
+    a, b = int(w.seq_off[s]), int(w.seq_off[s + 1])
+    one = lambda arr: None if arr is None else arr[s:s + 1]
+    return oracle.recurrence_bwd(w.x[a:b], w.dt[a:b], w.A, w.B[a:b], w.C[a:b], w.D, one(w.h0),
+                                 np.array([0, b - a]), dy[a:b], one(dfinal),
+                                 pairs=[(0, h) for h in heads])
+
+
+def sampled_check(w, g, pairs, label, dy, dfinal, group_seq=None):
+    """dx, ddt, dinit on sampled (sequence, head) pairs; dB and dC on the rows
+    of sequence group_seq[0] for group group_seq[1] (all its heads)."""
+    got = host(g, w)
+    so = w.seq_off
+    num = {k: 0.0 for k in ("dx", "ddt", "dh0")}
+    den = dict(num)
+    for s in sorted({s for s, _ in pairs}):
+        heads = [h for s2, h in pairs if s2 == s]
+        ref = seq_oracle(w, s, heads, dy, dfinal)
+        a, b = so[s], so[s + 1]
+        for h in heads:
+            for name, gv, rv in (("dx", got["dx"][a:b, h], ref["dx"][:, h]),
+                                 ("ddt", got["ddt"][a:b, h], ref["ddt"][:, h]),
+                                 ("dh0", got["dh0"][s, h], ref["dh0"][0, h])):
+                if rv.size:
+                    num[name] = max(num[name], float(np.max(np.abs(gv - rv))))
+                    den[name] = max(den[name], float(np.max(np.abs(rv))))
+    errs = {k: num[k] / den[k] for k in num if den[k] > 0}
+    if group_seq is not None:
+        s, gr = group_seq
+        hpg = w.nheads // w.ngroups
+        ref1 = seq_oracle(w, s, range(gr * hpg, (gr + 1) * hpg), dy, dfinal)
+        a, b = so[s], so[s + 1]
+        errs["dB"] = rel(got["dB"][a:b, gr], ref1["dB"][:, gr])
+        errs["dC"] = rel(got["dC"][a:b, gr], ref1["dC"][:, gr])
+    say(f"  {label}: " + ", ".join(f"{k} {v:.2e}" for k, v in errs.items()))
+    for k, v in errs.items():
+        assert v <= TOLB, f"{label}: {k} rel err {v:.3e}"
+
+
+def test_varlen_workload_sampled():
+    # 64 packed sequences of lengths U[1, 8192] (275,772 tokens), H 64, G 8,
+    # nonzero initial states: sampled pairs, and dB / dC of one (sequence, group)
+    w = workloads.make_workload("varlen_bf16")
+    dy, dfinal = workloads.make_output_grads(w, 9)
+    t = upload(w)
+    _, _, _, g = fwd_bwd(w, t, dy, dfinal)
+    lens = np.diff(w.seq_off)
+    s_long = int(np.argmax(lens))
+    pairs = sorted({(0, 0), (63, 63), (s_long, 17), (int(np.argmin(lens)), 40), (20, 5), (41, 62)})
+    sampled_check(w, g, pairs, "bwd varlen_bf16 sampled", dy, dfinal, group_seq=(s_long, 3))
+
+
+def test_long_n64_sampled():
+    # one 65,536-token sequence, 80 heads, N 64: 2048 chunks swept backwards
+    w = workloads.make_workload("long_n64")
+    dy, dfinal = workloads.make_output_grads(w, 10)
+    t = upload(w)
+    _, _, _, g = fwd_bwd(w, t, dy, dfinal)
+    pairs = [(0, 0), (0, 33), (0, 79)]
+    sampled_check(w, g, pairs, "bwd long_n64 sampled", dy, dfinal)
