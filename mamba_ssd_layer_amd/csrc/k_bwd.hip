@@ -31,11 +31,11 @@
 //   2. k_bwd_reverse walks each (sequence, two heads) backwards, keeping g on
 //      chip like the forward keeps h (g <- exp(a_last) g + C^T (exp(a_l) dy)),
 //      saving g_e of every chunk and writing dL/dh0;
-//   3. k_bwd_chunk, one block per (chunk, group), walks the group's heads:
-//      the chunk's B and C stay in LDS, each head's x, dy, h_s and g_e stream
-//      through a two-slot LDS ring; dx and ddt are written per head, dB and dC
-//      accumulate over the heads in registers and are written once, dA and dD
-//      are added atomically per head.
+//   3. k_bwd_chunk, one block of 8 wavefronts per (chunk, group), walks the
+//      group's heads: the chunk's B and C stay in LDS, each head's x, dy, h_s
+//      and g_e stream through an LDS ring; dx and ddt are written per head, dB
+//      and dC accumulate over the heads in registers and are written once, dA
+//      and dD are added atomically per head.
 #include "ssd_device.hpp"
 #include "ssd_launch.hpp"
 
@@ -78,7 +78,10 @@ __device__ __forceinline__ void wsync() {
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
-// chunk swizzle of an LDS tile row of NC 16-byte chunks (as the forward's)
+// XOR swizzle of the 16-byte chunk index of an LDS tile row of NC chunks by
+// the row (a bit-pair rotation of the row's low bits), so that 16 lanes
+// reading one chunk column of consecutive rows, and the transposing reads of
+// 4 rows, spread over the LDS banks
 template <int NC>
 __device__ __forceinline__ int swz(int r) {
   return NC == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
