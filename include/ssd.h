@@ -250,14 +250,15 @@ ssd_status ssd_fused_fwd(const void *x, const float *dt, const float *A, const v
                          const ssd_dims *dims, void *stream);
 
 /* ssd_fused_fwd that also saves, for the backward pass, the state entering
- * every 32-token chunk (the inter-chunk states of page "Mamba-2 Architecture:
- * State Space Duality Explained", "2. The Chunked SSD Algorithm", item 3),
- * rounded to bf16:
- *   chunk_states  device bf16 [nchunks][H][P][N], 16-byte aligned, not
- *                 overlapping any other argument; chunk c = the sequence-major
- *                 index of the 32-token chunk (sequence s's chunks start at
- *                 the sum of ceil(len_i / 32) over i < s); NULL: nothing saved
- *                 (then this is ssd_fused_fwd);
+ * every 64-token pair of chunks (the inter-chunk states of page "Mamba-2
+ * Architecture: State Space Duality Explained", "2. The Chunked SSD
+ * Algorithm", item 3, kept at every other 32-token chunk), rounded to bf16:
+ *   chunk_states  device bf16 [npairs][H][P][N], 16-byte aligned, not
+ *                 overlapping any other argument; pair b = the sequence-major
+ *                 index of the 64-token pair (sequence s's pairs start at the
+ *                 sum of ceil(len_i / 64) over i < s), holding the state
+ *                 before the pair's first token; NULL: nothing saved (then
+ *                 this is ssd_fused_fwd);
  *   states_bytes  its size, at least ssd_fused_states_size(dims), else
  *                 SSD_ERR_WORKSPACE.
  * Everything else as ssd_fused_fwd.  Returns after enqueueing. */
@@ -267,13 +268,13 @@ ssd_status ssd_fused_fwd_train(const void *x, const float *dt, const float *A, c
                                void *chunk_states, size_t states_bytes, const ssd_dims *dims,
                                void *stream);
 
-/* Bytes of ssd_fused_fwd_train's chunk_states for these dims (nchunks =
- * batch * ceil(seqlen / 32), or ceil(T / 32) + nseq for packed sequences);
+/* Bytes of ssd_fused_fwd_train's chunk_states for these dims (npairs =
+ * batch * ceil(seqlen / 64), or ceil(T / 64) + nseq for packed sequences);
  * 0 if the dims are invalid or outside ssd_fused_fwd's shapes.  Host-only. */
 size_t ssd_fused_states_size(const ssd_dims *dims);
 
 /* Workspace bytes of ssd_fused_bwd (the gradient w.r.t. the state leaving
- * every chunk, bf16, laid out like chunk_states).  Host-only. */
+ * every 64-token pair, bf16, laid out like chunk_states).  Host-only. */
 size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
 
 /* Gradients of the forward.  The pages give the recurrence h_t = exp(dt_t A)

@@ -121,7 +121,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
   int64_t tb, len;
   seq_range(cu, s, L, T, tb, len);
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
-  const int64_t cbase = chunk_base32(cu, s, L, T);
+  const int64_t pbase = pair_base64(cu, s, L, T);
   const int64_t sh = (int64_t)s * H + h;
   const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
   const float Ah = A[h];
@@ -165,16 +165,18 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     const int k = nck - 1 - i;
     // chunk k's loads have landed once at most the later ops are pending
     // (completion in issue order): the state-gradient stores of iterations
-    // i-2 and i-1 (SV each) and the loads of chunk k-1 (LDR)
-    wait_vmcnt_dyn((i >= 2 ? SV : 0) + (i + 1 < nck ? LDR : 0) + (i >= 1 ? SV : 0));
+    // i-2 and i-1 (SV each where one is stored) and the loads of chunk k-1 (LDR)
+    auto sv = [&](int m) { return ((nck - 1 - m) & 1) || m == 0 ? SV : 0; };
+    wait_vmcnt_dyn((i >= 2 ? sv(i - 2) : 0) + (i + 1 < nck ? LDR : 0) + (i >= 1 ? sv(i - 1) : 0));
     __syncthreads();
     const int slp = sl == 0 ? 2 : sl - 1;
     if (k - 2 >= 0) issue(k - 2, slp);
-    // the gradient flowing into chunk k from the later chunks
-    {
+    // the gradient flowing into chunk k from the later chunks, kept where it
+    // leaves a 64-token pair (k odd, or the sequence's last chunk)
+    if ((k & 1) || k == nck - 1) {
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        uint16_t *dst = gsave + ((cbase + k) * H + h) * (int64_t)(P * N) +
+        uint16_t *dst = gsave + ((pbase + (k >> 1)) * H + h) * (int64_t)(P * N) +
                         (int64_t)(32 * ph + 16 * pt + c16) * N + 8 * g4;
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
@@ -268,19 +270,23 @@ struct BwdCfg {
   static constexpr int P = 64, CQ = 32, NCB = N / 8, WAVES = 8;
   static constexpr int XT = CQ * P * 2;      // x or dy of a head: 32 rows x 128 B
   static constexpr int ST = P * N * 2;       // h_s or g_e of a head: 64 rows x N bf16
-  static constexpr int BT = CQ * N * 2;      // B or C of the chunk
+  static constexpr int BT = CQ * N * 2;      // B or C of a chunk
+  // a ring slot: x, dy, h_s, g_e, dt of the chunk; x or dy, dt of the neighbour chunk
   static constexpr int OX = 0, OY = XT, OH = 2 * XT, OG = OH + ST, ODT = OG + ST;
-  static constexpr int HSLOT = ODT + 256;
+  static constexpr int ONX = ODT + 256, ONDT = ONX + XT;
+  static constexpr int HSLOT = ONDT + 256;
   static constexpr int OB = R * HSLOT, OCC = OB + BT;   // R ring slots of a head's tiles
-  static constexpr int OOP = OCC + BT;                   // operands M, EL, ELT: [2][64 lanes][16 B] each
-  static constexpr int OTAB = OOP + 3 * 2048;            // per wavefront and buffer: 5 tables of 32 floats
-  static constexpr int TABW = 5 * CQ * 4;
+  static constexpr int ONBC = OCC + BT;                  // B or C of the neighbour chunk
+  static constexpr int OOP = ONBC + BT;                  // operands M, EL, ELT: [2][64 lanes][16 B] each
+  static constexpr int OTAB = OOP + 3 * 2048;            // per wavefront and buffer: 6 tables of 32 floats
+  static constexpr int TABW = 6 * CQ * 4;
   static constexpr int OPART = OTAB + 2 * WAVES * TABW;  // per buffer: the partial sums below
   static constexpr int PARTW = 512 * 4;
   static constexpr int TOTAL = OPART + 2 * PARTW;
   static constexpr int KP = ST / 1024 / WAVES;           // h_s (and g_e) pieces per wavefront
   static constexpr int LD = 1 + 2 * KP;                  // vector-memory ops a wavefront issues per head (+1: dt)
   static constexpr int NTW = N / 64;                     // tiles of dB (and dC) per wavefront
+  static constexpr int DTW = N / 32;                     // tiles of the derived state per wavefront
   static_assert(KP >= 1 && KP * WAVES * 1024 == ST, "state pieces");
   static_assert(TOTAL <= 160 * 1024, "LDS");
 };
@@ -302,9 +308,10 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   const int64_t c = blockIdx.x / G;
   const int g = static_cast<int>(blockIdx.x % G);
   if (c >= nchunks) return;
-  // chunk c of the sequence-major list -> (sequence, chunk within it)
+  // chunk c of the sequence-major list -> (sequence, chunk within it), and the
+  // index of the sequence's first 64-token pair (the saved states' layout)
   int s = -1;
-  int64_t k = 0, tb = 0, len = 0;
+  int64_t k = 0, tb = 0, len = 0, pb0 = 0;
   if (!cu) {
     const int64_t nckr = (L + CQ - 1) / CQ;
     if (nckr == 0) return;
@@ -312,8 +319,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     k = c % nckr;
     if (s >= rows) return;
     seq_range(cu, s, L, T, tb, len);
+    pb0 = (int64_t)s * ((L + 63) / 64);
   } else {
-    int64_t acc = 0;
+    int64_t acc = 0, pacc = 0;
     for (int i = 0; i < rows; ++i) {
       int64_t b, l;
       seq_range(cu, i, L, T, b, l);
@@ -323,12 +331,24 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
         k = c - acc;
         tb = b;
         len = l;
+        pb0 = pacc;
         break;
       }
       acc += n;
+      pacc += (l + 63) / 64;
     }
     if (s < 0) return;
   }
+  // The saved states are kept per 64-token pair of chunks: h_s entering the
+  // pair, g_e leaving it.  An even chunk reads its h_s; its g_e is derived
+  // from the pair's and the next chunk (unless it ends the sequence); an odd
+  // chunk reads its g_e and derives h_s from the pair's and the chunk before.
+  enum { NONE = 0, DG = 1, DH = 2 };
+  const int nck = static_cast<int>((len + CQ - 1) / CQ);
+  const int mode = (k & 1) ? DH : (k + 1 < nck ? DG : NONE);
+  const int64_t pidx = pb0 + (k >> 1);
+  const int64_t tn0 = tb + (k + (mode == DG ? 1 : -1)) * CQ;  // the neighbour chunk's first token
+  const int lastn = mode == NONE ? 0 : static_cast<int>(min((int64_t)CQ, tb + len - tn0)) - 1;
   const int64_t t0 = tb + k * CQ;
   const int last = static_cast<int>(min((int64_t)CQ, len - k * CQ)) - 1;
   const bool full = last == CQ - 1;
@@ -343,7 +363,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   unsigned char *opm = smem + F::OOP, *opel = opm + 2048, *opelt = opm + 4096;
   auto tab_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OTAB + (b * 8 + wave) * F::TABW); };
   auto part_of = [&](int b) { return reinterpret_cast<float *>(smem + F::OPART + b * F::PARTW); };
-  enum { TA2 = 0, TF = 32, TW = 64, TDT = 96, TEL = 128 };  // tables: a_l log2(e), exp(a_l), w_s, dt_s, exp(a_last - a_s)
+  // tables: a_l log2(e), exp(a_l), w_s, dt_s, exp(a_last - a_s), and the
+  // neighbour chunk's token factors (w'_s for h_s, exp(a'_l) for g_e)
+  enum { TA2 = 0, TF = 32, TW = 64, TDT = 96, TEL = 128, TNW = 160 };
   // partial sums: q_s [p-tile][s], v_l [p-tile][l], <g_e, h_s> [p-tile], column
   // sums of E o Z o L [lt][s] (all l >= s) and of K [lt][s] (l > s), row sums
   // of K [st][l] (s < l), diagonal of E [s]
@@ -375,13 +397,15 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   // x (wavefronts 0-3) or dy (4-7) piece wave % 4 (rows 8 (wave % 4) .. +7,
   // clamped to the chunk's end); h_s and g_e pieces wave + 8 k (the swizzle
   // repeats every 16 rows, so piece k's offsets are piece 0's plus 8 KB k); dt.
-  uint32_t xoff, hoff, dtoff;
+  uint32_t xoff, hoff, dtoff, nxoff, ndtoff;
   {
     const int m = (wave & 3) * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz<8>(r);
     xoff = static_cast<uint32_t>((min(r, last) * ldx + 8 * cc) * 2);
     const int mh = wave * 64 + lane, rh = mh / NCB, ch = (mh % NCB) ^ swz<NCB>(rh);
     hoff = static_cast<uint32_t>((rh * N + 8 * ch) * 2);
     dtoff = static_cast<uint32_t>(min(tl, last) * H * 4);
+    nxoff = static_cast<uint32_t>((min(r, lastn) * ldx + 8 * cc) * 2);
+    ndtoff = static_cast<uint32_t>(min(tl, lastn) * H * 4);
   }
   // head j's x, dy, h_s, g_e and dt into ring slot sl: scalar bases, fixed lane offsets
   auto issue_head = [&](int j, int sl) {
@@ -389,7 +413,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     const uint32_t base = lbase + sl * F::HSLOT;
     dma_lds16_sb(xoff, (wave < 4 ? x : dy) + t0 * ldx + (int64_t)h * P,
                  base + (wave < 4 ? F::OX : F::OY) + (wave & 3) * 1024);
-    const int64_t st0 = (c * H + h) * (int64_t)(P * N);
+    const int64_t st0 = (pidx * H + h) * (int64_t)(P * N);
 #pragma unroll
     for (int kk = 0; kk < KP; ++kk)
       dma_lds16_sb(hoff, hsave + st0 + 4096 * kk, base + F::OH + (wave + 8 * kk) * 1024);
@@ -397,6 +421,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     for (int kk = 0; kk < KP; ++kk)
       dma_lds16_sb(hoff, gsave + st0 + 4096 * kk, base + F::OG + (wave + 8 * kk) * 1024);
     if (wave == 0) dma_lds4_sb(dtoff, dt + t0 * H + h, base + F::ODT);
+    if (mode != NONE) {  // the neighbour chunk's x (for h_s) or dy (for g_e), and dt
+      if (wave < 4)
+        dma_lds16_sb(nxoff, (mode == DH ? x : dy) + tn0 * ldx + (int64_t)h * P,
+                     base + F::ONX + wave * 1024);
+      if (wave == 1) dma_lds4_sb(ndtoff, dt + tn0 * H + h, base + F::ONDT);
+    }
   };
 
   // ---- the chunk's B and C, then heads 0 .. R-2 ahead ----
@@ -409,8 +439,15 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
       dma_lds16((tile ? Cm : Bm) + (t0 + min(r, last)) * ldb + (int64_t)g * N + 8 * cc,
                 lbase + (tile ? F::OCC : F::OB) + pi * 1024);
     }
+    // the neighbour chunk's B (for h_s) or C (for g_e)
+    if (mode != NONE && wave < F::BT / 1024) {
+      const int m = wave * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz<NCB>(r);
+      dma_lds16((mode == DH ? Bm : Cm) + (tn0 + min(r, lastn)) * ldb + (int64_t)g * N + 8 * cc,
+                lbase + F::ONBC + wave * 1024);
+    }
   }
-  const int LDW = F::LD + (wave == 0 ? 1 : 0);
+  const int LDW = F::LD + (wave == 0 ? 1 : 0) +
+                  (mode != NONE ? (wave < 4 ? 1 : 0) + (wave == 1 ? 1 : 0) : 0);
   // stores and atomics a wavefront issues in iteration m: its dx tile of head
   // m; wavefront 4 also ddt, dA, dD of head m - 1
   auto stw = [&](int m) { return 1 + (wave == 4 && m >= 1 ? 2 + (dD ? 1 : 0) : 0); };
@@ -533,6 +570,18 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
       tab[TDT + tl] = dtv;
       tab[TEL + tl] = exp2b((alast - a) * kLog2eB);
     }
+    // the neighbour chunk's cumulative decay a' and its token factors
+    float enl = 0.f;  // exp(a'_last)
+    if (mode != NONE) {
+      const float *ndts = reinterpret_cast<const float *>(hsl + F::ONDT);
+      const float dtn = tl <= lastn ? ndts[tl] : 0.f;
+      const float an = scan32b(dtn * Ah);
+      const float anl = lane31(an);
+      enl = exp2b(anl * kLog2eB);
+      if (lane < 32)
+        tab[TNW + tl] = mode == DH ? exp2b((anl - an) * kLog2eB) * dtn
+                                   : (tl <= lastn ? exp2b(an * kLog2eB) : 0.f);
+    }
     wsync();
 
     // ---- phase 1: one tile of the masked products per wavefront ----
@@ -593,7 +642,35 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
       *reinterpret_cast<u32x2 *>(opelt + qb * 1024 + lane * 16 + qa * 8) =
           u32x2{pack_bf16x2(ev[0], ev[1]), pack_bf16x2(ev[2], ev[3])};
     }
-    __syncthreads();  // the head's operands and sums of phase 1 are in LDS
+    if (mode != NONE) {
+      // the derived state, in place over the loaded one: h_s = exp(a'_last)
+      // h_s' + B'^T (w' x') (the chunk before), or g_e = exp(a'_last) g_e' +
+      // C'^T (exp(a') dy') (the chunk after); tiles (p-tile, n-tile nd) with
+      // lane (c16 = p, g4) holding n = 16 nd + 4 g4 + 0..3
+      unsigned char *stile = mode == DH ? hsl + F::OH : hsl + F::OG;
+      const unsigned char *ntile = hsl + F::ONX;
+      const unsigned char *nbc = smem + F::ONBC;
+      const int nd = (F::DTW * wave) >> 2, pt0 = (F::DTW * wave) & 3;
+      const u32x4 aop = trn(nbc, N * 2, 4 * g4, 16 + 4 * g4, 16 * nd, true);
+      const f32x4 f0 = *reinterpret_cast<const f32x4 *>(tab + TNW + 4 * g4);
+      const f32x4 f1 = *reinterpret_cast<const f32x4 *>(tab + TNW + 16 + 4 * g4);
+#pragma unroll
+      for (int i = 0; i < F::DTW; ++i) {
+        const int ptd = pt0 + i;
+        const u32x4 t = trn(ntile, 128, 4 * g4, 16 + 4 * g4, 16 * ptd, false);
+        const u32x4 bop{pack_bf16x2(bf16lo(t.x) * f0.x, bf16hi(t.x) * f0.y),
+                        pack_bf16x2(bf16lo(t.y) * f0.z, bf16hi(t.y) * f0.w),
+                        pack_bf16x2(bf16lo(t.z) * f1.x, bf16hi(t.z) * f1.y),
+                        pack_bf16x2(bf16lo(t.w) * f1.z, bf16hi(t.w) * f1.w)};
+        const f32x4 d = mfma16b(aop, bop, f32x4{});
+        const int p = 16 * ptd + c16, n = 16 * nd + 4 * g4;
+        u32x2 *dst = reinterpret_cast<u32x2 *>(stile + p * (N * 2) + (((n >> 3) ^ swz<NCB>(p)) << 4) + (n & 7) * 2);
+        const u32x2 o = *dst;
+        *dst = u32x2{pack_bf16x2(enl * bf16lo(o.x) + d.x, enl * bf16hi(o.x) + d.y),
+                     pack_bf16x2(enl * bf16lo(o.y) + d.z, enl * bf16hi(o.y) + d.w)};
+      }
+    }
+    __syncthreads();  // the head's operands, sums of phase 1 and derived state are in LDS
 
     // ---- phase 2 ----
     const float Dh = Dv ? Dv[h] : 0.f;
@@ -744,12 +821,12 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
   const uint16_t *hs = static_cast<const uint16_t *>(hsave);
   const uint16_t *gs = static_cast<const uint16_t *>(gsave);
   uint16_t *dxo = static_cast<uint16_t *>(dx);
-  // N 64: two slots; N 128: three slots (two heads in flight); one block of 8 wavefronts a CU
+  // two ring slots (one head in flight ahead); one block of 8 wavefronts a CU
   if (N == 64)
     hipLaunchKernelGGL((k_bwd_chunk<64, 2>), grid, dim3(512), 0, stream, xi, dt, A, bi, ci, D, di, hs,
                        gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else if (N == 128)
-    hipLaunchKernelGGL((k_bwd_chunk<128, 3>), grid, dim3(512), 0, stream, xi, dt, A, bi, ci, D, di, hs,
+    hipLaunchKernelGGL((k_bwd_chunk<128, 2>), grid, dim3(512), 0, stream, xi, dt, A, bi, ci, D, di, hs,
                        gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else
     return hipErrorInvalidValue;

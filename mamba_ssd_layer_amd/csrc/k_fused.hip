@@ -169,7 +169,7 @@ void k_ssd_fused(
       hst[pt][j] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + prow + nrow(j)) : f32x4{};
   }
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
-  const int64_t cbase = SAVE ? chunk_base32(cu, s, L, T) : 0;
+  const int64_t pbase = SAVE ? pair_base64(cu, s, L, T) : 0;
   // The registers hold S = h / 2^lam: the decay of a chunk goes into lam
   // (wave-uniform) instead of into 2 N/16 x 4 multiplies a lane; S is
   // rescaled only when lam drops below -32, or before a chunk whose own
@@ -261,19 +261,19 @@ void k_ssd_fused(
     // chunk k has landed once at most the ops this wavefront issued after its
     // loads are pending: loads of later chunks (prologue, then one chunk per
     // iteration) and the y stores of the iterations in between
-    // (and, when saving, the state stores of those iterations: SVC each)
+    // (and, when saving, the state stores of the even ones: SVC each)
     {
       int n = k < D ? (min(D, nck) - 1 - k) * LDC : 0;
       for (int j = k < D ? 0 : k - D + 1; j < k; ++j)
-        n += (SAVE ? SVC : 0) + (j >= 1 ? STC : 0) + (j + D < nck ? LDC : 0);
+        n += (SAVE && !(j & 1) ? SVC : 0) + (j >= 1 ? STC : 0) + (j + D < nck ? LDC : 0);
       wait_vmcnt_dyn(n);
     }
     __syncthreads();  // every wavefront's share of chunk k is in; chunk k-1 is done everywhere
-    if (SAVE) {  // the state at the chunk's start, h = S 2^lam, rounded to bf16
+    if (SAVE && !(k & 1)) {  // the state entering the 64-token pair, h = S 2^lam, rounded to bf16
       const float e = exp2_fast(lam);
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        uint16_t *dst = hsave + ((cbase + k) * H + h) * (int64_t)(P * N) +
+        uint16_t *dst = hsave + ((pbase + (k >> 1)) * H + h) * (int64_t)(P * N) +
                         (int64_t)(32 * ph + 16 * pt + c16) * N + 8 * g4;
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {

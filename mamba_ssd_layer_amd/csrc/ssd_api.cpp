@@ -409,8 +409,14 @@ int64_t chunks32(const Plan &p) {
   return g.packed ? ceil_div(g.tokens, 32) + g.nrows : g.nrows * ceil_div(g.L, 32);
 }
 
+// 64-token pairs of chunks (packed: an upper bound, ceil(T/64) + nseq)
+int64_t pairs64(const Plan &p) {
+  const ssd::Geometry &g = p.geo;
+  return g.packed ? ceil_div(g.tokens, 64) + g.nrows : g.nrows * ceil_div(g.L, 64);
+}
+
 size_t chunk_states_bytes(const Plan &p) {
-  return align_up((size_t)chunks32(p) * p.geo.H * p.geo.P * p.geo.N * 2);
+  return align_up((size_t)pairs64(p) * p.geo.H * p.geo.P * p.geo.N * 2);
 }
 
 }  // namespace

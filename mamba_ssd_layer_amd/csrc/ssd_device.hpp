@@ -217,15 +217,15 @@ __device__ __forceinline__ void seq_range(const int32_t *cu, int s, int64_t L, i
   }
 }
 
-// Index of sequence s's first 32-token chunk in the sequence-major list of
-// the batch's 32-token chunks (the layout of saved per-chunk states).
-__device__ inline int64_t chunk_base32(const int32_t *cu, int s, int64_t L, int64_t T) {
-  if (!cu) return (int64_t)s * ((L + 31) / 32);
+// Index of sequence s's first 64-token pair of chunks in the sequence-major
+// list of the batch's pairs (the layout of the saved per-pair states).
+__device__ inline int64_t pair_base64(const int32_t *cu, int s, int64_t L, int64_t T) {
+  if (!cu) return (int64_t)s * ((L + 63) / 64);
   int64_t acc = 0;
   for (int i = 0; i < s; ++i) {
     int64_t tb, len;
     seq_range(cu, i, L, T, tb, len);
-    acc += (len + 31) / 32;
+    acc += (len + 63) / 64;
   }
   return acc;
 }

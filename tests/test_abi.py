@@ -341,14 +341,14 @@ def test_fused_pointers_and_overlaps():
 
 # ------------------------------------------- ssd_fused_fwd_train, ssd_fused_bwd
 def test_fused_states_size():
-    # bf16 [nchunks][H][P][N], nchunks = batch * ceil(L / 32), rounded up to 256 bytes
+    # bf16 [npairs][H][P][N], npairs = batch * ceil(L / 64), rounded up to 256 bytes
     d = good()  # 2 x 512 tokens, H 4, P 64, N 64
-    assert L.ssd_fused_states_size(ctypes.byref(d)) == 2 * 16 * 4 * 64 * 64 * 2
+    assert L.ssd_fused_states_size(ctypes.byref(d)) == 2 * 8 * 4 * 64 * 64 * 2
     d = make_dims(3, 1000, 4, 64, 128, 2, 0, SSD_BF16)
-    assert L.ssd_fused_states_size(ctypes.byref(d)) == 3 * 32 * 4 * 64 * 128 * 2
-    dp = make_dims(1, 1000, 4, 64, 64, 2, 3, SSD_BF16)  # packed: ceil(T / 32) + nseq
-    assert L.ssd_fused_states_size(ctypes.byref(dp)) == (32 + 3) * 4 * 64 * 64 * 2
-    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(dp)) == (32 + 3) * 4 * 64 * 64 * 2
+    assert L.ssd_fused_states_size(ctypes.byref(d)) == 3 * 16 * 4 * 64 * 128 * 2
+    dp = make_dims(1, 1000, 4, 64, 64, 2, 3, SSD_BF16)  # packed: ceil(T / 64) + nseq
+    assert L.ssd_fused_states_size(ctypes.byref(dp)) == (16 + 3) * 4 * 64 * 64 * 2
+    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(dp)) == (16 + 3) * 4 * 64 * 64 * 2
     for mut in (dict(io_dtype=SSD_F32), dict(headdim=128), dict(ngroups=4)):
         d = good()
         for k, val in mut.items():

@@ -120,9 +120,9 @@ def test_long_memory(kind):
     full_case(w, 7, label=f"bwd {kind}")
 
 
-def test_saved_chunk_states_are_prefix_final_states():
-    # the state entering 32-token chunk k of a row is the oracle's final state
-    # of the row's first 32 k tokens (from the same initial state)
+def test_saved_states_are_prefix_final_states():
+    # the state entering 64-token pair b of a row is the oracle's final state
+    # of the row's first 64 b tokens (from the same initial state)
     w = workloads.make_custom(2, 200, 4, 64, 64, 2, 256, "bf16", seed=2800, init_std=0.3)
     t = upload(w)
     st = ssd.make_fused_states(t["x"], t["B"], t["cu"])
@@ -130,14 +130,14 @@ def test_saved_chunk_states_are_prefix_final_states():
                   chunk_states=st)
     torch.cuda.synchronize()
     H, P, N, L = w.nheads, w.headdim, w.dstate, w.seqlen
-    nck = (L + 31) // 32
-    hs = st.view(torch.bfloat16)[: w.batch * nck * H * P * N].float().cpu().numpy()
-    hs = hs.reshape(w.batch, nck, H, P, N)
+    npair = (L + 63) // 64
+    hs = st.view(torch.bfloat16)[: w.batch * npair * H * P * N].float().cpu().numpy()
+    hs = hs.reshape(w.batch, npair, H, P, N)
     worst = 0.0
     for b in range(w.batch):
         sl = slice(b * L, (b + 1) * L)
-        for k in range(nck):
-            n = 32 * k
+        for k in range(npair):
+            n = 64 * k
             if n == 0:
                 ref = w.h0[b].astype(np.float64)
             else:
@@ -145,7 +145,7 @@ def test_saved_chunk_states_are_prefix_final_states():
                                          w.C[sl][:n], w.D, w.h0[b:b + 1], np.array([0, n]))
                 ref = f[0]
             worst = max(worst, rel(hs[b, k], ref))
-    say(f"  saved chunk states: rel err {worst:.3e}")
+    say(f"  saved states: rel err {worst:.3e}")
     assert worst <= 1e-2
 
 
