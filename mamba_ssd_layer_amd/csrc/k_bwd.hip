@@ -651,17 +651,18 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
       const unsigned char *ntile = hsl + F::ONX;
       const unsigned char *nbc = smem + F::ONBC;
       const int nd = (F::DTW * wave) >> 2, pt0 = (F::DTW * wave) & 3;
-      const u32x4 aop = trn(nbc, N * 2, 4 * g4, 16 + 4 * g4, 16 * nd, true);
+      // B'^T (or C'^T) rows n, K = token s, scaled by the token factors once
+      const u32x4 t = trn(nbc, N * 2, 4 * g4, 16 + 4 * g4, 16 * nd, true);
       const f32x4 f0 = *reinterpret_cast<const f32x4 *>(tab + TNW + 4 * g4);
       const f32x4 f1 = *reinterpret_cast<const f32x4 *>(tab + TNW + 16 + 4 * g4);
+      const u32x4 aop{pack_bf16x2(bf16lo(t.x) * f0.x, bf16hi(t.x) * f0.y),
+                      pack_bf16x2(bf16lo(t.y) * f0.z, bf16hi(t.y) * f0.w),
+                      pack_bf16x2(bf16lo(t.z) * f1.x, bf16hi(t.z) * f1.y),
+                      pack_bf16x2(bf16lo(t.w) * f1.z, bf16hi(t.w) * f1.w)};
 #pragma unroll
       for (int i = 0; i < F::DTW; ++i) {
         const int ptd = pt0 + i;
-        const u32x4 t = trn(ntile, 128, 4 * g4, 16 + 4 * g4, 16 * ptd, false);
-        const u32x4 bop{pack_bf16x2(bf16lo(t.x) * f0.x, bf16hi(t.x) * f0.y),
-                        pack_bf16x2(bf16lo(t.y) * f0.z, bf16hi(t.y) * f0.w),
-                        pack_bf16x2(bf16lo(t.z) * f1.x, bf16hi(t.z) * f1.y),
-                        pack_bf16x2(bf16lo(t.w) * f1.z, bf16hi(t.w) * f1.w)};
+        const u32x4 bop = trn(ntile, 128, 4 * g4, 16 + 4 * g4, 16 * ptd, false);
         const f32x4 d = mfma16b(aop, bop, f32x4{});
         const int p = 16 * ptd + c16, n = 16 * nd + 4 * g4;
         u32x2 *dst = reinterpret_cast<u32x2 *>(stile + p * (N * 2) + (((n >> 3) ^ swz<NCB>(p)) << 4) + (n & 7) * 2);
