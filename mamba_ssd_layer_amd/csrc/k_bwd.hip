@@ -305,9 +305,15 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   constexpr int KQ = N / 32;  // K steps over n
   __shared__ __align__(16) unsigned char smem[F::TOTAL];
 
-  const int64_t c = blockIdx.x / G;
-  const int g = static_cast<int>(blockIdx.x % G);
-  if (c >= nchunks) return;
+  // XCD-aware order: block b runs on XCD b % 8, which takes a contiguous range
+  // of (chunk, group) indices, so the two chunks of a 64-token pair (which
+  // read the same saved tiles) run on one XCD at about the same time and the
+  // second read is served by its L2
+  const int64_t nblk = nchunks * G, per = (nblk + 7) / 8;
+  const int64_t lb = (int64_t)(blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (lb >= nblk) return;
+  const int64_t c = lb / G;
+  const int g = static_cast<int>(lb % G);
   // chunk c of the sequence-major list -> (sequence, chunk within it), and the
   // index of the sequence's first 64-token pair (the saved states' layout)
   int s = -1;
@@ -814,7 +820,7 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
                             int64_t nchunks, int H, int N, int G, void *dx, float *ddt, float *dA,
                             float *dB, float *dC, float *dD, hipStream_t stream) {
   if (nchunks == 0) return hipSuccess;
-  const dim3 grid(static_cast<unsigned>(nchunks * G));
+  const dim3 grid(static_cast<unsigned>((nchunks * G + 7) / 8 * 8));
   const uint16_t *xi = static_cast<const uint16_t *>(x);
   const uint16_t *bi = static_cast<const uint16_t *>(B);
   const uint16_t *ci = static_cast<const uint16_t *>(C);
