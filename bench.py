@@ -229,22 +229,24 @@ def block_neighbours(torch, ssd, dev, w, steps: int, warmup: int):
 
 
 def backward_bytes(w):
-    """Compulsory HBM bytes of the two backward kernels (bf16 io, Q = 32 chunks,
-    c = total 32-token chunks, S sequences; state tiles s P N bytes per chunk
-    and head):
-      k_bwd_reverse  dy, C, dt in; the state gradient entering every chunk out;
+    """Compulsory HBM bytes of the two backward kernels (bf16 io, s = 2; S
+    sequences; states kept per 64-token pair, p = the batch's pairs, one
+    s P N tile per pair and head):
+      k_bwd_reverse  dy, C, dt in; the state gradient leaving every pair out;
                      dfinal in and dinit out per sequence:
-                     s T H P + s T G N + 4 T H + s c H P N + 8 S H P N
-      k_bwd_chunk    x, dy, B, C, dt, saved states and state gradients in;
-                     dx, ddt, dB, dC (float) out:
-                     3 s T H P + 2 s T G N + 8 T H + 8 T G N + 2 s c H P N"""
+                     s T H P + s T G N + 4 T H + s p H P N + 8 S H P N
+      k_bwd_chunk    x, dy, B, C, dt, every pair's saved state and state
+                     gradient in; dx, ddt, dB, dC (float) out:
+                     3 s T H P + 2 s T G N + 8 T H + 8 T G N + 2 s p H P N
+    (the neighbour-chunk rows a block also reads, and the second read of a
+    pair's tiles, are re-reads the kernel arranges to hit L2)"""
     T, H, P, N, G = w.tokens, w.nheads, w.headdim, w.dstate, w.ngroups
     S = w.nsequences
     lens = [int(w.seq_off[i + 1] - w.seq_off[i]) for i in range(S)]
-    c = sum(-(-L // FUSED_CHUNK) for L in lens)
+    pr = sum(-(-L // 64) for L in lens)
     s = 2
-    rev = s * T * H * P + s * T * G * N + 4 * T * H + s * c * H * P * N + 8 * S * H * P * N
-    chk = 3 * s * T * H * P + 2 * s * T * G * N + 8 * T * H + 8 * T * G * N + 2 * s * c * H * P * N
+    rev = s * T * H * P + s * T * G * N + 4 * T * H + s * pr * H * P * N + 8 * S * H * P * N
+    chk = 3 * s * T * H * P + 2 * s * T * G * N + 8 * T * H + 8 * T * G * N + 2 * s * pr * H * P * N
     return rev, chk
 
 
