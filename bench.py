@@ -321,9 +321,9 @@ def main() -> int:
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build measures one GPU only; the SSD forward shards over "
-              "(sequence, head) with no exchange, and no multi-GPU run is part of it. "
-              "Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU only: libssd has no multi-GPU path (the SSD forward "
+              "shards over (sequence, head) with no exchange). Run with --gpus 1.",
+              file=sys.stderr)
         return 2
 
     import numpy as np
