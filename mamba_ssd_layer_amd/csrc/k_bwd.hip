@@ -247,6 +247,20 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
   }
 }
 
+// The chunk pass's LDS tiles use another XOR swizzle, chosen for its access
+// patterns: row reads of 16 consecutive rows (one chunk column), transposing
+// reads of 8 consecutive rows x 2 chunks per 32 lanes, and transposing reads
+// of rows {0..3, 8..11} (+ 4, + 32 k) x 2 chunks.  The pair of chunks {c, c^1}
+// a row maps to is set by chunk bits 1 and up, which take (16 chunks) the
+// row's bits 0-1 and bit 2 XOR bit 3, or (8 chunks, 128-byte rows whose banks
+// repeat every other row) its bit 1 and bit 2 XOR bit 3; chunk bit 0 takes
+// the row's bit 3.  Every pattern then touches distinct banks.
+template <int NC>
+__device__ __forceinline__ int swz2(int r) {
+  return NC == 16 ? ((((r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2)) << 1) | ((r >> 3) & 1))
+                  : (((((r >> 1) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1)) << 1) | ((r >> 3) & 1));
+}
+
 // ---------------------------------------------------------------- pass 3
 // Block = (32-token chunk, group), 8 wavefronts (two per SIMD), walking the
 // group's heads.  LDS: the chunk's B and C (rows = tokens); an R-slot ring per
@@ -380,11 +394,11 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   // ---- operand reads ----
   // 16 bytes of a token row of x / dy (8 chunks): p = 32 kq + 8 g4 + 0..7
   auto rowx = [&](const unsigned char *t, int row, int kq) {
-    return *reinterpret_cast<const u32x4 *>(t + row * 128 + (((4 * kq + g4) ^ swz<8>(row)) << 4));
+    return *reinterpret_cast<const u32x4 *>(t + row * 128 + (((4 * kq + g4) ^ swz2<8>(row)) << 4));
   };
   // 16 bytes of a row of an N-wide tile (B, C, h_s, g_e): n = 32 q + 8 g4 + 0..7
   auto rown = [&](const unsigned char *t, int row, int q) {
-    return *reinterpret_cast<const u32x4 *>(t + row * (N * 2) + (((4 * q + g4) ^ swz<NCB>(row)) << 4));
+    return *reinterpret_cast<const u32x4 *>(t + row * (N * 2) + (((4 * q + g4) ^ swz2<NCB>(row)) << 4));
   };
   // transposing read: lane (c16, g4) gets column col0 + c16 of rows r0 + 0..3
   // and r1 + 0..3 (r0, r1 per lane group)
@@ -393,7 +407,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
 #pragma unroll
     for (int hf = 0; hf < 2; ++hf) {
       const int row = (hf ? r1 : r0) + (c16 >> 2), col = col0 + 4 * (c16 & 3);
-      const int cc = (col >> 3) ^ (wide ? swz<NCB>(row) : swz<8>(row));
+      const int cc = (col >> 3) ^ (wide ? swz2<NCB>(row) : swz2<8>(row));
       v[hf] = lds_read_tr16(t + row * rb + (cc << 4) + (col & 7) * 2);
     }
     return u32x4{v[0].x, v[0].y, v[1].x, v[1].y};
@@ -405,9 +419,9 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   // repeats every 16 rows, so piece k's offsets are piece 0's plus 8 KB k); dt.
   uint32_t xoff, hoff, dtoff, nxoff, ndtoff;
   {
-    const int m = (wave & 3) * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz<8>(r);
+    const int m = (wave & 3) * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz2<8>(r);
     xoff = static_cast<uint32_t>((min(r, last) * ldx + 8 * cc) * 2);
-    const int mh = wave * 64 + lane, rh = mh / NCB, ch = (mh % NCB) ^ swz<NCB>(rh);
+    const int mh = wave * 64 + lane, rh = mh / NCB, ch = (mh % NCB) ^ swz2<NCB>(rh);
     hoff = static_cast<uint32_t>((rh * N + 8 * ch) * 2);
     dtoff = static_cast<uint32_t>(min(tl, last) * H * 4);
     nxoff = static_cast<uint32_t>((min(r, lastn) * ldx + 8 * cc) * 2);
@@ -441,13 +455,13 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
 #pragma unroll
     for (int i = 0; i < BCP; ++i) {
       const int u = wave * BCP + i, tile = u / (F::BT / 1024), pi = u % (F::BT / 1024);
-      const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz<NCB>(r);
+      const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz2<NCB>(r);
       dma_lds16((tile ? Cm : Bm) + (t0 + min(r, last)) * ldb + (int64_t)g * N + 8 * cc,
                 lbase + (tile ? F::OCC : F::OB) + pi * 1024);
     }
     // the neighbour chunk's B (for h_s) or C (for g_e)
     if (mode != NONE && wave < F::BT / 1024) {
-      const int m = wave * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz<NCB>(r);
+      const int m = wave * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz2<NCB>(r);
       dma_lds16((mode == DH ? Bm : Cm) + (tn0 + min(r, lastn)) * ldb + (int64_t)g * N + 8 * cc,
                 lbase + F::ONBC + wave * 1024);
     }
@@ -671,7 +685,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
         const u32x4 bop = trn(ntile, 128, 4 * g4, 16 + 4 * g4, 16 * ptd, false);
         const f32x4 d = mfma16b(aop, bop, f32x4{});
         const int p = 16 * ptd + c16, n = 16 * nd + 4 * g4;
-        u32x2 *dst = reinterpret_cast<u32x2 *>(stile + p * (N * 2) + (((n >> 3) ^ swz<NCB>(p)) << 4) + (n & 7) * 2);
+        u32x2 *dst = reinterpret_cast<u32x2 *>(stile + p * (N * 2) + (((n >> 3) ^ swz2<NCB>(p)) << 4) + (n & 7) * 2);
         const u32x2 o = *dst;
         *dst = u32x2{pack_bf16x2(enl * bf16lo(o.x) + d.x, enl * bf16hi(o.x) + d.y),
                      pack_bf16x2(enl * bf16lo(o.y) + d.z, enl * bf16hi(o.y) + d.w)};
@@ -703,7 +717,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
       // lane: column s (or l) = 16 sh + c16, rows p = 16 pt + 4 g4 + r
       const int sx = 16 * sh + c16, col = 16 * pt + 4 * g4;
       const float ws = tab[TW + sx];
-      const int ro = sx * 128 + (((col >> 3) ^ swz<8>(sx)) << 4) + (col & 7) * 2;
+      const int ro = sx * 128 + (((col >> 3) ^ swz2<8>(sx)) << 4) + (col & 7) * 2;
       const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + ro);
       const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + ro);
       const float o0 = acc.x + ws * gb.x + Dh * bf16lo(dv.x);
