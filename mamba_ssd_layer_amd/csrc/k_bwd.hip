@@ -87,6 +87,20 @@ __device__ __forceinline__ int swz(int r) {
   return NC == 16 ? (((r & 3) << 2) | ((r >> 2) & 3)) : ((((r >> 1) & 1) << 2) | ((r >> 2) & 3));
 }
 
+// A second XOR swizzle, chosen for the access patterns of the x / dy tiles
+// (both passes) and the chunk pass's other tiles: row reads of 16 consecutive rows (one chunk column), transposing
+// reads of 8 consecutive rows x 2 chunks per 32 lanes, and transposing reads
+// of rows {0..3, 8..11} (+ 4, + 32 k) x 2 chunks.  The pair of chunks {c, c^1}
+// a row maps to is set by chunk bits 1 and up, which take (16 chunks) the
+// row's bits 0-1 and bit 2 XOR bit 3, or (8 chunks, 128-byte rows whose banks
+// repeat every other row) its bit 1 and bit 2 XOR bit 3; chunk bit 0 takes
+// the row's bit 3.  Every pattern then touches distinct banks.
+template <int NC>
+__device__ __forceinline__ int swz2(int r) {
+  return NC == 16 ? ((((r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2)) << 1) | ((r >> 3) & 1))
+                  : (((((r >> 1) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1)) << 1) | ((r >> 3) & 1));
+}
+
 // ---------------------------------------------------------------- pass 2
 // Block = (sequence, two heads of a group), 4 wavefronts (head hh, half ph);
 // wavefront (hh, ph) keeps rows p in [32 ph, 32 ph + 32) of head hh's g, held
@@ -143,7 +157,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     const uint32_t base = lds_off(smem) + sl * SLOT;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {  // rows 16 ph .. +15 of head hh's dy
-      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = (m & 7) ^ swz<8>(r);
+      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = (m & 7) ^ swz2<8>(r);
       dma_lds16(dy + (t0 + min(r, last)) * ldx + (int64_t)h * P + 8 * cc,
                 base + OY + hh * XH + 16 * ph * 128 + i * 1024);
     }
@@ -210,7 +224,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
 #pragma unroll
         for (int hf = 0; hf < 2; ++hf) {
           const int row = 16 * hf + 4 * g4 + (c16 >> 2), col = 32 * ph + 16 * pt + 4 * (c16 & 3);
-          const int cc = (col >> 3) ^ swz<8>(row);
+          const int cc = (col >> 3) ^ swz2<8>(row);
           t[hf] = lds_read_tr16(ys + row * 128 + (cc << 4) + (col & 7) * 2);
         }
         fy[pt] = u32x4{pack_bf16x2(bf16lo(t[0].x) * f0.x, bf16hi(t[0].x) * f0.y),
@@ -245,20 +259,6 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
       for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(dinit + prow + nrow(j)) = gst[pt][j];
     }
   }
-}
-
-// The chunk pass's LDS tiles use another XOR swizzle, chosen for its access
-// patterns: row reads of 16 consecutive rows (one chunk column), transposing
-// reads of 8 consecutive rows x 2 chunks per 32 lanes, and transposing reads
-// of rows {0..3, 8..11} (+ 4, + 32 k) x 2 chunks.  The pair of chunks {c, c^1}
-// a row maps to is set by chunk bits 1 and up, which take (16 chunks) the
-// row's bits 0-1 and bit 2 XOR bit 3, or (8 chunks, 128-byte rows whose banks
-// repeat every other row) its bit 1 and bit 2 XOR bit 3; chunk bit 0 takes
-// the row's bit 3.  Every pattern then touches distinct banks.
-template <int NC>
-__device__ __forceinline__ int swz2(int r) {
-  return NC == 16 ? ((((r & 3) | ((((r >> 2) ^ (r >> 3)) & 1) << 2)) << 1) | ((r >> 3) & 1))
-                  : (((((r >> 1) & 1) | ((((r >> 2) ^ (r >> 3)) & 1) << 1)) << 1) | ((r >> 3) & 1));
 }
 
 // ---------------------------------------------------------------- pass 3
