@@ -738,15 +738,13 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
         part[PQ + 32 * pt + sx] = qv;
         part[PV + 32 * pt + sx] = vv;
       }
-      if (sh == 0) {  // <g_e, h_s> over p-tile pt, from the same registers
-        float gh = 0.f;
+      if (sh == 0) {  // <g_e, h_s> over p-tile pt: the trace of (g_e h_s^T) on that tile
+        f32x4 gh4{};
 #pragma unroll
-        for (int q = 0; q < KQ; ++q) {
-          const u32x4 a = gr[q], b = hr[q];
-          gh += bf16lo(a.x) * bf16lo(b.x) + bf16hi(a.x) * bf16hi(b.x) + bf16lo(a.y) * bf16lo(b.y) +
-                bf16hi(a.y) * bf16hi(b.y) + bf16lo(a.z) * bf16lo(b.z) + bf16hi(a.z) * bf16hi(b.z) +
-                bf16lo(a.w) * bf16lo(b.w) + bf16hi(a.w) * bf16hi(b.w);
-        }
+        for (int q = 0; q < KQ; ++q) gh4 = mfma16b(gr[q], hr[q], gh4);
+        // lane (c16, g4) holds rows 4 g4 + r of column c16: the diagonal where 4 g4 + r = c16
+        const int r = c16 - 4 * g4;
+        float gh = r == 0 ? gh4.x : r == 1 ? gh4.y : r == 2 ? gh4.z : r == 3 ? gh4.w : 0.f;
         gh = rowsum16(gh);
         gh += __shfl_xor(gh, 16, 64);
         gh += __shfl_xor(gh, 32, 64);
