@@ -102,17 +102,26 @@ __device__ __forceinline__ int swz2(int r) {
 }
 
 // ---------------------------------------------------------------- pass 2
-// Block = (sequence, two heads of a group), 4 wavefronts (head hh, half ph);
-// wavefront (hh, ph) keeps rows p in [32 ph, 32 ph + 32) of head hh's g, held
-// transposed like the forward's state (tiles 2q, 2q+1 give lane group g4 the
-// n = 32q + 8 g4 + 0..7).  Chunks in reverse order through a three-slot ring
-// of dy (per head), C and dt.
-template <int N>
+// Block = (sequence or 256-token segment of one, two heads of a group), 4
+// wavefronts (head hh, half ph); wavefront (hh, ph) keeps rows p in
+// [32 ph, 32 ph + 32) of head hh's g, held transposed like the forward's state
+// (tiles 2q, 2q+1 give lane group g4 the n = 32q + 8 g4 + 0..7).  Chunks in
+// reverse order through a three-slot ring of dy (per head), C and dt.
+// MODE: RV_FULL walks a whole sequence from dfinal, saves g where each 64-token
+// pair ends and writes dL/dh0; for few (sequence, head-pair) blocks the sweep is
+// split into 256-token segments: RV_SEGSUM walks a segment from g = 0 and writes
+// its sum G_seg and its total decay (log) A_seg, k_bwd_gpass chains them, and
+// RV_SEG walks each segment again from the gradient entering it from the
+// right (gin) and saves g at its pair ends.
+enum { RV_FULL = 0, RV_SEGSUM = 1, RV_SEG = 2 };
+constexpr int kSegChunks = 8;  // 32-token chunks per segment
+
+template <int N, int MODE>
 __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     const uint16_t *__restrict__ dy, const float *__restrict__ dt, const float *__restrict__ A,
-    const uint16_t *__restrict__ Cm, const float *__restrict__ dfinal,
+    const uint16_t *__restrict__ Cm, const float *__restrict__ gstart,
     const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows, int H, int G,
-    uint16_t *__restrict__ gsave, float *__restrict__ dinit) {
+    uint16_t *__restrict__ gsave, float *__restrict__ gout, float *__restrict__ aseg) {
   constexpr int P = 64, CQ = 32, R = 3;
   constexpr int NT = N / 16, KQ = N / 32, NCB = N / 8;
   constexpr int XH = CQ * P * 2, BT = CQ * N * 2, DW = 256;
@@ -124,31 +133,70 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
   constexpr int SV = 2 * KQ;        // state-gradient stores a wavefront issues per chunk
   __shared__ __align__(16) unsigned char smem[AD + 4 * ADW];
 
-  int s, hb;
-  xcd_chunk_head(H / 2, s, hb);
-  if (s >= rows) return;
+  int s = -1, hb;
+  int64_t tb = 0, len = 0, gs = 0;  // gs: the segment's index in the batch's segment list
+  int kb = 0, ke = 0;               // the block's chunks [kb, ke) of its sequence
+  if (MODE == RV_FULL) {
+    xcd_chunk_head(H / 2, s, hb);
+    if (s >= rows) return;
+    seq_range(cu, s, L, T, tb, len);
+    ke = static_cast<int>((len + CQ - 1) / CQ);
+  } else {
+    int gsi;
+    xcd_chunk_head(H / 2, gsi, hb);
+    gs = gsi;
+    int64_t seg = -1;
+    if (!cu) {
+      const int64_t nsr = (L + kSegChunks * CQ - 1) / (kSegChunks * CQ);
+      if (nsr == 0) return;
+      s = static_cast<int>(gs / nsr);
+      seg = gs % nsr;
+      if (s >= rows) return;
+      seq_range(cu, s, L, T, tb, len);
+    } else {
+      int64_t acc = 0;
+      for (int i = 0; i < rows; ++i) {
+        int64_t b, l;
+        seq_range(cu, i, L, T, b, l);
+        const int64_t n = (l + kSegChunks * CQ - 1) / (kSegChunks * CQ);
+        if (gs < acc + n) {
+          s = i;
+          seg = gs - acc;
+          tb = b;
+          len = l;
+          break;
+        }
+        acc += n;
+      }
+      if (s < 0) return;
+    }
+    kb = static_cast<int>(seg) * kSegChunks;
+    ke = min(kb + kSegChunks, static_cast<int>((len + CQ - 1) / CQ));
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int c16 = lane & 15, g4 = lane >> 4;
   const int hh = wave >> 1, ph = wave & 1;
   const int h = 2 * hb + hh, g = 2 * hb / (H / G);
-  int64_t tb, len;
-  seq_range(cu, s, L, T, tb, len);
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
-  const int64_t pbase = pair_base64(cu, s, L, T);
+  const int nk = ke - kb;
+  const int64_t pbase = MODE == RV_SEGSUM ? 0 : pair_base64(cu, s, L, T);
   const int64_t sh = (int64_t)s * H + h;
   const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
   const float Ah = A[h];
   float *adw = reinterpret_cast<float *>(smem + AD + wave * ADW);
   auto nrow = [&](int j) { return 32 * (j >> 1) + 8 * g4 + 4 * (j & 1); };
 
+  // the state rows of (sequence, head) or (segment, head) in [P][N] fp32 buffers
+  const int64_t srow0 = (MODE == RV_FULL ? sh : gs * H + h) * P;
   f32x4 gst[2][NT];
 #pragma unroll
   for (int pt = 0; pt < 2; ++pt) {
-    const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N;
+    const int64_t prow = (srow0 + 32 * ph + 16 * pt + c16) * N;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      gst[pt][j] = dfinal ? *reinterpret_cast<const f32x4 *>(dfinal + prow + nrow(j)) : f32x4{};
+      gst[pt][j] = MODE == RV_SEGSUM || !gstart ? f32x4{}
+                                                : *reinterpret_cast<const f32x4 *>(gstart + prow + nrow(j));
   }
 
   auto issue = [&](int k, int sl) {
@@ -170,24 +218,26 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     dma_lds4(dt + (t0 + min(lane & 31, last)) * H + h, base + OD + wave * DW);
   };
 
-  // reverse order: iteration i handles chunk nck - 1 - i in slot i % 3
-  if (nck > 0) issue(nck - 1, 0);
-  if (nck > 1) issue(nck - 2, 1);
+  // the gradient flowing into chunk k from the later chunks is kept where it
+  // leaves a 64-token pair (k odd, or the sequence's last chunk)
+  auto saves = [&](int k) { return MODE != RV_SEGSUM && ((k & 1) || k == nck - 1); };
+  // reverse order: iteration i handles chunk ke - 1 - i in slot i % 3
+  if (nk > 0) issue(ke - 1, 0);
+  if (nk > 1) issue(ke - 2, 1);
   int sl = 0;
+  float asum = 0.f;  // the block's chunks' total decay exponent (RV_SEGSUM)
 #pragma unroll 1
-  for (int i = 0; i < nck; ++i) {
-    const int k = nck - 1 - i;
+  for (int i = 0; i < nk; ++i) {
+    const int k = ke - 1 - i;
     // chunk k's loads have landed once at most the later ops are pending
     // (completion in issue order): the state-gradient stores of iterations
     // i-2 and i-1 (SV each where one is stored) and the loads of chunk k-1 (LDR)
-    auto sv = [&](int m) { return ((nck - 1 - m) & 1) || m == 0 ? SV : 0; };
-    wait_vmcnt_dyn((i >= 2 ? sv(i - 2) : 0) + (i + 1 < nck ? LDR : 0) + (i >= 1 ? sv(i - 1) : 0));
+    auto sv = [&](int m) { return saves(ke - 1 - m) ? SV : 0; };
+    wait_vmcnt_dyn((i >= 2 ? sv(i - 2) : 0) + (i + 1 < nk ? LDR : 0) + (i >= 1 ? sv(i - 1) : 0));
     __syncthreads();
     const int slp = sl == 0 ? 2 : sl - 1;
-    if (k - 2 >= 0) issue(k - 2, slp);
-    // the gradient flowing into chunk k from the later chunks, kept where it
-    // leaves a 64-token pair (k odd, or the sequence's last chunk)
-    if ((k & 1) || k == nck - 1) {
+    if (k - 2 >= kb) issue(k - 2, slp);
+    if (saves(k)) {
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
         uint16_t *dst = gsave + ((pbase + (k >> 1)) * H + h) * (int64_t)(P * N) +
@@ -209,6 +259,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     const float dtv = tl <= last ? dts[lane] : 0.f;
     const float a = scan32b(dtv * Ah);
     const float alast = lane31(a);
+    asum += alast;
     // exp(a_l); 0 for the rows past a partial chunk's end (they repeat its last row)
     if (lane < 32) adw[tl] = tl <= last ? exp2b(a * kLog2eB) : 0.f;
     wsync();
@@ -251,14 +302,52 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     }
     sl = sl == 2 ? 0 : sl + 1;
   }
-  if (dinit) {
+  // RV_FULL: dL/dh0; RV_SEGSUM: the segment's G_seg and A_seg
+  if (MODE != RV_SEG && gout) {
 #pragma unroll
     for (int pt = 0; pt < 2; ++pt) {
-      const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N;
+      const int64_t prow = (srow0 + 32 * ph + 16 * pt + c16) * N;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(dinit + prow + nrow(j)) = gst[pt][j];
+      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(gout + prow + nrow(j)) = gst[pt][j];
     }
   }
+  if (MODE == RV_SEGSUM && ph == 0 && lane == 0) aseg[gs * H + h] = asum;
+}
+
+// The sweep over segments, per (sequence, head) and 4 elements of the P x N
+// gradient a thread: gin[seg] = g; g = exp(A_seg) g + G_seg, from dfinal (or 0)
+// down to the first segment; then dL/dh0 = g.
+__global__ __launch_bounds__(256) void k_bwd_gpass(
+    const float *__restrict__ gseg, const float *__restrict__ aseg,
+    const float *__restrict__ dfinal, const int32_t *__restrict__ cu, int64_t L, int64_t T,
+    int rows, int H, int PN, float *__restrict__ gin, float *__restrict__ dinit) {
+  const int s = blockIdx.z, h = blockIdx.y;
+  const int e = 4 * (blockIdx.x * 256 + threadIdx.x);
+  if (s >= rows || e >= PN) return;
+  int64_t tb, len, base = 0;
+  seq_range(cu, s, L, T, tb, len);
+  constexpr int SEGT = kSegChunks * 32;
+  if (!cu) {
+    base = (int64_t)s * ((L + SEGT - 1) / SEGT);
+  } else {
+    for (int i = 0; i < s; ++i) {
+      int64_t b, l;
+      seq_range(cu, i, L, T, b, l);
+      base += (l + SEGT - 1) / SEGT;
+    }
+  }
+  const int nseg = static_cast<int>((len + SEGT - 1) / SEGT);
+  const int64_t sh = (int64_t)s * H + h;
+  f32x4 gv = dfinal ? *reinterpret_cast<const f32x4 *>(dfinal + sh * PN + e) : f32x4{};
+#pragma unroll 1
+  for (int k = nseg - 1; k >= 0; --k) {
+    const int64_t o = ((base + k) * H + h) * (int64_t)PN + e;
+    const f32x4 gsum = *reinterpret_cast<const f32x4 *>(gseg + o);
+    const float d = exp2b(aseg[(base + k) * H + h] * kLog2eB);
+    *reinterpret_cast<f32x4 *>(gin + o) = gv;
+    gv = gv * d + gsum;
+  }
+  if (dinit) *reinterpret_cast<f32x4 *>(dinit + sh * PN + e) = gv;
 }
 
 // ---------------------------------------------------------------- pass 3
@@ -809,21 +898,31 @@ __global__ __launch_bounds__(256) void k_fill_f32(float *__restrict__ p, int64_t
 hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, const void *C,
                               const float *dfinal, const int32_t *cu, int64_t L, int64_t T,
                               int rows, int H, int N, int G, void *gsave, float *dinit,
+                              int64_t nseg, float *gseg, float *aseg, float *gin,
                               hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  const dim3 grid(xcd_grid(rows, H / 2));
+  if (N != 64 && N != 128) return hipErrorInvalidValue;
   const uint16_t *d = static_cast<const uint16_t *>(dy);
   const uint16_t *c = static_cast<const uint16_t *>(C);
   uint16_t *gs = static_cast<uint16_t *>(gsave);
-  if (N == 64)
-    hipLaunchKernelGGL(k_bwd_reverse<64>, grid, dim3(256), 0, stream, d, dt, A, c, dfinal, cu, L, T,
-                       rows, H, G, gs, dinit);
-  else if (N == 128)
-    hipLaunchKernelGGL(k_bwd_reverse<128>, grid, dim3(256), 0, stream, d, dt, A, c, dfinal, cu, L, T,
-                       rows, H, G, gs, dinit);
-  else
-    return hipErrorInvalidValue;
-  return hipGetLastError();
+  auto rev = [&](auto kern, int64_t units, const float *gstart, float *gout) {
+    hipLaunchKernelGGL(kern, dim3(xcd_grid(units, H / 2)), dim3(256), 0, stream, d, dt, A, c, gstart,
+                       cu, L, T, rows, H, G, gs, gout, aseg);
+    return hipGetLastError();
+  };
+  if (nseg == 0) {
+    return N == 64 ? rev(k_bwd_reverse<64, RV_FULL>, rows, dfinal, dinit)
+                   : rev(k_bwd_reverse<128, RV_FULL>, rows, dfinal, dinit);
+  }
+  hipError_t e = N == 64 ? rev(k_bwd_reverse<64, RV_SEGSUM>, nseg, nullptr, gseg)
+                         : rev(k_bwd_reverse<128, RV_SEGSUM>, nseg, nullptr, gseg);
+  if (e != hipSuccess) return e;
+  const int PN = 64 * N;
+  hipLaunchKernelGGL(k_bwd_gpass, dim3(PN / 1024, H, rows), dim3(256), 0, stream, gseg, aseg,
+                     dfinal, cu, L, T, rows, H, PN, gin, dinit);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  return N == 64 ? rev(k_bwd_reverse<64, RV_SEG>, nseg, gin, nullptr)
+                 : rev(k_bwd_reverse<128, RV_SEG>, nseg, gin, nullptr);
 }
 
 hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,

@@ -419,6 +419,43 @@ size_t chunk_states_bytes(const Plan &p) {
   return align_up((size_t)pairs64(p) * p.geo.H * p.geo.P * p.geo.N * 2);
 }
 
+// The backward's reverse sweep runs one block per (sequence, two heads); with
+// fewer such blocks than the GPU has CUs (256 on MI355X) it is split into
+// 256-token segments instead.  The decision depends on the dims only.
+bool bwd_segmented(const Plan &p) { return p.geo.nrows * (p.geo.H / 2) < 256; }
+
+// 256-token segments of the batch (packed: an upper bound, ceil(T/256) + nseq)
+int64_t segments256(const Plan &p) {
+  const ssd::Geometry &g = p.geo;
+  return g.packed ? ceil_div(g.tokens, 256) + g.nrows : g.nrows * ceil_div(g.L, 256);
+}
+
+// Backward workspace: the state gradients per pair (bf16), then, when the
+// sweep is segmented, the segment sums and incoming gradients (fp32) and the
+// segment decays.
+struct BwdWorkspace {
+  size_t gsave, gseg, gin, aseg, total;
+  int64_t nseg;
+};
+
+BwdWorkspace bwd_workspace(const Plan &p) {
+  BwdWorkspace w{};
+  w.gsave = 0;
+  size_t off = chunk_states_bytes(p);
+  if (bwd_segmented(p)) {
+    w.nseg = segments256(p);
+    const size_t tile = (size_t)w.nseg * p.geo.H * p.geo.P * p.geo.N * 4;
+    w.gseg = off;
+    off += align_up(tile);
+    w.gin = off;
+    off += align_up(tile);
+    w.aseg = off;
+    off += align_up((size_t)w.nseg * p.geo.H * 4);
+  }
+  w.total = off;
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -459,7 +496,11 @@ ssd_status ssd_fused_fwd_train(const void *x, const float *dt, const float *A, c
                                       static_cast<hipStream_t>(stream)));
 }
 
-size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims) { return ssd_fused_states_size(dims); }
+size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims) {
+  Plan p;
+  if (make_fused_plan(dims, &p) != SSD_OK) return 0;
+  return bwd_workspace(p).total;
+}
 
 ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const void *B,
                          const void *C, const float *D, const int32_t *cu_seqlens,
@@ -479,16 +520,17 @@ ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const v
   if ((dD != nullptr) != (D != nullptr)) return SSD_ERR_INVALID_ARG;
   if ((dfinal && !aligned(dfinal, 16)) || (dinit && !aligned(dinit, 16))) return SSD_ERR_INVALID_ARG;
   const size_t hb = chunk_states_bytes(p);
+  const BwdWorkspace bw = bwd_workspace(p);
   if (!chunk_states || !aligned(chunk_states, 16)) return SSD_ERR_INVALID_ARG;
   if (states_bytes < hb) return SSD_ERR_WORKSPACE;
-  if (!workspace || workspace_bytes < hb) return SSD_ERR_WORKSPACE;
+  if (!workspace || workspace_bytes < bw.total) return SSD_ERR_WORKSPACE;
   if (!aligned(workspace, 16)) return SSD_ERR_INVALID_ARG;
   // outputs overlap no input and no other output
   const Sizes z = tensor_bytes(p);
   const ssd::Geometry &g = p.geo;
   const size_t bdt = z.dt, bbc32 = (size_t)g.tokens * g.G * g.N * 4, bh = (size_t)g.H * 4;
   const void *ins[] = {x, dt, A, B, C, D, chunk_states, dy, dfinal, workspace};
-  const size_t insz[] = {z.x, bdt, bh, z.bc, z.bc, bh, hb, z.x, z.state, hb};
+  const size_t insz[] = {z.x, bdt, bh, z.bc, z.bc, bh, hb, z.x, z.state, bw.total};
   const void *outs[] = {dx, ddt, dA, dB, dC, dD, dinit};
   const size_t outsz[] = {z.x, bdt, bh, bbc32, bbc32, bh, z.state};
   for (int i = 0; i < 7; ++i) {
@@ -503,7 +545,9 @@ ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const v
   if (e == hipSuccess && dD) e = ssd::launch_fill_f32(dD, g.H, st);
   if (e == hipSuccess)
     e = ssd::launch_bwd_reverse(dy, dt, A, C, dfinal, cu, g.L, g.tokens, (int)g.nrows, g.H, g.N,
-                                g.G, workspace, dinit, st);
+                                g.G, workspace, dinit, bw.nseg, ws_ptr<float>(workspace, bw.gseg),
+                                ws_ptr<float>(workspace, bw.aseg), ws_ptr<float>(workspace, bw.gin),
+                                st);
   if (e == hipSuccess)
     e = ssd::launch_bwd_chunk(x, dt, A, B, C, D, dy, chunk_states, workspace, cu, g.L, g.tokens,
                               (int)g.nrows, chunks32(p), g.H, g.N, g.G, dx, ddt, dA, dB, dC, dD,

@@ -65,9 +65,12 @@ hipError_t launch_fused(const void *x, const float *dt, const float *A, const vo
                         int rows, int H, int P, int N, int G, void *y, float *hfin, void *hsave,
                         hipStream_t stream);
 // backward of the one-pass forward (bf16, P == 64, N in {64, 128}, even heads per group)
+// nseg > 0: the sweep split into that many 256-token segments (gseg, gin
+// [nseg][H][P][N] and aseg [nseg][H] fp32 scratch); 0: one pass per sequence
 hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, const void *C,
                               const float *dfinal, const int32_t *cu, int64_t L, int64_t T,
                               int rows, int H, int N, int G, void *gsave, float *dinit,
+                              int64_t nseg, float *gseg, float *aseg, float *gin,
                               hipStream_t stream);
 hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,
                             const void *C, const float *D, const void *dy, const void *hsave,

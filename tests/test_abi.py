@@ -348,7 +348,14 @@ def test_fused_states_size():
     assert L.ssd_fused_states_size(ctypes.byref(d)) == 3 * 16 * 4 * 64 * 128 * 2
     dp = make_dims(1, 1000, 4, 64, 64, 2, 3, SSD_BF16)  # packed: ceil(T / 64) + nseq
     assert L.ssd_fused_states_size(ctypes.byref(dp)) == (16 + 3) * 4 * 64 * 64 * 2
-    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(dp)) == (16 + 3) * 4 * 64 * 64 * 2
+    # the backward's workspace: the state gradients like the states; with few
+    # (sequence, head pair) blocks (here 3 x 2) also two fp32 tiles and a decay
+    # per 256-token segment and head (ceil(1000 / 256) + 3 segments)
+    nseg = 4 + 3
+    ws = (16 + 3) * 4 * 64 * 64 * 2 + 2 * nseg * 4 * 64 * 64 * 4 + 256
+    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(dp)) == ws
+    big = make_dims(8, 4096, 80, 64, 128, 1, 0, SSD_BF16)  # 8 x 40 blocks: one pass per sequence
+    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(big)) == 8 * 64 * 80 * 64 * 128 * 2
     for mut in (dict(io_dtype=SSD_F32), dict(headdim=128), dict(ngroups=4)):
         d = good()
         for k, val in mut.items():
@@ -393,9 +400,8 @@ def fused_bwd(d, sbytes=None, ws=FAKE + (20 << 30), wbytes=None, **kw):
     args = {k: FAKE + (i << 30) for i, k in enumerate(BWD_ARGS)}
     args.update(D=None, dD=None, cu=None, dfinal=None, dinit=None)
     args.update(kw)
-    need = L.ssd_fused_bwd_workspace_size(ctypes.byref(d))
-    sbytes = need if sbytes is None else sbytes
-    wbytes = need if wbytes is None else wbytes
+    sbytes = L.ssd_fused_states_size(ctypes.byref(d)) if sbytes is None else sbytes
+    wbytes = L.ssd_fused_bwd_workspace_size(ctypes.byref(d)) if wbytes is None else wbytes
     ptrs = [None if args[k] is None else v(args[k]) for k in BWD_ARGS]
     return L.ssd_fused_bwd(*ptrs[:8], ctypes.c_size_t(sbytes), *ptrs[8:], ctypes.byref(d),
                            None if ws is None else v(ws), ctypes.c_size_t(wbytes), None)
@@ -403,11 +409,12 @@ def fused_bwd(d, sbytes=None, ws=FAKE + (20 << 30), wbytes=None, **kw):
 
 def test_fused_bwd_validation():
     d = good()
-    need = L.ssd_fused_bwd_workspace_size(ctypes.byref(d))
+    sneed = L.ssd_fused_states_size(ctypes.byref(d))
+    wneed = L.ssd_fused_bwd_workspace_size(ctypes.byref(d))
     for k in ("x", "dt", "A", "B", "C", "dy", "dx", "ddt", "dA", "dB", "dC", "states"):
         assert fused_bwd(d, **{k: None}) == SSD_ERR_INVALID_ARG, k
-    assert fused_bwd(d, sbytes=need - 1) == SSD_ERR_WORKSPACE
-    assert fused_bwd(d, wbytes=need - 1) == SSD_ERR_WORKSPACE
+    assert fused_bwd(d, sbytes=sneed - 1) == SSD_ERR_WORKSPACE
+    assert fused_bwd(d, wbytes=wneed - 1) == SSD_ERR_WORKSPACE
     assert fused_bwd(d, ws=None) == SSD_ERR_WORKSPACE
     assert fused_bwd(d, dD=FAKE + (21 << 30)) == SSD_ERR_INVALID_ARG         # dD without D
     assert fused_bwd(d, D=FAKE + (21 << 30)) == SSD_ERR_INVALID_ARG          # D without dD
