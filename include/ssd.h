@@ -273,8 +273,10 @@ ssd_status ssd_fused_fwd_train(const void *x, const float *dt, const float *A, c
  * 0 if the dims are invalid or outside ssd_fused_fwd's shapes.  Host-only. */
 size_t ssd_fused_states_size(const ssd_dims *dims);
 
-/* Workspace bytes of ssd_fused_bwd (the gradient w.r.t. the state leaving
- * every 64-token pair, bf16, laid out like chunk_states).  Host-only. */
+/* Workspace bytes of ssd_fused_bwd: the gradient w.r.t. the state leaving
+ * every 64-token pair (bf16, laid out like chunk_states) and, when the sweep
+ * is split into segments (sequences x nheads / 2 < 256), two fp32 P x N tiles
+ * and a decay per segment and head.  Host-only. */
 size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
 
 /* Gradients of the forward.  The pages give the recurrence h_t = exp(dt_t A)
@@ -287,7 +289,11 @@ size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
  * Inputs (the forward's, same layouts): x, dt, A, B, C, D (may be NULL),
  * cu_seqlens, and
  *   chunk_states  what ssd_fused_fwd_train saved for these inputs and
- *                 init_state (states_bytes its size);
+ *                 init_state (states_bytes its size); equally the hprev
+ *                 buffer of an ssd_chunk_scan_fwd workspace for the same
+ *                 inputs with chunk_len 64 (bf16), which holds the same states
+ *                 in the same layout: the chunk-parallel forward for a few long
+ *                 sequences;
  *   dy            device bf16 [T, H, P], the gradient w.r.t. y;
  *   dfinal        device float [rows, H, P, N] or NULL (zero).
  * Outputs (device, overwritten; none may overlap an input or another output):
@@ -300,10 +306,12 @@ size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
  *   dinit float [rows, H, P, N] (the gradient w.r.t. init_state) or NULL.
  * workspace: device memory of at least ssd_fused_bwd_workspace_size(dims)
  * bytes, 16-byte aligned, else SSD_ERR_WORKSPACE.  Supported shapes are
- * ssd_fused_fwd's.  Three kernels on `stream` (dA and dD cleared, the
- * reverse sweep of the state gradient, the per-chunk gradients); the
- * per-chunk pass adds into dA and dD with float atomics, so those two sum in
- * an unspecified order.  Returns after enqueueing. */
+ * ssd_fused_fwd's.  On `stream`: dA and dD cleared; the reverse sweep of the
+ * state gradient (one pass per (sequence, two heads), or, with fewer such
+ * pairs than 256, per 256-token segment: segment sums, a chained pass, the
+ * segments again); the per-chunk gradients, which add into dA and dD with
+ * float atomics, so those two sum in an unspecified order.  Returns after
+ * enqueueing. */
 ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const void *B,
                          const void *C, const float *D, const int32_t *cu_seqlens,
                          const void *chunk_states, size_t states_bytes, const void *dy,

@@ -100,6 +100,20 @@ class SSDForward:
     def scan(self, x, B, C, D, y, stream=None):
         libssd.ssd_chunk_scan(x, B, C, D, y, self.chunk_len, self.dims, self.workspace, stream)
 
+    def saved_states(self) -> torch.Tensor:
+        """The hprev buffer of the workspace as bytes: with chunk_len 64 and bf16
+        io it holds, after a call, the state entering every 64-token chunk in the
+        layout fused_bwd takes as chunk_states (the chunk-parallel way to get
+        them for a few long sequences)."""
+        if self.chunk_len != 64 or self.dims.io_dtype != SSD_BF16:
+            raise SSDUnsupported(libssd.SSD_ERR_UNSUPPORTED,
+                                 "saved states need chunk_len 64 and bf16 io")
+        n = libssd.ssd_fused_states_size(self.dims)
+        if n == 0:
+            raise SSDUnsupported(libssd.SSD_ERR_UNSUPPORTED, "shape outside the one-pass forward")
+        off = self.layout.hprev_offset
+        return self.workspace[off:off + n]
+
     def view(self, name: str) -> torch.Tensor:
         """A typed view of one workspace buffer (acum, dtq, states, hprev,
         chunk_table, chunk_dir) in its documented shape."""

@@ -281,3 +281,25 @@ def test_long_n64_sampled():
     _, _, _, g = fwd_bwd(w, t, dy, dfinal)
     pairs = [(0, 0), (0, 33), (0, 79)]
     sampled_check(w, g, pairs, "bwd long_n64 sampled", dy, dfinal)
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_states_from_chunked_forward(packed):
+    # the four-stage forward with chunk length 64 leaves the same states in its
+    # workspace (hprev): the backward from them matches the oracle
+    if packed:
+        w = workloads.make_custom(1, 0, 4, 64, 128, 2, 64, "bf16", seed=3100, init_std=0.3,
+                                  lens=[300, 0, 65, 1000, 1])
+    else:
+        w = workloads.make_custom(2, 700, 4, 64, 64, 1, 64, "bf16", seed=3101, init_std=0.3)
+    dy, dfinal = workloads.make_output_grads(w, 12)
+    t = upload(w)
+    plan = ssd.SSDForward(ssd.dims_for(t["x"], t["B"], t["cu"]), 64, device=DEV)
+    plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"])
+    states = plan.saved_states()
+    dyd = torch.from_numpy(dy).to(DEV).to(torch.bfloat16).view(t["x"].shape)
+    g = ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], states, dyd,
+                      torch.from_numpy(dfinal).to(DEV), t["cu"])
+    torch.cuda.synchronize()
+    ref = oracle.recurrence_bwd(w.x, w.dt, w.A, w.B, w.C, w.D, w.h0, w.seq_off, dy, dfinal)
+    check_grads(w, g, ref, f"bwd from chunked-forward states ({'packed' if packed else 'fixed'})")
