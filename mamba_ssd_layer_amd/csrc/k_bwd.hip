@@ -352,11 +352,12 @@ __global__ __launch_bounds__(256) void k_bwd_gpass(
 
 // ---------------------------------------------------------------- pass 3
 // Block = (32-token chunk, group), 8 wavefronts (two per SIMD), walking the
-// group's heads.  LDS: the chunk's B and C (rows = tokens); an R-slot ring per
-// head of x and dy (rows = tokens, 8 chunks a row), h_s and g_e (rows = p, N/8
-// chunks a row) and dt; the head's masked products as ready MFMA operands;
-// per-wavefront tables and cross-wavefront partial sums (two buffers, by head
-// parity, since a head's sums are finished one head later).
+// group's heads.  LDS: the chunk's B and C (rows = tokens) and the neighbour
+// chunk's B or C; an R-slot ring per head of x and dy (rows = tokens, 8 chunks
+// a row), the pair's saved h_s and g_e (rows = p, N/8 chunks a row), dt, and
+// the neighbour chunk's x or dy and dt; the head's masked products as ready
+// MFMA operands; per-wavefront tables and cross-wavefront partial sums (two
+// buffers, by head parity, since a head's sums are finished one head later).
 // Tile conventions (16x16x32 MFMA): an "E-layout" tile (lt, st) holds
 // matrix[l][s] with lane (c16 = s, g4) rows l = 16 lt + 4 g4 + r; the tiles
 // lt = 0, 1 of one st together form a B operand with K = l in the order
@@ -365,9 +366,10 @@ __global__ __launch_bounds__(256) void k_bwd_gpass(
 // "ET-layout" tile (st, lt) holds matrix[s][l] the same way.
 // Per head: wavefronts 0-3 form one E-layout tile each of E = dy x^T and from
 // it M = Z o L dt_s, EL = E o L dt_s and the sums of K = E o Z o L dt_s;
-// wavefronts 4-7 one ET-layout tile each of E^T and EL^T; after a barrier each
-// wavefront computes one 16 x 16 tile of dx (p-tile w/2, s-tile w%2) with the
-// matching tile of h_s C^T, and N/64 tiles of dB and of dC.
+// wavefronts 4-7 one ET-layout tile each of E^T and EL^T; all of them derive
+// N/32 tiles of the state the pair does not hold for this chunk (in place);
+// after a barrier each wavefront computes one 16 x 16 tile of dx (p-tile w/2,
+// s-tile w%2) with the matching tile of h_s C^T, and N/64 tiles of dB and dC.
 template <int N, int R>
 struct BwdCfg {
   static constexpr int P = 64, CQ = 32, NCB = N / 8, WAVES = 8;
