@@ -259,7 +259,8 @@ def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
     dyd = torch.from_numpy(dy).to(dev).to(torch.bfloat16).view(t["x"].shape)
     dfd = torch.from_numpy(dfinal).to(dev)
     states = ssd.make_fused_states(t["x"], t["B"], t["cu"])
-    ws = torch.empty_like(states)
+    ws = torch.empty(ssd.libssd.ssd_fused_bwd_workspace_size(ssd.dims_for(t["x"], t["B"], t["cu"])),
+                     dtype=torch.uint8, device=dev)
     y = torch.empty_like(t["x"])
     fin = torch.empty_like(dfd)
     stream = torch.cuda.current_stream()
