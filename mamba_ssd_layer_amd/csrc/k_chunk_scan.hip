@@ -480,7 +480,13 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int nc,
     int H, int G, int hb, int nkb, uint16_t *__restrict__ y) {
   constexpr int Q = 256, P = 64;
-  static_assert(N == 64 || N == 128, "head-batched tile shape");
+  static_assert(N == 64 || N == 128 || N == 256, "head-batched tile shape");
+  // N 256: B is staged in two 128-column halves for the Z phase, and hprev
+  // has one LDS slot (loaded once the previous head's inter term is done)
+  constexpr int NH = N > 128 ? 2 : 1;  // B halves
+  constexpr int NBH = N / NH;          // columns of a staged B half
+  constexpr int NCBH = NBH / 8;        // its 16-byte chunks per row
+  constexpr int HSL = N > 128 ? 1 : 2; // hprev slots
   constexpr int NT = 512;             // threads
   constexpr int NW = 8;               // wavefronts
   constexpr int NLT = Q / 32;         // token tiles
@@ -491,14 +497,15 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
   constexpr int XB = Q * P * 2;       // x (then y) of one head
   constexpr int HB = P * N * 2;       // hprev of one head
   constexpr int ADB = 2 * Q * 4;      // acum and dt of one head
-  constexpr int BB = Q * N * 2;       // B of the chunk, Z phase only
+  constexpr int BB = Q * NBH * 2;     // B of the chunk (a half at N 256), Z phase only
   constexpr int PSB = 32 * P * 4;     // one handed-over partial sum (fp32)
   constexpr int XI = XB / 1024 / NW;  // 1 KB direct loads per wavefront
   constexpr int HI = HB / 1024 / NW;
   constexpr int BI = BB / 1024 / NW;
   static_assert(XI * NW * 1024 == XB && HI * NW * 1024 == HB && BI * NW * 1024 == BB, "1 KB loads");
   // [XS0][XS1][HS0][HS1][AD0][AD1][VT][PS0..PS3]; B is staged over XS0 + XS1
-  constexpr int XS0 = 0, XS1 = XB, HS0 = 2 * XB, HS1 = HS0 + HB, AD0 = HS1 + HB, AD1 = AD0 + ADB;
+  constexpr int XS0 = 0, XS1 = XB, HS0 = 2 * XB, HS1 = HS0 + (HSL - 1) * HB, AD0 = HS1 + HB,
+                AD1 = AD0 + ADB;
   constexpr int VT = AD1 + ADB, PS = VT + NLT * Q * 4, TOTAL = PS + 4 * PSB;
   static_assert(2 * XB >= BB, "B staging fits over the x ring");
   __shared__ __align__(16) unsigned char smem[TOTAL];
@@ -542,7 +549,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
   // Direct loads, 16-byte chunks XOR-swizzled per row.  Token rows past the
   // chunk's end repeat its last row: finite data that dt = 0 cancels, in rows
   // of y that are never stored.
-  auto issue_head = [&](const Lane &Ln, int hh, int slot) {
+  auto issue_head = [&](const Lane &Ln, int hh, int slot, bool with_h) {
     const int lane = Ln.lane;
     const uint16_t *xb = x + xrow0 + (int64_t)hh * P;
     unsigned char *xs = smem + (slot ? XS1 : XS0);
@@ -556,13 +563,23 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     const uint16_t *hp = hprev + ch * (P * N);
     unsigned char *hs = smem + (slot ? HS1 : HS0);
 #pragma unroll
-    for (int i = 0; i < HI; ++i) {
+    for (int i = 0; i < (with_h ? HI : 0); ++i) {
       const unsigned m = (wave * HI + i) * 64 + lane, r = m / NCB;
       const unsigned cc = (m % NCB) ^ chunk_swz(r, NCB);
       load_lds16(hp + r * N + cc * 8, hs + (wave * HI + i) * 1024);
     }
     if (wave < 2)  // wavefront 0: acum, 1: dt
       load_lds16((wave == 0 ? acum : dtq) + ch * Q + lane * 4, smem + (slot ? AD1 : AD0) + wave * 1024);
+  };
+  auto issue_hprev = [&](const Lane &Ln, int hh) {  // one-slot hprev (N 256)
+    const int lane = Ln.lane;
+    const uint16_t *hp = hprev + ((int64_t)c * H + hh) * (P * N);
+#pragma unroll
+    for (int i = 0; i < HI; ++i) {
+      const unsigned m = (wave * HI + i) * 64 + lane, r = m / NCB;
+      const unsigned cc = (m % NCB) ^ chunk_swz(r, NCB);
+      load_lds16(hp + r * N + cc * 8, smem + HS0 + (wave * HI + i) * 1024);
+    }
   };
   auto store_y = [&](const Lane &Ln, int hh, const unsigned char *ys) {
     const unsigned tid = Ln.tid;
@@ -581,45 +598,53 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     }
   };
 
-  // ---- Z phase: the chunk's B, head 0's data, and the C rows of the lane's
-  // own and handed-over tiles (registers)
-  {
-    const uint16_t *bb = Bm + ci.t0 * ldb + (int64_t)g * N;
-#pragma unroll
-    for (int i = 0; i < BI; ++i) {
-      const int m = (wave * BI + i) * 64 + lane;
-      const int r = m / NCB, cc = (m % NCB) ^ chunk_swz(m / NCB, NCB);
-      load_lds16(bb + (int64_t)min(r, ci.len - 1) * ldb + cc * 8, smem + XS0 + (wave * BI + i) * 1024);
-    }
-  }
+  // ---- Z phase: the chunk's B (in NH column halves), head 0's data, and the
+  // C rows of the lane's own and handed-over tiles (registers)
   const uint16_t *cbase = Cm + ci.t0 * ldb + (int64_t)g * N + kg * 8;
   u32x4 cown[KN], cdon[KN];
-  load_rows<KN>(cown, cbase + (int64_t)l * ldb, l < ci.len);
-  load_rows<KN>(cdon, cbase + (int64_t)(TD * 32 + col) * ldb, TD * 32 + col < ci.len);
-  wait_vmcnt<0>();
-  __syncthreads();
-  // slot k < 4: handed-over pair (TD, k) for k < nd, else own off-diagonal
-  // pair (T, k - nd) on a donor and (T, T - 3 + k) on a receiver (k = 3 unused
-  // there); slot 4: the diagonal pair (T, T).  Operands are picked by value,
-  // with no branches, so each tile is formed in the registers it stays in.
   f32x16 z[5];
 #pragma unroll
-  for (int k = 0; k < 5; ++k) {
-    const bool dk = k < nd;
-    const int zi = k == 4 ? T : (donor ? (dk ? k : k - nd) : min(T - 3 + k, T));
-    const unsigned char *brow = smem + XS0 + (32 * zi + col) * (N * 2);
-    f32x16 acc = f32x16{};
+  for (int k = 0; k < 5; ++k) z[k] = f32x16{};
 #pragma unroll
-    for (int q = 0; q < KN; ++q) {
-      const int cc = (2 * q + kg) ^ chunk_swz(col, NCB);
-      const u32x4 bq = *reinterpret_cast<const u32x4 *>(brow + cc * 16);
-      const u32x4 cq = dk ? cdon[q] : cown[q];
-      acc = mfma32x32x16(as_bf16x8(bq), as_bf16x8(cq), acc);
+  for (int half = 0; half < NH; ++half) {
+    if (half > 0) __syncthreads();  // the previous half is consumed
+    {
+      const uint16_t *bb = Bm + ci.t0 * ldb + (int64_t)g * N + half * NBH;
+#pragma unroll
+      for (int i = 0; i < BI; ++i) {
+        const int m = (wave * BI + i) * 64 + lane;
+        const int r = m / NCBH, cc = (m % NCBH) ^ chunk_swz(m / NCBH, NCBH);
+        load_lds16(bb + (int64_t)min(r, ci.len - 1) * ldb + cc * 8, smem + XS0 + (wave * BI + i) * 1024);
+      }
     }
-    z[k] = acc;
+    if (half == 0) {
+      load_rows<KN>(cown, cbase + (int64_t)l * ldb, l < ci.len);
+      load_rows<KN>(cdon, cbase + (int64_t)(TD * 32 + col) * ldb, TD * 32 + col < ci.len);
+    }
+    wait_vmcnt<0>();
+    __syncthreads();
+    // slot k < 4: handed-over pair (TD, k) for k < nd, else own off-diagonal
+    // pair (T, k - nd) on a donor and (T, T - 3 + k) on a receiver (k = 3 unused
+    // there); slot 4: the diagonal pair (T, T).  Operands are picked by value,
+    // with no branches, so each tile is formed in the registers it stays in.
+#pragma unroll
+    for (int k = 0; k < 5; ++k) {
+      const bool dk = k < nd;
+      const int zi = k == 4 ? T : (donor ? (dk ? k : k - nd) : min(T - 3 + k, T));
+      const unsigned char *brow = smem + XS0 + (32 * zi + col) * (NBH * 2);
+      f32x16 acc = z[k];
+#pragma unroll
+      for (int q = 0; q < KN / NH; ++q) {
+        const int cc = (2 * q + kg) ^ chunk_swz(col, NCBH);
+        const u32x4 bq = *reinterpret_cast<const u32x4 *>(brow + cc * 16);
+        const u32x4 cq = dk ? cdon[half * (KN / NH) + q] : cown[half * (KN / NH) + q];
+        acc = mfma32x32x16(as_bf16x8(bq), as_bf16x8(cq), acc);
+      }
+      z[k] = acc;
+    }
   }
   __syncthreads();  // B consumed: the x ring is free
-  issue_head(L0, hfirst, 0);
+  issue_head(L0, hfirst, 0, true);
 
   // X^T operands of source tile i by transposing LDS reads: lane (gq = lane/16,
   // d = lane%16) addresses token row 32i + 8h4 + 4kg + d/4, columns 4(d%4)..,
@@ -685,7 +710,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
         if (j0 + jj < jend && (int)s < 32 * (j0 + jj)) vt[(j0 + jj) * Q + s] = e[jj];
     }
     __syncthreads();  // v table ready; the other slot's y has been read out
-    if (hi + 1 < nh) issue_head(Lh, hh + 1, slot ^ 1);
+    if (hi + 1 < nh) issue_head(Lh, hh + 1, slot ^ 1, HSL == 2);
 
     f32x16 acc[TP];
     // 3. handed-over pairs (donors): sum over source tiles 0 .. nd-1 of tile TD
@@ -739,7 +764,8 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
         pair_xg(Lh, acc, xs, i, gv);
       }
     }
-    __syncthreads();  // handed-over sums are in LDS
+    __syncthreads();  // handed-over sums are in LDS; every inter term has read hprev
+    if (HSL == 1 && hi + 1 < nh) issue_hprev(Lh, hh + 1);
     // 5. handed-over sum (receivers), u_l, the diagonal pair, the skip term
     if (!donor) {
       const float *ps = reinterpret_cast<const float *>(smem + PS + s4 * PSB);
@@ -809,7 +835,7 @@ static void launch_sc(const void *x, const void *B, const void *C, const float *
                       const Geometry &geo, hipStream_t stream) {
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
   const dim3 grid(xcd_grid(geo.nc_max, geo.H));
-  if constexpr (Q == 256 && P == 64 && N <= 128) {
+  if constexpr (Q == 256 && P == 64) {
     int nkb = 1;
     const int hb = pick_heads_per_block(geo.nc_max, geo.H, geo.G, device_cus(), 1.5, nkb);
     hipLaunchKernelGGL((k_chunk_scan_hb<N>), dim3(xcd_grid(geo.nc_max, geo.G * nkb)), dim3(512), 0,
