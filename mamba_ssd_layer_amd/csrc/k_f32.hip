@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kF32Threads) void k_chunk_state_f32(
   }
 }
 
-// Block = (chunk, head); passes over 16-token row tiles.  Pass 1 fills
+// Block = (chunk, head, 16-token row tile).  Pass 1 fills
 // gm[li][s] = (C_l . B_s) exp(acum_l - acum_s) dt_s for s <= l (0 otherwise);
 // pass 2 forms y for the tile's tokens.
 __global__ __launch_bounds__(kF32Threads) void k_chunk_scan_f32(
@@ -67,7 +67,8 @@ __global__ __launch_bounds__(kF32Threads) void k_chunk_scan_f32(
   const int h = blockIdx.y;
   const int g = h / (H / G);
   const ChunkInfo ci = chunk_info(geom, c);
-  if (ci.len <= 0) return;
+  const int lt = blockIdx.z * kRowTile;
+  if (lt >= ci.len) return;
   const int64_t ch = (int64_t)c * H + h;
   for (int l = threadIdx.x; l < Q; l += kF32Threads) {
     sa[l] = acum[ch * Q + l];
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kF32Threads) void k_chunk_scan_f32(
   const float *hp = hprev + ch * (int64_t)P * N;
   float *yb = y + ci.t0 * ldx + (int64_t)h * P;
   const float Dh = Dv ? Dv[h] : 0.f;
-  for (int lt = 0; lt < ci.len; lt += kRowTile) {
+  {
     const int rows = min(kRowTile, ci.len - lt);
     const int span = lt + rows;  // sources s < span can be reached
     for (int idx = threadIdx.x; idx < rows * span; idx += kF32Threads) {
@@ -109,7 +110,6 @@ __global__ __launch_bounds__(kF32Threads) void k_chunk_scan_f32(
       const float xl = xb[l * ldx + p];
       yb[l * ldx + p] = intra + __expf(sa[l]) * inter + Dh * xl;
     }
-    __syncthreads();
   }
 }
 
@@ -132,7 +132,9 @@ hipError_t launch_chunk_scan_f32(const float *x, const float *B, const float *C,
   if (geo.nc_max == 0) return hipSuccess;
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
   const size_t smem = (size_t)(2 + kRowTile) * geo.Q * sizeof(float);
-  hipLaunchKernelGGL(k_chunk_scan_f32, dim3((unsigned)geo.nc_max, (unsigned)geo.H),
+  hipLaunchKernelGGL(k_chunk_scan_f32,
+                     dim3((unsigned)geo.nc_max, (unsigned)geo.H,
+                          (unsigned)((geo.Q + kRowTile - 1) / kRowTile)),
                      dim3(kF32Threads), smem, stream, x, B, C, D, acum, dtq, hprev, cg, geo.H,
                      geo.G, geo.P, geo.N, y);
   return hipGetLastError();
