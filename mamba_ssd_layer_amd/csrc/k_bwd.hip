@@ -154,21 +154,11 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
       if (s >= rows) return;
       seq_range(cu, s, L, T, tb, len);
     } else {
-      int64_t acc = 0;
-      for (int i = 0; i < rows; ++i) {
-        int64_t b, l;
-        seq_range(cu, i, L, T, b, l);
-        const int64_t n = (l + kSegChunks * CQ - 1) / (kSegChunks * CQ);
-        if (gs < acc + n) {
-          s = i;
-          seg = gs - acc;
-          tb = b;
-          len = l;
-          break;
-        }
-        acc += n;
-      }
+      int64_t before;
+      s = locate_unit(cu, rows, T, gs, kSegChunks * CQ, before);
       if (s < 0) return;
+      seg = gs - before;
+      seq_range(cu, s, L, T, tb, len);
     }
     kb = static_cast<int>(seg) * kSegChunks;
     ke = min(kb + kSegChunks, static_cast<int>((len + CQ - 1) / CQ));
@@ -323,19 +313,13 @@ __global__ __launch_bounds__(256) void k_bwd_gpass(
     int rows, int H, int PN, float *__restrict__ gin, float *__restrict__ dinit) {
   const int s = blockIdx.z, h = blockIdx.y;
   const int e = 4 * (blockIdx.x * 256 + threadIdx.x);
-  if (s >= rows || e >= PN) return;
-  int64_t tb, len, base = 0;
-  seq_range(cu, s, L, T, tb, len);
+  if (s >= rows) return;
   constexpr int SEGT = kSegChunks * 32;
-  if (!cu) {
-    base = (int64_t)s * ((L + SEGT - 1) / SEGT);
-  } else {
-    for (int i = 0; i < s; ++i) {
-      int64_t b, l;
-      seq_range(cu, i, L, T, b, l);
-      base += (l + SEGT - 1) / SEGT;
-    }
-  }
+  // (all lanes take part in the walk over the sequences before returning)
+  const int64_t base = cu ? units_before(cu, s, T, SEGT) : (int64_t)s * ((L + SEGT - 1) / SEGT);
+  if (e >= PN) return;
+  int64_t tb, len;
+  seq_range(cu, s, L, T, tb, len);
   const int nseg = static_cast<int>((len + SEGT - 1) / SEGT);
   const int64_t sh = (int64_t)s * H + h;
   f32x4 gv = dfinal ? *reinterpret_cast<const f32x4 *>(dfinal + sh * PN + e) : f32x4{};
@@ -432,23 +416,12 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     seq_range(cu, s, L, T, tb, len);
     pb0 = (int64_t)s * ((L + 63) / 64);
   } else {
-    int64_t acc = 0, pacc = 0;
-    for (int i = 0; i < rows; ++i) {
-      int64_t b, l;
-      seq_range(cu, i, L, T, b, l);
-      const int64_t n = (l + CQ - 1) / CQ;
-      if (c < acc + n) {
-        s = i;
-        k = c - acc;
-        tb = b;
-        len = l;
-        pb0 = pacc;
-        break;
-      }
-      acc += n;
-      pacc += (l + 63) / 64;
-    }
+    int64_t before;
+    s = locate_unit(cu, rows, T, c, CQ, before);
     if (s < 0) return;
+    k = c - before;
+    seq_range(cu, s, L, T, tb, len);
+    pb0 = units_before(cu, s, T, 64);
   }
   // The saved states are kept per 64-token pair of chunks: h_s entering the
   // pair, g_e leaving it.  An even chunk reads its h_s; its g_e is derived

@@ -217,17 +217,75 @@ __device__ __forceinline__ void seq_range(const int32_t *cu, int s, int64_t L, i
   }
 }
 
+// Packed batches (cu_seqlens): wave-parallel walks over the sequences, 64 a
+// step (lane i reads sequence i0 + i), so a block finds its place in a few
+// rounds of loads instead of one dependent load per sequence.  Every lane of
+// the wavefront must make the call (shuffles and ballots).
+
+// A value equal on every lane, moved to a scalar register (so that addresses
+// built from it stay wave-uniform).
+__device__ __forceinline__ int64_t uniform64(int64_t v) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(static_cast<uint64_t>(v) >> 32));
+  return static_cast<int64_t>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+// ceil(len_i / u) for sequence i (0 past the last sequence).
+__device__ __forceinline__ int64_t seq_units(const int32_t *cu, int i, int rows, int64_t T, int u) {
+  if (i >= rows) return 0;
+  int64_t tb, len;
+  seq_range(cu, i, 0, T, tb, len);
+  return (len + u - 1) / u;
+}
+
+// Inclusive prefix sum over the wavefront's 64 lanes.
+__device__ __forceinline__ int64_t wave_scan_incl(int64_t v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int64_t o = __shfl_up(v, d, 64);
+    if (lane >= d) v += o;
+  }
+  return v;
+}
+
+// Sum over the sequences i < s of ceil(len_i / u).
+__device__ inline int64_t units_before(const int32_t *cu, int s, int64_t T, int u) {
+  int64_t acc = 0;
+  for (int i0 = 0; i0 < s; i0 += 64) {
+    const int64_t v = seq_units(cu, i0 + (threadIdx.x & 63), s, T, u);
+    acc += __shfl(wave_scan_incl(v), 63, 64);
+  }
+  return uniform64(acc);
+}
+
+// Units of u tokens listed sequence-major (sequence i holds ceil(len_i / u)
+// of them): the sequence holding unit c, and in `before` the units of the
+// sequences ahead of it; -1 if c is past the last unit.
+__device__ inline int locate_unit(const int32_t *cu, int rows, int64_t T, int64_t c, int u,
+                                  int64_t &before) {
+  int64_t acc = 0;
+  for (int i0 = 0; i0 < rows; i0 += 64) {
+    const int64_t v = seq_units(cu, i0 + (threadIdx.x & 63), rows, T, u);
+    const int64_t incl = wave_scan_incl(v);
+    // the first lane whose running total passes c holds a nonempty sequence
+    const unsigned long long m = __ballot(acc + incl > c);
+    if (m) {
+      const int f = __builtin_ctzll(m);
+      before = uniform64(acc + __shfl(incl - v, f, 64));
+      return __builtin_amdgcn_readfirstlane(i0 + f);
+    }
+    acc += __shfl(incl, 63, 64);
+  }
+  before = uniform64(acc);
+  return -1;
+}
+
 // Index of sequence s's first 64-token pair of chunks in the sequence-major
 // list of the batch's pairs (the layout of the saved per-pair states).
 __device__ inline int64_t pair_base64(const int32_t *cu, int s, int64_t L, int64_t T) {
   if (!cu) return (int64_t)s * ((L + 63) / 64);
-  int64_t acc = 0;
-  for (int i = 0; i < s; ++i) {
-    int64_t tb, len;
-    seq_range(cu, i, L, T, tb, len);
-    acc += (len + 63) / 64;
-  }
-  return acc;
+  return units_before(cu, s, T, 64);
 }
 
 }  // namespace ssd
