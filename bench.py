@@ -8,8 +8,10 @@ supported, the one-pass forward (ssd_fused_fwd: the same steps per 32-token
 chunk with the state kept on chip).  `value` is the faster of the two (named
 in config.path); both are reported.  Prints one JSON line with whole-job
 tokens/s, the roofline position of that path's dominant kernel (timed with HIP
-events on the launch stream), per-kernel figures of the chunked stages, and
-the CPU oracle timed on a bounded sample of the same workload on the host
+events on the launch stream), per-kernel figures of the chunked stages (each
+kernel's bandwidth against the published peak and against a plain copy
+measured in the same run, and its algorithmic MFMA flops against the peak),
+and the CPU oracle timed on a bounded sample of the same workload on the host
 cores.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
@@ -138,6 +140,28 @@ def cpu_baseline(w, target_cpu_seconds: float = 20.0):
             "sample": f"{n} of {total_pairs} (sequence, head) pairs of {w.name}, "
                       f"{sample_tokens} token-heads, fp64 recurrence, {el:.2f} s wall on {used} "
                       f"threads ({per_pair:.2f} s for one pair on one thread)"}
+
+
+def copy_bandwidth(torch, dev, mib: int = 1024, reps: int = 5) -> float:
+    """GB/s of a plain elementwise copy (dst = -src, fp32, one read and one
+    write per element) of mib MiB: the bandwidth a streaming kernel can reach
+    on this GPU, next to the published 8 TB/s."""
+    n = (mib << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(2):
+        torch.neg(src, out=dst)
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        torch.neg(src, out=dst)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    t = e0.elapsed_time(e1) * 1e-3 / reps
+    del src, dst
+    return 2 * n * 4 / t / 1e9
 
 
 def decode_step(torch, ssd, workloads, dev, steps: int, warmup: int):
@@ -460,6 +484,18 @@ def main() -> int:
         torch.cuda.synchronize()
         for s in STAGES:
             stage_us[s] = sum(a.elapsed_time(b) for a, b in evs[s]) / len(evs[s]) * 1e3
+    copy_gbs = copy_bandwidth(torch, dev)
+    log(f"bench: plain copy {copy_gbs:.0f} GB/s")
+
+    def fracs(b, f, t):
+        """achieved bandwidth as a fraction of the measured copy's, and
+        algorithmic flops as a fraction of the MFMA peak"""
+        mfma_peak = BF16_MFMA_PEAK_TFLOPS if w.dtype == "bf16" else FP32_PEAK_TFLOPS
+        return {"copy_frac": round(b / t / 1e9 / copy_gbs, 4),
+                "mfma_frac": round(f / t / 1e12 / mfma_peak, 4)}
+
+    if fused is not None:
+        fused.update(fracs(fused["bytes"], fused["flops"], fused["us"] * 1e-6))
     kernels = {}
     for s in STAGES:
         b, f = algorithmic(w, s)
@@ -468,7 +504,7 @@ def main() -> int:
             t = stage_us[s] * 1e-6
             entry.update(us=round(stage_us[s], 2), GBs=round(b / t / 1e9, 1),
                          TFLOPs=round(f / t / 1e12, 2) if f else 0.0,
-                         hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4))
+                         hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4), **fracs(b, f, t))
         kernels[s] = entry
     def roofline_of(kernel: str, us: float):
         b, f = algorithmic(w, kernel)
@@ -484,6 +520,7 @@ def main() -> int:
                  "achieved": round(f / t / 1e12, 2), "peak": mfma_peak, "unit": "TFLOP/s"}
         r["frac"] = round(r["achieved"] / r["peak"], 4)
         r["traffic"] = load_traffic(kernel, w.name)
+        r.update(fracs(b, f, t))
         r["kernel"] = kernel
         r["kernel_us"] = round(us, 2)
         r["algorithmic_bytes"] = b
@@ -532,7 +569,8 @@ def main() -> int:
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu,
         "forwards": {"ssd_chunk_scan_fwd": chunked, "ssd_fused_fwd": fused},
-        "kernels": kernels, "decode_step": decode, "block_neighbours": block,
+        "kernels": kernels, "copy_GBs": round(copy_gbs, 1), "decode_step": decode,
+        "block_neighbours": block,
         "training_step": train,
     }
     print(json.dumps(out), flush=True)
