@@ -19,10 +19,12 @@ namespace {
 template <typename IO> struct Vec;
 template <> struct Vec<uint16_t> {
   static constexpr int N = 8;
-  __device__ static void load(const uint16_t *p, float (&v)[8]) {
-    const u32x4 q = *reinterpret_cast<const u32x4 *>(p);
+  __device__ static void unpack(const u32x4 &q, float (&v)[8]) {
     v[0] = bf16lo(q.x); v[1] = bf16hi(q.x); v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
     v[4] = bf16lo(q.z); v[5] = bf16hi(q.z); v[6] = bf16lo(q.w); v[7] = bf16hi(q.w);
+  }
+  __device__ static void load(const uint16_t *p, float (&v)[8]) {
+    unpack(*reinterpret_cast<const u32x4 *>(p), v);
   }
   __device__ static void store(uint16_t *p, const float (&v)[8]) {
     *reinterpret_cast<u32x4 *>(p) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
@@ -31,6 +33,10 @@ template <> struct Vec<uint16_t> {
 };
 template <> struct Vec<float> {
   static constexpr int N = 4;
+  __device__ static void unpack(const u32x4 &q, float (&v)[4]) {
+    v[0] = __uint_as_float(q.x); v[1] = __uint_as_float(q.y);
+    v[2] = __uint_as_float(q.z); v[3] = __uint_as_float(q.w);
+  }
   __device__ static void load(const float *p, float (&v)[4]) {
     const f32x4 q = *reinterpret_cast<const f32x4 *>(p);
     v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
@@ -42,11 +48,15 @@ template <> struct Vec<float> {
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
 
-constexpr int kConvRun = 32;  // tokens per thread
+constexpr int kConvRun = 16;  // tokens per thread
 
 // Thread = (channel group of VEC, run of kConvRun tokens), channel groups
-// fastest so a wavefront reads contiguous row segments.  The K-1 previous
-// inputs of the group stay in registers; at a sequence start they reset to 0.
+// fastest so a wavefront reads contiguous row segments.  A run inside one
+// sequence loads its kConvRun + K - 1 input rows up front (16 bytes each, all
+// in flight together; rows before the sequence start read as 0) and then
+// forms its outputs.  A run that crosses a sequence boundary walks its tokens
+// in order instead, keeping the K-1 previous inputs in registers and
+// resetting them to 0 at each sequence start.
 template <typename IO, int K>
 __global__ __launch_bounds__(256) void k_conv1d_silu(const IO *__restrict__ in, int64_t in_stride,
                                                      const float *__restrict__ weight,
@@ -91,6 +101,36 @@ __global__ __launch_bounds__(256) void k_conv1d_silu(const IO *__restrict__ in, 
   } else {
     s_begin = (t0 / seqlen) * seqlen;
     s_end = s_begin + seqlen;
+  }
+  if (t1 <= s_end) {
+    constexpr int NR = kConvRun + K - 1;
+    u32x4 raw[NR];  // raw[i] = the input row t0 - (K-1) + i
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+      const int64_t src = t0 - (K - 1) + i;
+      raw[i] = src >= s_begin && src < t1
+                   ? *reinterpret_cast<const u32x4 *>(in + src * in_stride + c0)
+                   : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kConvRun; ++i) {
+      if (t0 + i < t1) {
+        float acc[V], o[V];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = b[v];
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+          float r[V];
+          Vec<IO>::unpack(raw[i + j], r);
+#pragma unroll
+          for (int v = 0; v < V; ++v) acc[v] += w[v][j] * r[v];
+        }
+#pragma unroll
+        for (int v = 0; v < V; ++v) o[v] = silu(acc[v]);
+        Vec<IO>::store(out + (t0 + i) * out_stride + c0, o);
+      }
+    }
+    return;
   }
   float win[K > 1 ? K - 1 : 1][V];  // win[j] = input at t - (K-1) + j
 #pragma unroll
@@ -142,11 +182,12 @@ __global__ __launch_bounds__(256) void k_conv1d_silu(const IO *__restrict__ in, 
 
 // Block = ROWS consecutive token rows of `width` channels; thread t owns the
 // 16-byte column chunks t, t + 256, ... (up to CACHE of them), whose weights it
-// loads once.  Per row: g = y silu(z) in registers, squares summed over the
-// row (cross-lane shuffles, then one LDS slot per wavefront, double-buffered
-// so one barrier per row suffices), then g * rsqrt(mean + eps) * weight is
-// written; without a weight, g.  Rows wider than 256 * CACHE chunks form g
-// again for the chunks past the cache.
+// loads once.  The next row's y and z chunks are loaded while the current row
+// is reduced and written.  Per row: g = y silu(z) in registers, squares
+// summed over the row (cross-lane shuffles, then one LDS slot per wavefront,
+// double-buffered so one barrier per row suffices), then
+// g * rsqrt(mean + eps) * weight is written; without a weight, g.  Rows wider
+// than 256 * CACHE chunks form g again for the chunks past the cache.
 template <typename IO, int CACHE, int ROWS>
 __global__ __launch_bounds__(256) void k_gate_rmsnorm(const IO *y, const IO *z,
                                                       const float *__restrict__ weight, float eps,
@@ -163,9 +204,23 @@ __global__ __launch_bounds__(256) void k_gate_rmsnorm(const IO *y, const IO *z,
     for (int v = 0; v < V; ++v) wv[k][v] = (weight && i < nvec) ? weight[i * V + v] : 1.f;
   }
   const int64_t r0 = (int64_t)blockIdx.x * ROWS;
+  // raw 16-byte chunks of y and z of one row (zeros past the row's end)
+  auto load_row = [&](int64_t row, u32x4 (&ya)[CACHE], u32x4 (&za)[CACHE]) {
+#pragma unroll
+    for (int k = 0; k < CACHE; ++k) {
+      const int i = tid + 256 * k;
+      const bool ok = row < tokens && i < nvec;
+      ya[k] = ok ? *reinterpret_cast<const u32x4 *>(y + row * width + (int64_t)i * V) : u32x4{0u, 0u, 0u, 0u};
+      za[k] = ok ? *reinterpret_cast<const u32x4 *>(z + row * width + (int64_t)i * V) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  u32x4 yc[CACHE], zc[CACHE];
+  load_row(r0, yc, zc);
   for (int rr = 0; rr < ROWS; ++rr) {
     const int64_t row = r0 + rr;
     if (row >= tokens) break;
+    u32x4 yn[CACHE], zn[CACHE];
+    if (rr + 1 < ROWS) load_row(row + 1, yn, zn);
     const IO *yr = y + row * width;
     const IO *zr = z + row * width;
     IO *orow = out + row * width;
@@ -176,8 +231,8 @@ __global__ __launch_bounds__(256) void k_gate_rmsnorm(const IO *y, const IO *z,
       const int i = tid + 256 * k;
       if (i < nvec) {
         float a[V], c[V];
-        Vec<IO>::load(yr + i * V, a);
-        Vec<IO>::load(zr + i * V, c);
+        Vec<IO>::unpack(yc[k], a);
+        Vec<IO>::unpack(zc[k], c);
 #pragma unroll
         for (int v = 0; v < V; ++v) {
           g[k][v] = a[v] * silu(c[v]);
@@ -223,6 +278,13 @@ __global__ __launch_bounds__(256) void k_gate_rmsnorm(const IO *y, const IO *z,
         o[v] = weight ? gv * scale * weight[i * V + v] : gv;
       }
       Vec<IO>::store(orow + i * V, o);
+    }
+    if (rr + 1 < ROWS) {
+#pragma unroll
+      for (int k = 0; k < CACHE; ++k) {
+        yc[k] = yn[k];
+        zc[k] = zn[k];
+      }
     }
   }
 }
