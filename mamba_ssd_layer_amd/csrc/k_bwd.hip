@@ -106,7 +106,8 @@ __device__ __forceinline__ int swz2(int r) {
 // wavefronts (head hh, half ph); wavefront (hh, ph) keeps rows p in
 // [32 ph, 32 ph + 32) of head hh's g, held transposed like the forward's state
 // (tiles 2q, 2q+1 give lane group g4 the n = 32q + 8 g4 + 0..7).  Chunks in
-// reverse order through a three-slot ring of dy (per head), C and dt.
+// reverse order through an R-slot ring of dy (per head), C and dt, R - 1
+// chunks in flight ahead of the one being computed.
 // MODE: RV_FULL walks a whole sequence from dfinal, saves g where each 64-token
 // pair ends and writes dL/dh0; for few (sequence, head-pair) blocks the sweep is
 // split into 256-token segments: RV_SEGSUM walks a segment from g = 0 and writes
@@ -115,14 +116,17 @@ __device__ __forceinline__ int swz2(int r) {
 // right (gin) and saves g at its pair ends.
 enum { RV_FULL = 0, RV_SEGSUM = 1, RV_SEG = 2 };
 constexpr int kSegChunks = 8;  // 32-token chunks per segment
+// ring slots: kRevSlots - 1 chunks in flight (a fourth slot measured no faster:
+// the sweep is bound by its state-gradient stores, not by load latency)
+constexpr int kRevSlots = 3;
 
-template <int N, int MODE>
+template <int N, int MODE, int R>
 __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     const uint16_t *__restrict__ dy, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Cm, const float *__restrict__ gstart,
     const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows, int H, int G,
     uint16_t *__restrict__ gsave, float *__restrict__ gout, float *__restrict__ aseg) {
-  constexpr int P = 64, CQ = 32, R = 3;
+  constexpr int P = 64, CQ = 32, D = R - 1;  // D chunks in flight ahead
   constexpr int NT = N / 16, KQ = N / 32, NCB = N / 8;
   constexpr int XH = CQ * P * 2, BT = CQ * N * 2, DW = 256;
   constexpr int OY = 0, OC = 2 * XH, OD = OC + BT, SLOT = OD + 4 * DW;
@@ -131,6 +135,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
   static_assert(BCI * 4 * 1024 == BT, "C split over 4 wavefronts");
   constexpr int LDR = 2 + BCI + 1;  // vector-memory ops a wavefront issues per chunk load
   constexpr int SV = 2 * KQ;        // state-gradient stores a wavefront issues per chunk
+  static_assert(R >= 3 && D * SV + (D - 1) * LDR <= 47, "wait counts");
   __shared__ __align__(16) unsigned char smem[AD + 4 * ADW];
 
   int s = -1, hb;
@@ -211,22 +216,28 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
   // the gradient flowing into chunk k from the later chunks is kept where it
   // leaves a 64-token pair (k odd, or the sequence's last chunk)
   auto saves = [&](int k) { return MODE != RV_SEGSUM && ((k & 1) || k == nck - 1); };
-  // reverse order: iteration i handles chunk ke - 1 - i in slot i % 3
-  if (nk > 0) issue(ke - 1, 0);
-  if (nk > 1) issue(ke - 2, 1);
+  // reverse order: iteration i handles chunk ke - 1 - i in slot i % R
+#pragma unroll
+  for (int c = 0; c < D; ++c)
+    if (c < nk) issue(ke - 1 - c, c);
   int sl = 0;
   float asum = 0.f;  // the block's chunks' total decay exponent (RV_SEGSUM)
 #pragma unroll 1
   for (int i = 0; i < nk; ++i) {
     const int k = ke - 1 - i;
     // chunk k's loads have landed once at most the later ops are pending
-    // (completion in issue order): the state-gradient stores of iterations
-    // i-2 and i-1 (SV each where one is stored) and the loads of chunk k-1 (LDR)
-    auto sv = [&](int m) { return saves(ke - 1 - m) ? SV : 0; };
-    wait_vmcnt_dyn((i >= 2 ? sv(i - 2) : 0) + (i + 1 < nk ? LDR : 0) + (i >= 1 ? sv(i - 1) : 0));
+    // (completion in issue order): the prologue's later loads, then per
+    // iteration m < i the loads of iteration m + D (LDR) and m's
+    // state-gradient stores (SV where one is stored)
+    {
+      auto sv = [&](int m) { return saves(ke - 1 - m) ? SV : 0; };
+      int n = i < D ? (min(D, nk) - 1 - i) * LDR : sv(i - D);
+      for (int m = i < D ? 0 : i - D + 1; m < i; ++m) n += (m + D < nk ? LDR : 0) + sv(m);
+      wait_vmcnt_dyn(n);
+    }
     __syncthreads();
-    const int slp = sl == 0 ? 2 : sl - 1;
-    if (k - 2 >= kb) issue(k - 2, slp);
+    const int slp = sl == 0 ? R - 1 : sl - 1;  // slot of iteration i-1, and of i+D
+    if (k - D >= kb) issue(k - D, slp);
     if (saves(k)) {
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
@@ -290,7 +301,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) gst[pt][j] = mfma16b(ct, fy[pt], gst[pt][j]);
     }
-    sl = sl == 2 ? 0 : sl + 1;
+    sl = sl == R - 1 ? 0 : sl + 1;
   }
   // RV_FULL: dL/dh0; RV_SEGSUM: the segment's G_seg and A_seg
   if (MODE != RV_SEG && gout) {
@@ -886,18 +897,18 @@ hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, c
     return hipGetLastError();
   };
   if (nseg == 0) {
-    return N == 64 ? rev(k_bwd_reverse<64, RV_FULL>, rows, dfinal, dinit)
-                   : rev(k_bwd_reverse<128, RV_FULL>, rows, dfinal, dinit);
+    return N == 64 ? rev(k_bwd_reverse<64, RV_FULL, kRevSlots>, rows, dfinal, dinit)
+                   : rev(k_bwd_reverse<128, RV_FULL, kRevSlots>, rows, dfinal, dinit);
   }
-  hipError_t e = N == 64 ? rev(k_bwd_reverse<64, RV_SEGSUM>, nseg, nullptr, gseg)
-                         : rev(k_bwd_reverse<128, RV_SEGSUM>, nseg, nullptr, gseg);
+  hipError_t e = N == 64 ? rev(k_bwd_reverse<64, RV_SEGSUM, kRevSlots>, nseg, nullptr, gseg)
+                         : rev(k_bwd_reverse<128, RV_SEGSUM, kRevSlots>, nseg, nullptr, gseg);
   if (e != hipSuccess) return e;
   const int PN = 64 * N;
   hipLaunchKernelGGL(k_bwd_gpass, dim3(PN / 1024, H, rows), dim3(256), 0, stream, gseg, aseg,
                      dfinal, cu, L, T, rows, H, PN, gin, dinit);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  return N == 64 ? rev(k_bwd_reverse<64, RV_SEG>, nseg, gin, nullptr)
-                 : rev(k_bwd_reverse<128, RV_SEG>, nseg, gin, nullptr);
+  return N == 64 ? rev(k_bwd_reverse<64, RV_SEG, kRevSlots>, nseg, gin, nullptr)
+                 : rev(k_bwd_reverse<128, RV_SEG, kRevSlots>, nseg, gin, nullptr);
 }
 
 hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,
