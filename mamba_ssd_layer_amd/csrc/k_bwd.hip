@@ -241,15 +241,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     if (saves(k)) {
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        uint16_t *dst = gsave + ((pbase + (k >> 1)) * H + h) * (int64_t)(P * N) +
-                        (int64_t)(32 * ph + 16 * pt + c16) * N + 8 * g4;
+        u32x4 pk[KQ];  // row p = 32 ph + 16 pt + c16, n = 32 q + 8 g4 + 0..7
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
           const f32x4 u = gst[pt][2 * q], v = gst[pt][2 * q + 1];
-          *reinterpret_cast<u32x4 *>(dst + 32 * q) =
-              u32x4{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
-                    pack_bf16x2(v.z, v.w)};
+          pk[q] = u32x4{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
+                        pack_bf16x2(v.z, v.w)};
         }
+        store_rows128(gsave + ((pbase + (k >> 1)) * H + h) * (int64_t)(P * N) +
+                          (int64_t)(32 * ph + 16 * pt) * N,
+                      N, pk, c16, g4);
       }
     }
     const unsigned char *ys = smem + sl * SLOT + OY + hh * XH;

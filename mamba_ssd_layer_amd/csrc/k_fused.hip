@@ -273,15 +273,16 @@ void k_ssd_fused(
       const float e = exp2_fast(lam);
 #pragma unroll
       for (int pt = 0; pt < 2; ++pt) {
-        uint16_t *dst = hsave + ((pbase + (k >> 1)) * H + h) * (int64_t)(P * N) +
-                        (int64_t)(32 * ph + 16 * pt + c16) * N + 8 * g4;
+        u32x4 pk[KQ];  // row p = 32 ph + 16 pt + c16, n = 32 q + 8 g4 + 0..7
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
           const f32x4 u = hst[pt][2 * q] * e, v = hst[pt][2 * q + 1] * e;
-          *reinterpret_cast<u32x4 *>(dst + 32 * q) =
-              u32x4{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
-                    pack_bf16x2(v.z, v.w)};
+          pk[q] = u32x4{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
+                        pack_bf16x2(v.z, v.w)};
         }
+        store_rows128(hsave + ((pbase + (k >> 1)) * H + h) * (int64_t)(P * N) +
+                          (int64_t)(32 * ph + 16 * pt) * N,
+                      N, pk, c16, g4);
       }
     }
     const int slp = sl == 0 ? R - 1 : sl - 1;  // slot of chunk k-1, and of chunk k+D

@@ -217,6 +217,36 @@ __device__ __forceinline__ void seq_range(const int32_t *cu, int s, int64_t L, i
   }
 }
 
+// Stores 16 rows of a bf16 tile, 8 * KQ 16-byte chunks a row, held as lane
+// (c16 = lane % 16, g4 = lane / 16) owning chunk 4q + g4 of row c16 in v[q].
+// Storing v[q] as it stands writes 64-byte pieces of 16 rows; instead the
+// lanes of rows c16 and c16 + 8 trade the halves of each pair v[2m], v[2m+1]
+// (a DPP rotate by 8 lanes within each 16-lane row), so that each store
+// writes whole 128-byte segments of 8 rows.  The same number of stores is
+// issued.  row0 points at the first of the 16 rows; ld is the row pitch in
+// elements.
+template <int KQ>
+__device__ __forceinline__ void store_rows128(uint16_t *row0, int64_t ld, const u32x4 (&v)[KQ],
+                                              int c16, int g4) {
+  static_assert(KQ % 2 == 0, "pairs of 64-byte pieces");
+  auto ror8 = [](uint32_t a) {
+    return static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(a), 0x128, 0xF, 0xF, false));
+  };
+  const bool lo = c16 < 8;
+  const int r = c16 & 7, ch = g4 + 4 * (c16 >> 3);
+#pragma unroll
+  for (int m = 0; m < KQ / 2; ++m) {
+    const u32x4 x = v[2 * m], y = v[2 * m + 1];
+    const u32x4 rx{ror8(x.x), ror8(x.y), ror8(x.z), ror8(x.w)};
+    const u32x4 ry{ror8(y.x), ror8(y.y), ror8(y.z), ror8(y.w)};
+    // rows 0-7: own piece (chunk g4) or row c16 - 8's second piece (chunk 4 + g4);
+    // rows 8-15 likewise from the first pieces
+    const u32x4 a = lo ? x : ry, b = lo ? rx : y;
+    *reinterpret_cast<u32x4 *>(row0 + r * ld + 8 * (8 * m + ch)) = a;
+    *reinterpret_cast<u32x4 *>(row0 + (8 + r) * ld + 8 * (8 * m + ch)) = b;
+  }
+}
+
 // Packed batches (cu_seqlens): wave-parallel walks over the sequences, 64 a
 // step (lane i reads sequence i0 + i), so a block finds its place in a few
 // rounds of loads instead of one dependent load per sequence.  Every lane of
