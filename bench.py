@@ -52,9 +52,10 @@ def algorithmic(w, stage: str):
     Per token (T tokens, nc chunks, S sequences, s = element bytes of x/B/C/y,
     h = element bytes of the hprev buffer):
       chunk_cumsum   bytes 8 H                      (dt in, cumulative decay out)
-      chunk_state    bytes s H P + s G N + 8 H, plus 4 H P N per chunk (S out)
+      chunk_state    bytes s H P + s G N + 8 H, plus h H P N per chunk (S out, in
+                     the io precision like hprev)
                      flops 2 H P N
-      state_passing  bytes (4 + h) H P N per chunk, plus 4 H P N per sequence for
+      state_passing  bytes 2 h H P N per chunk (S in, hprev out), plus 4 H P N per sequence for
                      the final state (and 4 H P N more when an initial state is read)
       chunk_scan     bytes 2 s H P + 2 s G N + 8 H, plus h H P N per chunk
                      flops H (2 P N + (Q + 1) P) + G (Q + 1) N  (causal pairs only,
@@ -72,10 +73,10 @@ def algorithmic(w, stage: str):
     if stage == "chunk_cumsum":
         return 8 * T * H, 0
     if stage == "chunk_state":
-        return s * T * H * P + s * T * G * N + 8 * T * H + 4 * nc * H * P * N, 2 * T * H * P * N
+        return s * T * H * P + s * T * G * N + 8 * T * H + hsz * nc * H * P * N, 2 * T * H * P * N
     if stage == "state_passing":
         init = 4 * nseq * H * P * N if w.h0 is not None else 0
-        return (4 + hsz) * nc * H * P * N + 4 * nseq * H * P * N + init, 0
+        return 2 * hsz * nc * H * P * N + 4 * nseq * H * P * N + init, 0
     if stage == "chunk_scan":
         b = 2 * s * T * H * P + 2 * s * T * G * N + 8 * T * H + hsz * nc * H * P * N
         f = T * (H * (2 * P * N + (Q + 1) * P) + G * (Q + 1) * N)

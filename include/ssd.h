@@ -102,8 +102,9 @@ typedef struct {
  *                                 start; positions past a partial chunk's end hold
  *                                 the chunk's last value
  *   dtq    float [nc_max][H][Q]   dt transposed to chunk-major, 0 past the end
- *   states float [nc_max][H][P][N] chunk states S_c (decay-weighted sum of
- *                                 dt_l x_l B_l^T over the chunk)
+ *   states io    [nc_max][H][P][N] chunk states S_c (decay-weighted sum of
+ *                                 dt_l x_l B_l^T over the chunk, summed in fp32
+ *                                 and rounded once to the io type)
  *   hprev  io    [nc_max][H][P][N] state entering each chunk
  *   chunk_table  int32 [nc_max][4] (sequence, first token, length, 0)   packed only
  *   chunk_dir    int32 [nseq + 2]  first chunk of each sequence, then the total,

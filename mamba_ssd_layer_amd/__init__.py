@@ -120,6 +120,7 @@ class SSDForward:
         d, L, Q = self.dims, self.layout, self.chunk_len
         nc, H, P, N = L.nc_max, d.nheads, d.headdim, d.dstate
         ws = self.workspace
+        io = torch.bfloat16 if d.io_dtype == SSD_BF16 else torch.float32  # states and hprev
 
         def sl(off, n, dtype):
             nbytes = n * torch.tensor([], dtype=dtype).element_size()
@@ -130,10 +131,9 @@ class SSDForward:
         if name == "dtq":
             return sl(L.dtq_offset, nc * H * Q, torch.float32).view(nc, H, Q)
         if name == "states":
-            return sl(L.states_offset, nc * H * P * N, torch.float32).view(nc, H, P, N)
+            return sl(L.states_offset, nc * H * P * N, io).view(nc, H, P, N)
         if name == "hprev":
-            dt_ = torch.bfloat16 if d.io_dtype == SSD_BF16 else torch.float32
-            return sl(L.hprev_offset, nc * H * P * N, dt_).view(nc, H, P, N)
+            return sl(L.hprev_offset, nc * H * P * N, io).view(nc, H, P, N)
         if name == "chunk_table":
             return sl(L.chunk_table_offset, nc * 4, torch.int32).view(nc, 4)
         if name == "chunk_dir":

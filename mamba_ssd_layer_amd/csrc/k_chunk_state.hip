@@ -14,7 +14,8 @@
 // MFMA B-operands in registers: its 32x32 output tile's 32 columns n over all
 // Q tokens, read by transposing LDS reads (ds_read_b64_tr_b16) so the
 // contracted token index runs along each lane's registers.  Per head:
-//   1. S of the previous head, staged in LDS, is stored (16-byte segments);
+//   1. S of the previous head, staged in LDS, is rounded to bf16 (the io
+//      precision, like the hprev the hand-off writes) and stored;
 //      this head's x, already in its ring slot, is scaled in place by w_l in
 //      fp32 and rounded once to bf16;
 //   2. the next head's x, acum and dt go into the other slot by direct-to-LDS
@@ -36,7 +37,7 @@ template <int Q, int N>
 __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm, const float *__restrict__ acum,
     const float *__restrict__ dtq, ChunkGeom geom, int nc, int H, int G, int hb, int nkb,
-    float *__restrict__ states) {
+    uint16_t *__restrict__ states) {
   constexpr int P = 64;
   constexpr int NT = 512, NW = 8;
   constexpr int TPN = P / 32;                            // p tiles
@@ -107,7 +108,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
                  smem + (slot ? AD1 : AD0) + wave * (Q * 4));
   };
   auto store_s = [&](int t, int hh) {
-    float *out = states + ((int64_t)c * H + hh) * (P * N);
+    uint16_t *out = states + ((int64_t)c * H + hh) * (P * N);
 #pragma unroll
     for (int i = 0; i < P * N / 4 / NT; ++i) {
       const int u = t + i * NT;
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
 #pragma unroll
       for (int k = 1; k < KSPLIT; ++k)
         v += *reinterpret_cast<const f32x4 *>(smem + SS + k * SSB + (p * LSS + 4 * c4) * 4);
-      *reinterpret_cast<f32x4 *>(out + p * N + 4 * c4) = v;
+      *reinterpret_cast<u32x2 *>(out + p * N + 4 * c4) = u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
     }
   };
 
@@ -206,7 +207,7 @@ bool chunk_state_bf16_supported(int P, int N, int Q) {
 
 template <int Q, int P, int N>
 static void launch_cs(const void *x, const void *B, const float *acum, const float *dtq,
-                      float *states, const Geometry &geo, hipStream_t stream) {
+                      uint16_t *states, const Geometry &geo, hipStream_t stream) {
   static_assert(P == 64, "head dimension");
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
   int nkb = 1;
@@ -218,7 +219,7 @@ static void launch_cs(const void *x, const void *B, const float *acum, const flo
 
 template <int Q>
 static bool dispatch_cs_n(const void *x, const void *B, const float *acum, const float *dtq,
-                          float *states, const Geometry &geo, hipStream_t stream) {
+                          uint16_t *states, const Geometry &geo, hipStream_t stream) {
   switch (geo.N) {
     case 64: launch_cs<Q, 64, 64>(x, B, acum, dtq, states, geo, stream); return true;
     case 128: launch_cs<Q, 64, 128>(x, B, acum, dtq, states, geo, stream); return true;
@@ -228,8 +229,9 @@ static bool dispatch_cs_n(const void *x, const void *B, const float *acum, const
 }
 
 hipError_t launch_chunk_state_bf16(const void *x, const void *B, const float *acum,
-                                   const float *dtq, float *states, const Geometry &geo,
+                                   const float *dtq, void *states_v, const Geometry &geo,
                                    hipStream_t stream) {
+  uint16_t *states = static_cast<uint16_t *>(states_v);
   if (geo.nc_max == 0) return hipSuccess;
   if (!chunk_state_bf16_supported(geo.P, geo.N, geo.Q)) return hipErrorInvalidValue;
   bool ok = false;

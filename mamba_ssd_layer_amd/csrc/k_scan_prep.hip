@@ -188,14 +188,16 @@ hipError_t launch_chunk_cumsum(const float *dt, const float *A, const Geometry &
 // Thread = 4 consecutive state elements of one (sequence, head); it walks the
 // sequence's chunks in order: hprev[c] = h; h = exp(acum_last[c]) * h + S[c].
 // Loads of S are issued kBatch chunks ahead so the serial FMA chain does not
-// wait on HBM latency one chunk at a time.
+// wait on HBM latency one chunk at a time.  S and hprev are bf16 for bf16 io
+// (kBf16), fp32 otherwise; the carried state is fp32 either way.
 constexpr int kPassThreads = 256;
 constexpr int kPassVec = 4;
-constexpr int kBatch = 8;
+// chunks whose S loads are in flight together: 128 bytes a thread either way
+template <bool kBf16> constexpr int kBatch = kBf16 ? 16 : 8;
 
 template <bool kBf16>
 __global__ __launch_bounds__(kPassThreads) void k_state_passing(
-    const float *__restrict__ states, void *__restrict__ hprev_v, const float *__restrict__ acum,
+    const void *__restrict__ states_v, void *__restrict__ hprev_v, const float *__restrict__ acum,
     const float *init, float *final_state, int H, int PN, int Q, int nc_row,
     const int32_t *__restrict__ dir) {
   const int e0 = (blockIdx.x * kPassThreads + threadIdx.x) * kPassVec;
@@ -213,19 +215,28 @@ __global__ __launch_bounds__(kPassThreads) void k_state_passing(
   f32x4 st = {0.f, 0.f, 0.f, 0.f};
   const int64_t soff = ((int64_t)s * H + h) * PN + e0;
   if (init) st = *reinterpret_cast<const f32x4 *>(init + soff);
-  for (int c = cb; c < ce; c += kBatch) {
-    f32x4 sv[kBatch];
-    float dl[kBatch];
+  constexpr int NB = kBatch<kBf16>;
+  for (int c = cb; c < ce; c += NB) {
+    // raw loads only here (bf16 pairs are widened where they are used, so no
+    // load waits for another)
+    f32x4 sv[NB];
+    u32x2 sb[NB];
+    float dl[NB];
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < NB; ++k) {
       if (c + k < ce) {
         const int64_t ch = (int64_t)(c + k) * H + h;
-        sv[k] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(states + ch * PN + e0));
+        if (kBf16)
+          sb[k] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x2 *>(static_cast<const uint16_t *>(states_v) + ch * PN + e0));
+        else
+          sv[k] = __builtin_nontemporal_load(
+              reinterpret_cast<const f32x4 *>(static_cast<const float *>(states_v) + ch * PN + e0));
         dl[k] = acum[ch * Q + Q - 1];
       }
     }
 #pragma unroll
-    for (int k = 0; k < kBatch; ++k) {
+    for (int k = 0; k < NB; ++k) {
       if (c + k < ce) {
         const int64_t ch = (int64_t)(c + k) * H + h;
         if (kBf16) {
@@ -237,21 +248,24 @@ __global__ __launch_bounds__(kPassThreads) void k_state_passing(
           *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(hprev_v) + ch * PN + e0) = st;
         }
         const float d = __expf(dl[k]);
-        st = d * st + sv[k];
+        if (kBf16)
+          st = d * st + f32x4{bf16lo(sb[k].x), bf16hi(sb[k].x), bf16lo(sb[k].y), bf16hi(sb[k].y)};
+        else
+          st = d * st + sv[k];
       }
     }
   }
   if (final_state) *reinterpret_cast<f32x4 *>(final_state + soff) = st;
 }
 
-hipError_t launch_state_passing(const float *states, void *hprev, bool hprev_bf16,
+hipError_t launch_state_passing(const void *states, void *hprev, bool bf16,
                                 const float *acum, const float *init, float *final_state,
                                 const Geometry &geo, hipStream_t stream) {
   const int PN = geo.P * geo.N;
   if (geo.nrows == 0) return hipSuccess;
   const dim3 grid((unsigned)((PN / kPassVec + kPassThreads - 1) / kPassThreads), (unsigned)geo.H,
                   (unsigned)geo.nrows);
-  if (hprev_bf16) {
+  if (bf16) {
     hipLaunchKernelGGL(k_state_passing<true>, grid, dim3(kPassThreads), 0, stream, states, hprev,
                        acum, init, final_state, geo.H, PN, geo.Q, geo.nc_row,
                        geo.packed ? geo.dir : nullptr);

@@ -82,7 +82,7 @@ ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
   w.dtq_offset = off;
   off = align_up(off + nch * Q * sizeof(float));
   w.states_offset = off;
-  off = align_up(off + nch * (size_t)(P * N) * sizeof(float));
+  off = align_up(off + nch * (size_t)(P * N) * p.io_size);
   w.hprev_offset = off;
   off = align_up(off + nch * (size_t)(P * N) * p.io_size);
   if (g.packed) {
@@ -191,17 +191,18 @@ ssd_status run_cumsum(const float *dt, const float *A, const int32_t *cu, const 
 ssd_status run_state(const void *x, const void *B, const Plan &p, void *ws, hipStream_t st) {
   const float *acum = ws_ptr<float>(ws, p.ws.acum_offset);
   const float *dtq = ws_ptr<float>(ws, p.ws.dtq_offset);
-  float *states = ws_ptr<float>(ws, p.ws.states_offset);
+  void *states = ws_ptr<void>(ws, p.ws.states_offset);
   if (p.bf16)
     return hip_status(ssd::launch_chunk_state_bf16(x, B, acum, dtq, states, p.geo, st));
   return hip_status(ssd::launch_chunk_state_f32(static_cast<const float *>(x),
-                                                static_cast<const float *>(B), acum, dtq, states,
+                                                static_cast<const float *>(B), acum, dtq,
+                                                static_cast<float *>(states),
                                                 p.geo, st));
 }
 
 ssd_status run_pass(const float *init, float *fin, const Plan &p, void *ws, hipStream_t st) {
   return hip_status(ssd::launch_state_passing(
-      ws_ptr<float>(ws, p.ws.states_offset), ws_ptr<void>(ws, p.ws.hprev_offset), p.bf16,
+      ws_ptr<void>(ws, p.ws.states_offset), ws_ptr<void>(ws, p.ws.hprev_offset), p.bf16,
       ws_ptr<float>(ws, p.ws.acum_offset), init, fin, p.geo, st));
 }
 

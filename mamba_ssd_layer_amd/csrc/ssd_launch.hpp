@@ -24,13 +24,14 @@ hipError_t launch_chunk_table(const int32_t *cu_seqlens, const Geometry &geo, in
                               int32_t *dir, hipStream_t stream);
 hipError_t launch_chunk_cumsum(const float *dt, const float *A, const Geometry &geo, float *acum,
                                float *dtq, hipStream_t stream);
-hipError_t launch_state_passing(const float *states, void *hprev, bool hprev_bf16,
+// states and hprev are bf16 when bf16 is set, else fp32
+hipError_t launch_state_passing(const void *states, void *hprev, bool bf16,
                                 const float *acum, const float *init, float *final_state,
                                 const Geometry &geo, hipStream_t stream);
 // bf16 io, MFMA contractions
 bool chunk_state_bf16_supported(int P, int N, int Q);
 hipError_t launch_chunk_state_bf16(const void *x, const void *B, const float *acum,
-                                   const float *dtq, float *states, const Geometry &geo,
+                                   const float *dtq, void *states, const Geometry &geo,
                                    hipStream_t stream);
 bool chunk_scan_bf16_supported(int P, int N, int Q);
 hipError_t launch_chunk_scan_bf16(const void *x, const void *B, const void *C, const float *D,

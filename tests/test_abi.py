@@ -54,8 +54,8 @@ def _ws_expected(batch, L_, H, P, N, G, Q, nseq=0, io=2):
         nc = batch * math.ceil(L_ / Q)
     off = al(nc * H * Q * 4)
     off = al(off + nc * H * Q * 4)
-    off = al(off + nc * H * P * N * 4)
-    off = al(off + nc * H * P * N * io)
+    off = al(off + nc * H * P * N * io)  # chunk states, io precision
+    off = al(off + nc * H * P * N * io)  # hprev
     if nseq:
         off = al(off + nc * 16)
         off = al(off + (nseq + 2) * 4)

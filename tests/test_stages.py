@@ -82,7 +82,7 @@ def test_stages(name):
     # stage 2: chunk states
     plan.state(t["x"], t["B"])
     torch.cuda.synchronize()
-    S = plan.view("states").cpu().numpy()
+    S = plan.view("states").float().cpu().numpy()
     e = rel(S[cidx], it["S"])
     say(f"  {name}: chunk states rel err {e:.3e}")
     assert e <= tol
