@@ -707,10 +707,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
           u32x2{pack_bf16x2(mv[0], mv[1]), pack_bf16x2(mv[2], mv[3])};
       *reinterpret_cast<u32x2 *>(opel + qb * 1024 + lane * 16 + qa * 8) =
           u32x2{pack_bf16x2(elv[0], elv[1]), pack_bf16x2(elv[2], elv[3])};
-      t1 += __shfl_xor(t1, 16, 64);
-      t1 += __shfl_xor(t1, 32, 64);
-      ck += __shfl_xor(ck, 16, 64);
-      ck += __shfl_xor(ck, 32, 64);
+      t1 = xsum32(xsum16(t1));
+      ck = xsum32(xsum16(ck));
       if (lane < 16) {
         part[PC1 + 32 * qa + sx] = t1;
         part[PCK + 32 * qa + sx] = ck;
@@ -806,10 +804,8 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
       float qv = bf16lo(xv.x) * gb.x + bf16hi(xv.x) * gb.y + bf16lo(xv.y) * gb.z + bf16hi(xv.y) * gb.w;
       // v_l partial dy_l . (h_s C_l) (the same rows of dy: l = sx)
       float vv = bf16lo(dv.x) * hc.x + bf16hi(dv.x) * hc.y + bf16lo(dv.y) * hc.z + bf16hi(dv.y) * hc.w;
-      qv += __shfl_xor(qv, 16, 64);
-      qv += __shfl_xor(qv, 32, 64);
-      vv += __shfl_xor(vv, 16, 64);
-      vv += __shfl_xor(vv, 32, 64);
+      qv = xsum32(xsum16(qv));
+      vv = xsum32(xsum16(vv));
       if (lane < 16) {
         part[PQ + 32 * pt + sx] = qv;
         part[PV + 32 * pt + sx] = vv;
@@ -822,8 +818,7 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
         const int r = c16 - 4 * g4;
         float gh = r == 0 ? gh4.x : r == 1 ? gh4.y : r == 2 ? gh4.z : r == 3 ? gh4.w : 0.f;
         gh = rowsum16(gh);
-        gh += __shfl_xor(gh, 16, 64);
-        gh += __shfl_xor(gh, 32, 64);
+        gh = xsum32(xsum16(gh));
         if (lane == 0) part[PGH + pt] = gh;
       }
     }

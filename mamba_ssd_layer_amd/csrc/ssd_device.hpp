@@ -217,6 +217,19 @@ __device__ __forceinline__ void seq_range(const int32_t *cu, int s, int64_t L, i
   }
 }
 
+// v plus its value in lane ^ 16 (lane ^ 32): gfx950's permlane swaps exchange
+// the halves of a register pair without going through LDS; with both
+// operands v, lane i receives {v_i, v_partner} in some order, and both lanes
+// of a pair form the same sum.
+__device__ __forceinline__ float xsum16(float v) {
+  const auto q = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+__device__ __forceinline__ float xsum32(float v) {
+  const auto q = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(q[0]) + __uint_as_float(q[1]);
+}
+
 // Stores 16 rows of a bf16 tile, 8 * KQ 16-byte chunks a row, held as lane
 // (c16 = lane % 16, g4 = lane / 16) owning chunk 4q + g4 of row c16 in v[q].
 // Storing v[q] as it stands writes 64-byte pieces of 16 rows; instead the
