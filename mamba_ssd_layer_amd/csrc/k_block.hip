@@ -184,7 +184,7 @@ __global__ __launch_bounds__(256) void k_conv1d_silu(const IO *__restrict__ in, 
 // 16-byte column chunks t, t + 256, ... (up to CACHE of them), whose weights it
 // loads once.  The next row's y and z chunks are loaded while the current row
 // is reduced and written.  Per row: g = y silu(z) in registers, squares
-// summed over the row (cross-lane shuffles, then one LDS slot per wavefront,
+// summed over the row (DPP and permlane sums in the wavefront, then one LDS slot per wavefront,
 // double-buffered so one barrier per row suffices), then
 // g * rsqrt(mean + eps) * weight is written; without a weight, g.  Rows wider
 // than 256 * CACHE chunks form g again for the chunks past the cache.
@@ -252,8 +252,7 @@ __global__ __launch_bounds__(256) void k_gate_rmsnorm(const IO *y, const IO *z,
     }
     float scale = 1.f;
     if (weight) {
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off, 64);
+      ss = wave_sum(ss);
       if ((tid & 63) == 0) part[rr & 1][tid >> 6] = ss;
       __syncthreads();
       scale = rsqrtf((part[rr & 1][0] + part[rr & 1][1] + part[rr & 1][2] + part[rr & 1][3]) / width + eps);

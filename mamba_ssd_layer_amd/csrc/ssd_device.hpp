@@ -230,6 +230,16 @@ __device__ __forceinline__ float xsum32(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
+// Sum over all 64 lanes, every lane receiving it: within each 16-lane row by
+// DPP (quad swaps, half-row and row mirrors), then across rows by permlane swaps.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+  return xsum32(xsum16(v));
+}
+
 // Stores 16 rows of a bf16 tile, 8 * KQ 16-byte chunks a row, held as lane
 // (c16 = lane % 16, g4 = lane / 16) owning chunk 4q + g4 of row c16 in v[q].
 // Storing v[q] as it stands writes 64-byte pieces of 16 rows; instead the
