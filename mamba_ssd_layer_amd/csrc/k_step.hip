@@ -82,9 +82,8 @@ __global__ __launch_bounds__(256) void k_step(const IO *__restrict__ x, const fl
       *reinterpret_cast<f32x4 *>(st + (int64_t)p * N) = hv;
       part = cv[0] * hv.x + cv[1] * hv.y + cv[2] * hv.z + cv[3] * hv.w;
     }
-    // every lane takes part in the shuffles; a row's TPR lanes share `valid`
-#pragma unroll
-    for (int off = TPR / 2; off >= 1; off >>= 1) part += __shfl_xor(part, off, 64);
+    // every lane takes part in the lane exchanges; a row's TPR lanes share `valid`
+    part = group_sum<TPR>(part);
     if (valid && n4 == 0) st1(yr + p, part + Dh * xp);
   }
 }

@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 namespace ssd {
@@ -230,15 +231,24 @@ __device__ __forceinline__ float xsum32(float v) {
   return __uint_as_float(q[0]) + __uint_as_float(q[1]);
 }
 
-// Sum over all 64 lanes, every lane receiving it: within each 16-lane row by
-// DPP (quad swaps, half-row and row mirrors), then across rows by permlane swaps.
-__device__ __forceinline__ float wave_sum(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
-  return xsum32(xsum16(v));
+// Sum over aligned groups of W consecutive lanes (W a power of two up to 64),
+// every lane of a group receiving it: within 16-lane rows by DPP (quad swaps,
+// half-row and row mirrors), across rows by permlane swaps.
+template <int W>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "power of two");
+  auto dpp = [](float a, auto ctrl) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(a), decltype(ctrl)::value, 0xF, 0xF, false));
+  };
+  if (W >= 2) v += dpp(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1, 0, 3, 2]
+  if (W >= 4) v += dpp(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2, 3, 0, 1]
+  if (W >= 8) v += dpp(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  if (W >= 16) v += dpp(v, std::integral_constant<int, 0x140>{}); // row_mirror
+  if (W >= 32) v = xsum16(v);
+  if (W >= 64) v = xsum32(v);
+  return v;
 }
+__device__ __forceinline__ float wave_sum(float v) { return group_sum<64>(v); }
 
 // Stores 16 rows of a bf16 tile, 8 * KQ 16-byte chunks a row, held as lane
 // (c16 = lane % 16, g4 = lane / 16) owning chunk 4q + g4 of row c16 in v[q].
