@@ -18,8 +18,10 @@
 //      precision, like the hprev the hand-off writes) and stored;
 //      this head's x, already in its ring slot, is scaled in place by w_l in
 //      fp32 and rounded once to bf16;
-//   2. the next head's x, acum and dt go into the other slot by direct-to-LDS
-//      loads and land while this head computes;
+//   2. a later head's x, acum and dt go into the slot the previous head
+//      freed by direct-to-LDS loads (a three-slot ring keeps two heads in
+//      flight where the LDS allows, else two slots one head); each wavefront
+//      waits for exactly the operations it issued after a head's loads;
 //   3. each wavefront forms its tile(s) on v_mfma_f32_32x32x16_bf16 from
 //      transposing reads of the scaled x, and stages them in LDS (fp32).
 // With N = 64 the four tiles are split over K between wavefront pairs and the
@@ -33,7 +35,16 @@ namespace ssd {
 
 namespace {
 
-template <int Q, int N>
+// LDS bytes of k_chunk_state_hb<Q, N, R> (P = 64, 8 wavefronts): R slots of a
+// head's x and its acum/dt, the S staging (split over K when there are fewer
+// 32x32 tiles than wavefronts); B is staged over the same space first.
+constexpr int cs_lds_bytes(int Q, int N, int R) {
+  const int tiles = 2 * (N / 32), ksplit = tiles < 8 ? 8 / tiles : 1;
+  const int main = R * (Q * 64 * 2) + R * (2 * Q * 4) + ksplit * 64 * (N + 8) * 4;
+  return main > Q * N * 2 ? main : Q * N * 2;
+}
+
+template <int Q, int N, int R>
 __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm, const float *__restrict__ acum,
     const float *__restrict__ dtq, ChunkGeom geom, int nc, int H, int G, int hb, int nkb,
@@ -53,10 +64,14 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
   constexpr int SSB = P * LSS * 4;
   constexpr int XI = XB / 1024 / NW, BI = BB / 1024 / NW;
   static_assert(XI * NW * 1024 == XB && BI * NW * 1024 == BB, "1 KB loads");
-  // [XS0][XS1][AD0][AD1][SS x KSPLIT]; B is staged over all of it first
-  constexpr int XS0 = 0, XS1 = XB, AD0 = 2 * XB, AD1 = AD0 + ADB, SS = AD1 + ADB;
+  // [XS x R][AD x R][SS x KSPLIT]; B is staged over all of it first.  R ring
+  // slots: the loads of R - 1 heads are in flight while a head computes.
+  constexpr int AD = R * XB, SS = AD + R * ADB;
   constexpr int MAIN = SS + KSPLIT * SSB;
+  constexpr int SC = P * N / 4 / NT;  // S stores a thread issues per head
+  static_assert(R >= 2 && SC * NT * 4 == P * N, "ring, S stores");
   constexpr int TOTAL = MAIN > BB ? MAIN : BB;
+  static_assert(TOTAL == cs_lds_bytes(Q, N, R) && TOTAL <= 160 * 1024, "LDS");
   __shared__ __align__(16) unsigned char smem[TOTAL];
 
   int c, hk;
@@ -96,7 +111,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
   };
   auto issue_head = [&](int lane, int hh, int slot) {
     const uint16_t *xb = x + xrow0 + (int64_t)hh * P;
-    unsigned char *xs = smem + (slot ? XS1 : XS0);
+    unsigned char *xs = smem + slot * XB;
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       const int m = (wave * XI + i) * 64 + lane;
@@ -105,8 +120,11 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
     }
     if (wave < 2 && lane < Q / 4)  // wavefront 0: acum, 1: dt
       load_lds16((wave == 0 ? acum : dtq) + ((int64_t)c * H + hh) * Q + lane * 4,
-                 smem + (slot ? AD1 : AD0) + wave * (Q * 4));
+                 smem + AD + slot * ADB + wave * (Q * 4));
   };
+  // vector-memory ops a wavefront issues per head load (x pieces, plus acum
+  // or dt for wavefronts 0 and 1)
+  const int LC = XI + (wave < 2 ? 1 : 0);
   auto store_s = [&](int t, int hh) {
     uint16_t *out = states + ((int64_t)c * H + hh) * (P * N);
 #pragma unroll
@@ -142,22 +160,37 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
     for (int ks = 0; ks < KS; ++ks) bop[i][ks] = tr_op(tid & 63, smem, NCB, 16 * (kp * KS + ks), 32 * tn);
   }
   __syncthreads();  // B consumed: the rings are free
-  issue_head(tid & 63, hfirst, 0);
+#pragma unroll
+  for (int j = 0; j < R - 1; ++j)
+    if (j < nh) issue_head(tid & 63, hfirst + j, j);
 
+  int slot = 0;
 #pragma unroll 1
   for (int hi = 0; hi < nh; ++hi) {
     const int hh = hfirst + hi;
-    const int slot = hi & 1;
     // lane indices re-read per head, so lane-dependent addresses are formed
     // where they are used rather than kept live across heads
     int t = tid;
     asm volatile("" : "+v"(t));
     const int lane = t & 63, col = lane & 31, kg = lane >> 5;
-    unsigned char *xs = smem + (slot ? XS1 : XS0);
-    const float *sa = reinterpret_cast<const float *>(smem + (slot ? AD1 : AD0));
+    unsigned char *xs = smem + slot * XB;
+    const float *sa = reinterpret_cast<const float *>(smem + AD + slot * ADB);
     const float *sd = sa + Q;
 
-    wait_vmcnt<0>();  // this head's x, acum, dt; the stores of S two heads back
+    {
+      // this head's loads have landed once at most the ops issued after them
+      // are pending (completion in issue order): the prologue's later loads,
+      // then per head m < hi the S stores of head m - 1 and the loads of head
+      // m + R - 1
+      int n = 0;
+      if (hi < R - 1) {
+        n = (min(R - 1, nh) - 1 - hi) * LC;
+        for (int m = 0; m < hi; ++m) n += (m > 0 ? SC : 0) + (m + R - 1 < nh ? LC : 0);
+      } else {
+        for (int m = hi - R + 2; m < hi; ++m) n += SC + (m + R - 1 < nh ? LC : 0);
+      }
+      wait_vmcnt_dyn(n);
+    }
     __syncthreads();  // ... for every thread; the previous head is done everywhere
     if (hi > 0) store_s(t, hh - 1);
     {  // x_l *= w_l in place (fp32, one rounding)
@@ -178,7 +211,8 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
       }
     }
     __syncthreads();  // scaled x ready; staged S read out
-    if (hi + 1 < nh) issue_head(lane, hh + 1, slot ^ 1);
+    const int slp = slot == 0 ? R - 1 : slot - 1;  // head hi - 1's slot, free now
+    if (hi + R - 1 < nh) issue_head(lane, hh + R - 1, slp);
 
 #pragma unroll
     for (int i = 0; i < TPW; ++i) {
@@ -194,6 +228,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
 #pragma unroll
       for (int r = 0; r < 16; ++r) ss[(tp * 32 + acc_row(r, kg)) * LSS + tn * 32 + col] = acc[r];
     }
+    slot = slot == R - 1 ? 0 : slot + 1;
   }
   __syncthreads();
   store_s(tid, hfirst + nh - 1);
@@ -212,7 +247,9 @@ static void launch_cs(const void *x, const void *B, const float *acum, const flo
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
   int nkb = 1;
   const int hb = pick_heads_per_block(geo.nc_max, geo.H, geo.G, device_cus(), 1.0, nkb);
-  hipLaunchKernelGGL((k_chunk_state_hb<Q, N>), dim3(xcd_grid(geo.nc_max, geo.G * nkb)), dim3(512),
+  // three ring slots where the LDS allows (two heads' loads in flight)
+  constexpr int R = cs_lds_bytes(Q, N, 3) <= 160 * 1024 ? 3 : 2;
+  hipLaunchKernelGGL((k_chunk_state_hb<Q, N, R>), dim3(xcd_grid(geo.nc_max, geo.G * nkb)), dim3(512),
                      0, stream, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                      acum, dtq, cg, (int)geo.nc_max, geo.H, geo.G, hb, nkb, states);
 }
