@@ -278,10 +278,12 @@ def backward_bytes(w):
 def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
     """A forward that leaves the state entering every 64-token chunk, then the
     backward (ssd_fused_bwd) for seeded upstream gradients dy, dfinal; each
-    timed with HIP events on the launch stream. Two forwards leave those
-    states: the one-pass forward saving them (ssd_fused_fwd_train) and the
-    four-stage forward with chunk length 64 (its hprev); the faster is the
-    step's forward (fwd_train_path), the other is reported beside it."""
+    timed with HIP events on the launch stream. Three forwards leave those
+    states: the one-pass forward saving them (ssd_fused_fwd_train), the
+    four-stage forward with chunk length 64 (its hprev), and SSDTrainForward
+    (y from the four stages at chunk length 256, the states from the first
+    three at chunk length 64); the fastest is the step's forward
+    (fwd_train_path), the others are reported beside it."""
     dev = t["x"].device
     dy, dfinal = workloads.make_output_grads(w, 6100)
     dyd = torch.from_numpy(dy).to(dev).to(torch.bfloat16).view(t["x"].shape)
@@ -303,6 +305,12 @@ def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
         plan64(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"], y=y,
                final_state=fin)
 
+    tplan = ssd.SSDTrainForward(ssd.dims_for(t["x"], t["B"], t["cu"]), device=dev)
+
+    def fwd_split():
+        tplan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"], y=y,
+              final_state=fin)
+
     def bwd():
         ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], states, dyd, dfd, t["cu"],
                       workspace=ws)
@@ -320,24 +328,24 @@ def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / steps * 1e3
 
-    fus1 = timed(fwd)
-    fus64 = timed(fwd64)
+    by_path = {"ssd_fused_fwd_train": timed(fwd), "ssd_chunk_scan_fwd_q64": timed(fwd64),
+               "SSDTrainForward": timed(fwd_split)}
     bus = timed(bwd)
-    fus = min(fus1, fus64)
+    path = min(by_path, key=by_path.get)
+    fus = by_path[path]
     rev, chk = backward_bytes(w)
     T = w.tokens
-    res = {"fwd_train_us": round(fus, 2),
-           "fwd_train_path": "ssd_fused_fwd_train" if fus1 <= fus64 else "ssd_chunk_scan_fwd_q64",
-           "fwd_train_us_by_path": {"ssd_fused_fwd_train": round(fus1, 2),
-                                    "ssd_chunk_scan_fwd_q64": round(fus64, 2)},
+    res = {"fwd_train_us": round(fus, 2), "fwd_train_path": path,
+           "fwd_train_us_by_path": {k: round(v, 2) for k, v in by_path.items()},
            "bwd_us": round(bus, 2),
            "tokens_per_s": round(T / ((fus + bus) * 1e-6), 1),
            "bwd_tokens_per_s": round(T / (bus * 1e-6), 1),
            "bwd_bytes": {"k_bwd_reverse": rev, "k_bwd_chunk": chk},
            "bwd_GBs": round((rev + chk) / (bus * 1e-6) / 1e9, 1),
            "bwd_hbm_frac": round((rev + chk) / (bus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
-    log(f"bench: training step: forward saving states {fus1:.1f} us (one-pass), {fus64:.1f} us "
-        f"(four-stage, chunk 64), backward {bus:.1f} us, "
+    log(f"bench: training step: forward saving states {by_path['ssd_fused_fwd_train']:.1f} us "
+        f"(one-pass), {by_path['ssd_chunk_scan_fwd_q64']:.1f} us (four-stage, chunk 64), "
+        f"{by_path['SSDTrainForward']:.1f} us (chunk 256 + chunk-64 states), backward {bus:.1f} us, "
         f"{res['tokens_per_s'] / 1e6:.1f} M tokens/s")
     return res
 

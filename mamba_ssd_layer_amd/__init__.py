@@ -30,7 +30,7 @@ from . import libssd
 from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsupported,
                      SSDWorkspaceError, make_dims)
 
-__all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDError", "SSDInvalidArgument",
+__all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDTrainForward", "SSDError", "SSDInvalidArgument",
            "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "step",
            "conv1d_silu", "gate_rmsnorm", "fused_fwd", "make_fused_states", "fused_bwd"]
 
@@ -141,6 +141,30 @@ class SSDForward:
         raise KeyError(name)
 
 
+class SSDTrainForward:
+    """The chunk-parallel forward for training: y and the final state from the
+    four stages at chunk length 256 (head-batched kernels), and the state
+    entering every 64-token chunk -- what fused_bwd takes as chunk_states --
+    from the first three stages at chunk length 64 (the same kernels, bit for
+    bit the hprev a chunk-64 forward leaves).  For few long sequences, where
+    the one-pass forward has too few (sequence, head) blocks.  bf16 io."""
+
+    def __init__(self, dims, device="cuda"):
+        self.p256 = SSDForward(dims, 256, device=device)
+        self.p64 = SSDForward(dims, 64, device=device)
+
+    def __call__(self, x, dt, A, B, C, D=None, init_state=None, cu_seqlens=None, y=None,
+                 final_state=None, want_final: bool = True, stream=None):
+        """y, final_state, chunk_states (a view of this plan's workspace, valid
+        until the next call)."""
+        y, final_state = self.p256(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state,
+                                   want_final, stream)
+        self.p64.cumsum(dt, A, cu_seqlens, stream)
+        self.p64.state(x, B, stream)
+        self.p64.passing(init_state, None, stream)
+        return y, final_state, self.p64.saved_states()
+
+
 def chunk_scan_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
                    C: torch.Tensor, D: Optional[torch.Tensor] = None, chunk_len: int = 256,
                    init_state: Optional[torch.Tensor] = None,
@@ -162,7 +186,7 @@ def fused_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
     bf16, headdim 64, dstate 64 or 128; no workspace).  Same arguments and
     results as chunk_scan_fwd.  With chunk_states (a uint8 device buffer of
     fused_states_bytes(...) bytes, see make_fused_states) it also saves the
-    state entering every 32-token chunk for fused_bwd (ssd_fused_fwd_train)."""
+    state entering every 64-token chunk for fused_bwd (ssd_fused_fwd_train)."""
     dims = dims_for(x, B, cu_seqlens)
     if y is None:
         y = torch.empty_like(x)

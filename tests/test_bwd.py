@@ -303,3 +303,40 @@ def test_states_from_chunked_forward(packed):
     torch.cuda.synchronize()
     ref = oracle.recurrence_bwd(w.x, w.dt, w.A, w.B, w.C, w.D, w.h0, w.seq_off, dy, dfinal)
     check_grads(w, g, ref, f"bwd from chunked-forward states ({'packed' if packed else 'fixed'})")
+
+
+@pytest.mark.parametrize("packed", [False, True])
+def test_split_training_forward(packed):
+    # SSDTrainForward: y and the final state from chunk length 256, the states
+    # from the first three stages at chunk length 64 -- bit for bit the hprev of
+    # the chunk-64 forward; y within the forward's tolerance of the oracle; the
+    # backward from those states matches the oracle
+    if packed:
+        w = workloads.make_custom(1, 0, 4, 64, 128, 2, 64, "bf16", seed=3200, init_std=0.3,
+                                  lens=[300, 0, 65, 1000, 1])
+    else:
+        w = workloads.make_custom(2, 700, 4, 64, 64, 1, 64, "bf16", seed=3201, init_std=0.3)
+    dy, dfinal = workloads.make_output_grads(w, 13)
+    t = upload(w)
+    dims = ssd.dims_for(t["x"], t["B"], t["cu"])
+    tplan = ssd.SSDTrainForward(dims, device=DEV)
+    y, fin, states = tplan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"])
+    plan = ssd.SSDForward(dims, 64, device=DEV)
+    plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"])
+    torch.cuda.synchronize()
+    # the pairs the sequences use (a packed batch's buffer is sized by a bound)
+    lens = np.diff(w.seq_off)
+    nb = int(sum(-(-int(n) // 64) for n in lens)) * w.nheads * w.headdim * w.dstate * 2
+    assert torch.equal(states[:nb], plan.saved_states()[:nb])
+    y_ref, f_ref = oracle.recurrence(w.x, w.dt, w.A, w.B, w.C, w.D, w.h0, w.seq_off)
+    yg = y.float().cpu().numpy().reshape(y_ref.shape)
+    ey = float(np.max(np.abs(yg - y_ref)) / np.max(np.abs(y_ref)))
+    ef = float(np.max(np.abs(fin.cpu().numpy() - f_ref)) / np.max(np.abs(f_ref)))
+    say(f"  split training forward ({'packed' if packed else 'fixed'}): y {ey:.3e}, final {ef:.3e}")
+    assert ey <= 2e-2 and ef <= 2e-2
+    dyd = torch.from_numpy(dy).to(DEV).to(torch.bfloat16).view(t["x"].shape)
+    g = ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], states, dyd,
+                      torch.from_numpy(dfinal).to(DEV), t["cu"])
+    torch.cuda.synchronize()
+    ref = oracle.recurrence_bwd(w.x, w.dt, w.A, w.B, w.C, w.D, w.h0, w.seq_off, dy, dfinal)
+    check_grads(w, g, ref, f"bwd from split-forward states ({'packed' if packed else 'fixed'})")
