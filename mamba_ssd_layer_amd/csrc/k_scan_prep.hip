@@ -137,14 +137,22 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
       run += v[e] * a;
       pre[e] = run;
     }
+    // inclusive scan of the lane totals over the wavefront by DPP: shifts
+    // 1, 2, 4, 8 within each 16-lane row, then row 15's total carried into
+    // the next row and lane 31's into the upper half (invalid sources add 0)
     float incl = run;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float t = __shfl_up(incl, off, 64);
-      if (lane >= off) incl += t;
-    }
-    float excl = __shfl_up(incl, 1, 64);
-    if (lane == 0) excl = 0.f;
+    auto dpp = [](float x, auto ctrl, auto rows) {
+      return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), decltype(ctrl)::value,
+                                                        decltype(rows)::value, 0xF, false));
+    };
+    incl += dpp(incl, std::integral_constant<int, 0x111>{}, std::integral_constant<int, 0xF>{});
+    incl += dpp(incl, std::integral_constant<int, 0x112>{}, std::integral_constant<int, 0xF>{});
+    incl += dpp(incl, std::integral_constant<int, 0x114>{}, std::integral_constant<int, 0xF>{});
+    incl += dpp(incl, std::integral_constant<int, 0x118>{}, std::integral_constant<int, 0xF>{});
+    incl += dpp(incl, std::integral_constant<int, 0x142>{}, std::integral_constant<int, 0xA>{});
+    incl += dpp(incl, std::integral_constant<int, 0x143>{}, std::integral_constant<int, 0xC>{});
+    // exclusive value: the previous lane's inclusive one (DPP wave_shr:1, 0 into lane 0)
+    const float excl = dpp(incl, std::integral_constant<int, 0x138>{}, std::integral_constant<int, 0xF>{});
     // positions past a partial chunk's end repeat the value at its last token
     const int last = ci.len - 1;
     float mine = 0.f;
@@ -152,7 +160,7 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
     for (int e = 0; e < E; ++e) {
       if (e == last % E) mine = excl + pre[e];
     }
-    const float lastval = __shfl(mine, last / E, 64);
+    const float lastval = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), last / E));
     float *ao = acum + ((int64_t)c * H + h) * Q + lane * E;
     float *dq = dtq + ((int64_t)c * H + h) * Q + lane * E;
 #pragma unroll
