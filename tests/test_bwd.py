@@ -283,6 +283,22 @@ def test_long_n64_sampled():
     sampled_check(w, g, pairs, "bwd long_n64 sampled", dy, dfinal)
 
 
+def test_long_n64_split_training_forward_sampled():
+    # the training step's forward at this shape (SSDTrainForward: chunk 256 for
+    # y, chunk 64 for the states), then the segmented backward from its states
+    w = workloads.make_workload("long_n64")
+    dy, dfinal = workloads.make_output_grads(w, 11)
+    t = upload(w)
+    tplan = ssd.SSDTrainForward(ssd.dims_for(t["x"], t["B"], t["cu"]), device=DEV)
+    _, _, states = tplan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"])
+    dyd = torch.from_numpy(dy).to(DEV).to(torch.bfloat16).view(t["x"].shape)
+    g = ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], states, dyd,
+                      torch.from_numpy(dfinal).to(DEV), t["cu"])
+    torch.cuda.synchronize()
+    sampled_check(w, g, [(0, 5), (0, 46)], "bwd long_n64 from the split forward, sampled", dy,
+                  dfinal)
+
+
 @pytest.mark.parametrize("packed", [False, True])
 def test_states_from_chunked_forward(packed):
     # the four-stage forward with chunk length 64 leaves the same states in its
