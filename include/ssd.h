@@ -157,7 +157,8 @@ ssd_status ssd_chunk_cumsum(const float *dt, const float *A, int chunk_len,
  * x_l^T B_l over the chunk's tokens, the state each chunk would leave from a
  * zero start (page "Mamba-2 Architecture: State Space Duality Explained",
  * "2. The Chunked SSD Algorithm", item 2, with the decay weights the
- * recurrence implies).  Needs stage 1's output in the same workspace. */
+ * recurrence implies), summed in fp32 and stored in the io precision.  Needs
+ * stage 1's output in the same workspace. */
 ssd_status ssd_chunk_state(const void *x, const void *B, int chunk_len, const ssd_dims *dims,
                            void *workspace, size_t workspace_bytes, void *stream);
 
