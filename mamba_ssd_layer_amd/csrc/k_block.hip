@@ -30,6 +30,12 @@ template <> struct Vec<uint16_t> {
     *reinterpret_cast<u32x4 *>(p) = u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
                                           pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])};
   }
+  // a streaming (non-temporal) store: output nothing in this kernel reads again
+  __device__ static void store_nt(uint16_t *p, const float (&v)[8]) {
+    __builtin_nontemporal_store(u32x4{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]),
+                                      pack_bf16x2(v[4], v[5]), pack_bf16x2(v[6], v[7])},
+                                reinterpret_cast<u32x4 *>(p));
+  }
 };
 template <> struct Vec<float> {
   static constexpr int N = 4;
@@ -44,6 +50,9 @@ template <> struct Vec<float> {
   __device__ static void store(float *p, const float (&v)[4]) {
     *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
   }
+  __device__ static void store_nt(float *p, const float (&v)[4]) {
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
+  }
 };
 
 __device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
@@ -54,7 +63,7 @@ constexpr int kConvRun = 16;  // tokens per thread
 // fastest so a wavefront reads contiguous row segments.  A run inside one
 // sequence loads its kConvRun + K - 1 input rows up front (16 bytes each, all
 // in flight together; rows before the sequence start read as 0) and then
-// forms its outputs.  A run that crosses a sequence boundary walks its tokens
+// forms its outputs, written with streaming stores.  A run that crosses a sequence boundary walks its tokens
 // in order instead, keeping the K-1 previous inputs in registers and
 // resetting them to 0 at each sequence start.
 template <typename IO, int K>
@@ -127,7 +136,7 @@ __global__ __launch_bounds__(256) void k_conv1d_silu(const IO *__restrict__ in, 
         }
 #pragma unroll
         for (int v = 0; v < V; ++v) o[v] = silu(acc[v]);
-        Vec<IO>::store(out + (t0 + i) * out_stride + c0, o);
+        Vec<IO>::store_nt(out + (t0 + i) * out_stride + c0, o);
       }
     }
     return;
