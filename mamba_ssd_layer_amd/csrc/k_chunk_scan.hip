@@ -594,7 +594,8 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const unsigned u = tid + i * NT, r = u / NCX, gp = u % NCX;
-      if ((int)r < ci.len) *reinterpret_cast<u32x4 *>(yb + r * ldx32 + gp * 8) = v[i];
+      // streaming stores: nothing in this pass reads y again
+      if ((int)r < ci.len) __builtin_nontemporal_store(v[i], reinterpret_cast<u32x4 *>(yb + r * ldx32 + gp * 8));
     }
   };
 
