@@ -135,7 +135,9 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
 #pragma unroll
       for (int k = 1; k < KSPLIT; ++k)
         v += *reinterpret_cast<const f32x4 *>(smem + SS + k * SSB + (p * LSS + 4 * c4) * 4);
-      *reinterpret_cast<u32x2 *>(out + p * N + 4 * c4) = u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)};
+      // streaming stores: the next pass reads S once, from HBM
+      __builtin_nontemporal_store(u32x2{pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w)},
+                                  reinterpret_cast<u32x2 *>(out + p * N + 4 * c4));
     }
   };
 
