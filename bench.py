@@ -40,6 +40,7 @@ KERNEL_SOURCES = {
     "fused_fwd": "k_fused.hip",
 }
 FUSED_CHUNK = 32  # the one-pass forward's chunk length
+FLUSH_BYTES = 1 << 30  # written between timed steps: four times the 256 MB MALL
 
 
 def log(msg: str) -> None:
@@ -438,23 +439,57 @@ def main() -> int:
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev0 = torch.cuda.Event(enable_timing=True)
-    ev1 = torch.cuda.Event(enable_timing=True)
-    wall0 = time.perf_counter()
-    ev0.record(stream)
-    for _ in range(args.steps):
-        step()
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms = ev0.elapsed_time(ev1) / args.steps
+    # a write larger than the 256 MB MALL between timed steps, so no step
+    # starts with its inputs or intermediates in the memory-side cache
+    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+
+    def timed_steps(fn):
+        """Per-launch durations (us) of `steps` launches of fn, each bracketed
+        by HIP events on the launch stream with a MALL-flushing write before
+        it; plus the wall time of the whole region."""
+        evs = []
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for i in range(args.steps):
+            flush.fill_(float(i))
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return [a.elapsed_time(b) * 1e3 for a, b in evs], time.perf_counter() - w0
+
+    def back_to_back(fn):
+        """Mean duration (us) of `steps` launches issued back to back (no flush)."""
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / args.steps * 1e3
+
+    def summary(per, wall):
+        return {"us": round(float(np.median(per)), 2), "mean_us": round(float(np.mean(per)), 2),
+                "min_us": round(float(np.min(per)), 2), "max_us": round(float(np.max(per)), 2),
+                "wall_s": round(wall, 3)}
+
+    per, wall = timed_steps(step)
+    chunked_t = summary(per, wall)
+    chunked_t["back_to_back_us"] = round(back_to_back(step), 2)
+    ms = chunked_t["us"] / 1e3
     value = T / (ms / 1e3)
-    log(f"bench: chunked forward {ms * 1e3:.1f} us/step ({wall / args.steps * 1e6:.1f} us wall), "
+    log(f"bench: chunked forward median {chunked_t['us']:.1f} us/step (flushed; mean "
+        f"{chunked_t['mean_us']:.1f}, back to back {chunked_t['back_to_back_us']:.1f}), "
         f"{value / 1e6:.1f} M tokens/s")
 
     # the one-pass forward on the same inputs, where its shape is supported
     fused = None
-    if w.dtype == "bf16" and P == 64 and N in (64, 128) and (H // G) % 2 == 0:
+    if w.dtype == "bf16" and ssd.libssd.ssd_fused_states_size(dims) > 0:
         yf = torch.empty_like(x)
         ff = torch.empty_like(fin)
 
@@ -463,27 +498,21 @@ def main() -> int:
 
         for _ in range(args.warmup):
             fstep()
-        torch.cuda.synchronize()
-        fe0 = torch.cuda.Event(enable_timing=True)
-        fe1 = torch.cuda.Event(enable_timing=True)
-        fwall0 = time.perf_counter()
-        fe0.record(stream)
-        for _ in range(args.steps):
-            fstep()
-        fe1.record(stream)
-        torch.cuda.synchronize()
-        fwall = time.perf_counter() - fwall0
-        fms = fe0.elapsed_time(fe1) / args.steps
+        fper, fwall = timed_steps(fstep)
+        fsum = summary(fper, fwall)
+        fsum["back_to_back_us"] = round(back_to_back(fstep), 2)
         fb, ff_ = algorithmic(w, "fused_fwd")
-        ft = fms * 1e-3
-        fused = {"us": round(fms * 1e3, 2), "wall_us": round(fwall / args.steps * 1e6, 2),
-                 "tokens_per_s": round(T / ft, 1), "bytes": fb, "flops": ff_,
+        ft = fsum["us"] * 1e-6
+        fused = {**fsum, "tokens_per_s": round(T / ft, 1), "bytes": fb, "flops": ff_,
                  "GBs": round(fb / ft / 1e9, 1), "TFLOPs": round(ff_ / ft / 1e12, 2),
                  "hbm_frac": round(fb / ft / 1e9 / HBM_PEAK_GBS, 4)}
-        log(f"bench: one-pass forward {fms * 1e3:.1f} us/step, {T / ft / 1e6:.1f} M tokens/s")
+        log(f"bench: one-pass forward median {fsum['us']:.1f} us/step (flushed; mean "
+            f"{fsum['mean_us']:.1f}, back to back {fsum['back_to_back_us']:.1f}), "
+            f"{T / ft / 1e6:.1f} M tokens/s")
 
-    # per-stage times: the same stages launched one by one, HIP events between
-    stage_us = {}
+    # per-stage times: the same stages launched one by one, each after a
+    # MALL-flushing write, HIP events around each launch (median over steps)
+    stage_us, stage_mean_us = {}, {}
     if not args.no_stage_timing:
         calls = {
             "chunk_cumsum": lambda: plan.cumsum(dt, A, cu),
@@ -491,18 +520,22 @@ def main() -> int:
             "state_passing": lambda: plan.passing(h0, fin),
             "chunk_scan": lambda: plan.scan(x, Bm, Cm, D, y),
         }
-        evs = {s: [] for s in STAGES}
-        for _ in range(args.steps):
-            for s in STAGES:
+        evs = {s_: [] for s_ in STAGES}
+        for i in range(args.steps):
+            for s_ in STAGES:
+                flush.fill_(float(i))
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
-                calls[s]()
+                calls[s_]()
                 e1.record(stream)
-                evs[s].append((e0, e1))
+                evs[s_].append((e0, e1))
         torch.cuda.synchronize()
-        for s in STAGES:
-            stage_us[s] = sum(a.elapsed_time(b) for a, b in evs[s]) / len(evs[s]) * 1e3
+        for s_ in STAGES:
+            d_ = [a_.elapsed_time(b_) * 1e3 for a_, b_ in evs[s_]]
+            stage_us[s_] = float(np.median(d_))
+            stage_mean_us[s_] = float(np.mean(d_))
+    del flush
     copy_gbs = copy_bandwidth(torch, dev)
     log(f"bench: plain copy {copy_gbs:.0f} GB/s")
 
@@ -521,7 +554,7 @@ def main() -> int:
         entry = {"bytes": b, "flops": f}
         if s in stage_us:
             t = stage_us[s] * 1e-6
-            entry.update(us=round(stage_us[s], 2), GBs=round(b / t / 1e9, 1),
+            entry.update(us=round(stage_us[s], 2), mean_us=round(stage_mean_us[s], 2), GBs=round(b / t / 1e9, 1),
                          TFLOPs=round(f / t / 1e12, 2) if f else 0.0,
                          hbm_frac=round(b / t / 1e9 / HBM_PEAK_GBS, 4), **fracs(b, f, t))
         kernels[s] = entry
@@ -549,12 +582,11 @@ def main() -> int:
     chunked_roofline = None
     if stage_us:
         dom = max(stage_us, key=stage_us.get)
-        chunked_roofline = roofline_of(dom, stage_us[dom])
-    chunked = {"us": round(ms * 1e3, 2), "wall_us": round(wall / args.steps * 1e6, 2),
-               "tokens_per_s": round(value, 1), "roofline": chunked_roofline}
+        chunked_roofline = roofline_of(dom, stage_mean_us[dom])
+    chunked = {**chunked_t, "tokens_per_s": round(value, 1), "roofline": chunked_roofline}
     path, roofline, ms_step = "ssd_chunk_scan_fwd", chunked_roofline, ms
     if fused is not None:
-        fused["roofline"] = roofline_of("fused_fwd", fused["us"])
+        fused["roofline"] = roofline_of("fused_fwd", fused["mean_us"])
         if fused["us"] < ms * 1e3:
             path, roofline, ms_step, value = ("ssd_fused_fwd", fused["roofline"], fused["us"] / 1e3,
                                               fused["tokens_per_s"])
@@ -583,6 +615,10 @@ def main() -> int:
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms_step, 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
+        "timing": (f"value: the median of {args.steps} launches, each after a "
+                   f"{FLUSH_BYTES >> 20} MiB write that flushes the 256 MB MALL, HIP events on the "
+                   "launch stream; roofline.achieved: algorithmic bytes / the mean of the same "
+                   "launches"),
         "config": {**workloads.describe(w), "path": path,
                    "chunk": FUSED_CHUNK if path == "ssd_fused_fwd" else w.chunk,
                    "parallelism": "none (1 GPU)"},

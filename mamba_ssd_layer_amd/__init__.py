@@ -31,7 +31,7 @@ from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsuppo
                      SSDWorkspaceError, make_dims)
 
 __all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDTrainForward", "SSDError", "SSDInvalidArgument",
-           "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "step",
+           "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "validate_cu_seqlens", "step",
            "conv1d_silu", "gate_rmsnorm", "fused_fwd", "make_fused_states", "fused_bwd"]
 
 
@@ -41,6 +41,25 @@ def _io_dtype(t: torch.Tensor) -> int:
     if t.dtype == torch.float32:
         return SSD_F32
     raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, f"unsupported dtype {t.dtype}")
+
+
+def validate_cu_seqlens(cu_seqlens: Optional[torch.Tensor], tokens: int) -> None:
+    """Checks packed-batch offsets on the host (0 first, non-decreasing, the
+    token count last) and raises SSDInvalidArgument otherwise.  The kernels
+    stay inside their buffers on malformed offsets but would return wrong
+    results without an error.  A tensor is copied to the host (one
+    synchronisation) only the first time it is seen in its current version
+    (torch bumps a tensor's version on every in-place write, also through
+    another view); the mark lives on the tensor object and dies with it."""
+    if cu_seqlens is None:
+        return
+    if cu_seqlens.dtype != torch.int32 or cu_seqlens.dim() != 1:
+        raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "cu_seqlens must be 1-D int32")
+    mark = (cu_seqlens._version, int(tokens))
+    if getattr(cu_seqlens, "_libssd_checked", None) == mark:
+        return
+    libssd.check_cu_seqlens(cu_seqlens.cpu().tolist(), tokens)
+    cu_seqlens._libssd_checked = mark
 
 
 def dims_for(x: torch.Tensor, B: torch.Tensor, cu_seqlens: Optional[torch.Tensor] = None):
@@ -76,6 +95,8 @@ class SSDForward:
 
     def __call__(self, x, dt, A, B, C, D=None, init_state=None, cu_seqlens=None, y=None,
                  final_state=None, want_final: bool = True, stream=None):
+        if cu_seqlens is not None:
+            validate_cu_seqlens(cu_seqlens, self.dims.seqlen)
         if y is None:
             y = torch.empty_like(x)
         if final_state is None and want_final:
@@ -87,6 +108,8 @@ class SSDForward:
 
     # per-stage calls on the plan's workspace (for checks and timing)
     def cumsum(self, dt, A, cu_seqlens=None, stream=None):
+        if cu_seqlens is not None:
+            validate_cu_seqlens(cu_seqlens, self.dims.seqlen)
         libssd.ssd_chunk_cumsum(dt, A, self.chunk_len, cu_seqlens, self.dims, self.workspace,
                                 stream)
 
@@ -188,6 +211,8 @@ def fused_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
     fused_states_bytes(...) bytes, see make_fused_states) it also saves the
     state entering every 64-token chunk for fused_bwd (ssd_fused_fwd_train)."""
     dims = dims_for(x, B, cu_seqlens)
+    if cu_seqlens is not None:
+        validate_cu_seqlens(cu_seqlens, dims.seqlen)
     if y is None:
         y = torch.empty_like(x)
     if final_state is None and want_final:
@@ -227,6 +252,8 @@ def fused_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
     dD [H] (None when D is None) and dinit [rows, H, P, N] (None unless
     want_dinit)."""
     dims = dims_for(x, B, cu_seqlens)
+    if cu_seqlens is not None:
+        validate_cu_seqlens(cu_seqlens, dims.seqlen)
     dev = x.device
     nrows = dims.nseq if dims.nseq > 0 else dims.batch
     if workspace is None:
@@ -281,6 +308,7 @@ def conv1d_silu(inp: torch.Tensor, weight: torch.Tensor, bias: Optional[torch.Te
             raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "packed inp must be [T, C]")
         T = inp.shape[0]
         batch, seqlen, nseq = 1, T, cu_seqlens.numel() - 1
+        validate_cu_seqlens(cu_seqlens, T)
     else:
         if inp.dim() != 3:
             raise SSDInvalidArgument(libssd.SSD_ERR_INVALID_ARG, "inp must be [B, L, C]")

@@ -33,10 +33,11 @@ ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
   if (d->batch < 1 || d->seqlen < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 ||
       d->ngroups < 1 || d->nseq < 0)
     return SSD_ERR_INVALID_ARG;
-  if (d->nheads % d->ngroups != 0) return SSD_ERR_INVALID_ARG;
   if (d->nseq > 0 && d->batch != 1) return SSD_ERR_INVALID_ARG;
   if (chunk_len < 1) return SSD_ERR_INVALID_ARG;
   if (chunk_len != 64 && chunk_len != 128 && chunk_len != 256) return SSD_ERR_UNSUPPORTED;
+  // heads split evenly over the groups: the only head-to-group map compiled
+  if (d->nheads % d->ngroups != 0) return SSD_ERR_UNSUPPORTED;
   const int64_t H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
   const bool bf16 = d->io_dtype == SSD_BF16;
   if (P % 16 != 0 || N % 16 != 0 || P > 256 || N > 256) return SSD_ERR_UNSUPPORTED;
@@ -306,8 +307,9 @@ ssd_status ssd_step(const void *x, const float *dt, const float *A, const void *
   if (d->reserved != 0) return SSD_ERR_INVALID_ARG;
   if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
   if (d->batch < 0 || d->seqlen != 1 || d->nseq != 0 || d->nheads < 1 || d->headdim < 1 ||
-      d->dstate < 1 || d->ngroups < 1 || d->nheads % d->ngroups != 0)
+      d->dstate < 1 || d->ngroups < 1)
     return SSD_ERR_INVALID_ARG;
+  if (d->nheads % d->ngroups != 0) return SSD_ERR_UNSUPPORTED;
   const int64_t S = d->batch, H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
   if (!ssd::step_supported((int)N)) return SSD_ERR_UNSUPPORTED;
   // one block per (sequence, head); element offsets of the state below 2^62

@@ -157,11 +157,62 @@ def ssd_get_workspace_layout(dims: ssd_dims, chunk_len: int) -> ssd_workspace_la
 def _ptr(t: Optional[torch.Tensor]):
     if t is None:
         return None
+    if not isinstance(t, torch.Tensor):
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "expected a torch tensor")
     if not t.is_cuda:
         raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "tensor is not on the GPU")
     if not t.is_contiguous():
         raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "tensor is not contiguous")
     return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _io_torch(dims) -> torch.dtype:
+    return torch.bfloat16 if dims.io_dtype == SSD_BF16 else torch.float32
+
+
+def _sizes(dims):
+    """(T, H, P, N, G, rows) of a dims struct (T = tokens, rows = sequences)."""
+    T = dims.seqlen if dims.nseq > 0 else dims.batch * dims.seqlen
+    rows = dims.nseq if dims.nseq > 0 else dims.batch
+    return T, dims.nheads, dims.headdim, dims.dstate, dims.ngroups, rows
+
+
+def _t(t: Optional[torch.Tensor], dtype: torch.dtype, numel: int, name: str,
+       optional: bool = False) -> Optional[torch.Tensor]:
+    """t after checking that it is present (unless optional), of dtype `dtype`
+    and of exactly `numel` elements: the C entry points see only a pointer,
+    so a wrong dtype or size would make the kernels read or write past the
+    buffer.  Where it lives is checked when its pointer is taken (_ptrs)."""
+    if t is None:
+        if optional or numel == 0:
+            return None
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, f"{name} must be {dtype}, got {t.dtype}")
+    if t.numel() != numel:
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG,
+                                 f"{name} must hold {numel} elements, got {t.numel()}")
+    return t
+
+
+def _ptrs(*ts):
+    """Device pointers of already checked tensors (None stays None)."""
+    return [_ptr(t) for t in ts]
+
+
+def _cu(cu: Optional[torch.Tensor], dims):
+    if dims.nseq > 0:
+        return _t(cu, torch.int32, dims.nseq + 1, "cu_seqlens")
+    if cu is not None:
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG,
+                                 "cu_seqlens given for a fixed-length batch (dims.nseq == 0)")
+    return None
+
+
+def _bytes(t: Optional[torch.Tensor]) -> int:
+    return 0 if t is None else t.numel() * t.element_size()
 
 
 def _stream(stream) -> ctypes.c_void_p:
@@ -170,48 +221,82 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def _fwd(dims, x=None, dt=None, A=None, B=None, C=None, D=None, y=None, need=()):
+    """The forward's token tensors, checked against dims; those named in
+    `need` must be present."""
+    T, H, P, N, G, _ = _sizes(dims)
+    io = _io_torch(dims)
+    f32 = torch.float32
+    opt = lambda k: k not in need
+    return (_t(x, io, T * H * P, "x", opt("x")), _t(dt, f32, T * H, "dt", opt("dt")),
+            _t(A, f32, H, "A", opt("A")), _t(B, io, T * G * N, "B", opt("B")),
+            _t(C, io, T * G * N, "C", opt("C")), _t(D, f32, H, "D", optional=True),
+            _t(y, io, T * H * P, "y", opt("y")))
+
+
+ALL = ("x", "dt", "A", "B", "C", "y")
+
+
+def _state(t, dims, name):
+    T, H, P, N, G, rows = _sizes(dims)
+    return _t(t, torch.float32, rows * H * P * N, name, optional=True)
+
+
 def ssd_chunk_scan_fwd(x, dt, A, B, C, D, chunk_len, init_state, cu_seqlens, y, final_state,
                        dims, workspace, stream=None) -> None:
-    _check(_lib.ssd_chunk_scan_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                   int(chunk_len), _ptr(init_state), _ptr(cu_seqlens), _ptr(y),
-                                   _ptr(final_state), ctypes.byref(dims), _ptr(workspace),
-                                   workspace.numel() * workspace.element_size(), _stream(stream)))
+    ts = _fwd(dims, x, dt, A, B, C, D, y, need=ALL)
+    hi, cu, hf = _state(init_state, dims, "init_state"), _cu(cu_seqlens, dims), \
+        _state(final_state, dims, "final_state")
+    px, pdt, pA, pB, pC, pD, py, phi, pcu, phf, pws = _ptrs(*ts, hi, cu, hf, workspace)
+    _check(_lib.ssd_chunk_scan_fwd(px, pdt, pA, pB, pC, pD, int(chunk_len), phi, pcu, py, phf,
+                                   ctypes.byref(dims), pws, _bytes(workspace), _stream(stream)))
 
 
 def ssd_chunk_cumsum(dt, A, chunk_len, cu_seqlens, dims, workspace, stream=None) -> None:
-    _check(_lib.ssd_chunk_cumsum(_ptr(dt), _ptr(A), int(chunk_len), _ptr(cu_seqlens),
-                                 ctypes.byref(dims), _ptr(workspace),
-                                 workspace.numel() * workspace.element_size(), _stream(stream)))
+    _, dt, A, _, _, _, _ = _fwd(dims, dt=dt, A=A, need=("dt", "A"))
+    pdt, pA, pcu, pws = _ptrs(dt, A, _cu(cu_seqlens, dims), workspace)
+    _check(_lib.ssd_chunk_cumsum(pdt, pA, int(chunk_len), pcu, ctypes.byref(dims), pws,
+                                 _bytes(workspace), _stream(stream)))
 
 
 def ssd_chunk_state(x, B, chunk_len, dims, workspace, stream=None) -> None:
-    _check(_lib.ssd_chunk_state(_ptr(x), _ptr(B), int(chunk_len), ctypes.byref(dims),
-                                _ptr(workspace), workspace.numel() * workspace.element_size(),
-                                _stream(stream)))
+    x, _, _, B, _, _, _ = _fwd(dims, x=x, B=B, need=("x", "B"))
+    px, pB, pws = _ptrs(x, B, workspace)
+    _check(_lib.ssd_chunk_state(px, pB, int(chunk_len), ctypes.byref(dims), pws,
+                                _bytes(workspace), _stream(stream)))
 
 
 def ssd_state_passing(init_state, final_state, chunk_len, dims, workspace, stream=None) -> None:
-    _check(_lib.ssd_state_passing(_ptr(init_state), _ptr(final_state), int(chunk_len),
-                                  ctypes.byref(dims), _ptr(workspace),
-                                  workspace.numel() * workspace.element_size(), _stream(stream)))
+    phi, phf, pws = _ptrs(_state(init_state, dims, "init_state"),
+                          _state(final_state, dims, "final_state"), workspace)
+    _check(_lib.ssd_state_passing(phi, phf, int(chunk_len), ctypes.byref(dims), pws,
+                                  _bytes(workspace), _stream(stream)))
 
 
 def ssd_chunk_scan(x, B, C, D, y, chunk_len, dims, workspace, stream=None) -> None:
-    _check(_lib.ssd_chunk_scan(_ptr(x), _ptr(B), _ptr(C), _ptr(D), _ptr(y), int(chunk_len),
-                               ctypes.byref(dims), _ptr(workspace),
-                               workspace.numel() * workspace.element_size(), _stream(stream)))
+    x, _, _, B, C, D, y = _fwd(dims, x=x, B=B, C=C, D=D, y=y, need=("x", "B", "C", "y"))
+    px, pB, pC, pD, py, pws = _ptrs(x, B, C, D, y, workspace)
+    _check(_lib.ssd_chunk_scan(px, pB, pC, pD, py, int(chunk_len), ctypes.byref(dims), pws,
+                               _bytes(workspace), _stream(stream)))
 
 
 def ssd_step(x, dt, A, B, C, D, state, y, dims, stream=None) -> None:
-    _check(_lib.ssd_step(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
-                         _ptr(y), ctypes.byref(dims), _stream(stream)))
+    # one token per sequence: T = rows = dims.batch
+    ts = _fwd(dims, x, dt, A, B, C, D, y, need=ALL)
+    T, H, P, N, G, rows = _sizes(dims)
+    st = _t(state, torch.float32, rows * H * P * N, "state")
+    px, pdt, pA, pB, pC, pD, py, pst = _ptrs(*ts, st)
+    _check(_lib.ssd_step(px, pdt, pA, pB, pC, pD, pst, py, ctypes.byref(dims), _stream(stream)))
 
 
 def ssd_fused_fwd(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, dims,
                   stream=None) -> None:
-    _check(_lib.ssd_fused_fwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                              _ptr(init_state), _ptr(cu_seqlens), _ptr(y), _ptr(final_state),
-                              ctypes.byref(dims), _stream(stream)))
+    ts = _fwd(dims, x, dt, A, B, C, D, y, need=ALL)
+    hi, cu, hf = _state(init_state, dims, "init_state"), _cu(cu_seqlens, dims), \
+        _state(final_state, dims, "final_state")
+    px, pdt, pA, pB, pC, pD, py, phi, pcu, phf = _ptrs(*ts, hi, cu, hf)
+    _check(_lib.ssd_fused_fwd(px, pdt, pA, pB, pC, pD, phi, pcu, py, phf, ctypes.byref(dims),
+                              _stream(stream)))
 
 
 def ssd_fused_states_size(dims) -> int:
@@ -224,19 +309,44 @@ def ssd_fused_bwd_workspace_size(dims) -> int:
 
 def ssd_fused_fwd_train(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, chunk_states,
                         states_bytes, dims, stream=None) -> None:
-    _check(_lib.ssd_fused_fwd_train(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                                    _ptr(init_state), _ptr(cu_seqlens), _ptr(y),
-                                    _ptr(final_state), _ptr(chunk_states), int(states_bytes),
-                                    ctypes.byref(dims), _stream(stream)))
+    ts = _fwd(dims, x, dt, A, B, C, D, y, need=ALL)
+    hi, cu, hf = _state(init_state, dims, "init_state"), _cu(cu_seqlens, dims), \
+        _state(final_state, dims, "final_state")
+    if chunk_states is not None and int(states_bytes) > _bytes(chunk_states):
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "states_bytes exceeds its buffer")
+    px, pdt, pA, pB, pC, pD, py, phi, pcu, phf, pcs = _ptrs(*ts, hi, cu, hf, chunk_states)
+    _check(_lib.ssd_fused_fwd_train(px, pdt, pA, pB, pC, pD, phi, pcu, py, phf, pcs,
+                                    int(states_bytes), ctypes.byref(dims), _stream(stream)))
 
 
 def ssd_fused_bwd(x, dt, A, B, C, D, cu_seqlens, chunk_states, states_bytes, dy, dfinal, dx, ddt,
                   dA, dB, dC, dD, dinit, dims, workspace, workspace_bytes, stream=None) -> None:
-    _check(_lib.ssd_fused_bwd(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
-                              _ptr(cu_seqlens), _ptr(chunk_states), int(states_bytes), _ptr(dy),
-                              _ptr(dfinal), _ptr(dx), _ptr(ddt), _ptr(dA), _ptr(dB), _ptr(dC),
-                              _ptr(dD), _ptr(dinit), ctypes.byref(dims), _ptr(workspace),
+    x, dt, A, B, C, D, _ = _fwd(dims, x, dt, A, B, C, D, need=("x", "dt", "A", "B", "C"))
+    T, H, P, N, G, rows = _sizes(dims)
+    io, f32 = _io_torch(dims), torch.float32
+    outs = (_t(dy, io, T * H * P, "dy"), _state(dfinal, dims, "dfinal"),
+            _t(dx, io, T * H * P, "dx"), _t(ddt, f32, T * H, "ddt"), _t(dA, f32, H, "dA"),
+            _t(dB, f32, T * G * N, "dB"), _t(dC, f32, T * G * N, "dC"),
+            _t(dD, f32, H, "dD", optional=True), _state(dinit, dims, "dinit"))
+    if int(states_bytes) > _bytes(chunk_states) or int(workspace_bytes) > _bytes(workspace):
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "byte count exceeds its buffer")
+    cu = _cu(cu_seqlens, dims)
+    (px, pdt, pA, pB, pC, pD, pcu, pcs, pdy, pdf, pdx, pddt, pdA, pdB, pdC, pdD, pdi,
+     pws) = _ptrs(x, dt, A, B, C, D, cu, chunk_states, *outs, workspace)
+    _check(_lib.ssd_fused_bwd(px, pdt, pA, pB, pC, pD, pcu, pcs, int(states_bytes), pdy, pdf, pdx,
+                              pddt, pdA, pdB, pdC, pdD, pdi, ctypes.byref(dims), pws,
                               int(workspace_bytes), _stream(stream)))
+
+
+def check_cu_seqlens(cu_host, T: int) -> None:
+    """Host-side check of packed-batch offsets (a host copy of cu_seqlens):
+    cu[0] == 0, non-decreasing, cu[-1] == T.  The kernels never leave their
+    buffers on malformed offsets, but the results would be wrong without an
+    error; this turns that case into SSDInvalidArgument."""
+    c = [int(v) for v in cu_host]
+    if not c or c[0] != 0 or c[-1] != int(T) or any(b < a for a, b in zip(c, c[1:])):
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG,
+                                 "cu_seqlens must start at 0, not decrease and end at T")
 
 
 def _raw_ptr(t: Optional[torch.Tensor], offset_elems: int = 0):
@@ -248,16 +358,49 @@ def _raw_ptr(t: Optional[torch.Tensor], offset_elems: int = 0):
     return ctypes.c_void_p(t.data_ptr() + offset_elems * t.element_size()) if t.numel() else None
 
 
+def _span_ok(t: torch.Tensor, rows: int, stride: int, channels: int, name: str) -> None:
+    """rows of `stride` elements starting at t's first element, of which the
+    first `channels` are used, must lie inside t's storage."""
+    if rows == 0:
+        return
+    need = (rows - 1) * stride + channels
+    have = t.untyped_storage().nbytes() // t.element_size() - t.storage_offset()
+    if need > have:
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, f"{name} is smaller than its rows span")
+
+
 def ssd_conv1d_silu(inp, in_stride, weight, bias, kernel_width, out, out_stride, batch, seqlen,
                     nseq, cu_seqlens, channels, io_dtype, stream=None) -> None:
     """inp / out: tensors whose first element is channel 0 of token 0 (row
     strides given in elements, so they may be column slices of wider rows)."""
-    _check(_lib.ssd_conv1d_silu(_raw_ptr(inp), int(in_stride), _ptr(weight), _ptr(bias),
-                                int(kernel_width), _raw_ptr(out), int(out_stride), int(batch),
-                                int(seqlen), int(nseq), _ptr(cu_seqlens), int(channels),
+    io = torch.bfloat16 if io_dtype == SSD_BF16 else torch.float32
+    T = int(seqlen) if int(nseq) > 0 else int(batch) * int(seqlen)
+    for t, name, stride in ((inp, "inp", in_stride), (out, "out", out_stride)):
+        if t is None:
+            if T:
+                raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, f"{name} is required")
+            continue
+        if t.dtype != io:
+            raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, f"{name} must be {io}, got {t.dtype}")
+        _span_ok(t, T, int(stride), int(channels), name)
+    C, K = int(channels), int(kernel_width)
+    cu = None
+    if int(nseq) > 0:
+        cu = _t(cu_seqlens, torch.int32, int(nseq) + 1, "cu_seqlens")
+    elif cu_seqlens is not None:
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "cu_seqlens given without nseq")
+    pw, pb, pcu = _ptrs(_t(weight, torch.float32, C * K, "weight"),
+                        _t(bias, torch.float32, C, "bias", optional=True), cu)
+    _check(_lib.ssd_conv1d_silu(_raw_ptr(inp), int(in_stride), pw, pb, K, _raw_ptr(out),
+                                int(out_stride), int(batch), int(seqlen), int(nseq), pcu, C,
                                 int(io_dtype), _stream(stream)))
 
 
 def ssd_gate_rmsnorm(y, z, weight, eps, out, tokens, width, io_dtype, stream=None) -> None:
-    _check(_lib.ssd_gate_rmsnorm(_ptr(y), _ptr(z), _ptr(weight), float(eps), _ptr(out),
-                                 int(tokens), int(width), int(io_dtype), _stream(stream)))
+    io = torch.bfloat16 if io_dtype == SSD_BF16 else torch.float32
+    n = int(tokens) * int(width)
+    py, pz, pw, po = _ptrs(_t(y, io, n, "y"), _t(z, io, n, "z"),
+                           _t(weight, torch.float32, int(width), "weight", optional=True),
+                           _t(out, io, n, "out"))
+    _check(_lib.ssd_gate_rmsnorm(py, pz, pw, float(eps), po, int(tokens), int(width),
+                                 int(io_dtype), _stream(stream)))

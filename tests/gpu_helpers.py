@@ -82,6 +82,67 @@ def check_full(w, y, fin, tol=None, label=""):
     return ey, ef, y_ref, f_ref
 
 
+def _pair_blocks(w, budget_bytes=1 << 29):
+    """(sequence, head range) blocks covering every pair, each small enough
+    that its fp64 oracle output stays under budget_bytes."""
+    lens = np.diff(w.seq_off)
+    per_head = lambda s: max(1, int(lens[s])) * w.headdim * 8
+    for s in range(w.nsequences):
+        hc = int(max(16, min(w.nheads, budget_bytes // per_head(s))))
+        for h0 in range(0, w.nheads, hc):
+            yield s, h0, min(w.nheads, h0 + hc)
+
+
+def check_whole(w, y, fin, tol=None, label="", head_tokens=None, chunk=None):
+    """Whole-tensor comparison with the oracle on workloads too large to hold
+    the fp64 reference at once: every (sequence, head) pair is computed by the
+    oracle in blocks (one sequence, a run of heads) and compared with the
+    matching slice of y and final_state; the bound is applied to the maxima
+    over the whole tensors, max|y - y_ref| / max|y_ref|.  head_tokens: also
+    bound the error on the first k tokens of each chunk (chunk length
+    `chunk`, default the workload's), where the state handed in dominates."""
+    tol = TOL[w.dtype] if tol is None else tol
+    chunk = chunk or w.chunk
+    so = w.seq_off
+    num = den = fnum = fden = hnum = hden = 0.0
+    fg_all = fin.cpu().numpy()
+    npairs = 0
+    for s, ha, hb in _pair_blocks(w):
+        pairs = [(s, h) for h in range(ha, hb)]
+        ys, fs = oracle.recurrence_workload(w, pairs=pairs)
+        t0, t1 = int(so[s]), int(so[s + 1])
+        if t1 > t0:
+            yg = y.view(w.tokens, w.nheads, w.headdim)[t0:t1, ha:hb].float().cpu().numpy()
+        for k, h in enumerate(range(ha, hb)):
+            ref = ys[k]
+            if ref.size:
+                got = yg[:, k]
+                d = np.abs(got - ref)
+                num = max(num, float(d.max()))
+                den = max(den, float(np.abs(ref).max()))
+                if head_tokens:
+                    sel = (np.arange(ref.shape[0]) % chunk) < head_tokens
+                    hnum = max(hnum, float(d[sel].max()))
+                    hden = max(hden, float(np.abs(ref[sel]).max()))
+            fnum = max(fnum, float(np.max(np.abs(fg_all[s, h] - fs[k]))))
+            fden = max(fden, float(np.max(np.abs(fs[k]))))
+            npairs += 1
+    assert npairs == w.nsequences * w.nheads
+    ey = num / den if den else num
+    ef = fnum / fden if fden else fnum
+    msg = (f"  {label or w.name}: all {npairs} (sequence, head) pairs, y rel err {ey:.3e}, "
+           f"final rel err {ef:.3e}")
+    if head_tokens:
+        eh = hnum / hden if hden else hnum
+        msg += f", first-{head_tokens}-tokens-of-chunk{chunk} rel err {eh:.3e}"
+    say(msg + f" (tol {tol:g})")
+    assert ey <= tol, f"y rel err {ey} > {tol}"
+    assert ef <= tol, f"final rel err {ef} > {tol}"
+    if head_tokens:
+        assert eh <= tol, f"chunk-head rel err {eh} > {tol}"
+    return ey, ef
+
+
 def sample_pairs(w, n, seed=0):
     """A spread of (sequence, head) pairs: first/last sequence and head, the
     longest and shortest sequence, plus random ones."""

@@ -112,7 +112,7 @@ def good():
     (dict(batch=0), SSD_ERR_INVALID_ARG),
     (dict(seqlen=-1), SSD_ERR_INVALID_ARG),
     (dict(nheads=0), SSD_ERR_INVALID_ARG),
-    (dict(ngroups=3), SSD_ERR_INVALID_ARG),          # 4 % 3 != 0
+    (dict(ngroups=3), SSD_ERR_UNSUPPORTED),          # 4 % 3 != 0
     (dict(nseq=2), SSD_ERR_INVALID_ARG),             # packed needs batch == 1
     (dict(io_dtype=7), SSD_ERR_INVALID_ARG),
     (dict(reserved=1), SSD_ERR_INVALID_ARG),
@@ -225,7 +225,7 @@ def test_step_dims():
     d = good_step(); d.nseq = 3
     assert step(d) == SSD_ERR_INVALID_ARG
     d = good_step(); d.ngroups = 3
-    assert step(d) == SSD_ERR_INVALID_ARG          # G must divide H
+    assert step(d) == SSD_ERR_UNSUPPORTED          # G must divide H
     d = good_step(); d.dstate = 96
     assert step(d) == SSD_ERR_UNSUPPORTED
     d = good_step(); d.io_dtype = 7
@@ -314,7 +314,7 @@ def fused(d, **kw):
     (dict(dstate=256), SSD_ERR_UNSUPPORTED),
     (dict(ngroups=4), SSD_ERR_UNSUPPORTED),           # heads per group must be even
     (dict(nheads=6, ngroups=2), SSD_ERR_UNSUPPORTED),
-    (dict(ngroups=3), SSD_ERR_INVALID_ARG),
+    (dict(ngroups=3), SSD_ERR_UNSUPPORTED),           # 4 % 3 != 0
     (dict(reserved=1), SSD_ERR_INVALID_ARG),
     (dict(batch=-1), SSD_ERR_INVALID_ARG),
 ])

@@ -1,7 +1,7 @@
 """ssd_fused_fwd (the one-pass forward, state kept on chip) on the GPU against
 the fp64 oracle, at the forward's tolerance (max |err| / max |ref| <= 2e-2 for
-bf16): full comparison on small problems, sampled (sequence, head) pairs on
-the full-size workloads, and the edge cases of the chunked forward's tests
+bf16): every output compared, the full-size workloads by streaming the
+oracle over blocks of (sequence, head) pairs, and the edge cases of the chunked forward's tests
 (ragged tails, empty and one-token sequences, slow decay, aliased states).
 """
 import numpy as np
@@ -16,8 +16,10 @@ if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
 import mamba_ssd_layer_amd as ssd  # noqa: E402
-from gpu_helpers import (TOL, check_full, check_sampled, rel, run, sample_pairs, say,  # noqa: E402
-                         upload, y_host)
+from gpu_helpers import (TOL, check_full, check_whole, rel, run, say, upload,  # noqa: E402
+                         y_host)
+
+FUSED_CHUNK = 32  # the one-pass forward walks 32-token chunks
 
 
 def run_fused(w, t=None, init="h0", final_state=None):
@@ -36,18 +38,27 @@ def test_small_bf16_full():
     check_full(w, y, fin, label="fused small_bf16")
 
 
-def test_large_bf16_sampled():
+def test_large_bf16_whole():
     # the headline shape: 8 x 4096 tokens, 80 heads, P 64, N 128
     w = workloads.make_workload("large_bf16")
     y, fin, _ = run_fused(w)
-    check_sampled(w, y, fin, sample_pairs(w, 16), label="fused large_bf16")
+    check_whole(w, y, fin, label="fused large_bf16", head_tokens=8, chunk=FUSED_CHUNK)
 
 
-def test_varlen_sampled():
+def test_varlen_whole():
     # 64 packed sequences of mixed length, 8 groups, nonzero initial states
     w = workloads.make_workload("varlen_bf16")
     y, fin, _ = run_fused(w)
-    check_sampled(w, y, fin, sample_pairs(w, 12), label="fused varlen_bf16")
+    check_whole(w, y, fin, label="fused varlen_bf16", head_tokens=8, chunk=FUSED_CHUNK)
+
+
+@pytest.mark.parametrize("name", ["long_n64", "long_n128"])
+def test_long_context_whole(name):
+    # one 65,536-token sequence: the state is carried (with its running
+    # power-of-two scale) across 2,048 chunks
+    w = workloads.make_workload(name)
+    y, fin, _ = run_fused(w)
+    check_whole(w, y, fin, label=f"fused {name}", head_tokens=8, chunk=FUSED_CHUNK)
 
 
 @pytest.mark.parametrize("N", [64, 128])
@@ -73,7 +84,13 @@ def test_long_memory(kind):
           "dt_small": dict(dt_const=1e-3)}[kind]
     w = workloads.make_custom(2, 1500, 4, 64, 128, 1, 256, "bf16", seed=1300, init_std=0.5, **kw)
     y, fin, _ = run_fused(w)
-    check_full(w, y, fin, label=f"fused {kind}")
+    _, _, y_ref, _ = check_full(w, y, fin, label=f"fused {kind}")
+    # first 8 tokens of each 32-token chunk, where the state handed in dominates
+    yg = y_host(y, w)
+    sel = np.tile((np.arange(w.seqlen) % FUSED_CHUNK) < 8, w.batch)
+    e = np.max(np.abs(yg[sel] - y_ref[sel])) / np.max(np.abs(y_ref[sel]))
+    say(f"    first 8 tokens of each chunk: rel err {e:.3e}")
+    assert e <= TOL["bf16"]
 
 
 @pytest.mark.parametrize("dt_shift", [-1.0, 0.5])

@@ -15,6 +15,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():
     pytest.skip("needs a GPU", allow_module_level=True)
 
+import mamba_ssd_layer_amd as ssd  # noqa: E402
 from gpu_helpers import plan_for, rel, say, upload, y_host  # noqa: E402
 
 CASES = {
@@ -113,7 +114,12 @@ def test_chunk_table_rejects_bad_cu_seqlens_without_faulting():
     t = upload(w)
     t["cu"] = torch.tensor([0, 100, 60, 230], dtype=torch.int32, device=t["x"].device)
     plan = plan_for(w, t)
-    plan.cumsum(t["dt"], t["A"], t["cu"])
+    # the Python plan refuses such offsets on the host ...
+    with pytest.raises(ssd.SSDInvalidArgument):
+        plan.cumsum(t["dt"], t["A"], t["cu"])
+    # ... the C entry point takes them and the device side contains them
+    ssd.libssd.ssd_chunk_cumsum(t["dt"], t["A"], plan.chunk_len, t["cu"], plan.dims,
+                                plan.workspace)
     torch.cuda.synchronize()
     d = plan.view("chunk_dir").cpu().numpy()
     assert d[-1] != 0
