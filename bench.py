@@ -596,7 +596,7 @@ def main() -> int:
         decode = decode_step(torch, ssd, workloads, dev, args.steps, args.warmup)
 
     train = None
-    if fused is not None and not args.no_train:
+    if fused is not None and not args.no_train and ssd.libssd.ssd_fused_bwd_workspace_size(dims) > 0:
         train = training_step(torch, ssd, workloads, w,
                               {"x": x, "dt": dt, "A": A, "B": Bm, "C": Cm, "D": D, "h0": h0,
                                "cu": cu}, args.steps, args.warmup)

@@ -8,7 +8,7 @@ include/ssd.h).  This package is its Python face:
                      allocates y / final_state / workspace, runs the forward
   SSDForward         a reusable plan (fixed dims, workspace allocated once)
   fused_fwd()        the same forward in one pass per (sequence, head), no workspace
-                     (bf16, headdim 64, dstate 64 / 128)
+                     (bf16, head dim 64 / 128 / 192 / 256, dstate 64 / 128 / 256)
   step()             one recurrent decode step per sequence, state updated in place
   conv1d_silu()      the causal depthwise conv1d + SiLU before the core
   gate_rmsnorm()     y * SiLU(z), then RMS norm over the channel width, after it
@@ -206,7 +206,7 @@ def fused_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
               chunk_states: Optional[torch.Tensor] = None,
               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """y, final_state = SSD forward in one pass per (sequence, head) (ssd_fused_fwd:
-    bf16, headdim 64, dstate 64 or 128; no workspace).  Same arguments and
+    bf16, head dim 64 / 128 / 192 / 256, dstate 64 / 128 / 256; no workspace).  Same arguments and
     results as chunk_scan_fwd.  With chunk_states (a uint8 device buffer of
     fused_states_bytes(...) bytes, see make_fused_states) it also saves the
     state entering every 64-token chunk for fused_bwd (ssd_fused_fwd_train)."""
@@ -259,7 +259,9 @@ def fused_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
     if workspace is None:
         n = libssd.ssd_fused_bwd_workspace_size(dims)
         if n == 0:
-            raise SSDUnsupported(libssd.SSD_ERR_UNSUPPORTED, "shape outside the one-pass forward")
+            raise SSDUnsupported(libssd.SSD_ERR_UNSUPPORTED,
+                                 "shape outside the backward's (bf16, head dim 64, N 64 or 128, "
+                                 "an even number of heads per group)")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
     out = dict(dx=torch.empty_like(x), ddt=torch.empty(dt.shape, dtype=torch.float32, device=dev),
                dA=torch.empty(dims.nheads, dtype=torch.float32, device=dev),

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
     const uint16_t *__restrict__ Cm, const float *__restrict__ Dv, const float *__restrict__ acum,
     const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int nc,
-    int H, int G, uint16_t *__restrict__ y) {
+    int H, int G, int hr, uint16_t *__restrict__ y) {
   static_assert(P == 64 && N % 64 == 0 && Q % 64 == 0, "tile shape");
   constexpr int NT = Q;          // threads
   constexpr int NW = Q / 64;     // wavefronts
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(Q, Q >= 128 ? 2 : 1) void k_chunk_scan_lds(
   const float al1 = sa[l1], al2 = sa[l2];
   const float u1 = __expf(al1 - sa[32 * j1]);  // <= 1: exp(acum_l - acum at the tile's start)
   const float u2 = __expf(al2 - sa[32 * j2]);
-  const float Dh = Dv ? Dv[h] : 0.f;
+  const float Dh = Dv ? Dv[h / hr] : 0.f;
 
   f32x16 acc1[TP], acc2[TP];
 #pragma unroll
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     const uint16_t *__restrict__ x, const uint16_t *__restrict__ Bm,
     const uint16_t *__restrict__ Cm, const float *__restrict__ Dv, const float *__restrict__ acum,
     const float *__restrict__ dtq, const uint16_t *__restrict__ hprev, ChunkGeom geom, int nc,
-    int H, int G, int hb, int nkb, uint16_t *__restrict__ y) {
+    int H, int G, int hb, int nkb, int hr, uint16_t *__restrict__ y) {
   constexpr int Q = 256, P = 64;
   static_assert(N == 64 || N == 128 || N == 256, "head-batched tile shape");
   // N 256: B is staged in two 128-column halves for the Z phase, and hprev
@@ -696,6 +696,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     const int l = T * 32 + col;
 
     wait_vmcnt<0>();  // this head's loads; the stores of y two heads back
+    wait_lgkmcnt0();  // this wavefront's y staging of the previous head
     __syncthreads();  // ... for every thread; the previous head is done everywhere
     if (hi > 0) store_y(Lh, hh - 1, smem + (slot ? XS0 : XS1));
     {  // column s = tid % Q; rows 1..3 (first half of the block) or 4..7
@@ -791,7 +792,7 @@ __global__ __launch_bounds__(512, 1) void k_chunk_scan_hb(
     }
     {  // D x_l in fp32: rows p = 32t + 8rb + 4kg + e of column l are 4
        // consecutive elements of x row l
-      const float Dh = Dv ? Dv[hh] : 0.f;
+      const float Dh = Dv ? Dv[hh / hr] : 0.f;
 #pragma unroll
       for (int t = 0; t < TP; ++t) {
 #pragma unroll
@@ -843,13 +844,13 @@ static void launch_sc(const void *x, const void *B, const void *C, const float *
                        stream, static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                        static_cast<const uint16_t *>(C), D, acum, dtq,
                        static_cast<const uint16_t *>(hprev), cg, (int)geo.nc_max, geo.H, geo.G, hb,
-                       nkb, static_cast<uint16_t *>(y));
+                       nkb, geo.hr, static_cast<uint16_t *>(y));
   } else {
     hipLaunchKernelGGL((k_chunk_scan_lds<Q, P, N>), grid, dim3(Q), 0, stream,
                        static_cast<const uint16_t *>(x), static_cast<const uint16_t *>(B),
                        static_cast<const uint16_t *>(C), D, acum, dtq,
                        static_cast<const uint16_t *>(hprev), cg, (int)geo.nc_max, geo.H, geo.G,
-                       static_cast<uint16_t *>(y));
+                       geo.hr, static_cast<uint16_t *>(y));
   }
 }
 

@@ -94,40 +94,52 @@ __device__ __forceinline__ void wave_sync() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Geometry of one kernel instance: N state size, HPB heads per block, R ring slots.
-template <int N, int HPB, int R>
+// Geometry of one kernel instance: N state size, HPB heads per block, PW
+// state rows p per wavefront (32 or 16: 64 / PW wavefronts per head), R ring
+// slots.
+template <int N, int HPB, int PW, int R>
 struct FusedCfg {
-  static constexpr int P = 64, CQ = 32, WAVES = 2 * HPB, THREADS = 64 * WAVES;
+  static constexpr int P = 64, CQ = 32, WPH = P / PW, WAVES = WPH * HPB, THREADS = 64 * WAVES;
+  static constexpr int PT = PW / 16;             // 16-column state tiles per wavefront
+  static constexpr int XR = CQ / WPH;            // x / y rows of a chunk a wavefront moves
+  static constexpr int XI = XR * P * 2 / 1024;   // ... in 1 KB direct-to-LDS loads / row stores
   static constexpr int XH = CQ * P * 2;          // x of one head and chunk: 32 rows x 128 B
   static constexpr int BT = CQ * N * 2;          // B (or C) of a chunk
-  static constexpr int DW = 64 * 4;              // one wavefront's dt piece
+  static constexpr int DW = 64 * 4;              // the chunk's dt piece (wavefront 0 loads it)
   static constexpr int OX = 0, OB = HPB * XH, OC = OB + BT, OD = OC + BT;
-  static constexpr int SLOT = OD + WAVES * DW;
+  static constexpr int SLOT = OD + DW;
   static constexpr int AD = R * SLOT;            // per wavefront: [al2 | bs2 | w], 32 floats each
   static constexpr int ADW = 3 * CQ * 4;
   static constexpr int TOTAL = AD + WAVES * ADW;
   static constexpr int BCI = 2 * BT / 1024 / WAVES;  // 1 KB pieces of B and C per wavefront
-  static constexpr int LDC = 2 + BCI + 1;        // vector-memory ops a wavefront issues per chunk load
-  static constexpr int STC = 2;                  // ... per chunk of y it stores
+  static constexpr int LDC = XI + BCI;           // vector-memory ops a wavefront issues per chunk
+                                                 // load (+1 for wavefront 0's dt piece)
+  static constexpr int STC = XI;                 // ... per chunk of y it stores
   static constexpr int BLOCKS_PER_CU = (160 * 1024) / TOTAL;
-  static constexpr int WAVES_PER_SIMD = BLOCKS_PER_CU * WAVES / 4;
-  static_assert(BCI * WAVES * 1024 == 2 * BT, "B and C split evenly over the wavefronts");
-  static_assert(32 * HPB <= 64 * WAVES, "dt pieces");
-  static constexpr int SVC = N / 16;             // ... per saved chunk-start state
-  static_assert(R >= 3 && (R - 2) * (LDC + STC + SVC) <= 47, "wait counts");
-  static_assert(BLOCKS_PER_CU >= 1 && WAVES_PER_SIMD >= 2, "occupancy");
+  // waves a SIMD must hold for BLOCKS_PER_CU blocks (at most 3: the kernel
+  // needs ~140-200 VGPRs, so more would spill)
+  static constexpr int WAVES_PER_SIMD_LDS = (BLOCKS_PER_CU * WAVES + 3) / 4;
+  static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_LDS < 3 ? WAVES_PER_SIMD_LDS : 3;
+  static_assert(PW == 16 || PW == 32, "state rows per wavefront");
+  static_assert(XI >= 1 && XI * 1024 == XR * P * 2, "x rows in 1 KB pieces");
+  static_assert(BCI >= 1 && BCI * WAVES * 1024 == 2 * BT, "B and C split evenly over the wavefronts");
+  static_assert(CQ * HPB <= 64, "one dt piece a chunk");
+  static constexpr int SVC = PT * N / 32;        // ... per saved chunk-start state
+  static_assert(R >= 2 && (R - 2) * (LDC + 1 + STC + SVC) <= 47, "wait counts");
+  static_assert(BLOCKS_PER_CU >= 1 && WAVES_PER_SIMD >= 1, "occupancy");
 };
 
-template <int N, int HPB, int R, bool SAVE>
-__global__ __launch_bounds__((FusedCfg<N, HPB, R>::THREADS), (FusedCfg<N, HPB, R>::WAVES_PER_SIMD))
+template <int N, int HPB, int PW, int R, bool SAVE>
+__global__ __launch_bounds__((FusedCfg<N, HPB, PW, R>::THREADS),
+                             (FusedCfg<N, HPB, PW, R>::WAVES_PER_SIMD))
 void k_ssd_fused(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
     const float *__restrict__ h0, const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows,
-    int H, int G, uint16_t *__restrict__ y, float *__restrict__ hfin,
+    int H, int G, int hr, uint16_t *__restrict__ y, float *__restrict__ hfin,
     uint16_t *__restrict__ hsave) {
-  using F = FusedCfg<N, HPB, R>;
-  constexpr int P = F::P, CQ = F::CQ;
+  using F = FusedCfg<N, HPB, PW, R>;
+  constexpr int P = F::P, CQ = F::CQ, WPH = F::WPH, PT = F::PT, XR = F::XR, XI = F::XI;
   constexpr int NT = N / 16;   // state tiles per p-tile (over n)
   constexpr int KQ = N / 32;   // K steps over n
   constexpr int NCB = N / 8;   // 16-byte chunks per B / C row
@@ -143,7 +155,8 @@ void k_ssd_fused(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int c16 = lane & 15, g4 = lane >> 4;
-  const int hh = wave >> 1, ph = wave & 1;
+  const int hh = wave / WPH, pq = wave % WPH;  // head of the block, state-row slice
+  const int p0 = PW * pq;                       // the slice's first row p
   const int h0b = HPB * hb;  // the block's first head
   const int h = h0b + hh;
   const int g = h0b / (H / G);
@@ -151,19 +164,20 @@ void k_ssd_fused(
   seq_range(cu, s, L, T, tb, len);
   const int64_t sh = (int64_t)s * H + h;
   const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
-  const float Ah = A[h];
-  const float Dh = Dv ? Dv[h] : 0.f;
+  const int Hd = H / hr;  // heads of dt, A and D: kernel head h takes those of h / hr
+  const float Ah = A[h / hr];
+  const float Dh = Dv ? Dv[h / hr] : 0.f;
   float *adw = reinterpret_cast<float *>(smem + AD + wave * ADW);
 
-  // state h^T: hst[pt][j] holds column p = 32 ph + 16 pt + c16 and rows
+  // state h^T: hst[pt][j] holds column p = p0 + 16 pt + c16 and rows
   // n = nrow(j) + r, nrow(j) = 32 (j/2) + 8 g4 + 4 (j%2): tiles 2q and 2q+1
   // together give lane group g4 the 8 consecutive n = 32q + 8 g4 + 0..7, so a
   // K step of the inter term reads its C operand as one 16-byte piece
   auto nrow = [&](int j) { return 32 * (j >> 1) + 8 * g4 + 4 * (j & 1); };
-  f32x4 hst[2][NT];
+  f32x4 hst[PT][NT];
 #pragma unroll
-  for (int pt = 0; pt < 2; ++pt) {
-    const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N;
+  for (int pt = 0; pt < PT; ++pt) {
+    const int64_t prow = (sh * P + p0 + 16 * pt + c16) * N;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
       hst[pt][j] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + prow + nrow(j)) : f32x4{};
@@ -180,11 +194,11 @@ void k_ssd_fused(
   // Each load is a wave-uniform base (the chunk's first row) plus a per-lane
   // byte offset fixed for the whole sequence; only a partial last chunk
   // recomputes the offsets with its rows clamped.
-  uint32_t xoff[2], bcoff[BCI], dtoff;
+  uint32_t xoff[XI], bcoff[BCI], dtoff;
   auto lane_offsets = [&](int last) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {  // rows 16 ph .. 16 ph + 15 of head hh's x, 8 chunks each
-      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = (m & 7) ^ rot_swz<8>(r);
+    for (int i = 0; i < XI; ++i) {  // rows XR pq .. XR pq + XR - 1 of head hh's x, 8 chunks each
+      const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = (m & 7) ^ rot_swz<8>(r);
       xoff[i] = static_cast<uint32_t>((min(r, last) * ldx + (int64_t)h * P + 8 * cc) * 2);
     }
 #pragma unroll
@@ -193,10 +207,10 @@ void k_ssd_fused(
       const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ rot_swz<NCB>(r);
       bcoff[i] = static_cast<uint32_t>((min(r, last) * ldb + (int64_t)g * N + 8 * cc) * 2);
     }
-    // dt of the block's heads: entry e = token * HPB + head, 64 entries a
-    // wavefront (past the last entry every lane reads that one)
-    const int e = min(wave * 64 + lane, CQ * HPB - 1);
-    dtoff = static_cast<uint32_t>((min(e / HPB, last) * H + h0b + e % HPB) * 4);
+    // dt of the block's heads: entry e = token * HPB + head, one 64-entry
+    // piece (past the last entry every lane reads that one)
+    const int e = min(lane, CQ * HPB - 1);
+    dtoff = static_cast<uint32_t>((min(e / HPB, last) * Hd + (h0b + e % HPB) / hr) * 4);
   };
   lane_offsets(CQ - 1);
   auto issue = [&](int k, int sl) {
@@ -205,28 +219,28 @@ void k_ssd_fused(
     if (last < CQ - 1) lane_offsets(last);
     const uint32_t base = lds_off(smem) + sl * SLOT;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) dma_lds16_sb(xoff[i], x + t0 * ldx, base + OX + hh * XH + 16 * ph * 128 + i * 1024);
+    for (int i = 0; i < XI; ++i) dma_lds16_sb(xoff[i], x + t0 * ldx, base + OX + hh * XH + XR * pq * 128 + i * 1024);
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {
       const int u = wave * BCI + i, tile = u / (BT / 1024), pi = u % (BT / 1024);
       dma_lds16_sb(bcoff[i], (tile ? Cm : Bm) + t0 * ldb, base + (tile ? OC : OB) + pi * 1024);
     }
-    dma_lds4_sb(dtoff, dt + t0 * H, base + OD + wave * DW);
+    if (wave == 0) dma_lds4_sb(dtoff, dt + t0 * Hd, base + OD);
   };
-  // rows 16 ph .. 16 ph + 15 of head hh's y of chunk k (staged in slot sl): STC stores
+  // rows XR pq .. XR pq + XR - 1 of head hh's y of chunk k (staged in slot sl): STC stores
   auto store_y = [&](int k, int sl) {
     const int64_t t0 = tb + (int64_t)k * CQ;
     const int rem = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ));
     const unsigned char *ys = smem + sl * SLOT + OX + hh * XH;
-    u32x4 v[2];
+    u32x4 v[XI];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = m & 7;
+    for (int i = 0; i < XI; ++i) {
+      const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = m & 7;
       v[i] = *reinterpret_cast<const u32x4 *>(ys + r * 128 + ((cc ^ rot_swz<8>(r)) << 4));
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int m = i * 64 + lane, r = 16 * ph + (m >> 3), cc = m & 7;
+    for (int i = 0; i < XI; ++i) {
+      const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = m & 7;
       if (r < rem) *reinterpret_cast<u32x4 *>(y + (t0 + r) * ldx + (int64_t)h * P + 8 * cc) = v[i];
     }
   };
@@ -252,6 +266,7 @@ void k_ssd_fused(
   };
 
   constexpr int D = R - 1;  // chunks in flight ahead of the one being computed
+  const int ldc = LDC + (wave == 0 ? 1 : 0);  // wavefront 0 also loads the dt piece
 #pragma unroll
   for (int c = 0; c < D; ++c)
     if (c < nck) issue(c, c);
@@ -263,17 +278,18 @@ void k_ssd_fused(
     // iteration) and the y stores of the iterations in between
     // (and, when saving, the state stores of the even ones: SVC each)
     {
-      int n = k < D ? (min(D, nck) - 1 - k) * LDC : 0;
+      int n = k < D ? (min(D, nck) - 1 - k) * ldc : 0;
       for (int j = k < D ? 0 : k - D + 1; j < k; ++j)
-        n += (SAVE && !(j & 1) ? SVC : 0) + (j >= 1 ? STC : 0) + (j + D < nck ? LDC : 0);
+        n += (SAVE && !(j & 1) ? SVC : 0) + (j >= 1 ? STC : 0) + (j + D < nck ? ldc : 0);
       wait_vmcnt_dyn(n);
     }
+    wait_lgkmcnt0();  // this wavefront's y staging of chunk k-1 is in LDS
     __syncthreads();  // every wavefront's share of chunk k is in; chunk k-1 is done everywhere
     if (SAVE && !(k & 1)) {  // the state entering the 64-token pair, h = S 2^lam, rounded to bf16
       const float e = exp2_fast(lam);
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
-        u32x4 pk[KQ];  // row p = 32 ph + 16 pt + c16, n = 32 q + 8 g4 + 0..7
+      for (int pt = 0; pt < PT; ++pt) {
+        u32x4 pk[KQ];  // row p = p0 + 16 pt + c16, n = 32 q + 8 g4 + 0..7
 #pragma unroll
         for (int q = 0; q < KQ; ++q) {
           const f32x4 u = hst[pt][2 * q] * e, v = hst[pt][2 * q + 1] * e;
@@ -281,7 +297,7 @@ void k_ssd_fused(
                         pack_bf16x2(v.z, v.w)};
         }
         store_rows128(hsave + ((pbase + (k >> 1)) * H + h) * (int64_t)(P * N) +
-                          (int64_t)(32 * ph + 16 * pt) * N,
+                          (int64_t)(p0 + 16 * pt) * N,
                       N, pk, c16, g4);
       }
     }
@@ -289,7 +305,7 @@ void k_ssd_fused(
     if (k >= 1) store_y(k - 1, slp);
     if (k + D < nck) issue(k + D, slp);
 
-    unsigned char *xh = smem + sl * SLOT + OX + hh * XH;  // head hh's x tile (this wavefront: columns 32 ph ..)
+    unsigned char *xh = smem + sl * SLOT + OX + hh * XH;  // head hh's x tile (this wavefront: columns p0 ..)
     const unsigned char *bs = smem + sl * SLOT + OB;
     const unsigned char *cs = smem + sl * SLOT + OC;
     const float *dts = reinterpret_cast<const float *>(smem + sl * SLOT + OD);
@@ -318,15 +334,15 @@ void k_ssd_fused(
     for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
       for (int q = 0; q < KQ; ++q) cop[lt][q] = row_op(cs, 16 * lt + c16, q);
-    f32x4 ya[2][2];
+    f32x4 ya[PT][2];
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
+    for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = f32x4{};
 #pragma unroll
     for (int q = 0; q < KQ; ++q) {
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
+      for (int pt = 0; pt < PT; ++pt) {
         const f32x4 u = hst[pt][2 * q], v = hst[pt][2 * q + 1];
         const u32x4 sop{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
                         pack_bf16x2(v.z, v.w)};
@@ -337,7 +353,7 @@ void k_ssd_fused(
     const float al0 = adw[c16], al1 = adw[16 + c16];
     const float f0 = exp2_fast(al0 + lam), f1 = exp2_fast(al1 + lam);
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
+    for (int pt = 0; pt < PT; ++pt) {
       ya[pt][0] *= f0;
       ya[pt][1] *= f1;
     }
@@ -371,20 +387,20 @@ void k_ssd_fused(
                      pack_bf16x2(g11[0], g11[1]), pack_bf16x2(g11[2], g11[3])};
     }
     // X^T in the same token order: s = 4 g4 + {0..3}, 16 + 4 g4 + {0..3}
-    u32x4 xop[2];
+    u32x4 xop[PT];
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      const u32x2 t0 = tr4(xh, 128, 8, 4 * g4, 32 * ph + 16 * pt);
-      const u32x2 t1 = tr4(xh, 128, 8, 16 + 4 * g4, 32 * ph + 16 * pt);
+    for (int pt = 0; pt < PT; ++pt) {
+      const u32x2 t0 = tr4(xh, 128, 8, 4 * g4, p0 + 16 * pt);
+      const u32x2 t1 = tr4(xh, 128, 8, 16 + 4 * g4, p0 + 16 * pt);
       xop[pt] = u32x4{t0.x, t0.y, t1.x, t1.y};
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(xop[pt], gop[lt], ya[pt][lt]);
     }
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {  // D x: rows p = 16 pt + 4 g4 + r of token l
+    for (int pt = 0; pt < PT; ++pt) {  // D x: rows p = 16 pt + 4 g4 + r of token l
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) {
-        const int l = 16 * lt + c16, col = 32 * ph + 16 * pt + 4 * g4;
+        const int l = 16 * lt + c16, col = p0 + 16 * pt + 4 * g4;
         const u32x2 v = *reinterpret_cast<const u32x2 *>(
             xh + l * 128 + (((col >> 3) ^ rot_swz<8>(l)) << 4) + (col & 7) * 2);
         ya[pt][lt].x += Dh * bf16lo(v.x);
@@ -401,16 +417,16 @@ void k_ssd_fused(
       if (steep) {
         const float e = exp2_fast(lam + a2last);
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
+        for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
           for (int j = 0; j < NT; ++j) hst[pt][j] *= e;
       }
       lam = steep ? 0.f : lam + a2last;
       const f32x4 w0 = *reinterpret_cast<const f32x4 *>(adw + 2 * CQ + 4 * g4);
       const f32x4 w1 = *reinterpret_cast<const f32x4 *>(adw + 2 * CQ + 16 + 4 * g4);
-      u32x4 xw[2];
+      u32x4 xw[PT];
 #pragma unroll
-      for (int pt = 0; pt < 2; ++pt) {
+      for (int pt = 0; pt < PT; ++pt) {
         const u32x4 q = xop[pt];
         xw[pt] = u32x4{pack_bf16x2(bf16lo(q.x) * w0.x, bf16hi(q.x) * w0.y),
                        pack_bf16x2(bf16lo(q.y) * w0.z, bf16hi(q.y) * w0.w),
@@ -422,12 +438,12 @@ void k_ssd_fused(
         const u32x2 t0 = trb(bs, 4 * g4, j), t1 = trb(bs, 16 + 4 * g4, j);
         const u32x4 bt{t0.x, t0.y, t1.x, t1.y};
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt) hst[pt][j] = mfma16(bt, xw[pt], hst[pt][j]);
+        for (int pt = 0; pt < PT; ++pt) hst[pt][j] = mfma16(bt, xw[pt], hst[pt][j]);
       }
       if (lam < -32.f) {
         const float e = exp2_fast(lam);
 #pragma unroll
-        for (int pt = 0; pt < 2; ++pt)
+        for (int pt = 0; pt < PT; ++pt)
 #pragma unroll
           for (int j = 0; j < NT; ++j) hst[pt][j] *= e;
         lam = 0.f;
@@ -436,10 +452,10 @@ void k_ssd_fused(
 
     // y staged (bf16) over this wavefront's columns of the x tile, now fully read
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
+    for (int pt = 0; pt < PT; ++pt) {
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) {
-        const int l = 16 * lt + c16, col = 32 * ph + 16 * pt + 4 * g4;
+        const int l = 16 * lt + c16, col = p0 + 16 * pt + 4 * g4;
         const u32x2 o{pack_bf16x2(ya[pt][lt].x, ya[pt][lt].y), pack_bf16x2(ya[pt][lt].z, ya[pt][lt].w)};
         *reinterpret_cast<u32x2 *>(xh + l * 128 + (((col >> 3) ^ rot_swz<8>(l)) << 4) + (col & 7) * 2) = o;
       }
@@ -447,14 +463,15 @@ void k_ssd_fused(
     sl = sl == R - 1 ? 0 : sl + 1;
   }
   if (nck > 0) {
-    __syncthreads();  // both halves of the last chunk's y are staged
+    wait_lgkmcnt0();
+    __syncthreads();  // every wavefront's part of the last chunk's y is staged
     store_y(nck - 1, (nck - 1) % R);
   }
   if (hfin) {
     const float e = exp2_fast(lam);
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt) {
-      const int64_t prow = (sh * P + 32 * ph + 16 * pt + c16) * N;
+    for (int pt = 0; pt < PT; ++pt) {
+      const int64_t prow = (sh * P + p0 + 16 * pt + c16) * N;
 #pragma unroll
       for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(hfin + prow + nrow(j)) = hst[pt][j] * e;
     }
@@ -464,39 +481,61 @@ void k_ssd_fused(
 }  // namespace
 
 bool fused_supported(int H, int P, int N, int G) {
-  return P == 64 && (N == 64 || N == 128) && (H / G) % 2 == 0;
+  return P == 64 && (N == 64 || N == 128 || N == 256) && H % G == 0;
 }
 
 namespace {
-template <int N, int HPB, int R, bool SAVE>
+template <int N, int HPB, int PW, int R, bool SAVE>
 void launch_fused_t(const uint16_t *x, const float *dt, const float *A, const uint16_t *B,
                     const uint16_t *C, const float *D, const float *h0, const int32_t *cu, int64_t L,
-                    int64_t T, int rows, int H, int G, uint16_t *y, float *hfin, uint16_t *hsave,
-                    hipStream_t stream) {
-  hipLaunchKernelGGL((k_ssd_fused<N, HPB, R, SAVE>), dim3(xcd_grid(rows, H / HPB)),
-                     dim3(FusedCfg<N, HPB, R>::THREADS), 0, stream, x, dt, A, B, C, D, h0, cu, L, T,
-                     rows, H, G, y, hfin, hsave);
+                    int64_t T, int rows, int H, int G, int hr, uint16_t *y, float *hfin,
+                    uint16_t *hsave, hipStream_t stream) {
+  hipLaunchKernelGGL((k_ssd_fused<N, HPB, PW, R, SAVE>), dim3(xcd_grid(rows, H / HPB)),
+                     dim3(FusedCfg<N, HPB, PW, R>::THREADS), 0, stream, x, dt, A, B, C, D, h0, cu,
+                     L, T, rows, H, G, hr, y, hfin, hsave);
+}
+
+// Instances: two heads a block (four wavefronts of 32 state rows, a three-slot
+// ring) where the heads of a group pair up and the (sequence, head pair)
+// blocks fill the GPU; else one head a block (two wavefronts, a two-slot ring,
+// up to three blocks a CU), which doubles the blocks of few long sequences.
+// N = 256 takes one head a block in four wavefronts of 16 rows (the state of
+// a wavefront stays at 64 registers).
+template <int N, bool SAVE>
+void launch_fused_n(bool pairs, const uint16_t *x, const float *dt, const float *A,
+                    const uint16_t *B, const uint16_t *C, const float *D, const float *h0,
+                    const int32_t *cu, int64_t L, int64_t T, int rows, int H, int G, int hr,
+                    uint16_t *y, float *hfin, uint16_t *hsave, hipStream_t stream) {
+  if constexpr (N == 256) {
+    launch_fused_t<N, 1, 16, 2, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
+  } else {
+    if (pairs) launch_fused_t<N, 2, 32, 3, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
+    else launch_fused_t<N, 1, 32, 2, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
+  }
 }
 }  // namespace
 
 hipError_t launch_fused(const void *x, const float *dt, const float *A, const void *B, const void *C,
                         const float *D, const float *h0, const int32_t *cu, int64_t L, int64_t T,
-                        int rows, int H, int P, int N, int G, void *y, float *hfin, void *hsave,
-                        hipStream_t stream) {
+                        int rows, int H, int P, int N, int G, int hr, void *y, float *hfin,
+                        void *hsave, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  if (!fused_supported(H, P, N, G)) return hipErrorInvalidValue;
+  if (!fused_supported(H, P, N, G) || hr < 1 || H % hr != 0) return hipErrorInvalidValue;
   const uint16_t *xi = static_cast<const uint16_t *>(x);
   const uint16_t *bi = static_cast<const uint16_t *>(B);
   const uint16_t *ci = static_cast<const uint16_t *>(C);
   uint16_t *yo = static_cast<uint16_t *>(y);
   uint16_t *hs = static_cast<uint16_t *>(hsave);
-  if (N == 64) {
-    if (hs) launch_fused_t<64, 2, 3, true>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, hs, stream);
-    else launch_fused_t<64, 2, 3, false>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, hs, stream);
-  } else {
-    if (hs) launch_fused_t<128, 2, 3, true>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, hs, stream);
-    else launch_fused_t<128, 2, 3, false>(xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, yo, hfin, hs, stream);
+  const bool pairs = (H / G) % 2 == 0 && (int64_t)rows * (H / 2) >= device_cus();
+#define SSD_FUSED_N(NN)                                                                           \
+  if (hs) launch_fused_n<NN, true>(pairs, xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, hr, yo, hfin, hs, stream); \
+  else launch_fused_n<NN, false>(pairs, xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, hr, yo, hfin, hs, stream);
+  switch (N) {
+    case 64: SSD_FUSED_N(64) break;
+    case 128: SSD_FUSED_N(128) break;
+    default: SSD_FUSED_N(256) break;
   }
+#undef SSD_FUSED_N
   return hipGetLastError();
 }
 

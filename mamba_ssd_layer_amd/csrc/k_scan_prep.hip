@@ -100,13 +100,14 @@ hipError_t launch_chunk_table(const int32_t *cu_seqlens, const Geometry &geo, in
 // values: lane i holds Q/64 consecutive tokens, a serial prefix in registers,
 // then an inclusive scan of the lane totals across the wavefront.  Outputs are
 // transposed to chunk-major, Q-contiguous rows (acum, dtq), so the contraction
-// kernels read them with unit stride.
+// kernels read them with unit stride.  H heads of dt and A; with hr > 1 each
+// head's rows are written for its hr kernel heads h * hr .. h * hr + hr - 1.
 constexpr int kCumsumHeads = 16;
 
 template <int Q>
 __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ dt,
                                                       const float *__restrict__ A, ChunkGeom geom,
-                                                      int H, float *__restrict__ acum,
+                                                      int H, int hr, float *__restrict__ acum,
                                                       float *__restrict__ dtq) {
   constexpr int E = Q / 64;  // tokens per lane
   __shared__ float sdt[kCumsumHeads][Q + 1];
@@ -161,12 +162,14 @@ __global__ __launch_bounds__(256) void k_chunk_cumsum(const float *__restrict__ 
       if (e == last % E) mine = excl + pre[e];
     }
     const float lastval = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine), last / E));
-    float *ao = acum + ((int64_t)c * H + h) * Q + lane * E;
-    float *dq = dtq + ((int64_t)c * H + h) * Q + lane * E;
+    for (int r = 0; r < hr; ++r) {
+      float *ao = acum + ((int64_t)c * H * hr + (int64_t)h * hr + r) * Q + lane * E;
+      float *dq = dtq + ((int64_t)c * H * hr + (int64_t)h * hr + r) * Q + lane * E;
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      ao[e] = lane * E + e < ci.len ? excl + pre[e] : lastval;
-      dq[e] = v[e];
+      for (int e = 0; e < E; ++e) {
+        ao[e] = lane * E + e < ci.len ? excl + pre[e] : lastval;
+        dq[e] = v[e];
+      }
     }
   }
 }
@@ -175,16 +178,17 @@ hipError_t launch_chunk_cumsum(const float *dt, const float *A, const Geometry &
                                float *dtq, hipStream_t stream) {
   if (geo.nc_max == 0) return hipSuccess;
   const ChunkGeom cg{geo.L, geo.nc_row, geo.Q, geo.table};
-  const dim3 grid((unsigned)geo.nc_max, (unsigned)((geo.H + kCumsumHeads - 1) / kCumsumHeads));
+  const int Hd = geo.H / geo.hr;  // heads of dt and A
+  const dim3 grid((unsigned)geo.nc_max, (unsigned)((Hd + kCumsumHeads - 1) / kCumsumHeads));
   switch (geo.Q) {
     case 64:
-      hipLaunchKernelGGL(k_chunk_cumsum<64>, grid, dim3(256), 0, stream, dt, A, cg, geo.H, acum, dtq);
+      hipLaunchKernelGGL(k_chunk_cumsum<64>, grid, dim3(256), 0, stream, dt, A, cg, Hd, geo.hr, acum, dtq);
       break;
     case 128:
-      hipLaunchKernelGGL(k_chunk_cumsum<128>, grid, dim3(256), 0, stream, dt, A, cg, geo.H, acum, dtq);
+      hipLaunchKernelGGL(k_chunk_cumsum<128>, grid, dim3(256), 0, stream, dt, A, cg, Hd, geo.hr, acum, dtq);
       break;
     case 256:
-      hipLaunchKernelGGL(k_chunk_cumsum<256>, grid, dim3(256), 0, stream, dt, A, cg, geo.H, acum, dtq);
+      hipLaunchKernelGGL(k_chunk_cumsum<256>, grid, dim3(256), 0, stream, dt, A, cg, Hd, geo.hr, acum, dtq);
       break;
     default:
       return hipErrorInvalidValue;

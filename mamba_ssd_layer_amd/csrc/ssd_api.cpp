@@ -38,9 +38,12 @@ ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
   if (chunk_len != 64 && chunk_len != 128 && chunk_len != 256) return SSD_ERR_UNSUPPORTED;
   // heads split evenly over the groups: the only head-to-group map compiled
   if (d->nheads % d->ngroups != 0) return SSD_ERR_UNSUPPORTED;
-  const int64_t H = d->nheads, P = d->headdim, N = d->dstate, G = d->ngroups;
+  const int64_t Hd = d->nheads, Pd = d->headdim, N = d->dstate, G = d->ngroups;
   const bool bf16 = d->io_dtype == SSD_BF16;
-  if (P % 16 != 0 || N % 16 != 0 || P > 256 || N > 256) return SSD_ERR_UNSUPPORTED;
+  if (Pd % 16 != 0 || N % 16 != 0 || Pd > 256 || N > 256) return SSD_ERR_UNSUPPORTED;
+  // bf16: a head dim of 64 hr runs as hr kernel heads of 64 state rows
+  const int64_t hr = bf16 && Pd % 64 == 0 ? Pd / 64 : 1;
+  const int64_t H = Hd * hr, P = Pd / hr;
   if (bf16 && (!ssd::chunk_state_bf16_supported((int)P, (int)N, chunk_len) ||
                !ssd::chunk_scan_bf16_supported((int)P, (int)N, chunk_len)))
     return SSD_ERR_UNSUPPORTED;
@@ -70,6 +73,7 @@ ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
   g.P = (int32_t)P;
   g.N = (int32_t)N;
   g.G = (int32_t)G;
+  g.hr = (int32_t)hr;
   g.packed = d->nseq > 0;
   g.table = nullptr;
   g.dir = nullptr;
@@ -132,7 +136,7 @@ Sizes tensor_bytes(const Plan &p) {
   Sizes s;
   s.x = (size_t)g.tokens * g.H * g.P * p.io_size;
   s.bc = (size_t)g.tokens * g.G * g.N * p.io_size;
-  s.dt = (size_t)g.tokens * g.H * sizeof(float);
+  s.dt = (size_t)g.tokens * (g.H / g.hr) * sizeof(float);
   s.state = (size_t)g.nrows * g.H * g.P * g.N * sizeof(float);
   return s;
 }
@@ -406,6 +410,12 @@ ssd_status make_fused_plan(const ssd_dims *dims, Plan *p) {
   return SSD_OK;
 }
 
+// The backward's shapes: head dim 64 (no head split), N in {64, 128}, an even
+// number of heads per group (its reverse sweep pairs the heads of a group).
+bool bwd_supported(const Plan &p) {
+  return p.geo.hr == 1 && (p.geo.N == 64 || p.geo.N == 128) && (p.geo.H / p.geo.G) % 2 == 0;
+}
+
 // 32-token chunks of the batch (packed: an upper bound, ceil(T/32) + nseq)
 int64_t chunks32(const Plan &p) {
   const ssd::Geometry &g = p.geo;
@@ -495,13 +505,13 @@ ssd_status ssd_fused_fwd_train(const void *x, const float *dt, const float *A, c
   const ssd::Geometry &g = p.geo;
   return hip_status(ssd::launch_fused(x, dt, A, B, C, D, init_state,
                                       g.packed ? cu_seqlens : nullptr, g.L, g.tokens, (int)g.nrows,
-                                      g.H, g.P, g.N, g.G, y, final_state, chunk_states,
+                                      g.H, g.P, g.N, g.G, g.hr, y, final_state, chunk_states,
                                       static_cast<hipStream_t>(stream)));
 }
 
 size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims) {
   Plan p;
-  if (make_fused_plan(dims, &p) != SSD_OK) return 0;
+  if (make_fused_plan(dims, &p) != SSD_OK || !bwd_supported(p)) return 0;
   return bwd_workspace(p).total;
 }
 
@@ -514,6 +524,7 @@ ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const v
   Plan p;
   ssd_status s = make_fused_plan(dims, &p);
   if (s != SSD_OK) return s;
+  if (!bwd_supported(p)) return SSD_ERR_UNSUPPORTED;
   if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
   if ((s = check_scan_args(x, B, C, D, dy, dt, p)) != SSD_OK) return s;
   if (!tok_ptr_ok(dx, p, 16) || !tok_ptr_ok(ddt, p, 4) || !tok_ptr_ok(dB, p, 16) ||

@@ -166,6 +166,15 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((n & 0xF) | ((n >> 4) << 14) | (0x7 << 4) | (0xF << 8));
 }
 
+// s_waitcnt lgkmcnt(0) leaving vmcnt and expcnt alone.  Written out before a
+// barrier that publishes LDS writes to the other wavefronts: at a loop's back
+// edge, where the barrier follows an explicit vmcnt wait, the compiler has
+// been seen to emit the barrier without waiting for an LDS write just
+// before it (gfx950, ROCm 7.2 hipcc).
+__device__ __forceinline__ void wait_lgkmcnt0() {
+  __builtin_amdgcn_s_waitcnt(0xF | (0x3 << 14) | (0x7 << 4) | (0x0 << 8));
+}
+
 // s_waitcnt vmcnt(n) for a run-time n (a switch over the immediates); counts
 // above 47 wait for everything.
 __device__ __forceinline__ void wait_vmcnt_dyn(int n) {

@@ -14,7 +14,12 @@ struct Geometry {
   int32_t Q;        // chunk length
   int64_t nc_max;   // chunks laid out in the workspace
   int64_t nrows;    // sequences: batch (fixed) or nseq (packed)
-  int32_t H, P, N, G;
+  int32_t H, P, N, G;   // kernel heads and head dim (see hr)
+  // Heads split: with bf16 io and a head dim of 64 hr, each head's P x N state
+  // runs as hr kernel heads of 64 rows (rows p of the state never interact, and
+  // x, y, the states and the workspace have the same memory layout either
+  // way); kernel head h takes dt, A and D of head h / hr.  1 otherwise.
+  int32_t hr;
   bool packed;
   const int32_t *table;  // packed: chunk table in the workspace
   const int32_t *dir;    // packed: chunk directory in the workspace
@@ -34,6 +39,7 @@ hipError_t launch_chunk_state_bf16(const void *x, const void *B, const float *ac
                                    const float *dtq, void *states, const Geometry &geo,
                                    hipStream_t stream);
 bool chunk_scan_bf16_supported(int P, int N, int Q);
+// D is indexed by kernel head / geo.hr
 hipError_t launch_chunk_scan_bf16(const void *x, const void *B, const void *C, const float *D,
                                   const float *acum, const float *dtq, const void *hprev, void *y,
                                   const Geometry &geo, hipStream_t stream);
@@ -59,12 +65,13 @@ hipError_t launch_conv1d_silu(const void *in, int64_t in_stride, const float *we
 hipError_t launch_gate_rmsnorm(const void *y, const void *z, const float *weight, float eps,
                                void *out, int64_t tokens, int width, bool bf16, hipStream_t stream);
 
-// the whole forward in one pass per (sequence, head)
+// the whole forward in one pass per (sequence, head); H kernel heads of P rows,
+// dt, A and D of kernel head h at h / hr
 bool fused_supported(int H, int P, int N, int G);
 hipError_t launch_fused(const void *x, const float *dt, const float *A, const void *B, const void *C,
                         const float *D, const float *h0, const int32_t *cu, int64_t L, int64_t T,
-                        int rows, int H, int P, int N, int G, void *y, float *hfin, void *hsave,
-                        hipStream_t stream);
+                        int rows, int H, int P, int N, int G, int hr, void *y, float *hfin,
+                        void *hsave, hipStream_t stream);
 // backward of the one-pass forward (bf16, P == 64, N in {64, 128}, even heads per group)
 // nseg > 0: the sweep split into that many 256-token segments (gseg, gin
 // [nseg][H][P][N] and aseg [nseg][H] fp32 scratch); 0: one pass per sequence

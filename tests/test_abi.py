@@ -309,11 +309,10 @@ def fused(d, **kw):
 
 @pytest.mark.parametrize("mut,expect", [
     (dict(io_dtype=SSD_F32), SSD_ERR_UNSUPPORTED),    # bf16 only
-    (dict(headdim=128), SSD_ERR_UNSUPPORTED),         # P == 64 only
-    (dict(dstate=32), SSD_ERR_UNSUPPORTED),
-    (dict(dstate=256), SSD_ERR_UNSUPPORTED),
-    (dict(ngroups=4), SSD_ERR_UNSUPPORTED),           # heads per group must be even
-    (dict(nheads=6, ngroups=2), SSD_ERR_UNSUPPORTED),
+    (dict(headdim=32), SSD_ERR_UNSUPPORTED),          # head dim a multiple of 64
+    (dict(headdim=96), SSD_ERR_UNSUPPORTED),
+    (dict(headdim=320), SSD_ERR_UNSUPPORTED),         # at most 256
+    (dict(dstate=32), SSD_ERR_UNSUPPORTED),           # N in {64, 128, 256}
     (dict(ngroups=3), SSD_ERR_UNSUPPORTED),           # 4 % 3 != 0
     (dict(reserved=1), SSD_ERR_INVALID_ARG),
     (dict(batch=-1), SSD_ERR_INVALID_ARG),
@@ -323,6 +322,38 @@ def test_fused_dims(mut, expect):
     for k, val in mut.items():
         setattr(d, k, val)
     assert fused(d) == expect
+    assert L.ssd_fused_states_size(ctypes.byref(d)) == 0
+
+
+@pytest.mark.parametrize("mut", [
+    dict(),
+    dict(headdim=128), dict(headdim=192), dict(headdim=256),   # heads split into 64-row halves
+    dict(dstate=128), dict(dstate=256),
+    dict(ngroups=4),                                          # one head per group
+    dict(nheads=6, ngroups=2),                                # three heads per group
+])
+def test_fused_supported_shapes(mut):
+    # host-only: a supported shape has a nonzero saved-state size (no launch here)
+    d = good()
+    for k, val in mut.items():
+        setattr(d, k, val)
+    n = L.ssd_fused_states_size(ctypes.byref(d))
+    pairs = d.batch * -(-d.seqlen // 64)
+    assert n == -(-(pairs * d.nheads * d.headdim * d.dstate * 2) // 256) * 256
+    # the chunked forward takes the same shapes
+    assert L.ssd_workspace_size(ctypes.byref(d), 256) > 0
+
+
+@pytest.mark.parametrize("mut,ok", [
+    (dict(), True), (dict(dstate=128), True),
+    (dict(dstate=256), False), (dict(headdim=128), False),
+    (dict(ngroups=4), False), (dict(nheads=6, ngroups=2), False),
+])
+def test_backward_shapes(mut, ok):
+    d = good()
+    for k, val in mut.items():
+        setattr(d, k, val)
+    assert (L.ssd_fused_bwd_workspace_size(ctypes.byref(d)) > 0) == ok
 
 
 def test_fused_pointers_and_overlaps():
@@ -356,12 +387,13 @@ def test_fused_states_size():
     assert L.ssd_fused_bwd_workspace_size(ctypes.byref(dp)) == ws
     big = make_dims(8, 4096, 80, 64, 128, 1, 0, SSD_BF16)  # 8 x 40 blocks: one pass per sequence
     assert L.ssd_fused_bwd_workspace_size(ctypes.byref(big)) == 8 * 64 * 80 * 64 * 128 * 2
-    for mut in (dict(io_dtype=SSD_F32), dict(headdim=128), dict(ngroups=4)):
+    for mut, fwd_ok in ((dict(io_dtype=SSD_F32), False), (dict(headdim=128), True),
+                        (dict(ngroups=4), True), (dict(dstate=256), True)):
         d = good()
         for k, val in mut.items():
             setattr(d, k, val)
-        assert L.ssd_fused_states_size(ctypes.byref(d)) == 0
-        assert L.ssd_fused_bwd_workspace_size(ctypes.byref(d)) == 0
+        assert (L.ssd_fused_states_size(ctypes.byref(d)) > 0) == fwd_ok
+        assert L.ssd_fused_bwd_workspace_size(ctypes.byref(d)) == 0  # outside the backward's shapes
 
 
 def fused_train(d, states=FAKE + (8 << 30), nbytes=None, **kw):

@@ -120,10 +120,12 @@ def test_long_memory(kind):
     full_case(w, 7, label=f"bwd {kind}")
 
 
-def test_saved_states_are_prefix_final_states():
+@pytest.mark.parametrize("P,N", [(64, 64), (128, 128), (64, 256)])
+def test_saved_states_are_prefix_final_states(P, N):
     # the state entering 64-token pair b of a row is the oracle's final state
-    # of the row's first 64 b tokens (from the same initial state)
-    w = workloads.make_custom(2, 200, 4, 64, 64, 2, 256, "bf16", seed=2800, init_std=0.3)
+    # of the row's first 64 b tokens (from the same initial state); the saving
+    # forward also serves head dims above 64 and N 256 (the backward does not)
+    w = workloads.make_custom(2, 200, 4, P, N, 2, 256, "bf16", seed=2800 + P + N, init_std=0.3)
     t = upload(w)
     st = ssd.make_fused_states(t["x"], t["B"], t["cu"])
     ssd.fused_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"],
@@ -203,6 +205,14 @@ def test_unsupported_and_invalid():
     t = upload(w)
     with pytest.raises(ssd.SSDUnsupported):
         ssd.make_fused_states(t["x"], t["B"])
+    # forward-only shapes: head dim 128, N 256, odd heads per group
+    for P, N, H, G in ((128, 64, 4, 1), (64, 256, 4, 1), (64, 64, 3, 1)):
+        w = workloads.make_custom(1, 64, H, P, N, G, 256, "bf16", seed=3002)
+        t = upload(w)
+        st = ssd.make_fused_states(t["x"], t["B"])
+        with pytest.raises(ssd.SSDUnsupported):
+            ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], st,
+                          torch.zeros_like(t["x"]))
     w = workloads.make_custom(1, 64, 4, 64, 64, 1, 256, "bf16", seed=3001)
     t = upload(w)
     st = ssd.make_fused_states(t["x"], t["B"])

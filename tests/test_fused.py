@@ -52,7 +52,7 @@ def test_varlen_whole():
     check_whole(w, y, fin, label="fused varlen_bf16", head_tokens=8, chunk=FUSED_CHUNK)
 
 
-@pytest.mark.parametrize("name", ["long_n64", "long_n128"])
+@pytest.mark.parametrize("name", ["long_n64", "long_n128", "long_n256"])
 def test_long_context_whole(name):
     # one 65,536-token sequence: the state is carried (with its running
     # power-of-two scale) across 2,048 chunks
@@ -67,6 +67,40 @@ def test_ragged_tail(N):
     w = workloads.make_custom(3, 1000, 4, 64, N, 2, 256, "bf16", seed=1100 + N, init_std=0.2)
     y, fin, _ = run_fused(w)
     check_full(w, y, fin, label=f"fused ragged N{N}")
+
+
+@pytest.mark.parametrize("P,N", [(64, 256), (128, 64), (128, 128), (128, 256), (256, 128)])
+def test_head_dims_and_state_sizes(P, N):
+    # head dim 64 r as r kernel heads of 64 rows; N 256 in four wavefronts of
+    # 16 state rows; ragged tail, two groups, nonzero initial state
+    w = workloads.make_custom(2, 1000, 4, P, N, 2, 256, "bf16", seed=1250 + P + N, init_std=0.2)
+    y, fin, _ = run_fused(w)
+    check_full(w, y, fin, label=f"fused P{P} N{N}")
+
+
+@pytest.mark.parametrize("H,G", [(6, 2), (5, 5), (3, 1)])
+def test_odd_heads_per_group(H, G):
+    # one head a block where the heads of a group do not pair up
+    w = workloads.make_custom(2, 500, H, 64, 128, G, 256, "bf16", seed=1260 + H, init_std=0.2)
+    y, fin, _ = run_fused(w)
+    check_full(w, y, fin, label=f"fused H{H} G{G}")
+
+
+@pytest.mark.parametrize("N", [64, 128])
+def test_head_pairs_path(N):
+    # enough (sequence, head pair) blocks to fill the GPU: the two-heads-a-block
+    # instance (the small problems above take the one-head instance)
+    w = workloads.make_custom(4, 300, 128, 64, N, 8, 256, "bf16", seed=1270 + N, init_std=0.2)
+    y, fin, _ = run_fused(w)
+    check_full(w, y, fin, label=f"fused head pairs N{N}")
+
+
+@pytest.mark.parametrize("kind", ["A_zero", "dt_small"])
+def test_long_memory_n256(kind):
+    kw = {"A_zero": dict(a_zero=True), "dt_small": dict(dt_const=1e-3)}[kind]
+    w = workloads.make_custom(2, 900, 4, 64, 256, 1, 256, "bf16", seed=1280, init_std=0.5, **kw)
+    y, fin, _ = run_fused(w)
+    check_full(w, y, fin, label=f"fused N256 {kind}")
 
 
 @pytest.mark.parametrize("G", [1, 4])
@@ -152,7 +186,7 @@ def test_agrees_with_chunked_forward():
 
 
 def test_unsupported_shapes_raise():
-    w = workloads.make_custom(1, 64, 4, 32, 64, 1, 256, "bf16", seed=1900)
+    w = workloads.make_custom(1, 64, 4, 32, 64, 1, 256, "bf16", seed=1900)  # head dim 32
     t = upload(w)
     with pytest.raises(ssd.SSDUnsupported):
         ssd.fused_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"])

@@ -94,6 +94,33 @@ def test_state_sizes(N):
     check_full(w, y, fin, label=f"N{N}")
 
 
+@pytest.mark.parametrize("chunk", [64, 128, 256])
+@pytest.mark.parametrize("P", [128, 256])
+def test_head_dims(P, chunk):
+    # a head dim of 64 r runs as r kernel heads of 64 state rows sharing the
+    # head's dt, A and D; ragged tail, two groups, nonzero initial state
+    w = workloads.make_custom(2, 700, 4, P, 128, 2, chunk, "bf16", seed=250 + P + chunk,
+                              init_std=0.2)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label=f"P{P} Q{chunk}")
+
+
+def test_block_example_shape():
+    # the gated Mamba-2 block of the architecture page's Step 2: model width
+    # 512, expansion 2, 8 heads -> head dim 128, state 128
+    w = workloads.make_custom(2, 1024, 8, 128, 128, 1, 256, "bf16", seed=260)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label="block example P128 N128")
+
+
+def test_head_dim_128_packed():
+    lens = [300, 0, 257, 1, 64, 900]
+    w = workloads.make_custom(1, 0, 4, 128, 64, 2, 128, "bf16", seed=270, lens=lens,
+                              init_std=0.3)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label="P128 packed")
+
+
 @pytest.mark.parametrize("G", [1, 2, 8])
 def test_groups(G):
     w = workloads.make_custom(2, 600, 8, 64, 64, G, 128, "bf16", seed=300 + G)
