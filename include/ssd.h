@@ -30,10 +30,11 @@
  *
  * Memory and ownership.  Every pointer argument except `dims` and the layout
  * struct is device memory owned by the caller.  The library allocates
- * nothing, keeps no mutable global state and never synchronises: every entry
- * point only enqueues kernels on `stream` (a hipStream_t; NULL = the default
- * stream) and returns.  Calls on different streams are independent provided
- * they use distinct workspaces.
+ * nothing and never synchronises: every entry point only enqueues kernels on
+ * `stream` (a hipStream_t; NULL = the default stream) and returns.  Calls on
+ * different streams are independent provided they use distinct workspaces.
+ * Its one piece of global state is the fixed scratch array that
+ * ssd_chunk_scan_fwd_noalloc uses as its workspace (see there).
  *
  * Alignment.  x, B, C, y, init_state, final_state: 16 bytes; dt, A, D: 4
  * bytes; workspace: 256 bytes.
@@ -143,6 +144,28 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, co
                               const float *init_state, const int32_t *cu_seqlens, void *y,
                               float *final_state, const ssd_dims *dims, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* ssd_chunk_scan_fwd without a workspace argument and without allocating, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc).  The workspace is a
+ * fixed array of SSD_NOALLOC_SCRATCH_BYTES in the global memory of every
+ * device the library runs on, reserved for the life of the process; the call
+ * uses the current device's (hipGetDevice), which must be the device of
+ * `stream`.  Problems whose ssd_workspace_size(dims, chunk_len) exceeds it
+ * return SSD_ERR_WORKSPACE (checked before any HIP call; e.g. B 4, L 2048,
+ * H 24, P 64, N 128 at chunk 256 needs about 26 MB).  Every call on one
+ * device shares that array: calls that overlap in time on one device (other
+ * streams, other threads) race and give wrong results.  The array keeps the
+ * last call's contents; nothing in it needs clearing, since every stage
+ * writes what a later one reads.  Otherwise identical to ssd_chunk_scan_fwd
+ * (arguments, layouts, aliasing, errors, results bit for bit).  The first
+ * call on a device looks the array's device address up (hipGetSymbolAddress)
+ * and keeps it; no call allocates.  Returns after enqueueing. */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                      const void *B, const void *C, const float *D, int chunk_len,
+                                      const float *init_state, const int32_t *cu_seqlens, void *y,
+                                      float *final_state, const ssd_dims *dims, void *stream);
 
 /* Stage 1 (chunk_cumsum): for packed batches first builds the chunk table and
  * directory from cu_seqlens; then writes acum and dtq.  The log-space

@@ -5,6 +5,8 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
+
 #include "ssd.h"
 #include "ssd_launch.hpp"
 
@@ -303,6 +305,61 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A, co
   if ((s = run_state(x, B, p, workspace, st)) != SSD_OK) return s;
   if ((s = run_pass(init_state, final_state, p, workspace, st)) != SSD_OK) return s;
   return run_scan(x, B, C, D, y, p, workspace, st);
+}
+
+}  // extern "C"
+
+// The allocation-free forward's workspace: one fixed array in every device's
+// global memory, held until the process ends.  In host code `scratch` only
+// names the symbol; its device address (a different one on each device) comes
+// from hipGetSymbolAddress and is the only form passed to kernels.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_scratch[kMaxDevices];
+
+// Device address of the current device's scratch array, looked up once per
+// device (with that device current) and kept.
+ssd_status current_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return SSD_ERR_HIP;
+  void *ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return SSD_ERR_HIP;
+    g_scratch[dev].store(ptr, std::memory_order_release);
+  }
+  *out = ptr;
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                      const void *B, const void *C, const float *D, int chunk_len,
+                                      const float *init_state, const int32_t *cu_seqlens, void *y,
+                                      float *final_state, const ssd_dims *dims, void *stream) {
+  Plan p;
+  ssd_status s = make_plan(dims, chunk_len, &p);
+  if (s != SSD_OK) return s;
+  if (p.ws.total_bytes > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+  if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
+  if ((s = check_state_args(x, B, p)) != SSD_OK) return s;
+  if ((s = check_pass_args(init_state, final_state, p)) != SSD_OK) return s;
+  if ((s = check_scan_args(x, B, C, D, y, dt, p)) != SSD_OK) return s;
+  void *ws = nullptr;
+  if ((s = current_scratch(&ws)) != SSD_OK) return s;
+  if ((s = bind_workspace(&p, ws, SSD_NOALLOC_SCRATCH_BYTES)) != SSD_OK) return s;
+  // Nothing in the workspace needs clearing: every stage writes what a later
+  // one reads (the chunk table included) before it is read.
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if ((s = run_cumsum(dt, A, cu_seqlens, p, ws, st)) != SSD_OK) return s;
+  if ((s = run_state(x, B, p, ws, st)) != SSD_OK) return s;
+  if ((s = run_pass(init_state, final_state, p, ws, st)) != SSD_OK) return s;
+  return run_scan(x, B, C, D, y, p, ws, st);
 }
 
 ssd_status ssd_step(const void *x, const float *dt, const float *A, const void *B, const void *C,

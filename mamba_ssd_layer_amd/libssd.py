@@ -57,7 +57,12 @@ class ssd_workspace_layout(ctypes.Structure):
                 ("chunk_table_offset", ctypes.c_size_t), ("chunk_dir_offset", ctypes.c_size_t)]
 
 
+# SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h: the largest workspace of
+# ssd_chunk_scan_fwd_noalloc
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
 EXPORTS = ["ssd_workspace_size", "ssd_get_workspace_layout", "ssd_chunk_scan_fwd",
+           "ssd_chunk_scan_fwd_noalloc",
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
            "ssd_step", "ssd_conv1d_silu", "ssd_gate_rmsnorm", "ssd_fused_fwd",
            "ssd_fused_fwd_train", "ssd_fused_states_size", "ssd_fused_bwd_workspace_size",
@@ -78,6 +83,8 @@ def _load() -> ctypes.CDLL:
     lib.ssd_get_workspace_layout.argtypes = [dims_p, i32, ctypes.POINTER(ssd_workspace_layout)]
     lib.ssd_chunk_scan_fwd.restype = i32
     lib.ssd_chunk_scan_fwd.argtypes = [p, p, p, p, p, p, i32, p, p, p, p, dims_p, p, sz, p]
+    lib.ssd_chunk_scan_fwd_noalloc.restype = i32
+    lib.ssd_chunk_scan_fwd_noalloc.argtypes = [p, p, p, p, p, p, i32, p, p, p, p, dims_p, p]
     lib.ssd_chunk_cumsum.restype = i32
     lib.ssd_chunk_cumsum.argtypes = [p, p, i32, p, dims_p, p, sz, p]
     lib.ssd_chunk_state.restype = i32
@@ -250,6 +257,16 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D, chunk_len, init_state, cu_seqlens, y, 
     px, pdt, pA, pB, pC, pD, py, phi, pcu, phf, pws = _ptrs(*ts, hi, cu, hf, workspace)
     _check(_lib.ssd_chunk_scan_fwd(px, pdt, pA, pB, pC, pD, int(chunk_len), phi, pcu, py, phf,
                                    ctypes.byref(dims), pws, _bytes(workspace), _stream(stream)))
+
+
+def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D, chunk_len, init_state, cu_seqlens, y,
+                               final_state, dims, stream=None) -> None:
+    ts = _fwd(dims, x, dt, A, B, C, D, y, need=ALL)
+    hi, cu, hf = _state(init_state, dims, "init_state"), _cu(cu_seqlens, dims), \
+        _state(final_state, dims, "final_state")
+    px, pdt, pA, pB, pC, pD, py, phi, pcu, phf = _ptrs(*ts, hi, cu, hf)
+    _check(_lib.ssd_chunk_scan_fwd_noalloc(px, pdt, pA, pB, pC, pD, int(chunk_len), phi, pcu, py,
+                                           phf, ctypes.byref(dims), _stream(stream)))
 
 
 def ssd_chunk_cumsum(dt, A, chunk_len, cu_seqlens, dims, workspace, stream=None) -> None:

@@ -458,3 +458,35 @@ def test_fused_bwd_validation():
     assert fused_bwd(dp) == SSD_ERR_INVALID_ARG                              # packed needs cu
     d.io_dtype = SSD_F32
     assert fused_bwd(d) == SSD_ERR_UNSUPPORTED
+
+
+# ---------------------------------------------------------------- ssd_chunk_scan_fwd_noalloc
+def test_noalloc_scratch_size_matches_the_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define SSD_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == libssd.NOALLOC_SCRATCH_BYTES
+
+
+def noalloc(d, Q=256, **kw):
+    v = ctypes.c_void_p
+    args = dict(x=FAKE, dt=FAKE + (1 << 30), A=FAKE + (2 << 30), B=FAKE + (3 << 30),
+                C=FAKE + (4 << 30), D=None, init=None, cu=None, y=FAKE + (7 << 30), fin=None)
+    args.update(kw)
+    a = [None if args[k] is None else v(args[k]) for k in ("x", "dt", "A", "B", "C", "D")]
+    b = [None if args[k] is None else v(args[k]) for k in ("init", "cu", "y", "fin")]
+    return L.ssd_chunk_scan_fwd_noalloc(*a, Q, *b, ctypes.byref(d), None)
+
+
+def test_noalloc_validates_before_any_hip_call():
+    # beyond the scratch array: refused (the large layer's ~350 MB workspace)
+    big = make_dims(8, 4096, 80, 64, 128, 1, 0, SSD_BF16)
+    assert L.ssd_workspace_size(ctypes.byref(big), 256) > libssd.NOALLOC_SCRATCH_BYTES
+    assert noalloc(big) == SSD_ERR_WORKSPACE
+    # the same argument checks as the workspace forward
+    d = good()
+    assert noalloc(d, x=None) == SSD_ERR_INVALID_ARG
+    assert noalloc(d, y=FAKE) == SSD_ERR_INVALID_ARG               # y == x
+    assert noalloc(d, Q=100) == SSD_ERR_UNSUPPORTED
+    d.ngroups = 3
+    assert noalloc(d) == SSD_ERR_UNSUPPORTED
+
