@@ -365,7 +365,7 @@ def main() -> int:
                     help="skip the forward-with-saved-states + backward timing")
     ap.add_argument("--no-block", action="store_true",
                     help="skip the conv1d+SiLU and gate+RMS-norm measurements")
-    ap.add_argument("--settle-ms", type=float, default=300.0,
+    ap.add_argument("--settle-ms", type=float, default=2500.0,
                     help="untimed forward steps for this long before the first timed region, so "
                          "every path is timed at the GPU's sustained clock")
     ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
@@ -429,29 +429,41 @@ def main() -> int:
     def step():
         plan(x, dt, A, Bm, Cm, D, h0, cu, y=y, final_state=fin)
 
-    # clock settling before anything is timed: the GPU starts from idle clocks,
-    # so the first timed path would otherwise run partly below its sustained
-    # clock (untimed; the timed regions below are exactly `steps` steps each)
+    # between timed steps, a buffer four times the 256 MB MALL is written and
+    # then read, so no step starts with its inputs or intermediates in the
+    # memory-side cache; the read leaves the MALL holding clean lines (after
+    # the write alone it holds 256 MB of dirty ones, which the next timed
+    # kernel would pay to write back: chunk_state 111 -> 170 us at the large
+    # layer)
+    flush_buf = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
+    flush_sum = torch.empty((), dtype=torch.float32, device=dev)
+
+    def flush(i: int = 0) -> None:
+        flush_buf.fill_(float(i))
+        torch.sum(flush_buf, dim=0, out=flush_sum)
+
+    # clock settling before anything is timed: the GPU starts from idle clocks
+    # and takes over a second of sustained work to reach its steady clock, so
+    # the first timed path would otherwise run partly below it (untimed; the
+    # timed regions below are exactly `steps` steps each)
     t_settle = time.perf_counter()
     while time.perf_counter() - t_settle < args.settle_ms * 1e-3:
+        flush()
         step()
         torch.cuda.synchronize()
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    # a write larger than the 256 MB MALL between timed steps, so no step
-    # starts with its inputs or intermediates in the memory-side cache
-    flush = torch.empty(FLUSH_BYTES // 4, dtype=torch.float32, device=dev)
 
     def timed_steps(fn):
         """Per-launch durations (us) of `steps` launches of fn, each bracketed
-        by HIP events on the launch stream with a MALL-flushing write before
-        it; plus the wall time of the whole region."""
+        by HIP events on the launch stream with a MALL flush before it; plus
+        the wall time of the whole region."""
         evs = []
         torch.cuda.synchronize()
         w0 = time.perf_counter()
         for i in range(args.steps):
-            flush.fill_(float(i))
+            flush(i)
             e0 = torch.cuda.Event(enable_timing=True)
             e1 = torch.cuda.Event(enable_timing=True)
             e0.record(stream)
@@ -511,7 +523,7 @@ def main() -> int:
             f"{T / ft / 1e6:.1f} M tokens/s")
 
     # per-stage times: the same stages launched one by one, each after a
-    # MALL-flushing write, HIP events around each launch (median over steps)
+    # MALL flush, HIP events around each launch (median over steps)
     stage_us, stage_mean_us = {}, {}
     if not args.no_stage_timing:
         calls = {
@@ -523,7 +535,7 @@ def main() -> int:
         evs = {s_: [] for s_ in STAGES}
         for i in range(args.steps):
             for s_ in STAGES:
-                flush.fill_(float(i))
+                flush(i)
                 e0 = torch.cuda.Event(enable_timing=True)
                 e1 = torch.cuda.Event(enable_timing=True)
                 e0.record(stream)
@@ -535,7 +547,7 @@ def main() -> int:
             d_ = [a_.elapsed_time(b_) * 1e3 for a_, b_ in evs[s_]]
             stage_us[s_] = float(np.median(d_))
             stage_mean_us[s_] = float(np.mean(d_))
-    del flush
+    del flush_buf
     copy_gbs = copy_bandwidth(torch, dev)
     log(f"bench: plain copy {copy_gbs:.0f} GB/s")
 
@@ -616,9 +628,9 @@ def main() -> int:
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic",
         "timing": (f"value: the median of {args.steps} launches, each after a "
-                   f"{FLUSH_BYTES >> 20} MiB write that flushes the 256 MB MALL, HIP events on the "
-                   "launch stream; roofline.achieved: algorithmic bytes / the mean of the same "
-                   "launches"),
+                   f"{FLUSH_BYTES >> 20} MiB write and read that flush the 256 MB MALL, HIP events "
+                   "on the launch stream; roofline.achieved: algorithmic bytes / the mean of the "
+                   "same launches"),
         "config": {**workloads.describe(w), "path": path,
                    "chunk": FUSED_CHUNK if path == "ssd_fused_fwd" else w.chunk,
                    "parallelism": "none (1 GPU)"},

@@ -36,9 +36,11 @@
 //      then scaled by exp(a_l);
 //   2. intra term: Z^T = B C^T for the three nonzero 16 x 16 tiles of the
 //      causal 32 x 32 block (same K order), the decay exp(a_l - a_s) dt_s
-//      applied per element in the log2 domain and the tile above the diagonal
-//      masked, then Y^T += X^T G^T with the accumulators as B-operands and
-//      X^T from transposing LDS reads in the matching token order; plus D x;
+//      applied per element as exp(a_l) times a per-token table of
+//      dt_s exp(-a_s) (per element in the log2 domain for a chunk that decays
+//      below 2^-40) and the tile above the diagonal masked, then Y^T += X^T G^T
+//      with the accumulators as B-operands and X^T from transposing LDS reads
+//      in the matching token order; plus D x in fp32;
 //   3. state: h^T = exp(a_last) h^T + B^T (w x) with w_s = exp(a_last - a_s)
 //      dt_s, from transposing reads of B and the same X^T registers.
 #include "ssd_device.hpp"
@@ -108,8 +110,8 @@ struct FusedCfg {
   static constexpr int DW = 64 * 4;              // the chunk's dt piece (wavefront 0 loads it)
   static constexpr int OX = 0, OB = HPB * XH, OC = OB + BT, OD = OC + BT;
   static constexpr int SLOT = OD + DW;
-  static constexpr int AD = R * SLOT;            // per wavefront: [al2 | bs2 | w], 32 floats each
-  static constexpr int ADW = 3 * CQ * 4;
+  static constexpr int AD = R * SLOT;            // per wavefront: [al2 | bs2 | w | vs], 32 floats each
+  static constexpr int ADW = 4 * CQ * 4;
   static constexpr int TOTAL = AD + WAVES * ADW;
   static constexpr int BCI = 2 * BT / 1024 / WAVES;  // 1 KB pieces of B and C per wavefront
   static constexpr int LDC = XI + BCI;           // vector-memory ops a wavefront issues per chunk
@@ -213,11 +215,19 @@ void k_ssd_fused(
     dtoff = static_cast<uint32_t>((min(e / HPB, last) * Hd + (h0b + e % HPB) / hr) * 4);
   };
   lane_offsets(CQ - 1);
+  const uint32_t smem0 = __builtin_amdgcn_readfirstlane(lds_off(smem));
+  // y row pieces this wavefront stores: byte offsets from a chunk's first row
+  uint32_t yoff[XI];
+#pragma unroll
+  for (int i = 0; i < XI; ++i) {
+    const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = m & 7;
+    yoff[i] = static_cast<uint32_t>((r * ldx + (int64_t)h * P + 8 * cc) * 2);
+  }
   auto issue = [&](int k, int sl) {
     const int64_t t0 = tb + (int64_t)k * CQ;
     const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
     if (last < CQ - 1) lane_offsets(last);
-    const uint32_t base = lds_off(smem) + sl * SLOT;
+    const uint32_t base = smem0 + sl * SLOT;
 #pragma unroll
     for (int i = 0; i < XI; ++i) dma_lds16_sb(xoff[i], x + t0 * ldx, base + OX + hh * XH + XR * pq * 128 + i * 1024);
 #pragma unroll
@@ -238,10 +248,11 @@ void k_ssd_fused(
       const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = m & 7;
       v[i] = *reinterpret_cast<const u32x4 *>(ys + r * 128 + ((cc ^ rot_swz<8>(r)) << 4));
     }
+    unsigned char *yb = reinterpret_cast<unsigned char *>(y + t0 * ldx);  // wave-uniform
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
-      const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = m & 7;
-      if (r < rem) *reinterpret_cast<u32x4 *>(y + (t0 + r) * ldx + (int64_t)h * P + 8 * cc) = v[i];
+      const int r = XR * pq + ((i * 64 + lane) >> 3);
+      if (r < rem) *reinterpret_cast<u32x4 *>(yb + yoff[i]) = v[i];
     }
   };
   // row operand of a B or C tile in the state's K order: K step q gives lane
@@ -325,6 +336,8 @@ void k_ssd_fused(
       adw[tl] = al;                              // log2 exp(a_l)
       adw[CQ + tl] = bs;                         // log2(dt_s exp(-a_s))
       adw[2 * CQ + tl] = exp2_fast(bs + wshift);  // the state update's token weight
+      // dt_s exp(-a_s) itself, at most dt_s 2^40 where the chunk is not steep
+      adw[3 * CQ + tl] = exp2_fast(fminf(bs, 126.f));
     }
     wave_sync();
 
@@ -351,14 +364,18 @@ void k_ssd_fused(
       }
     }
     const float al0 = adw[c16], al1 = adw[16 + c16];
-    const float f0 = exp2_fast(al0 + lam), f1 = exp2_fast(al1 + lam);
+    // exp(a_l) for the lane's tokens l = c16, 16 + c16
+    const float u0 = exp2_fast(al0), u1 = exp2_fast(al1);
+    const float el = exp2_fast(lam);
+    const float f0 = u0 * el, f1 = u1 * el;
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
       ya[pt][0] *= f0;
       ya[pt][1] *= f1;
     }
 
-    // 2. intra term: Z^T tiles (s-block, l-block) = (0,0), (1,1), (0,1)
+    // 2. intra term: Z^T tiles (s-block, l-block) = (0,0), (1,1), (0,1);
+    // G^T = Z^T exp(a_l - a_s) dt_s on s <= l
     u32x4 gop[2];
     {
       f32x4 z00{}, z11{}, z01{};
@@ -370,17 +387,31 @@ void k_ssd_fused(
         z11 = mfma16(b1, cop[1][q], z11);
       }
       // lane holds s = 16 sb + 4 g4 + r, l = 16 lb + c16
-      const f32x4 bs0 = *reinterpret_cast<const f32x4 *>(adw + CQ + 4 * g4);
-      const f32x4 bs1 = *reinterpret_cast<const f32x4 *>(adw + CQ + 16 + 4 * g4);
       float g00[4], g11[4], g01[4];
+      if (!steep) {
+        // exp(a_l - a_s) dt_s = exp(a_l) (dt_s exp(-a_s)): both factors finite
+        // when the chunk decays by less than 2^-40 (the masked s > l side too)
+        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(adw + 3 * CQ + 4 * g4);
+        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(adw + 3 * CQ + 16 + 4 * g4);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const float keep = 4 * g4 + r <= c16 ? 1.f : 0.f;
-        // for s > l the exponent may be large; min() keeps it finite so the
-        // 0 mask wins
-        g00[r] = z00[r] * (exp2_fast(fminf(al0 + bs0[r], 64.f)) * keep);
-        g11[r] = z11[r] * (exp2_fast(fminf(al1 + bs1[r], 64.f)) * keep);
-        g01[r] = z01[r] * exp2_fast(al1 + bs0[r]);
+        for (int r = 0; r < 4; ++r) {
+          const float keep = 4 * g4 + r <= c16 ? 1.f : 0.f;
+          g00[r] = z00[r] * (u0 * v0[r] * keep);
+          g11[r] = z11[r] * (u1 * v1[r] * keep);
+          g01[r] = z01[r] * (u1 * v0[r]);
+        }
+      } else {
+        const f32x4 bs0 = *reinterpret_cast<const f32x4 *>(adw + CQ + 4 * g4);
+        const f32x4 bs1 = *reinterpret_cast<const f32x4 *>(adw + CQ + 16 + 4 * g4);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const float keep = 4 * g4 + r <= c16 ? 1.f : 0.f;
+          // for s > l the exponent may be large; min() keeps it finite so the
+          // 0 mask wins
+          g00[r] = z00[r] * (exp2_fast(fminf(al0 + bs0[r], 64.f)) * keep);
+          g11[r] = z11[r] * (exp2_fast(fminf(al1 + bs1[r], 64.f)) * keep);
+          g01[r] = z01[r] * exp2_fast(al1 + bs0[r]);
+        }
       }
       gop[0] = u32x4{pack_bf16x2(g00[0], g00[1]), pack_bf16x2(g00[2], g00[3]), 0u, 0u};
       gop[1] = u32x4{pack_bf16x2(g01[0], g01[1]), pack_bf16x2(g01[2], g01[3]),
@@ -397,7 +428,7 @@ void k_ssd_fused(
       for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(xop[pt], gop[lt], ya[pt][lt]);
     }
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {  // D x: rows p = 16 pt + 4 g4 + r of token l
+    for (int pt = 0; pt < PT; ++pt) {  // D x in fp32: rows p = 16 pt + 4 g4 + r of token l
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) {
         const int l = 16 * lt + c16, col = p0 + 16 * pt + 4 * g4;
