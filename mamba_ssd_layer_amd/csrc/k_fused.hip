@@ -107,15 +107,18 @@ struct FusedCfg {
   static constexpr int XI = XR * P * 2 / 1024;   // ... in 1 KB direct-to-LDS loads / row stores
   static constexpr int XH = CQ * P * 2;          // x of one head and chunk: 32 rows x 128 B
   static constexpr int BT = CQ * N * 2;          // B (or C) of a chunk
-  static constexpr int DW = 64 * 4;              // the chunk's dt piece (wavefront 0 loads it)
+  static constexpr int DTP = (CQ * HPB + 63) / 64;  // 64-entry dt pieces of a chunk
+  static constexpr int DW = 64 * 4;              // one dt piece (wavefront i < DTP loads piece i)
   static constexpr int OX = 0, OB = HPB * XH, OC = OB + BT, OD = OC + BT;
-  static constexpr int SLOT = OD + DW;
+  static constexpr int SLOT = OD + DTP * DW;
   static constexpr int AD = R * SLOT;            // per wavefront: [al2 | bs2 | w | vs], 32 floats each
   static constexpr int ADW = 4 * CQ * 4;
   static constexpr int TOTAL = AD + WAVES * ADW;
-  static constexpr int BCI = 2 * BT / 1024 / WAVES;  // 1 KB pieces of B and C per wavefront
+  static constexpr int NPC = 2 * BT / 1024;     // 1 KB pieces of B and C
+  static constexpr int BCI = (NPC + WAVES - 1) / WAVES;  // ... at most per wavefront (piece
+                                                 // u goes to wavefront u % WAVES)
   static constexpr int LDC = XI + BCI;           // vector-memory ops a wavefront issues per chunk
-                                                 // load (+1 for wavefront 0's dt piece)
+                                                 // load, at most (+1 with a dt piece)
   static constexpr int STC = XI;                 // ... per chunk of y it stores
   static constexpr int BLOCKS_PER_CU = (160 * 1024) / TOTAL;
   // waves a SIMD must hold for BLOCKS_PER_CU blocks (at most 3: the kernel
@@ -124,8 +127,8 @@ struct FusedCfg {
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_LDS < 3 ? WAVES_PER_SIMD_LDS : 3;
   static_assert(PW == 16 || PW == 32, "state rows per wavefront");
   static_assert(XI >= 1 && XI * 1024 == XR * P * 2, "x rows in 1 KB pieces");
-  static_assert(BCI >= 1 && BCI * WAVES * 1024 == 2 * BT, "B and C split evenly over the wavefronts");
-  static_assert(CQ * HPB <= 64, "one dt piece a chunk");
+  static_assert(BCI >= 1 && NPC * 1024 == 2 * BT, "B and C in 1 KB pieces");
+  static_assert(DTP <= WAVES, "a wavefront per dt piece");
   static constexpr int SVC = PT * N / 32;        // ... per saved chunk-start state
   static_assert(R >= 2 && (R - 2) * (LDC + 1 + STC + SVC) <= 47, "wait counts");
   static_assert(BLOCKS_PER_CU >= 1 && WAVES_PER_SIMD >= 1, "occupancy");
@@ -146,7 +149,7 @@ void k_ssd_fused(
   constexpr int KQ = N / 32;   // K steps over n
   constexpr int NCB = N / 8;   // 16-byte chunks per B / C row
   constexpr int XH = F::XH, BT = F::BT, DW = F::DW, OX = F::OX, OB = F::OB, OC = F::OC, OD = F::OD;
-  constexpr int SLOT = F::SLOT, AD = F::AD, ADW = F::ADW, BCI = F::BCI, LDC = F::LDC, STC = F::STC,
+  constexpr int SLOT = F::SLOT, AD = F::AD, ADW = F::ADW, BCI = F::BCI, STC = F::STC, WAVES = F::WAVES,
                 SVC = F::SVC;
   __shared__ __align__(16) unsigned char smem[F::TOTAL];
 
@@ -205,13 +208,13 @@ void k_ssd_fused(
     }
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {  // B and C pieces
-      const int u = wave * BCI + i, pi = u % (BT / 1024);
+      const int u = wave + i * WAVES, pi = u % (BT / 1024);
       const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ rot_swz<NCB>(r);
       bcoff[i] = static_cast<uint32_t>((min(r, last) * ldb + (int64_t)g * N + 8 * cc) * 2);
     }
-    // dt of the block's heads: entry e = token * HPB + head, one 64-entry
-    // piece (past the last entry every lane reads that one)
-    const int e = min(lane, CQ * HPB - 1);
+    // dt of the block's heads: entry e = token * HPB + head, 64-entry pieces
+    // (past the last entry every lane reads that one)
+    const int e = min(wave * 64 + lane, CQ * HPB - 1);
     dtoff = static_cast<uint32_t>((min(e / HPB, last) * Hd + (h0b + e % HPB) / hr) * 4);
   };
   lane_offsets(CQ - 1);
@@ -232,10 +235,11 @@ void k_ssd_fused(
     for (int i = 0; i < XI; ++i) dma_lds16_sb(xoff[i], x + t0 * ldx, base + OX + hh * XH + XR * pq * 128 + i * 1024);
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {
-      const int u = wave * BCI + i, tile = u / (BT / 1024), pi = u % (BT / 1024);
+      const int u = wave + i * WAVES, tile = u / (BT / 1024), pi = u % (BT / 1024);
+      if (F::NPC % WAVES != 0 && u >= F::NPC) break;  // wave-uniform
       dma_lds16_sb(bcoff[i], (tile ? Cm : Bm) + t0 * ldb, base + (tile ? OC : OB) + pi * 1024);
     }
-    if (wave == 0) dma_lds4_sb(dtoff, dt + t0 * Hd, base + OD);
+    if (wave < F::DTP) dma_lds4_sb(dtoff, dt + t0 * Hd, base + OD + wave * DW);
   };
   // rows XR pq .. XR pq + XR - 1 of head hh's y of chunk k (staged in slot sl): STC stores
   auto store_y = [&](int k, int sl) {
@@ -277,7 +281,9 @@ void k_ssd_fused(
   };
 
   constexpr int D = R - 1;  // chunks in flight ahead of the one being computed
-  const int ldc = LDC + (wave == 0 ? 1 : 0);  // wavefront 0 also loads the dt piece
+  // vector-memory ops this wavefront issues per chunk load: x rows, its B/C
+  // pieces, and dt piece `wave` for wavefronts below DTP
+  const int ldc = XI + (F::NPC - wave + WAVES - 1) / WAVES + (wave < F::DTP ? 1 : 0);
 #pragma unroll
   for (int c = 0; c < D; ++c)
     if (c < nck) issue(c, c);
@@ -533,14 +539,15 @@ void launch_fused_t(const uint16_t *x, const float *dt, const float *A, const ui
 // N = 256 takes one head a block in four wavefronts of 16 rows (the state of
 // a wavefront stays at 64 registers).
 template <int N, bool SAVE>
-void launch_fused_n(bool pairs, const uint16_t *x, const float *dt, const float *A,
+void launch_fused_n(int hpb, const uint16_t *x, const float *dt, const float *A,
                     const uint16_t *B, const uint16_t *C, const float *D, const float *h0,
                     const int32_t *cu, int64_t L, int64_t T, int rows, int H, int G, int hr,
                     uint16_t *y, float *hfin, uint16_t *hsave, hipStream_t stream) {
   if constexpr (N == 256) {
     launch_fused_t<N, 1, 16, 2, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
   } else {
-    if (pairs) launch_fused_t<N, 2, 32, 3, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
+    if (hpb == 3) launch_fused_t<N, 3, 32, 3, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
+    else if (hpb == 2) launch_fused_t<N, 2, 32, 3, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
     else launch_fused_t<N, 1, 32, 2, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
   }
 }
@@ -557,10 +564,13 @@ hipError_t launch_fused(const void *x, const float *dt, const float *A, const vo
   const uint16_t *ci = static_cast<const uint16_t *>(C);
   uint16_t *yo = static_cast<uint16_t *>(y);
   uint16_t *hs = static_cast<uint16_t *>(hsave);
-  const bool pairs = (H / G) % 2 == 0 && (int64_t)rows * (H / 2) >= device_cus();
+  const int cus = device_cus();
+  const int HG = H / G;
+  const int hpb = HG % 3 == 0 && (int64_t)rows * (H / 3) >= cus ? 3
+                  : HG % 2 == 0 && (int64_t)rows * (H / 2) >= cus ? 2 : 1;
 #define SSD_FUSED_N(NN)                                                                           \
-  if (hs) launch_fused_n<NN, true>(pairs, xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, hr, yo, hfin, hs, stream); \
-  else launch_fused_n<NN, false>(pairs, xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, hr, yo, hfin, hs, stream);
+  if (hs) launch_fused_n<NN, true>(hpb, xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, hr, yo, hfin, hs, stream); \
+  else launch_fused_n<NN, false>(hpb, xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, hr, yo, hfin, hs, stream);
   switch (N) {
     case 64: SSD_FUSED_N(64) break;
     case 128: SSD_FUSED_N(128) break;

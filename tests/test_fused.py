@@ -95,6 +95,15 @@ def test_head_pairs_path(N):
     check_full(w, y, fin, label=f"fused head pairs N{N}")
 
 
+@pytest.mark.parametrize("N", [64, 128])
+def test_head_triples_path(N):
+    # three heads a block (one block a CU): 4 rows x 192 heads (G 2, 96 heads a
+    # group) make 256 head-triple blocks
+    w = workloads.make_custom(4, 300, 192, 64, N, 2, 256, "bf16", seed=1275 + N, init_std=0.2)
+    y, fin, _ = run_fused(w)
+    check_full(w, y, fin, label=f"fused head triples N{N}")
+
+
 @pytest.mark.parametrize("kind", ["A_zero", "dt_small"])
 def test_long_memory_n256(kind):
     kw = {"A_zero": dict(a_zero=True), "dt_small": dict(dt_const=1e-3)}[kind]
