@@ -78,23 +78,28 @@ typedef struct {
   int64_t nheads;   /* H */
   int64_t headdim;  /* P */
   int64_t dstate;   /* N */
-  int64_t ngroups;  /* G, must divide H */
+  int64_t ngroups;  /* G; H not a multiple of G returns SSD_ERR_UNSUPPORTED */
   int64_t nseq;     /* 0: fixed-length batch; > 0: packed sequences given by cu_seqlens */
   int32_t io_dtype; /* an ssd_dtype */
   int32_t reserved; /* must be 0 */
 } ssd_dims;
 
 /* Supported shapes.
- *   chunk_len Q in {64, 128, 256}.
- *   SSD_BF16: headdim P == 64, dstate N in {64, 128, 256}; all contractions on
- *             bf16 MFMA with fp32 accumulation; y rounded to nearest-even.
+ *   chunk_len Q in {64, 128, 256}; nheads a multiple of ngroups.
+ *   SSD_BF16: headdim P in {64, 128, 192, 256}, dstate N in {64, 128, 256};
+ *             all contractions on bf16 MFMA with fp32 accumulation; y rounded
+ *             to nearest-even.  A head of P = 64 r runs as r kernel heads of
+ *             64 state rows (rows p of the state never interact), which share
+ *             the head's dt, A and D.
  *   SSD_F32:  headdim and dstate multiples of 16, at most 256; fp32 throughout.
  *   T, nseq and every sequence length below 2^31.
  * Anything else valid returns SSD_ERR_UNSUPPORTED. */
 
 /* Byte offsets of the workspace buffers (all 256-byte aligned).  The
  * per-stage entry points below read and write these; tests read them to check
- * each stage.  nc_max chunks are laid out, numbered sequence-major:
+ * each stage.  H and P below are the kernel heads and rows: with bf16 and a
+ * head dim of 64 r, H = r nheads and P = 64 (the same bytes as [nheads][64 r]).
+ * nc_max chunks are laid out, numbered sequence-major:
  *   fixed length: nc_max = batch * ceil(seqlen / Q), chunk c = b * ceil(L/Q) + k
  *   packed:       nc_max = ceil(T / Q) + nseq (upper bound; the exact count is
  *                 written to the chunk directory), chunks restart at each
@@ -264,8 +269,10 @@ ssd_status ssd_gate_rmsnorm(const void *y, const void *z, const float *weight, f
  * no chunk_len: it walks chunks of 32 tokens, and chunking is exact).  The
  * arguments, layouts, aliasing rules and results are those of
  * ssd_chunk_scan_fwd, to rounding.
- * Supported: SSD_BF16, headdim P == 64, dstate N in {64, 128}, an even
- * number of heads per group (nheads / ngroups); else SSD_ERR_UNSUPPORTED.  It keeps one block per (sequence, head) busy for the
+ * Supported: SSD_BF16, headdim P in {64, 128, 192, 256} (a head of 64 r
+ * rows runs as r kernel heads sharing dt, A, D), dstate N in {64, 128, 256},
+ * nheads a multiple of ngroups; else SSD_ERR_UNSUPPORTED.  It keeps one block
+ * per (sequence, kernel head), or per 2 or 3 heads of a group, busy for the
  * sequence's whole length, so it pays off when sequences x heads fills the
  * GPU (hundreds or more); a single long sequence is better served by the
  * chunk-parallel ssd_chunk_scan_fwd.  Returns after enqueueing. */
@@ -330,8 +337,10 @@ size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
  *   dD   float [H], NULL exactly when D is NULL
  *   dinit float [rows, H, P, N] (the gradient w.r.t. init_state) or NULL.
  * workspace: device memory of at least ssd_fused_bwd_workspace_size(dims)
- * bytes, 16-byte aligned, else SSD_ERR_WORKSPACE.  Supported shapes are
- * ssd_fused_fwd's.  On `stream`: dA and dD cleared; the reverse sweep of the
+ * bytes, 16-byte aligned, else SSD_ERR_WORKSPACE.  Supported: SSD_BF16,
+ * headdim 64, dstate N in {64, 128}, an even number of heads per group; else
+ * SSD_ERR_UNSUPPORTED (and ssd_fused_bwd_workspace_size returns 0).  On
+ * `stream`: dA and dD cleared; the reverse sweep of the
  * state gradient (one pass per (sequence, two heads), or, with fewer such
  * pairs than 256, per 256-token segment: segment sums, a chained pass, the
  * segments again); the per-chunk gradients, which add into dA and dD with

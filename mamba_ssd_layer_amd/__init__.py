@@ -139,9 +139,12 @@ class SSDForward:
 
     def view(self, name: str) -> torch.Tensor:
         """A typed view of one workspace buffer (acum, dtq, states, hprev,
-        chunk_table, chunk_dir) in its documented shape."""
+        chunk_table, chunk_dir) in its documented shape.  acum and dtq hold
+        one row per kernel head: with bf16 and a head dim of 64 r, head h
+        runs as the r kernel heads h r .. h r + r - 1 (the same values)."""
         d, L, Q = self.dims, self.layout, self.chunk_len
         nc, H, P, N = L.nc_max, d.nheads, d.headdim, d.dstate
+        Hk = H * (P // 64) if d.io_dtype == SSD_BF16 else H  # kernel heads
         ws = self.workspace
         io = torch.bfloat16 if d.io_dtype == SSD_BF16 else torch.float32  # states and hprev
 
@@ -150,9 +153,9 @@ class SSDForward:
             return ws[off:off + nbytes].view(dtype)
 
         if name == "acum":
-            return sl(L.acum_offset, nc * H * Q, torch.float32).view(nc, H, Q)
+            return sl(L.acum_offset, nc * Hk * Q, torch.float32).view(nc, Hk, Q)
         if name == "dtq":
-            return sl(L.dtq_offset, nc * H * Q, torch.float32).view(nc, H, Q)
+            return sl(L.dtq_offset, nc * Hk * Q, torch.float32).view(nc, Hk, Q)
         if name == "states":
             return sl(L.states_offset, nc * H * P * N, io).view(nc, H, P, N)
         if name == "hprev":

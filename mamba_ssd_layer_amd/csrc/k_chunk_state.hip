@@ -193,6 +193,9 @@ __global__ __launch_bounds__(512, 1) void k_chunk_state_hb(
       }
       wait_vmcnt_dyn(n);
     }
+    // the previous head's S tile (LDS writes) complete before the barrier: the
+    // compiler does not always add this wait at the loop's back edge
+    wait_lgkmcnt0();
     __syncthreads();  // ... for every thread; the previous head is done everywhere
     if (hi > 0) store_s(t, hh - 1);
     {  // x_l *= w_l in place (fp32, one rounding)

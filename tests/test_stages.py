@@ -27,6 +27,9 @@ CASES = {
     "packed_bf16": dict(batch=1, seqlen=0, nheads=4, headdim=64, dstate=64, ngroups=4,
                         chunk=128, dtype="bf16", seed=3, init_std=0.3,
                         lens=[5, 300, 0, 128, 129, 1]),
+    # head dim 128: each head runs as two kernel heads of 64 state rows
+    "split_bf16": dict(batch=2, seqlen=333, nheads=2, headdim=128, dstate=64, ngroups=1,
+                       chunk=64, dtype="bf16", seed=5, init_std=0.3),
 }
 # per-stage tolerances (relative to the max of the reference)
 TOL_STAGE = {"f32": 1e-5, "bf16": 1e-2}
@@ -66,17 +69,19 @@ def test_stages(name):
     torch.cuda.synchronize()
     acum = plan.view("acum").cpu().numpy()
     dtq = plan.view("dtq").cpu().numpy()
+    # kernel heads: a head of 64 r rows is r kernel heads with its dt and A
+    hr = acum.shape[1] // w.nheads
     num = den = 0.0
     for k, c in enumerate(cidx):
         n = lens[k]
-        ref = it["Acum"][k, :, :n]
+        ref = np.repeat(it["Acum"][k, :, :n], hr, axis=0)
         num = max(num, float(np.max(np.abs(acum[c, :, :n] - ref))))
         den = max(den, float(np.max(np.abs(ref))))
         # padding past a partial chunk repeats the last value; dt is zero there
         assert np.array_equal(acum[c, :, n:], np.repeat(acum[c, :, n - 1:n], w.chunk - n, axis=1))
         assert np.all(dtq[c, :, n:] == 0)
         t0 = it["chunk_start"][k]
-        assert np.array_equal(dtq[c, :, :n], w.dt[t0:t0 + n].T)
+        assert np.array_equal(dtq[c, :, :n], np.repeat(w.dt[t0:t0 + n].T, hr, axis=0))
     say(f"  {name}: acum rel err {num / den:.3e}")
     assert num / den <= 1e-5
 
