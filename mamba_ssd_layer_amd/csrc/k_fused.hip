@@ -195,7 +195,7 @@ void k_ssd_fused(
   // decay exceeds 2^-40 (there the exact per-chunk form is used).
   float lam = 0.f;
 
-  // chunk k's loads into ring slot sl: LDC vector-memory ops per wavefront.
+  // a chunk's loads into its ring slot: LDC vector-memory ops per wavefront.
   // Each load is a wave-uniform base (the chunk's first row) plus a per-lane
   // byte offset fixed for the whole sequence; only a partial last chunk
   // recomputes the offsets with its rows clamped.
@@ -226,38 +226,49 @@ void k_ssd_fused(
     const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = m & 7;
     yoff[i] = static_cast<uint32_t>((r * ldx + (int64_t)h * P + 8 * cc) * 2);
   }
-  auto issue = [&](int k, int sl) {
-    const int64_t t0 = tb + (int64_t)k * CQ;
-    const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
-    if (last < CQ - 1) lane_offsets(last);
-    const uint32_t base = smem0 + sl * SLOT;
+  // Chunks are loaded and their y stored in order, so each side keeps running
+  // wave-uniform pointers that advance by one chunk per call; only the last
+  // chunk can be partial (lastlen tokens).
+  const int lastlen = static_cast<int>(len - (int64_t)(nck - 1) * CQ);
+  const uint16_t *xg = x + tb * ldx, *bg = Bm + tb * ldb, *cg = Cm + tb * ldb;
+  const float *dg = dt + tb * Hd;
+  uint16_t *yg = y + tb * ldx;
+  // this wavefront's LDS destinations within a slot
+  const uint32_t ldsx = smem0 + OX + hh * XH + XR * pq * 128;
+  auto issue = [&](int k, uint32_t soff) {
+    if (k == nck - 1 && lastlen < CQ) lane_offsets(lastlen - 1);
 #pragma unroll
-    for (int i = 0; i < XI; ++i) dma_lds16_sb(xoff[i], x + t0 * ldx, base + OX + hh * XH + XR * pq * 128 + i * 1024);
+    for (int i = 0; i < XI; ++i) dma_lds16_sb(xoff[i], xg, ldsx + soff + i * 1024);
 #pragma unroll
     for (int i = 0; i < BCI; ++i) {
       const int u = wave + i * WAVES, tile = u / (BT / 1024), pi = u % (BT / 1024);
       if (F::NPC % WAVES != 0 && u >= F::NPC) break;  // wave-uniform
-      dma_lds16_sb(bcoff[i], (tile ? Cm : Bm) + t0 * ldb, base + (tile ? OC : OB) + pi * 1024);
+      dma_lds16_sb(bcoff[i], tile ? cg : bg, smem0 + soff + (tile ? OC : OB) + pi * 1024);
     }
-    if (wave < F::DTP) dma_lds4_sb(dtoff, dt + t0 * Hd, base + OD + wave * DW);
+    if (wave < F::DTP) dma_lds4_sb(dtoff, dg, smem0 + soff + OD + wave * DW);
+    xg += CQ * ldx;
+    bg += CQ * ldb;
+    cg += CQ * ldb;
+    dg += CQ * Hd;
   };
-  // rows XR pq .. XR pq + XR - 1 of head hh's y of chunk k (staged in slot sl): STC stores
-  auto store_y = [&](int k, int sl) {
-    const int64_t t0 = tb + (int64_t)k * CQ;
-    const int rem = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ));
-    const unsigned char *ys = smem + sl * SLOT + OX + hh * XH;
+  // rows XR pq .. XR pq + XR - 1 of head hh's y of chunk k (staged in the
+  // slot at byte offset soff): STC stores
+  auto store_y = [&](int k, uint32_t soff) {
+    const int rem = k == nck - 1 ? lastlen : CQ;
+    const unsigned char *ys = smem + soff + OX + hh * XH;
     u32x4 v[XI];
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = m & 7;
       v[i] = *reinterpret_cast<const u32x4 *>(ys + r * 128 + ((cc ^ rot_swz<8>(r)) << 4));
     }
-    unsigned char *yb = reinterpret_cast<unsigned char *>(y + t0 * ldx);  // wave-uniform
+    unsigned char *yb = reinterpret_cast<unsigned char *>(yg);  // wave-uniform
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       const int r = XR * pq + ((i * 64 + lane) >> 3);
       if (r < rem) *reinterpret_cast<u32x4 *>(yb + yoff[i]) = v[i];
     }
+    yg += CQ * ldx;
   };
   // row operand of a B or C tile in the state's K order: K step q gives lane
   // group g4 n = 32q + 8 g4 + {0..7}, one 16-byte chunk
@@ -284,17 +295,35 @@ void k_ssd_fused(
   // vector-memory ops this wavefront issues per chunk load: x rows, its B/C
   // pieces, and dt piece `wave` for wavefronts below DTP
   const int ldc = XI + (F::NPC - wave + WAVES - 1) / WAVES + (wave < F::DTP ? 1 : 0);
+  // ... the same as constants, where every wavefront has NPC / WAVES B/C pieces
+  constexpr bool EVEN_BC = F::NPC % WAVES == 0;
+  constexpr int LD0 = XI + F::NPC / WAVES, LD1 = LD0 + 1;  // without / with a dt piece
+  constexpr int SLOTS = R * SLOT;
+  // wait counts known at compile time in the steady state (with saving, only
+  // for at most two slots in flight, where the parity of k - 1 decides)
+  constexpr bool STATIC_WAIT = EVEN_BC && (D <= 2 || !SAVE);
 #pragma unroll
   for (int c = 0; c < D; ++c)
-    if (c < nck) issue(c, c);
-  int sl = 0;
+    if (c < nck) issue(c, c * SLOT);
+  uint32_t soff = 0;  // byte offset of chunk k's slot
 #pragma unroll 1
   for (int k = 0; k < nck; ++k) {
     // chunk k has landed once at most the ops this wavefront issued after its
     // loads are pending: loads of later chunks (prologue, then one chunk per
     // iteration) and the y stores of the iterations in between
     // (and, when saving, the state stores of the even ones: SVC each)
-    {
+    if (STATIC_WAIT && k >= D && k + D <= nck) {
+      // steady state: the last D - 1 iterations each issued STC stores and
+      // one chunk load (and, when saving, iteration k - 1 its state if even)
+      const bool dtw = wave < F::DTP, sv = SAVE && D == 2 && !((k - 1) & 1);
+      if (dtw) {
+        if (sv) wait_vmcnt<(D - 1) * (STC + LD1) + SVC>();
+        else wait_vmcnt<(D - 1) * (STC + LD1)>();
+      } else {
+        if (sv) wait_vmcnt<(D - 1) * (STC + LD0) + SVC>();
+        else wait_vmcnt<(D - 1) * (STC + LD0)>();
+      }
+    } else {
       int n = k < D ? (min(D, nck) - 1 - k) * ldc : 0;
       for (int j = k < D ? 0 : k - D + 1; j < k; ++j)
         n += (SAVE && !(j & 1) ? SVC : 0) + (j >= 1 ? STC : 0) + (j + D < nck ? ldc : 0);
@@ -318,16 +347,15 @@ void k_ssd_fused(
                       N, pk, c16, g4);
       }
     }
-    const int slp = sl == 0 ? R - 1 : sl - 1;  // slot of chunk k-1, and of chunk k+D
-    if (k >= 1) store_y(k - 1, slp);
-    if (k + D < nck) issue(k + D, slp);
+    const uint32_t sprev = soff == 0 ? SLOTS - SLOT : soff - SLOT;  // chunk k-1's slot, and k+D's
+    if (k >= 1) store_y(k - 1, sprev);
+    if (k + D < nck) issue(k + D, sprev);
 
-    unsigned char *xh = smem + sl * SLOT + OX + hh * XH;  // head hh's x tile (this wavefront: columns p0 ..)
-    const unsigned char *bs = smem + sl * SLOT + OB;
-    const unsigned char *cs = smem + sl * SLOT + OC;
-    const float *dts = reinterpret_cast<const float *>(smem + sl * SLOT + OD);
-    const int last = static_cast<int>(min((int64_t)CQ, len - (int64_t)k * CQ)) - 1;
-
+    unsigned char *xh = smem + soff + OX + hh * XH;  // head hh's x tile (this wavefront: columns p0 ..)
+    const unsigned char *bs = smem + soff + OB;
+    const unsigned char *cs = smem + soff + OC;
+    const float *dts = reinterpret_cast<const float *>(smem + soff + OD);
+    const int last = k == nck - 1 ? lastlen - 1 : CQ - 1;
     // cumulative decay (lanes l and 32 + l hold token l) and per-token tables
     const int tl = lane & 31;
     const float dtv = tl <= last ? dts[tl * HPB + hh] : 0.f;
@@ -497,12 +525,12 @@ void k_ssd_fused(
         *reinterpret_cast<u32x2 *>(xh + l * 128 + (((col >> 3) ^ rot_swz<8>(l)) << 4) + (col & 7) * 2) = o;
       }
     }
-    sl = sl == R - 1 ? 0 : sl + 1;
+    soff = soff == SLOTS - SLOT ? 0 : soff + SLOT;
   }
   if (nck > 0) {
     wait_lgkmcnt0();
     __syncthreads();  // every wavefront's part of the last chunk's y is staged
-    store_y(nck - 1, (nck - 1) % R);
+    store_y(nck - 1, ((nck - 1) % R) * SLOT);
   }
   if (hfin) {
     const float e = exp2_fast(lam);
