@@ -38,9 +38,10 @@
 //      causal 32 x 32 block (same K order), the decay exp(a_l - a_s) dt_s
 //      applied per element as exp(a_l) times a per-token table of
 //      dt_s exp(-a_s) (per element in the log2 domain for a chunk that decays
-//      below 2^-40) and the tile above the diagonal masked, then Y^T += X^T G^T
+//      below 2^-96) and the tile above the diagonal masked, then Y^T += X^T G^T
 //      with the accumulators as B-operands and X^T from transposing LDS reads
-//      in the matching token order; plus D x in fp32;
+//      in the matching token order; plus D x as X^T diag(D), D split into two
+//      bf16 parts;
 //   3. state: h^T = exp(a_last) h^T + B^T (w x) with w_s = exp(a_last - a_s)
 //      dt_s, from transposing reads of B and the same X^T registers.
 #include "ssd_device.hpp"
@@ -362,7 +363,8 @@ void k_ssd_fused(
     const float a = scan32(dtv * Ah);
     const float alast = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), 31));
     const float a2last = alast * kLog2e;
-    const bool steep = a2last < -40.f;          // exact per-chunk form for this chunk
+    const bool steep = a2last < -40.f;          // exact per-chunk state update for this chunk
+    const bool gsep = a2last >= -96.f;          // separable intra-chunk decay (see below)
     const float wshift = steep ? a2last : -lam;  // log2 of w_s / (dt_s exp(-a_s))
     if (lane < 32) {
       const float al = a * kLog2e;
@@ -370,7 +372,7 @@ void k_ssd_fused(
       adw[tl] = al;                              // log2 exp(a_l)
       adw[CQ + tl] = bs;                         // log2(dt_s exp(-a_s))
       adw[2 * CQ + tl] = exp2_fast(bs + wshift);  // the state update's token weight
-      // dt_s exp(-a_s) itself, at most dt_s 2^40 where the chunk is not steep
+      // dt_s exp(-a_s) itself, at most dt_s 2^96 where gsep holds
       adw[3 * CQ + tl] = exp2_fast(fminf(bs, 126.f));
     }
     wave_sync();
@@ -422,9 +424,10 @@ void k_ssd_fused(
       }
       // lane holds s = 16 sb + 4 g4 + r, l = 16 lb + c16
       float g00[4], g11[4], g01[4];
-      if (!steep) {
-        // exp(a_l - a_s) dt_s = exp(a_l) (dt_s exp(-a_s)): both factors finite
-        // when the chunk decays by less than 2^-40 (the masked s > l side too)
+      if (gsep) {
+        // exp(a_l - a_s) dt_s = exp(a_l) (dt_s exp(-a_s)): both factors normal
+        // floats when the chunk decays by less than 2^-96 (and their product
+        // finite on the masked s > l side too)
         const f32x4 v0 = *reinterpret_cast<const f32x4 *>(adw + 3 * CQ + 4 * g4);
         const f32x4 v1 = *reinterpret_cast<const f32x4 *>(adw + 3 * CQ + 16 + 4 * g4);
 #pragma unroll
