@@ -2,13 +2,16 @@
 """Benchmark of the Mamba-2 SSD chunked-scan forward (libssd) on one MI355X.
 
 A step is one full forward over one batch of seeded synthetic input already
-resident in HBM, timed two ways: the chunked forward (ssd_chunk_scan_fwd:
-chunk_cumsum, chunk_state, state_passing, chunk_scan) and, where its shape is
-supported, the one-pass forward (ssd_fused_fwd: the same steps per 32-token
-chunk with the state kept on chip).  `value` is the faster of the two (named
-in config.path); both are reported.  Prints one JSON line with whole-job
-tokens/s, the roofline position of that path's dominant kernel (timed with HIP
-events on the launch stream), per-kernel figures of the chunked stages (each
+resident in HBM, timed up to three ways: the chunked forward
+(ssd_chunk_scan_fwd: chunk_cumsum, chunk_state, state_passing, chunk_scan);
+where its shape is supported, the one-pass forward (ssd_fused_fwd: the same
+steps per 32-token chunk with the state kept on chip); and, for few long
+fixed-length sequences, the one-pass forward over segments
+(ssd_fused_fwd_split).  `value` is the fastest (named in config.path); all are
+reported.  Prints one JSON line with whole-job tokens/s, the roofline position
+of that path's dominant kernel (the whole path for the split forward; timed
+with HIP events on the launch stream), per-kernel figures of the chunked
+stages (each
 kernel's bandwidth against the published peak and against a plain copy
 measured in the same run, and its algorithmic MFMA flops against the peak),
 and the CPU oracle timed on a bounded sample of the same workload on the host
@@ -37,7 +40,7 @@ STAGES = ["chunk_cumsum", "chunk_state", "state_passing", "chunk_scan"]
 KERNEL_SOURCES = {
     "chunk_cumsum": "k_scan_prep.hip", "state_passing": "k_scan_prep.hip",
     "chunk_state": "k_chunk_state.hip", "chunk_scan": "k_chunk_scan.hip",
-    "fused_fwd": "k_fused.hip",
+    "fused_fwd": "k_fused.hip", "fused_fwd_split": "k_fused.hip",
 }
 FUSED_CHUNK = 32  # the one-pass forward's chunk length
 FLUSH_BYTES = 1 << 30  # written between timed steps: four times the 256 MB MALL
@@ -64,6 +67,9 @@ def algorithmic(w, stage: str):
       fused_fwd      bytes 2 s H P + 2 s G N + 4 H, plus 4 H P N per sequence for
                      the final state (and the initial state when read)
                      flops H (4 P N + 33 P) + 33 G N  (Q = 32: inter, state, intra)
+      fused_fwd_split  the forward's, as fused_fwd (its state-only pass re-reads
+                     x, B and dt of all segments but the last, and the segment
+                     states cross HBM: work of the split, not of the forward)
     """
     T, H, P, N, G, Q = w.tokens, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk
     nseq = w.nsequences
@@ -82,7 +88,7 @@ def algorithmic(w, stage: str):
         b = 2 * s * T * H * P + 2 * s * T * G * N + 8 * T * H + hsz * nc * H * P * N
         f = T * (H * (2 * P * N + (Q + 1) * P) + G * (Q + 1) * N)
         return b, f
-    if stage == "fused_fwd":
+    if stage in ("fused_fwd", "fused_fwd_split"):
         q = FUSED_CHUNK
         init = 4 * nseq * H * P * N if w.h0 is not None else 0
         b = 2 * s * T * H * P + 2 * s * T * G * N + 4 * T * H + 4 * nseq * H * P * N + init
@@ -522,6 +528,35 @@ def main() -> int:
             f"{fsum['mean_us']:.1f}, back to back {fsum['back_to_back_us']:.1f}), "
             f"{T / ft / 1e6:.1f} M tokens/s")
 
+    # the split one-pass forward, where the library cuts the sequences into
+    # segments (few long fixed-length sequences)
+    split = None
+    seg_len = ssd.libssd.ssd_fused_split_seg_len(dims) if fused is not None and not w.nseq else 0
+    if 0 < seg_len < w.seqlen:
+        ys_ = torch.empty_like(x)
+        fs_ = torch.empty_like(fin)
+        wsp = torch.empty(ssd.libssd.ssd_fused_split_workspace_size(dims, seg_len),
+                          dtype=torch.uint8, device=dev)
+
+        def sstep():
+            ssd.fused_fwd_split(x, dt, A, Bm, Cm, D, h0, y=ys_, final_state=fs_, seg_len=seg_len,
+                                workspace=wsp)
+
+        for _ in range(args.warmup):
+            sstep()
+        sper, swall = timed_steps(sstep)
+        ssum = summary(sper, swall)
+        ssum["back_to_back_us"] = round(back_to_back(sstep), 2)
+        sb, sf = algorithmic(w, "fused_fwd_split")
+        st_ = ssum["us"] * 1e-6
+        split = {**ssum, "seg_len": seg_len, "tokens_per_s": round(T / st_, 1), "bytes": sb,
+                 "flops": sf, "GBs": round(sb / st_ / 1e9, 1),
+                 "TFLOPs": round(sf / st_ / 1e12, 2),
+                 "hbm_frac": round(sb / st_ / 1e9 / HBM_PEAK_GBS, 4)}
+        log(f"bench: split one-pass forward (segments of {seg_len}) median {ssum['us']:.1f} "
+            f"us/step (flushed; mean {ssum['mean_us']:.1f}, back to back "
+            f"{ssum['back_to_back_us']:.1f}), {T / st_ / 1e6:.1f} M tokens/s")
+
     # per-stage times: the same stages launched one by one, each after a
     # MALL flush, HIP events around each launch (median over steps)
     stage_us, stage_mean_us = {}, {}
@@ -560,6 +595,8 @@ def main() -> int:
 
     if fused is not None:
         fused.update(fracs(fused["bytes"], fused["flops"], fused["us"] * 1e-6))
+    if split is not None:
+        split.update(fracs(split["bytes"], split["flops"], split["us"] * 1e-6))
     kernels = {}
     for s in STAGES:
         b, f = algorithmic(w, s)
@@ -599,9 +636,16 @@ def main() -> int:
     path, roofline, ms_step = "ssd_chunk_scan_fwd", chunked_roofline, ms
     if fused is not None:
         fused["roofline"] = roofline_of("fused_fwd", fused["mean_us"])
-        if fused["us"] < ms * 1e3:
+        if fused["us"] < ms_step * 1e3:
             path, roofline, ms_step, value = ("ssd_fused_fwd", fused["roofline"], fused["us"] / 1e3,
                                               fused["tokens_per_s"])
+    if split is not None:
+        # three launches (state-only pass, hand-off, forward): the roofline of
+        # the whole path, its algorithmic bytes over its mean time
+        split["roofline"] = roofline_of("fused_fwd_split", split["mean_us"])
+        if split["us"] < ms_step * 1e3:
+            path, roofline, ms_step, value = ("ssd_fused_fwd_split", split["roofline"],
+                                              split["us"] / 1e3, split["tokens_per_s"])
 
     decode = None
     if not args.no_decode:
@@ -632,10 +676,12 @@ def main() -> int:
                    "on the launch stream; roofline.achieved: algorithmic bytes / the mean of the "
                    "same launches"),
         "config": {**workloads.describe(w), "path": path,
-                   "chunk": FUSED_CHUNK if path == "ssd_fused_fwd" else w.chunk,
+                   "chunk": FUSED_CHUNK if path.startswith("ssd_fused_fwd") else w.chunk,
+                   **({"seg_len": split["seg_len"]} if path == "ssd_fused_fwd_split" else {}),
                    "parallelism": "none (1 GPU)"},
         "roofline": roofline, "cpu_baseline": cpu,
-        "forwards": {"ssd_chunk_scan_fwd": chunked, "ssd_fused_fwd": fused},
+        "forwards": {"ssd_chunk_scan_fwd": chunked, "ssd_fused_fwd": fused,
+                     "ssd_fused_fwd_split": split},
         "kernels": kernels, "copy_GBs": round(copy_gbs, 1), "decode_step": decode,
         "block_neighbours": block,
         "training_step": train,

@@ -300,6 +300,48 @@ ssd_status ssd_fused_fwd_train(const void *x, const float *dt, const float *A, c
                                void *chunk_states, size_t states_bytes, const ssd_dims *dims,
                                void *stream);
 
+/* The one-pass forward for few, long fixed-length sequences, where one block
+ * per (sequence, head) leaves the GPU idle: each sequence is cut into
+ * segments of seg_len tokens and the chunked algorithm of page "Mamba-2
+ * Architecture: State Space Duality Explained", "2. The Chunked SSD
+ * Algorithm", is applied one level up (blockwise evaluation, glossary page
+ * "State Space Duality", "Why it is useful"), with the one-pass kernel as the
+ * per-segment step:
+ *   1. every segment but the last, from a zero state: its end state and total
+ *      decay (a state-only pass: x, B and dt are read, nothing is written but
+ *      the workspace);
+ *   2. the hand-off h_{j+1} = exp(sum of dt A over segment j) h_j + S_j from
+ *      init_state (or 0), giving the state entering every segment;
+ *   3. every segment from its entering state: y, and final_state from the
+ *      last one.
+ * Arguments, layouts and results are ssd_fused_fwd's (cu_seqlens absent:
+ * fixed-length batches only, nseq > 0 returns SSD_ERR_UNSUPPORTED), to
+ * rounding; final_state may alias init_state.
+ *   seg_len    tokens per segment, a positive multiple of 32, else
+ *              SSD_ERR_INVALID_ARG; seg_len >= seqlen runs ssd_fused_fwd
+ *              (no workspace needed).
+ *   workspace  device memory of at least ssd_fused_split_workspace_size(dims,
+ *              seg_len) bytes (else SSD_ERR_WORKSPACE), 256-byte aligned,
+ *              overlapping no argument: fp32 [batch][nseg][H][P][N] states
+ *              entering the segments, then fp32 [batch][nseg-1][H] segment
+ *              decays (log2), nseg = ceil(seqlen / seg_len).
+ * Supported shapes are ssd_fused_fwd's.  Returns after enqueueing. */
+ssd_status ssd_fused_fwd_split(const void *x, const float *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *init_state, void *y,
+                               float *final_state, int64_t seg_len, const ssd_dims *dims,
+                               void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of ssd_fused_fwd_split for these dims and seg_len (0 when
+ * seg_len >= seqlen, or when the arguments are invalid).  Host-only. */
+size_t ssd_fused_split_workspace_size(const ssd_dims *dims, int64_t seg_len);
+
+/* A segment length for ssd_fused_fwd_split on the current device: seqlen
+ * rounded up to 32 (no split) when sequences x heads already give two blocks
+ * per compute unit, else the power of two (at least 512) that gives about 8
+ * (segment, head) rows per compute unit; 0 outside ssd_fused_fwd's shapes or
+ * for packed sequences.  Host-only (queries the device's compute units). */
+int64_t ssd_fused_split_seg_len(const ssd_dims *dims);
+
 /* Bytes of ssd_fused_fwd_train's chunk_states for these dims (npairs =
  * batch * ceil(seqlen / 64), or ceil(T / 64) + nseq for packed sequences);
  * 0 if the dims are invalid or outside ssd_fused_fwd's shapes.  Host-only. */

@@ -32,7 +32,8 @@ from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsuppo
 
 __all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDTrainForward", "SSDError", "SSDInvalidArgument",
            "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "validate_cu_seqlens", "step",
-           "conv1d_silu", "gate_rmsnorm", "fused_fwd", "make_fused_states", "fused_bwd"]
+           "conv1d_silu", "gate_rmsnorm", "fused_fwd", "fused_fwd_split", "fused_split_seg_len",
+           "make_fused_states", "fused_bwd"]
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -229,6 +230,41 @@ def fused_fwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
         libssd.ssd_fused_fwd_train(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state,
                                    chunk_states, chunk_states.numel() * chunk_states.element_size(),
                                    dims, stream)
+    return y, final_state
+
+
+def fused_split_seg_len(x: torch.Tensor, B: torch.Tensor) -> int:
+    """The library's segment length for fused_fwd_split on this device (the
+    sequence length rounded up to 32, i.e. no split, when sequences x heads
+    already fill the GPU)."""
+    return libssd.ssd_fused_split_seg_len(dims_for(x, B, None))
+
+
+def fused_fwd_split(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                    C: torch.Tensor, D: Optional[torch.Tensor] = None,
+                    init_state: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
+                    final_state: Optional[torch.Tensor] = None, want_final: bool = True,
+                    seg_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                    stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """y, final_state = the one-pass forward over segments of seg_len tokens
+    (ssd_fused_fwd_split: fixed-length batches; a state-only pass, the
+    hand-off between segments, then every segment from its entering state).
+    Same arguments and results as fused_fwd without cu_seqlens.  seg_len
+    defaults to fused_split_seg_len; workspace (uint8, device) is allocated
+    when not given."""
+    dims = dims_for(x, B, None)
+    if seg_len is None:
+        seg_len = libssd.ssd_fused_split_seg_len(dims)
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None and want_final:
+        final_state = torch.empty((dims.batch, dims.nheads, dims.headdim, dims.dstate),
+                                  dtype=torch.float32, device=x.device)
+    need = libssd.ssd_fused_split_workspace_size(dims, seg_len)
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    libssd.ssd_fused_fwd_split(x, dt, A, B, C, D, init_state, y, final_state, seg_len, dims,
+                               workspace, stream)
     return y, final_state
 
 

@@ -99,8 +99,8 @@ __device__ __forceinline__ void wave_sync() {
 
 // Geometry of one kernel instance: N state size, HPB heads per block, PW
 // state rows p per wavefront (32 or 16: 64 / PW wavefronts per head), R ring
-// slots.
-template <int N, int HPB, int PW, int R>
+// slots; ST: the state-only pass (no C, no y).
+template <int N, int HPB, int PW, int R, bool ST = false>
 struct FusedCfg {
   static constexpr int P = 64, CQ = 32, WPH = P / PW, WAVES = WPH * HPB, THREADS = 64 * WAVES;
   static constexpr int PT = PW / 16;             // 16-column state tiles per wavefront
@@ -110,17 +110,18 @@ struct FusedCfg {
   static constexpr int BT = CQ * N * 2;          // B (or C) of a chunk
   static constexpr int DTP = (CQ * HPB + 63) / 64;  // 64-entry dt pieces of a chunk
   static constexpr int DW = 64 * 4;              // one dt piece (wavefront i < DTP loads piece i)
-  static constexpr int OX = 0, OB = HPB * XH, OC = OB + BT, OD = OC + BT;
+  static constexpr int OX = 0, OB = HPB * XH, OC = OB + BT, OD = OC + (ST ? 0 : BT);
   static constexpr int SLOT = OD + DTP * DW;
   static constexpr int AD = R * SLOT;            // per wavefront: [al2 | bs2 | w | vs], 32 floats each
   static constexpr int ADW = 4 * CQ * 4;
   static constexpr int TOTAL = AD + WAVES * ADW;
-  static constexpr int NPC = 2 * BT / 1024;     // 1 KB pieces of B and C
+  static constexpr int NBC = ST ? 1 : 2;         // B (and C) tiles a chunk loads
+  static constexpr int NPC = NBC * BT / 1024;    // 1 KB pieces of B and C
   static constexpr int BCI = (NPC + WAVES - 1) / WAVES;  // ... at most per wavefront (piece
                                                  // u goes to wavefront u % WAVES)
   static constexpr int LDC = XI + BCI;           // vector-memory ops a wavefront issues per chunk
                                                  // load, at most (+1 with a dt piece)
-  static constexpr int STC = XI;                 // ... per chunk of y it stores
+  static constexpr int STC = ST ? 0 : XI;        // ... per chunk of y it stores
   static constexpr int BLOCKS_PER_CU = (160 * 1024) / TOTAL;
   // waves a SIMD must hold for BLOCKS_PER_CU blocks (at most 3: the kernel
   // needs ~140-200 VGPRs, so more would spill)
@@ -128,23 +129,56 @@ struct FusedCfg {
   static constexpr int WAVES_PER_SIMD = WAVES_PER_SIMD_LDS < 3 ? WAVES_PER_SIMD_LDS : 3;
   static_assert(PW == 16 || PW == 32, "state rows per wavefront");
   static_assert(XI >= 1 && XI * 1024 == XR * P * 2, "x rows in 1 KB pieces");
-  static_assert(BCI >= 1 && NPC * 1024 == 2 * BT, "B and C in 1 KB pieces");
+  static_assert(BCI >= 1 && NPC * 1024 == NBC * BT, "B and C in 1 KB pieces");
   static_assert(DTP <= WAVES, "a wavefront per dt piece");
   static constexpr int SVC = PT * N / 32;        // ... per saved chunk-start state
   static_assert(R >= 2 && (R - 2) * (LDC + 1 + STC + SVC) <= 47, "wait counts");
   static_assert(BLOCKS_PER_CU >= 1 && WAVES_PER_SIMD >= 1, "occupancy");
 };
 
-template <int N, int HPB, int PW, int R, bool SAVE>
-__global__ __launch_bounds__((FusedCfg<N, HPB, PW, R>::THREADS),
-                             (FusedCfg<N, HPB, PW, R>::WAVES_PER_SIMD))
-void k_ssd_fused(
-    const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
-    const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
-    const float *__restrict__ h0, const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows,
-    int H, int G, int hr, uint16_t *__restrict__ y, float *__restrict__ hfin,
-    uint16_t *__restrict__ hsave) {
-  using F = FusedCfg<N, HPB, PW, R>;
+// What a launch walks: rows of tokens (sequences, or segments of them), each
+// from a given state.
+struct FusedArgs {
+  const uint16_t *x;
+  const float *dt, *A;
+  const uint16_t *B, *C;
+  const float *D;
+  const float *h0;       // initial state of each sequence [rows0, H, P, N], or NULL
+  const int32_t *cu;     // packed sequences (then S = L, nsr = 1), or NULL
+  int64_t L, T;          // tokens per sequence (fixed length), total tokens
+  int64_t S;             // tokens per segment (L when not split)
+  int nsr;               // segments of a sequence this launch walks
+  int rows;              // blocks' rows: sequences x nsr
+  int H, G, hr;
+  uint16_t *y;
+  float *hfin;           // final state of each sequence (last segment), or NULL
+  uint16_t *hsave;       // SAVE: bf16 state entering every 64-token pair
+  const float *hin;      // split forward: the state entering each segment,
+                         // [seq][nsr][H][P][N] (then h0 is not read)
+  float *sseg;           // state-only pass: segment j's end state from 0 into
+                         // [seq][j + 1] of a [seq][nsr + 1][H][P][N] buffer ...
+  float *lseg;           // ... and its total log2 decay into [seq][nsr][H]
+};
+
+enum FusedMode { kFwd = 0, kFwdSave = 1, kState = 2 };
+
+template <int N, int HPB, int PW, int R, int MODE>
+__global__ __launch_bounds__((FusedCfg<N, HPB, PW, R, MODE == kState>::THREADS),
+                             (FusedCfg<N, HPB, PW, R, MODE == kState>::WAVES_PER_SIMD))
+void k_ssd_fused(const FusedArgs args) {
+  constexpr bool SAVE = MODE == kFwdSave, ST = MODE == kState;
+  using F = FusedCfg<N, HPB, PW, R, ST>;
+  const uint16_t *__restrict__ x = args.x;
+  const float *__restrict__ dt = args.dt;
+  const float *__restrict__ A = args.A;
+  const uint16_t *__restrict__ Bm = args.B;
+  const uint16_t *__restrict__ Cm = args.C;
+  const float *__restrict__ Dv = args.D;
+  const int32_t *__restrict__ cu = args.cu;
+  const int64_t L = args.L, T = args.T;
+  const int H = args.H, G = args.G, hr = args.hr;
+  uint16_t *__restrict__ y = args.y;
+  uint16_t *__restrict__ hsave = args.hsave;
   constexpr int P = F::P, CQ = F::CQ, WPH = F::WPH, PT = F::PT, XR = F::XR, XI = F::XI;
   constexpr int NT = N / 16;   // state tiles per p-tile (over n)
   constexpr int KQ = N / 32;   // K steps over n
@@ -156,7 +190,7 @@ void k_ssd_fused(
 
   int s, hb;
   xcd_chunk_head(H / HPB, s, hb);
-  if (s >= rows) return;
+  if (s >= args.rows) return;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
@@ -166,9 +200,29 @@ void k_ssd_fused(
   const int h0b = HPB * hb;  // the block's first head
   const int h = h0b + hh;
   const int g = h0b / (H / G);
+  // row s: segment seg of sequence sq (packed sequences are never split)
   int64_t tb, len;
-  seq_range(cu, s, L, T, tb, len);
-  const int64_t sh = (int64_t)s * H + h;
+  int sq = s, seg = 0;
+  if (cu) {
+    seq_range(cu, s, L, T, tb, len);
+  } else {
+    sq = s / args.nsr;
+    seg = s - sq * args.nsr;
+    tb = (int64_t)sq * L + (int64_t)seg * args.S;
+    len = min(args.S, L - (int64_t)seg * args.S);
+  }
+  constexpr int64_t PN = (int64_t)P * N;
+  // the state entering the row, and where the state leaving it goes
+  const float *h0p;
+  float *hfp;
+  if (ST) {
+    h0p = nullptr;
+    hfp = args.sseg + (((int64_t)sq * (args.nsr + 1) + seg + 1) * H + h) * PN;
+  } else {
+    h0p = args.hin ? args.hin + ((int64_t)s * H + h) * PN
+                   : args.h0 ? args.h0 + ((int64_t)sq * H + h) * PN : nullptr;
+    hfp = seg == args.nsr - 1 && args.hfin ? args.hfin + ((int64_t)sq * H + h) * PN : nullptr;
+  }
   const int64_t ldx = (int64_t)H * P, ldb = (int64_t)G * N;
   const int Hd = H / hr;  // heads of dt, A and D: kernel head h takes those of h / hr
   const float Ah = A[h / hr];
@@ -183,10 +237,10 @@ void k_ssd_fused(
   f32x4 hst[PT][NT];
 #pragma unroll
   for (int pt = 0; pt < PT; ++pt) {
-    const int64_t prow = (sh * P + p0 + 16 * pt + c16) * N;
+    const int64_t prow = (int64_t)(p0 + 16 * pt + c16) * N;
 #pragma unroll
     for (int j = 0; j < NT; ++j)
-      hst[pt][j] = h0 ? *reinterpret_cast<const f32x4 *>(h0 + prow + nrow(j)) : f32x4{};
+      hst[pt][j] = h0p ? *reinterpret_cast<const f32x4 *>(h0p + prow + nrow(j)) : f32x4{};
   }
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
   const int64_t pbase = SAVE ? pair_base64(cu, s, L, T) : 0;
@@ -195,6 +249,7 @@ void k_ssd_fused(
   // rescaled only when lam drops below -32, or before a chunk whose own
   // decay exceeds 2^-40 (there the exact per-chunk form is used).
   float lam = 0.f;
+  float lsum = 0.f;  // state-only pass: the row's total log2 decay
 
   // a chunk's loads into its ring slot: LDC vector-memory ops per wavefront.
   // Each load is a wave-uniform base (the chunk's first row) plus a per-lane
@@ -349,7 +404,7 @@ void k_ssd_fused(
       }
     }
     const uint32_t sprev = soff == 0 ? SLOTS - SLOT : soff - SLOT;  // chunk k-1's slot, and k+D's
-    if (k >= 1) store_y(k - 1, sprev);
+    if (!ST && k >= 1) store_y(k - 1, sprev);
     if (k + D < nck) issue(k + D, sprev);
 
     unsigned char *xh = smem + soff + OX + hh * XH;  // head hh's x tile (this wavefront: columns p0 ..)
@@ -377,105 +432,111 @@ void k_ssd_fused(
     }
     wave_sync();
 
-    // 1. inter term
-    u32x4 cop[2][KQ];
-#pragma unroll
-    for (int lt = 0; lt < 2; ++lt)
-#pragma unroll
-      for (int q = 0; q < KQ; ++q) cop[lt][q] = row_op(cs, 16 * lt + c16, q);
-    f32x4 ya[PT][2];
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt)
-#pragma unroll
-      for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = f32x4{};
-#pragma unroll
-    for (int q = 0; q < KQ; ++q) {
-#pragma unroll
-      for (int pt = 0; pt < PT; ++pt) {
-        const f32x4 u = hst[pt][2 * q], v = hst[pt][2 * q + 1];
-        const u32x4 sop{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
-                        pack_bf16x2(v.z, v.w)};
-#pragma unroll
-        for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(sop, cop[lt][q], ya[pt][lt]);
-      }
-    }
-    const float al0 = adw[c16], al1 = adw[16 + c16];
-    // exp(a_l) for the lane's tokens l = c16, 16 + c16
-    const float u0 = exp2_fast(al0), u1 = exp2_fast(al1);
-    const float el = exp2_fast(lam);
-    const float f0 = u0 * el, f1 = u1 * el;
-#pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
-      ya[pt][0] *= f0;
-      ya[pt][1] *= f1;
-    }
-
-    // 2. intra term: Z^T tiles (s-block, l-block) = (0,0), (1,1), (0,1);
-    // G^T = Z^T exp(a_l - a_s) dt_s on s <= l
-    u32x4 gop[2];
-    {
-      f32x4 z00{}, z11{}, z01{};
-#pragma unroll
-      for (int q = 0; q < KQ; ++q) {
-        const u32x4 b0 = row_op(bs, c16, q), b1 = row_op(bs, 16 + c16, q);
-        z00 = mfma16(b0, cop[0][q], z00);
-        z01 = mfma16(b0, cop[1][q], z01);
-        z11 = mfma16(b1, cop[1][q], z11);
-      }
-      // lane holds s = 16 sb + 4 g4 + r, l = 16 lb + c16
-      float g00[4], g11[4], g01[4];
-      if (gsep) {
-        // exp(a_l - a_s) dt_s = exp(a_l) (dt_s exp(-a_s)): both factors normal
-        // floats when the chunk decays by less than 2^-96 (and their product
-        // finite on the masked s > l side too)
-        const f32x4 v0 = *reinterpret_cast<const f32x4 *>(adw + 3 * CQ + 4 * g4);
-        const f32x4 v1 = *reinterpret_cast<const f32x4 *>(adw + 3 * CQ + 16 + 4 * g4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float keep = 4 * g4 + r <= c16 ? 1.f : 0.f;
-          g00[r] = z00[r] * (u0 * v0[r] * keep);
-          g11[r] = z11[r] * (u1 * v1[r] * keep);
-          g01[r] = z01[r] * (u1 * v0[r]);
-        }
-      } else {
-        const f32x4 bs0 = *reinterpret_cast<const f32x4 *>(adw + CQ + 4 * g4);
-        const f32x4 bs1 = *reinterpret_cast<const f32x4 *>(adw + CQ + 16 + 4 * g4);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float keep = 4 * g4 + r <= c16 ? 1.f : 0.f;
-          // for s > l the exponent may be large; min() keeps it finite so the
-          // 0 mask wins
-          g00[r] = z00[r] * (exp2_fast(fminf(al0 + bs0[r], 64.f)) * keep);
-          g11[r] = z11[r] * (exp2_fast(fminf(al1 + bs1[r], 64.f)) * keep);
-          g01[r] = z01[r] * exp2_fast(al1 + bs0[r]);
-        }
-      }
-      gop[0] = u32x4{pack_bf16x2(g00[0], g00[1]), pack_bf16x2(g00[2], g00[3]), 0u, 0u};
-      gop[1] = u32x4{pack_bf16x2(g01[0], g01[1]), pack_bf16x2(g01[2], g01[3]),
-                     pack_bf16x2(g11[0], g11[1]), pack_bf16x2(g11[2], g11[3])};
-    }
-    // X^T in the same token order: s = 4 g4 + {0..3}, 16 + 4 g4 + {0..3}
+    // X^T in the token order of the intra term's K steps and of the state
+    // update: s = 4 g4 + {0..3}, 16 + 4 g4 + {0..3}
     u32x4 xop[PT];
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
       const u32x2 t0 = tr4(xh, 128, 8, 4 * g4, p0 + 16 * pt);
       const u32x2 t1 = tr4(xh, 128, 8, 16 + 4 * g4, p0 + 16 * pt);
       xop[pt] = u32x4{t0.x, t0.y, t1.x, t1.y};
-#pragma unroll
-      for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(xop[pt], gop[lt], ya[pt][lt]);
     }
+    f32x4 ya[PT][2];
+    if constexpr (!ST) {
+      // 1. inter term
+      u32x4 cop[2][KQ];
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {  // D x in fp32: rows p = 16 pt + 4 g4 + r of token l
+      for (int lt = 0; lt < 2; ++lt)
 #pragma unroll
-      for (int lt = 0; lt < 2; ++lt) {
-        const int l = 16 * lt + c16, col = p0 + 16 * pt + 4 * g4;
-        const u32x2 v = *reinterpret_cast<const u32x2 *>(
-            xh + l * 128 + (((col >> 3) ^ rot_swz<8>(l)) << 4) + (col & 7) * 2);
-        ya[pt][lt].x += Dh * bf16lo(v.x);
-        ya[pt][lt].y += Dh * bf16hi(v.x);
-        ya[pt][lt].z += Dh * bf16lo(v.y);
-        ya[pt][lt].w += Dh * bf16hi(v.y);
+        for (int q = 0; q < KQ; ++q) cop[lt][q] = row_op(cs, 16 * lt + c16, q);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = f32x4{};
+#pragma unroll
+      for (int q = 0; q < KQ; ++q) {
+#pragma unroll
+        for (int pt = 0; pt < PT; ++pt) {
+          const f32x4 u = hst[pt][2 * q], v = hst[pt][2 * q + 1];
+          const u32x4 sop{pack_bf16x2(u.x, u.y), pack_bf16x2(u.z, u.w), pack_bf16x2(v.x, v.y),
+                          pack_bf16x2(v.z, v.w)};
+#pragma unroll
+          for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(sop, cop[lt][q], ya[pt][lt]);
+        }
       }
+      const float al0 = adw[c16], al1 = adw[16 + c16];
+      // exp(a_l) for the lane's tokens l = c16, 16 + c16
+      const float u0 = exp2_fast(al0), u1 = exp2_fast(al1);
+      const float el = exp2_fast(lam);
+      const float f0 = u0 * el, f1 = u1 * el;
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {
+        ya[pt][0] *= f0;
+        ya[pt][1] *= f1;
+      }
+
+      // 2. intra term: Z^T tiles (s-block, l-block) = (0,0), (1,1), (0,1);
+      // G^T = Z^T exp(a_l - a_s) dt_s on s <= l
+      u32x4 gop[2];
+      {
+        f32x4 z00{}, z11{}, z01{};
+#pragma unroll
+        for (int q = 0; q < KQ; ++q) {
+          const u32x4 b0 = row_op(bs, c16, q), b1 = row_op(bs, 16 + c16, q);
+          z00 = mfma16(b0, cop[0][q], z00);
+          z01 = mfma16(b0, cop[1][q], z01);
+          z11 = mfma16(b1, cop[1][q], z11);
+        }
+        // lane holds s = 16 sb + 4 g4 + r, l = 16 lb + c16
+        float g00[4], g11[4], g01[4];
+        if (gsep) {
+          // exp(a_l - a_s) dt_s = exp(a_l) (dt_s exp(-a_s)): both factors normal
+          // floats when the chunk decays by less than 2^-96 (and their product
+          // finite on the masked s > l side too)
+          const f32x4 v0 = *reinterpret_cast<const f32x4 *>(adw + 3 * CQ + 4 * g4);
+          const f32x4 v1 = *reinterpret_cast<const f32x4 *>(adw + 3 * CQ + 16 + 4 * g4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float keep = 4 * g4 + r <= c16 ? 1.f : 0.f;
+            g00[r] = z00[r] * (u0 * v0[r] * keep);
+            g11[r] = z11[r] * (u1 * v1[r] * keep);
+            g01[r] = z01[r] * (u1 * v0[r]);
+          }
+        } else {
+          const f32x4 bs0 = *reinterpret_cast<const f32x4 *>(adw + CQ + 4 * g4);
+          const f32x4 bs1 = *reinterpret_cast<const f32x4 *>(adw + CQ + 16 + 4 * g4);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float keep = 4 * g4 + r <= c16 ? 1.f : 0.f;
+            // for s > l the exponent may be large; min() keeps it finite so the
+            // 0 mask wins
+            g00[r] = z00[r] * (exp2_fast(fminf(al0 + bs0[r], 64.f)) * keep);
+            g11[r] = z11[r] * (exp2_fast(fminf(al1 + bs1[r], 64.f)) * keep);
+            g01[r] = z01[r] * exp2_fast(al1 + bs0[r]);
+          }
+        }
+        gop[0] = u32x4{pack_bf16x2(g00[0], g00[1]), pack_bf16x2(g00[2], g00[3]), 0u, 0u};
+        gop[1] = u32x4{pack_bf16x2(g01[0], g01[1]), pack_bf16x2(g01[2], g01[3]),
+                       pack_bf16x2(g11[0], g11[1]), pack_bf16x2(g11[2], g11[3])};
+      }
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt)
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) ya[pt][lt] = mfma16(xop[pt], gop[lt], ya[pt][lt]);
+#pragma unroll
+      for (int pt = 0; pt < PT; ++pt) {  // D x in fp32: rows p = 16 pt + 4 g4 + r of token l
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+          const int l = 16 * lt + c16, col = p0 + 16 * pt + 4 * g4;
+          const u32x2 v = *reinterpret_cast<const u32x2 *>(
+              xh + l * 128 + (((col >> 3) ^ rot_swz<8>(l)) << 4) + (col & 7) * 2);
+          ya[pt][lt].x += Dh * bf16lo(v.x);
+          ya[pt][lt].y += Dh * bf16hi(v.x);
+          ya[pt][lt].z += Dh * bf16lo(v.y);
+          ya[pt][lt].w += Dh * bf16hi(v.y);
+        }
+      }
+
     }
 
     // 3. state: h = exp(a_last) h + B^T (w x), as S = h / 2^lam: normally
@@ -490,6 +551,7 @@ void k_ssd_fused(
           for (int j = 0; j < NT; ++j) hst[pt][j] *= e;
       }
       lam = steep ? 0.f : lam + a2last;
+      if (ST) lsum += a2last;
       const f32x4 w0 = *reinterpret_cast<const f32x4 *>(adw + 2 * CQ + 4 * g4);
       const f32x4 w1 = *reinterpret_cast<const f32x4 *>(adw + 2 * CQ + 16 + 4 * g4);
       u32x4 xw[PT];
@@ -520,7 +582,7 @@ void k_ssd_fused(
 
     // y staged (bf16) over this wavefront's columns of the x tile, now fully read
 #pragma unroll
-    for (int pt = 0; pt < PT; ++pt) {
+    for (int pt = 0; pt < (ST ? 0 : PT); ++pt) {
 #pragma unroll
       for (int lt = 0; lt < 2; ++lt) {
         const int l = 16 * lt + c16, col = p0 + 16 * pt + 4 * g4;
@@ -530,20 +592,21 @@ void k_ssd_fused(
     }
     soff = soff == SLOTS - SLOT ? 0 : soff + SLOT;
   }
-  if (nck > 0) {
+  if (!ST && nck > 0) {
     wait_lgkmcnt0();
     __syncthreads();  // every wavefront's part of the last chunk's y is staged
     store_y(nck - 1, ((nck - 1) % R) * SLOT);
   }
-  if (hfin) {
+  if (hfp) {
     const float e = exp2_fast(lam);
 #pragma unroll
     for (int pt = 0; pt < PT; ++pt) {
-      const int64_t prow = (sh * P + p0 + 16 * pt + c16) * N;
+      const int64_t prow = (int64_t)(p0 + 16 * pt + c16) * N;
 #pragma unroll
-      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(hfin + prow + nrow(j)) = hst[pt][j] * e;
+      for (int j = 0; j < NT; ++j) *reinterpret_cast<f32x4 *>(hfp + prow + nrow(j)) = hst[pt][j] * e;
     }
   }
+  if (ST && pq == 0 && lane == 0) args.lseg[(int64_t)s * H + h] = lsum;
 }
 
 }  // namespace
@@ -553,33 +616,68 @@ bool fused_supported(int H, int P, int N, int G) {
 }
 
 namespace {
-template <int N, int HPB, int PW, int R, bool SAVE>
-void launch_fused_t(const uint16_t *x, const float *dt, const float *A, const uint16_t *B,
-                    const uint16_t *C, const float *D, const float *h0, const int32_t *cu, int64_t L,
-                    int64_t T, int rows, int H, int G, int hr, uint16_t *y, float *hfin,
-                    uint16_t *hsave, hipStream_t stream) {
-  hipLaunchKernelGGL((k_ssd_fused<N, HPB, PW, R, SAVE>), dim3(xcd_grid(rows, H / HPB)),
-                     dim3(FusedCfg<N, HPB, PW, R>::THREADS), 0, stream, x, dt, A, B, C, D, h0, cu,
-                     L, T, rows, H, G, hr, y, hfin, hsave);
+template <int N, int HPB, int PW, int R, int MODE>
+void launch_fused_t(const FusedArgs &a, hipStream_t stream) {
+  hipLaunchKernelGGL((k_ssd_fused<N, HPB, PW, R, MODE>), dim3(xcd_grid(a.rows, a.H / HPB)),
+                     dim3(FusedCfg<N, HPB, PW, R, MODE == kState>::THREADS), 0, stream, a);
 }
 
 // Instances: two heads a block (four wavefronts of 32 state rows, a three-slot
-// ring) where the heads of a group pair up and the (sequence, head pair)
-// blocks fill the GPU; else one head a block (two wavefronts, a two-slot ring,
-// up to three blocks a CU), which doubles the blocks of few long sequences.
-// N = 256 takes one head a block in four wavefronts of 16 rows (the state of
-// a wavefront stays at 64 registers).
-template <int N, bool SAVE>
-void launch_fused_n(int hpb, const uint16_t *x, const float *dt, const float *A,
-                    const uint16_t *B, const uint16_t *C, const float *D, const float *h0,
-                    const int32_t *cu, int64_t L, int64_t T, int rows, int H, int G, int hr,
-                    uint16_t *y, float *hfin, uint16_t *hsave, hipStream_t stream) {
+// ring) where the heads of a group pair up and the (row, head pair) blocks
+// fill the GPU, three where they divide by three and those fill it; else one
+// head a block (two wavefronts, a two-slot ring, up to three blocks a CU),
+// which doubles the blocks of few long sequences.  N = 256 takes one head a
+// block in four wavefronts of 16 rows (the state of a wavefront stays at 64
+// registers).
+template <int N, int MODE>
+void launch_fused_n(int hpb, const FusedArgs &a, hipStream_t stream) {
   if constexpr (N == 256) {
-    launch_fused_t<N, 1, 16, 2, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
+    launch_fused_t<N, 1, 16, 2, MODE>(a, stream);
   } else {
-    if (hpb == 3) launch_fused_t<N, 3, 32, 3, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
-    else if (hpb == 2) launch_fused_t<N, 2, 32, 3, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
-    else launch_fused_t<N, 1, 32, 2, SAVE>(x, dt, A, B, C, D, h0, cu, L, T, rows, H, G, hr, y, hfin, hsave, stream);
+    if (hpb == 3) launch_fused_t<N, 3, 32, 3, MODE>(a, stream);
+    else if (hpb == 2) launch_fused_t<N, 2, 32, 3, MODE>(a, stream);
+    else launch_fused_t<N, 1, 32, 2, MODE>(a, stream);
+  }
+}
+
+hipError_t launch_any(const FusedArgs &a, int N, int mode, hipStream_t stream) {
+  const int cus = device_cus();
+  const int HG = a.H / a.G;
+  const int hpb = HG % 3 == 0 && (int64_t)a.rows * (a.H / 3) >= cus ? 3
+                  : HG % 2 == 0 && (int64_t)a.rows * (a.H / 2) >= cus ? 2 : 1;
+#define SSD_FUSED_N(NN)                                                  \
+  if (mode == kFwdSave) launch_fused_n<NN, kFwdSave>(hpb, a, stream);    \
+  else if (mode == kState) launch_fused_n<NN, kState>(hpb, a, stream);   \
+  else launch_fused_n<NN, kFwd>(hpb, a, stream);
+  switch (N) {
+    case 64: SSD_FUSED_N(64) break;
+    case 128: SSD_FUSED_N(128) break;
+    default: SSD_FUSED_N(256) break;
+  }
+#undef SSD_FUSED_N
+  return hipGetLastError();
+}
+
+// Hand-off over the segments (the inter-chunk recurrence one level up): per
+// (sequence, kernel head) and 4 consecutive state elements a thread, the
+// state entering segment 0 (h0, or 0) into hbuf[sq][0], then
+// h <- 2^lseg[sq][j] h + hbuf[sq][j + 1] in place along j = 0 .. nseg-2, so
+// that hbuf[sq][j] ends as the state entering segment j.
+__global__ __launch_bounds__(256) void k_seg_pass(float *__restrict__ hbuf,
+                                                  const float *__restrict__ lseg,
+                                                  const float *__restrict__ h0, int nseq, int nseg,
+                                                  int H, int PN4) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // (sq, h, e4)
+  if (i >= (int64_t)nseq * H * PN4) return;
+  const int64_t e4 = i % PN4, sh = i / PN4;
+  const int64_t sq = sh / H, h = sh % H;
+  f32x4 v = h0 ? reinterpret_cast<const f32x4 *>(h0)[sh * PN4 + e4] : f32x4{};
+  f32x4 *hb = reinterpret_cast<f32x4 *>(hbuf) + (sq * nseg * H + h) * PN4 + e4;
+  *hb = v;
+  for (int j = 0; j + 1 < nseg; ++j) {
+    f32x4 *p = hb + (int64_t)(j + 1) * H * PN4;
+    v = v * __builtin_amdgcn_exp2f(lseg[(sq * (nseg - 1) + j) * H + h]) + *p;
+    *p = v;
   }
 }
 }  // namespace
@@ -590,25 +688,76 @@ hipError_t launch_fused(const void *x, const float *dt, const float *A, const vo
                         void *hsave, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
   if (!fused_supported(H, P, N, G) || hr < 1 || H % hr != 0) return hipErrorInvalidValue;
-  const uint16_t *xi = static_cast<const uint16_t *>(x);
-  const uint16_t *bi = static_cast<const uint16_t *>(B);
-  const uint16_t *ci = static_cast<const uint16_t *>(C);
-  uint16_t *yo = static_cast<uint16_t *>(y);
-  uint16_t *hs = static_cast<uint16_t *>(hsave);
-  const int cus = device_cus();
-  const int HG = H / G;
-  const int hpb = HG % 3 == 0 && (int64_t)rows * (H / 3) >= cus ? 3
-                  : HG % 2 == 0 && (int64_t)rows * (H / 2) >= cus ? 2 : 1;
-#define SSD_FUSED_N(NN)                                                                           \
-  if (hs) launch_fused_n<NN, true>(hpb, xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, hr, yo, hfin, hs, stream); \
-  else launch_fused_n<NN, false>(hpb, xi, dt, A, bi, ci, D, h0, cu, L, T, rows, H, G, hr, yo, hfin, hs, stream);
-  switch (N) {
-    case 64: SSD_FUSED_N(64) break;
-    case 128: SSD_FUSED_N(128) break;
-    default: SSD_FUSED_N(256) break;
+  FusedArgs a{};
+  a.x = static_cast<const uint16_t *>(x);
+  a.dt = dt;
+  a.A = A;
+  a.B = static_cast<const uint16_t *>(B);
+  a.C = static_cast<const uint16_t *>(C);
+  a.D = D;
+  a.h0 = h0;
+  a.cu = cu;
+  a.L = L;
+  a.T = T;
+  a.S = L;
+  a.nsr = 1;
+  a.rows = rows;
+  a.H = H;
+  a.G = G;
+  a.hr = hr;
+  a.y = static_cast<uint16_t *>(y);
+  a.hfin = hfin;
+  a.hsave = static_cast<uint16_t *>(hsave);
+  return launch_any(a, N, hsave ? kFwdSave : kFwd, stream);
+}
+
+hipError_t launch_fused_split(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *h0, int64_t L,
+                              int nseq, int64_t S, int H, int P, int N, int G, int hr, void *y,
+                              float *hfin, float *sseg, float *lseg, hipStream_t stream) {
+  if (nseq == 0 || L == 0) return hipSuccess;
+  if (!fused_supported(H, P, N, G) || hr < 1 || H % hr != 0 || S <= 0 || S % 32 != 0)
+    return hipErrorInvalidValue;
+  const int nseg = static_cast<int>((L + S - 1) / S);
+  FusedArgs a{};
+  a.x = static_cast<const uint16_t *>(x);
+  a.dt = dt;
+  a.A = A;
+  a.B = static_cast<const uint16_t *>(B);
+  a.C = static_cast<const uint16_t *>(C);
+  a.D = D;
+  a.L = L;
+  a.T = L * nseq;
+  a.S = S;
+  a.H = H;
+  a.G = G;
+  a.hr = hr;
+  hipError_t e;
+  if (nseg > 1) {
+    // 1. every segment but the last, from a zero state: its end state and decay
+    a.nsr = nseg - 1;
+    a.rows = nseq * (nseg - 1);
+    a.sseg = sseg;
+    a.lseg = lseg;
+    if ((e = launch_any(a, N, kState, stream)) != hipSuccess) return e;
+    // 2. the states entering the segments (so that step 3 does not read h0,
+    // which final_state may alias)
+    const int PN4 = P * N / 4;
+    const int64_t n = (int64_t)nseq * H * PN4;
+    hipLaunchKernelGGL(k_seg_pass, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, sseg,
+                       lseg, h0, nseq, nseg, H, PN4);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-#undef SSD_FUSED_N
-  return hipGetLastError();
+  // 3. every segment from its entering state: y, and the final state
+  a.nsr = nseg;
+  a.rows = nseq * nseg;
+  a.h0 = h0;
+  a.hin = nseg > 1 ? sseg : nullptr;
+  a.sseg = nullptr;
+  a.lseg = nullptr;
+  a.y = static_cast<uint16_t *>(y);
+  a.hfin = hfin;
+  return launch_any(a, N, kFwd, stream);
 }
 
 }  // namespace ssd

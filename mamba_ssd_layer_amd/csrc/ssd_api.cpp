@@ -566,6 +566,97 @@ ssd_status ssd_fused_fwd_train(const void *x, const float *dt, const float *A, c
                                       static_cast<hipStream_t>(stream)));
 }
 
+}  // extern "C"
+
+namespace {
+
+// The split one-pass forward: fixed-length sequences cut into segments of
+// seg_len tokens; its workspace holds the state entering every segment (fp32,
+// [nrows][nseg][H][P][N]) and, for every segment but the last, its log2 decay
+// (fp32, [nrows][nseg-1][H]).
+struct SplitWorkspace {
+  size_t sseg, lseg, total;
+  int64_t nseg;
+};
+
+SplitWorkspace split_workspace(const Plan &p, int64_t seg_len) {
+  SplitWorkspace w{};
+  w.nseg = ceil_div(p.geo.L, seg_len);
+  const int64_t nj = w.nseg > 1 ? w.nseg - 1 : 0;
+  if (nj == 0) return w;
+  const ssd::Geometry &g = p.geo;
+  w.sseg = 0;
+  w.lseg = align_up((size_t)g.nrows * w.nseg * g.H * g.P * g.N * 4);
+  w.total = w.lseg + align_up((size_t)g.nrows * nj * g.H * 4);
+  return w;
+}
+
+ssd_status make_split_plan(const ssd_dims *dims, int64_t seg_len, Plan *p) {
+  ssd_status s = make_fused_plan(dims, p);
+  if (s != SSD_OK) return s;
+  if (seg_len < 32 || seg_len % 32 != 0) return SSD_ERR_INVALID_ARG;
+  if (p->geo.packed) return SSD_ERR_UNSUPPORTED;
+  const int64_t nseg = ceil_div(p->geo.L, seg_len);
+  if (p->geo.nrows * nseg >= ((int64_t)1 << 24) / p->geo.H) return SSD_ERR_UNSUPPORTED;
+  return SSD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_fused_split_workspace_size(const ssd_dims *dims, int64_t seg_len) {
+  Plan p;
+  if (make_split_plan(dims, seg_len, &p) != SSD_OK) return 0;
+  return split_workspace(p, seg_len).total;
+}
+
+int64_t ssd_fused_split_seg_len(const ssd_dims *dims) {
+  Plan p;
+  if (make_fused_plan(dims, &p) != SSD_OK || p.geo.packed) return 0;
+  const ssd::Geometry &g = p.geo;
+  const int64_t L32 = ceil_div(g.L, 32) * 32;
+  const int64_t units = g.nrows * g.H, cus = ssd::device_cus();
+  if (L32 == 0 || units >= 2 * cus) return L32;  // enough (sequence, head) rows already
+  // about 8 (segment, head) rows a CU, segments a power of two of at least 512 tokens
+  const int64_t want = g.nrows * g.L * g.H / (8 * cus);
+  int64_t S = 512;
+  while (S * 2 <= want) S *= 2;
+  return S < L32 ? S : L32;
+}
+
+ssd_status ssd_fused_fwd_split(const void *x, const float *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *init_state, void *y,
+                               float *final_state, int64_t seg_len, const ssd_dims *dims,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  Plan p;
+  ssd_status s = make_split_plan(dims, seg_len, &p);
+  if (s != SSD_OK) return s;
+  if ((s = check_cumsum_args(dt, A, nullptr, p)) != SSD_OK) return s;
+  if ((s = check_state_args(x, B, p)) != SSD_OK) return s;
+  if ((s = check_pass_args(init_state, final_state, p)) != SSD_OK) return s;
+  if ((s = check_scan_args(x, B, C, D, y, dt, p)) != SSD_OK) return s;
+  const SplitWorkspace w = split_workspace(p, seg_len);
+  if (w.total > 0) {
+    if (!workspace || workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
+    if (!aligned(workspace, 256)) return SSD_ERR_INVALID_ARG;
+    const Sizes z = tensor_bytes(p);
+    if (overlaps(workspace, w.total, x, z.x) || overlaps(workspace, w.total, y, z.x) ||
+        overlaps(workspace, w.total, B, z.bc) || overlaps(workspace, w.total, C, z.bc) ||
+        overlaps(workspace, w.total, dt, z.dt) ||
+        overlaps(workspace, w.total, init_state, z.state) ||
+        overlaps(workspace, w.total, final_state, z.state))
+      return SSD_ERR_INVALID_ARG;
+  }
+  const ssd::Geometry &g = p.geo;
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  return hip_status(ssd::launch_fused_split(
+      x, dt, A, B, C, D, init_state, g.L, (int)g.nrows, seg_len, g.H, g.P, g.N, g.G, g.hr, y,
+      final_state, w.total ? reinterpret_cast<float *>(ws + w.sseg) : nullptr,
+      w.total ? reinterpret_cast<float *>(ws + w.lseg) : nullptr,
+      static_cast<hipStream_t>(stream)));
+}
+
 size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims) {
   Plan p;
   if (make_fused_plan(dims, &p) != SSD_OK || !bwd_supported(p)) return 0;

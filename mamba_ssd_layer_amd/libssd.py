@@ -66,6 +66,7 @@ EXPORTS = ["ssd_workspace_size", "ssd_get_workspace_layout", "ssd_chunk_scan_fwd
            "ssd_chunk_cumsum", "ssd_chunk_state", "ssd_state_passing", "ssd_chunk_scan",
            "ssd_step", "ssd_conv1d_silu", "ssd_gate_rmsnorm", "ssd_fused_fwd",
            "ssd_fused_fwd_train", "ssd_fused_states_size", "ssd_fused_bwd_workspace_size",
+           "ssd_fused_fwd_split", "ssd_fused_split_workspace_size", "ssd_fused_split_seg_len",
            "ssd_fused_bwd",
            "ssd_status_string", "ssd_version"]
 
@@ -106,6 +107,13 @@ def _load() -> ctypes.CDLL:
     lib.ssd_fused_fwd_train.argtypes = [p, p, p, p, p, p, p, p, p, p, p, sz, dims_p, p]
     lib.ssd_fused_states_size.restype = sz
     lib.ssd_fused_states_size.argtypes = [dims_p]
+    lib.ssd_fused_fwd_split.restype = i32
+    lib.ssd_fused_fwd_split.argtypes = [p, p, p, p, p, p, p, p, p, ctypes.c_int64, dims_p, p, sz,
+                                        p]
+    lib.ssd_fused_split_workspace_size.restype = sz
+    lib.ssd_fused_split_workspace_size.argtypes = [dims_p, ctypes.c_int64]
+    lib.ssd_fused_split_seg_len.restype = ctypes.c_int64
+    lib.ssd_fused_split_seg_len.argtypes = [dims_p]
     lib.ssd_fused_bwd_workspace_size.restype = sz
     lib.ssd_fused_bwd_workspace_size.argtypes = [dims_p]
     lib.ssd_fused_bwd.restype = i32
@@ -314,6 +322,29 @@ def ssd_fused_fwd(x, dt, A, B, C, D, init_state, cu_seqlens, y, final_state, dim
     px, pdt, pA, pB, pC, pD, py, phi, pcu, phf = _ptrs(*ts, hi, cu, hf)
     _check(_lib.ssd_fused_fwd(px, pdt, pA, pB, pC, pD, phi, pcu, py, phf, ctypes.byref(dims),
                               _stream(stream)))
+
+
+def ssd_fused_fwd_split(x, dt, A, B, C, D, init_state, y, final_state, seg_len, dims, workspace,
+                        stream=None) -> None:
+    if dims.nseq > 0:
+        raise SSDUnsupported(SSD_ERR_UNSUPPORTED, "the split forward takes fixed-length batches")
+    ts = _fwd(dims, x, dt, A, B, C, D, y, need=ALL)
+    hi, hf = _state(init_state, dims, "init_state"), _state(final_state, dims, "final_state")
+    need = ssd_fused_split_workspace_size(dims, seg_len)
+    ws = _t(workspace, torch.uint8, _bytes(workspace), "workspace", optional=need == 0)
+    if need and _bytes(ws) < need:
+        raise SSDWorkspaceError(SSD_ERR_WORKSPACE, f"workspace has {_bytes(ws)} bytes, needs {need}")
+    px, pdt, pA, pB, pC, pD, py, phi, phf, pws = _ptrs(*ts, hi, hf, ws)
+    _check(_lib.ssd_fused_fwd_split(px, pdt, pA, pB, pC, pD, phi, py, phf, int(seg_len),
+                                    ctypes.byref(dims), pws, _bytes(ws), _stream(stream)))
+
+
+def ssd_fused_split_workspace_size(dims, seg_len) -> int:
+    return int(_lib.ssd_fused_split_workspace_size(ctypes.byref(dims), int(seg_len)))
+
+
+def ssd_fused_split_seg_len(dims) -> int:
+    return int(_lib.ssd_fused_split_seg_len(ctypes.byref(dims)))
 
 
 def ssd_fused_states_size(dims) -> int:

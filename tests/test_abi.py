@@ -490,3 +490,50 @@ def test_noalloc_validates_before_any_hip_call():
     d.ngroups = 3
     assert noalloc(d) == SSD_ERR_UNSUPPORTED
 
+
+def _split_ws(b, L, H, P, N, S):
+    al = lambda v: (v + 255) // 256 * 256
+    nseg = -(-L // S)
+    if nseg <= 1:
+        return 0
+    hr = P // 64 if P % 64 == 0 else 1
+    Hk, Pk = H * hr, P // hr
+    return al(b * nseg * Hk * Pk * N * 4) + al(b * (nseg - 1) * Hk * 4)
+
+
+@pytest.mark.parametrize("case", [(1, 65536, 80, 64, 128, 1024), (8, 4096, 80, 64, 128, 1024),
+                                  (2, 1000, 4, 128, 64, 256), (3, 100, 2, 64, 256, 32),
+                                  (2, 500, 4, 64, 64, 512)])
+def test_split_workspace_size(case):
+    b, L_, H, P, N, S = case
+    d = make_dims(b, L_, H, P, N, 1, 0, SSD_BF16)
+    assert L.ssd_fused_split_workspace_size(ctypes.byref(d), S) == _split_ws(b, L_, H, P, N, S)
+
+
+def test_split_validates_before_any_hip_call():
+    v = ctypes.c_void_p
+    d = make_dims(2, 1000, 4, 64, 64, 1, 0, SSD_BF16)
+    dp = ctypes.byref(d)
+    need = L.ssd_fused_split_workspace_size(dp, 256)
+    args = lambda S, ws, wsb, y=FAKE + (3 << 30): L.ssd_fused_fwd_split(
+        v(FAKE), v(FAKE + (5 << 30)), v(FAKE + (6 << 30)), v(FAKE + (1 << 30)),
+        v(FAKE + (2 << 30)), None, None, v(y), None, S, dp, v(ws), wsb, None)
+    assert args(0, FAKE + (4 << 30), need) == SSD_ERR_INVALID_ARG      # seg_len 0
+    assert args(100, FAKE + (4 << 30), need) == SSD_ERR_INVALID_ARG    # not a multiple of 32
+    assert args(256, FAKE + (4 << 30), need - 1) == SSD_ERR_WORKSPACE  # too small
+    assert args(256, 0, need) == SSD_ERR_WORKSPACE                    # missing
+    assert args(256, FAKE + (4 << 30) + 16, need) == SSD_ERR_INVALID_ARG  # misaligned
+    assert args(256, FAKE + (4 << 30), need, y=FAKE) == SSD_ERR_INVALID_ARG  # y == x
+    assert args(256, FAKE, need) == SSD_ERR_INVALID_ARG                # workspace over x
+    # packed sequences are not split; f32 io and P 32 are outside the one-pass shapes
+    dpk = make_dims(1, 1000, 4, 64, 64, 1, 3, SSD_BF16)
+    assert L.ssd_fused_fwd_split(v(FAKE), v(FAKE + (5 << 30)), v(FAKE + (6 << 30)),
+                                 v(FAKE + (1 << 30)), v(FAKE + (2 << 30)), None, None,
+                                 v(FAKE + (3 << 30)), None, 256, ctypes.byref(dpk),
+                                 v(FAKE + (4 << 30)), 1 << 40, None) == SSD_ERR_UNSUPPORTED
+    for dd in (make_dims(2, 1000, 4, 64, 64, 1, 0, SSD_F32), make_dims(2, 1000, 4, 32, 64, 1, 0,
+                                                                       SSD_BF16)):
+        assert L.ssd_fused_fwd_split(v(FAKE), v(FAKE + (5 << 30)), v(FAKE + (6 << 30)),
+                                     v(FAKE + (1 << 30)), v(FAKE + (2 << 30)), None, None,
+                                     v(FAKE + (3 << 30)), None, 256, ctypes.byref(dd),
+                                     v(FAKE + (4 << 30)), 1 << 40, None) == SSD_ERR_UNSUPPORTED
