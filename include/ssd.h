@@ -85,13 +85,17 @@ typedef struct {
 } ssd_dims;
 
 /* Supported shapes.
- *   chunk_len Q in {64, 128, 256}; nheads a multiple of ngroups.
- *   SSD_BF16: headdim P in {64, 128, 192, 256}, dstate N in {64, 128, 256};
- *             all contractions on bf16 MFMA with fp32 accumulation; y rounded
- *             to nearest-even.  A head of P = 64 r runs as r kernel heads of
- *             64 state rows (rows p of the state never interact), which share
- *             the head's dt, A and D.
- *   SSD_F32:  headdim and dstate multiples of 16, at most 256; fp32 throughout.
+ *   chunk_len Q in {64, 128, 256}; nheads a multiple of ngroups; headdim and
+ *   dstate multiples of 16, at most 256.
+ *   SSD_BF16, headdim P in {64, 128, 192, 256} and dstate N in {64, 128,
+ *             256}: every contraction on bf16 MFMA with fp32 accumulation; y
+ *             rounded to nearest-even.  A head of P = 64 r runs as r kernel
+ *             heads of 64 state rows (rows p of the state never interact),
+ *             which share the head's dt, A and D.
+ *   SSD_BF16, other shapes: chunk_state and chunk_scan on the fp32 vector
+ *             ALU (bf16 widened exactly, fp32 arithmetic, chunk states and
+ *             hprev in bf16, y rounded to nearest-even) -- correct, not fast.
+ *   SSD_F32:  fp32 throughout, on the vector ALU.
  *   T, nseq and every sequence length below 2^31.
  * Anything else valid returns SSD_ERR_UNSUPPORTED. */
 

@@ -145,7 +145,7 @@ class SSDForward:
         runs as the r kernel heads h r .. h r + r - 1 (the same values)."""
         d, L, Q = self.dims, self.layout, self.chunk_len
         nc, H, P, N = L.nc_max, d.nheads, d.headdim, d.dstate
-        Hk = H * (P // 64) if d.io_dtype == SSD_BF16 else H  # kernel heads
+        Hk = (L.dtq_offset - L.acum_offset) // (nc * Q * 4) if nc else H  # kernel heads
         ws = self.workspace
         io = torch.bfloat16 if d.io_dtype == SSD_BF16 else torch.float32  # states and hprev
 

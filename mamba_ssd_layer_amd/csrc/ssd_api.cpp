@@ -24,6 +24,7 @@ struct Plan {
   ssd::Geometry geo;
   ssd_workspace_layout ws;
   bool bf16;
+  bool mfma;  // bf16 on the MFMA stage kernels (else the vector-ALU ones)
   size_t io_size;
 };
 
@@ -43,12 +44,13 @@ ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
   const int64_t Hd = d->nheads, Pd = d->headdim, N = d->dstate, G = d->ngroups;
   const bool bf16 = d->io_dtype == SSD_BF16;
   if (Pd % 16 != 0 || N % 16 != 0 || Pd > 256 || N > 256) return SSD_ERR_UNSUPPORTED;
-  // bf16: a head dim of 64 hr runs as hr kernel heads of 64 state rows
-  const int64_t hr = bf16 && Pd % 64 == 0 ? Pd / 64 : 1;
+  // bf16: a head dim of 64 hr runs as hr kernel heads of 64 state rows on the
+  // MFMA stage kernels; the other bf16 shapes (head dims not a multiple of 64,
+  // state sizes other than 64 / 128 / 256) run on the vector-ALU ones
+  const bool mfma = bf16 && Pd % 64 == 0 && ssd::chunk_state_bf16_supported(64, (int)N, chunk_len) &&
+                    ssd::chunk_scan_bf16_supported(64, (int)N, chunk_len);
+  const int64_t hr = mfma ? Pd / 64 : 1;
   const int64_t H = Hd * hr, P = Pd / hr;
-  if (bf16 && (!ssd::chunk_state_bf16_supported((int)P, (int)N, chunk_len) ||
-               !ssd::chunk_scan_bf16_supported((int)P, (int)N, chunk_len)))
-    return SSD_ERR_UNSUPPORTED;
   // grid limits: heads and rows sit on grid y / z (at most 65535)
   const int64_t nrows = d->nseq > 0 ? d->nseq : d->batch;
   if (H > 65535 || nrows > 65535) return SSD_ERR_UNSUPPORTED;
@@ -63,6 +65,7 @@ ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
 
   Plan p{};
   p.bf16 = bf16;
+  p.mfma = mfma;
   p.io_size = bf16 ? 2 : 4;
   ssd::Geometry &g = p.geo;
   g.tokens = T;
@@ -199,12 +202,9 @@ ssd_status run_state(const void *x, const void *B, const Plan &p, void *ws, hipS
   const float *acum = ws_ptr<float>(ws, p.ws.acum_offset);
   const float *dtq = ws_ptr<float>(ws, p.ws.dtq_offset);
   void *states = ws_ptr<void>(ws, p.ws.states_offset);
-  if (p.bf16)
+  if (p.mfma)
     return hip_status(ssd::launch_chunk_state_bf16(x, B, acum, dtq, states, p.geo, st));
-  return hip_status(ssd::launch_chunk_state_f32(static_cast<const float *>(x),
-                                                static_cast<const float *>(B), acum, dtq,
-                                                static_cast<float *>(states),
-                                                p.geo, st));
+  return hip_status(ssd::launch_chunk_state_vec(x, B, acum, dtq, states, p.bf16, p.geo, st));
 }
 
 ssd_status run_pass(const float *init, float *fin, const Plan &p, void *ws, hipStream_t st) {
@@ -218,11 +218,10 @@ ssd_status run_scan(const void *x, const void *B, const void *C, const float *D,
   const float *acum = ws_ptr<float>(ws, p.ws.acum_offset);
   const float *dtq = ws_ptr<float>(ws, p.ws.dtq_offset);
   const void *hprev = ws_ptr<void>(ws, p.ws.hprev_offset);
-  if (p.bf16)
+  if (p.mfma)
     return hip_status(ssd::launch_chunk_scan_bf16(x, B, C, D, acum, dtq, hprev, y, p.geo, st));
-  return hip_status(ssd::launch_chunk_scan_f32(
-      static_cast<const float *>(x), static_cast<const float *>(B), static_cast<const float *>(C),
-      D, acum, dtq, static_cast<const float *>(hprev), static_cast<float *>(y), p.geo, st));
+  return hip_status(
+      ssd::launch_chunk_scan_vec(x, B, C, D, acum, dtq, hprev, y, p.bf16, p.geo, st));
 }
 
 }  // namespace

@@ -43,13 +43,14 @@ bool chunk_scan_bf16_supported(int P, int N, int Q);
 hipError_t launch_chunk_scan_bf16(const void *x, const void *B, const void *C, const float *D,
                                   const float *acum, const float *dtq, const void *hprev, void *y,
                                   const Geometry &geo, hipStream_t stream);
-// fp32 io, fp32 vector-ALU contractions
-hipError_t launch_chunk_state_f32(const float *x, const float *B, const float *acum,
-                                  const float *dtq, float *states, const Geometry &geo,
+// fp32 vector-ALU contractions, for fp32 io and for the bf16 shapes the MFMA
+// kernels do not take (states / hprev in the io precision)
+hipError_t launch_chunk_state_vec(const void *x, const void *B, const float *acum,
+                                  const float *dtq, void *states, bool bf16, const Geometry &geo,
                                   hipStream_t stream);
-hipError_t launch_chunk_scan_f32(const float *x, const float *B, const float *C, const float *D,
-                                 const float *acum, const float *dtq, const float *hprev, float *y,
-                                 const Geometry &geo, hipStream_t stream);
+hipError_t launch_chunk_scan_vec(const void *x, const void *B, const void *C, const float *D,
+                                 const float *acum, const float *dtq, const void *hprev, void *y,
+                                 bool bf16, const Geometry &geo, hipStream_t stream);
 
 // single-token recurrent step (decode)
 bool step_supported(int N);

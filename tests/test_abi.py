@@ -69,6 +69,7 @@ def _ws_expected(batch, L_, H, P, N, G, Q, nseq=0, io=2):
     (1, 275772, 64, 64, 128, 8, 256, 64, SSD_BF16),
     (1, 256, 4, 16, 16, 1, 64, 0, SSD_F32),
     (3, 1000, 2, 64, 64, 2, 128, 0, SSD_BF16),
+    (2, 300, 4, 32, 48, 2, 64, 0, SSD_BF16),      # bf16 on the vector-ALU kernels
 ])
 def test_workspace_layout(case):
     b, L_, H, P, N, G, Q, nseq, io = case
@@ -116,9 +117,9 @@ def good():
     (dict(nseq=2), SSD_ERR_INVALID_ARG),             # packed needs batch == 1
     (dict(io_dtype=7), SSD_ERR_INVALID_ARG),
     (dict(reserved=1), SSD_ERR_INVALID_ARG),
-    (dict(headdim=32), SSD_ERR_UNSUPPORTED),          # bf16 path compiled for P = 64
     (dict(headdim=72), SSD_ERR_UNSUPPORTED),          # not a multiple of 16
-    (dict(dstate=48), SSD_ERR_UNSUPPORTED),
+    (dict(headdim=272), SSD_ERR_UNSUPPORTED),         # above 256
+    (dict(dstate=40), SSD_ERR_UNSUPPORTED),
     (dict(dstate=512), SSD_ERR_UNSUPPORTED),
     (dict(nheads=70000, ngroups=1), SSD_ERR_UNSUPPORTED),
 ])
@@ -128,6 +129,17 @@ def test_bad_dims(mut, expect):
         setattr(d, k, v)
     wsb = 1 << 40
     assert fwd(d, wsb=wsb) == expect
+
+
+@pytest.mark.parametrize("P,N", [(16, 16), (32, 64), (48, 128), (96, 32), (112, 256), (64, 48),
+                                 (128, 16), (240, 80)])
+def test_bf16_vector_path_shapes_are_accepted(P, N):
+    # bf16 head dims and state sizes outside the MFMA kernels' set (P a
+    # multiple of 64 with N in {64, 128, 256}) run on the vector-ALU stage
+    # kernels: every multiple of 16 up to 256 is a valid shape
+    d = make_dims(2, 300, 4, P, N, 2, 0, SSD_BF16)
+    for Q in (64, 128, 256):
+        assert L.ssd_workspace_size(ctypes.byref(d), Q) > 0
 
 
 @pytest.mark.parametrize("Q,expect", [(32, SSD_ERR_UNSUPPORTED), (100, SSD_ERR_UNSUPPORTED),
@@ -194,7 +206,7 @@ def test_per_stage_entry_points_validate():
 
 def test_layout_rejects_like_fwd():
     d = good()
-    d.headdim = 48
+    d.headdim = 56  # not a multiple of 16
     with pytest.raises(libssd.SSDUnsupported):
         libssd.ssd_get_workspace_layout(d, 256)
     assert libssd.ssd_workspace_size(d, 256) == 0

@@ -105,6 +105,25 @@ def test_head_dims(P, chunk):
     check_full(w, y, fin, label=f"P{P} Q{chunk}")
 
 
+@pytest.mark.parametrize("P,N,chunk", [(32, 64, 64), (16, 16, 128), (48, 128, 256), (96, 32, 64),
+                                       (64, 48, 128), (112, 256, 256)])
+def test_bf16_vector_path_shapes(P, N, chunk):
+    # bf16 shapes outside the MFMA kernels' set run on the vector-ALU stage
+    # kernels (bf16 in, fp32 arithmetic, states and hprev in bf16, y rounded):
+    # ragged tail, two groups, nonzero initial state
+    w = workloads.make_custom(2, 333, 4, P, N, 2, chunk, "bf16", seed=280 + P + N + chunk,
+                              init_std=0.2)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label=f"bf16 vector path P{P} N{N} Q{chunk}")
+
+
+def test_bf16_vector_path_packed():
+    lens = [100, 0, 257, 1, 64, 300]
+    w = workloads.make_custom(1, 0, 4, 32, 64, 2, 64, "bf16", seed=290, lens=lens, init_std=0.3)
+    y, fin, _, _ = run(w)
+    check_full(w, y, fin, label="bf16 vector path P32 packed")
+
+
 def test_block_example_shape():
     # the gated Mamba-2 block of the architecture page's Step 2: model width
     # 512, expansion 2, 8 heads -> head dim 128, state 128

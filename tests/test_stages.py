@@ -27,6 +27,9 @@ CASES = {
     "packed_bf16": dict(batch=1, seqlen=0, nheads=4, headdim=64, dstate=64, ngroups=4,
                         chunk=128, dtype="bf16", seed=3, init_std=0.3,
                         lens=[5, 300, 0, 128, 129, 1]),
+    # bf16 on the vector-ALU stage kernels (head dim 32, state 48)
+    "vector_bf16": dict(batch=2, seqlen=300, nheads=4, headdim=32, dstate=48, ngroups=2,
+                        chunk=128, dtype="bf16", seed=6, init_std=0.3),
     # head dim 128: each head runs as two kernel heads of 64 state rows
     "split_bf16": dict(batch=2, seqlen=333, nheads=2, headdim=128, dstate=64, ngroups=1,
                        chunk=64, dtype="bf16", seed=5, init_std=0.3),
