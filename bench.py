@@ -357,6 +357,55 @@ def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
     return res
 
 
+def training_step_general(torch, ssd, workloads, w, t, plan, steps: int, warmup: int):
+    """The training step where the fast backward does not take the shape (fp32
+    io, N = 256, head dims other than 64): the four-stage forward, then the
+    general backward (ssd_chunk_scan_bwd: the chunk states formed again, every
+    gradient on the vector ALU), each timed with HIP events on the launch
+    stream."""
+    dev = t["x"].device
+    dy, dfinal = workloads.make_output_grads(w, 6100)
+    dyd = torch.from_numpy(dy).to(dev).to(t["x"].dtype).view(t["x"].shape)
+    dfd = torch.from_numpy(dfinal).to(dev)
+    dims = ssd.dims_for(t["x"], t["B"], t["cu"])
+    ws = torch.empty(ssd.libssd.ssd_chunk_scan_bwd_workspace_size(dims), dtype=torch.uint8,
+                     device=dev)
+    y = torch.empty_like(t["x"])
+    fin = torch.empty_like(dfd)
+    stream = torch.cuda.current_stream()
+
+    def fwd():
+        plan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"], y=y,
+             final_state=fin)
+
+    def bwd():
+        ssd.chunk_scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], dyd, dfd,
+                           init_state=t["h0"], cu_seqlens=t["cu"], workspace=ws)
+
+    def timed(fn):
+        for _ in range(warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps * 1e3
+
+    fus, bus = timed(fwd), timed(bwd)
+    T = w.tokens
+    res = {"fwd_train_us": round(fus, 2), "fwd_train_path": "ssd_chunk_scan_fwd",
+           "bwd_path": "ssd_chunk_scan_bwd", "bwd_us": round(bus, 2),
+           "tokens_per_s": round(T / ((fus + bus) * 1e-6), 1),
+           "bwd_tokens_per_s": round(T / (bus * 1e-6), 1)}
+    log(f"bench: training step (general backward): forward {fus:.1f} us, backward {bus:.1f} us, "
+        f"{res['tokens_per_s'] / 1e6:.2f} M tokens/s")
+    return res
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -652,10 +701,12 @@ def main() -> int:
         decode = decode_step(torch, ssd, workloads, dev, args.steps, args.warmup)
 
     train = None
+    tens = {"x": x, "dt": dt, "A": A, "B": Bm, "C": Cm, "D": D, "h0": h0, "cu": cu}
     if fused is not None and not args.no_train and ssd.libssd.ssd_fused_bwd_workspace_size(dims) > 0:
-        train = training_step(torch, ssd, workloads, w,
-                              {"x": x, "dt": dt, "A": A, "B": Bm, "C": Cm, "D": D, "h0": h0,
-                               "cu": cu}, args.steps, args.warmup)
+        train = training_step(torch, ssd, workloads, w, tens, args.steps, args.warmup)
+    elif not args.no_train and ssd.libssd.ssd_chunk_scan_bwd_workspace_size(dims) > 0:
+        train = training_step_general(torch, ssd, workloads, w, tens, plan, args.steps,
+                                      args.warmup)
 
     block = None
     if not args.no_block:

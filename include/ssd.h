@@ -351,6 +351,39 @@ int64_t ssd_fused_split_seg_len(const ssd_dims *dims);
  * 0 if the dims are invalid or outside ssd_fused_fwd's shapes.  Host-only. */
 size_t ssd_fused_states_size(const ssd_dims *dims);
 
+/* Gradients of ssd_chunk_scan_fwd for every shape it takes (fp32 or bf16,
+ * head dims and state sizes multiples of 16 up to 256, fixed-length or packed
+ * batches): the chain rule through the recurrence (as ssd_fused_bwd below),
+ * evaluated blockwise in 64-token chunks on the fp32 vector ALU, with no
+ * saved states: it first runs the forward's chunk_cumsum, chunk_state and
+ * state_passing again into the workspace (the state entering every chunk),
+ * then the reverse hand-off of the state gradient from d(final_state) (the
+ * sums of exp(a_l) dy_l C_l^T per chunk), then every gradient per (chunk,
+ * group).  The general path: correct, not tuned; ssd_fused_bwd is the fast
+ * one where its shapes apply.
+ *   x, dt, A, B, C, D, init_state, cu_seqlens, dims: as for the forward;
+ *   dy   upstream gradient of y, like y;  dfinal: of final_state, fp32
+ *        [rows, H, P, N] 16-byte aligned, or NULL (zero);
+ *   dx   like x (io dtype);  ddt float [T, H];  dB, dC float [T, G, N]
+ *        (summed over the heads of a group);  dA float [H];  dD float [H],
+ *        NULL exactly when D is NULL;  dinit float [rows, H, P, N] or NULL.
+ * workspace: device memory of at least ssd_chunk_scan_bwd_workspace_size(dims)
+ * bytes (else SSD_ERR_WORKSPACE), 256-byte aligned.  Outputs overlap no input
+ * and no other output (else SSD_ERR_INVALID_ARG).  On `stream`: dA and dD are
+ * cleared and then added to with float atomics per (chunk, head), so they sum
+ * in an unspecified order; every other output is written once.  Returns after
+ * enqueueing. */
+ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *init_state,
+                              const int32_t *cu_seqlens, const void *dy, const float *dfinal,
+                              void *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                              float *dinit, const ssd_dims *dims, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of ssd_chunk_scan_bwd (0 if the dims are invalid or
+ * unsupported).  Host-only. */
+size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims *dims);
+
 /* Workspace bytes of ssd_fused_bwd: the gradient w.r.t. the state leaving
  * every 64-token pair (bf16, laid out like chunk_states) and, when the sweep
  * is split into segments (sequences x nheads / 2 < 256), two fp32 P x N tiles

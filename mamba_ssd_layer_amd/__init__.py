@@ -33,7 +33,7 @@ from .libssd import (SSD_BF16, SSD_F32, SSDError, SSDInvalidArgument, SSDUnsuppo
 __all__ = ["libssd", "chunk_scan_fwd", "SSDForward", "SSDTrainForward", "SSDError", "SSDInvalidArgument",
            "SSDUnsupported", "SSDWorkspaceError", "make_dims", "dims_for", "validate_cu_seqlens", "step",
            "conv1d_silu", "gate_rmsnorm", "fused_fwd", "fused_fwd_split", "fused_split_seg_len",
-           "make_fused_states", "fused_bwd"]
+           "make_fused_states", "fused_bwd", "chunk_scan_bwd"]
 
 
 def _io_dtype(t: torch.Tensor) -> int:
@@ -313,6 +313,39 @@ def fused_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
                          chunk_states.numel() * chunk_states.element_size(), dy, dfinal,
                          out["dx"], out["ddt"], out["dA"], out["dB"], out["dC"], out["dD"],
                          out["dinit"], dims, workspace, workspace.numel(), stream)
+    return out
+
+
+def chunk_scan_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tensor,
+                   C: torch.Tensor, D: Optional[torch.Tensor], dy: torch.Tensor,
+                   dfinal: Optional[torch.Tensor] = None,
+                   init_state: Optional[torch.Tensor] = None,
+                   cu_seqlens: Optional[torch.Tensor] = None, want_dinit: bool = True,
+                   workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of chunk_scan_fwd (ssd_chunk_scan_bwd: every shape the
+    forward takes, fp32 or bf16; no saved states, the chunk states are formed
+    again) for the loss sum <dy, y> + sum <dfinal, final_state>.  Returns the
+    same dict as fused_bwd (dx like x)."""
+    dims = dims_for(x, B, cu_seqlens)
+    if cu_seqlens is not None:
+        validate_cu_seqlens(cu_seqlens, dims.seqlen)
+    dev = x.device
+    nrows = dims.nseq if dims.nseq > 0 else dims.batch
+    if workspace is None:
+        n = libssd.ssd_chunk_scan_bwd_workspace_size(dims)
+        if n == 0:
+            raise SSDUnsupported(libssd.SSD_ERR_UNSUPPORTED, "shape outside the forward's")
+        workspace = torch.empty(n, dtype=torch.uint8, device=dev)
+    out = dict(dx=torch.empty_like(x), ddt=torch.empty(dt.shape, dtype=torch.float32, device=dev),
+               dA=torch.empty(dims.nheads, dtype=torch.float32, device=dev),
+               dB=torch.empty(B.shape, dtype=torch.float32, device=dev),
+               dC=torch.empty(C.shape, dtype=torch.float32, device=dev),
+               dD=torch.empty(dims.nheads, dtype=torch.float32, device=dev) if D is not None else None,
+               dinit=torch.empty((nrows, dims.nheads, dims.headdim, dims.dstate),
+                                 dtype=torch.float32, device=dev) if want_dinit else None)
+    libssd.ssd_chunk_scan_bwd(x, dt, A, B, C, D, init_state, cu_seqlens, dy, dfinal, out["dx"],
+                              out["ddt"], out["dA"], out["dB"], out["dC"], out["dD"],
+                              out["dinit"], dims, workspace, workspace.numel(), stream)
     return out
 
 

@@ -19,7 +19,7 @@ OBJDIR = os.path.join(HERE, "_build")
 
 SOURCES = ["ssd_api.cpp", "k_scan_prep.hip", "k_chunk_state.hip", "k_chunk_scan.hip", "k_f32.hip",
            "k_step.hip", "k_block.hip",
-           "k_fused.hip", "k_bwd.hip"]
+           "k_fused.hip", "k_bwd.hip", "k_bwd_vec.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

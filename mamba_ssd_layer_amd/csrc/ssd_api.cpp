@@ -29,7 +29,8 @@ struct Plan {
 };
 
 // Validates dims + chunk length and computes geometry and workspace layout.
-ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
+// vec: run every stage on the vector-ALU kernels (one kernel head per head)
+ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan, bool vec = false) {
   if (!d || !plan) return SSD_ERR_INVALID_ARG;
   if (d->reserved != 0) return SSD_ERR_INVALID_ARG;
   if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARG;
@@ -47,7 +48,8 @@ ssd_status make_plan(const ssd_dims *d, int chunk_len, Plan *plan) {
   // bf16: a head dim of 64 hr runs as hr kernel heads of 64 state rows on the
   // MFMA stage kernels; the other bf16 shapes (head dims not a multiple of 64,
   // state sizes other than 64 / 128 / 256) run on the vector-ALU ones
-  const bool mfma = bf16 && Pd % 64 == 0 && ssd::chunk_state_bf16_supported(64, (int)N, chunk_len) &&
+  const bool mfma = !vec && bf16 && Pd % 64 == 0 &&
+                    ssd::chunk_state_bf16_supported(64, (int)N, chunk_len) &&
                     ssd::chunk_scan_bf16_supported(64, (int)N, chunk_len);
   const int64_t hr = mfma ? Pd / 64 : 1;
   const int64_t H = Hd * hr, P = Pd / hr;
@@ -654,6 +656,89 @@ ssd_status ssd_fused_fwd_split(const void *x, const float *dt, const float *A, c
       final_state, w.total ? reinterpret_cast<float *>(ws + w.sseg) : nullptr,
       w.total ? reinterpret_cast<float *>(ws + w.lseg) : nullptr,
       static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"
+
+namespace {
+
+// The general backward: the forward's workspace at the vector path's chunk
+// length (acum, dtq, chunk states, hprev, chunk table), then per chunk and
+// head two fp32 P x N tiles: the dy C^T sums of the reverse hand-off, and the
+// state gradient entering each chunk from the right.
+struct VecBwdWorkspace {
+  size_t rsum, ge, total;
+};
+
+VecBwdWorkspace vec_bwd_workspace(const Plan &p) {
+  VecBwdWorkspace w{};
+  const size_t tile = (size_t)p.ws.nc_max * p.geo.H * p.geo.P * p.geo.N * 4;
+  w.rsum = align_up(p.ws.total_bytes);
+  w.ge = w.rsum + align_up(tile);
+  w.total = w.ge + align_up(tile);
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims *dims) {
+  Plan p;
+  if (make_plan(dims, ssd::bwd_vec_chunk_len(), &p, true) != SSD_OK) return 0;
+  return vec_bwd_workspace(p).total;
+}
+
+ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *init_state,
+                              const int32_t *cu_seqlens, const void *dy, const float *dfinal,
+                              void *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                              float *dinit, const ssd_dims *dims, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+  Plan p;
+  ssd_status s = make_plan(dims, ssd::bwd_vec_chunk_len(), &p, true);
+  if (s != SSD_OK) return s;
+  if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
+  if ((s = check_scan_args(x, B, C, D, dy, dt, p)) != SSD_OK) return s;
+  if ((s = check_pass_args(init_state, nullptr, p)) != SSD_OK) return s;
+  if (!tok_ptr_ok(dx, p, 16) || !tok_ptr_ok(ddt, p, 4) || !tok_ptr_ok(dB, p, 16) ||
+      !tok_ptr_ok(dC, p, 16))
+    return SSD_ERR_INVALID_ARG;
+  if (!dA || !aligned(dA, 4) || (dD && !aligned(dD, 4))) return SSD_ERR_INVALID_ARG;
+  if ((dD != nullptr) != (D != nullptr)) return SSD_ERR_INVALID_ARG;
+  if ((dfinal && !aligned(dfinal, 16)) || (dinit && !aligned(dinit, 16))) return SSD_ERR_INVALID_ARG;
+  const VecBwdWorkspace vw = vec_bwd_workspace(p);
+  if (!workspace || workspace_bytes < vw.total) return SSD_ERR_WORKSPACE;
+  // (binds the packed batch's chunk table and directory in the workspace)
+  if ((s = bind_workspace(&p, workspace, workspace_bytes)) != SSD_OK) return s;
+  // outputs overlap no input and no other output
+  const Sizes z = tensor_bytes(p);
+  const ssd::Geometry &g = p.geo;
+  const size_t bbc32 = (size_t)g.tokens * g.G * g.N * 4, bh = (size_t)g.H * 4;
+  const void *ins[] = {x, dt, A, B, C, D, init_state, dy, dfinal, workspace};
+  const size_t insz[] = {z.x, z.dt, bh, z.bc, z.bc, bh, z.state, z.x, z.state, vw.total};
+  const void *outs[] = {dx, ddt, dA, dB, dC, dD, dinit};
+  const size_t outsz[] = {z.x, z.dt, bh, bbc32, bbc32, bh, z.state};
+  for (int i = 0; i < 7; ++i) {
+    for (int j = 0; j < 10; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return SSD_ERR_INVALID_ARG;
+    for (int j = i + 1; j < 7; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return SSD_ERR_INVALID_ARG;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  // the forward's chunk states again (the state entering every chunk)
+  if ((s = run_cumsum(dt, A, cu_seqlens, p, workspace, st)) != SSD_OK) return s;
+  if ((s = run_state(x, B, p, workspace, st)) != SSD_OK) return s;
+  if ((s = run_pass(init_state, nullptr, p, workspace, st)) != SSD_OK) return s;
+  hipError_t e = ssd::launch_fill_f32(dA, g.H, st);
+  if (e == hipSuccess && dD) e = ssd::launch_fill_f32(dD, g.H, st);
+  if (e == hipSuccess)
+    e = ssd::launch_bwd_vec(x, A, B, C, D, dy, dfinal, ws_ptr<float>(workspace, p.ws.acum_offset),
+                            ws_ptr<float>(workspace, p.ws.dtq_offset),
+                            ws_ptr<void>(workspace, p.ws.hprev_offset),
+                            ws_ptr<float>(workspace, vw.rsum), ws_ptr<float>(workspace, vw.ge),
+                            p.bf16, g, dx, ddt, dA, dB, dC, dD, dinit, st);
+  return hip_status(e);
 }
 
 size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims) {

@@ -98,6 +98,18 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
                             float *dB, float *dC, float *dD, hipStream_t stream);
 hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t stream);
 
+// the general backward on the vector ALU, from the forward's workspace at chunk
+// length bwd_vec_chunk_len() (acum, dtq, hprev in the io precision): the dy C^T
+// sums per chunk into R, the state gradient entering every chunk from the
+// right into GE (fp32 [nc][H][P][N] each) and d(init_state), then every
+// gradient per (chunk, group); dA and dD must be zeroed before
+int bwd_vec_chunk_len();
+hipError_t launch_bwd_vec(const void *x, const float *A, const void *B, const void *C,
+                          const float *D, const void *dy, const float *dfinal, const float *acum,
+                          const float *dtq, const void *hprev, float *R, float *GE, bool bf16,
+                          const Geometry &geo, void *dx, float *ddt, float *dA, float *dB,
+                          float *dC, float *dD, float *dinit, hipStream_t stream);
+
 // Compute units of the current device (cached per device).
 inline int device_cus() {
   static int cache[64];

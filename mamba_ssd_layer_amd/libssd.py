@@ -67,6 +67,7 @@ EXPORTS = ["ssd_workspace_size", "ssd_get_workspace_layout", "ssd_chunk_scan_fwd
            "ssd_step", "ssd_conv1d_silu", "ssd_gate_rmsnorm", "ssd_fused_fwd",
            "ssd_fused_fwd_train", "ssd_fused_states_size", "ssd_fused_bwd_workspace_size",
            "ssd_fused_fwd_split", "ssd_fused_split_workspace_size", "ssd_fused_split_seg_len",
+           "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
            "ssd_fused_bwd",
            "ssd_status_string", "ssd_version"]
 
@@ -114,6 +115,10 @@ def _load() -> ctypes.CDLL:
     lib.ssd_fused_split_workspace_size.argtypes = [dims_p, ctypes.c_int64]
     lib.ssd_fused_split_seg_len.restype = ctypes.c_int64
     lib.ssd_fused_split_seg_len.argtypes = [dims_p]
+    lib.ssd_chunk_scan_bwd.restype = i32
+    lib.ssd_chunk_scan_bwd.argtypes = [p] * 17 + [dims_p, p, sz, p]
+    lib.ssd_chunk_scan_bwd_workspace_size.restype = sz
+    lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [dims_p]
     lib.ssd_fused_bwd_workspace_size.restype = sz
     lib.ssd_fused_bwd_workspace_size.argtypes = [dims_p]
     lib.ssd_fused_bwd.restype = i32
@@ -384,6 +389,30 @@ def ssd_fused_bwd(x, dt, A, B, C, D, cu_seqlens, chunk_states, states_bytes, dy,
     _check(_lib.ssd_fused_bwd(px, pdt, pA, pB, pC, pD, pcu, pcs, int(states_bytes), pdy, pdf, pdx,
                               pddt, pdA, pdB, pdC, pdD, pdi, ctypes.byref(dims), pws,
                               int(workspace_bytes), _stream(stream)))
+
+
+def ssd_chunk_scan_bwd_workspace_size(dims) -> int:
+    return int(_lib.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(dims)))
+
+
+def ssd_chunk_scan_bwd(x, dt, A, B, C, D, init_state, cu_seqlens, dy, dfinal, dx, ddt, dA, dB, dC,
+                       dD, dinit, dims, workspace, workspace_bytes, stream=None) -> None:
+    x, dt, A, B, C, D, _ = _fwd(dims, x, dt, A, B, C, D, need=("x", "dt", "A", "B", "C"))
+    T, H, P, N, G, rows = _sizes(dims)
+    io, f32 = _io_torch(dims), torch.float32
+    hi = _state(init_state, dims, "init_state")
+    outs = (_t(dy, io, T * H * P, "dy"), _state(dfinal, dims, "dfinal"),
+            _t(dx, io, T * H * P, "dx"), _t(ddt, f32, T * H, "ddt"), _t(dA, f32, H, "dA"),
+            _t(dB, f32, T * G * N, "dB"), _t(dC, f32, T * G * N, "dC"),
+            _t(dD, f32, H, "dD", optional=True), _state(dinit, dims, "dinit"))
+    if int(workspace_bytes) > _bytes(workspace):
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "byte count exceeds its buffer")
+    cu = _cu(cu_seqlens, dims)
+    (px, pdt, pA, pB, pC, pD, phi, pcu, pdy, pdf, pdx, pddt, pdA, pdB, pdC, pdD, pdi,
+     pws) = _ptrs(x, dt, A, B, C, D, hi, cu, *outs, workspace)
+    _check(_lib.ssd_chunk_scan_bwd(px, pdt, pA, pB, pC, pD, phi, pcu, pdy, pdf, pdx, pddt, pdA,
+                                   pdB, pdC, pdD, pdi, ctypes.byref(dims), pws,
+                                   int(workspace_bytes), _stream(stream)))
 
 
 def check_cu_seqlens(cu_host, T: int) -> None:

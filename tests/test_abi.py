@@ -549,3 +549,49 @@ def test_split_validates_before_any_hip_call():
                                      v(FAKE + (1 << 30)), v(FAKE + (2 << 30)), None, None,
                                      v(FAKE + (3 << 30)), None, 256, ctypes.byref(dd),
                                      v(FAKE + (4 << 30)), 1 << 40, None) == SSD_ERR_UNSUPPORTED
+
+
+def _gbwd_ws(b, L_, H, P, N, G, nseq, io):
+    al = lambda v: (v + 255) // 256 * 256
+    nc, fwd_total = _ws_expected(b, L_, H, P, N, G, 64, nseq, io)
+    tile = al(nc * H * P * N * 4)
+    return al(fwd_total) + 2 * tile
+
+
+@pytest.mark.parametrize("case", [(1, 256, 4, 16, 16, 1, 0, SSD_F32), (2, 1000, 4, 64, 256, 2, 0, SSD_BF16),
+                                  (1, 700, 4, 32, 64, 2, 6, SSD_BF16), (8, 4096, 80, 64, 128, 1, 0, SSD_BF16)])
+def test_general_bwd_workspace_size(case):
+    b, L_, H, P, N, G, nseq, io = case
+    d = make_dims(b, L_, H, P, N, G, nseq, io)
+    got = L.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(d))
+    assert got == _gbwd_ws(b, L_, H, P, N, G, nseq, 2 if io == SSD_BF16 else 4)
+
+
+def test_general_bwd_validates_before_any_hip_call():
+    v = ctypes.c_void_p
+    d = make_dims(2, 300, 4, 32, 48, 2, 0, SSD_BF16)
+    dp = ctypes.byref(d)
+    need = L.ssd_chunk_scan_bwd_workspace_size(dp)
+    assert need > 0
+    F = lambda k: v(FAKE + (k << 30))
+    base = dict(x=F(0), dt=F(1), A=F(2), B=F(3), C=F(4), D=None, init=None, cu=None, dy=F(5),
+                dfinal=None, dx=F(6), ddt=F(7), dA=F(8), dB=F(9), dC=F(10), dD=None, dinit=None,
+                ws=F(11), wsb=need)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return L.ssd_chunk_scan_bwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"],
+                                    a["cu"], a["dy"], a["dfinal"], a["dx"], a["ddt"], a["dA"],
+                                    a["dB"], a["dC"], a["dD"], a["dinit"], dp, a["ws"], a["wsb"],
+                                    None)
+    assert call(wsb=need - 1) == SSD_ERR_WORKSPACE
+    assert call(ws=None) == SSD_ERR_WORKSPACE
+    assert call(ws=v(FAKE + (11 << 30) + 64)) == SSD_ERR_INVALID_ARG   # misaligned
+    assert call(dx=None) == SSD_ERR_INVALID_ARG
+    assert call(dA=None) == SSD_ERR_INVALID_ARG
+    assert call(dD=F(12)) == SSD_ERR_INVALID_ARG                       # dD without D
+    assert call(dx=F(0)) == SSD_ERR_INVALID_ARG                        # dx over x
+    assert call(dB=F(10)) == SSD_ERR_INVALID_ARG                       # dB over dC
+    assert call(ws=F(6)) == SSD_ERR_INVALID_ARG                        # workspace over dx
+    bad = make_dims(2, 300, 4, 40, 48, 2, 0, SSD_BF16)                 # head dim 40
+    assert L.ssd_chunk_scan_bwd_workspace_size(ctypes.byref(bad)) == 0
