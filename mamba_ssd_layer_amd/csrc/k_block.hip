@@ -55,7 +55,11 @@ template <> struct Vec<float> {
   }
 };
 
-__device__ __forceinline__ float silu(float v) { return v / (1.f + __expf(-v)); }
+// SiLU with the hardware reciprocal (about 1 ulp) in place of an IEEE
+// division: the correctly rounded divide is a dozen vector instructions per
+// element and made the convolution VALU-bound (195 -> 154 us at 32,768 tokens
+// x 5376 channels); the result is rounded to bf16 or kept to ~1e-7 in fp32
+__device__ __forceinline__ float silu(float v) { return v * __builtin_amdgcn_rcpf(1.f + __expf(-v)); }
 
 constexpr int kConvRun = 16;  // tokens per thread
 
