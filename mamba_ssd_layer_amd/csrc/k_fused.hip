@@ -132,7 +132,7 @@ struct FusedCfg {
   static_assert(BCI >= 1 && NPC * 1024 == NBC * BT, "B and C in 1 KB pieces");
   static_assert(DTP <= WAVES, "a wavefront per dt piece");
   static constexpr int SVC = PT * N / 32;        // ... per saved chunk-start state
-  static_assert(R >= 2 && STC + (R - 2) * (LDC + 1 + STC + SVC) <= 47, "wait counts");
+  static_assert(R >= 2 && (R - 2) * (LDC + 1 + STC + SVC) <= 47, "wait counts");
   static_assert(BLOCKS_PER_CU >= 1 && WAVES_PER_SIMD >= 1, "occupancy");
 };
 
@@ -307,20 +307,17 @@ void k_ssd_fused(const FusedArgs args) {
     cg += CQ * ldb;
     dg += CQ * Hd;
   };
-  // rows XR pq .. XR pq + XR - 1 of head hh's y of a chunk, staged in the
-  // slot at byte offset soff: read into registers (read_y), then, once the
-  // slot's next loads are issued, written as STC row stores (write_y for
-  // chunk k)
-  auto read_y = [&](uint32_t soff, u32x4 (&v)[XI]) {
+  // rows XR pq .. XR pq + XR - 1 of head hh's y of chunk k (staged in the
+  // slot at byte offset soff): STC stores
+  auto store_y = [&](int k, uint32_t soff) {
+    const int rem = k == nck - 1 ? lastlen : CQ;
     const unsigned char *ys = smem + soff + OX + hh * XH;
+    u32x4 v[XI];
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
       const int m = i * 64 + lane, r = XR * pq + (m >> 3), cc = m & 7;
       v[i] = *reinterpret_cast<const u32x4 *>(ys + r * 128 + ((cc ^ rot_swz<8>(r)) << 4));
     }
-  };
-  auto write_y = [&](int k, const u32x4 (&v)[XI]) {
-    const int rem = k == nck - 1 ? lastlen : CQ;
     unsigned char *yb = reinterpret_cast<unsigned char *>(yg);  // wave-uniform
 #pragma unroll
     for (int i = 0; i < XI; ++i) {
@@ -369,23 +366,21 @@ void k_ssd_fused(const FusedArgs args) {
   for (int k = 0; k < nck; ++k) {
     // chunk k has landed once at most the ops this wavefront issued after its
     // loads are pending: loads of later chunks (prologue, then one chunk per
-    // iteration), the y stores of the iteration that issued chunk k and of
-    // those in between (and, when saving, the state stores of the even ones:
-    // SVC each)
-    if (STATIC_WAIT && k >= D + 1 && k + D <= nck) {
-      // steady state: iteration k - D issued STC stores after chunk k's
-      // loads, the last D - 1 iterations each one chunk load and STC stores
-      // (and, when saving, iteration k - 1 its state if even)
+    // iteration) and the y stores of the iterations in between
+    // (and, when saving, the state stores of the even ones: SVC each)
+    if (STATIC_WAIT && k >= D && k + D <= nck) {
+      // steady state: the last D - 1 iterations each issued STC stores and
+      // one chunk load (and, when saving, iteration k - 1 its state if even)
       const bool dtw = wave < F::DTP, sv = SAVE && D == 2 && !((k - 1) & 1);
       if (dtw) {
-        if (sv) wait_vmcnt<STC + (D - 1) * (STC + LD1) + SVC>();
-        else wait_vmcnt<STC + (D - 1) * (STC + LD1)>();
+        if (sv) wait_vmcnt<(D - 1) * (STC + LD1) + SVC>();
+        else wait_vmcnt<(D - 1) * (STC + LD1)>();
       } else {
-        if (sv) wait_vmcnt<STC + (D - 1) * (STC + LD0) + SVC>();
-        else wait_vmcnt<STC + (D - 1) * (STC + LD0)>();
+        if (sv) wait_vmcnt<(D - 1) * (STC + LD0) + SVC>();
+        else wait_vmcnt<(D - 1) * (STC + LD0)>();
       }
     } else {
-      int n = k < D ? (min(D, nck) - 1 - k) * ldc : (k - D >= 1 ? STC : 0);
+      int n = k < D ? (min(D, nck) - 1 - k) * ldc : 0;
       for (int j = k < D ? 0 : k - D + 1; j < k; ++j)
         n += (SAVE && !(j & 1) ? SVC : 0) + (j >= 1 ? STC : 0) + (j + D < nck ? ldc : 0);
       wait_vmcnt_dyn(n);
@@ -409,16 +404,8 @@ void k_ssd_fused(const FusedArgs args) {
       }
     }
     const uint32_t sprev = soff == 0 ? SLOTS - SLOT : soff - SLOT;  // chunk k-1's slot, and k+D's
-    // chunk k-1's y leaves its slot for registers before the slot's next
-    // loads are issued, and goes out after them, so that waiting for a
-    // chunk's loads never waits for the y stores issued just before them
-    u32x4 yv[XI];
-    if (!ST && k >= 1) {
-      read_y(sprev, yv);
-      wait_lgkmcnt0();
-    }
+    if (!ST && k >= 1) store_y(k - 1, sprev);
     if (k + D < nck) issue(k + D, sprev);
-    if (!ST && k >= 1) write_y(k - 1, yv);
 
     unsigned char *xh = smem + soff + OX + hh * XH;  // head hh's x tile (this wavefront: columns p0 ..)
     const unsigned char *bs = smem + soff + OB;
@@ -608,10 +595,7 @@ void k_ssd_fused(const FusedArgs args) {
   if (!ST && nck > 0) {
     wait_lgkmcnt0();
     __syncthreads();  // every wavefront's part of the last chunk's y is staged
-    u32x4 yv[XI];
-    read_y(((nck - 1) % R) * SLOT, yv);
-    wait_lgkmcnt0();
-    write_y(nck - 1, yv);
+    store_y(nck - 1, ((nck - 1) % R) * SLOT);
   }
   if (hfp) {
     const float e = exp2_fast(lam);
