@@ -35,17 +35,31 @@ namespace {
 
 constexpr int kVT = 256;    // threads a block
 constexpr int kVQ = 64;     // chunk length of this path
-constexpr int kTB = 8;      // tokens a thread takes together (operands loaded once for them)
 
-__device__ __forceinline__ float vld(const float *p) { return *p; }
-__device__ __forceinline__ float vld(const uint16_t *p) { return __uint_as_float((uint32_t)*p << 16); }
-__device__ __forceinline__ void vst(float *p, float v) { *p = v; }
-__device__ __forceinline__ void vst(uint16_t *p, float v) {
-  *p = static_cast<uint16_t>(pack_bf16x2(v, 0.f) & 0xffffu);
+// 4 consecutive elements of an io tensor as floats (one 16-byte fp32 or
+// 8-byte bf16 load; the offsets used here are multiples of 4 elements of rows
+// whose lengths are multiples of 16), and the matching store
+__device__ __forceinline__ void ld4(const float *p, float (&v)[4]) {
+  const f32x4 q = *reinterpret_cast<const f32x4 *>(p);
+  v[0] = q.x; v[1] = q.y; v[2] = q.z; v[3] = q.w;
+}
+__device__ __forceinline__ void ld4(const uint16_t *p, float (&v)[4]) {
+  const u32x2 q = *reinterpret_cast<const u32x2 *>(p);
+  v[0] = bf16lo(q.x); v[1] = bf16hi(q.x); v[2] = bf16lo(q.y); v[3] = bf16hi(q.y);
+}
+__device__ __forceinline__ void st4(float *p, const float (&v)[4]) {
+  *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
+}
+__device__ __forceinline__ void st4(uint16_t *p, const float (&v)[4]) {
+  *reinterpret_cast<u32x2 *>(p) = u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+}
+__device__ __forceinline__ float dot4(const float (&a)[4], const float (&b)[4]) {
+  return a[0] * b[0] + a[1] * b[1] + a[2] * b[2] + a[3] * b[3];
 }
 
-// R_c = sum_l e^{a_l} dy_l C_l^T per (chunk, head): block = (chunk, head),
-// thread = state elements (p, n).
+// R_c = sum_l e^{a_l} dy_l C_l^T per (chunk, head): block = (chunk, head);
+// each thread forms 4 x 4 tiles (p, n) of the P x N product over the chunk's
+// tokens from 4-element loads of dy and C.
 template <typename IO>
 __global__ __launch_bounds__(kVT) void k_bwd_rsum_vec(const IO *__restrict__ dy,
                                                      const IO *__restrict__ Cm,
@@ -64,11 +78,24 @@ __global__ __launch_bounds__(kVT) void k_bwd_rsum_vec(const IO *__restrict__ dy,
   const IO *yb = dy + ci.t0 * ldx + (int64_t)h * P;
   const IO *cb = Cm + ci.t0 * ldb + (int64_t)(h / (H / G)) * N;
   float *out = R + ch * (int64_t)P * N;
-  for (int e = threadIdx.x; e < P * N; e += kVT) {
-    const int p = e / N, n = e - p * N;
-    float acc = 0.f;
-    for (int l = 0; l < ci.len; ++l) acc += vld(yb + l * ldx + p) * sw[l] * vld(cb + l * ldb + n);
-    out[e] = acc;
+  const int N4 = N / 4, ntile = (P / 4) * N4;
+  for (int tile = threadIdx.x; tile < ntile; tile += kVT) {
+    const int p0 = 4 * (tile / N4), n0 = 4 * (tile % N4);
+    float acc[4][4] = {};
+    for (int l = 0; l < ci.len; ++l) {
+      float a[4], b[4];
+      ld4(yb + l * ldx + p0, a);
+      ld4(cb + l * ldb + n0, b);
+      const float w = sw[l];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float ai = a[i] * w;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[i][k] += ai * b[k];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) st4(out + (int64_t)(p0 + i) * N + n0, acc[i]);
   }
 }
 
@@ -96,10 +123,14 @@ __global__ __launch_bounds__(kVT) void k_bwd_pass_vec(const float *__restrict__ 
   if (dinit) *reinterpret_cast<f32x4 *>(dinit + soff) = ge;
 }
 
-// Per (chunk, group): Z once, then per head of the group E, the per-token
-// scalars and dx, ddt; dB and dC summed over the heads (each of their elements
+// Per (chunk, group): Z once, then per head of the group E, dx, dB, dC and the
+// per-token scalars; dB and dC summed over the heads (each of their elements
 // is owned by one thread of the one block of its chunk and group: the first
-// head writes it, the others add); dA and dD added atomically per head.
+// head writes it, the others add); dA and dD added atomically per head.  The
+// products over p, n and the chunk's tokens are formed in 4 x 4 register
+// tiles from 4-element loads (the chunk's rows of x, dy, B and C, and the
+// head's P x N tiles of the state and its gradient, are re-read from the
+// caches); the triangular 64 x 64 matrices live in LDS.
 template <typename IO>
 __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
     const IO *__restrict__ x, const float *__restrict__ A, const IO *__restrict__ Bm,
@@ -108,10 +139,10 @@ __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
     const float *__restrict__ GE, ChunkGeom geom, int H, int G, int P, int N,
     IO *__restrict__ dx, float *__restrict__ ddt, float *__restrict__ dA, float *__restrict__ dB,
     float *__restrict__ dC, float *__restrict__ dD) {
-  __shared__ float Z[kVQ][kVQ + 1];  // C_l . B_s (s <= l), the block's
-  __shared__ float E[kVQ][kVQ + 1];  // dy_l . x_s, then (dy_l . x_s) e^{a_l - a_s}
-  __shared__ float M[kVQ][kVQ + 1];  // (C_l . B_s) e^{a_l - a_s}
-  __shared__ float sa[kVQ], sd[kVQ], sq[kVQ], sv[kVQ];
+  __shared__ float Zs[kVQ][kVQ + 1];  // C_l . B_s on s <= l (0 elsewhere)
+  __shared__ float Es[kVQ][kVQ + 1];  // (dy_l . x_s) e^{a_l - a_s} on s <= l (0 elsewhere)
+  __shared__ float Ms[kVQ][kVQ + 1];  // (C_l . B_s) e^{a_l - a_s}; later prefix sums of K
+  __shared__ float sa[kVQ], sd[kVQ], sw[kVQ], sq[kVQ], sv[kVQ];
   __shared__ float red[3];  // <ge, h_s>, dA, dD of the head
   const int c = blockIdx.x, g = blockIdx.y;
   const ChunkInfo ci = chunk_info(geom, c);
@@ -123,13 +154,35 @@ __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
   const IO *bb = Bm + ci.t0 * ldb + (int64_t)g * N;
   const IO *cb = Cm + ci.t0 * ldb + (int64_t)g * N;
   const int64_t PN = (int64_t)P * N;
+  const int N4 = N / 4, P4 = P / 4, L4 = (len + 3) / 4;
+  // the 4 x 4 tile (l0.., s0..) of the 64 x 64 token matrices this thread forms
+  const int l0 = 4 * (tid >> 4), s0 = 4 * (tid & 15);
+  const bool tri = s0 <= l0 + 3 && l0 < len;  // the tile meets the chunk's lower triangle
+  auto row = [&](int t) { return min(t, len - 1); };  // rows past the end read the last one
 
-  for (int i = tid; i < len * len; i += kVT) {
-    const int l = i / len, s = i - l * len;
-    float z = 0.f;
-    if (s <= l)
-      for (int n = 0; n < N; ++n) z += vld(cb + l * ldb + n) * vld(bb + s * ldb + n);
-    Z[l][s] = z;
+  {  // Z = C B^T
+    float acc[4][4] = {};
+    if (tri) {
+      for (int n = 0; n < N; n += 4) {
+        float a[4][4], b[4][4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ld4(cb + row(l0 + i) * ldb + n, a[i]);
+          ld4(bb + row(s0 + i) * ldb + n, b[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) acc[i][k] += dot4(a[i], b[k]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int l = l0 + i, s = s0 + k;
+        Zs[l][s] = s <= l && l < len ? acc[i][k] : 0.f;
+      }
   }
   float *dBc = dB + ci.t0 * ldb + (int64_t)g * N;
   float *dCc = dC + ci.t0 * ldb + (int64_t)g * N;
@@ -143,122 +196,196 @@ __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
     const float *ge = GE + ch * PN;
     const float Ah = A[h];
     const float Dh = Dv ? Dv[h] : 0.f;
-    __syncthreads();  // the previous head is done with the tables, E and M
+    __syncthreads();  // the previous head is done with the tables, Es and Ms
     if (tid < kVQ) {
-      sa[tid] = acum[ch * kVQ + tid];
+      sa[tid] = acum[ch * kVQ + tid];  // past the chunk's end: its last value
       sd[tid] = tid < len ? dtq[ch * kVQ + tid] : 0.f;
       sq[tid] = 0.f;
       sv[tid] = 0.f;
     }
     if (tid < 3) red[tid] = 0.f;
-    for (int i = tid; i < len * len; i += kVT) {
-      const int l = i / len, s = i - l * len;
-      float e = 0.f;
-      if (s <= l)
-        for (int p = 0; p < P; ++p) e += vld(yb + l * ldx + p) * vld(xb + s * ldx + p);
-      E[l][s] = e;
-    }
     __syncthreads();
     const float alast = sa[kVQ - 1];
-    // the decay L_ls = e^{a_l - a_s} (s <= l) folded in: E <- E o L, M = Z o L
-    for (int i = tid; i < len * len; i += kVT) {
-      const int l = i / len, s = i - l * len;
-      const float dec = s <= l ? __expf(sa[l] - sa[s]) : 0.f;
-      E[l][s] *= dec;
-      M[l][s] = Z[l][s] * dec;
+    if (tid < kVQ) sw[tid] = __expf(alast - sa[tid]);
+    {  // E = dy x^T, with the decay L_ls = e^{a_l - a_s} folded in; M = Z o L
+      float acc[4][4] = {};
+      if (tri) {
+        for (int p = 0; p < P; p += 4) {
+          float a[4][4], b[4][4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ld4(yb + row(l0 + i) * ldx + p, a[i]);
+            ld4(xb + row(s0 + i) * ldx + p, b[i]);
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) acc[i][k] += dot4(a[i], b[k]);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int l = l0 + i, s = s0 + k;
+          const float dec = s <= l && l < len ? __expf(sa[l] - sa[s]) : 0.f;
+          Es[l][s] = acc[i][k] * dec;
+          Ms[l][s] = Zs[l][s] * dec;
+        }
     }
-    // <ge, h_s>
-    {
+    {  // <ge, h_s>
       float part = 0.f;
-      for (int64_t e = tid; e < PN; e += kVT) part += ge[e] * vld(hs + e);
+      for (int64_t e = 4 * (int64_t)tid; e < PN; e += 4 * kVT) {
+        float a[4], b[4];
+        ld4(ge + e, a);
+        ld4(hs + e, b);
+        part += dot4(a, b);
+      }
       atomicAdd(&red[0], part);
     }
     __syncthreads();
-    // (token block of kTB, n): dB and dC of this head, q_t and v_t partial sums;
-    // every operand loaded once per block of tokens
-    const int ntb = (len + kTB - 1) / kTB;
-    for (int i = tid; i < ntb * N; i += kVT) {
-      const int t0 = (i / N) * kTB, n = i % N;
-      float xge[kTB], dyh[kTB], sB[kTB], sC[kTB];
+    // (t, n) tiles: xge = x ge, dyh = dy h_s over p; sB = (E o L)^T C over
+    // l >= t; sC = (E o L) (dt B) over s <= t; then this head's dB, dC and
+    // the per-token q_t = sum_n xge B_t, v_t = sum_n dyh C_t
+    for (int tile = tid; tile < L4 * N4; tile += kVT) {
+      const int t0 = 4 * (tile / N4), n0 = 4 * (tile % N4);
+      float xg[4][4] = {}, dh[4][4] = {}, sB[4][4] = {}, sC[4][4] = {};
+      for (int p = 0; p < P; p += 4) {
+        float xa[4][4], ya[4][4], gv[4][4], hv[4][4];
 #pragma unroll
-      for (int k = 0; k < kTB; ++k) xge[k] = dyh[k] = sB[k] = sC[k] = 0.f;
-      for (int p = 0; p < P; ++p) {
-        const float gv = ge[(int64_t)p * N + n], hv = vld(hs + (int64_t)p * N + n);
+        for (int i = 0; i < 4; ++i) {
+          ld4(xb + row(t0 + i) * ldx + p, xa[i]);
+          ld4(yb + row(t0 + i) * ldx + p, ya[i]);
+          ld4(ge + (int64_t)(p + i) * N + n0, gv[i]);
+          ld4(hs + (int64_t)(p + i) * N + n0, hv[i]);
+        }
 #pragma unroll
-        for (int k = 0; k < kTB; ++k) {
-          const int t = min(t0 + k, len - 1);
-          xge[k] += vld(xb + t * ldx + p) * gv;
-          dyh[k] += vld(yb + t * ldx + p) * hv;
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k)
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+              xg[i][m] += xa[i][k] * gv[k][m];
+              dh[i][m] += ya[i][k] * hv[k][m];
+            }
+      }
+      for (int l = t0; l < len; ++l) {
+        float cv[4];
+        ld4(cb + l * ldb + n0, cv);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float e = Es[l][t0 + i];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) sB[i][m] += e * cv[m];
         }
       }
-      for (int l = t0; l < len; ++l) {  // sum over l >= t of (E o L)_lt C_l
-        const float cv = vld(cb + l * ldb + n);
+      const int se = min(t0 + 4, len);
+      for (int s = 0; s < se; ++s) {
+        float bv[4];
+        ld4(bb + s * ldb + n0, bv);
+        const float ds = sd[s];
 #pragma unroll
-        for (int k = 0; k < kTB; ++k)
-          if (t0 + k <= l) sB[k] += E[l][t0 + k] * cv;
+        for (int i = 0; i < 4; ++i) {
+          const float e = Es[t0 + i][s] * ds;
+#pragma unroll
+          for (int m = 0; m < 4; ++m) sC[i][m] += e * bv[m];
+        }
       }
-      for (int s = 0; s < min(t0 + kTB, len); ++s) {  // sum over s <= t of (E o L)_ts dt_s B_s
-        const float bv = sd[s] * vld(bb + s * ldb + n);
 #pragma unroll
-        for (int k = 0; k < kTB; ++k)
-          if (s <= t0 + k && t0 + k < len) sC[k] += E[t0 + k][s] * bv;
-      }
-#pragma unroll
-      for (int k = 0; k < kTB; ++k) {
-        const int t = t0 + k;
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + i;
         if (t >= len) break;
-        const float at = sa[t];
-        const float vb = sd[t] * (sB[k] + __expf(alast - at) * xge[k]);
-        const float vc = __expf(at) * dyh[k] + sC[k];
-        const int64_t o = (int64_t)t * ldb + n;
-        dBc[o] = j ? dBc[o] + vb : vb;
-        dCc[o] = j ? dCc[o] + vc : vc;
-        atomicAdd(&sq[t], xge[k] * vld(bb + t * ldb + n));
-        atomicAdd(&sv[t], dyh[k] * vld(cb + t * ldb + n));
+        const float ea = __expf(sa[t]);
+        float vb[4], vc[4], bt[4], ct[4];
+        ld4(bb + t * ldb + n0, bt);
+        ld4(cb + t * ldb + n0, ct);
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          vb[m] = sd[t] * (sB[i][m] + sw[t] * xg[i][m]);
+          vc[m] = ea * dh[i][m] + sC[i][m];
+        }
+        float *ob = dBc + (int64_t)t * ldb + n0, *oc = dCc + (int64_t)t * ldb + n0;
+        if (j) {
+          float pb[4], pc[4];
+          ld4(ob, pb);
+          ld4(oc, pc);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            vb[m] += pb[m];
+            vc[m] += pc[m];
+          }
+        }
+        st4(ob, vb);
+        st4(oc, vc);
+        atomicAdd(&sq[t], dot4(xg[i], bt));
+        atomicAdd(&sv[t], dot4(dh[i], ct));
       }
     }
-    // (token block of kTB, p): dx
-    for (int i = tid; i < ntb * P; i += kVT) {
-      const int t0 = (i / P) * kTB, p = i % P;
-      float sz[kTB], gb[kTB];
+    // (t, p) tiles: dx = D dy + dt (sz + e^{a_last - a_t} gb) with
+    // sz = (Z o L)^T dy over l >= t and gb = B ge^T over n
+    for (int tile = tid; tile < L4 * P4; tile += kVT) {
+      const int t0 = 4 * (tile / P4), p0 = 4 * (tile % P4);
+      float sz[4][4] = {}, gb[4][4] = {};
+      for (int l = t0; l < len; ++l) {
+        float yv[4];
+        ld4(yb + l * ldx + p0, yv);
 #pragma unroll
-      for (int k = 0; k < kTB; ++k) sz[k] = gb[k] = 0.f;
-      for (int l = t0; l < len; ++l) {  // sum over l >= t of (Z o L)_lt dy_l
-        const float yv = vld(yb + l * ldx + p);
+        for (int i = 0; i < 4; ++i) {
+          const float m = Ms[l][t0 + i];
 #pragma unroll
-        for (int k = 0; k < kTB; ++k)
-          if (t0 + k <= l) sz[k] += M[l][t0 + k] * yv;
+          for (int k = 0; k < 4; ++k) sz[i][k] += m * yv[k];
+        }
       }
-      for (int n = 0; n < N; ++n) {
-        const float gv = ge[(int64_t)p * N + n];
+      for (int n = 0; n < N; n += 4) {
+        float bt[4][4], gv[4][4];
 #pragma unroll
-        for (int k = 0; k < kTB; ++k) gb[k] += gv * vld(bb + min(t0 + k, len - 1) * ldb + n);
+        for (int i = 0; i < 4; ++i) {
+          ld4(bb + row(t0 + i) * ldb + n, bt[i]);
+          ld4(ge + (int64_t)(p0 + i) * N + n, gv[i]);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int k = 0; k < 4; ++k) gb[i][k] += dot4(bt[i], gv[k]);
       }
 #pragma unroll
-      for (int k = 0; k < kTB; ++k) {
-        const int t = t0 + k;
+      for (int i = 0; i < 4; ++i) {
+        const int t = t0 + i;
         if (t >= len) break;
-        vst(dx + (ci.t0 + t) * ldx + (int64_t)h * P + p,
-            Dh * vld(yb + t * ldx + p) + sd[t] * (sz[k] + __expf(alast - sa[t]) * gb[k]));
+        float yv[4], o[4];
+        ld4(yb + t * ldx + p0, yv);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) o[k] = Dh * yv[k] + sd[t] * (sz[i][k] + sw[t] * gb[i][k]);
+        st4(dx + (ci.t0 + t) * ldx + (int64_t)h * P + p0, o);
+      }
+    }
+    __syncthreads();  // sq, sv complete; Ms is free
+    // R_t = sum over l >= t > s of K_ls, K_ls = (E o L)_ls dt_s Z_ls: each row's
+    // exclusive prefix sums over s (Ms[l][t] = sum_{s<t} K_ls for t <= l) ...
+    if (tid < len) {
+      const int l = tid;
+      float run = 0.f;
+      for (int t = 0; t <= l; ++t) {
+        const float k = Es[l][t] * sd[t] * Zs[l][t];
+        Ms[l][t] = run;
+        run += k;
       }
     }
     __syncthreads();
-    // per token: ddt, and this head's dA and dD (E holds E o L, whose
-    // diagonal is E's)
+    // ... then per token t the sums down column t, and ddt, dA, dD
     if (tid < len) {
       const int t = tid;
-      const float at = sa[t];
       float term1 = 0.f, Rt = 0.f, Vt = 0.f, Ut = __expf(alast) * red[0];
       for (int l = t; l < len; ++l) {
-        term1 += E[l][t] * Z[l][t];
+        term1 += Es[l][t] * Zs[l][t];
+        Rt += Ms[l][t];
         Vt += __expf(sa[l]) * sv[l];
-        for (int s = 0; s < t; ++s) Rt += E[l][s] * sd[s] * Z[l][s];
       }
-      for (int s = 0; s < t; ++s) Ut += __expf(alast - sa[s]) * sd[s] * sq[s];
+      for (int s = 0; s < t; ++s) Ut += sw[s] * sd[s] * sq[s];
       const float w = Rt + Vt + Ut;
-      ddt[(ci.t0 + t) * (int64_t)H + h] = term1 + __expf(alast - at) * sq[t] + Ah * w;
+      ddt[(ci.t0 + t) * (int64_t)H + h] = term1 + sw[t] * sq[t] + Ah * w;
       atomicAdd(&red[1], sd[t] * w);
-      atomicAdd(&red[2], E[t][t]);
+      atomicAdd(&red[2], Es[t][t]);
     }
     __syncthreads();
     if (tid == 0) {

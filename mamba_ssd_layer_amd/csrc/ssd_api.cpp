@@ -670,6 +670,17 @@ struct VecBwdWorkspace {
   size_t rsum, ge, total;
 };
 
+// The general backward forms the chunk states again with the forward's stage
+// kernels at its 64-token chunks: bf16 with a 64-row head dim and a state size
+// the MFMA stage kernels take (one kernel head a head, so the layouts the
+// vector backward reads are the same) uses those; every other shape the
+// vector-ALU ones.
+ssd_status make_vec_bwd_plan(const ssd_dims *dims, Plan *p) {
+  const ssd_status s = make_plan(dims, ssd::bwd_vec_chunk_len(), p, false);
+  if (s != SSD_OK || (p->mfma && p->geo.P == dims->headdim)) return s;
+  return make_plan(dims, ssd::bwd_vec_chunk_len(), p, true);
+}
+
 VecBwdWorkspace vec_bwd_workspace(const Plan &p) {
   VecBwdWorkspace w{};
   const size_t tile = (size_t)p.ws.nc_max * p.geo.H * p.geo.P * p.geo.N * 4;
@@ -685,7 +696,7 @@ extern "C" {
 
 size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims *dims) {
   Plan p;
-  if (make_plan(dims, ssd::bwd_vec_chunk_len(), &p, true) != SSD_OK) return 0;
+  if (make_vec_bwd_plan(dims, &p) != SSD_OK) return 0;
   return vec_bwd_workspace(p).total;
 }
 
@@ -696,7 +707,7 @@ ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, co
                               float *dinit, const ssd_dims *dims, void *workspace,
                               size_t workspace_bytes, void *stream) {
   Plan p;
-  ssd_status s = make_plan(dims, ssd::bwd_vec_chunk_len(), &p, true);
+  ssd_status s = make_vec_bwd_plan(dims, &p);
   if (s != SSD_OK) return s;
   if ((s = check_cumsum_args(dt, A, cu_seqlens, p)) != SSD_OK) return s;
   if ((s = check_scan_args(x, B, C, D, dy, dt, p)) != SSD_OK) return s;

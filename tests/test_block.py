@@ -124,3 +124,26 @@ def test_gate_rmsnorm_in_place():
     torch.cuda.synchronize()
     assert out.data_ptr() == y.data_ptr()
     assert rel(y.float().cpu().numpy(), oracle.gate_rmsnorm(yh, zh, w, 1e-6)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_silu_saturation(dtype):
+    # pre-activations far into both tails and around 0: with weight 1, no bias
+    # and width 1 the convolution is silu(x) itself, and the gate with z = x
+    # and y = 1 is silu(x) too; SiLU goes to 0 on the left (1 + e^{-v}
+    # overflows) and to v on the right, with no inf or NaN on the way
+    v = np.concatenate([-np.logspace(3, -30, 60), [0.0], np.logspace(-30, 3, 60),
+                        [-89.0, -88.0, -87.0, -20.0, -1.0, 1.0, 20.0, 87.0, 88.0, 89.0]])
+    v = np.concatenate([v, np.zeros(-len(v) % 8)])  # 8 channels a token row
+    x = torch.from_numpy(v.astype(np.float32)).to(DEV).to(DT[dtype]).view(-1, 8)
+    xh = x.float().cpu().numpy().astype(np.float64)
+    out = ssd.conv1d_silu(x.view(1, -1, 8), torch.ones(8, 1, device=DEV), None)
+    gout = ssd.gate_rmsnorm(torch.ones_like(x), x, None, eps=1e-5)
+    torch.cuda.synchronize()
+    ref = oracle.conv1d_silu(xh, np.ones((8, 1)), None, np.array([0, xh.shape[0]]))
+    for name, got in (("conv", out.float().cpu().numpy().reshape(-1, 8)),
+                      ("gate", gout.float().cpu().numpy().reshape(-1, 8))):
+        assert np.all(np.isfinite(got)), name
+        err = np.abs(got - ref) / np.maximum(np.abs(ref), 1.0)
+        say(f"  silu tails {name} {dtype}: max err / max(1, |ref|) {err.max():.3e}")
+        assert err.max() <= TOL[dtype]
