@@ -144,6 +144,9 @@ __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
   __shared__ float Ms[kVQ][kVQ + 1];  // (C_l . B_s) e^{a_l - a_s}; later prefix sums of K
   __shared__ float sa[kVQ], sd[kVQ], sw[kVQ], sq[kVQ], sv[kVQ];
   __shared__ float red[3];  // <ge, h_s>, dA, dD of the head
+  // 16-row (or 16-column) slices of the operands of the (t, n) and (t, p)
+  // products, 16-byte aligned rows read as 4-element vectors
+  __shared__ __align__(16) float Sx[16][kVQ], Sy[16][kVQ], Sg[16][kVQ], Sh[16][kVQ];
   const int c = blockIdx.x, g = blockIdx.y;
   const ChunkInfo ci = chunk_info(geom, c);
   const int len = ci.len;
@@ -154,7 +157,7 @@ __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
   const IO *bb = Bm + ci.t0 * ldb + (int64_t)g * N;
   const IO *cb = Cm + ci.t0 * ldb + (int64_t)g * N;
   const int64_t PN = (int64_t)P * N;
-  const int N4 = N / 4, P4 = P / 4, L4 = (len + 3) / 4;
+
   // the 4 x 4 tile (l0.., s0..) of the 64 x 64 token matrices this thread forms
   const int l0 = 4 * (tid >> 4), s0 = 4 * (tid & 15);
   const bool tri = s0 <= l0 + 3 && l0 < len;  // the tile meets the chunk's lower triangle
@@ -244,31 +247,60 @@ __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
       atomicAdd(&red[0], part);
     }
     __syncthreads();
-    // (t, n) tiles: xge = x ge, dyh = dy h_s over p; sB = (E o L)^T C over
-    // l >= t; sC = (E o L) (dt B) over s <= t; then this head's dB, dC and
-    // the per-token q_t = sum_n xge B_t, v_t = sum_n dyh C_t
-    for (int tile = tid; tile < L4 * N4; tile += kVT) {
-      const int t0 = 4 * (tile / N4), n0 = 4 * (tile % N4);
-      float xg[4][4] = {}, dh[4][4] = {}, sB[4][4] = {}, sC[4][4] = {};
-      for (int p = 0; p < P; p += 4) {
-        float xa[4][4], ya[4][4], gv[4][4], hv[4][4];
+    // (t, n) tiles, 64 columns n at a time: xge = x ge, dyh = dy h_s over p,
+    // from 16-row slices of x, dy (transposed), ge and h_s staged in LDS (each
+    // read from the caches once per column block instead of once per token
+    // tile); sB = (E o L)^T C over l >= t; sC = (E o L) (dt B) over s <= t;
+    // then this head's dB, dC and the per-token q_t = sum_n xge B_t,
+    // v_t = sum_n dyh C_t.  Thread = (token tile ti, column tile ci) of the block.
+    const int ti = tid >> 4, ci4 = 4 * (tid & 15);
+    for (int nb = 0; nb < N; nb += 64) {
+      const int ncols = min(64, N - nb);  // a multiple of 16
+      const int t0 = 4 * ti, n0 = nb + ci4;
+      const bool act = ci4 < ncols;
+      float xg[4][4] = {}, dh[4][4] = {};
+      for (int p0 = 0; p0 < P; p0 += 16) {
+        __syncthreads();  // the previous slice (or phase) is done with the buffer
+        {  // x, dy rows t, columns p0 .. p0+15 -> [k][t]; ge, h_s rows p0 .. p0+15
+          const int t = tid >> 2, k4 = 4 * (tid & 3);
+          float xa[4], ya[4];
+          ld4(xb + row(t) * ldx + p0 + k4, xa);
+          ld4(yb + row(t) * ldx + p0 + k4, ya);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ld4(xb + row(t0 + i) * ldx + p, xa[i]);
-          ld4(yb + row(t0 + i) * ldx + p, ya[i]);
-          ld4(ge + (int64_t)(p + i) * N + n0, gv[i]);
-          ld4(hs + (int64_t)(p + i) * N + n0, hv[i]);
+          for (int m = 0; m < 4; ++m) {
+            Sx[k4 + m][t] = xa[m];
+            Sy[k4 + m][t] = ya[m];
+          }
+          const int k = tid >> 4, c4 = 4 * (tid & 15);
+          float gv[4] = {}, hv[4] = {};
+          if (c4 < ncols) {
+            ld4(ge + (int64_t)(p0 + k) * N + nb + c4, gv);
+            ld4(hs + (int64_t)(p0 + k) * N + nb + c4, hv);
+          }
+          st4(&Sg[k][c4], gv);
+          st4(&Sh[k][c4], hv);
         }
+        __syncthreads();
+        if (act) {
+#pragma unroll 4
+          for (int k = 0; k < 16; ++k) {
+            float xa[4], ya[4], gv[4], hv[4];
+            ld4(&Sx[k][t0], xa);
+            ld4(&Sy[k][t0], ya);
+            ld4(&Sg[k][ci4], gv);
+            ld4(&Sh[k][ci4], hv);
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
+            for (int i = 0; i < 4; ++i)
 #pragma unroll
-          for (int k = 0; k < 4; ++k)
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-              xg[i][m] += xa[i][k] * gv[k][m];
-              dh[i][m] += ya[i][k] * hv[k][m];
-            }
+              for (int m = 0; m < 4; ++m) {
+                xg[i][m] += xa[i] * gv[m];
+                dh[i][m] += ya[i] * hv[m];
+              }
+          }
+        }
       }
+      if (!act || t0 >= len) continue;
+      float sB[4][4] = {}, sC[4][4] = {};
       for (int l = t0; l < len; ++l) {
         float cv[4];
         ld4(cb + l * ldb + n0, cv);
@@ -321,11 +353,43 @@ __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
         atomicAdd(&sv[t], dot4(dh[i], ct));
       }
     }
-    // (t, p) tiles: dx = D dy + dt (sz + e^{a_last - a_t} gb) with
-    // sz = (Z o L)^T dy over l >= t and gb = B ge^T over n
-    for (int tile = tid; tile < L4 * P4; tile += kVT) {
-      const int t0 = 4 * (tile / P4), p0 = 4 * (tile % P4);
-      float sz[4][4] = {}, gb[4][4] = {};
+    // (t, p) tiles, 64 rows p at a time: dx = D dy + dt (sz + e^{a_last - a_t} gb)
+    // with sz = (Z o L)^T dy over l >= t and gb = B ge^T over n, the latter from
+    // 16-column slices of B and ge staged (transposed) in LDS
+    for (int pb = 0; pb < P; pb += 64) {
+      const int prows = min(64, P - pb);  // a multiple of 16
+      const int t0 = 4 * ti, p0 = pb + ci4;
+      const bool act = ci4 < prows;
+      float gb[4][4] = {};
+      for (int n0 = 0; n0 < N; n0 += 16) {
+        __syncthreads();
+        {  // B rows t and ge rows pb + r, columns n0 .. n0+15 -> [k][t], [k][r]
+          const int r = tid >> 2, k4 = 4 * (tid & 3);
+          float bv[4], gv[4] = {};
+          ld4(bb + row(r) * ldb + n0 + k4, bv);
+          if (r < prows) ld4(ge + (int64_t)(pb + r) * N + n0 + k4, gv);
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            Sx[k4 + m][r] = bv[m];
+            Sg[k4 + m][r] = gv[m];
+          }
+        }
+        __syncthreads();
+        if (act) {
+#pragma unroll 4
+          for (int k = 0; k < 16; ++k) {
+            float bv[4], gv[4];
+            ld4(&Sx[k][t0], bv);
+            ld4(&Sg[k][ci4], gv);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+              for (int m = 0; m < 4; ++m) gb[i][m] += bv[i] * gv[m];
+          }
+        }
+      }
+      if (!act || t0 >= len) continue;
+      float sz[4][4] = {};
       for (int l = t0; l < len; ++l) {
         float yv[4];
         ld4(yb + l * ldx + p0, yv);
@@ -335,18 +399,6 @@ __global__ __launch_bounds__(kVT) void k_bwd_chunk_vec(
 #pragma unroll
           for (int k = 0; k < 4; ++k) sz[i][k] += m * yv[k];
         }
-      }
-      for (int n = 0; n < N; n += 4) {
-        float bt[4][4], gv[4][4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ld4(bb + row(t0 + i) * ldb + n, bt[i]);
-          ld4(ge + (int64_t)(p0 + i) * N + n, gv[i]);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-#pragma unroll
-          for (int k = 0; k < 4; ++k) gb[i][k] += dot4(bt[i], gv[k]);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
