@@ -417,14 +417,18 @@ size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
  *   dinit float [rows, H, P, N] (the gradient w.r.t. init_state) or NULL.
  * workspace: device memory of at least ssd_fused_bwd_workspace_size(dims)
  * bytes, 16-byte aligned, else SSD_ERR_WORKSPACE.  Supported: SSD_BF16,
- * headdim 64, dstate N in {64, 128}, an even number of heads per group; else
- * SSD_ERR_UNSUPPORTED (and ssd_fused_bwd_workspace_size returns 0).  On
+ * headdim 64, dstate N in {64, 128, 256}, an even number of heads per group;
+ * else SSD_ERR_UNSUPPORTED (and ssd_fused_bwd_workspace_size returns 0).  On
  * `stream`: dA and dD cleared; the reverse sweep of the
  * state gradient (one pass per (sequence, two heads), or, with fewer such
  * pairs than 256, per 256-token segment: segment sums, a chained pass, the
  * segments again); the per-chunk gradients, which add into dA and dD with
- * float atomics, so those two sum in an unspecified order.  Returns after
- * enqueueing. */
+ * float atomics, so those two sum in an unspecified order.  N = 256 runs
+ * these steps once per half of the state's columns (the columns never mix in
+ * the recurrence): each half's B, C, saved states and dfinal are copied into
+ * the workspace, its dB, dC and dinit copied back into their columns, and
+ * the second half's dx and ddt added to the first's (dx then carries one
+ * more bf16 rounding).  Returns after enqueueing. */
 ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const void *B,
                          const void *C, const float *D, const int32_t *cu_seqlens,
                          const void *chunk_states, size_t states_bytes, const void *dy,

@@ -270,8 +270,7 @@ def fused_fwd_split(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch
 
 def make_fused_states(x: torch.Tensor, B: torch.Tensor,
                       cu_seqlens: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """A device byte buffer for fused_fwd's saved chunk states (or for
-    fused_bwd's workspace, which has the same size)."""
+    """A device byte buffer for fused_fwd's saved chunk states."""
     dims = dims_for(x, B, cu_seqlens)
     n = libssd.ssd_fused_states_size(dims)
     if n == 0:
@@ -299,7 +298,7 @@ def fused_bwd(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch.Tenso
         n = libssd.ssd_fused_bwd_workspace_size(dims)
         if n == 0:
             raise SSDUnsupported(libssd.SSD_ERR_UNSUPPORTED,
-                                 "shape outside the backward's (bf16, head dim 64, N 64 or 128, "
+                                 "shape outside the backward's (bf16, head dim 64, N 64, 128 or 256, "
                                  "an even number of heads per group)")
         workspace = torch.empty(n, dtype=torch.uint8, device=dev)
     out = dict(dx=torch.empty_like(x), ddt=torch.empty(dt.shape, dtype=torch.float32, device=dev),

@@ -933,6 +933,62 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
   return hipGetLastError();
 }
 
+namespace {
+// rows x units 16-byte pieces from rows src_ld bytes apart to rows dst_ld
+// bytes apart (a column block of a row-major tensor into a packed one, or back)
+__global__ __launch_bounds__(256) void k_copy2d16(const unsigned char *__restrict__ src,
+                                                  int64_t src_ld, unsigned char *__restrict__ dst,
+                                                  int64_t dst_ld, int64_t rows, int units) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= rows * units) return;
+  const int64_t r = i / units, u = i - r * units;
+  *reinterpret_cast<u32x4 *>(dst + r * dst_ld + u * 16) =
+      *reinterpret_cast<const u32x4 *>(src + r * src_ld + u * 16);
+}
+// acc += add: bf16 (8 elements a thread, the sum rounded to nearest even) and fp32
+__global__ __launch_bounds__(256) void k_add_bf16(uint16_t *__restrict__ acc,
+                                                  const uint16_t *__restrict__ add, int64_t n8) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  const u32x4 a = reinterpret_cast<const u32x4 *>(acc)[i], b = reinterpret_cast<const u32x4 *>(add)[i];
+  u32x4 o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    o[k] = pack_bf16x2(bf16lo(a[k]) + bf16lo(b[k]), bf16hi(a[k]) + bf16hi(b[k]));
+  reinterpret_cast<u32x4 *>(acc)[i] = o;
+}
+__global__ __launch_bounds__(256) void k_add_f32(float *__restrict__ acc,
+                                                 const float *__restrict__ add, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) acc[i] += add[i];
+}
+}  // namespace
+
+hipError_t launch_copy2d16(const void *src, int64_t src_ld, void *dst, int64_t dst_ld,
+                           int64_t rows, int units, hipStream_t stream) {
+  const int64_t n = rows * units;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_copy2d16, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                     static_cast<const unsigned char *>(src), src_ld,
+                     static_cast<unsigned char *>(dst), dst_ld, rows, units);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_bf16(void *acc, const void *add, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  const int64_t n8 = n / 8;  // n is a multiple of 8 (token rows of a head dim of 64)
+  hipLaunchKernelGGL(k_add_bf16, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0,
+                     stream, static_cast<uint16_t *>(acc), static_cast<const uint16_t *>(add), n8);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_f32(float *acc, const float *add, int64_t n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_add_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
+                     acc, add, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t stream) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(k_fill_f32, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,

@@ -468,10 +468,13 @@ ssd_status make_fused_plan(const ssd_dims *dims, Plan *p) {
   return SSD_OK;
 }
 
-// The backward's shapes: head dim 64 (no head split), N in {64, 128}, an even
-// number of heads per group (its reverse sweep pairs the heads of a group).
+// The backward's shapes: head dim 64 (no head split), N in {64, 128, 256}, an
+// even number of heads per group (its reverse sweep pairs the heads of a
+// group).  Its kernels hold N <= 128; N = 256 runs as two halves of 128 state
+// columns (split_bwd).
 bool bwd_supported(const Plan &p) {
-  return p.geo.hr == 1 && (p.geo.N == 64 || p.geo.N == 128) && (p.geo.H / p.geo.G) % 2 == 0;
+  return p.geo.hr == 1 && (p.geo.N == 64 || p.geo.N == 128 || p.geo.N == 256) &&
+         (p.geo.H / p.geo.G) % 2 == 0;
 }
 
 // 32-token chunks of the batch (packed: an upper bound, ceil(T/32) + nseq)
@@ -507,9 +510,37 @@ int64_t segments256(const Plan &p) {
 struct BwdWorkspace {
   size_t gsave, gseg, gin, aseg, total;
   int64_t nseg;
+  // N = 256, after one half's own workspace: its B, C, saved states and
+  // d(final_state), its dx and ddt (the second half's, added to the first's),
+  // dB, dC and d(init_state)
+  size_t sh, bh, ch, dfh, dxh, ddth, dbh, dch, dih;
 };
 
 BwdWorkspace bwd_workspace(const Plan &p) {
+  if (p.geo.N == 256) {
+    Plan ph = p;
+    ph.geo.N = 128;
+    BwdWorkspace w = bwd_workspace(ph);
+    const ssd::Geometry &g = p.geo;
+    const size_t bc = (size_t)g.tokens * g.G * 128, st = (size_t)g.nrows * g.H * g.P * 128;
+    size_t off = w.total;
+    auto take = [&](size_t bytes) {
+      const size_t o = off;
+      off += align_up(bytes);
+      return o;
+    };
+    w.sh = take(chunk_states_bytes(ph));
+    w.bh = take(bc * 2);
+    w.ch = take(bc * 2);
+    w.dfh = take(st * 4);
+    w.dxh = take((size_t)g.tokens * g.H * g.P * 2);
+    w.ddth = take((size_t)g.tokens * g.H * 4);
+    w.dbh = take(bc * 4);
+    w.dch = take(bc * 4);
+    w.dih = take(st * 4);
+    w.total = off;
+    return w;
+  }
   BwdWorkspace w{};
   w.gsave = 0;
   size_t off = chunk_states_bytes(p);
@@ -525,6 +556,67 @@ BwdWorkspace bwd_workspace(const Plan &p) {
   }
   w.total = off;
   return w;
+}
+
+// The backward at N = 256 as two runs of the N = 128 kernels.  The state's
+// columns n never mix in the recurrence: the state gradient, dB, dC and
+// d(init_state) of columns [128 k, 128 k + 128) come from those columns of B,
+// C, the saved states and d(final_state) alone, and dx, ddt and dA are sums
+// over n, so each half adds its part (the D dy term and dD only in the first).
+// Each half's inputs are copied out of the 256-column rows into packed
+// 128-column buffers in the workspace, its dB, dC and d(init_state) copied
+// back into their columns, and the second half's dx and ddt added to the
+// first's.
+hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const float *dt,
+                     const float *A, const void *B, const void *C, const float *D,
+                     const int32_t *cu, const void *chunk_states, const void *dy,
+                     const float *dfinal, void *dx, float *ddt, float *dA, float *dB, float *dC,
+                     float *dD, float *dinit, void *workspace, hipStream_t st) {
+  const ssd::Geometry &g = p.geo;
+  unsigned char *ws = static_cast<unsigned char *>(workspace);
+  void *Sh = ws + bw.sh, *Bh = ws + bw.bh, *Ch = ws + bw.ch, *dxh = ws + bw.dxh;
+  float *dfh = dfinal ? reinterpret_cast<float *>(ws + bw.dfh) : nullptr;
+  float *ddth = reinterpret_cast<float *>(ws + bw.ddth);
+  float *dBh = reinterpret_cast<float *>(ws + bw.dbh), *dCh = reinterpret_cast<float *>(ws + bw.dch);
+  float *dih = dinit ? reinterpret_cast<float *>(ws + bw.dih) : nullptr;
+  const int64_t trows = g.tokens * g.G;          // (token, group) rows of B, C, dB, dC
+  const int64_t srows = pairs64(p) * g.H * g.P;  // state rows of the saved states
+  const int64_t frows = g.nrows * g.H * g.P;     // state rows of d(final), d(init)
+  const unsigned char *b = static_cast<const unsigned char *>(B);
+  const unsigned char *c = static_cast<const unsigned char *>(C);
+  const unsigned char *s = static_cast<const unsigned char *>(chunk_states);
+  hipError_t e = ssd::launch_fill_f32(dA, g.H, st);
+  if (e == hipSuccess && dD) e = ssd::launch_fill_f32(dD, g.H, st);
+  for (int k = 0; k < 2 && e == hipSuccess; ++k) {
+    const int64_t o2 = k * 256, o4 = k * 512;  // the half's byte offset in a bf16 / fp32 row
+    e = ssd::launch_copy2d16(b + o2, 512, Bh, 256, trows, 16, st);
+    if (e == hipSuccess) e = ssd::launch_copy2d16(c + o2, 512, Ch, 256, trows, 16, st);
+    if (e == hipSuccess) e = ssd::launch_copy2d16(s + o2, 512, Sh, 256, srows, 16, st);
+    if (e == hipSuccess && dfinal)
+      e = ssd::launch_copy2d16(reinterpret_cast<const unsigned char *>(dfinal) + o4, 1024, dfh,
+                               512, frows, 32, st);
+    if (e == hipSuccess)
+      e = ssd::launch_bwd_reverse(dy, dt, A, Ch, dfh, cu, g.L, g.tokens, (int)g.nrows, g.H, 128,
+                                  g.G, workspace, dih, bw.nseg, ws_ptr<float>(workspace, bw.gseg),
+                                  ws_ptr<float>(workspace, bw.aseg),
+                                  ws_ptr<float>(workspace, bw.gin), st);
+    if (e == hipSuccess)
+      e = ssd::launch_bwd_chunk(x, dt, A, Bh, Ch, k ? nullptr : D, dy, Sh, workspace, cu, g.L,
+                                g.tokens, (int)g.nrows, chunks32(p), g.H, 128, g.G, k ? dxh : dx,
+                                k ? ddth : ddt, dA, dBh, dCh, k ? nullptr : dD, st);
+    if (e == hipSuccess)
+      e = ssd::launch_copy2d16(dBh, 512, reinterpret_cast<unsigned char *>(dB) + o4, 1024, trows,
+                               32, st);
+    if (e == hipSuccess)
+      e = ssd::launch_copy2d16(dCh, 512, reinterpret_cast<unsigned char *>(dC) + o4, 1024, trows,
+                               32, st);
+    if (e == hipSuccess && dinit)
+      e = ssd::launch_copy2d16(dih, 512, reinterpret_cast<unsigned char *>(dinit) + o4, 1024,
+                               frows, 32, st);
+  }
+  if (e == hipSuccess) e = ssd::launch_add_bf16(dx, dxh, g.tokens * g.H * g.P, st);
+  if (e == hipSuccess) e = ssd::launch_add_f32(ddt, ddth, g.tokens * g.H, st);
+  return e;
 }
 
 }  // namespace
@@ -798,6 +890,9 @@ ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const v
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   const int32_t *cu = g.packed ? cu_seqlens : nullptr;
+  if (g.N == 256)
+    return hip_status(split_bwd(p, bw, x, dt, A, B, C, D, cu, chunk_states, dy, dfinal, dx, ddt,
+                                dA, dB, dC, dD, dinit, workspace, st));
   hipError_t e = ssd::launch_fill_f32(dA, g.H, st);
   if (e == hipSuccess && dD) e = ssd::launch_fill_f32(dD, g.H, st);
   if (e == hipSuccess)

@@ -358,7 +358,7 @@ def test_fused_supported_shapes(mut):
 
 @pytest.mark.parametrize("mut,ok", [
     (dict(), True), (dict(dstate=128), True),
-    (dict(dstate=256), False), (dict(headdim=128), False),
+    (dict(dstate=256), True), (dict(dstate=32), False), (dict(headdim=128), False),
     (dict(ngroups=4), False), (dict(nheads=6, ngroups=2), False),
 ])
 def test_backward_shapes(mut, ok):
@@ -399,8 +399,18 @@ def test_fused_states_size():
     assert L.ssd_fused_bwd_workspace_size(ctypes.byref(dp)) == ws
     big = make_dims(8, 4096, 80, 64, 128, 1, 0, SSD_BF16)  # 8 x 40 blocks: one pass per sequence
     assert L.ssd_fused_bwd_workspace_size(ctypes.byref(big)) == 8 * 64 * 80 * 64 * 128 * 2
+    # N 256: the workspace of an N 128 backward (two halves run in turn), then
+    # one half's saved states, B, C, d(final), dx, ddt, dB, dC, d(init)
+    d = good()  # 2 x 512 tokens, H 4, P 64, G 1
+    d.dstate = 256
+    T, H, P, rows = 1024, 4, 64, 2
+    nseg = 2 * 2
+    half = 2 * 8 * H * P * 128 * 2 + 2 * nseg * H * P * 128 * 4 + 256
+    extra = (2 * 8 * H * P * 128 * 2 + 2 * T * 128 * 2 + rows * H * P * 128 * 4 + T * H * P * 2
+             + T * H * 4 + 2 * T * 128 * 4 + rows * H * P * 128 * 4)
+    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(d)) == half + extra
     for mut, fwd_ok in ((dict(io_dtype=SSD_F32), False), (dict(headdim=128), True),
-                        (dict(ngroups=4), True), (dict(dstate=256), True)):
+                        (dict(ngroups=4), True)):
         d = good()
         for k, val in mut.items():
             setattr(d, k, val)

@@ -76,7 +76,7 @@ def test_small_full():
     full_case(w, 1, label="bwd small N64 G2")
 
 
-@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("N", [64, 128, 256])
 def test_ragged_tail(N):
     # 1000 tokens a row: 31 full 32-token chunks and a tail of 8
     w = workloads.make_custom(3, 1000, 4, 64, N, 2, 256, "bf16", seed=2200 + N, init_std=0.2)
@@ -88,6 +88,20 @@ def test_groups(G):
     # 8 heads: 8 heads share B, C (G 1) or 2 do (G 4); dB, dC sum over them
     w = workloads.make_custom(2, 600, 8, 64, 128, G, 256, "bf16", seed=2300 + G, init_std=0.1)
     full_case(w, 3, label=f"bwd G{G}")
+
+
+def test_n256_full():
+    # N 256 runs as two halves of 128 state columns: dB, dC, d(init) of each
+    # half in its own columns, dx, ddt, dA summed over the halves
+    w = workloads.make_custom(2, 640, 4, 64, 256, 2, 256, "bf16", seed=2150, init_std=0.3)
+    full_case(w, 21, label="bwd N256 G2")
+
+
+def test_n256_packed_no_dfinal():
+    lens = [1, 0, 33, 64, 65, 500]
+    w = workloads.make_custom(1, 0, 4, 64, 256, 1, 256, "bf16", seed=2160, lens=lens,
+                              init_std=0.3)
+    full_case(w, 22, dfinal_std=0.0, label="bwd N256 packed, no dfinal")
 
 
 def test_varlen_edge_lengths():
@@ -124,7 +138,7 @@ def test_long_memory(kind):
 def test_saved_states_are_prefix_final_states(P, N):
     # the state entering 64-token pair b of a row is the oracle's final state
     # of the row's first 64 b tokens (from the same initial state); the saving
-    # forward also serves head dims above 64 and N 256 (the backward does not)
+    # forward also serves head dims above 64 (the backward does not)
     w = workloads.make_custom(2, 200, 4, P, N, 2, 256, "bf16", seed=2800 + P + N, init_std=0.3)
     t = upload(w)
     st = ssd.make_fused_states(t["x"], t["B"], t["cu"])
@@ -205,8 +219,8 @@ def test_unsupported_and_invalid():
     t = upload(w)
     with pytest.raises(ssd.SSDUnsupported):
         ssd.make_fused_states(t["x"], t["B"])
-    # forward-only shapes: head dim 128, N 256, odd heads per group
-    for P, N, H, G in ((128, 64, 4, 1), (64, 256, 4, 1), (64, 64, 3, 1)):
+    # forward-only shapes: head dim 128, odd heads per group
+    for P, N, H, G in ((128, 64, 4, 1), (64, 64, 3, 1)):
         w = workloads.make_custom(1, 64, H, P, N, G, 256, "bf16", seed=3002)
         t = upload(w)
         st = ssd.make_fused_states(t["x"], t["B"])
@@ -291,6 +305,16 @@ def test_long_n64_sampled():
     _, _, _, g = fwd_bwd(w, t, dy, dfinal)
     pairs = [(0, 0), (0, 33), (0, 79)]
     sampled_check(w, g, pairs, "bwd long_n64 sampled", dy, dfinal)
+
+
+def test_long_n256_sampled():
+    # one 65,536-token sequence, 80 heads, N 256: the two-half backward over
+    # 1024 pairs of chunks, sampled heads
+    w = workloads.make_workload("long_n256")
+    dy, dfinal = workloads.make_output_grads(w, 14)
+    t = upload(w)
+    _, _, _, g = fwd_bwd(w, t, dy, dfinal)
+    sampled_check(w, g, [(0, 0), (0, 41), (0, 79)], "bwd long_n256 sampled", dy, dfinal)
 
 
 def test_long_n64_split_training_forward_sampled():

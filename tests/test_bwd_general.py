@@ -101,9 +101,10 @@ def test_slow_and_fast_decay():
         check(w, 6 + k, f"general bwd A range {rng}")
 
 
-def test_agrees_with_the_fast_backward():
+@pytest.mark.parametrize("N", [128, 256])
+def test_agrees_with_the_fast_backward(N):
     # a shape both backward paths take: the same gradients to the bf16 bound
-    w = workloads.make_custom(2, 640, 4, 64, 128, 2, 64, "bf16", seed=3500, init_std=0.3)
+    w = workloads.make_custom(2, 640, 4, 64, N, 2, 64, "bf16", seed=3500 + N, init_std=0.3)
     g, dy, dfinal = run_bwd(w, 7)
     t = upload(w)
     st = ssd.make_fused_states(t["x"], t["B"], t["cu"])
@@ -120,7 +121,7 @@ def test_agrees_with_the_fast_backward():
 
 
 def test_long_n256_whole():
-    # one 65,536-token sequence, 80 heads, N 256 (the shape the fast backward
-    # does not take): every gradient against the oracle
+    # one 65,536-token sequence, 80 heads, N 256: every gradient against the
+    # oracle
     w = workloads.make_workload("long_n256")
     check(w, 8, "general bwd long_n256")
