@@ -396,7 +396,7 @@ template <int N, int R>
 __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
-    const uint16_t *__restrict__ dy, const uint16_t *__restrict__ hsave,
+    const uint16_t *__restrict__ dy, const uint16_t *__restrict__ hsave, int hsld,
     const uint16_t *__restrict__ gsave, const int32_t *__restrict__ cu, int64_t L, int64_t T,
     int rows, int64_t nchunks, int H, int G, uint16_t *__restrict__ dx,
     float *__restrict__ ddt, float *__restrict__ dA, float *__restrict__ dB,
@@ -493,12 +493,13 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
   // x (wavefronts 0-3) or dy (4-7) piece wave % 4 (rows 8 (wave % 4) .. +7,
   // clamped to the chunk's end); h_s and g_e pieces wave + 8 k (the swizzle
   // repeats every 16 rows, so piece k's offsets are piece 0's plus 8 KB k); dt.
-  uint32_t xoff, hoff, dtoff, nxoff, ndtoff;
+  uint32_t xoff, hoff, hsoff, dtoff, nxoff, ndtoff;
   {
     const int m = (wave & 3) * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz2<8>(r);
     xoff = static_cast<uint32_t>((min(r, last) * ldx + 8 * cc) * 2);
     const int mh = wave * 64 + lane, rh = mh / NCB, ch = (mh % NCB) ^ swz2<NCB>(rh);
     hoff = static_cast<uint32_t>((rh * N + 8 * ch) * 2);
+    hsoff = static_cast<uint32_t>((rh * hsld + 8 * ch) * 2);
     dtoff = static_cast<uint32_t>(min(tl, last) * H * 4);
     nxoff = static_cast<uint32_t>((min(r, lastn) * ldx + 8 * cc) * 2);
     ndtoff = static_cast<uint32_t>(min(tl, lastn) * H * 4);
@@ -510,9 +511,11 @@ __global__ __launch_bounds__(512, 1) void k_bwd_chunk(
     dma_lds16_sb(xoff, (wave < 4 ? x : dy) + t0 * ldx + (int64_t)h * P,
                  base + (wave < 4 ? F::OX : F::OY) + (wave & 3) * 1024);
     const int64_t st0 = (pidx * H + h) * (int64_t)(P * N);
+    const int64_t sh0 = (pidx * H + h) * (int64_t)P * hsld;
 #pragma unroll
     for (int kk = 0; kk < KP; ++kk)
-      dma_lds16_sb(hoff, hsave + st0 + 4096 * kk, base + F::OH + (wave + 8 * kk) * 1024);
+      dma_lds16_sb(hsoff, hsave + sh0 + (int64_t)(4096 / N) * hsld * kk,
+                   base + F::OH + (wave + 8 * kk) * 1024);
 #pragma unroll
     for (int kk = 0; kk < KP; ++kk)
       dma_lds16_sb(hoff, gsave + st0 + 4096 * kk, base + F::OG + (wave + 8 * kk) * 1024);
@@ -909,10 +912,11 @@ hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, c
 
 hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,
                             const void *C, const float *D, const void *dy, const void *hsave,
-                            const void *gsave, const int32_t *cu, int64_t L, int64_t T, int rows,
-                            int64_t nchunks, int H, int N, int G, void *dx, float *ddt, float *dA,
-                            float *dB, float *dC, float *dD, hipStream_t stream) {
+                            int hsld, const void *gsave, const int32_t *cu, int64_t L, int64_t T,
+                            int rows, int64_t nchunks, int H, int N, int G, void *dx, float *ddt,
+                            float *dA, float *dB, float *dC, float *dD, hipStream_t stream) {
   if (nchunks == 0) return hipSuccess;
+  if (hsld < N || hsld % 8) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((nchunks * G + 7) / 8 * 8));
   const uint16_t *xi = static_cast<const uint16_t *>(x);
   const uint16_t *bi = static_cast<const uint16_t *>(B);
@@ -924,10 +928,10 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
   // two ring slots (one head in flight ahead); one block of 8 wavefronts a CU
   if (N == 64)
     hipLaunchKernelGGL((k_bwd_chunk<64, 2>), grid, dim3(512), 0, stream, xi, dt, A, bi, ci, D, di, hs,
-                       gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+                       hsld, gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else if (N == 128)
     hipLaunchKernelGGL((k_bwd_chunk<128, 2>), grid, dim3(512), 0, stream, xi, dt, A, bi, ci, D, di, hs,
-                       gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+                       hsld, gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();

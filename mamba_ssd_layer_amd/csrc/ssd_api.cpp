@@ -510,10 +510,10 @@ int64_t segments256(const Plan &p) {
 struct BwdWorkspace {
   size_t gsave, gseg, gin, aseg, total;
   int64_t nseg;
-  // N = 256, after one half's own workspace: its B, C, saved states and
-  // d(final_state), its dx and ddt (the second half's, added to the first's),
-  // dB, dC and d(init_state)
-  size_t sh, bh, ch, dfh, dxh, ddth, dbh, dch, dih;
+  // N = 256, after one half's own workspace: its B, C and d(final_state), its
+  // dx and ddt (the second half's, added to the first's), dB, dC and
+  // d(init_state)
+  size_t bh, ch, dfh, dxh, ddth, dbh, dch, dih;
 };
 
 BwdWorkspace bwd_workspace(const Plan &p) {
@@ -529,7 +529,6 @@ BwdWorkspace bwd_workspace(const Plan &p) {
       off += align_up(bytes);
       return o;
     };
-    w.sh = take(chunk_states_bytes(ph));
     w.bh = take(bc * 2);
     w.ch = take(bc * 2);
     w.dfh = take(st * 4);
@@ -563,8 +562,9 @@ BwdWorkspace bwd_workspace(const Plan &p) {
 // d(init_state) of columns [128 k, 128 k + 128) come from those columns of B,
 // C, the saved states and d(final_state) alone, and dx, ddt and dA are sums
 // over n, so each half adds its part (the D dy term and dD only in the first).
-// Each half's inputs are copied out of the 256-column rows into packed
-// 128-column buffers in the workspace, its dB, dC and d(init_state) copied
+// Each half's B, C and d(final_state) are copied out of the 256-column rows
+// into packed 128-column buffers in the workspace (the saved states are read
+// in place, their rows 256 columns apart), its dB, dC and d(init_state) copied
 // back into their columns, and the second half's dx and ddt added to the
 // first's.
 hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const float *dt,
@@ -574,13 +574,12 @@ hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const
                      float *dD, float *dinit, void *workspace, hipStream_t st) {
   const ssd::Geometry &g = p.geo;
   unsigned char *ws = static_cast<unsigned char *>(workspace);
-  void *Sh = ws + bw.sh, *Bh = ws + bw.bh, *Ch = ws + bw.ch, *dxh = ws + bw.dxh;
+  void *Bh = ws + bw.bh, *Ch = ws + bw.ch, *dxh = ws + bw.dxh;
   float *dfh = dfinal ? reinterpret_cast<float *>(ws + bw.dfh) : nullptr;
   float *ddth = reinterpret_cast<float *>(ws + bw.ddth);
   float *dBh = reinterpret_cast<float *>(ws + bw.dbh), *dCh = reinterpret_cast<float *>(ws + bw.dch);
   float *dih = dinit ? reinterpret_cast<float *>(ws + bw.dih) : nullptr;
   const int64_t trows = g.tokens * g.G;          // (token, group) rows of B, C, dB, dC
-  const int64_t srows = pairs64(p) * g.H * g.P;  // state rows of the saved states
   const int64_t frows = g.nrows * g.H * g.P;     // state rows of d(final), d(init)
   const unsigned char *b = static_cast<const unsigned char *>(B);
   const unsigned char *c = static_cast<const unsigned char *>(C);
@@ -591,7 +590,6 @@ hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const
     const int64_t o2 = k * 256, o4 = k * 512;  // the half's byte offset in a bf16 / fp32 row
     e = ssd::launch_copy2d16(b + o2, 512, Bh, 256, trows, 16, st);
     if (e == hipSuccess) e = ssd::launch_copy2d16(c + o2, 512, Ch, 256, trows, 16, st);
-    if (e == hipSuccess) e = ssd::launch_copy2d16(s + o2, 512, Sh, 256, srows, 16, st);
     if (e == hipSuccess && dfinal)
       e = ssd::launch_copy2d16(reinterpret_cast<const unsigned char *>(dfinal) + o4, 1024, dfh,
                                512, frows, 32, st);
@@ -601,9 +599,9 @@ hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const
                                   ws_ptr<float>(workspace, bw.aseg),
                                   ws_ptr<float>(workspace, bw.gin), st);
     if (e == hipSuccess)
-      e = ssd::launch_bwd_chunk(x, dt, A, Bh, Ch, k ? nullptr : D, dy, Sh, workspace, cu, g.L,
-                                g.tokens, (int)g.nrows, chunks32(p), g.H, 128, g.G, k ? dxh : dx,
-                                k ? ddth : ddt, dA, dBh, dCh, k ? nullptr : dD, st);
+      e = ssd::launch_bwd_chunk(x, dt, A, Bh, Ch, k ? nullptr : D, dy, s + o2, 256, workspace,
+                                cu, g.L, g.tokens, (int)g.nrows, chunks32(p), g.H, 128, g.G,
+                                k ? dxh : dx, k ? ddth : ddt, dA, dBh, dCh, k ? nullptr : dD, st);
     if (e == hipSuccess)
       e = ssd::launch_copy2d16(dBh, 512, reinterpret_cast<unsigned char *>(dB) + o4, 1024, trows,
                                32, st);
@@ -901,7 +899,7 @@ ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const v
                                 ws_ptr<float>(workspace, bw.aseg), ws_ptr<float>(workspace, bw.gin),
                                 st);
   if (e == hipSuccess)
-    e = ssd::launch_bwd_chunk(x, dt, A, B, C, D, dy, chunk_states, workspace, cu, g.L, g.tokens,
+    e = ssd::launch_bwd_chunk(x, dt, A, B, C, D, dy, chunk_states, g.N, workspace, cu, g.L, g.tokens,
                               (int)g.nrows, chunks32(p), g.H, g.N, g.G, dx, ddt, dA, dB, dC, dD,
                               st);
   return hip_status(e);

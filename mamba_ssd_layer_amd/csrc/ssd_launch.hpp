@@ -91,11 +91,13 @@ hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, c
                               int rows, int H, int N, int G, void *gsave, float *dinit,
                               int64_t nseg, float *gseg, float *aseg, float *gin,
                               hipStream_t stream);
+// hsave: the saved states, rows of hsld >= N elements (N, or 2N when hsave
+// points into one half of the columns of N = 256 states)
 hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,
                             const void *C, const float *D, const void *dy, const void *hsave,
-                            const void *gsave, const int32_t *cu, int64_t L, int64_t T, int rows,
-                            int64_t nchunks, int H, int N, int G, void *dx, float *ddt, float *dA,
-                            float *dB, float *dC, float *dD, hipStream_t stream);
+                            int hsld, const void *gsave, const int32_t *cu, int64_t L, int64_t T,
+                            int rows, int64_t nchunks, int H, int N, int G, void *dx, float *ddt,
+                            float *dA, float *dB, float *dC, float *dD, hipStream_t stream);
 hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t stream);
 // rows x units 16-byte pieces between row-major layouts (byte row strides)
 hipError_t launch_copy2d16(const void *src, int64_t src_ld, void *dst, int64_t dst_ld,
