@@ -97,6 +97,13 @@ def test_n256_full():
     full_case(w, 21, label="bwd N256 G2")
 
 
+def test_n256_many_heads():
+    # 4 rows x 128 heads in 8 groups: 256 (row, head pair) blocks in the reverse
+    # sweep (one pass per block, not segmented), 16 heads walked per chunk block
+    w = workloads.make_custom(4, 300, 128, 64, 256, 8, 256, "bf16", seed=2170, init_std=0.2)
+    full_case(w, 23, label="bwd N256 many heads")
+
+
 def test_n256_packed_no_dfinal():
     lens = [1, 0, 33, 64, 65, 500]
     w = workloads.make_custom(1, 0, 4, 64, 256, 1, 256, "bf16", seed=2160, lens=lens,

@@ -86,10 +86,11 @@ def test_odd_heads_per_group(H, G):
     check_full(w, y, fin, label=f"fused H{H} G{G}")
 
 
-@pytest.mark.parametrize("N", [64, 128])
+@pytest.mark.parametrize("N", [64, 128, 256])
 def test_head_pairs_path(N):
     # enough (sequence, head pair) blocks to fill the GPU: the two-heads-a-block
-    # instance (the small problems above take the one-head instance)
+    # instance at N 64 and 128 (the small problems above take the one-head
+    # instance); N 256 takes one head a block at any size
     w = workloads.make_custom(4, 300, 128, 64, N, 8, 256, "bf16", seed=1270 + N, init_std=0.2)
     y, fin, _ = run_fused(w)
     check_full(w, y, fin, label=f"fused head pairs N{N}")
