@@ -387,7 +387,9 @@ size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims *dims);
 /* Workspace bytes of ssd_fused_bwd: the gradient w.r.t. the state leaving
  * every 64-token pair (bf16, laid out like chunk_states) and, when the sweep
  * is split into segments (sequences x nheads / 2 < 256), two fp32 P x N tiles
- * and a decay per segment and head.  Host-only. */
+ * and a decay per segment and head.  At N = 256 those of N = 128 (each half
+ * of the state's columns runs in turn), then one half's B and C (bf16),
+ * dfinal, dB, dC and dinit (fp32), dx (bf16) and ddt.  Host-only. */
 size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
 
 /* Gradients of the forward.  The pages give the recurrence h_t = exp(dt_t A)
