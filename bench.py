@@ -285,12 +285,13 @@ def backward_bytes(w):
 def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
     """A forward that leaves the state entering every 64-token chunk, then the
     backward (ssd_fused_bwd) for seeded upstream gradients dy, dfinal; each
-    timed with HIP events on the launch stream. Three forwards leave those
-    states: the one-pass forward saving them (ssd_fused_fwd_train), the
-    four-stage forward with chunk length 64 (its hprev), and SSDTrainForward
-    (y from the four stages at chunk length 256, the states from the first
-    three at chunk length 64); the fastest is the step's forward
-    (fwd_train_path), the others are reported beside it."""
+    timed with HIP events on the launch stream. Three or four forwards leave
+    those states: the one-pass forward saving them (ssd_fused_fwd_train), the
+    four-stage forward with chunk length 64 (its hprev), SSDTrainForward (y
+    from the four stages at chunk length 256, the states from the first three
+    at chunk length 64) and, where the library cuts the sequences, the split
+    one-pass forward saving them (ssd_fused_fwd_split_train); the fastest is
+    the step's forward (fwd_train_path), the others are reported beside it."""
     dev = t["x"].device
     dy, dfinal = workloads.make_output_grads(w, 6100)
     dyd = torch.from_numpy(dy).to(dev).to(torch.bfloat16).view(t["x"].shape)
@@ -318,6 +319,20 @@ def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
         tplan(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], t["cu"], y=y,
               final_state=fin)
 
+    # the split one-pass forward saving the states, where the library cuts the
+    # sequences (fixed-length batches; segments a multiple of 64 tokens)
+    dims = ssd.dims_for(t["x"], t["B"], t["cu"])
+    seg = ssd.libssd.ssd_fused_split_seg_len(dims) if not w.nseq else 0
+    fwd_seg = None
+    if 0 < seg < w.seqlen and seg % 64 == 0:
+        wseg = torch.empty(max(1, ssd.libssd.ssd_fused_split_workspace_size(dims, seg)),
+                           dtype=torch.uint8, device=dev)
+
+        def fwd_seg():
+            ssd.fused_fwd_split(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], y=y,
+                                final_state=fin, seg_len=seg, workspace=wseg,
+                                chunk_states=states)
+
     def bwd():
         ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], states, dyd, dfd, t["cu"],
                       workspace=ws)
@@ -337,6 +352,8 @@ def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
 
     by_path = {"ssd_fused_fwd_train": timed(fwd), "ssd_chunk_scan_fwd_q64": timed(fwd64),
                "SSDTrainForward": timed(fwd_split)}
+    if fwd_seg is not None:
+        by_path["ssd_fused_fwd_split_train"] = timed(fwd_seg)
     bus = timed(bwd)
     path = min(by_path, key=by_path.get)
     fus = by_path[path]
@@ -352,7 +369,10 @@ def training_step(torch, ssd, workloads, w, t, steps: int, warmup: int):
            "bwd_hbm_frac": round((rev + chk) / (bus * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)}
     log(f"bench: training step: forward saving states {by_path['ssd_fused_fwd_train']:.1f} us "
         f"(one-pass), {by_path['ssd_chunk_scan_fwd_q64']:.1f} us (four-stage, chunk 64), "
-        f"{by_path['SSDTrainForward']:.1f} us (chunk 256 + chunk-64 states), backward {bus:.1f} us, "
+        f"{by_path['SSDTrainForward']:.1f} us (chunk 256 + chunk-64 states), "
+        + (f"{by_path['ssd_fused_fwd_split_train']:.1f} us (split one-pass), "
+           if "ssd_fused_fwd_split_train" in by_path else "")
+        + f"backward {bus:.1f} us, "
         f"{res['tokens_per_s'] / 1e6:.1f} M tokens/s")
     return res
 

@@ -335,6 +335,27 @@ ssd_status ssd_fused_fwd_split(const void *x, const float *dt, const float *A, c
                                float *final_state, int64_t seg_len, const ssd_dims *dims,
                                void *workspace, size_t workspace_bytes, void *stream);
 
+/* ssd_fused_fwd_split that also saves the state entering every 64-token pair
+ * of chunks for the backward pass (ssd_fused_bwd), like ssd_fused_fwd_train:
+ * step 3 stores, at the top of every other 32-token chunk of each segment,
+ * its state rounded to bf16 (the state entering a segment is the one step 2
+ * handed it, so the saved states differ from ssd_fused_fwd_train's by
+ * rounding only).
+ *   chunk_states  device, [npairs][H][P][N] bf16, ssd_fused_fwd_train's
+ *                 layout, 16-byte aligned, overlapping no other argument;
+ *                 NULL returns SSD_ERR_INVALID_ARG;
+ *   states_bytes  its size, at least ssd_fused_states_size(dims), else
+ *                 SSD_ERR_WORKSPACE;
+ *   seg_len       a positive multiple of 64 (a segment starts a pair), else
+ *                 SSD_ERR_INVALID_ARG.
+ * Everything else as ssd_fused_fwd_split.  Returns after enqueueing. */
+ssd_status ssd_fused_fwd_split_train(const void *x, const float *dt, const float *A,
+                                     const void *B, const void *C, const float *D,
+                                     const float *init_state, void *y, float *final_state,
+                                     void *chunk_states, size_t states_bytes, int64_t seg_len,
+                                     const ssd_dims *dims, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* Workspace bytes of ssd_fused_fwd_split for these dims and seg_len (0 when
  * seg_len >= seqlen, or when the arguments are invalid).  Host-only. */
 size_t ssd_fused_split_workspace_size(const ssd_dims *dims, int64_t seg_len);

@@ -245,13 +245,16 @@ def fused_fwd_split(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch
                     init_state: Optional[torch.Tensor] = None, y: Optional[torch.Tensor] = None,
                     final_state: Optional[torch.Tensor] = None, want_final: bool = True,
                     seg_len: Optional[int] = None, workspace: Optional[torch.Tensor] = None,
+                    chunk_states: Optional[torch.Tensor] = None,
                     stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """y, final_state = the one-pass forward over segments of seg_len tokens
     (ssd_fused_fwd_split: fixed-length batches; a state-only pass, the
     hand-off between segments, then every segment from its entering state).
     Same arguments and results as fused_fwd without cu_seqlens.  seg_len
     defaults to fused_split_seg_len; workspace (uint8, device) is allocated
-    when not given."""
+    when not given.  chunk_states (from make_fused_states; seg_len a multiple
+    of 64): also save the state entering every 64-token pair for fused_bwd
+    (ssd_fused_fwd_split_train)."""
     dims = dims_for(x, B, None)
     if seg_len is None:
         seg_len = libssd.ssd_fused_split_seg_len(dims)
@@ -263,8 +266,13 @@ def fused_fwd_split(x: torch.Tensor, dt: torch.Tensor, A: torch.Tensor, B: torch
     need = libssd.ssd_fused_split_workspace_size(dims, seg_len)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
-    libssd.ssd_fused_fwd_split(x, dt, A, B, C, D, init_state, y, final_state, seg_len, dims,
-                               workspace, stream)
+    if chunk_states is not None:
+        libssd.ssd_fused_fwd_split_train(x, dt, A, B, C, D, init_state, y, final_state,
+                                         chunk_states, chunk_states.numel(), seg_len, dims,
+                                         workspace, stream)
+    else:
+        libssd.ssd_fused_fwd_split(x, dt, A, B, C, D, init_state, y, final_state, seg_len, dims,
+                                   workspace, stream)
     return y, final_state
 
 

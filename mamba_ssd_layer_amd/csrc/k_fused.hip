@@ -243,7 +243,12 @@ void k_ssd_fused(const FusedArgs args) {
       hst[pt][j] = h0p ? *reinterpret_cast<const f32x4 *>(h0p + prow + nrow(j)) : f32x4{};
   }
   const int nck = static_cast<int>((len + CQ - 1) / CQ);
-  const int64_t pbase = SAVE ? pair_base64(cu, s, L, T) : 0;
+  // the row's first 64-token pair in the saved states' layout: a segment of a
+  // split sequence starts seg S / 64 pairs into its sequence (S a multiple of
+  // 64 when saving)
+  const int64_t pbase = !SAVE ? 0
+                        : cu  ? pair_base64(cu, s, L, T)
+                              : (int64_t)sq * ((L + 63) / 64) + (int64_t)seg * (args.S / 64);
   // The registers hold S = h / 2^lam: the decay of a chunk goes into lam
   // (wave-uniform) instead of into 2 N/16 x 4 multiplies a lane; S is
   // rescaled only when lam drops below -32, or before a chunk whose own
@@ -714,9 +719,11 @@ hipError_t launch_fused(const void *x, const float *dt, const float *A, const vo
 hipError_t launch_fused_split(const void *x, const float *dt, const float *A, const void *B,
                               const void *C, const float *D, const float *h0, int64_t L,
                               int nseq, int64_t S, int H, int P, int N, int G, int hr, void *y,
-                              float *hfin, float *sseg, float *lseg, hipStream_t stream) {
+                              float *hfin, float *sseg, float *lseg, void *hsave,
+                              hipStream_t stream) {
   if (nseq == 0 || L == 0) return hipSuccess;
-  if (!fused_supported(H, P, N, G) || hr < 1 || H % hr != 0 || S <= 0 || S % 32 != 0)
+  if (!fused_supported(H, P, N, G) || hr < 1 || H % hr != 0 || S <= 0 || S % 32 != 0 ||
+      (hsave && S % 64 != 0))
     return hipErrorInvalidValue;
   const int nseg = static_cast<int>((L + S - 1) / S);
   FusedArgs a{};
@@ -748,7 +755,8 @@ hipError_t launch_fused_split(const void *x, const float *dt, const float *A, co
                        lseg, h0, nseq, nseg, H, PN4);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  // 3. every segment from its entering state: y, and the final state
+  // 3. every segment from its entering state: y, and the final state (and,
+  // when saving, the state entering every 64-token pair)
   a.nsr = nseg;
   a.rows = nseq * nseg;
   a.h0 = h0;
@@ -757,7 +765,8 @@ hipError_t launch_fused_split(const void *x, const float *dt, const float *A, co
   a.lseg = nullptr;
   a.y = static_cast<uint16_t *>(y);
   a.hfin = hfin;
-  return launch_any(a, N, kFwd, stream);
+  a.hsave = static_cast<uint16_t *>(hsave);
+  return launch_any(a, N, hsave ? kFwdSave : kFwd, stream);
 }
 
 }  // namespace ssd

@@ -716,10 +716,16 @@ int64_t ssd_fused_split_seg_len(const ssd_dims *dims) {
   return S < L32 ? S : L32;
 }
 
-ssd_status ssd_fused_fwd_split(const void *x, const float *dt, const float *A, const void *B,
-                               const void *C, const float *D, const float *init_state, void *y,
-                               float *final_state, int64_t seg_len, const ssd_dims *dims,
-                               void *workspace, size_t workspace_bytes, void *stream) {
+}  // extern "C"
+
+namespace {
+
+// ssd_fused_fwd_split with or without saving the per-pair states
+ssd_status split_fwd(const void *x, const float *dt, const float *A, const void *B, const void *C,
+                     const float *D, const float *init_state, void *y, float *final_state,
+                     void *chunk_states, size_t states_bytes, int64_t seg_len,
+                     const ssd_dims *dims, void *workspace, size_t workspace_bytes,
+                     void *stream) {
   Plan p;
   ssd_status s = make_split_plan(dims, seg_len, &p);
   if (s != SSD_OK) return s;
@@ -728,10 +734,10 @@ ssd_status ssd_fused_fwd_split(const void *x, const float *dt, const float *A, c
   if ((s = check_pass_args(init_state, final_state, p)) != SSD_OK) return s;
   if ((s = check_scan_args(x, B, C, D, y, dt, p)) != SSD_OK) return s;
   const SplitWorkspace w = split_workspace(p, seg_len);
+  const Sizes z = tensor_bytes(p);
   if (w.total > 0) {
     if (!workspace || workspace_bytes < w.total) return SSD_ERR_WORKSPACE;
     if (!aligned(workspace, 256)) return SSD_ERR_INVALID_ARG;
-    const Sizes z = tensor_bytes(p);
     if (overlaps(workspace, w.total, x, z.x) || overlaps(workspace, w.total, y, z.x) ||
         overlaps(workspace, w.total, B, z.bc) || overlaps(workspace, w.total, C, z.bc) ||
         overlaps(workspace, w.total, dt, z.dt) ||
@@ -739,13 +745,47 @@ ssd_status ssd_fused_fwd_split(const void *x, const float *dt, const float *A, c
         overlaps(workspace, w.total, final_state, z.state))
       return SSD_ERR_INVALID_ARG;
   }
+  if (chunk_states) {
+    if (seg_len % 64 != 0 || !aligned(chunk_states, 16)) return SSD_ERR_INVALID_ARG;
+    const size_t hb = chunk_states_bytes(p);
+    if (states_bytes < hb) return SSD_ERR_WORKSPACE;
+    if (overlaps(chunk_states, hb, x, z.x) || overlaps(chunk_states, hb, y, z.x) ||
+        overlaps(chunk_states, hb, B, z.bc) || overlaps(chunk_states, hb, C, z.bc) ||
+        overlaps(chunk_states, hb, dt, z.dt) || overlaps(chunk_states, hb, init_state, z.state) ||
+        overlaps(chunk_states, hb, final_state, z.state) ||
+        (w.total > 0 && overlaps(chunk_states, hb, workspace, w.total)))
+      return SSD_ERR_INVALID_ARG;
+  }
   const ssd::Geometry &g = p.geo;
   unsigned char *ws = static_cast<unsigned char *>(workspace);
   return hip_status(ssd::launch_fused_split(
       x, dt, A, B, C, D, init_state, g.L, (int)g.nrows, seg_len, g.H, g.P, g.N, g.G, g.hr, y,
       final_state, w.total ? reinterpret_cast<float *>(ws + w.sseg) : nullptr,
-      w.total ? reinterpret_cast<float *>(ws + w.lseg) : nullptr,
+      w.total ? reinterpret_cast<float *>(ws + w.lseg) : nullptr, chunk_states,
       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_fused_fwd_split(const void *x, const float *dt, const float *A, const void *B,
+                               const void *C, const float *D, const float *init_state, void *y,
+                               float *final_state, int64_t seg_len, const ssd_dims *dims,
+                               void *workspace, size_t workspace_bytes, void *stream) {
+  return split_fwd(x, dt, A, B, C, D, init_state, y, final_state, nullptr, 0, seg_len, dims,
+                   workspace, workspace_bytes, stream);
+}
+
+ssd_status ssd_fused_fwd_split_train(const void *x, const float *dt, const float *A,
+                                     const void *B, const void *C, const float *D,
+                                     const float *init_state, void *y, float *final_state,
+                                     void *chunk_states, size_t states_bytes, int64_t seg_len,
+                                     const ssd_dims *dims, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
+  if (!chunk_states) return SSD_ERR_INVALID_ARG;
+  return split_fwd(x, dt, A, B, C, D, init_state, y, final_state, chunk_states, states_bytes,
+                   seg_len, dims, workspace, workspace_bytes, stream);
 }
 
 }  // extern "C"

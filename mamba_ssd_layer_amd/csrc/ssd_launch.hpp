@@ -78,11 +78,14 @@ hipError_t launch_fused(const void *x, const float *dt, const float *A, const vo
 // (end state from zero into sseg [nseq][j + 1] of a [nseq][nseg][H][P][N]
 // buffer, total log2 decay into lseg [nseq][nseg-1][H]), a hand-off pass
 // turning sseg into the states entering every segment, then the forward of
-// every segment from its entering state (h0 read only by the hand-off)
+// every segment from its entering state (h0 read only by the hand-off); with
+// hsave (S a multiple of 64) the last pass also saves the state entering
+// every 64-token pair, in ssd_fused_fwd_train's layout
 hipError_t launch_fused_split(const void *x, const float *dt, const float *A, const void *B,
                               const void *C, const float *D, const float *h0, int64_t L,
                               int nseq, int64_t S, int H, int P, int N, int G, int hr, void *y,
-                              float *hfin, float *sseg, float *lseg, hipStream_t stream);
+                              float *hfin, float *sseg, float *lseg, void *hsave,
+                              hipStream_t stream);
 // backward of the one-pass forward (bf16, P == 64, N in {64, 128}, even heads per group)
 // nseg > 0: the sweep split into that many 256-token segments (gseg, gin
 // [nseg][H][P][N] and aseg [nseg][H] fp32 scratch); 0: one pass per sequence

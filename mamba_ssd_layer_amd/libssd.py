@@ -67,6 +67,7 @@ EXPORTS = ["ssd_workspace_size", "ssd_get_workspace_layout", "ssd_chunk_scan_fwd
            "ssd_step", "ssd_conv1d_silu", "ssd_gate_rmsnorm", "ssd_fused_fwd",
            "ssd_fused_fwd_train", "ssd_fused_states_size", "ssd_fused_bwd_workspace_size",
            "ssd_fused_fwd_split", "ssd_fused_split_workspace_size", "ssd_fused_split_seg_len",
+           "ssd_fused_fwd_split_train",
            "ssd_chunk_scan_bwd", "ssd_chunk_scan_bwd_workspace_size",
            "ssd_fused_bwd",
            "ssd_status_string", "ssd_version"]
@@ -111,6 +112,9 @@ def _load() -> ctypes.CDLL:
     lib.ssd_fused_fwd_split.restype = i32
     lib.ssd_fused_fwd_split.argtypes = [p, p, p, p, p, p, p, p, p, ctypes.c_int64, dims_p, p, sz,
                                         p]
+    lib.ssd_fused_fwd_split_train.restype = i32
+    lib.ssd_fused_fwd_split_train.argtypes = [p, p, p, p, p, p, p, p, p, p, sz, ctypes.c_int64,
+                                              dims_p, p, sz, p]
     lib.ssd_fused_split_workspace_size.restype = sz
     lib.ssd_fused_split_workspace_size.argtypes = [dims_p, ctypes.c_int64]
     lib.ssd_fused_split_seg_len.restype = ctypes.c_int64
@@ -342,6 +346,26 @@ def ssd_fused_fwd_split(x, dt, A, B, C, D, init_state, y, final_state, seg_len, 
     px, pdt, pA, pB, pC, pD, py, phi, phf, pws = _ptrs(*ts, hi, hf, ws)
     _check(_lib.ssd_fused_fwd_split(px, pdt, pA, pB, pC, pD, phi, py, phf, int(seg_len),
                                     ctypes.byref(dims), pws, _bytes(ws), _stream(stream)))
+
+
+def ssd_fused_fwd_split_train(x, dt, A, B, C, D, init_state, y, final_state, chunk_states,
+                              states_bytes, seg_len, dims, workspace, stream=None) -> None:
+    if dims.nseq > 0:
+        raise SSDUnsupported(SSD_ERR_UNSUPPORTED, "the split forward takes fixed-length batches")
+    ts = _fwd(dims, x, dt, A, B, C, D, y, need=ALL)
+    hi, hf = _state(init_state, dims, "init_state"), _state(final_state, dims, "final_state")
+    need = ssd_fused_split_workspace_size(dims, seg_len)
+    ws = _t(workspace, torch.uint8, _bytes(workspace), "workspace", optional=need == 0)
+    if need and _bytes(ws) < need:
+        raise SSDWorkspaceError(SSD_ERR_WORKSPACE, f"workspace has {_bytes(ws)} bytes, needs {need}")
+    if chunk_states is None:
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "chunk_states is required")
+    if int(states_bytes) > _bytes(chunk_states):
+        raise SSDInvalidArgument(SSD_ERR_INVALID_ARG, "states_bytes exceeds its buffer")
+    px, pdt, pA, pB, pC, pD, py, phi, phf, pcs, pws = _ptrs(*ts, hi, hf, chunk_states, ws)
+    _check(_lib.ssd_fused_fwd_split_train(px, pdt, pA, pB, pC, pD, phi, py, phf, pcs,
+                                          int(states_bytes), int(seg_len), ctypes.byref(dims),
+                                          pws, _bytes(ws), _stream(stream)))
 
 
 def ssd_fused_split_workspace_size(dims, seg_len) -> int:

@@ -561,6 +561,25 @@ def test_split_validates_before_any_hip_call():
                                      v(FAKE + (4 << 30)), 1 << 40, None) == SSD_ERR_UNSUPPORTED
 
 
+def test_split_train_validates_before_any_hip_call():
+    v = ctypes.c_void_p
+    d = make_dims(2, 1000, 4, 64, 64, 1, 0, SSD_BF16)
+    dp = ctypes.byref(d)
+    need = L.ssd_fused_split_workspace_size(dp, 256)
+    hb = L.ssd_fused_states_size(dp)
+    ST = FAKE + (8 << 30)
+    args = lambda S=256, st=ST, stb=hb, wsb=need: L.ssd_fused_fwd_split_train(
+        v(FAKE), v(FAKE + (5 << 30)), v(FAKE + (6 << 30)), v(FAKE + (1 << 30)),
+        v(FAKE + (2 << 30)), None, None, v(FAKE + (3 << 30)), None, v(st), stb, S, dp,
+        v(FAKE + (4 << 30)), wsb, None)
+    assert args(st=0) == SSD_ERR_INVALID_ARG              # the states are required
+    assert args(S=96, wsb=1 << 30) == SSD_ERR_INVALID_ARG  # a multiple of 32, not of 64
+    assert args(stb=hb - 1) == SSD_ERR_WORKSPACE           # states buffer too small
+    assert args(st=ST + 8) == SSD_ERR_INVALID_ARG          # misaligned
+    assert args(st=FAKE + (4 << 30)) == SSD_ERR_INVALID_ARG  # over the workspace
+    assert args(st=FAKE + (3 << 30)) == SSD_ERR_INVALID_ARG  # over y
+
+
 def _gbwd_ws(b, L_, H, P, N, G, nseq, io):
     al = lambda v: (v + 255) // 256 * 256
     nc, fwd_total = _ws_expected(b, L_, H, P, N, G, 64, nseq, io)

@@ -324,6 +324,66 @@ def test_long_n256_sampled():
     sampled_check(w, g, [(0, 0), (0, 41), (0, 79)], "bwd long_n256 sampled", dy, dfinal)
 
 
+@pytest.mark.parametrize("N", [64, 256])
+def test_split_one_pass_saving_states(N):
+    # ssd_fused_fwd_split_train: 2000 tokens a row in segments of 512 (the
+    # last 464), initial states.  y and the final state bit for bit those of
+    # the split forward without saving; the saved states those of the oracle's
+    # prefixes (segment starts included); the backward from them the oracle's
+    w = workloads.make_custom(2, 2000, 4, 64, N, 2, 256, "bf16", seed=3300 + N, init_std=0.3)
+    dy, dfinal = workloads.make_output_grads(w, 15)
+    t = upload(w)
+    y1, f1 = ssd.fused_fwd_split(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"],
+                                 seg_len=512)
+    st = ssd.make_fused_states(t["x"], t["B"])
+    y2, f2 = ssd.fused_fwd_split(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"],
+                                 seg_len=512, chunk_states=st)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+    H, P, L = w.nheads, w.headdim, w.seqlen
+    npair = (L + 63) // 64
+    hs = st.view(torch.bfloat16)[: w.batch * npair * H * P * N].float().cpu().numpy()
+    hs = hs.reshape(w.batch, npair, H, P, N)
+    worst = 0.0
+    for b in range(w.batch):
+        sl = slice(b * L, (b + 1) * L)
+        for k in (0, 1, 7, 8, 9, 16, 24, npair - 1):  # pairs 8, 16, 24 start segments
+            n = 64 * k
+            if n == 0:
+                ref = w.h0[b].astype(np.float64)
+            else:
+                _, f = oracle.recurrence(w.x[sl][:n], w.dt[sl][:n], w.A, w.B[sl][:n],
+                                         w.C[sl][:n], w.D, w.h0[b:b + 1], np.array([0, n]))
+                ref = f[0]
+            worst = max(worst, rel(hs[b, k], ref))
+    say(f"  split saving N{N}: saved states rel err {worst:.3e}")
+    assert worst <= 1e-2
+    dyd = torch.from_numpy(dy).to(DEV).to(torch.bfloat16).view(t["x"].shape)
+    g = ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], st, dyd,
+                      torch.from_numpy(dfinal).to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.recurrence_bwd(w.x, w.dt, w.A, w.B, w.C, w.D, w.h0, w.seq_off, dy, dfinal)
+    check_grads(w, g, ref, f"bwd from the split one-pass forward's states N{N}")
+
+
+def test_long_n128_split_one_pass_saving_sampled():
+    # the 65,536-token sequence at the library's segment length: the backward
+    # from the split one-pass forward's saved states, sampled heads
+    w = workloads.make_workload("long_n128")
+    dy, dfinal = workloads.make_output_grads(w, 16)
+    t = upload(w)
+    S = ssd.fused_split_seg_len(t["x"], t["B"])
+    st = ssd.make_fused_states(t["x"], t["B"])
+    ssd.fused_fwd_split(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["h0"], seg_len=S,
+                        chunk_states=st)
+    dyd = torch.from_numpy(dy).to(DEV).to(torch.bfloat16).view(t["x"].shape)
+    g = ssd.fused_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], st, dyd,
+                      torch.from_numpy(dfinal).to(DEV))
+    torch.cuda.synchronize()
+    sampled_check(w, g, [(0, 3), (0, 50)], f"bwd long_n128 from the split one-pass forward S{S}",
+                  dy, dfinal)
+
+
 def test_long_n64_split_training_forward_sampled():
     # the training step's forward at this shape (SSDTrainForward: chunk 256 for
     # y, chunk 64 for the states), then the segmented backward from its states
