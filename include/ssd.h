@@ -444,9 +444,10 @@ size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
  * else SSD_ERR_UNSUPPORTED (and ssd_fused_bwd_workspace_size returns 0).  On
  * `stream`: dA and dD cleared; the reverse sweep of the
  * state gradient (one pass per (sequence, two heads), or, with fewer such
- * pairs than 256, per 256-token segment: segment sums, a chained pass, the
- * segments again); the per-chunk gradients, which add into dA and dD with
- * float atomics, so those two sum in an unspecified order.  N = 256 runs
+ * pairs than 256, per segment: segment sums, a chained pass, the segments
+ * again; segments of the longest power of two from 256 tokens that still
+ * gives 1024 (segment, head pair) blocks); the per-chunk gradients, which add
+ * into dA and dD with float atomics, so those two sum in an unspecified order.  N = 256 runs
  * these steps once per half of the state's columns (the columns never mix in
  * the recurrence): each half's B, C, saved states and dfinal are copied into
  * the workspace, its dB, dC and dinit copied back into their columns, and

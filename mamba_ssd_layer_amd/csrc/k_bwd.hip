@@ -102,7 +102,7 @@ __device__ __forceinline__ int swz2(int r) {
 }
 
 // ---------------------------------------------------------------- pass 2
-// Block = (sequence or 256-token segment of one, two heads of a group), 4
+// Block = (sequence or segment of one, two heads of a group), 4
 // wavefronts (head hh, half ph); wavefront (hh, ph) keeps rows p in
 // [32 ph, 32 ph + 32) of head hh's g, held transposed like the forward's state
 // (tiles 2q, 2q+1 give lane group g4 the n = 32q + 8 g4 + 0..7).  Chunks in
@@ -110,12 +110,11 @@ __device__ __forceinline__ int swz2(int r) {
 // chunks in flight ahead of the one being computed.
 // MODE: RV_FULL walks a whole sequence from dfinal, saves g where each 64-token
 // pair ends and writes dL/dh0; for few (sequence, head-pair) blocks the sweep is
-// split into 256-token segments: RV_SEGSUM walks a segment from g = 0 and writes
-// its sum G_seg and its total decay (log) A_seg, k_bwd_gpass chains them, and
-// RV_SEG walks each segment again from the gradient entering it from the
-// right (gin) and saves g at its pair ends.
+// split into segments of segc 32-token chunks: RV_SEGSUM walks a segment from
+// g = 0 and writes its sum G_seg and its total decay (log) A_seg, k_bwd_gpass
+// chains them, and RV_SEG walks each segment again from the gradient entering
+// it from the right (gin) and saves g at its pair ends.
 enum { RV_FULL = 0, RV_SEGSUM = 1, RV_SEG = 2 };
-constexpr int kSegChunks = 8;  // 32-token chunks per segment
 // ring slots: kRevSlots - 1 chunks in flight (a fourth slot measured no faster:
 // the sweep is bound by its state-gradient stores, not by load latency)
 constexpr int kRevSlots = 3;
@@ -124,7 +123,7 @@ template <int N, int MODE, int R>
 __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     const uint16_t *__restrict__ dy, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Cm, const float *__restrict__ gstart,
-    const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows, int H, int G,
+    const int32_t *__restrict__ cu, int64_t L, int64_t T, int rows, int H, int G, int segc,
     uint16_t *__restrict__ gsave, float *__restrict__ gout, float *__restrict__ aseg) {
   constexpr int P = 64, CQ = 32, D = R - 1;  // D chunks in flight ahead
   constexpr int NT = N / 16, KQ = N / 32, NCB = N / 8;
@@ -152,7 +151,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
     gs = gsi;
     int64_t seg = -1;
     if (!cu) {
-      const int64_t nsr = (L + kSegChunks * CQ - 1) / (kSegChunks * CQ);
+      const int64_t nsr = (L + (int64_t)segc * CQ - 1) / ((int64_t)segc * CQ);
       if (nsr == 0) return;
       s = static_cast<int>(gs / nsr);
       seg = gs % nsr;
@@ -160,13 +159,13 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
       seq_range(cu, s, L, T, tb, len);
     } else {
       int64_t before;
-      s = locate_unit(cu, rows, T, gs, kSegChunks * CQ, before);
+      s = locate_unit(cu, rows, T, gs, segc * CQ, before);
       if (s < 0) return;
       seg = gs - before;
       seq_range(cu, s, L, T, tb, len);
     }
-    kb = static_cast<int>(seg) * kSegChunks;
-    ke = min(kb + kSegChunks, static_cast<int>((len + CQ - 1) / CQ));
+    kb = static_cast<int>(seg) * segc;
+    ke = min(kb + segc, static_cast<int>((len + CQ - 1) / CQ));
   }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -322,17 +321,17 @@ __global__ __launch_bounds__(256, 2) void k_bwd_reverse(
 __global__ __launch_bounds__(256) void k_bwd_gpass(
     const float *__restrict__ gseg, const float *__restrict__ aseg,
     const float *__restrict__ dfinal, const int32_t *__restrict__ cu, int64_t L, int64_t T,
-    int rows, int H, int PN, float *__restrict__ gin, float *__restrict__ dinit) {
+    int rows, int H, int PN, int segt, float *__restrict__ gin, float *__restrict__ dinit) {
   const int s = blockIdx.z, h = blockIdx.y;
   const int e = 4 * (blockIdx.x * 256 + threadIdx.x);
   if (s >= rows) return;
-  constexpr int SEGT = kSegChunks * 32;
-  // (all lanes take part in the walk over the sequences before returning)
-  const int64_t base = cu ? units_before(cu, s, T, SEGT) : (int64_t)s * ((L + SEGT - 1) / SEGT);
+  // segt: tokens per segment (all lanes take part in the walk over the
+  // sequences before returning)
+  const int64_t base = cu ? units_before(cu, s, T, segt) : (int64_t)s * ((L + segt - 1) / segt);
   if (e >= PN) return;
   int64_t tb, len;
   seq_range(cu, s, L, T, tb, len);
-  const int nseg = static_cast<int>((len + SEGT - 1) / SEGT);
+  const int nseg = static_cast<int>((len + segt - 1) / segt);
   const int64_t sh = (int64_t)s * H + h;
   f32x4 gv = dfinal ? *reinterpret_cast<const f32x4 *>(dfinal + sh * PN + e) : f32x4{};
 #pragma unroll 1
@@ -883,16 +882,18 @@ __global__ __launch_bounds__(256) void k_fill_f32(float *__restrict__ p, int64_t
 hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, const void *C,
                               const float *dfinal, const int32_t *cu, int64_t L, int64_t T,
                               int rows, int H, int N, int G, void *gsave, float *dinit,
-                              int64_t nseg, float *gseg, float *aseg, float *gin,
+                              int64_t nseg, int seg_len, float *gseg, float *aseg, float *gin,
                               hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  if (N != 64 && N != 128) return hipErrorInvalidValue;
+  if ((N != 64 && N != 128) || (nseg > 0 && (seg_len < 32 || seg_len % 32 != 0)))
+    return hipErrorInvalidValue;
+  const int segc = seg_len / 32;
   const uint16_t *d = static_cast<const uint16_t *>(dy);
   const uint16_t *c = static_cast<const uint16_t *>(C);
   uint16_t *gs = static_cast<uint16_t *>(gsave);
   auto rev = [&](auto kern, int64_t units, const float *gstart, float *gout) {
     hipLaunchKernelGGL(kern, dim3(xcd_grid(units, H / 2)), dim3(256), 0, stream, d, dt, A, c, gstart,
-                       cu, L, T, rows, H, G, gs, gout, aseg);
+                       cu, L, T, rows, H, G, segc, gs, gout, aseg);
     return hipGetLastError();
   };
   if (nseg == 0) {
@@ -904,7 +905,7 @@ hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, c
   if (e != hipSuccess) return e;
   const int PN = 64 * N;
   hipLaunchKernelGGL(k_bwd_gpass, dim3(PN / 1024, H, rows), dim3(256), 0, stream, gseg, aseg,
-                     dfinal, cu, L, T, rows, H, PN, gin, dinit);
+                     dfinal, cu, L, T, rows, H, PN, seg_len, gin, dinit);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   return N == 64 ? rev(k_bwd_reverse<64, RV_SEG, kRevSlots>, nseg, gin, nullptr)
                  : rev(k_bwd_reverse<128, RV_SEG, kRevSlots>, nseg, gin, nullptr);

@@ -495,13 +495,29 @@ size_t chunk_states_bytes(const Plan &p) {
 
 // The backward's reverse sweep runs one block per (sequence, two heads); with
 // fewer such blocks than the GPU has CUs (256 on MI355X) it is split into
-// 256-token segments instead.  The decision depends on the dims only.
+// segments instead.  The decisions depend on the dims only.
 bool bwd_segmented(const Plan &p) { return p.geo.nrows * (p.geo.H / 2) < 256; }
 
-// 256-token segments of the batch (packed: an upper bound, ceil(T/256) + nseq)
-int64_t segments256(const Plan &p) {
+// Segments of seg_len tokens in the batch (packed: an upper bound,
+// ceil(T / seg_len) + nseq)
+int64_t bwd_segments(const Plan &p, int64_t seg_len) {
   const ssd::Geometry &g = p.geo;
-  return g.packed ? ceil_div(g.tokens, 256) + g.nrows : g.nrows * ceil_div(g.L, 256);
+  return g.packed ? ceil_div(g.tokens, seg_len) + g.nrows : g.nrows * ceil_div(g.L, seg_len);
+}
+
+// The segment length: the longest power of two from 256 tokens up that still
+// gives at least 1024 (segment, head pair) blocks, four a CU.  Longer segments
+// move fewer segment sums and entering gradients (fp32 P x N tiles, written and
+// read twice) at the same parallelism.
+int64_t bwd_seg_len(const Plan &p) {
+  const ssd::Geometry &g = p.geo;
+  const int64_t pairs = g.H / 2;
+  auto blocks = [&](int64_t S) {
+    return (g.packed ? ceil_div(g.tokens, S) : g.nrows * ceil_div(g.L, S)) * pairs;
+  };
+  int64_t S = 256;
+  while (S < ((int64_t)1 << 20) && blocks(2 * S) >= 1024) S *= 2;
+  return S;
 }
 
 // Backward workspace: the state gradients per pair (bf16), then, when the
@@ -509,7 +525,7 @@ int64_t segments256(const Plan &p) {
 // segment decays.
 struct BwdWorkspace {
   size_t gsave, gseg, gin, aseg, total;
-  int64_t nseg;
+  int64_t nseg, seglen;
   // N = 256, after one half's own workspace: its B, C and d(final_state), its
   // dx and ddt (the second half's, added to the first's), dB, dC and
   // d(init_state)
@@ -544,7 +560,8 @@ BwdWorkspace bwd_workspace(const Plan &p) {
   w.gsave = 0;
   size_t off = chunk_states_bytes(p);
   if (bwd_segmented(p)) {
-    w.nseg = segments256(p);
+    w.seglen = bwd_seg_len(p);
+    w.nseg = bwd_segments(p, w.seglen);
     const size_t tile = (size_t)w.nseg * p.geo.H * p.geo.P * p.geo.N * 4;
     w.gseg = off;
     off += align_up(tile);
@@ -595,7 +612,8 @@ hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const
                                512, frows, 32, st);
     if (e == hipSuccess)
       e = ssd::launch_bwd_reverse(dy, dt, A, Ch, dfh, cu, g.L, g.tokens, (int)g.nrows, g.H, 128,
-                                  g.G, workspace, dih, bw.nseg, ws_ptr<float>(workspace, bw.gseg),
+                                  g.G, workspace, dih, bw.nseg, (int)bw.seglen,
+                                  ws_ptr<float>(workspace, bw.gseg),
                                   ws_ptr<float>(workspace, bw.aseg),
                                   ws_ptr<float>(workspace, bw.gin), st);
     if (e == hipSuccess)
@@ -935,9 +953,9 @@ ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const v
   if (e == hipSuccess && dD) e = ssd::launch_fill_f32(dD, g.H, st);
   if (e == hipSuccess)
     e = ssd::launch_bwd_reverse(dy, dt, A, C, dfinal, cu, g.L, g.tokens, (int)g.nrows, g.H, g.N,
-                                g.G, workspace, dinit, bw.nseg, ws_ptr<float>(workspace, bw.gseg),
-                                ws_ptr<float>(workspace, bw.aseg), ws_ptr<float>(workspace, bw.gin),
-                                st);
+                                g.G, workspace, dinit, bw.nseg, (int)bw.seglen,
+                                ws_ptr<float>(workspace, bw.gseg), ws_ptr<float>(workspace, bw.aseg),
+                                ws_ptr<float>(workspace, bw.gin), st);
   if (e == hipSuccess)
     e = ssd::launch_bwd_chunk(x, dt, A, B, C, D, dy, chunk_states, g.N, workspace, cu, g.L, g.tokens,
                               (int)g.nrows, chunks32(p), g.H, g.N, g.G, dx, ddt, dA, dB, dC, dD,

@@ -87,12 +87,13 @@ hipError_t launch_fused_split(const void *x, const float *dt, const float *A, co
                               float *hfin, float *sseg, float *lseg, void *hsave,
                               hipStream_t stream);
 // backward of the one-pass forward (bf16, P == 64, N in {64, 128}, even heads per group)
-// nseg > 0: the sweep split into that many 256-token segments (gseg, gin
-// [nseg][H][P][N] and aseg [nseg][H] fp32 scratch); 0: one pass per sequence
+// nseg > 0: the sweep split into that many segments of seg_len tokens (a
+// multiple of 32; gseg, gin [nseg][H][P][N] and aseg [nseg][H] fp32 scratch);
+// 0: one pass per sequence
 hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, const void *C,
                               const float *dfinal, const int32_t *cu, int64_t L, int64_t T,
                               int rows, int H, int N, int G, void *gsave, float *dinit,
-                              int64_t nseg, float *gseg, float *aseg, float *gin,
+                              int64_t nseg, int seg_len, float *gseg, float *aseg, float *gin,
                               hipStream_t stream);
 // hsave: the saved states, rows of hsld >= N elements (N, or 2N when hsave
 // points into one half of the columns of N = 256 states)

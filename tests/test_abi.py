@@ -399,6 +399,15 @@ def test_fused_states_size():
     assert L.ssd_fused_bwd_workspace_size(ctypes.byref(dp)) == ws
     big = make_dims(8, 4096, 80, 64, 128, 1, 0, SSD_BF16)  # 8 x 40 blocks: one pass per sequence
     assert L.ssd_fused_bwd_workspace_size(ctypes.byref(big)) == 8 * 64 * 80 * 64 * 128 * 2
+    # one 65,536-token sequence, 80 heads (40 head pairs): segments of 2048
+    # tokens, the longest power of two giving at least 1024 (segment, head pair)
+    # blocks (4096 would give 640); packed, ceil(T / 2048) + nseq segments
+    per = lambda nseg, N: 2 * nseg * 80 * 64 * N * 4 + -(-(nseg * 80 * 4) // 256) * 256
+    ln = make_dims(1, 65536, 80, 64, 128, 1, 0, SSD_BF16)
+    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(ln)) == 1024 * 80 * 64 * 128 * 2 + per(32, 128)
+    lp = make_dims(1, 65536, 80, 64, 64, 1, 2, SSD_BF16)
+    assert L.ssd_fused_bwd_workspace_size(ctypes.byref(lp)) == \
+        (1024 + 2) * 80 * 64 * 64 * 2 + per(32 + 2, 64)
     # N 256: the workspace of an N 128 backward (two halves run in turn), then
     # one half's B, C, d(final), dx, ddt, dB, dC, d(init)
     d = good()  # 2 x 512 tokens, H 4, P 64, G 1

@@ -384,6 +384,21 @@ def test_long_n128_split_one_pass_saving_sampled():
                   dy, dfinal)
 
 
+def test_packed_long_sequences_sampled():
+    # two packed sequences of 40,000 and 25,536 tokens, 80 heads: 80 (sequence,
+    # head pair) blocks, so the reverse sweep runs in 2048-token segments over
+    # packed sequences (a segment may end at a sequence's end); sampled heads
+    # of both sequences (the state gradient the segments hand on enters dx,
+    # ddt and d(init_state))
+    w = workloads.make_custom(1, 0, 80, 64, 128, 1, 256, "bf16", seed=3400, lens=[40000, 25536],
+                              init_std=0.3)
+    dy, dfinal = workloads.make_output_grads(w, 17)
+    t = upload(w)
+    _, _, _, g = fwd_bwd(w, t, dy, dfinal)
+    pairs = [(0, 0), (0, 47), (1, 13), (1, 79)]
+    sampled_check(w, g, pairs, "bwd two long packed sequences, sampled", dy, dfinal)
+
+
 def test_long_n64_split_training_forward_sampled():
     # the training step's forward at this shape (SSDTrainForward: chunk 256 for
     # y, chunk 64 for the states), then the segmented backward from its states
