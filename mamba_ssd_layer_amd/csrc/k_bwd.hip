@@ -346,7 +346,7 @@ __global__ __launch_bounds__(256) void k_bwd_gpass(
 }
 
 // ---------------------------------------------------------------- pass 3
-// Block = (32-token chunk, group), 8 wavefronts (two per SIMD), walking the
+// Block = (32-token chunk, group), 16 wavefronts (four per SIMD), walking the
 // group's heads.  LDS: the chunk's B and C (rows = tokens) and the neighbour
 // chunk's B or C; an R-slot ring per head of x and dy (rows = tokens, 8 chunks
 // a row), the pair's saved h_s and g_e (rows = p, N/8 chunks a row), dt, and
@@ -360,20 +360,18 @@ __global__ __launch_bounds__(256) void k_bwd_gpass(
 // transposing reads of token rows in that order for the A operand.  An
 // "ET-layout" tile (st, lt) holds matrix[s][l] the same way.
 // Per head: wavefronts 0-3 form one E-layout tile each of E = dy x^T and from
-// it M = Z o L dt_s, EL = E o L dt_s and the sums of K = E o Z o L dt_s;
-// wavefronts 4-7 one ET-layout tile each of E^T and EL^T; all of them derive
-// N/32 tiles of the state the pair does not hold for this chunk (in place);
-// after a barrier each wavefront computes one 16 x 16 tile of dx (p-tile w/2,
-// s-tile w%2) with the matching tile of h_s C^T, and N/64 tiles of dB and dC.
-// With W = 16 wavefronts (four a SIMD; the LDS is the same) the head's work
-// is spread thinner: wavefronts 0-7 form the E / ET tiles as above, 8-15 the
-// derived state; after the barrier wavefronts 0-7 take the g_e side (dx tile,
-// q_s, dB) and 8-15 the h_s side (h_s C^T and v_l, <g_e, h_s>, dC), and only
-// wavefront 4 finishes the previous head's per-token scalars.
-template <int N, int R, int W = 8>
+// it M = Z o L dt_s, EL = E o L dt_s and the sums of K = E o Z o L dt_s,
+// wavefronts 4-7 one ET-layout tile each of E^T and EL^T, and wavefronts 8-15
+// derive N/32 tiles each of the state the pair does not hold for this chunk
+// (in place).  After a barrier wavefront w < 8 takes the g_e side: one 16 x 16
+// tile of dx (p-tile w/2, s-tile w%2), its q_s partial and N/64 tiles of dB;
+// wavefront 8 + w the h_s side: the matching tile of h_s C^T for v_l,
+// <g_e, h_s> over p-tile w/2 (w even) and N/64 tiles of dC.  Wavefront 4
+// finishes the previous head's per-token scalars.  (Eight wavefronts, two a
+// SIMD, each doing both sides, measured 6-8% slower.)
+template <int N, int R>
 struct BwdCfg {
-  static constexpr int P = 64, CQ = 32, NCB = N / 8, WAVES = W;
-  static constexpr bool SPLIT = W == 16;
+  static constexpr int P = 64, CQ = 32, NCB = N / 8, WAVES = 16;
   static constexpr int XT = CQ * P * 2;      // x or dy of a head: 32 rows x 128 B
   static constexpr int ST = P * N * 2;       // h_s or g_e of a head: 64 rows x N bf16
   static constexpr int BT = CQ * N * 2;      // B or C of a chunk
@@ -389,18 +387,19 @@ struct BwdCfg {
   static constexpr int OPART = OTAB + 2 * WAVES * TABW;  // per buffer: the partial sums below
   static constexpr int PARTW = 512 * 4;
   static constexpr int TOTAL = OPART + 2 * PARTW;
-  static constexpr int KP = ST / 1024 / WAVES;           // h_s (and g_e) pieces per wavefront
-  static constexpr int NTW = N / 64;                     // tiles of dB (and dC) per wavefront (W = 8),
-                                                         // of dB or of dC (W = 16)
+  static constexpr int KP = ST / 1024 / WAVES;           // h_s (and g_e) pieces per wavefront; 0:
+                                                         // one piece a wavefront, h_s for the
+                                                         // first half of them, g_e for the rest
+  static constexpr int NTW = N / 64;                     // tiles of dB (or of dC) per wavefront
   static constexpr int DTW = N / 32;                     // tiles of the derived state per wavefront
-                                                         // that derives (all 8, or 8-15 of 16)
-  static_assert(W == 8 || W == 16, "wavefronts a block");
-  static_assert(KP >= 1 && KP * WAVES * 1024 == ST, "state pieces");
+                                                         // of the eight that derive
+  static_assert((KP >= 1 && KP * WAVES * 1024 == ST) || (KP == 0 && 2 * ST == WAVES * 1024),
+                "state pieces");
   static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
-template <int N, int R, int W = 8>
-__global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
+template <int N, int R>
+__global__ __launch_bounds__(1024, 1) void k_bwd_chunk(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
     const uint16_t *__restrict__ dy, const uint16_t *__restrict__ hsave, int hsld,
@@ -408,10 +407,9 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
     int rows, int64_t nchunks, int H, int G, uint16_t *__restrict__ dx,
     float *__restrict__ ddt, float *__restrict__ dA, float *__restrict__ dB,
     float *__restrict__ dC, float *__restrict__ dD) {
-  using F = BwdCfg<N, R, W>;
+  using F = BwdCfg<N, R>;
   constexpr int P = F::P, CQ = F::CQ, NCB = F::NCB, KP = F::KP, NTW = F::NTW;
-  constexpr bool SPLIT = F::SPLIT;
-  constexpr int NT = 64 * W;  // threads
+  constexpr int W = F::WAVES, NT = 64 * W;  // wavefronts, threads
   constexpr int KQ = N / 32;  // K steps over n
   __shared__ __align__(16) unsigned char smem[F::TOTAL];
 
@@ -502,12 +500,13 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
   // x (wavefronts 0-3) or dy (4-7) piece wave % 4 (rows 8 (wave % 4) .. +7,
   // clamped to the chunk's end); h_s and g_e pieces wave + W k (the swizzle
   // repeats every 16 rows, so piece k's offsets are piece 0's plus 8 KB k); dt;
-  // the neighbour chunk's x or dy piece wave % 4 (wavefronts 0-3, or 8-11 of 16).
+  // the neighbour chunk's x or dy piece wave % 4 (wavefronts 8-11).
   uint32_t xoff, hoff, hsoff, dtoff, nxoff, ndtoff;
   {
     const int m = (wave & 3) * 64 + lane, r = m >> 3, cc = (m & 7) ^ swz2<8>(r);
     xoff = static_cast<uint32_t>((min(r, last) * ldx + 8 * cc) * 2);
-    const int mh = wave * 64 + lane, rh = mh / NCB, ch = (mh % NCB) ^ swz2<NCB>(rh);
+    const int mh = (KP ? wave : wave % (W / 2)) * 64 + lane, rh = mh / NCB,
+              ch = (mh % NCB) ^ swz2<NCB>(rh);
     hoff = static_cast<uint32_t>((rh * N + 8 * ch) * 2);
     hsoff = static_cast<uint32_t>((rh * hsld + 8 * ch) * 2);
     dtoff = static_cast<uint32_t>(min(tl, last) * H * 4);
@@ -515,24 +514,31 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
     ndtoff = static_cast<uint32_t>(min(tl, lastn) * H * 4);
   }
   // the wavefronts that load the neighbour chunk's x / dy pieces and its dt
-  const bool nxw = SPLIT ? (wave >= 8 && wave < 12) : wave < 4;
-  const int ndtw = SPLIT ? 12 : 1;
+  const bool nxw = wave >= 8 && wave < 12;
+  const int ndtw = 12;
   // head j's x, dy, h_s, g_e and dt into ring slot sl: scalar bases, fixed lane offsets
   auto issue_head = [&](int j, int sl) {
     const int h = g * hpg + j;
     const uint32_t base = lbase + sl * F::HSLOT;
-    if (!SPLIT || wave < 8)
+    if (wave < 8)
       dma_lds16_sb(xoff, (wave < 4 ? x : dy) + t0 * ldx + (int64_t)h * P,
                    base + (wave < 4 ? F::OX : F::OY) + (wave & 3) * 1024);
     const int64_t st0 = (pidx * H + h) * (int64_t)(P * N);
     const int64_t sh0 = (pidx * H + h) * (int64_t)P * hsld;
+    if constexpr (KP == 0) {
+      if (wave < W / 2)
+        dma_lds16_sb(hsoff, hsave + sh0, base + F::OH + wave * 1024);
+      else
+        dma_lds16_sb(hoff, gsave + st0, base + F::OG + (wave - W / 2) * 1024);
+    } else {
 #pragma unroll
-    for (int kk = 0; kk < KP; ++kk)
-      dma_lds16_sb(hsoff, hsave + sh0 + (int64_t)(512 * W / N) * hsld * kk,
-                   base + F::OH + (wave + W * kk) * 1024);
+      for (int kk = 0; kk < KP; ++kk)
+        dma_lds16_sb(hsoff, hsave + sh0 + (int64_t)(512 * W / N) * hsld * kk,
+                     base + F::OH + (wave + W * kk) * 1024);
 #pragma unroll
-    for (int kk = 0; kk < KP; ++kk)
-      dma_lds16_sb(hoff, gsave + st0 + 512 * W * kk, base + F::OG + (wave + W * kk) * 1024);
+      for (int kk = 0; kk < KP; ++kk)
+        dma_lds16_sb(hoff, gsave + st0 + 512 * W * kk, base + F::OG + (wave + W * kk) * 1024);
+    }
     if (wave == 0) dma_lds4_sb(dtoff, dt + t0 * H + h, base + F::ODT);
     if (mode != NONE) {  // the neighbour chunk's x (for h_s) or dy (for g_e), and dt
       if (nxw)
@@ -544,11 +550,12 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
 
   // ---- the chunk's B and C, then heads 0 .. R-2 ahead ----
   {
-    constexpr int BCP = 2 * F::BT / 1024 / W;
-    static_assert(BCP >= 1 && BCP * W * 1024 == 2 * F::BT, "B and C pieces");
+    // pieces u = wave, wave + W, ... of the 2 BT / 1024 of B and C
+    constexpr int NBCP = 2 * F::BT / 1024;
 #pragma unroll
-    for (int i = 0; i < BCP; ++i) {
-      const int u = wave * BCP + i, tile = u / (F::BT / 1024), pi = u % (F::BT / 1024);
+    for (int i = 0; i < (NBCP + W - 1) / W; ++i) {
+      const int u = wave + W * i, tile = u / (F::BT / 1024), pi = u % (F::BT / 1024);
+      if (u >= NBCP) break;
       const int m = pi * 64 + lane, r = m / NCB, cc = (m % NCB) ^ swz2<NCB>(r);
       dma_lds16((tile ? Cm : Bm) + (t0 + min(r, last)) * ldb + (int64_t)g * N + 8 * cc,
                 lbase + (tile ? F::OCC : F::OB) + pi * 1024);
@@ -562,11 +569,11 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
   }
   // vector-memory ops a wavefront issues per head: its x or dy piece, the
   // h_s and g_e pieces, dt, the neighbour chunk's piece and dt
-  const int LDW = (!SPLIT || wave < 8 ? 1 : 0) + 2 * KP + (wave == 0 ? 1 : 0) +
+  const int LDW = (wave < 8 ? 1 : 0) + (KP ? 2 * KP : 1) + (wave == 0 ? 1 : 0) +
                   (mode != NONE ? (nxw ? 1 : 0) + (wave == ndtw ? 1 : 0) : 0);
   // stores and atomics a wavefront issues in iteration m: its dx tile of head
-  // m (every wavefront, or 0-7 of 16); wavefront 4 also ddt, dA, dD of head m - 1
-  const int dxw = !SPLIT || wave < 8 ? 1 : 0;
+  // m (wavefronts 0-7); wavefront 4 also ddt, dA, dD of head m - 1
+  const int dxw = wave < 8 ? 1 : 0;
   auto stw = [&](int m) { return dxw + (wave == 4 && m >= 1 ? 2 + (dD ? 1 : 0) : 0); };
 #pragma unroll
   for (int jj = 0; jj < R - 1; ++jj)
@@ -578,9 +585,8 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
   const bool etile = wave < 4;               // E-layout tile (lt, st) = (wave / 2, wave % 2)
   const int qa = (wave >> 1) & 1, qb = wave & 1;  // E: (lt, st) = (qa, qb); ET: (st, lt) = (qa, qb)
   const int pt = (wave & 7) >> 1, sh = wave & 1;  // dx / h_s C^T tile (p-tile, s- or l-tile)
-  // the wavefront that finishes a head's per-token scalars (W = 8: all of 4-7
-  // compute them, 4 writes)
-  const bool fin = SPLIT ? wave == 4 : !etile;
+  // the wavefront that finishes a head's per-token scalars
+  const bool fin = wave == 4;
   // Z = C B^T, the E-layout tile (qa, qb) (wavefronts 0-3)
   f32x4 z{};
   if (etile) {
@@ -588,12 +594,9 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
     for (int q = 0; q < KQ; ++q) z = mfma16b(rown(csm, 16 * qa + c16, q), rown(bsm, 16 * qb + c16, q), z);
   }
 
-  f32x4 dBa[NTW], dCa[NTW];
+  f32x4 dBa[NTW];  // this wavefront's tiles of dB (wavefronts 0-7) or dC (8-15)
 #pragma unroll
-  for (int i = 0; i < NTW; ++i) {
-    dBa[i] = f32x4{};
-    dCa[i] = f32x4{};
-  }
+  for (int i = 0; i < NTW; ++i) dBa[i] = f32x4{};
 
   // ---- per-token scalars of head jj (its partials complete): computed by
   // wavefronts 4-7 (one per SIMD, while 0-3 start the next head's heavier
@@ -741,7 +744,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
         const int r = c16 & 3;
         part[PDE + sx] = r == 0 ? e.x : r == 1 ? e.y : r == 2 ? e.z : e.w;
       }
-    } else if (!SPLIT || wave < 8) {
+    } else if (wave < 8) {
       // ET-layout (st, lt) = (qa, qb): s = 16 qa + 4 g4 + r, l = 16 qb + c16
       f32x4 et{};
 #pragma unroll
@@ -760,7 +763,7 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
       *reinterpret_cast<u32x2 *>(opelt + qb * 1024 + lane * 16 + qa * 8) =
           u32x2{pack_bf16x2(ev[0], ev[1]), pack_bf16x2(ev[2], ev[3])};
     }
-    if (mode != NONE && (!SPLIT || wave >= 8)) {
+    if (mode != NONE && wave >= 8) {
       // the derived state, in place over the loaded one: h_s = exp(a'_last)
       // h_s' + B'^T (w' x') (the chunk before), or g_e = exp(a'_last) g_e' +
       // C'^T (exp(a') dy') (the chunk after); tiles (p-tile, n-tile nd) with
@@ -794,10 +797,11 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
 
     // ---- phase 2 ----
     const float Dh = Dv ? Dv[h] : 0.f;
-    if constexpr (SPLIT) {
-      // the same products as below, wavefronts 0-7 on the g_e side and 8-15 on
-      // the h_s side; dBa holds this wavefront's tiles of dB (g_e side) or dC
-      const int nt = wave & 7;  // n-tile of dB or dC (s-tiles 0 .. NTW - 1)
+    {
+      // wavefronts 0-7 on the g_e side, 8-15 on the h_s side; dBa holds this
+      // wavefront's tiles of dB (g_e side) or dC
+      // n-tile of dB or dC, s-tiles t0d .. t0d + NTW - 1
+      const int nt = (NTW * (wave & 7)) >> 1, t0d = (NTW * (wave & 7)) & 1;
       const int sx = 16 * sh + c16, col = 16 * pt + 4 * g4;
       const int ro = sx * 128 + (((col >> 3) ^ swz2<8>(sx)) << 4) + (col & 7) * 2;
       const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + ro);
@@ -832,12 +836,13 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
           gsT[kq] = trn(gss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-          const u32x4 elop = *reinterpret_cast<const u32x4 *>(opel + i * 1024 + lane * 16);
+          const int t = t0d + i;
+          const u32x4 elop = *reinterpret_cast<const u32x4 *>(opel + t * 1024 + lane * 16);
           dBa[i] = mfma16b(ct, elop, dBa[i]);
           f32x4 gx{};
 #pragma unroll
-          for (int kq = 0; kq < 2; ++kq) gx = mfma16b(gsT[kq], rowx(xs, 16 * i + c16, kq), gx);
-          dBa[i] += gx * tab[TW + 16 * i + c16];
+          for (int kq = 0; kq < 2; ++kq) gx = mfma16b(gsT[kq], rowx(xs, 16 * t + c16, kq), gx);
+          dBa[i] += gx * tab[TW + 16 * t + c16];
         }
       } else {
         u32x4 hr[KQ];
@@ -868,98 +873,16 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
           hsT[kq] = trn(hss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-          const u32x4 eltop = *reinterpret_cast<const u32x4 *>(opelt + i * 1024 + lane * 16);
+          const int t = t0d + i;
+          const u32x4 eltop = *reinterpret_cast<const u32x4 *>(opelt + t * 1024 + lane * 16);
           dBa[i] = mfma16b(bt, eltop, dBa[i]);
           f32x4 hy{};
 #pragma unroll
-          for (int kq = 0; kq < 2; ++kq) hy = mfma16b(hsT[kq], rowx(ys, 16 * i + c16, kq), hy);
-          dBa[i] += hy * tab[TF + 16 * i + c16];
+          for (int kq = 0; kq < 2; ++kq) hy = mfma16b(hsT[kq], rowx(ys, 16 * t + c16, kq), hy);
+          dBa[i] += hy * tab[TF + 16 * t + c16];
         }
       }
-    } else {
-    {
-      // rows 16 pt + c16 of g_e and h_s (n = 32 q + 8 g4 + 0..7): the A
-      // operands of g_e B^T and h_s C^T, and together all of p-tile pt
-      u32x4 gr[KQ], hr[KQ];
-#pragma unroll
-      for (int q = 0; q < KQ; ++q) {
-        gr[q] = rown(gss, 16 * pt + c16, q);
-        hr[q] = rown(hss, 16 * pt + c16, q);
-      }
-      // dx tile (p-tile pt, s-tile sh): dy^T M + w_s g_e B^T + D dy; q_s partial
-      const u32x4 dyt = trn(ys, 128, 4 * g4, 16 + 4 * g4, 16 * pt, false);
-      const u32x4 mop = *reinterpret_cast<const u32x4 *>(opm + sh * 1024 + lane * 16);
-      f32x4 acc = mfma16b(dyt, mop, f32x4{});
-      f32x4 gb{}, hc{};
-#pragma unroll
-      for (int q = 0; q < KQ; ++q) {
-        gb = mfma16b(gr[q], rown(bsm, 16 * sh + c16, q), gb);
-        hc = mfma16b(hr[q], rown(csm, 16 * sh + c16, q), hc);
-      }
-      // lane: column s (or l) = 16 sh + c16, rows p = 16 pt + 4 g4 + r
-      const int sx = 16 * sh + c16, col = 16 * pt + 4 * g4;
-      const float ws = tab[TW + sx];
-      const int ro = sx * 128 + (((col >> 3) ^ swz2<8>(sx)) << 4) + (col & 7) * 2;
-      const u32x2 dv = *reinterpret_cast<const u32x2 *>(ys + ro);
-      const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + ro);
-      const float o0 = acc.x + ws * gb.x + Dh * bf16lo(dv.x);
-      const float o1 = acc.y + ws * gb.y + Dh * bf16hi(dv.x);
-      const float o2 = acc.z + ws * gb.z + Dh * bf16lo(dv.y);
-      const float o3 = acc.w + ws * gb.w + Dh * bf16hi(dv.y);
-      if (sx <= last)
-        *reinterpret_cast<u32x2 *>(dx + (t0 + sx) * ldx + (int64_t)h * P + col) =
-            u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
-      float qv = bf16lo(xv.x) * gb.x + bf16hi(xv.x) * gb.y + bf16lo(xv.y) * gb.z + bf16hi(xv.y) * gb.w;
-      // v_l partial dy_l . (h_s C_l) (the same rows of dy: l = sx)
-      float vv = bf16lo(dv.x) * hc.x + bf16hi(dv.x) * hc.y + bf16lo(dv.y) * hc.z + bf16hi(dv.y) * hc.w;
-      qv = xsum32(xsum16(qv));
-      vv = xsum32(xsum16(vv));
-      if (lane < 16) {
-        part[PQ + 32 * pt + sx] = qv;
-        part[PV + 32 * pt + sx] = vv;
-      }
-      if (sh == 0) {  // <g_e, h_s> over p-tile pt: the trace of (g_e h_s^T) on that tile
-        f32x4 gh4{};
-#pragma unroll
-        for (int q = 0; q < KQ; ++q) gh4 = mfma16b(gr[q], hr[q], gh4);
-        // lane (c16, g4) holds rows 4 g4 + r of column c16: the diagonal where 4 g4 + r = c16
-        const int r = c16 - 4 * g4;
-        float gh = r == 0 ? gh4.x : r == 1 ? gh4.y : r == 2 ? gh4.z : r == 3 ? gh4.w : 0.f;
-        gh = rowsum16(gh);
-        gh = xsum32(xsum16(gh));
-        if (lane == 0) part[PGH + pt] = gh;
-      }
     }
-    {
-      // dB, dC tiles: n-tile nt, s-tiles (l-tiles) t0d .. t0d + NTW - 1
-      const int nt = (NTW * wave) >> 1, t0d = (NTW * wave) & 1;
-      const u32x4 ct = trn(csm, N * 2, 4 * g4, 16 + 4 * g4, 16 * nt, true);
-      const u32x4 bt = trn(bsm, N * 2, 4 * g4, 16 + 4 * g4, 16 * nt, true);
-      u32x4 gsT[2], hsT[2];  // g_e^T, h_s^T rows n = 16 nt + c16, K = p = 32 kq + 8 g4 + 0..7
-#pragma unroll
-      for (int kq = 0; kq < 2; ++kq) {
-        gsT[kq] = trn(gss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
-        hsT[kq] = trn(hss, N * 2, 32 * kq + 8 * g4, 32 * kq + 8 * g4 + 4, 16 * nt, true);
-      }
-#pragma unroll
-      for (int i = 0; i < NTW; ++i) {
-        const int t = t0d + i;
-        const u32x4 elop = *reinterpret_cast<const u32x4 *>(opel + t * 1024 + lane * 16);
-        const u32x4 eltop = *reinterpret_cast<const u32x4 *>(opelt + t * 1024 + lane * 16);
-        dBa[i] = mfma16b(ct, elop, dBa[i]);
-        dCa[i] = mfma16b(bt, eltop, dCa[i]);
-        f32x4 gx{}, hy{};
-#pragma unroll
-        for (int kq = 0; kq < 2; ++kq) {
-          gx = mfma16b(gsT[kq], rowx(xs, 16 * t + c16, kq), gx);
-          hy = mfma16b(hsT[kq], rowx(ys, 16 * t + c16, kq), hy);
-        }
-        const float ws = tab[TW + 16 * t + c16], fl = tab[TF + 16 * t + c16];
-        dBa[i] += gx * ws;
-        dCa[i] += hy * fl;
-      }
-    }
-    }  // W = 8
     pAh = Ah;
     palast = alast;
   }
@@ -967,24 +890,14 @@ __global__ __launch_bounds__(64 * W, 1) void k_bwd_chunk(
   if (fin) finish(hpg - 1, pAh, palast);
 
   // ---- dB, dC of the chunk's rows: lane column s, rows n = 16 nt + 4 g4 + r ----
-  if constexpr (SPLIT) {
+  {
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
-      const int sx = 16 * i + c16;
+      const int nt = (NTW * (wave & 7)) >> 1, t = ((NTW * (wave & 7)) & 1) + i;
+      const int sx = 16 * t + c16;
       if (sx <= last)
         *reinterpret_cast<f32x4 *>((wave < 8 ? dB : dC) + (t0 + sx) * ldb + (int64_t)g * N +
-                                   16 * (wave & 7) + 4 * g4) = dBa[i];
-    }
-    return;
-  }
-#pragma unroll
-  for (int i = 0; i < NTW; ++i) {
-    const int nt = (NTW * wave) >> 1, t = ((NTW * wave) & 1) + i;
-    const int sx = 16 * t + c16;
-    if (sx <= last) {
-      const int64_t off = (t0 + sx) * ldb + (int64_t)g * N + 16 * nt + 4 * g4;
-      *reinterpret_cast<f32x4 *>(dB + off) = dBa[i];
-      *reinterpret_cast<f32x4 *>(dC + off) = dCa[i];
+                                   16 * nt + 4 * g4) = dBa[i];
     }
   }
 }
@@ -1043,14 +956,14 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
   const uint16_t *hs = static_cast<const uint16_t *>(hsave);
   const uint16_t *gs = static_cast<const uint16_t *>(gsave);
   uint16_t *dxo = static_cast<uint16_t *>(dx);
-  // two ring slots (one head in flight ahead); one block a CU, of 8 wavefronts
-  // (N 64) or 16 (N 128: the LDS holds one block either way, and four
-  // wavefronts a SIMD hide more of each head's chain of dependent steps)
+  // two ring slots (one head in flight ahead); one block a CU (the LDS holds
+  // one), of 16 wavefronts: four a SIMD hide more of each head's chain of
+  // dependent steps than two did
   if (N == 64)
-    hipLaunchKernelGGL((k_bwd_chunk<64, 2, 8>), grid, dim3(512), 0, stream, xi, dt, A, bi, ci, D, di,
-                       hs, hsld, gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+    hipLaunchKernelGGL((k_bwd_chunk<64, 2>), grid, dim3(1024), 0, stream, xi, dt, A, bi, ci, D,
+                       di, hs, hsld, gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else if (N == 128)
-    hipLaunchKernelGGL((k_bwd_chunk<128, 2, 16>), grid, dim3(1024), 0, stream, xi, dt, A, bi, ci, D,
+    hipLaunchKernelGGL((k_bwd_chunk<128, 2>), grid, dim3(1024), 0, stream, xi, dt, A, bi, ci, D,
                        di, hs, hsld, gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
   else
     return hipErrorInvalidValue;
