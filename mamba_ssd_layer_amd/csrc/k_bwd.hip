@@ -31,7 +31,7 @@
 //   2. k_bwd_reverse walks each (sequence, two heads) backwards, keeping g on
 //      chip like the forward keeps h (g <- exp(a_last) g + C^T (exp(a_l) dy)),
 //      saving g_e of every chunk and writing dL/dh0;
-//   3. k_bwd_chunk, one block of 8 wavefronts per (chunk, group), walks the
+//   3. k_bwd_chunk, one block of 16 wavefronts per (chunk, group), walks the
 //      group's heads: the chunk's B and C stay in LDS, each head's x, dy, h_s
 //      and g_e stream through an LDS ring; dx and ddt are written per head, dB
 //      and dC accumulate over the heads in registers and are written once, dA
@@ -599,8 +599,9 @@ __global__ __launch_bounds__(1024, 1) void k_bwd_chunk(
   for (int i = 0; i < NTW; ++i) dBa[i] = f32x4{};
 
   // ---- per-token scalars of head jj (its partials complete): computed by
-  // wavefronts 4-7 (one per SIMD, while 0-3 start the next head's heavier
-  // phase 1); wavefront 4 writes ddt and adds dA, dD ----
+  // wavefront 4 at the top of the next head's iteration, before its ET tile
+  // (0-3 start that head's heavier E tiles meanwhile); it writes ddt and adds
+  // dA, dD ----
   auto finish = [&](int jj, float Ah, float alast) {
     const int h = g * hpg + jj;
     const float *tab = tab_of(jj & 1);
