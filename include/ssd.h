@@ -410,7 +410,7 @@ size_t ssd_chunk_scan_bwd_workspace_size(const ssd_dims *dims);
  * is split into segments (sequences x nheads / 2 < 256), two fp32 P x N tiles
  * and a decay per segment and head.  At N = 256 those of N = 128 (each half
  * of the state's columns runs in turn), then one half's B and C (bf16),
- * dfinal, dB, dC and dinit (fp32), dx (bf16) and ddt.  Host-only. */
+ * dfinal, dB, dC and dinit (fp32) and ddt.  Host-only. */
 size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
 
 /* Gradients of the forward.  The pages give the recurrence h_t = exp(dt_t A)
@@ -450,9 +450,9 @@ size_t ssd_fused_bwd_workspace_size(const ssd_dims *dims);
  * into dA and dD with float atomics, so those two sum in an unspecified order.  N = 256 runs
  * these steps once per half of the state's columns (the columns never mix in
  * the recurrence): each half's B, C, saved states and dfinal are copied into
- * the workspace, its dB, dC and dinit copied back into their columns, and
- * the second half's dx and ddt added to the first's (dx then carries one
- * more bf16 rounding).  Returns after enqueueing. */
+ * the workspace, its dB, dC and dinit copied back into their columns; the
+ * second half adds its dx into the first's (read back as bf16) before its one
+ * rounding, and its ddt is added to the first's.  Returns after enqueueing. */
 ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const void *B,
                          const void *C, const float *D, const int32_t *cu_seqlens,
                          const void *chunk_states, size_t states_bytes, const void *dy,

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(256) void k_bwd_gpass(
 // <g_e, h_s> over p-tile w/2 (w even) and N/64 tiles of dC.  Wavefront 4
 // finishes the previous head's per-token scalars.  (Eight wavefronts, two a
 // SIMD, each doing both sides, measured 6-8% slower.)
-template <int N, int R>
+template <int N, int R, bool ACC = false>
 struct BwdCfg {
   static constexpr int P = 64, CQ = 32, NCB = N / 8, WAVES = 16;
   static constexpr int XT = CQ * P * 2;      // x or dy of a head: 32 rows x 128 B
@@ -378,7 +378,10 @@ struct BwdCfg {
   // a ring slot: x, dy, h_s, g_e, dt of the chunk; x or dy, dt of the neighbour chunk
   static constexpr int OX = 0, OY = XT, OH = 2 * XT, OG = OH + ST, ODT = OG + ST;
   static constexpr int ONX = ODT + 256, ONDT = ONX + XT;
-  static constexpr int HSLOT = ONDT + 256;
+  // ACC: the dx already written for the head (rows = tokens, like x), which
+  // this pass adds its own to
+  static constexpr int OAX = ONDT + 256;
+  static constexpr int HSLOT = OAX + (ACC ? XT : 0);
   static constexpr int OB = R * HSLOT, OCC = OB + BT;   // R ring slots of a head's tiles
   static constexpr int ONBC = OCC + BT;                  // B or C of the neighbour chunk
   static constexpr int OOP = ONBC + BT;                  // operands M, EL, ELT: [2][64 lanes][16 B] each
@@ -398,16 +401,16 @@ struct BwdCfg {
   static_assert(TOTAL <= 160 * 1024, "LDS");
 };
 
-template <int N, int R>
+template <int N, int R, bool ACC = false>
 __global__ __launch_bounds__(1024, 1) void k_bwd_chunk(
     const uint16_t *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const uint16_t *__restrict__ Bm, const uint16_t *__restrict__ Cm, const float *__restrict__ Dv,
     const uint16_t *__restrict__ dy, const uint16_t *__restrict__ hsave, int hsld,
     const uint16_t *__restrict__ gsave, const int32_t *__restrict__ cu, int64_t L, int64_t T,
-    int rows, int64_t nchunks, int H, int G, uint16_t *__restrict__ dx,
+    int rows, int64_t nchunks, int H, int G, const uint16_t *dxacc, uint16_t *dx,
     float *__restrict__ ddt, float *__restrict__ dA, float *__restrict__ dB,
     float *__restrict__ dC, float *__restrict__ dD) {
-  using F = BwdCfg<N, R>;
+  using F = BwdCfg<N, R, ACC>;
   constexpr int P = F::P, CQ = F::CQ, NCB = F::NCB, KP = F::KP, NTW = F::NTW;
   constexpr int W = F::WAVES, NT = 64 * W;  // wavefronts, threads
   constexpr int KQ = N / 32;  // K steps over n
@@ -546,6 +549,8 @@ __global__ __launch_bounds__(1024, 1) void k_bwd_chunk(
                      base + F::ONX + (wave & 3) * 1024);
       if (wave == ndtw) dma_lds4_sb(ndtoff, dt + tn0 * H + h, base + F::ONDT);
     }
+    if (ACC && wave >= 12)  // piece wave % 4 of the dx to add to (rows as for x)
+      dma_lds16_sb(xoff, dxacc + t0 * ldx + (int64_t)h * P, base + F::OAX + (wave & 3) * 1024);
   };
 
   // ---- the chunk's B and C, then heads 0 .. R-2 ahead ----
@@ -570,7 +575,8 @@ __global__ __launch_bounds__(1024, 1) void k_bwd_chunk(
   // vector-memory ops a wavefront issues per head: its x or dy piece, the
   // h_s and g_e pieces, dt, the neighbour chunk's piece and dt
   const int LDW = (wave < 8 ? 1 : 0) + (KP ? 2 * KP : 1) + (wave == 0 ? 1 : 0) +
-                  (mode != NONE ? (nxw ? 1 : 0) + (wave == ndtw ? 1 : 0) : 0);
+                  (mode != NONE ? (nxw ? 1 : 0) + (wave == ndtw ? 1 : 0) : 0) +
+                  (ACC && wave >= 12 ? 1 : 0);
   // stores and atomics a wavefront issues in iteration m: its dx tile of head
   // m (wavefronts 0-7); wavefront 4 also ddt, dA, dD of head m - 1
   const int dxw = wave < 8 ? 1 : 0;
@@ -819,10 +825,17 @@ __global__ __launch_bounds__(1024, 1) void k_bwd_chunk(
         for (int q = 0; q < KQ; ++q) gb = mfma16b(gr[q], rown(bsm, 16 * sh + c16, q), gb);
         const float ws = tab[TW + sx];
         const u32x2 xv = *reinterpret_cast<const u32x2 *>(xs + ro);
-        const float o0 = acc.x + ws * gb.x + Dh * bf16lo(dv.x);
-        const float o1 = acc.y + ws * gb.y + Dh * bf16hi(dv.x);
-        const float o2 = acc.z + ws * gb.z + Dh * bf16lo(dv.y);
-        const float o3 = acc.w + ws * gb.w + Dh * bf16hi(dv.y);
+        float o0 = acc.x + ws * gb.x + Dh * bf16lo(dv.x);
+        float o1 = acc.y + ws * gb.y + Dh * bf16hi(dv.x);
+        float o2 = acc.z + ws * gb.z + Dh * bf16lo(dv.y);
+        float o3 = acc.w + ws * gb.w + Dh * bf16hi(dv.y);
+        if constexpr (ACC) {
+          const u32x2 av = *reinterpret_cast<const u32x2 *>(hsl + F::OAX + ro);
+          o0 += bf16lo(av.x);
+          o1 += bf16hi(av.x);
+          o2 += bf16lo(av.y);
+          o3 += bf16hi(av.y);
+        }
         if (sx <= last)
           *reinterpret_cast<u32x2 *>(dx + (t0 + sx) * ldx + (int64_t)h * P + col) =
               u32x2{pack_bf16x2(o0, o1), pack_bf16x2(o2, o3)};
@@ -945,9 +958,11 @@ hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, c
 hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,
                             const void *C, const float *D, const void *dy, const void *hsave,
                             int hsld, const void *gsave, const int32_t *cu, int64_t L, int64_t T,
-                            int rows, int64_t nchunks, int H, int N, int G, void *dx, float *ddt,
-                            float *dA, float *dB, float *dC, float *dD, hipStream_t stream) {
+                            int rows, int64_t nchunks, int H, int N, int G, const void *dxacc,
+                            void *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                            hipStream_t stream) {
   if (nchunks == 0) return hipSuccess;
+  if (dxacc && N != 128) return hipErrorInvalidValue;
   if (hsld < N || hsld % 8) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>((nchunks * G + 7) / 8 * 8));
   const uint16_t *xi = static_cast<const uint16_t *>(x);
@@ -960,12 +975,21 @@ hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, cons
   // two ring slots (one head in flight ahead); one block a CU (the LDS holds
   // one), of 16 wavefronts: four a SIMD hide more of each head's chain of
   // dependent steps than two did
+  // (dxacc: dx adds into what dxacc holds, read tile by tile before each is
+  // written, so dxacc may be dx itself)
+  const uint16_t *dxa = static_cast<const uint16_t *>(dxacc);
   if (N == 64)
     hipLaunchKernelGGL((k_bwd_chunk<64, 2>), grid, dim3(1024), 0, stream, xi, dt, A, bi, ci, D,
-                       di, hs, hsld, gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+                       di, hs, hsld, gs, cu, L, T, rows, nchunks, H, G, dxa, dxo, ddt, dA, dB, dC,
+                       dD);
+  else if (N == 128 && dxa)
+    hipLaunchKernelGGL((k_bwd_chunk<128, 2, true>), grid, dim3(1024), 0, stream, xi, dt, A, bi, ci,
+                       D, di, hs, hsld, gs, cu, L, T, rows, nchunks, H, G, dxa, dxo, ddt, dA, dB,
+                       dC, dD);
   else if (N == 128)
     hipLaunchKernelGGL((k_bwd_chunk<128, 2>), grid, dim3(1024), 0, stream, xi, dt, A, bi, ci, D,
-                       di, hs, hsld, gs, cu, L, T, rows, nchunks, H, G, dxo, ddt, dA, dB, dC, dD);
+                       di, hs, hsld, gs, cu, L, T, rows, nchunks, H, G, dxa, dxo, ddt, dA, dB, dC,
+                       dD);
   else
     return hipErrorInvalidValue;
   return hipGetLastError();
@@ -983,18 +1007,7 @@ __global__ __launch_bounds__(256) void k_copy2d16(const unsigned char *__restric
   *reinterpret_cast<u32x4 *>(dst + r * dst_ld + u * 16) =
       *reinterpret_cast<const u32x4 *>(src + r * src_ld + u * 16);
 }
-// acc += add: bf16 (8 elements a thread, the sum rounded to nearest even) and fp32
-__global__ __launch_bounds__(256) void k_add_bf16(uint16_t *__restrict__ acc,
-                                                  const uint16_t *__restrict__ add, int64_t n8) {
-  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (i >= n8) return;
-  const u32x4 a = reinterpret_cast<const u32x4 *>(acc)[i], b = reinterpret_cast<const u32x4 *>(add)[i];
-  u32x4 o;
-#pragma unroll
-  for (int k = 0; k < 4; ++k)
-    o[k] = pack_bf16x2(bf16lo(a[k]) + bf16lo(b[k]), bf16hi(a[k]) + bf16hi(b[k]));
-  reinterpret_cast<u32x4 *>(acc)[i] = o;
-}
+// acc += add (fp32)
 __global__ __launch_bounds__(256) void k_add_f32(float *__restrict__ acc,
                                                  const float *__restrict__ add, int64_t n) {
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -1009,14 +1022,6 @@ hipError_t launch_copy2d16(const void *src, int64_t src_ld, void *dst, int64_t d
   hipLaunchKernelGGL(k_copy2d16, dim3(static_cast<unsigned>((n + 255) / 256)), dim3(256), 0, stream,
                      static_cast<const unsigned char *>(src), src_ld,
                      static_cast<unsigned char *>(dst), dst_ld, rows, units);
-  return hipGetLastError();
-}
-
-hipError_t launch_add_bf16(void *acc, const void *add, int64_t n, hipStream_t stream) {
-  if (n <= 0) return hipSuccess;
-  const int64_t n8 = n / 8;  // n is a multiple of 8 (token rows of a head dim of 64)
-  hipLaunchKernelGGL(k_add_bf16, dim3(static_cast<unsigned>((n8 + 255) / 256)), dim3(256), 0,
-                     stream, static_cast<uint16_t *>(acc), static_cast<const uint16_t *>(add), n8);
   return hipGetLastError();
 }
 

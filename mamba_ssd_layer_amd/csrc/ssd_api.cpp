@@ -527,9 +527,8 @@ struct BwdWorkspace {
   size_t gsave, gseg, gin, aseg, total;
   int64_t nseg, seglen;
   // N = 256, after one half's own workspace: its B, C and d(final_state), its
-  // dx and ddt (the second half's, added to the first's), dB, dC and
-  // d(init_state)
-  size_t bh, ch, dfh, dxh, ddth, dbh, dch, dih;
+  // ddt (the second half's, added to the first's), dB, dC and d(init_state)
+  size_t bh, ch, dfh, ddth, dbh, dch, dih;
 };
 
 BwdWorkspace bwd_workspace(const Plan &p) {
@@ -548,7 +547,6 @@ BwdWorkspace bwd_workspace(const Plan &p) {
     w.bh = take(bc * 2);
     w.ch = take(bc * 2);
     w.dfh = take(st * 4);
-    w.dxh = take((size_t)g.tokens * g.H * g.P * 2);
     w.ddth = take((size_t)g.tokens * g.H * 4);
     w.dbh = take(bc * 4);
     w.dch = take(bc * 4);
@@ -582,8 +580,8 @@ BwdWorkspace bwd_workspace(const Plan &p) {
 // Each half's B, C and d(final_state) are copied out of the 256-column rows
 // into packed 128-column buffers in the workspace (the saved states are read
 // in place, their rows 256 columns apart), its dB, dC and d(init_state) copied
-// back into their columns, and the second half's dx and ddt added to the
-// first's.
+// back into their columns; the second half's per-chunk pass adds its dx into
+// the first's as it writes it, and its ddt is added to the first's after.
 hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const float *dt,
                      const float *A, const void *B, const void *C, const float *D,
                      const int32_t *cu, const void *chunk_states, const void *dy,
@@ -591,7 +589,7 @@ hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const
                      float *dD, float *dinit, void *workspace, hipStream_t st) {
   const ssd::Geometry &g = p.geo;
   unsigned char *ws = static_cast<unsigned char *>(workspace);
-  void *Bh = ws + bw.bh, *Ch = ws + bw.ch, *dxh = ws + bw.dxh;
+  void *Bh = ws + bw.bh, *Ch = ws + bw.ch;
   float *dfh = dfinal ? reinterpret_cast<float *>(ws + bw.dfh) : nullptr;
   float *ddth = reinterpret_cast<float *>(ws + bw.ddth);
   float *dBh = reinterpret_cast<float *>(ws + bw.dbh), *dCh = reinterpret_cast<float *>(ws + bw.dch);
@@ -619,7 +617,8 @@ hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const
     if (e == hipSuccess)
       e = ssd::launch_bwd_chunk(x, dt, A, Bh, Ch, k ? nullptr : D, dy, s + o2, 256, workspace,
                                 cu, g.L, g.tokens, (int)g.nrows, chunks32(p), g.H, 128, g.G,
-                                k ? dxh : dx, k ? ddth : ddt, dA, dBh, dCh, k ? nullptr : dD, st);
+                                k ? dx : nullptr, dx, k ? ddth : ddt, dA, dBh, dCh,
+                                k ? nullptr : dD, st);
     if (e == hipSuccess)
       e = ssd::launch_copy2d16(dBh, 512, reinterpret_cast<unsigned char *>(dB) + o4, 1024, trows,
                                32, st);
@@ -630,7 +629,6 @@ hipError_t split_bwd(const Plan &p, const BwdWorkspace &bw, const void *x, const
       e = ssd::launch_copy2d16(dih, 512, reinterpret_cast<unsigned char *>(dinit) + o4, 1024,
                                frows, 32, st);
   }
-  if (e == hipSuccess) e = ssd::launch_add_bf16(dx, dxh, g.tokens * g.H * g.P, st);
   if (e == hipSuccess) e = ssd::launch_add_f32(ddt, ddth, g.tokens * g.H, st);
   return e;
 }
@@ -958,8 +956,8 @@ ssd_status ssd_fused_bwd(const void *x, const float *dt, const float *A, const v
                                 ws_ptr<float>(workspace, bw.gin), st);
   if (e == hipSuccess)
     e = ssd::launch_bwd_chunk(x, dt, A, B, C, D, dy, chunk_states, g.N, workspace, cu, g.L, g.tokens,
-                              (int)g.nrows, chunks32(p), g.H, g.N, g.G, dx, ddt, dA, dB, dC, dD,
-                              st);
+                              (int)g.nrows, chunks32(p), g.H, g.N, g.G, nullptr, dx, ddt, dA, dB,
+                              dC, dD, st);
   return hip_status(e);
 }
 

@@ -100,14 +100,14 @@ hipError_t launch_bwd_reverse(const void *dy, const float *dt, const float *A, c
 hipError_t launch_bwd_chunk(const void *x, const float *dt, const float *A, const void *B,
                             const void *C, const float *D, const void *dy, const void *hsave,
                             int hsld, const void *gsave, const int32_t *cu, int64_t L, int64_t T,
-                            int rows, int64_t nchunks, int H, int N, int G, void *dx, float *ddt,
-                            float *dA, float *dB, float *dC, float *dD, hipStream_t stream);
+                            int rows, int64_t nchunks, int H, int N, int G, const void *dxacc,
+                            void *dx, float *ddt, float *dA, float *dB, float *dC, float *dD,
+                            hipStream_t stream);
 hipError_t launch_fill_f32(float *p, int64_t n, hipStream_t stream);
 // rows x units 16-byte pieces between row-major layouts (byte row strides)
 hipError_t launch_copy2d16(const void *src, int64_t src_ld, void *dst, int64_t dst_ld,
                            int64_t rows, int units, hipStream_t stream);
 // acc += add elementwise: bf16 (n a multiple of 8, 16-byte aligned) and fp32
-hipError_t launch_add_bf16(void *acc, const void *add, int64_t n, hipStream_t stream);
 hipError_t launch_add_f32(float *acc, const float *add, int64_t n, hipStream_t stream);
 
 // the general backward on the vector ALU, from the forward's workspace at chunk

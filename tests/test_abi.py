@@ -409,13 +409,14 @@ def test_fused_states_size():
     assert L.ssd_fused_bwd_workspace_size(ctypes.byref(lp)) == \
         (1024 + 2) * 80 * 64 * 64 * 2 + per(32 + 2, 64)
     # N 256: the workspace of an N 128 backward (two halves run in turn), then
-    # one half's B, C, d(final), dx, ddt, dB, dC, d(init)
+    # one half's B, C, d(final), ddt, dB, dC, d(init) (the second half adds its
+    # dx into the first's as it writes it)
     d = good()  # 2 x 512 tokens, H 4, P 64, G 1
     d.dstate = 256
     T, H, P, rows = 1024, 4, 64, 2
     nseg = 2 * 2
     half = 2 * 8 * H * P * 128 * 2 + 2 * nseg * H * P * 128 * 4 + 256
-    extra = (2 * T * 128 * 2 + rows * H * P * 128 * 4 + T * H * P * 2
+    extra = (2 * T * 128 * 2 + rows * H * P * 128 * 4
              + T * H * 4 + 2 * T * 128 * 4 + rows * H * P * 128 * 4)
     assert L.ssd_fused_bwd_workspace_size(ctypes.byref(d)) == half + extra
     for mut, fwd_ok in ((dict(io_dtype=SSD_F32), False), (dict(headdim=128), True),
